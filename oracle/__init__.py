@@ -1,0 +1,139 @@
+"""fp64 CPU oracle of the VLA per-head forward recurrence -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library never calls it and the
+two share no code; the only common module is ``gen`` (seeded input draws).
+
+The arithmetic lives in ``vla_oracle.c`` (plain C, fp64, one token at a time,
+following "Variational Linear Attention" (arXiv 2605.11196) section 3.3,
+Eqs. (9)-(11)).  This wrapper only marshals arrays and runs independent heads
+on a thread pool (the C call releases the GIL).
+
+Pins (tests/test_oracle_pins.py) tie each part to something other than the
+oracle itself: brute-force inverses of the penalty matrix, the first token
+worked by hand, the d = 1 closed form, the epsilon branch, the delta-rule and
+cumulative-sum special cases, the state-update invariants, continuation and
+head independence.  No function here is left unpinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vla_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force: bool = True) -> str:
+    """Compile vla_oracle.c with the host C compiler (no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
+                        _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        f = lib.vla_oracle_forward
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double] + [_dp] * 18
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_dp)
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    if shape is not None and a.shape != shape:
+        raise ValueError(f"expected shape {shape}, got {a.shape}")
+    return a
+
+
+def forward_head(q, k, v, u, lambda0=0.1, eps=1e-4, S0=None, A0=None, zkey0=None,
+                 trace=False):
+    """Run one head: q, k, v, u are [T, d].  Returns a dict with ``o`` [T, d],
+    final ``S``, ``A`` [d, d] and ``zkey`` [d]; with ``trace`` also per-token
+    ``delta`` [T], ``alpha``, ``e``, ``z`` [T, d], ``den`` [T], ``A_t``, ``S_t``
+    [T, d, d]."""
+    q = _f64(q)
+    T, d = q.shape
+    k, v, u = _f64(k, (T, d)), _f64(v, (T, d)), _f64(u, (T, d))
+    S0, A0, zkey0 = _f64(S0, (d, d)), _f64(A0, (d, d)), _f64(zkey0, (d,))
+    o = np.zeros((T, d))
+    S = np.zeros((d, d))
+    A = np.zeros((d, d))
+    zk = np.zeros(d)
+    tr = {}
+    if trace:
+        tr = dict(delta=np.zeros(T), alpha=np.zeros((T, d)), e=np.zeros((T, d)),
+                  z=np.zeros((T, d)), den=np.zeros(T), A_t=np.zeros((T, d, d)),
+                  S_t=np.zeros((T, d, d)))
+    rc = _load().vla_oracle_forward(
+        T, d, float(lambda0), float(eps), _ptr(q), _ptr(k), _ptr(v), _ptr(u),
+        _ptr(S0), _ptr(A0), _ptr(zkey0), _ptr(o), _ptr(S), _ptr(A), _ptr(zk),
+        _ptr(tr.get("delta")), _ptr(tr.get("alpha")), _ptr(tr.get("e")), _ptr(tr.get("z")),
+        _ptr(tr.get("den")), _ptr(tr.get("A_t")), _ptr(tr.get("S_t")))
+    if rc != 0:
+        raise ValueError(f"vla_oracle_forward failed with code {rc}")
+    out = dict(o=o, S=S, A=A, zkey=zk)
+    out.update(tr)
+    return out
+
+
+def default_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, n)
+
+
+def forward(q, k, v, u, lambda0=0.1, eps=1e-4, S0=None, A0=None, zkey0=None,
+            workers=None):
+    """All heads of [B, H, T, d] inputs (independent heads on a thread pool).
+
+    S0, A0 ([B, H, d, d]) and zkey0 ([B, H, d]) are optional initial states.
+    Returns ``o`` [B, H, T, d] and final ``S``, ``A``, ``zkey``.
+    """
+    q = np.asarray(q)
+    B, H, T, d = q.shape
+    o = np.zeros((B, H, T, d))
+    S = np.zeros((B, H, d, d))
+    A = np.zeros((B, H, d, d))
+    zk = np.zeros((B, H, d))
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        r = forward_head(q[b, h], k[b, h], v[b, h], u[b, h], lambda0, eps,
+                         None if S0 is None else S0[b, h],
+                         None if A0 is None else A0[b, h],
+                         None if zkey0 is None else zkey0[b, h])
+        o[b, h], S[b, h], A[b, h], zk[b, h] = r["o"], r["S"], r["A"], r["zkey"]
+
+    n = min(workers or default_workers(), B * H)
+    if n <= 1:
+        for bh in range(B * H):
+            one(bh)
+    else:
+        with ThreadPoolExecutor(max_workers=n) as ex:
+            list(ex.map(one, range(B * H)))
+    return dict(o=o, S=S, A=A, zkey=zk)
