@@ -1,0 +1,154 @@
+#!/usr/bin/env python3
+"""Benchmark of the VLA forward recurrence on one MI355X.
+
+One step = one ``vla_forward`` over the whole batch of the d_h = 64, T = 4096
+workload (B = 8, H = 16, bf16 q/k/v/u, fp32 state), writing o and the final
+S, A and zkey.  Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line with the throughput in tokens*heads/s, the percentage of
+the MI355X FP32 vector peak, a roofline record for the forward kernel
+(algorithmic FLOP / average kernel time from HIP events on the launch stream)
+and the fp64 CPU oracle timed on the host cores over a bounded sample of heads.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "VLA fwd tokens·heads/sec (fp32 state) + % of MI355X FP32 vector peak"
+UNIT = "tokens*heads/s"
+FP32_VECTOR_PEAK_TFLOPS = 157.3          # MI355X published FP32 vector peak
+WORKLOAD = 3                              # B=8, H=16, d_h=64, T=4096, bf16 inputs
+
+
+def flops_per_token_head(d: int) -> int:
+    """Algorithmic work of one token of one head: the matrix-vector products
+    A u^, A k^, S k^ and S phi(q) (2 d^2 each) and the rank-1 updates of A and
+    S (2 d^2 each); O(d) terms are not counted."""
+    return 12 * d * d
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the oracle timing (e.g. under a profiler)")
+    p.add_argument("--cpu-heads", type=int, default=0,
+                   help="heads in the CPU-baseline sample (0 = every head of the workload)")
+    return p.parse_args()
+
+
+def cpu_baseline(cfg, n_heads_req: int):
+    """fp64 oracle on the host cores over a bounded sample of whole heads of the
+    same workload (each head is an independent T-token sequence)."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import gen
+    import oracle
+
+    cores = oracle.default_workers()
+    n_heads = min(n_heads_req or cfg.B * cfg.H, cfg.B * cfg.H)
+    heads = [divmod(i, cfg.H) for i in range(n_heads)]
+    inputs = []
+    for b, h in heads:
+        hi = gen.head_inputs(cfg, b, h)
+        inputs.append([hi[n].astype(np.float64) for n in "qkvu"])
+    used = min(cores, n_heads)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=used) as ex:
+        list(ex.map(lambda a: oracle.forward_head(*a, cfg.lambda0, cfg.eps), inputs))
+    wall = time.perf_counter() - t0
+    return {"value": n_heads * cfg.T / wall, "unit": UNIT, "cores": used, "kind": "oracle",
+            "sample": f"{n_heads} of {cfg.B * cfg.H} heads, T={cfg.T}, d_h={cfg.d}, fp64, "
+                      f"wall {wall:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "heads shard across GPUs with no communication, see the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import long_context_sequence_amd as vla
+
+    cfg = gen.config(WORKLOAD)
+    B, H, T, d = cfg.B, cfg.H, cfg.T, cfg.d
+    dev = torch.device("cuda:0")
+    x = gen.make_inputs(cfg)
+    t = {n: torch.from_numpy(x[n]).to(dev).view(torch.bfloat16) for n in "qkvu"}
+    o = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    A = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    zk = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        vla.vla_forward(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps,
+                        o=o, S_out=S, A_out=A, zkey_out=zk, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    kern_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    tok_heads = B * H * T
+    value = tok_heads / (ms_per_step / 1e3)
+    flop = flops_per_token_head(d) * tok_heads
+    achieved_tflops = flop / (kern_ms / 1e3) / 1e12
+    pct_peak = 100.0 * (flop / (ms_per_step / 1e3) / 1e12) / FP32_VECTOR_PEAK_TFLOPS
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "H": H, "d_h": d, "T": T,
+                   "input_dtype": cfg.dtype, "state_dtype": "f32",
+                   "lambda0": cfg.lambda0, "eps": cfg.eps, "parallelism": "single GPU"},
+        "pct_fp32_vector_peak": pct_peak,
+        "roofline": {"bound": "alu", "achieved": achieved_tflops,
+                     "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                     "kernel_ms": kern_ms, "flop_per_launch": flop},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,103 @@
+/*
+ * vla.h -- C ABI of the MI355X (gfx950) Variational Linear Attention library.
+ *
+ * The operation is the per-head VLA recurrence of "Variational Linear
+ * Attention: Stable Associative Memory for Long-Context Transformers"
+ * (arXiv 2605.11196), section 3.3, Eqs. (9), (10) and (11), with the initial
+ * state of section 3.2 (A_0 = I / lambda0).  For every (batch b, head h), one
+ * token t at a time:
+ *
+ *   k^ = k_t / |k_t|,  u^ = u_t / |u_t|            (a zero vector stays zero)
+ *   z = A u^,  delta = 1 + u^' z,  A <- A - z z' / delta                 Eq. (9)
+ *   e = v_t - S k^ (old S),  alpha^ = A k^ / |A k^| (new A),  S <- S + e alpha^'
+ *                                                                         Eq. (10)
+ *   zkey <- zkey + phi(k_t),  phi = ELU + 1 applied to the raw key,
+ *   o_t = S phi(q_t) / max(phi(q_t)' zkey, eps)  (new S)                   Eq. (11)
+ *
+ * Data layout (all row-major, contiguous, no strides):
+ *   q, k, v, u : [B][H][T][d_h] of the input type (fp32 or bf16), on the device
+ *   o          : [B][H][T][d_h] fp32
+ *   S, A       : [B][H][d_h][d_h] fp32; S[i][j] has i = value index and
+ *                j = key index (o = S phi(q)); A is stored in full (symmetric)
+ *   zkey       : [B][H][d_h] fp32, the running sum of phi(k)
+ * Every pointer is a device pointer and must be 16-byte aligned.
+ *
+ * Supported: d_h in {16, 32, 64, 96, 128}; B, H >= 1; T >= 0; finite
+ * lambda0 > 0 and eps > 0.  State arithmetic is fp32 throughout; bf16 inputs
+ * are widened exactly.
+ *
+ * Ownership and execution: the caller owns every buffer.  Calls are
+ * asynchronous on `stream` (a hipStream_t; NULL = the null stream) and never
+ * synchronise.  Arguments are checked before anything is launched; on an
+ * argument error nothing is launched and no buffer is touched.  A failed launch
+ * returns VLA_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ * synchronisation.  NaN or Inf inputs propagate without being reported.
+ * Concurrent calls on different streams that write the same buffers race.
+ */
+#ifndef VLA_H
+#define VLA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum vla_status {
+    VLA_OK = 0,
+    VLA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size or constant */
+    VLA_ERR_UNSUPPORTED = 2,   /* d_h or dtype this library has no kernel for   */
+    VLA_ERR_HIP = 3            /* a HIP runtime call or launch failed           */
+} vla_status;
+
+typedef enum vla_dtype {
+    VLA_F32 = 0,
+    VLA_BF16 = 1
+} vla_dtype;
+
+/*
+ * vla_forward -- run T tokens of every (b, h) head in one launch.
+ *
+ * q, k, v, u   inputs [B][H][T][d_h] of type in_dtype (required when T > 0).
+ * lambda0      penalty initialiser: the default A_0 is I / lambda0.
+ * eps          floor of the readout denominator (Eq. 11).
+ * o            output [B][H][T][d_h] fp32 (required when T > 0).
+ * S_out, A_out, zkey_out
+ *              final state [B][H][d][d], [B][H][d][d], [B][H][d]; each may be
+ *              NULL to skip it.  They may alias S0, A0, zkey0 (in-place update).
+ * S0, A0, zkey0
+ *              initial state in the same layout, or NULL for the defaults
+ *              S_0 = 0, A_0 = I / lambda0, zkey_0 = 0.  A0 must be symmetric
+ *              positive definite (as every A_t of the recurrence is).
+ * stream       hipStream_t to launch on.
+ *
+ * T == 0 launches a copy of the initial state to the requested outputs.
+ */
+vla_status vla_forward(const void *q, const void *k, const void *v, const void *u,
+                       int in_dtype, int B, int H, int T, int d_h,
+                       float lambda0, float eps,
+                       float *o, float *S_out, float *A_out, float *zkey_out,
+                       const float *S0, const float *A0, const float *zkey0,
+                       void *stream);
+
+/*
+ * vla_step -- one decode token for every (b, h) head: the same recurrence as
+ * vla_forward with T = 1, continuing from the caller's state, which is updated
+ * in place.  This is the streaming form of the method: the state is fixed-size
+ * (S, A, zkey) and no key/value cache is kept.
+ *
+ * q, k, v, u   inputs [B][H][d_h] of type in_dtype.
+ * S, A, zkey   in/out state [B][H][d][d], [B][H][d][d], [B][H][d] (required).
+ * o            output [B][H][d_h] fp32.
+ */
+vla_status vla_step(const void *q, const void *k, const void *v, const void *u,
+                    int in_dtype, int B, int H, int d_h, float eps,
+                    float *S, float *A, float *zkey, float *o,
+                    void *stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *vla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VLA_H */

@@ -1,0 +1,154 @@
+"""ctypes binding of libvla.so (include/vla.h): argument marshalling only.
+
+Every step of the recurrence runs in the library's HIP kernels.  PyTorch is
+used only for device memory and the current stream.  There is no fallback: if
+the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvla.so")
+
+VLA_OK, VLA_ERR_INVALID_ARG, VLA_ERR_UNSUPPORTED, VLA_ERR_HIP = 0, 1, 2, 3
+VLA_F32, VLA_BF16 = 0, 1
+
+_vp = ctypes.c_void_p
+_lib = None
+
+
+class VLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def load() -> ctypes.CDLL:
+    """Load libvla.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; build it with "
+                "`python -m long_context_sequence_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.vla_forward.restype = ctypes.c_int
+        lib.vla_forward.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        lib.vla_step.restype = ctypes.c_int
+        lib.vla_step.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_float, _vp, _vp, _vp, _vp, _vp]
+        lib.vla_status_string.restype = ctypes.c_char_p
+        lib.vla_status_string.argtypes = [ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().vla_status_string(int(status)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return VLA_F32
+    if t.dtype == torch.bfloat16:
+        return VLA_BF16
+    raise TypeError(f"unsupported input dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _check(t, name, shape, dtype=None, device=None):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def vla_forward(q, k, v, u, lambda0: float = 0.1, eps: float = 1e-4, *,
+                o=None, S_out=None, A_out=None, zkey_out=None,
+                S0=None, A0=None, zkey0=None, return_state: bool = False, stream=None):
+    """VLA forward over [B, H, T, d_h] device tensors (float32 or bfloat16).
+
+    Returns ``o`` ([B, H, T, d_h] float32), or ``(o, S, A, zkey)`` when
+    ``return_state`` is set or any state output is passed.  ``S0, A0, zkey0``
+    continue from a given state.  Launches on ``stream`` (default: PyTorch's
+    current stream) without synchronising.
+    """
+    torch = _torch()
+    B, H, T, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("u", u)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    f32 = torch.float32
+    if o is None:
+        o = torch.empty((B, H, T, d), dtype=f32, device=dev)
+    want_state = return_state or any(x is not None for x in (S_out, A_out, zkey_out))
+    if return_state:
+        S_out = torch.empty((B, H, d, d), dtype=f32, device=dev) if S_out is None else S_out
+        A_out = torch.empty((B, H, d, d), dtype=f32, device=dev) if A_out is None else A_out
+        zkey_out = torch.empty((B, H, d), dtype=f32, device=dev) if zkey_out is None else zkey_out
+    _check(o, "o", (B, H, T, d), f32, dev)
+    for name, t, shp in (("S_out", S_out, (B, H, d, d)), ("A_out", A_out, (B, H, d, d)),
+                         ("zkey_out", zkey_out, (B, H, d)), ("S0", S0, (B, H, d, d)),
+                         ("A0", A0, (B, H, d, d)), ("zkey0", zkey0, (B, H, d))):
+        _check(t, name, shp, f32, dev)
+    st = load().vla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _dtype_code(q), B, H, T, d,
+                            float(lambda0), float(eps), _ptr(o), _ptr(S_out), _ptr(A_out),
+                            _ptr(zkey_out), _ptr(S0), _ptr(A0), _ptr(zkey0), _stream(stream))
+    if st != VLA_OK:
+        raise VLAError(st, "vla_forward")
+    return (o, S_out, A_out, zkey_out) if want_state else o
+
+
+def vla_step(q, k, v, u, S, A, zkey, eps: float = 1e-4, *, o=None, stream=None):
+    """One decode token: q, k, v, u are [B, H, d_h]; S, A ([B, H, d, d]) and
+    zkey ([B, H, d]) float32 state tensors are updated in place.  Returns o
+    ([B, H, d_h] float32)."""
+    torch = _torch()
+    B, H, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("u", u)):
+        _check(t, name, (B, H, d), q.dtype, dev)
+    f32 = torch.float32
+    if o is None:
+        o = torch.empty((B, H, d), dtype=f32, device=dev)
+    _check(o, "o", (B, H, d), f32, dev)
+    _check(S, "S", (B, H, d, d), f32, dev)
+    _check(A, "A", (B, H, d, d), f32, dev)
+    _check(zkey, "zkey", (B, H, d), f32, dev)
+    st = load().vla_step(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _dtype_code(q), B, H, d,
+                         float(eps), _ptr(S), _ptr(A), _ptr(zkey), _ptr(o), _stream(stream))
+    if st != VLA_OK:
+        raise VLAError(st, "vla_step")
+    return o
+
+
+def vla_status_string(status: int) -> str:
+    return status_string(status)

@@ -1,0 +1,34 @@
+// vla_common.h -- internal declarations shared by the library's HIP sources.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vla {
+
+// Launch arguments after the C-ABI checks (see include/vla.h for meaning).
+struct FwdArgs {
+    const void *q, *k, *v, *u;
+    int dtype;            // 0 = fp32, 1 = bf16
+    int B, H, T, d;
+    float lambda0, eps;
+    float *o, *S_out, *A_out, *zk_out;
+    const float *S0, *A0, *zk0;
+    hipStream_t stream;
+};
+
+// Input widening: fp32 as is, bf16 (stored as its 16 bit pattern) exactly.
+__device__ __forceinline__ float load_in(const float *p, size_t i) { return p[i]; }
+__device__ __forceinline__ float load_in(const uint16_t *p, size_t i)
+{
+    return __uint_as_float(((uint32_t)p[i]) << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// phi = ELU + 1 (ELU with alpha = 1): x + 1 for x > 0, exp(x) otherwise.
+__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+hipError_t launch_forward_ref(const FwdArgs &a);
+
+}  // namespace vla

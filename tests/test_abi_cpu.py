@@ -1,0 +1,102 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments with the documented codes before
+launching anything (these calls return before any HIP runtime call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_sequence_amd as vla
+from long_context_sequence_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "vla.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vla_[a-z_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    names = _declared_functions()
+    assert {"vla_forward", "vla_step", "vla_status_string"} <= set(names)
+    lib = ctypes.CDLL(vla.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in vla.h but not exported"
+
+
+def test_status_strings():
+    for code in range(4):
+        s = vla.vla_status_string(code)
+        assert s.startswith("VLA_")
+    assert "unknown" in vla.vla_status_string(99)
+
+
+FAKE = 0x10000           # 16-byte aligned, never dereferenced: checks fail first
+MIS = 0x10004            # misaligned
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, dt=0, B=1, H=1, T=4, d=64, lam=0.1, eps=1e-4,
+             o=FAKE, S=None, A=None, z=None, S0=None, A0=None, z0=None, stream=None)
+    a.update(kw)
+    return B.load().vla_forward(a["q"], a["k"], a["v"], a["u"], a["dt"], a["B"], a["H"], a["T"],
+                                a["d"], a["lam"], a["eps"], a["o"], a["S"], a["A"], a["z"],
+                                a["S0"], a["A0"], a["z0"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), B.VLA_ERR_INVALID_ARG),
+    (dict(o=None), B.VLA_ERR_INVALID_ARG),
+    (dict(k=MIS), B.VLA_ERR_INVALID_ARG),
+    (dict(S=MIS), B.VLA_ERR_INVALID_ARG),
+    (dict(B=0), B.VLA_ERR_INVALID_ARG),
+    (dict(H=-1), B.VLA_ERR_INVALID_ARG),
+    (dict(T=-1), B.VLA_ERR_INVALID_ARG),
+    (dict(lam=0.0), B.VLA_ERR_INVALID_ARG),
+    (dict(lam=float("nan")), B.VLA_ERR_INVALID_ARG),
+    (dict(eps=0.0), B.VLA_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), B.VLA_ERR_INVALID_ARG),
+    (dict(d=48), B.VLA_ERR_UNSUPPORTED),
+    (dict(d=256), B.VLA_ERR_UNSUPPORTED),
+    (dict(dt=2), B.VLA_ERR_UNSUPPORTED),
+    (dict(B=1 << 16, H=1 << 16), B.VLA_ERR_INVALID_ARG),
+])
+def test_forward_argument_errors(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_forward_empty_no_outputs_is_ok():
+    # T = 0 with no state outputs requested: nothing to do, nothing launched.
+    assert _fwd(T=0, q=None, k=None, v=None, u=None, o=None) == B.VLA_OK
+
+
+def _step(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, dt=1, B=2, H=2, d=128, eps=1e-4,
+             S=FAKE, A=FAKE, z=FAKE, o=FAKE, stream=None)
+    a.update(kw)
+    return B.load().vla_step(a["q"], a["k"], a["v"], a["u"], a["dt"], a["B"], a["H"], a["d"],
+                             a["eps"], a["S"], a["A"], a["z"], a["o"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=None), B.VLA_ERR_INVALID_ARG),
+    (dict(A=None), B.VLA_ERR_INVALID_ARG),
+    (dict(z=None), B.VLA_ERR_INVALID_ARG),
+    (dict(o=MIS), B.VLA_ERR_INVALID_ARG),
+    (dict(eps=-1.0), B.VLA_ERR_INVALID_ARG),
+    (dict(d=100), B.VLA_ERR_UNSUPPORTED),
+    (dict(B=0), B.VLA_ERR_INVALID_ARG),
+])
+def test_step_argument_errors(kw, code):
+    assert _step(**kw) == code
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        vla.vla_forward(x, x, x, x)

@@ -1,0 +1,248 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle on
+the same seeded inputs.
+
+Gate (fp32 state): max|x_gpu - x_ref| / max|x_ref| <= 2e-3 for o and for the
+final S, A and zkey.  Small cases compare every head; the full-size workloads
+run every head on the GPU in the benchmark's launch configuration and compare
+sampled heads (the oracle computes heads independently).
+"""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GATE = 2e-3
+
+
+def _vla():
+    import long_context_sequence_amd as vla
+    return vla
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _to_dev(x, cfg, dev):
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    return t.view(torch.bfloat16) if cfg.dtype == "bf16" else t
+
+
+def _f64(x, cfg):
+    return (gen.bf16_bits_to_f32(x) if cfg.dtype == "bf16" else x).astype(np.float64)
+
+
+def rel(g, r):
+    g = np.asarray(g, dtype=np.float64)
+    return float(np.abs(g - r).max() / max(np.abs(r).max(), 1e-30))
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _gpu_forward(cfg, x, dev, **kw):
+    t = {n: _to_dev(x[n], cfg, dev) for n in "qkvu"}
+    out = _vla().vla_forward(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps,
+                             return_state=True, **kw)
+    torch.cuda.synchronize()
+    return [a.cpu().numpy() for a in out]
+
+
+def _check(name, got, ref, gate=GATE):
+    e = rel(got, ref)
+    _say(f"  {name}: rel err {e:.3e}")
+    assert e <= gate, f"{name}: {e:.3e} > {gate}"
+
+
+def _compare_heads(cfg, x, out, heads):
+    o, S, A, zk = out
+    for (b, h) in heads:
+        r = oracle.forward_head(*(_f64(x[n][b, h], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+        _say(f" head ({b},{h})")
+        _check("o", o[b, h], r["o"])
+        _check("S", S[b, h], r["S"])
+        _check("A", A[b, h], r["A"])
+        _check("zkey", zk[b, h], r["zkey"])
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_small_workloads_every_head(cid):
+    dev = _dev()
+    cfg = gen.config(cid)
+    _say(f"workload {cfg.name}")
+    x = gen.make_inputs(cfg)
+    out = _gpu_forward(cfg, x, dev)
+    ref = oracle.forward(*(_f64(x[n], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+    for name, g in zip(("o", "S", "A", "zkey"), out):
+        _check(name, g, ref[name])
+
+
+@pytest.mark.parametrize("cid,heads", [
+    (3, [(0, 0), (3, 7), (5, 11), (7, 15)]),
+    (4, [(0, 0), (1, 17), (3, 31)]),
+])
+def test_full_size_sampled_heads(cid, heads):
+    dev = _dev()
+    cfg = gen.config(cid)
+    _say(f"workload {cfg.name} (full size)")
+    x = gen.make_inputs(cfg)
+    out = _gpu_forward(cfg, x, dev)
+    assert np.isfinite(out[0]).all()
+    _compare_heads(cfg, x, out, heads)
+
+
+@pytest.mark.slow
+def test_long_context_full_size_with_decode():
+    """B=2, H=32, d=128, T=65536 bf16, then 4096 single-token decode steps
+    continuing from the final state; sampled heads checked over both parts."""
+    from concurrent.futures import ThreadPoolExecutor
+    dev = _dev()
+    vla = _vla()
+    cfg = gen.config(5)
+    _say(f"workload {cfg.name} (full size)")
+    x = gen.make_inputs(cfg)
+    heads = [(0, 5), (1, 30)]
+
+    def ref_head(bh):
+        b, h = bh
+        r1 = oracle.forward_head(*(_f64(x[n][b, h], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+        r2 = oracle.forward_head(*(_f64(x[n + "_dec"][b, h], cfg) for n in "qkvu"),
+                                 cfg.lambda0, cfg.eps, S0=r1["S"], A0=r1["A"], zkey0=r1["zkey"])
+        return r1, r2
+
+    with ThreadPoolExecutor(max_workers=len(heads)) as ex:
+        refs = ex.submit(lambda: list(map(ref_head, heads)))
+        o, S, A, zk = _gpu_forward(cfg, x, dev)
+        assert np.isfinite(o).all()
+        _say(" decode 4096 steps")
+        St, At, zt = (torch.from_numpy(a).to(dev) for a in (S, A, zk))
+        dec = {n: _to_dev(x[n + "_dec"], cfg, dev) for n in "qkvu"}
+        od = torch.empty((cfg.B, cfg.H, cfg.decode, cfg.d), dtype=torch.float32, device=dev)
+        for t in range(cfg.decode):
+            od[:, :, t] = vla.vla_step(*(dec[n][:, :, t].contiguous() for n in "qkvu"),
+                                       St, At, zt, cfg.eps)
+        torch.cuda.synchronize()
+        od = od.cpu().numpy()
+        refs = refs.result()
+    for (b, h), (r1, r2) in zip(heads, refs):
+        _say(f" head ({b},{h})")
+        _check("o", o[b, h], r1["o"])
+        _check("S", S[b, h], r1["S"])
+        _check("A", A[b, h], r1["A"])
+        _check("zkey", zk[b, h], r1["zkey"])
+        _check("o_decode", od[b, h], r2["o"])
+        _check("S_after_decode", St[b, h].cpu().numpy(), r2["S"])
+        _check("A_after_decode", At[b, h].cpu().numpy(), r2["A"])
+        _check("zkey_after_decode", zt[b, h].cpu().numpy(), r2["zkey"])
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 96, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 37, 300])
+def test_shape_sweep_every_head(d, dtype, T):
+    dev = _dev()
+    base = gen.config(3 if dtype == "bf16" else 2)
+    import dataclasses
+    cfg = dataclasses.replace(base, d=d).with_sizes(B=2, H=3, T=T)
+    _say(f"sweep d={d} {dtype} T={T}")
+    x = gen.make_inputs(cfg)
+    out = _gpu_forward(cfg, x, dev)
+    ref = oracle.forward(*(_f64(x[n], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+    for name, g in zip(("o", "S", "A", "zkey"), out):
+        _check(name, g, ref[name])
+
+
+def test_empty_sequence_copies_state():
+    dev = _dev()
+    vla = _vla()
+    B, H, d = 2, 2, 32
+    e = torch.empty((B, H, 0, d), device=dev)
+    o, S, A, zk = vla.vla_forward(e, e, e, e, 0.25, 1e-4, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(S.cpu(), torch.zeros(B, H, d, d))
+    assert torch.equal(A.cpu(), (torch.eye(d) * 4.0).expand(B, H, d, d))
+    assert torch.equal(zk.cpu(), torch.zeros(B, H, d))
+    S0 = torch.randn(B, H, d, d, device=dev)
+    A0 = torch.randn(B, H, d, d, device=dev)
+    z0 = torch.rand(B, H, d, device=dev)
+    o, S, A, zk = vla.vla_forward(e, e, e, e, 0.1, 1e-4, S0=S0, A0=A0, zkey0=z0, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S0) and torch.equal(A, A0) and torch.equal(zk, z0)
+
+
+def test_continuation_from_state_and_in_place():
+    dev = _dev()
+    vla = _vla()
+    cfg = gen.config(2).with_sizes(B=2, H=2, T=200)
+    x = gen.make_inputs(cfg)
+    T1 = 83
+    t = {n: torch.from_numpy(x[n]).to(dev) for n in "qkvu"}
+    first = {n: t[n][:, :, :T1].contiguous() for n in "qkvu"}
+    second = {n: t[n][:, :, T1:].contiguous() for n in "qkvu"}
+    o1, S, A, zk = vla.vla_forward(*(first[n] for n in "qkvu"), return_state=True)
+    # second part updates the state in place (outputs alias the initial state)
+    o2 = vla.vla_forward(*(second[n] for n in "qkvu"), S0=S, A0=A, zkey0=zk,
+                         S_out=S, A_out=A, zkey_out=zk)[0]
+    torch.cuda.synchronize()
+    ref = oracle.forward(*(x[n].astype(np.float64) for n in "qkvu"))
+    _check("o", np.concatenate([o1.cpu().numpy(), o2.cpu().numpy()], axis=2), ref["o"])
+    _check("S", S.cpu().numpy(), ref["S"])
+    _check("A", A.cpu().numpy(), ref["A"])
+    _check("zkey", zk.cpu().numpy(), ref["zkey"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_step_matches_oracle(dtype):
+    dev = _dev()
+    vla = _vla()
+    cfg = gen.config(5 if dtype == "bf16" else 2).with_sizes(B=2, H=2, T=64, decode=0)
+    x = gen.make_inputs(cfg)
+    B, H, d = cfg.B, cfg.H, cfg.d
+    S = torch.zeros(B, H, d, d, device=dev)
+    A = (torch.eye(d, device=dev) / cfg.lambda0).expand(B, H, d, d).contiguous()
+    zk = torch.zeros(B, H, d, device=dev)
+    t = {n: _to_dev(x[n], cfg, dev) for n in "qkvu"}
+    outs = []
+    for i in range(cfg.T):
+        outs.append(vla.vla_step(*(t[n][:, :, i].contiguous() for n in "qkvu"), S, A, zk, cfg.eps))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=2).cpu().numpy()
+    ref = oracle.forward(*(_f64(x[n], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+    _check("o", o, ref["o"])
+    _check("S", S.cpu().numpy(), ref["S"])
+    _check("A", A.cpu().numpy(), ref["A"])
+    _check("zkey", zk.cpu().numpy(), ref["zkey"])
+
+
+def test_degenerate_tokens():
+    """Zero keys, zero penalty directions and very negative queries (the eps
+    branch of the readout denominator)."""
+    dev = _dev()
+    cfg = gen.config(2).with_sizes(B=1, H=2, T=96)
+    x = gen.make_inputs(cfg)
+    x["k"][:, :, 5] = 0.0
+    x["u"][:, :, 9] = 0.0
+    x["u"][:, 1, 20:40] = 0.0
+    x["q"][:, :, 0:3] = -60.0
+    x["q"][:, :, 50] = -60.0
+    out = _gpu_forward(cfg, x, dev)
+    ref = oracle.forward(*(x[n].astype(np.float64) for n in "qkvu"), cfg.lambda0, cfg.eps)
+    for name, g in zip(("o", "S", "A", "zkey"), out):
+        _check(name, g, ref[name])
+
+
+def test_run_to_run_bitwise_deterministic():
+    dev = _dev()
+    cfg = gen.config(3).with_sizes(B=2, H=4, T=512)
+    x = gen.make_inputs(cfg)
+    a = _gpu_forward(cfg, x, dev)
+    b = _gpu_forward(cfg, x, dev)
+    for ga, gb in zip(a, b):
+        assert np.array_equal(ga, gb)
