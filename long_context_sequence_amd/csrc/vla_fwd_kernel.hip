@@ -5,35 +5,37 @@
 // Eqs. (9) (Sherman-Morrison downdate of A), (10) (gated delta write of S) and
 // (11) (ELU+1 readout with the running key sum); A_0 = I / lambda0 (section 3.2).
 //
-// Mapping.  One workgroup owns one (batch, head) for all T tokens, with
-// NW = d/16 wavefronts.  Wave w owns rows 16w .. 16w+15 of both A and S; lane
-// l = 16g + n (g = lane group = 16-lane DPP row, n = row within it) holds row
-// 16w + n and the columns of group g:
+// Mapping.  One workgroup owns one (batch, head) for all T tokens.  It has
+// 2*NH wavefronts, NH = d/16: "A-waves" 0..NH-1 carry the penalty chain (Eq. 9
+// and the gate of Eq. 10) and "S-waves" NH..2NH-1 carry the memory chain (the
+// write of Eq. 10 and the readout of Eq. 11), so every SIMD runs one wave of
+// each chain and overlaps the stalls of one with the arithmetic of the other.
+// Wave h of a chain owns rows 16h .. 16h+15 of its matrix; lane l = 16g + n
+// (g = lane group = 16-lane DPP row, n = row within it) holds row 16h + n and
+// the columns of group g:
 //     columns 16g + m            for m = 0..15
 //     columns 64 + SW1 g + m     for m = 0..SW1-1   (SW1 = (d-64)/4)
-// so each lane keeps CPL = 16 + SW1 entries of A and of S in VGPRs for the
-// whole sequence.  A "lane-distributed" vector keeps element 16g + n in lane
-// 16g + n (and element 64 + SW1 g + n in a second register), so the value of
-// column j for the whole 16-lane row is one DPP row_newbcast away: every
-// multiply-add of a matrix-vector product or rank-1 update is a single
-// v_fmac_f32 with a DPP-broadcast source operand.  Row results are summed over
-// the four lane groups with the gfx950 permlane32/permlane16 swaps.
+// i.e. CPL = 16 + SW1 matrix entries per lane, in VGPRs for the whole sequence.
+// A "lane-distributed" vector keeps element 16g + n in lane 16g + n (and
+// element 64 + SW1 g + n in a second register), so column j of the whole 16-lane
+// row is one DPP row_newbcast away: every multiply-add of the matrix-vector
+// products and rank-1 updates is a single v_fmac_f32 with a DPP-broadcast
+// source.  Row sums over the four lane groups use the gfx950 permlane32/16 swaps.
 //
-// Per token, the only cross-wave exchange is one LDS all-gather of z (the
-// Sherman-Morrison vector) and of y (= A k^), plus four dot-product partials,
-// behind a single s_barrier.  The penalty chain runs one token ahead of the
-// memory chain and the readout one token behind it:
-//     iteration t:  A-pass of token t   (apply z_{t-1}; z_t = A u^_t, w_t = A k^_t)
-//                   S-pass of token t-1 (apply e_{t-2} alpha^_{t-2}; S k^_{t-1},
-//                                        S phi(q_{t-1}); e_{t-1})
-//                   readout of token t-2
-// using A_t k^ = A_{t-1} k^ - z (z'k^)/delta (Eq. 9 applied to k^), so that
-// y_t = A_t k^_t needs only row-local data and two scalars.
+// Per token, the only cross-wave exchange is an LDS all-gather of z (the
+// Sherman-Morrison vector) and y (= A k^) plus four dot-product partials, behind
+// one s_barrier.  The penalty chain runs one token ahead of the memory chain and
+// the readout one token behind it:
+//     iteration t:  A-waves: apply z_{t-1}; z_t = A u^_t, w_t = A k^_t;
+//                            y_{t-1} = w_{t-1} - z_{t-1} (z_{t-1}'k^_{t-1})/delta
+//                            (Eq. 9 applied to k^, i.e. A_{t-1} k^ from A_{t-2} k^)
+//                   S-waves: apply e_{t-2} alpha^_{t-2}; S k^_{t-1}, S phi(q_{t-1});
+//                            e_{t-1}; readout o_{t-2}
 //
 // State-independent work (k^, u^, phi(q), the key-sum prefix and the readout
 // denominator) is done per tile of TT tokens in a prologue and kept in an LDS
-// ring of TT+8 token slots; the raw inputs of the next tile are prefetched into
-// registers while the current tile runs.
+// ring of RING token records; the raw inputs of the next tile are prefetched
+// into registers while the current tile runs.
 #include <utility>
 
 #include "vla_common.h"
@@ -54,8 +56,8 @@ __device__ __forceinline__ void sfor(F &&f)
 
 // acc += x[lane M of this 16-lane row] * y.
 // The broadcast source x must not be written by a VALU instruction right before
-// this (DPP read-after-VALU-write hazard): every x used here comes straight from
-// an LDS load.
+// this (DPP read-after-VALU-write hazard, invisible to the compiler inside asm):
+// every x used here comes straight from an LDS load.
 template <int M>
 __device__ __forceinline__ void fmac_bc(float &acc, float x, float y)
 {
@@ -64,14 +66,26 @@ __device__ __forceinline__ void fmac_bc(float &acc, float x, float y)
         : "v"(x), "v"(y), "n"(M));
 }
 
-// Sum over lanes l, l^16, l^32, l^48 (the four lane groups); every lane gets the
-// same bits.
-__device__ __forceinline__ float sum_groups(float x)
+// acc = x[lane M of this 16-lane row] * y (same hazard rule as fmac_bc).
+template <int M>
+__device__ __forceinline__ void fmul_bc(float &acc, float x, float y)
 {
-    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "=v"(acc)
+        : "v"(x), "v"(y), "n"(M));
+}
+
+// x, y <- their sums over lanes l, l^16, l^32, l^48 (the four lane groups), in
+// every lane, bit-identical across lanes.
+__device__ __forceinline__ void sum2_groups(float &x, float &y)
+{
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    const float X = __uint_as_float(p[0]) + __uint_as_float(p[1]);   // rows: x02 x13 y02 y13
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(X), __float_as_uint(X), false, false);
+    const float Q = __uint_as_float(r[0]) + __uint_as_float(r[1]);   // rows: x x y y
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(Q), __float_as_uint(Q), false, false);
+    x = __uint_as_float(b[0]);
+    y = __uint_as_float(b[1]);
 }
 
 template <int CTRL>
@@ -90,58 +104,47 @@ __device__ __forceinline__ float sum_row16(float x)
     return x;
 }
 
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
 template <int D>
 struct FastCfg {
-    static constexpr int NW = D / 16;            // wavefronts per workgroup
-    static constexpr int NT = 64 * NW;
+    static constexpr int NH = D / 16;            // wavefronts per chain
+    static constexpr int NHP = (NH + 3) / 4 * 4; // partials row padded to 16 bytes
+    static constexpr int NT = 128 * NH;          // A-waves + S-waves
     static constexpr int SW1 = (D - 64) / 4;     // second column segment per lane group
     static constexpr int CPL = 16 + SW1;         // matrix columns per lane
-    static constexpr int TT = D > 96 ? 32 : 64;  // tokens per prologue tile
-    static constexpr int RING = TT + 8;          // LDS token slots (>= TT + 2)
-    static constexpr int RS = D + 4;             // padded LDS row stride (floats)
-    static constexpr int CPT = D * TT / NT;      // prologue columns per thread
+    static constexpr int TT = 32;                // tokens per prologue tile
+    static constexpr int RING = 64;              // token records in LDS (power of 2, >= TT + 2)
+                                                 // plus one alias record in front (see below)
+    static constexpr int RS = 4 * D + 4;         // record stride in floats: k^, u^, phi(q), v
+    static constexpr int KH = 0, UH = D, PQ = 2 * D, VV = 3 * D;   // record fields
+    static constexpr int ZS = D + 4;             // stride of the key-sum scratch rows
+    static constexpr int CPT = D * TT / NT;      // prologue columns per thread (4)
     static constexpr int NCH = D / CPT;          // prologue column chunks per token
 };
 
-// 16 (fp32) or 8/16 (bf16) consecutive inputs of one token, held in registers.
+// CPT consecutive inputs of one token, held in registers.
 template <typename Tin, int N> struct RawVec;
-template <int N> struct RawVec<float, N> {
-    float4 x[N / 4];
+template <> struct RawVec<float, 4> {
+    float4 x;
     __device__ __forceinline__ void load(const float *p, bool ok)
     {
-#pragma unroll
-        for (int i = 0; i < N / 4; ++i)
-            x[i] = ok ? reinterpret_cast<const float4 *>(p)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        x = ok ? *reinterpret_cast<const float4 *>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __device__ __forceinline__ float get(int i) const
     {
-        const float4 &v = x[i >> 2];
-        switch (i & 3) {
-        case 0: return v.x;
-        case 1: return v.y;
-        case 2: return v.z;
-        default: return v.w;
-        }
+        return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
     }
 };
-template <int N> struct RawVec<uint16_t, N> {
-    uint4 x[N / 8];
+template <> struct RawVec<uint16_t, 4> {
+    uint2 x;
     __device__ __forceinline__ void load(const uint16_t *p, bool ok)
     {
-#pragma unroll
-        for (int i = 0; i < N / 8; ++i)
-            x[i] = ok ? reinterpret_cast<const uint4 *>(p)[i] : make_uint4(0u, 0u, 0u, 0u);
+        x = ok ? *reinterpret_cast<const uint2 *>(p) : make_uint2(0u, 0u);
     }
     __device__ __forceinline__ float get(int i) const
     {
-        const uint4 &v = x[i >> 3];
-        uint32_t wd;
-        switch ((i >> 1) & 3) {
-        case 0: wd = v.x; break;
-        case 1: wd = v.y; break;
-        case 2: wd = v.z; break;
-        default: wd = v.w; break;
-        }
+        const uint32_t wd = (i >> 1) ? x.y : x.x;
         return (i & 1) ? bf16_hi(wd) : bf16_lo(wd);
     }
 };
@@ -155,53 +158,44 @@ vla_fwd_fast(const Tin *__restrict__ q, const Tin *__restrict__ k,
              const float *S0, const float *A0, const float *zk0)
 {
     using C = FastCfg<D>;
-    constexpr int NW = C::NW, NT = C::NT, SW1 = C::SW1, CPL = C::CPL, TT = C::TT;
-    constexpr int RING = C::RING, RS = C::RS, CPT = C::CPT, NCH = C::NCH;
+    constexpr int NH = C::NH, NHP = C::NHP, NT = C::NT, SW1 = C::SW1, CPL = C::CPL, TT = C::TT;
+    constexpr int RING = C::RING, RS = C::RS, ZS = C::ZS, CPT = C::CPT, NCH = C::NCH;
+    constexpr int KH = C::KH, UH = C::UH, PQ = C::PQ, VV = C::VV;
 
-    __shared__ __align__(16) float s_kh[RING * RS];   // k^ per token slot
-    __shared__ __align__(16) float s_uh[RING * RS];   // u^
-    __shared__ __align__(16) float s_pq[RING * RS];   // phi(q)
-    __shared__ __align__(16) float s_v[RING * RS];    // v
-    __shared__ __align__(16) float s_zk[TT * RS];     // phi(k), then the key sum, of a tile
-    __shared__ float s_rden[RING];                    // 1 / max(phi(q)' zkey, eps)
-    __shared__ float s_part[2][NCH][TT];              // prologue partial sums
-    __shared__ float s_z[2][D];                       // all-gather of z_t
-    __shared__ float s_y[2][D];                       // all-gather of y_{t-1}
-    __shared__ float s_red[2][4][NW];                 // per-wave dot-product partials
+    // token records: slot s at s_rec[(s + 1) * RS]; s_rec[0 .. RS) repeats the
+    // phi(q) field of slot RING-1, so the phi(q) of token t-1 is always one record
+    // before the record of token t
+    __shared__ __align__(16) float s_rec[(RING + 1) * RS];
+    __shared__ __align__(16) float s_zk[TT * ZS];       // phi(k), then the key sum, of a tile
+    __shared__ float s_rden[RING];                      // 1 / max(phi(q)' zkey, eps)
+    __shared__ float s_part[2][NCH][TT];                // prologue partial sums
+    __shared__ __align__(16) float s_z[2][D];           // all-gather of z_t
+    __shared__ __align__(16) float s_y[2][D];           // all-gather of y_{t-1}
+    __shared__ __align__(16) float s_red[2][4][NHP];    // per-wave dot-product partials
+    __shared__ float s_sink[64];                        // target of masked-off exchange writes
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, g = l >> 4, n = l & 15;
-    const int row = 16 * w + n;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+    const int l = tid & 63, g = l >> 4, n = l & 15;
+    const bool awave = w < NH;
+    const int wh = awave ? w : w - NH;
+    const int row = 16 * wh + n;
     const size_t bh = blockIdx.x;
     const size_t DD = (size_t)D * D;
-    // lane-distributed second-segment element of this lane (lanes n >= SW1 read a
-    // valid dummy; their values are never broadcast)
+    // second-segment lane-distributed element (lanes n >= SW1 read a valid dummy
+    // element; their values are never broadcast)
     const int l1 = 64 + SW1 * g + (n < SW1 ? n : (SW1 > 0 ? SW1 - 1 : 0));
 
-    // ---------------------------------------------------------------- state
-    float a[CPL], s[CPL];
-    sfor<CPL>([&](auto mm) {
-        constexpr int m = decltype(mm)::value;
-        const int j = m < 16 ? 16 * g + m : 64 + SW1 * g + (m - 16);
-        const size_t idx = bh * DD + (size_t)row * D + j;
-        a[m] = A0 ? A0[idx] : (row == j ? 1.f / lambda0 : 0.f);
-        s[m] = S0 ? S0[idx] : 0.f;
-    });
     float zk_run = 0.f, zk_cmp = 0.f;          // key-sum column tid (tid < D), Kahan
     if (tid < D && zk0) zk_run = zk0[bh * D + tid];
 
-    for (int i = tid; i < RING * RS; i += NT) {
-        s_kh[i] = 0.f;
-        s_uh[i] = 0.f;
-        s_pq[i] = 0.f;
-        s_v[i] = 0.f;
-    }
+    for (int i = tid; i < (RING + 1) * RS; i += NT) s_rec[i] = 0.f;
     for (int i = tid; i < RING; i += NT) s_rden[i] = 0.f;
     for (int i = tid; i < 2 * D; i += NT) {
         (&s_z[0][0])[i] = 0.f;
         (&s_y[0][0])[i] = 0.f;
     }
-    for (int i = tid; i < 2 * 4 * NW; i += NT) (&s_red[0][0][0])[i] = 0.f;
+    for (int i = tid; i < 2 * 4 * NHP; i += NT) (&s_red[0][0][0])[i] = 0.f;
 
     // prologue thread mapping: token tl of the tile, columns [ch*CPT, ch*CPT+CPT)
     const int tl = tid % TT, ch = tid / TT;
@@ -216,168 +210,234 @@ vla_fwd_fast(const Tin *__restrict__ q, const Tin *__restrict__ k,
         rv.load(v + off, ok);
         ru.load(u + off, ok);
     };
-    prefetch(0);
-    __syncthreads();
 
-    // carried row values (lane's row 16w+n; identical in the four lane groups)
-    float zr = 0.f, wr = 0.f;   // z_{t-1}, w_{t-1} = A_{t-2} k^_{t-1}
-    float ep = 0.f, pp = 0.f;   // e_{t-2}, (S_{t-3} phi(q_{t-2}))
+    // State-independent work of the tile starting at token t0 (all threads; four
+    // barriers).  Leaves k^, u^, phi(q), v of each token in its record and
+    // 1/max(phi(q)'zkey, eps) in s_rden, and advances the key sums.
+    auto prologue = [&](int t0) {
+        const int t = t0 + tl;
+        const bool ok = t < T;
+        const int slot = t & (RING - 1);
+        const int rec = (slot + 1) * RS;
+        float pk = 0.f, pu = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            pk = fmaf(rk.get(i), rk.get(i), pk);
+            pu = fmaf(ru.get(i), ru.get(i), pu);
+        }
+        s_part[0][ch][tl] = pk;
+        s_part[1][ch][tl] = pu;
+        __syncthreads();
+        float nk = 0.f, nu = 0.f;
+#pragma unroll 8
+        for (int c2 = 0; c2 < NCH; ++c2) {
+            nk += s_part[0][c2][tl];
+            nu += s_part[1][c2][tl];
+        }
+        const float ik = nk > 0.f ? 1.f / sqrtf(nk) : 0.f;
+        const float iu = nu > 0.f ? 1.f / sqrtf(nu) : 0.f;
+        const int cb = ch * CPT;
+        float4 kh4, uh4, pq4, v4, pk4;
+        kh4.x = rk.get(0) * ik; kh4.y = rk.get(1) * ik; kh4.z = rk.get(2) * ik; kh4.w = rk.get(3) * ik;
+        uh4.x = ru.get(0) * iu; uh4.y = ru.get(1) * iu; uh4.z = ru.get(2) * iu; uh4.w = ru.get(3) * iu;
+        pq4.x = phi(rq.get(0)); pq4.y = phi(rq.get(1)); pq4.z = phi(rq.get(2)); pq4.w = phi(rq.get(3));
+        v4.x = rv.get(0); v4.y = rv.get(1); v4.z = rv.get(2); v4.w = rv.get(3);
+        pk4.x = ok ? phi(rk.get(0)) : 0.f; pk4.y = ok ? phi(rk.get(1)) : 0.f;
+        pk4.z = ok ? phi(rk.get(2)) : 0.f; pk4.w = ok ? phi(rk.get(3)) : 0.f;
+        *reinterpret_cast<float4 *>(&s_rec[rec + KH + cb]) = kh4;
+        *reinterpret_cast<float4 *>(&s_rec[rec + UH + cb]) = uh4;
+        *reinterpret_cast<float4 *>(&s_rec[rec + PQ + cb]) = pq4;
+        *reinterpret_cast<float4 *>(&s_rec[rec + VV + cb]) = v4;
+        if (slot == RING - 1) *reinterpret_cast<float4 *>(&s_rec[PQ + cb]) = pq4;   // alias record
+        *reinterpret_cast<float4 *>(&s_zk[tl * ZS + cb]) = pk4;
+        __syncthreads();
+        if (tid < D) {   // inclusive running key sum down the tile, per column
+#pragma unroll 8
+            for (int tt = 0; tt < TT; ++tt) {
+                const float x = s_zk[tt * ZS + tid];
+                const float yk = x - zk_cmp;
+                const float ts = zk_run + yk;
+                zk_cmp = (ts - zk_run) - yk;
+                zk_run = ts;
+                s_zk[tt * ZS + tid] = zk_run;
+            }
+        }
+        __syncthreads();
+        const float4 zz = *reinterpret_cast<const float4 *>(&s_zk[tl * ZS + cb]);
+        float pd = pq4.x * zz.x;
+        pd = fmaf(pq4.y, zz.y, pd);
+        pd = fmaf(pq4.z, zz.z, pd);
+        pd = fmaf(pq4.w, zz.w, pd);
+        s_part[0][ch][tl] = pd;
+        __syncthreads();
+        if (ch == 0) {
+            float dsum = 0.f;
+#pragma unroll 8
+            for (int c2 = 0; c2 < NCH; ++c2) dsum += s_part[0][c2][tl];
+            s_rden[slot] = 1.f / fmaxf(dsum, eps);
+        }
+        // s_rden of a token is first read two iterations later, after two barriers.
+    };
 
-    const int ntiles = (T + 2 + TT - 1) / TT;
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int t0 = tile * TT;
-        // ------------------------------------------- tile prologue (no state)
-        {
-            const int t = t0 + tl;
-            const bool ok = t < T;
-            const int slot = t % RING;
-            float pk = 0.f, pu = 0.f;
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                pk = fmaf(rk.get(i), rk.get(i), pk);
-                pu = fmaf(ru.get(i), ru.get(i), pu);
+    // Runs every tile: prologue, prefetch of the next tile, then the token
+    // iterations (one barrier each), unrolled by two so that buffer parities are
+    // compile-time constants.
+    auto run = [&](auto &&step) {
+        prefetch(0);
+        __syncthreads();
+        const int ntiles = (T + 2 + TT - 1) / TT;
+        for (int tile = 0; tile < ntiles; ++tile) {
+            const int t0 = tile * TT;
+            prologue(t0);
+            if (tile + 1 < ntiles) prefetch(t0 + TT);
+            const int tend = min(t0 + TT, T + 2);
+            int t = t0;                                    // t0 is even
+            for (; t + 1 < tend; t += 2) {
+                step(t, std::integral_constant<int, 0>{});
+                __syncthreads();
+                step(t + 1, std::integral_constant<int, 1>{});
+                __syncthreads();
             }
-            s_part[0][ch][tl] = pk;
-            s_part[1][ch][tl] = pu;
-            __syncthreads();
-            float nk = 0.f, nu = 0.f;
-#pragma unroll
-            for (int c2 = 0; c2 < NCH; ++c2) {
-                nk += s_part[0][c2][tl];
-                nu += s_part[1][c2][tl];
+            if (t < tend) {
+                step(t, std::integral_constant<int, 0>{});
+                __syncthreads();
             }
-            const float ik = nk > 0.f ? 1.f / sqrtf(nk) : 0.f;
-            const float iu = nu > 0.f ? 1.f / sqrtf(nu) : 0.f;
-            const int base = slot * RS + ch * CPT;
+        }
+    };
+
+    float m_[CPL];   // A-waves: rows of A; S-waves: rows of S
+    if (awave) {
+        // ================================================ penalty chain (A)
+        sfor<CPL>([&](auto mm) {
+            constexpr int m = decltype(mm)::value;
+            const int j = m < 16 ? 16 * g + m : 64 + SW1 * g + (m - 16);
+            m_[m] = A0 ? A0[bh * DD + (size_t)row * D + j] : (row == j ? 1.f / lambda0 : 0.f);
+        });
+        // exchange partials: group 0 u^_t.z_t, 1 k^_t.z_t, 2 |y_{t-1}|^2,
+        // 3 y_{t-1}.phi(q_{t-1}) (the record before token t's); element offset of
+        // the record entry each group multiplies in, relative to token t's record
+        const int o_part = (g == 0 ? UH + row : g == 1 ? KH + row : PQ + row - RS);
+        // group 0 lanes write z, group 2 lanes y, lane n == 0 of each group its
+        // partial; every other lane writes to the sink
+        float *const p_zy = g == 0 ? &s_z[0][row] : g == 2 ? &s_y[0][row] : &s_sink[l];
+        const int zy_par = (g == 0 || g == 2) ? D : 0;
+        float *const p_red = n == 0 ? &s_red[0][g][wh] : &s_sink[l];
+        const int red_par = n == 0 ? 4 * NHP : 0;
+        float zr = 0.f, wr = 0.f;   // z_{t-1}, w_{t-1} = A_{t-2} k^_{t-1}
+
+        run([&](int t, auto parity) {
+            constexpr int P = decltype(parity)::value;  // t & 1
+            constexpr int PB = P ^ 1;                   // buffers written in iteration t-1
+            const int st = ((t & (RING - 1)) + 1) * RS; // record of token t
+            const float zc0 = s_z[PB][l], zc1 = SW1 ? s_z[PB][l1] : 0.f;   // z_{t-1}
+            const float4 ru4 = *reinterpret_cast<const float4 *>(&s_red[PB][0][0]);
+            const float4 rk4 = *reinterpret_cast<const float4 *>(&s_red[PB][1][0]);
+            float ud = (ru4.x + ru4.y) + (ru4.z + ru4.w);
+            float kd = (rk4.x + rk4.y) + (rk4.z + rk4.w);
+            if constexpr (NH > 4) {
 #pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                s_kh[base + i] = rk.get(i) * ik;
-                s_uh[base + i] = ru.get(i) * iu;
-                s_pq[base + i] = phi(rq.get(i));
-                s_v[base + i] = rv.get(i);
-                s_zk[tl * RS + ch * CPT + i] = ok ? phi(rk.get(i)) : 0.f;
-            }
-            __syncthreads();
-            if (tid < D) {   // inclusive running key sum down the tile, per column
-                for (int tt = 0; tt < TT; ++tt) {
-                    const float x = s_zk[tt * RS + tid];
-                    const float yk = x - zk_cmp;
-                    const float ts = zk_run + yk;
-                    zk_cmp = (ts - zk_run) - yk;
-                    zk_run = ts;
-                    s_zk[tt * RS + tid] = zk_run;
+                for (int ww = 4; ww < NH; ++ww) {
+                    ud += s_red[PB][0][ww];
+                    kd += s_red[PB][1][ww];
                 }
             }
-            __syncthreads();
-            float pd = 0.f;
-#pragma unroll
-            for (int i = 0; i < CPT; ++i)
-                pd = fmaf(s_pq[base + i], s_zk[tl * RS + ch * CPT + i], pd);
-            s_part[0][ch][tl] = pd;
-            __syncthreads();
-            if (ch == 0) {
-                float dsum = 0.f;
-#pragma unroll
-                for (int c2 = 0; c2 < NCH; ++c2) dsum += s_part[0][c2][tl];
-                s_rden[slot] = 1.f / fmaxf(dsum, eps);
-            }
-            // s_rden[slot] is first read two iterations later, after two barriers.
-        }
-        if (tile + 1 < ntiles) prefetch(t0 + TT);
-
-        const int tend = min(t0 + TT, T + 2);
-        for (int t = t0; t < tend; ++t) {
-            const int pb = (t + 1) & 1, cb = t & 1;
-            const int st = t % RING;                  // slot of token t
-            const int sp = (t + RING - 1) % RING;     // slot of token t-1
-
-            // ---- P1: results of the exchange for token t-1
-            const float zc0 = s_z[pb][l], zc1 = SW1 ? s_z[pb][l1] : 0.f;   // z_{t-1}
-            const float yc0 = s_y[pb][l], yc1 = SW1 ? s_y[pb][l1] : 0.f;   // y_{t-2}
-            float ud = 0.f, kd = 0.f, yy = 0.f, yq = 0.f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                ud += s_red[pb][0][ww];    // u^_{t-1}' z_{t-1}
-                kd += s_red[pb][1][ww];    // k^_{t-1}' z_{t-1}
-                yy += s_red[pb][2][ww];    // |y_{t-2}|^2
-                yq += s_red[pb][3][ww];    // y_{t-2}' phi(q_{t-2})
-            }
-            const float invd = 1.f / (1.f + ud);              // 1 / delta_{t-1}
+            const float invd = fast_rcp(1.f + ud);             // 1 / delta_{t-1}
             const float nc = -(zr * invd);                     // -z_i / delta
             const float yr = wr - zr * (kd * invd);           // y_{t-1} = A_{t-1} k^_{t-1}
+            const float u0 = s_rec[st + UH + l], u1 = SW1 ? s_rec[st + UH + l1] : 0.f;
+            const float k0 = s_rec[st + KH + l], k1 = SW1 ? s_rec[st + KH + l1] : 0.f;
+            const float mem = s_rec[st + o_part];
+            float za, wa;
+            sfor<CPL>([&](auto mm) {
+                constexpr int m = decltype(mm)::value;
+                if constexpr (m == 0) {
+                    fmac_bc<0>(m_[0], zc0, nc);
+                    fmul_bc<0>(za, u0, m_[0]);
+                    fmul_bc<0>(wa, k0, m_[0]);
+                } else if constexpr (m < 16) {
+                    fmac_bc<m>(m_[m], zc0, nc);
+                    fmac_bc<m>(za, u0, m_[m]);
+                    fmac_bc<m>(wa, k0, m_[m]);
+                } else {
+                    fmac_bc<m - 16>(m_[m], zc1, nc);
+                    fmac_bc<m - 16>(za, u1, m_[m]);
+                    fmac_bc<m - 16>(wa, k1, m_[m]);
+                }
+            });
+            sum2_groups(za, wa);                               // z_t, w_t (rows)
+            const float lhs = g < 2 ? za : yr;
+            const float rhs = g == 2 ? yr : mem;
+            p_red[P * red_par] = sum_row16(lhs * rhs);
+            p_zy[P * zy_par] = g == 0 ? za : yr;
+            zr = za;
+            wr = wa;
+        });
+    } else {
+        // ================================================ memory chain (S)
+        sfor<CPL>([&](auto mm) {
+            constexpr int m = decltype(mm)::value;
+            const int j = m < 16 ? 16 * g + m : 64 + SW1 * g + (m - 16);
+            m_[m] = S0 ? S0[bh * DD + (size_t)row * D + j] : 0.f;
+        });
+        float ep = 0.f, pp = 0.f;   // e_{t-2}, S_{t-3} phi(q_{t-2})
+        float *const o_row = o + tok_base * D + row;
+
+        run([&](int t, auto parity) {
+            constexpr int P = decltype(parity)::value;
+            constexpr int PB = P ^ 1;
+            const int sp = (((t - 1) & (RING - 1)) + 1) * RS;   // record of token t-1
+            const float yc0 = s_y[PB][l], yc1 = SW1 ? s_y[PB][l1] : 0.f;   // y_{t-2}
+            const float4 ry4 = *reinterpret_cast<const float4 *>(&s_red[PB][2][0]);
+            const float4 rq4 = *reinterpret_cast<const float4 *>(&s_red[PB][3][0]);
+            float yy = (ry4.x + ry4.y) + (ry4.z + ry4.w);
+            float yq = (rq4.x + rq4.y) + (rq4.z + rq4.w);
+            if constexpr (NH > 4) {
+#pragma unroll
+                for (int ww = 4; ww < NH; ++ww) {
+                    yy += s_red[PB][2][ww];
+                    yq += s_red[PB][3][ww];
+                }
+            }
             const float ny = yy > 0.f ? rsqrtf(yy) : 0.f;     // 1 / |y_{t-2}|
-            if (t >= 2 && t - 2 < T && g == 0) {               // readout of token t-2
-                const float aq = yq * ny;                      // alpha^' phi(q)
-                o[(tok_base + (size_t)(t - 2)) * D + row] = (pp + ep * aq) * s_rden[(t - 2) % RING];
-            }
-
-            // ---- P2: A-pass of token t
-            const float u0 = s_uh[st * RS + l], u1 = SW1 ? s_uh[st * RS + l1] : 0.f;
-            const float k0 = s_kh[st * RS + l], k1 = SW1 ? s_kh[st * RS + l1] : 0.f;
-            float za = 0.f, wa = 0.f;
-            sfor<CPL>([&](auto mm) {
-                constexpr int m = decltype(mm)::value;
-                if constexpr (m < 16) {
-                    fmac_bc<m>(a[m], zc0, nc);
-                    fmac_bc<m>(za, u0, a[m]);
-                    fmac_bc<m>(wa, k0, a[m]);
-                } else {
-                    fmac_bc<m - 16>(a[m], zc1, nc);
-                    fmac_bc<m - 16>(za, u1, a[m]);
-                    fmac_bc<m - 16>(wa, k1, a[m]);
-                }
-            });
-            const float zn = sum_groups(za), wn = sum_groups(wa);
-
-            // ---- P3: S-pass of token t-1
-            const float kp0 = s_kh[sp * RS + l], kp1 = SW1 ? s_kh[sp * RS + l1] : 0.f;
-            const float q0 = s_pq[sp * RS + l], q1 = SW1 ? s_pq[sp * RS + l1] : 0.f;
-            const float vrow = s_v[sp * RS + row];
+            if (t >= 2 && t - 2 < T)                           // o_{t-2} = S_{t-2} phi(q) / den
+                o_row[(size_t)(t - 2) * D] =
+                    (pp + ep * (yq * ny)) * s_rden[(t - 2) & (RING - 1)];   // 4 lanes per row
+            const float kp0 = s_rec[sp + KH + l], kp1 = SW1 ? s_rec[sp + KH + l1] : 0.f;
+            const float q0 = s_rec[sp + PQ + l], q1 = SW1 ? s_rec[sp + PQ + l1] : 0.f;
+            const float vrow = s_rec[sp + VV + row];
             const float se = ep * ny;          // alpha^_{t-2,j} e_{t-2,i} = y_j * (e_i / |y|)
-            float ra = 0.f, pa = 0.f;
+            float ra, pa;
             sfor<CPL>([&](auto mm) {
                 constexpr int m = decltype(mm)::value;
-                if constexpr (m < 16) {
-                    fmac_bc<m>(s[m], yc0, se);
-                    fmac_bc<m>(ra, kp0, s[m]);
-                    fmac_bc<m>(pa, q0, s[m]);
+                if constexpr (m == 0) {
+                    fmac_bc<0>(m_[0], yc0, se);
+                    fmul_bc<0>(ra, kp0, m_[0]);
+                    fmul_bc<0>(pa, q0, m_[0]);
+                } else if constexpr (m < 16) {
+                    fmac_bc<m>(m_[m], yc0, se);
+                    fmac_bc<m>(ra, kp0, m_[m]);
+                    fmac_bc<m>(pa, q0, m_[m]);
                 } else {
-                    fmac_bc<m - 16>(s[m], yc1, se);
-                    fmac_bc<m - 16>(ra, kp1, s[m]);
-                    fmac_bc<m - 16>(pa, q1, s[m]);
+                    fmac_bc<m - 16>(m_[m], yc1, se);
+                    fmac_bc<m - 16>(ra, kp1, m_[m]);
+                    fmac_bc<m - 16>(pa, q1, m_[m]);
                 }
             });
-            const float rn = sum_groups(ra), pn = sum_groups(pa);
-
-            // ---- P4: exchange (one s_barrier)
-            // group 0: u^_t'z_t, group 1: k^_t'z_t, group 2: |y_{t-1}|^2,
-            // group 3: y_{t-1}'phi(q_{t-1}), each summed over this wave's 16 rows
-            const float rhs_mem = g == 0 ? s_uh[st * RS + row]
-                                : g == 1 ? s_kh[st * RS + row] : s_pq[sp * RS + row];
-            const float lhs = g < 2 ? zn : yr;
-            const float rhs = g == 2 ? yr : rhs_mem;
-            const float part = sum_row16(lhs * rhs);
-            if (n == 0) s_red[cb][g][w] = part;
-            if (g == 0) {
-                s_z[cb][row] = zn;
-                s_y[cb][row] = yr;
-            }
-            zr = zn;
-            wr = wn;
-            ep = vrow - rn;    // e_{t-1} = v - S_{t-2} k^  (S before token t-1's write)
-            pp = pn;
-            __syncthreads();
-        }
+            sum2_groups(ra, pa);
+            ep = vrow - ra;    // e_{t-1} = v - S k^ with S before token t-1's write
+            pp = pa;
+        });
     }
 
     // ---------------------------------------------------------------- epilogue
-    sfor<CPL>([&](auto mm) {
-        constexpr int m = decltype(mm)::value;
-        const int j = m < 16 ? 16 * g + m : 64 + SW1 * g + (m - 16);
-        const size_t idx = bh * DD + (size_t)row * D + j;
-        if (A_out) A_out[idx] = a[m];
-        if (S_out) S_out[idx] = s[m];
-    });
+    float *const out = awave ? A_out : S_out;
+    if (out) {
+        sfor<CPL>([&](auto mm) {
+            constexpr int m = decltype(mm)::value;
+            const int j = m < 16 ? 16 * g + m : 64 + SW1 * g + (m - 16);
+            out[bh * DD + (size_t)row * D + j] = m_[m];
+        });
+    }
     if (zk_out && tid < D) zk_out[bh * D + tid] = zk_run;
 }
 
