@@ -75,23 +75,98 @@ __device__ __forceinline__ void fmul_bc(float &acc, float x, float y)
         : "v"(x), "v"(y), "n"(M));
 }
 
+// One pass over a lane's CPL matrix entries:
+//     mv[m] += x[col m] * mult                  (rank-1 update of the row)
+//     acc1   = sum_m y1[col m] * mv[m]          (two matrix-vector products with
+//     acc2   = sum_m y2[col m] * mv[m]           the updated row)
+// where x, y1, y2 are lane-distributed vectors (registers ..0: columns 16g + m,
+// registers ..1: columns 64 + SW1 g + m).  Each asm block covers 8 columns in the
+// order update(i+1), acc1(i), acc2(i): an entry is read three instructions after
+// its update and an accumulator three instructions after its previous write.
+// Inside a block the DPP sources (x, y1, y2) are never written, so no wait states
+// are needed; every DPP source comes straight from an LDS load.
+#define VLA_MAC(D, S, M, L) "v_fmac_f32_dpp " D ", " S ", " M " row_newbcast:" #L " row_mask:0xf bank_mask:0xf\n\t"
+#define VLA_MUL(D, S, M, L) "v_mul_f32_dpp " D ", " S ", " M " row_newbcast:" #L " row_mask:0xf bank_mask:0xf\n\t"
+// operands: %0..%7 entries, %8 acc1, %9 acc2, %10 x, %11 mult, %12 y1, %13 y2
+#define VLA_CHUNK(A0, L0, L1, L2, L3, L4, L5, L6, L7)                                   \
+    VLA_MAC("%0", "%10", "%11", L0) VLA_MAC("%1", "%10", "%11", L1)                     \
+    A0("%8", "%12", "%0", L0) A0("%9", "%13", "%0", L0)                                  \
+    VLA_MAC("%2", "%10", "%11", L2) VLA_MAC("%8", "%12", "%1", L1) VLA_MAC("%9", "%13", "%1", L1) \
+    VLA_MAC("%3", "%10", "%11", L3) VLA_MAC("%8", "%12", "%2", L2) VLA_MAC("%9", "%13", "%2", L2) \
+    VLA_MAC("%4", "%10", "%11", L4) VLA_MAC("%8", "%12", "%3", L3) VLA_MAC("%9", "%13", "%3", L3) \
+    VLA_MAC("%5", "%10", "%11", L5) VLA_MAC("%8", "%12", "%4", L4) VLA_MAC("%9", "%13", "%4", L4) \
+    VLA_MAC("%6", "%10", "%11", L6) VLA_MAC("%8", "%12", "%5", L5) VLA_MAC("%9", "%13", "%5", L5) \
+    VLA_MAC("%7", "%10", "%11", L7) VLA_MAC("%8", "%12", "%6", L6) VLA_MAC("%9", "%13", "%6", L6) \
+    VLA_MAC("%8", "%12", "%7", L7) VLA_MAC("%9", "%13", "%7", L7)
+
+// FIRST: the accumulators start here (multiply instead of multiply-add).
+// HI: columns use DPP lanes 8..15 of the row instead of 0..7.
+template <bool FIRST, bool HI>
+__device__ __forceinline__ void pass_chunk(float *e, float &acc1, float &acc2, float x,
+                                           float mult, float y1, float y2)
+{
+    if constexpr (FIRST && !HI) {
+        asm volatile(VLA_CHUNK(VLA_MUL, 0, 1, 2, 3, 4, 5, 6, 7)
+                     : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]), "+v"(e[4]), "+v"(e[5]),
+                       "+v"(e[6]), "+v"(e[7]), "=&v"(acc1), "=&v"(acc2)
+                     : "v"(x), "v"(mult), "v"(y1), "v"(y2));
+    } else if constexpr (!HI) {
+        asm volatile(VLA_CHUNK(VLA_MAC, 0, 1, 2, 3, 4, 5, 6, 7)
+                     : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]), "+v"(e[4]), "+v"(e[5]),
+                       "+v"(e[6]), "+v"(e[7]), "+v"(acc1), "+v"(acc2)
+                     : "v"(x), "v"(mult), "v"(y1), "v"(y2));
+    } else {
+        static_assert(!FIRST, "a pass starts at columns 0..7");
+        asm volatile(VLA_CHUNK(VLA_MAC, 8, 9, 10, 11, 12, 13, 14, 15)
+                     : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]), "+v"(e[4]), "+v"(e[5]),
+                       "+v"(e[6]), "+v"(e[7]), "+v"(acc1), "+v"(acc2)
+                     : "v"(x), "v"(mult), "v"(y1), "v"(y2));
+    }
+}
+
+template <int CPL, int SW1>
+__device__ __forceinline__ void row_pass(float (&mv)[CPL], float x0, float x1, float mult,
+                                         float y10, float y11, float y20, float y21,
+                                         float &acc1, float &acc2)
+{
+    pass_chunk<true, false>(&mv[0], acc1, acc2, x0, mult, y10, y20);
+    pass_chunk<false, true>(&mv[8], acc1, acc2, x0, mult, y10, y20);
+    if constexpr (SW1 >= 8) pass_chunk<false, false>(&mv[16], acc1, acc2, x1, mult, y11, y21);
+    if constexpr (SW1 == 16) pass_chunk<false, true>(&mv[24], acc1, acc2, x1, mult, y11, y21);
+}
+
+// v_permlane32_swap / v_permlane16_swap with the two wait states a VALU write
+// of either operand needs before the swap reads it.  Issued from asm so that the
+// compiler does not pad them with the long wait it assumes after the DPP
+// multiply-add asm blocks.  After permlane32: a = [a_lo, b_lo], b = [a_hi, b_hi]
+// (32-lane halves); after permlane16: a = [a0, b0, a2, b2], b = [a1, b1, a3, b3]
+// (16-lane rows).
+__device__ __forceinline__ void pl32_swap(float &a, float &b)
+{
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void pl16_swap(float &a, float &b)
+{
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
 // x, y <- their sums over lanes l, l^16, l^32, l^48 (the four lane groups), in
 // every lane, bit-identical across lanes.
 __device__ __forceinline__ void sum2_groups(float &x, float &y)
 {
-    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    const float X = __uint_as_float(p[0]) + __uint_as_float(p[1]);   // rows: x02 x13 y02 y13
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(X), __float_as_uint(X), false, false);
-    const float Q = __uint_as_float(r[0]) + __uint_as_float(r[1]);   // rows: x x y y
-    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(Q), __float_as_uint(Q), false, false);
-    x = __uint_as_float(b[0]);
-    y = __uint_as_float(b[1]);
+    pl32_swap(x, y);
+    float X = x + y, X2 = X;        // rows: x02 x13 y02 y13
+    pl16_swap(X, X2);
+    float Q = X + X2, Q2 = Q;       // rows: x x y y
+    pl32_swap(Q, Q2);
+    x = Q;
+    y = Q2;
 }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
 {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
 // Sum over the 16 lanes of a DPP row (xor 1, xor 2, half-mirror, mirror).
@@ -119,35 +194,37 @@ struct FastCfg {
     static constexpr int RS = 4 * D + 4;         // record stride in floats: k^, u^, phi(q), v
     static constexpr int KH = 0, UH = D, PQ = 2 * D, VV = 3 * D;   // record fields
     static constexpr int ZS = D + 4;             // stride of the key-sum scratch rows
-    static constexpr int CPT = D * TT / NT;      // prologue columns per thread (4)
-    static constexpr int NCH = D / CPT;          // prologue column chunks per token
+    static constexpr int PT = 16 * TT;           // prologue threads: 16 per token
+    static constexpr int CPT = D / 16;           // prologue columns per thread (4, 6, 8)
 };
 
 // CPT consecutive inputs of one token, held in registers.
 template <typename Tin, int N> struct RawVec;
-template <> struct RawVec<float, 4> {
-    float4 x;
+template <int N> struct RawVec<float, N> {   // N in {4, 6, 8}; 8-byte aligned
+    float2 x[N / 2];
     __device__ __forceinline__ void load(const float *p, bool ok)
     {
-        x = ok ? *reinterpret_cast<const float4 *>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i)
+            x[i] = ok ? reinterpret_cast<const float2 *>(p)[i] : make_float2(0.f, 0.f);
     }
-    __device__ __forceinline__ float get(int i) const
-    {
-        return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
-    }
+    __device__ __forceinline__ float get(int i) const { return (i & 1) ? x[i >> 1].y : x[i >> 1].x; }
 };
-template <> struct RawVec<uint16_t, 4> {
-    uint2 x;
+template <int N> struct RawVec<uint16_t, N> {   // N in {4, 6, 8}; 4-byte aligned
+    uint32_t x[N / 2];
     __device__ __forceinline__ void load(const uint16_t *p, bool ok)
     {
-        x = ok ? *reinterpret_cast<const uint2 *>(p) : make_uint2(0u, 0u);
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) x[i] = ok ? reinterpret_cast<const uint32_t *>(p)[i] : 0u;
     }
     __device__ __forceinline__ float get(int i) const
     {
-        const uint32_t wd = (i >> 1) ? x.y : x.x;
-        return (i & 1) ? bf16_hi(wd) : bf16_lo(wd);
+        return (i & 1) ? bf16_hi(x[i >> 1]) : bf16_lo(x[i >> 1]);
     }
 };
+
+// phi = ELU + 1 with the hardware exp2 path (relative error ~1e-6 here).
+__device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
 template <int D, typename Tin>
 __global__ void __launch_bounds__(FastCfg<D>::NT)
@@ -159,7 +236,7 @@ vla_fwd_fast(const Tin *__restrict__ q, const Tin *__restrict__ k,
 {
     using C = FastCfg<D>;
     constexpr int NH = C::NH, NHP = C::NHP, NT = C::NT, SW1 = C::SW1, CPL = C::CPL, TT = C::TT;
-    constexpr int RING = C::RING, RS = C::RS, ZS = C::ZS, CPT = C::CPT, NCH = C::NCH;
+    constexpr int RING = C::RING, RS = C::RS, ZS = C::ZS, CPT = C::CPT, PT = C::PT;
     constexpr int KH = C::KH, UH = C::UH, PQ = C::PQ, VV = C::VV;
 
     // token records: slot s at s_rec[(s + 1) * RS]; s_rec[0 .. RS) repeats the
@@ -168,7 +245,6 @@ vla_fwd_fast(const Tin *__restrict__ q, const Tin *__restrict__ k,
     __shared__ __align__(16) float s_rec[(RING + 1) * RS];
     __shared__ __align__(16) float s_zk[TT * ZS];       // phi(k), then the key sum, of a tile
     __shared__ float s_rden[RING];                      // 1 / max(phi(q)' zkey, eps)
-    __shared__ float s_part[2][NCH][TT];                // prologue partial sums
     __shared__ __align__(16) float s_z[2][D];           // all-gather of z_t
     __shared__ __align__(16) float s_y[2][D];           // all-gather of y_{t-1}
     __shared__ __align__(16) float s_red[2][4][NHP];    // per-wave dot-product partials
@@ -186,8 +262,8 @@ vla_fwd_fast(const Tin *__restrict__ q, const Tin *__restrict__ k,
     // element; their values are never broadcast)
     const int l1 = 64 + SW1 * g + (n < SW1 ? n : (SW1 > 0 ? SW1 - 1 : 0));
 
-    float zk_run = 0.f, zk_cmp = 0.f;          // key-sum column tid (tid < D), Kahan
-    if (tid < D && zk0) zk_run = zk0[bh * D + tid];
+    float zk_run = 0.f, zk_cmp = 0.f;          // key sum of column tid (tid < D) before
+    if (tid < D && zk0) zk_run = zk0[bh * D + tid];   // the tile, Kahan-compensated
 
     for (int i = tid; i < (RING + 1) * RS; i += NT) s_rec[i] = 0.f;
     for (int i = tid; i < RING; i += NT) s_rden[i] = 0.f;
@@ -197,86 +273,78 @@ vla_fwd_fast(const Tin *__restrict__ q, const Tin *__restrict__ k,
     }
     for (int i = tid; i < 2 * 4 * NHP; i += NT) (&s_red[0][0][0])[i] = 0.f;
 
-    // prologue thread mapping: token tl of the tile, columns [ch*CPT, ch*CPT+CPT)
-    const int tl = tid % TT, ch = tid / TT;
+    // prologue thread mapping: 16 threads per token (one DPP row), token tl of the
+    // tile, columns [c*CPT, c*CPT+CPT); threads tid >= PT only join the barriers
+    const bool pthr = tid < PT;
+    const int tl = (tid >> 4) & (TT - 1), c = tid & 15;
     const size_t tok_base = bh * (size_t)T;
     RawVec<Tin, CPT> rq, rk, rv, ru;
     auto prefetch = [&](int t0) {
+        if (!pthr) return;
         const int t = t0 + tl;
         const bool ok = t < T;
-        const size_t off = (tok_base + (size_t)(ok ? t : 0)) * D + (size_t)ch * CPT;
+        const size_t off = (tok_base + (size_t)(ok ? t : 0)) * D + (size_t)c * CPT;
         rq.load(q + off, ok);
         rk.load(k + off, ok);
         rv.load(v + off, ok);
         ru.load(u + off, ok);
     };
 
-    // State-independent work of the tile starting at token t0 (all threads; four
+    // State-independent work of the tile starting at token t0 (all threads; two
     // barriers).  Leaves k^, u^, phi(q), v of each token in its record and
     // 1/max(phi(q)'zkey, eps) in s_rden, and advances the key sums.
     auto prologue = [&](int t0) {
         const int t = t0 + tl;
         const bool ok = t < T;
         const int slot = t & (RING - 1);
-        const int rec = (slot + 1) * RS;
-        float pk = 0.f, pu = 0.f;
+        const int rec = (slot + 1) * RS + c * CPT;
+        float pq[CPT];
+        if (pthr) {
+            float pk = 0.f, pu = 0.f;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            pk = fmaf(rk.get(i), rk.get(i), pk);
-            pu = fmaf(ru.get(i), ru.get(i), pu);
-        }
-        s_part[0][ch][tl] = pk;
-        s_part[1][ch][tl] = pu;
-        __syncthreads();
-        float nk = 0.f, nu = 0.f;
-#pragma unroll 8
-        for (int c2 = 0; c2 < NCH; ++c2) {
-            nk += s_part[0][c2][tl];
-            nu += s_part[1][c2][tl];
-        }
-        const float ik = nk > 0.f ? 1.f / sqrtf(nk) : 0.f;
-        const float iu = nu > 0.f ? 1.f / sqrtf(nu) : 0.f;
-        const int cb = ch * CPT;
-        float4 kh4, uh4, pq4, v4, pk4;
-        kh4.x = rk.get(0) * ik; kh4.y = rk.get(1) * ik; kh4.z = rk.get(2) * ik; kh4.w = rk.get(3) * ik;
-        uh4.x = ru.get(0) * iu; uh4.y = ru.get(1) * iu; uh4.z = ru.get(2) * iu; uh4.w = ru.get(3) * iu;
-        pq4.x = phi(rq.get(0)); pq4.y = phi(rq.get(1)); pq4.z = phi(rq.get(2)); pq4.w = phi(rq.get(3));
-        v4.x = rv.get(0); v4.y = rv.get(1); v4.z = rv.get(2); v4.w = rv.get(3);
-        pk4.x = ok ? phi(rk.get(0)) : 0.f; pk4.y = ok ? phi(rk.get(1)) : 0.f;
-        pk4.z = ok ? phi(rk.get(2)) : 0.f; pk4.w = ok ? phi(rk.get(3)) : 0.f;
-        *reinterpret_cast<float4 *>(&s_rec[rec + KH + cb]) = kh4;
-        *reinterpret_cast<float4 *>(&s_rec[rec + UH + cb]) = uh4;
-        *reinterpret_cast<float4 *>(&s_rec[rec + PQ + cb]) = pq4;
-        *reinterpret_cast<float4 *>(&s_rec[rec + VV + cb]) = v4;
-        if (slot == RING - 1) *reinterpret_cast<float4 *>(&s_rec[PQ + cb]) = pq4;   // alias record
-        *reinterpret_cast<float4 *>(&s_zk[tl * ZS + cb]) = pk4;
-        __syncthreads();
-        if (tid < D) {   // inclusive running key sum down the tile, per column
-#pragma unroll 8
-            for (int tt = 0; tt < TT; ++tt) {
-                const float x = s_zk[tt * ZS + tid];
-                const float yk = x - zk_cmp;
-                const float ts = zk_run + yk;
-                zk_cmp = (ts - zk_run) - yk;
-                zk_run = ts;
-                s_zk[tt * ZS + tid] = zk_run;
+            for (int i = 0; i < CPT; ++i) {
+                pk = fmaf(rk.get(i), rk.get(i), pk);
+                pu = fmaf(ru.get(i), ru.get(i), pu);
+            }
+            const float nk = sum_row16(pk), nu = sum_row16(pu);    // |k_t|^2, |u_t|^2
+            const float ik = nk > 0.f ? 1.f / sqrtf(nk) : 0.f;
+            const float iu = nu > 0.f ? 1.f / sqrtf(nu) : 0.f;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                pq[i] = phi_fast(rq.get(i));
+                s_rec[rec + KH + i] = rk.get(i) * ik;
+                s_rec[rec + UH + i] = ru.get(i) * iu;
+                s_rec[rec + PQ + i] = pq[i];
+                s_rec[rec + VV + i] = rv.get(i);
+                if (slot == RING - 1) s_rec[PQ + c * CPT + i] = pq[i];   // alias record
+                s_zk[tl * ZS + c * CPT + i] = ok ? phi_fast(rk.get(i)) : 0.f;
             }
         }
         __syncthreads();
-        const float4 zz = *reinterpret_cast<const float4 *>(&s_zk[tl * ZS + cb]);
-        float pd = pq4.x * zz.x;
-        pd = fmaf(pq4.y, zz.y, pd);
-        pd = fmaf(pq4.z, zz.z, pd);
-        pd = fmaf(pq4.w, zz.w, pd);
-        s_part[0][ch][tl] = pd;
-        __syncthreads();
-        if (ch == 0) {
-            float dsum = 0.f;
+        if (tid < D) {
+            // inclusive key sum per column: prefix inside the tile from zero, added
+            // to the compensated sum of the earlier tiles
+            float loc = 0.f;
 #pragma unroll 8
-            for (int c2 = 0; c2 < NCH; ++c2) dsum += s_part[0][c2][tl];
-            s_rden[slot] = 1.f / fmaxf(dsum, eps);
+            for (int tt = 0; tt < TT; ++tt) {
+                loc += s_zk[tt * ZS + tid];
+                s_zk[tt * ZS + tid] = zk_run + loc;
+            }
+            const float yk = loc - zk_cmp;
+            const float ts = zk_run + yk;
+            zk_cmp = (ts - zk_run) - yk;
+            zk_run = ts;
         }
-        // s_rden of a token is first read two iterations later, after two barriers.
+        __syncthreads();
+        if (pthr) {
+            float pd = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) pd = fmaf(pq[i], s_zk[tl * ZS + c * CPT + i], pd);
+            pd = sum_row16(pd);
+            if (c == 0) s_rden[slot] = 1.f / fmaxf(pd, eps);
+        }
+        // s_rden of a token is first read two iterations later, after two barriers;
+        // s_zk is next written after at least one token barrier.
     };
 
     // Runs every tile: prologue, prefetch of the next tile, then the token
@@ -348,22 +416,7 @@ vla_fwd_fast(const Tin *__restrict__ q, const Tin *__restrict__ k,
             const float k0 = s_rec[st + KH + l], k1 = SW1 ? s_rec[st + KH + l1] : 0.f;
             const float mem = s_rec[st + o_part];
             float za, wa;
-            sfor<CPL>([&](auto mm) {
-                constexpr int m = decltype(mm)::value;
-                if constexpr (m == 0) {
-                    fmac_bc<0>(m_[0], zc0, nc);
-                    fmul_bc<0>(za, u0, m_[0]);
-                    fmul_bc<0>(wa, k0, m_[0]);
-                } else if constexpr (m < 16) {
-                    fmac_bc<m>(m_[m], zc0, nc);
-                    fmac_bc<m>(za, u0, m_[m]);
-                    fmac_bc<m>(wa, k0, m_[m]);
-                } else {
-                    fmac_bc<m - 16>(m_[m], zc1, nc);
-                    fmac_bc<m - 16>(za, u1, m_[m]);
-                    fmac_bc<m - 16>(wa, k1, m_[m]);
-                }
-            });
+            row_pass<CPL, SW1>(m_, zc0, zc1, nc, u0, u1, k0, k1, za, wa);
             sum2_groups(za, wa);                               // z_t, w_t (rows)
             const float lhs = g < 2 ? za : yr;
             const float rhs = g == 2 ? yr : mem;
@@ -407,22 +460,7 @@ vla_fwd_fast(const Tin *__restrict__ q, const Tin *__restrict__ k,
             const float vrow = s_rec[sp + VV + row];
             const float se = ep * ny;          // alpha^_{t-2,j} e_{t-2,i} = y_j * (e_i / |y|)
             float ra, pa;
-            sfor<CPL>([&](auto mm) {
-                constexpr int m = decltype(mm)::value;
-                if constexpr (m == 0) {
-                    fmac_bc<0>(m_[0], yc0, se);
-                    fmul_bc<0>(ra, kp0, m_[0]);
-                    fmul_bc<0>(pa, q0, m_[0]);
-                } else if constexpr (m < 16) {
-                    fmac_bc<m>(m_[m], yc0, se);
-                    fmac_bc<m>(ra, kp0, m_[m]);
-                    fmac_bc<m>(pa, q0, m_[m]);
-                } else {
-                    fmac_bc<m - 16>(m_[m], yc1, se);
-                    fmac_bc<m - 16>(ra, kp1, m_[m]);
-                    fmac_bc<m - 16>(pa, q1, m_[m]);
-                }
-            });
+            row_pass<CPL, SW1>(m_, yc0, yc1, se, kp0, kp1, q0, q1, ra, pa);
             sum2_groups(ra, pa);
             ep = vrow - ra;    // e_{t-1} = v - S k^ with S before token t-1's write
             pp = pa;
