@@ -11,8 +11,10 @@ the MI355X FP32 vector peak, a roofline record for the forward kernel
 and the fp64 CPU oracle timed on the host cores over a bounded sample of heads.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -24,6 +26,33 @@ METRIC = "VLA fwd tokens·heads/sec (fp32 state) + % of MI355X FP32 vector peak"
 UNIT = "tokens*heads/s"
 FP32_VECTOR_PEAK_TFLOPS = 157.3          # MI355X published FP32 vector peak
 WORKLOAD = 3                              # B=8, H=16, d_h=64, T=4096, bf16 inputs
+KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_fwd_kernel.hip",
+                  "long_context_sequence_amd/csrc/vla_common.h"]
+TRAFFIC_SUMMARY = "profiles/vla_fwd_fast_b8h16_d64_t4096_bf16.txt"
+COPY_BYTES = 1 << 30                      # plain copy used to scale the HBM counters
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the forward kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE scaled by a plain copy of known
+    size), or None if there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"^kernel_source_sha256:\s*([0-9a-f]+)", txt, re.M)
+    m_traf = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
+    if not m_hash or not m_traf or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_traf.group(1))
 
 
 def flops_per_token_head(d: int) -> int:
@@ -42,7 +71,22 @@ def parse():
                    help="skip the oracle timing (e.g. under a profiler)")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads in the CPU-baseline sample (0 = every head of the workload)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     return p.parse_args()
+
+
+def calibrate_copy(reps: int = 3):
+    """A plain device-to-device copy of COPY_BYTES, for scaling FETCH_SIZE /
+    WRITE_SIZE counter readings to bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": COPY_BYTES,
+                      "bytes_written": COPY_BYTES, "reps": reps}), flush=True)
 
 
 def cpu_baseline(cfg, n_heads_req: int):
@@ -78,6 +122,10 @@ def main():
               "heads shard across GPUs with no communication, see the design notes.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import numpy as np
     import torch
@@ -142,7 +190,8 @@ def main():
         "pct_fp32_vector_peak": pct_peak,
         "roofline": {"bound": "alu", "achieved": achieved_tflops,
                      "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
+                     "traffic": measured_traffic(),
                      "kernel_ms": kern_ms, "flop_per_launch": flop},
     }
     if not args.no_cpu_baseline:
