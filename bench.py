@@ -115,6 +115,39 @@ def cpu_baseline(cfg, n_heads_req: int):
                       f"wall {wall:.2f} s"}
 
 
+def decode_bench(vla, torch, steps: int = 256):
+    """Single-token decode (vla_step) on the long-context decode shape: B=2,
+    H=32, d_h=128, bf16 inputs, state from a 64-token forward.  Each step reads
+    and writes the fp32 state (S, A: d^2 each, zkey: d) of every head."""
+    import gen
+    cfg = gen.config(5).with_sizes(T=64, decode=steps)
+    B, H, d = cfg.B, cfg.H, cfg.d
+    dev = torch.device("cuda:0")
+    x = gen.make_inputs(cfg)
+    t = {n: torch.from_numpy(x[n]).to(dev).view(torch.bfloat16) for n in x}
+    _, S, A, zk = vla.vla_forward(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps,
+                                  return_state=True)
+    dec = {n: t[n + "_dec"].permute(2, 0, 1, 3).contiguous() for n in "qkvu"}   # [steps,B,H,d]
+    o = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(8):
+        vla.vla_step(dec["q"][i], dec["k"][i], dec["v"][i], dec["u"][i], S, A, zk, cfg.eps,
+                     o=o, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        vla.vla_step(dec["q"][i], dec["k"][i], dec["v"][i], dec["u"][i], S, A, zk, cfg.eps,
+                     o=o, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    state_bytes = B * H * (2 * (2 * d * d + d) * 4 + 4 * d * 2 + d * 4)
+    return {"workload": "b2h32_d128_bf16 vla_step (one token for 64 heads)", "steps": steps,
+            "us_per_step": us, "tokens_heads_per_s": B * H / (us * 1e-6),
+            "state_bytes_per_step": state_bytes, "state_GBps": state_bytes / (us * 1e-6) / 1e9}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -194,6 +227,7 @@ def main():
                      "traffic": measured_traffic(),
                      "kernel_ms": kern_ms, "flop_per_launch": flop},
     }
+    res["decode"] = decode_bench(vla, torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
     print(json.dumps(res), flush=True)

@@ -24,12 +24,12 @@ vla_status check_common(int in_dtype, int B, int H, int d_h, float eps)
     return VLA_OK;
 }
 
-// Sequences go to the register-resident kernel when it covers d_h; single
-// decode tokens and d_h in {16, 32} use the LDS kernel.
-vla_status launch(const vla::FwdArgs &a, bool single_token)
+// d_h in {64, 96, 128} runs on the register-resident kernel (also for a single
+// decode token: every state element is read and written by the same lane, so the
+// state may be updated in place); d_h in {16, 32} uses the LDS kernel.
+vla_status launch(const vla::FwdArgs &a)
 {
-    hipError_t e = (!single_token && vla::fast_supported(a.d)) ? vla::launch_forward_fast(a)
-                                                               : vla::launch_forward_ref(a);
+    hipError_t e = vla::fast_supported(a.d) ? vla::launch_forward_fast(a) : vla::launch_forward_ref(a);
     return e == hipSuccess ? VLA_OK : VLA_ERR_HIP;
 }
 
@@ -56,7 +56,7 @@ extern "C" vla_status vla_forward(const void *q, const void *k, const void *v, c
 
     vla::FwdArgs a{q, k, v, u, in_dtype, B, H, T, d_h, lambda0, eps,
                    o, S_out, A_out, zkey_out, S0, A0, zkey0, (hipStream_t)stream};
-    return launch(a, false);
+    return launch(a);
 }
 
 extern "C" vla_status vla_step(const void *q, const void *k, const void *v, const void *u,
@@ -71,7 +71,7 @@ extern "C" vla_status vla_step(const void *q, const void *k, const void *v, cons
     // lambda0 only shapes the default A_0, which a step never uses (A is given).
     vla::FwdArgs a{q, k, v, u, in_dtype, B, H, 1, d_h, 1.0f, eps,
                    o, S, A, zkey, S, A, zkey, (hipStream_t)stream};
-    return launch(a, true);
+    return launch(a);
 }
 
 extern "C" const char *vla_status_string(int status)

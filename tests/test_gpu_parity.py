@@ -159,6 +159,34 @@ def test_shape_sweep_every_head(d, dtype, T):
         _check(name, g, ref[name])
 
 
+@pytest.mark.parametrize("T", [2, 30, 31, 32, 33, 63, 64, 65])
+def test_tile_boundaries(T):
+    """Sequence lengths around the 32-token prologue tile (the memory chain and
+    the readout run two tokens behind the penalty chain)."""
+    dev = _dev()
+    cfg = gen.config(3).with_sizes(B=1, H=2, T=T)
+    _say(f"tile boundary T={T}")
+    x = gen.make_inputs(cfg)
+    out = _gpu_forward(cfg, x, dev)
+    ref = oracle.forward(*(_f64(x[n], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+    for name, g in zip(("o", "S", "A", "zkey"), out):
+        _check(name, g, ref[name])
+
+
+def test_many_heads_grid():
+    """More (b, h) heads than compute units: 512 workgroups."""
+    dev = _dev()
+    cfg = gen.config(2).with_sizes(B=4, H=128, T=40)
+    _say("grid of 512 heads")
+    x = gen.make_inputs(cfg)
+    out = _gpu_forward(cfg, x, dev)
+    heads = [(0, 0), (1, 77), (3, 127), (2, 5)]
+    for (b, h) in heads:
+        r = oracle.forward_head(*(x[n][b, h].astype(np.float64) for n in "qkvu"))
+        _check(f"o[{b},{h}]", out[0][b, h], r["o"])
+        _check(f"S[{b},{h}]", out[1][b, h], r["S"])
+
+
 def test_empty_sequence_copies_state():
     dev = _dev()
     vla = _vla()
