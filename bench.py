@@ -6,9 +6,11 @@ workload (B = 8, H = 16, bf16 q/k/v/u, fp32 state), writing o and the final
 S, A and zkey.  Inputs are resident in HBM before the timed region.
 
 Prints ONE JSON line with the throughput in tokens*heads/s, the percentage of
-the MI355X FP32 vector peak, a roofline record for the forward kernel
-(algorithmic FLOP / average kernel time from HIP events on the launch stream)
-and the fp64 CPU oracle timed on the host cores over a bounded sample of heads.
+the MI355X FP32 peak, a roofline record for the forward kernel (algorithmic
+FLOP / average kernel time from HIP events on the launch stream; the kernel
+does its d x d products on fp32 matrix cores, whose dense peak equals the FP32
+vector peak) and the fp64 CPU oracle timed on the host cores over a bounded
+sample of heads.
 """
 import argparse
 import hashlib
@@ -24,11 +26,13 @@ if ROOT not in sys.path:
 
 METRIC = "VLA fwd tokens·heads/sec (fp32 state) + % of MI355X FP32 vector peak"
 UNIT = "tokens*heads/s"
-FP32_VECTOR_PEAK_TFLOPS = 157.3          # MI355X published FP32 vector peak
+FP32_VECTOR_PEAK_TFLOPS = 157.3          # MI355X published FP32 vector (and dense fp32 matrix) peak
 WORKLOAD = 3                              # B=8, H=16, d_h=64, T=4096, bf16 inputs
-KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_fwd_kernel.hip",
+KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_chunk_kernel.hip",
+                  "long_context_sequence_amd/csrc/vla_chunk_parts.h",
+                  "long_context_sequence_amd/csrc/vla_dpp_blocks.h",
                   "long_context_sequence_amd/csrc/vla_common.h"]
-TRAFFIC_SUMMARY = "profiles/vla_fwd_fast_b8h16_d64_t4096_bf16.txt"
+TRAFFIC_SUMMARY = "profiles/vla_fwd_fused_b8h16_d64_t4096_bf16.txt"
 COPY_BYTES = 1 << 30                      # plain copy used to scale the HBM counters
 
 
@@ -53,6 +57,24 @@ def measured_traffic():
     if not m_hash or not m_traf or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_traf.group(1))
+
+
+def device_peak_tflops():
+    """FP32 peak recomputed from the device: compute units x clock x 256 FLOP per
+    clock per CU (the figure behind the published 157.3 TFLOP/s), or None."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return None
+    cus, khz = ctypes.c_int(0), ctypes.c_int(0)
+    # hipDeviceAttributeMultiprocessorCount = 63, hipDeviceAttributeClockRate = 5 (kHz)
+    if hip.hipDeviceGetAttribute(ctypes.byref(cus), 63, 0) != 0:
+        return None
+    if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, 0) != 0:
+        return None
+    return {"cus": cus.value, "clock_mhz": khz.value / 1e3,
+            "tflops": cus.value * khz.value * 1e3 * 256 / 1e12}
 
 
 def flops_per_token_head(d: int) -> int:
@@ -196,7 +218,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    kern_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    launch_ms = [s.elapsed_time(e) for s, e in ev]
+    kern_ms = float(np.mean(launch_ms))
     ms_per_step = wall * 1e3 / args.steps
     tok_heads = B * H * T
     value = tok_heads / (ms_per_step / 1e3)
@@ -221,11 +244,13 @@ def main():
                    "input_dtype": cfg.dtype, "state_dtype": "f32",
                    "lambda0": cfg.lambda0, "eps": cfg.eps, "parallelism": "single GPU"},
         "pct_fp32_vector_peak": pct_peak,
-        "roofline": {"bound": "alu", "achieved": achieved_tflops,
+        "roofline": {"bound": "mfma", "achieved": achieved_tflops,
                      "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
                      "traffic": measured_traffic(),
-                     "kernel_ms": kern_ms, "flop_per_launch": flop},
+                     "kernel_ms": kern_ms, "kernel_ms_median": float(np.median(launch_ms)),
+                     "flop_per_launch": flop, "dtype": "fp32"},
+        "device_peak": device_peak_tflops(),
     }
     res["decode"] = decode_bench(vla, torch)
     if not args.no_cpu_baseline:

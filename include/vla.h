@@ -28,7 +28,11 @@
  *
  * Ownership and execution: the caller owns every buffer.  Calls are
  * asynchronous on `stream` (a hipStream_t; NULL = the null stream) and never
- * synchronise.  Arguments are checked before anything is launched; on an
+ * synchronise.  By default the library allocates nothing.  With the environment
+ * variable VLA_SPLIT=1, d_h in {64, 96, 128} runs each head's two chains on two
+ * compute units when the whole grid fits; that mode allocates a per-device
+ * scratch ring on first use (grown when needed, kept until the process ends),
+ * and calls that overlap on one device then race on it.  Arguments are checked before anything is launched; on an
  * argument error nothing is launched and no buffer is touched.  A failed launch
  * returns VLA_ERR_HIP.  Faults inside a kernel surface at the caller's next
  * synchronisation.  NaN or Inf inputs propagate without being reported.

@@ -24,12 +24,12 @@ vla_status check_common(int in_dtype, int B, int H, int d_h, float eps)
     return VLA_OK;
 }
 
-// d_h in {64, 96, 128} runs on the register-resident kernel (also for a single
+// d_h in {64, 96, 128} runs on the chunked matrix-core kernel (also for a single
 // decode token: every state element is read and written by the same lane, so the
 // state may be updated in place); d_h in {16, 32} uses the LDS kernel.
 vla_status launch(const vla::FwdArgs &a)
 {
-    hipError_t e = vla::fast_supported(a.d) ? vla::launch_forward_fast(a) : vla::launch_forward_ref(a);
+    hipError_t e = vla::chunk_supported(a.d) ? vla::launch_forward_chunk(a) : vla::launch_forward_ref(a);
     return e == hipSuccess ? VLA_OK : VLA_ERR_HIP;
 }
 

@@ -1,0 +1,625 @@
+// vla_chunk_parts.h -- device parts of the chunked matrix-core kernels of the
+// VLA recurrence (d_h in {64, 96, 128}): data layout, input staging and the two
+// chains.  The kernels in vla_chunk_kernel.hip only arrange them in time.
+//
+// Source: "Variational Linear Attention" (arXiv 2605.11196), section 3.3,
+// Eqs. (9) (Sherman-Morrison downdate of A), (10) (gated delta write of S) and
+// (11) (ELU+1 readout with the running key sum); A_0 = I / lambda0 (section 3.2).
+//
+// Blocked form.  Tokens are taken in chunks of C = 16.  With A and S the states
+// at the start of a chunk, U^, K^, Phi, V (d x C) the chunk's normalised u, k,
+// phi(q) and raw v as columns, the C token steps compose exactly (up to rounding):
+//
+//   penalty chain (Eq. 9).   Z0 = A U^, Y0 = A K^, G = U^' Z0, and the LDL'
+//   factorisation I + G = L D L' (L unit lower triangular).  The C downdates
+//   of A are one Woodbury step,  A <- A - Z0 (I + G)^-1 Z0',  and the vectors
+//   A_t k^_t (A_t after token t's own downdate) are the columns of
+//       W = Y0 - Z0 L^-T ((D^-1 L^-1 U^' Y0) o Up),      Up_{ct} = [c <= t],
+//   because the downdates up to token t use the leading (t+1) x (t+1) block of
+//   I + G, whose factor is the leading block of L D L'.   alpha^_t = w_t / |w_t|.
+//
+//   memory chain (Eqs. 10, 11).  N_{ct} = alpha^_c' k^_t for c < t (0 otherwise),
+//   E = (V - S K^) (I + N)^-1 holds the errors e_t of the token steps, and
+//       S <- S + E Alpha^',     S_t phi(q_t) = S phi(q_t) + E ((Alpha^' Phi) o Up)_t.
+//
+// Mapping.  A chain runs on NA wavefronts (NA = 4 for d = 64, 128 and 6 for
+// d = 96).  Each wave owns BPW = d / (16 NA) column blocks of 16 of its stored
+// matrix, which is the TRANSPOSE of the state (As = A', Ss = S'), kept in MFMA
+// accumulator layout for the whole sequence: tile (rho, b) of block b, register
+// r of lane l = 16 g + n holds
+//       Xs[16 rho + 4 g + r][16 b + n].
+// v_mfma_f32_16x16x4_f32 takes A[m][k] from lane 16 k' + m and B[k][n] from lane
+// 16 k' + n (k' = the lane group) and returns D[4 g + r][n] in register r of
+// lane 16 g + n.  Used as the B operand with k = 16 rho + 4 g + r, a state tile
+// gives the products X' [U^ K^] = (A [U^ K^])' one 16 x 16 tile per block with
+// no data movement; the rank-16 updates accumulate into the same registers.
+// Every other operand is read from LDS in the layout its product needs.
+//
+// The 16 x 16 factorisations run in registers with one matrix row per lane of a
+// 16-lane DPP row (row_newbcast broadcasts a matrix entry along it); the inverses
+// of the unit triangular factors are computed four columns at a time, one per
+// lane group.
+#pragma once
+#include <utility>
+
+#include "vla_common.h"
+#include "vla_dpp_blocks.h"
+
+namespace vla {
+namespace chunk {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+template <typename F, int... Is>
+__device__ __forceinline__ void sfor_impl(F &&f, std::integer_sequence<int, Is...>)
+{
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void sfor(F &&f)
+{
+    sfor_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ f4 mma(float a, float b, f4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Four k-steps of a 16 x 16 product, c + sum_s A_s B_s, split over two
+// accumulators so that consecutive matrix-core operations are independent.
+__device__ __forceinline__ f4 mma4(const float (&a)[4], const float (&b)[4], f4 c)
+{
+    f4 c1 = mma(a[1], b[1], (f4){0.f, 0.f, 0.f, 0.f});
+    c = mma(a[0], b[0], c);
+    c1 = mma(a[3], b[3], c1);
+    c = mma(a[2], b[2], c);
+    return c + c1;
+}
+__device__ __forceinline__ f4 mma4(f4 a, f4 b, f4 c)
+{
+    const float aa[4] = {a[0], a[1], a[2], a[3]}, ba[4] = {b[0], b[1], b[2], b[3]};
+    return mma4(aa, ba, c);
+}
+
+// 16-byte loads and stores (LDS or global)
+__device__ __forceinline__ f4 ld4(const float *p) { return *reinterpret_cast<const f4 *>(p); }
+__device__ __forceinline__ void st4(float *p, f4 x) { *reinterpret_cast<f4 *>(p) = x; }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over the 16 lanes of a DPP row (xor 1, xor 2, half-mirror, mirror).
+__device__ __forceinline__ float sum_row16(float x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    x += dpp<0x140>(x);
+    return x;
+}
+
+// x[lane J of this 16-lane row], after the two wait states a VALU write of x
+// needs before a DPP read (x may come straight from an inline-asm FMA).
+template <int J>
+__device__ __forceinline__ float bcast(float x)
+{
+    float r;
+    asm volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
+                 : "=v"(r)
+                 : "v"(x), "n"(J));
+    return r;
+}
+
+// Compiler-only ordering point between LDS writes and reads of other lanes of
+// the same wave (LDS executes one wave's instructions in order).
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
+// Workgroup barrier for LDS traffic only.  Unlike __syncthreads() it does not
+// wait for outstanding global loads and stores, so prefetches into registers
+// stay in flight across it (their consumers wait for them as usual).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One input element kept as loaded (bf16 stays a bit pattern), so that the load
+// can stay in flight until the value is used.
+template <typename Tin> struct Raw1;
+template <> struct Raw1<float> {
+    float x;
+    __device__ __forceinline__ void load(const float *p, size_t i) { x = p[i]; }
+    __device__ __forceinline__ float get() const { return x; }
+};
+template <> struct Raw1<uint16_t> {
+    uint32_t x;
+    __device__ __forceinline__ void load(const uint16_t *p, size_t i) { x = p[i]; }
+    __device__ __forceinline__ float get() const { return __uint_as_float(x << 16); }
+};
+
+// CPT consecutive inputs of one token, held in registers.
+template <typename Tin, int N> struct RawVec;
+template <int N> struct RawVec<float, N> {   // N in {4, 6, 8}; 8-byte aligned
+    float2 x[N / 2];
+    __device__ __forceinline__ void load(const float *p)
+    {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) x[i] = reinterpret_cast<const float2 *>(p)[i];
+    }
+    __device__ __forceinline__ float get(int i) const { return (i & 1) ? x[i >> 1].y : x[i >> 1].x; }
+};
+template <int N> struct RawVec<uint16_t, N> {   // N in {4, 6, 8}; 4-byte aligned
+    uint32_t x[N / 2];
+    __device__ __forceinline__ void load(const uint16_t *p)
+    {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) x[i] = reinterpret_cast<const uint32_t *>(p)[i];
+    }
+    __device__ __forceinline__ float get(int i) const
+    {
+        return (i & 1) ? bf16_hi(x[i >> 1]) : bf16_lo(x[i >> 1]);
+    }
+};
+
+// phi = ELU + 1 with the hardware exp2 path (relative error ~1e-6 here).
+__device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+
+template <int D>
+struct Cfg {
+    static constexpr int C = 16;                   // tokens per chunk
+    static constexpr int NB = D / 16;              // 16-column blocks of a state
+    static constexpr int NA = NB % 4 == 0 ? 4 : NB;// waves per chain
+    static constexpr int BPW = NB / NA;            // column blocks per wave
+    static constexpr int PA = BPW == 1 ? 2 : 1;    // partial accumulators per d x d product
+    static constexpr int LD = D + 4;               // row stride of [token][i] arrays
+    static constexpr int LT = C + 4;               // row stride of [i][token] and C x C arrays
+    static constexpr int CPT = D / 16;             // staged columns per thread (16 per token)
+    static constexpr int WSLOT = 16 * D + 16 * NA; // floats of one chunk's W' and |w|^2 partials
+};
+
+// Everything a head keeps in LDS (every member a multiple of 16 bytes).
+template <int D>
+struct Lds {
+    static constexpr int C = Cfg<D>::C, NA = Cfg<D>::NA, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
+    float uh[2][C * LD];     // u^   [token][i], by chunk parity
+    float kh[2][C * LD];     // k^
+    float ph[2][C * LD];     // phi(q)
+    float zk[C * LD];        // phi(k), then the key sum, of the chunk being staged
+    float rden[2][C];        // 1 / max(phi(q)' zkey, eps)
+    float z0[C * LD];        // Z0 [token][i]
+    float y0[C * LD];        // Y0 [token][i]
+    float z0t[D * LT];       // Z0 [i][token]
+    float w[C * LD];         // W [token][i]
+    float wt[2][D * LT];     // W [i][token], by chunk parity
+    float gp[NA][2][C * LT]; // per A-wave: I + U^'Z0 (wave 0) or U^'Z0, and U^'Y0
+    float nrm[NA][C];        // per A-wave: partial |w_t|^2
+    float nq[NA][2][C * LT]; // per S-wave: Alpha^'K^, Alpha^'Phi
+    float lit[NA][C * LT];   // per A-wave: L^-1 transposed
+    float inv[NA][C];        // per A-wave: 1 / d_j
+    float tit[NA][C * LT];   // per S-wave: (I+N)^-1 transposed
+};
+
+// Where the penalty chain leaves W' and the |w|^2 partials of a chunk: in LDS
+// for a memory chain in the same workgroup ...
+template <int D>
+struct WToLds {
+    Lds<D> &L;
+    int sp, g, n;
+    __device__ __forceinline__ void block(int b, f4 wt)
+    {
+        constexpr int LD = Cfg<D>::LD, LT = Cfg<D>::LT;
+        sfor<4>([&](auto r) { L.w[(4 * g + r) * LD + 16 * b + n] = wt[int(r)]; });
+        st4(&L.wt[sp][(16 * b + n) * LT + 4 * g], wt);
+    }
+    __device__ __forceinline__ void norms(int wi, f4 nr)
+    {
+        if (n == 0) st4(&L.nrm[wi][4 * g], nr);
+    }
+};
+// ... or in a global ring slot ([i][token] rows of 16, then NA x 16 partials) for
+// a memory chain on another compute unit.
+template <int D>
+struct WToGlobal {
+    float *slot;
+    int g, n;
+    __device__ __forceinline__ void block(int b, f4 wt) { st4(&slot[(16 * b + n) * 16 + 4 * g], wt); }
+    __device__ __forceinline__ void norms(int wi, f4 nr)
+    {
+        if (n == 0) st4(&slot[16 * D + 16 * wi + 4 * g], nr);
+    }
+};
+
+// Per-thread view of one head: lane coordinates, input pointers and the two
+// chains' steps.  A wave with chain index wi owns column blocks wi*BPW + bb.
+template <int D, typename Tin>
+struct Head {
+    using Cf = Cfg<D>;
+    static constexpr int C = Cf::C, NB = Cf::NB, NA = Cf::NA, BPW = Cf::BPW, PA = Cf::PA;
+    static constexpr int LD = Cf::LD, LT = Cf::LT, CPT = Cf::CPT;
+    typedef f4 State[BPW][NB];
+
+    Lds<D> &L;
+    const Tin *q, *k, *v, *u;
+    float *o;
+    int T;
+    float eps;
+    size_t tok0;     // first token row of the head
+    int g, n, wi;    // lane group, lane in group, wave index within its chain
+    // staging: 16 threads per token (one DPP row), token tl, columns [cc*CPT, +CPT);
+    // thread ts < D also owns key-sum column ts
+    int ts, tl, cc;
+    bool pthr;
+    float zk_run = 0.f, zk_cmp = 0.f;   // Kahan-compensated key sum of column ts
+    RawVec<Tin, CPT> rq, rk, ru;
+
+    __device__ __forceinline__ Head(Lds<D> &L_, const Tin *q_, const Tin *k_, const Tin *v_,
+                                    const Tin *u_, float *o_, int T_, float eps_, size_t bh,
+                                    int lane, int wi_, int ts_, bool stager)
+        : L(L_), q(q_), k(k_), v(v_), u(u_), o(o_), T(T_), eps(eps_), tok0(bh * (size_t)T_),
+          g(lane >> 4), n(lane & 15), wi(wi_), ts(ts_), tl((ts_ >> 4) & (C - 1)), cc(ts_ & 15),
+          pthr(stager && ts_ < 16 * C)
+    {
+    }
+
+    // ------------------------------------------------------------ state I/O
+    // The d x d state is row-major in memory; the tiles hold its transpose.
+    __device__ __forceinline__ void load_state(State &st, const float *src, float diag) const
+    {
+        sfor<BPW>([&](auto bb) {
+            const int row = 16 * (wi * BPW + bb) + n;
+            sfor<NB>([&](auto rho) {
+                const int col = 16 * rho + 4 * g;
+                if (src) {
+                    st[bb][rho] = ld4(&src[(size_t)row * D + col]);
+                } else {
+                    f4 x;
+                    sfor<4>([&](auto r) { x[int(r)] = row == col + r ? diag : 0.f; });
+                    st[bb][rho] = x;
+                }
+            });
+        });
+    }
+    __device__ __forceinline__ void store_state(const State &st, float *dst) const
+    {
+        sfor<BPW>([&](auto bb) {
+            const int row = 16 * (wi * BPW + bb) + n;
+            sfor<NB>([&](auto rho) { st4(&dst[(size_t)row * D + 16 * rho + 4 * g], st[bb][rho]); });
+        });
+    }
+
+    // ------------------------------------------------------------ staging
+    // raw inputs of chunk cq into registers (rows past T re-read row T-1; stage1
+    // zeroes them).  WQ: q (memory chain), WU: u (penalty chain); k always.
+    template <bool WQ, bool WU>
+    __device__ __forceinline__ void prefetch(int cq)
+    {
+        if (!pthr) return;
+        const int t = cq * C + tl;
+        const size_t off = (tok0 + (size_t)(t < T ? t : T - 1)) * D + (size_t)cc * CPT;
+        if constexpr (WQ) rq.load(q + off);
+        rk.load(k + off);
+        if constexpr (WU) ru.load(u + off);
+    }
+    // k^ (and u^, or phi(q) and phi(k)) of chunk cq into its LDS slot
+    template <bool WQ, bool WU>
+    __device__ __forceinline__ void stage1(int cq)
+    {
+        if (!pthr) return;
+        const int slot = cq & 1;
+        const bool ok = cq * C + tl < T;
+        float pk = 0.f, pu = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            pk = fmaf(rk.get(i), rk.get(i), pk);
+            if constexpr (WU) pu = fmaf(ru.get(i), ru.get(i), pu);
+        }
+        const float nk = sum_row16(pk);
+        const float ik = ok && nk > 0.f ? rsqrtf(nk) : 0.f;
+        float iu = 0.f;
+        if constexpr (WU) {
+            const float nu = sum_row16(pu);
+            iu = ok && nu > 0.f ? rsqrtf(nu) : 0.f;
+        }
+        const int e0 = tl * LD + cc * CPT;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            L.kh[slot][e0 + i] = rk.get(i) * ik;
+            if constexpr (WU) L.uh[slot][e0 + i] = ru.get(i) * iu;
+            if constexpr (WQ) {
+                L.ph[slot][e0 + i] = phi_fast(rq.get(i));
+                L.zk[e0 + i] = ok ? phi_fast(rk.get(i)) : 0.f;
+            }
+        }
+    }
+    // inclusive key sum per column: prefix inside the chunk, added to the
+    // compensated sum of the earlier chunks
+    __device__ __forceinline__ void stage2()
+    {
+        if (ts >= D) return;
+        float f[C];
+#pragma unroll
+        for (int tt = 0; tt < C; ++tt) f[tt] = L.zk[tt * LD + ts];
+        float loc = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < C; ++tt) {
+            loc += f[tt];
+            L.zk[tt * LD + ts] = zk_run + loc;
+        }
+        const float yk = loc - zk_cmp;
+        const float tsum = zk_run + yk;
+        zk_cmp = (tsum - zk_run) - yk;
+        zk_run = tsum;
+    }
+    // readout denominators of chunk cq
+    __device__ __forceinline__ void stage3(int cq)
+    {
+        if (!pthr) return;
+        const int slot = cq & 1;
+        const int e0 = tl * LD + cc * CPT;
+        float pd = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) pd = fmaf(L.ph[slot][e0 + i], L.zk[e0 + i], pd);
+        pd = sum_row16(pd);
+        if (cc == 0) L.rden[slot][tl] = __builtin_amdgcn_rcpf(fmaxf(pd, eps));
+    }
+    // V' rows 4g+r of chunk cq (own blocks), kept as loaded
+    __device__ __forceinline__ void load_v(int cq, Raw1<Tin> (&vraw)[BPW][4]) const
+    {
+        sfor<BPW>([&](auto bb) {
+            const int b = wi * BPW + bb;
+            sfor<4>([&](auto r) {
+                const int t = min(cq * C + 4 * g + r, T - 1);
+                vraw[bb][r].load(v, (tok0 + t) * D + 16 * b + n);
+            });
+        });
+    }
+
+    // ------------------------------------------------------------ penalty chain
+    // Z0' and Y0' of the own blocks (y kept for the second half), Z0 and Y0 into
+    // LDS, and this wave's partials of U^'Z0 and U^'Y0 (rows i of its blocks).
+    __device__ __forceinline__ void a_products(const State &st, int p, f4 (&y)[BPW])
+    {
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        const int sp = p & 1;
+        const float *ub = L.uh[sp], *kb = L.kh[sp];
+        f4 z[BPW], za[BPW][PA], ya[BPW][PA];
+        sfor<BPW>([&](auto bb) { sfor<PA>([&](auto h) { za[bb][h] = zero; ya[bb][h] = zero; }); });
+        sfor<NB>([&](auto rho) {
+            constexpr int h = decltype(rho)::value % PA;
+            const f4 au = ld4(&ub[n * LD + 16 * rho + 4 * g]);
+            const f4 ak = ld4(&kb[n * LD + 16 * rho + 4 * g]);
+            sfor<4>([&](auto r) {
+                sfor<BPW>([&](auto bb) {
+                    za[bb][h] = mma(au[int(r)], st[bb][rho][int(r)], za[bb][h]);
+                    ya[bb][h] = mma(ak[int(r)], st[bb][rho][int(r)], ya[bb][h]);
+                });
+            });
+        });
+        sfor<BPW>([&](auto bb) {
+            z[bb] = za[bb][0];
+            y[bb] = ya[bb][0];
+            if constexpr (PA == 2) {
+                z[bb] += za[bb][1];
+                y[bb] += ya[bb][1];
+            }
+        });
+        // z[bb] register r = Z0[16b + n][4g + r]; same for y
+        sfor<BPW>([&](auto bb) {
+            const int b = wi * BPW + bb;
+            sfor<4>([&](auto r) {
+                L.z0[(4 * g + r) * LD + 16 * b + n] = z[bb][int(r)];
+                L.y0[(4 * g + r) * LD + 16 * b + n] = y[bb][int(r)];
+            });
+            st4(&L.z0t[(16 * b + n) * LT + 4 * g], z[bb]);
+        });
+        wave_lds_order();
+        f4 gu = zero, gk = zero;
+        sfor<BPW>([&](auto bb) {
+            const int b = wi * BPW + bb;
+            const f4 au = ld4(&ub[n * LD + 16 * b + 4 * g]);
+            const f4 bz = ld4(&L.z0[n * LD + 16 * b + 4 * g]);
+            const f4 by = ld4(&L.y0[n * LD + 16 * b + 4 * g]);
+            gu = mma4(au, bz, gu);
+            gk = mma4(au, by, gk);
+        });
+        if (wi == 0) sfor<4>([&](auto r) { gu[int(r)] += 4 * g + r == n ? 1.f : 0.f; });
+        sfor<4>([&](auto r) {
+            L.gp[wi][0][(4 * g + r) * LT + n] = gu[int(r)];
+            L.gp[wi][1][(4 * g + r) * LT + n] = gk[int(r)];
+        });
+    }
+
+    // Factorise I + G, downdate the own blocks of As, and hand W' and the |w|^2
+    // partials of the chunk to `wout`.
+    template <class WOut>
+    __device__ __forceinline__ void a_update(State &st, const f4 (&y)[BPW], WOut &&wout)
+    {
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        // row n of M = I + G in every lane group; B operand of U^'Y0
+        float Mr[16], gub[4];
+        sfor<4>([&](auto q4) {
+            f4 a = ld4(&L.gp[0][0][n * LT + 4 * q4]);
+            sfor<NA - 1>([&](auto w2) { a += ld4(&L.gp[w2 + 1][0][n * LT + 4 * q4]); });
+            sfor<4>([&](auto r) { Mr[4 * q4 + r] = a[int(r)]; });
+        });
+        sfor<4>([&](auto c) {
+            float a = L.gp[0][1][(4 * c + g) * LT + n];
+            sfor<NA - 1>([&](auto w2) { a += L.gp[w2 + 1][1][(4 * c + g) * LT + n]; });
+            gub[c] = a;
+        });
+        // LDL' (column by column): lane n holds row n.  LDr[j] = L[n][j] d_j
+        // (d_j in lane j), NLr[j] = -L[n][j] for n > j, 0 otherwise.
+        float LDr[16], NLr[16];
+        float invd = 0.f;   // 1 / d_n
+        sfor<16>([&](auto jj) {
+            constexpr int j = decltype(jj)::value;
+            float acc = Mr[j];
+            if constexpr (j > 0) ldl_block<j, 0, (j < 8 ? j : 8)>(acc, LDr, NLr);
+            if constexpr (j > 8) ldl_block<j, 8, j - 8>(acc, LDr, NLr);
+            const float inv = __builtin_amdgcn_rcpf(bcast<j>(acc));
+            LDr[j] = acc;
+            NLr[j] = n > j ? -(acc * inv) : 0.f;
+            invd = n == j ? inv : invd;
+        });
+        // L^-1 by forward substitution, four columns at a time: lane group g
+        // computes column 4c + g in X[c] (lane n = row n).
+        float X[4];
+        sfor<4>([&](auto c) { X[c] = n == 4 * c + g ? 1.f : 0.f; });
+        asm volatile(VLA_LINV_BLOCK
+                     : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3])
+                     : "v"(NLr[0]), "v"(NLr[1]), "v"(NLr[2]), "v"(NLr[3]), "v"(NLr[4]),
+                       "v"(NLr[5]), "v"(NLr[6]), "v"(NLr[7]), "v"(NLr[8]), "v"(NLr[9]),
+                       "v"(NLr[10]), "v"(NLr[11]), "v"(NLr[12]), "v"(NLr[13]), "v"(NLr[14]));
+        float DX[4];
+        sfor<4>([&](auto c) { DX[c] = X[c] * invd; });
+        if (g == 0) L.inv[wi][n] = invd;
+        sfor<4>([&](auto c) { L.lit[wi][(4 * c + g) * LT + n] = X[c]; });
+        wave_lds_order();
+        const f4 inv4 = ld4(&L.inv[wi][4 * g]);        // 1 / d_{4g+r}
+        const f4 lit = ld4(&L.lit[wi][n * LT + 4 * g]);  // L^-1 [4g+r][n]
+        // -(D^-1 L^-1 U^'Y0 o Up): A operand of W'
+        f4 hm = mma4(DX, gub, zero);
+        sfor<4>([&](auto r) { hm[int(r)] = 4 * g + r <= n ? -hm[int(r)] : 0.f; });
+        f4 nr = zero;
+        sfor<BPW>([&](auto bb) {
+            const int b = wi * BPW + bb;
+            float zb[4];   // Z0'[4c+g][16b+n]
+            sfor<4>([&](auto c) { zb[c] = L.z0[(4 * c + g) * LD + 16 * b + n]; });
+            const f4 q2 = mma4(X, zb, zero);        // L^-1 Z0'
+            const f4 q1 = q2 * inv4;                // D^-1 L^-1 Z0'
+            const f4 xt = mma4(lit, q1, zero);      // (I + G)^-1 Z0' = L^-T D^-1 L^-1 Z0'
+            // W' = Y0' - ((D^-1 L^-1 U^'Y0) o Up)' L^-1 Z0'
+            const f4 wt = mma4(hm, q2, y[bb]);
+            const f4 nx = -xt;
+            f4 az[NB];
+            sfor<NB>([&](auto rho) { az[rho] = ld4(&L.z0t[(16 * rho + n) * LT + 4 * g]); });
+            sfor<4>([&](auto r) {      // As <- As - Z0 (I + G)^-1 Z0'
+                sfor<NB>([&](auto rho) { st[bb][rho] = mma(az[rho][int(r)], nx[int(r)], st[bb][rho]); });
+            });
+            wout.block(b, wt);
+            nr += wt * wt;
+        });
+        sfor<4>([&](auto r) { nr[int(r)] = sum_row16(nr[int(r)]); });
+        wout.norms(wi, nr);
+    }
+
+    // ------------------------------------------------------------ memory chain
+    // S K^ and S Phi of chunk cq (own blocks), before its write
+    __device__ __forceinline__ void s_products(const State &st, int cq, f4 (&sk)[BPW], f4 (&sq)[BPW]) const
+    {
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        const int sl = cq & 1;
+        const float *kb = L.kh[sl], *pb = L.ph[sl];
+        f4 ska[BPW][PA], sqa[BPW][PA];
+        sfor<BPW>([&](auto bb) { sfor<PA>([&](auto h) { ska[bb][h] = zero; sqa[bb][h] = zero; }); });
+        sfor<NB>([&](auto rho) {
+            constexpr int h = decltype(rho)::value % PA;
+            const f4 ak = ld4(&kb[n * LD + 16 * rho + 4 * g]);
+            const f4 ap = ld4(&pb[n * LD + 16 * rho + 4 * g]);
+            sfor<4>([&](auto r) {
+                sfor<BPW>([&](auto bb) {
+                    ska[bb][h] = mma(ak[int(r)], st[bb][rho][int(r)], ska[bb][h]);
+                    sqa[bb][h] = mma(ap[int(r)], st[bb][rho][int(r)], sqa[bb][h]);
+                });
+            });
+        });
+        sfor<BPW>([&](auto bb) {
+            sk[bb] = ska[bb][0];
+            sq[bb] = sqa[bb][0];
+            if constexpr (PA == 2) {
+                sk[bb] += ska[bb][1];
+                sq[bb] += sqa[bb][1];
+            }
+        });
+    }
+    // 1/|w_t| of chunk cq and this wave's partials of Alpha^'K^, Alpha^'Phi
+    // (from W in L.w and the |w|^2 partials in L.nrm)
+    __device__ __forceinline__ void s_grams(int cq, f4 &invn4)
+    {
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        const int sl = cq & 1;
+        float ns = L.nrm[0][n];
+        f4 ns4 = ld4(&L.nrm[0][4 * g]);
+        sfor<NA - 1>([&](auto w2) {
+            ns += L.nrm[w2 + 1][n];
+            ns4 += ld4(&L.nrm[w2 + 1][4 * g]);
+        });
+        const float invm = ns > 0.f ? rsqrtf(ns) : 0.f;   // 1 / |w_n|
+        sfor<4>([&](auto r) { invn4[int(r)] = ns4[int(r)] > 0.f ? rsqrtf(ns4[int(r)]) : 0.f; });
+        const float *kb = L.kh[sl], *pb = L.ph[sl];
+        f4 gn = zero, gq = zero;
+        sfor<BPW>([&](auto bb) {
+            const int b = wi * BPW + bb;
+            const f4 aw = ld4(&L.w[n * LD + 16 * b + 4 * g]) * invm;
+            const f4 bk = ld4(&kb[n * LD + 16 * b + 4 * g]);
+            const f4 bp = ld4(&pb[n * LD + 16 * b + 4 * g]);
+            gn = mma4(aw, bk, gn);
+            gq = mma4(aw, bp, gq);
+        });
+        sfor<4>([&](auto r) {
+            L.nq[wi][0][(4 * g + r) * LT + n] = gn[int(r)];
+            L.nq[wi][1][(4 * g + r) * LT + n] = gq[int(r)];
+        });
+    }
+    // (I + N)^-1, the errors E, the readout o of chunk cq and the write of S
+    // (W [i][token] of the chunk at wtb)
+    __device__ __forceinline__ void s_update(State &st, int cq, const f4 (&sk)[BPW], const f4 (&sq)[BPW],
+                                             f4 invn4, const Raw1<Tin> (&vraw)[BPW][4], const float *wtb)
+    {
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        const int sl = cq & 1;
+        const int t0 = cq * C;
+        // row n of -N (strictly upper) in every lane group; A operand of the
+        // readout: (Alpha^'Phi o Up)[4g+r][n]
+        float NNr[16];
+        f4 qa;
+        sfor<4>([&](auto q4) {
+            f4 a = ld4(&L.nq[0][0][n * LT + 4 * q4]);
+            sfor<NA - 1>([&](auto w2) { a += ld4(&L.nq[w2 + 1][0][n * LT + 4 * q4]); });
+            sfor<4>([&](auto r) {
+                constexpr int kx = 4 * decltype(q4)::value + decltype(r)::value;
+                NNr[kx] = n < kx ? -a[int(r)] : 0.f;
+            });
+        });
+        sfor<4>([&](auto r) {
+            float a = L.nq[0][1][(4 * g + r) * LT + n];
+            sfor<NA - 1>([&](auto w2) { a += L.nq[w2 + 1][1][(4 * g + r) * LT + n]; });
+            qa[int(r)] = 4 * g + r <= n ? a : 0.f;
+        });
+        // (I + N)^-1 by back substitution, four columns at a time: lane group
+        // g computes column 4c + g in X[c] (lane n = row n).
+        float X[4];
+        sfor<4>([&](auto c) { X[c] = n == 4 * c + g ? 1.f : 0.f; });
+        asm volatile(VLA_TINV_BLOCK
+                     : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3])
+                     : "v"(NNr[1]), "v"(NNr[2]), "v"(NNr[3]), "v"(NNr[4]), "v"(NNr[5]),
+                       "v"(NNr[6]), "v"(NNr[7]), "v"(NNr[8]), "v"(NNr[9]), "v"(NNr[10]),
+                       "v"(NNr[11]), "v"(NNr[12]), "v"(NNr[13]), "v"(NNr[14]), "v"(NNr[15]));
+        sfor<4>([&](auto c) { L.tit[wi][(4 * c + g) * LT + n] = X[c]; });
+        wave_lds_order();
+        const f4 ta = ld4(&L.tit[wi][n * LT + 4 * g]);   // (I+N)^-1 [4g+r][n]
+        const f4 rd = ld4(&L.rden[sl][4 * g]);
+        sfor<BPW>([&](auto bb) {
+            const int b = wi * BPW + bb;
+            f4 vm;                           // (V - S K^)' rows 4g+r
+            sfor<4>([&](auto r) {
+                vm[int(r)] = (t0 + 4 * g + r < T ? vraw[bb][r].get() : 0.f) - sk[bb][int(r)];
+            });
+            const f4 e = mma4(ta, vm, zero);      // E' = (I+N)^-T (V - S K^)'
+            const f4 ob = mma4(qa, e, sq[bb]);    // (S_t phi(q_t))'
+            sfor<4>([&](auto r) {
+                const int t = t0 + 4 * g + r;
+                if (t < T) o[(tok0 + t) * D + 16 * b + n] = ob[int(r)] * rd[int(r)];
+            });
+            const f4 es = e * invn4;              // rows of (E diag(1/|w|))'
+            f4 aw[NB];
+            sfor<NB>([&](auto rho) { aw[rho] = ld4(&wtb[(16 * rho + n) * LT + 4 * g]); });
+            sfor<4>([&](auto r) {                 // Ss <- Ss + W diag(1/|w|) E'
+                sfor<NB>([&](auto rho) { st[bb][rho] = mma(aw[rho][int(r)], es[int(r)], st[bb][rho]); });
+            });
+        });
+    }
+};
+
+}  // namespace chunk
+}  // namespace vla

@@ -31,8 +31,8 @@ __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : expf(
 
 hipError_t launch_forward_ref(const FwdArgs &a);
 
-// Register-resident kernel (d_h in {64, 96, 128}).
-bool fast_supported(int d);
-hipError_t launch_forward_fast(const FwdArgs &a);
+// Chunked matrix-core kernel (d_h in {64, 96, 128}).
+bool chunk_supported(int d);
+hipError_t launch_forward_chunk(const FwdArgs &a);
 
 }  // namespace vla

@@ -159,10 +159,10 @@ def test_shape_sweep_every_head(d, dtype, T):
         _check(name, g, ref[name])
 
 
-@pytest.mark.parametrize("T", [2, 30, 31, 32, 33, 63, 64, 65])
+@pytest.mark.parametrize("T", [2, 15, 16, 17, 31, 32, 33, 47, 48, 49, 64, 65])
 def test_tile_boundaries(T):
-    """Sequence lengths around the 32-token prologue tile (the memory chain and
-    the readout run two tokens behind the penalty chain)."""
+    """Sequence lengths around the 16-token chunks (a ragged last chunk, the
+    memory chain one chunk behind the penalty chain, two-slot staging)."""
     dev = _dev()
     cfg = gen.config(3).with_sizes(B=1, H=2, T=T)
     _say(f"tile boundary T={T}")
@@ -274,3 +274,53 @@ def test_run_to_run_bitwise_deterministic():
     b = _gpu_forward(cfg, x, dev)
     for ga, gb in zip(a, b):
         assert np.array_equal(ga, gb)
+
+
+# ---------------------------------------------------------------------------
+# The two-workgroup arrangement (one compute unit per chain, chunks handed over
+# through device memory) is selected with VLA_SPLIT=1 when the whole grid fits.
+
+
+@pytest.fixture
+def split_mode(monkeypatch):
+    monkeypatch.setenv("VLA_SPLIT", "1")
+
+
+@pytest.mark.parametrize("d,dtype,T", [(64, "bf16", 300), (64, "f32", 16), (96, "f32", 129),
+                                       (128, "bf16", 77), (128, "f32", 1)])
+def test_split_shapes_every_head(split_mode, d, dtype, T):
+    dev = _dev()
+    base = gen.config(3 if dtype == "bf16" else 2)
+    import dataclasses
+    cfg = dataclasses.replace(base, d=d).with_sizes(B=2, H=3, T=T)
+    _say(f"split d={d} {dtype} T={T}")
+    x = gen.make_inputs(cfg)
+    out = _gpu_forward(cfg, x, dev)
+    ref = oracle.forward(*(_f64(x[n], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+    for name, g in zip(("o", "S", "A", "zkey"), out):
+        _check(name, g, ref[name])
+
+
+def test_split_full_size_sampled_heads(split_mode):
+    dev = _dev()
+    cfg = gen.config(3)
+    _say(f"split {cfg.name} (full size)")
+    x = gen.make_inputs(cfg)
+    out = _gpu_forward(cfg, x, dev)
+    assert np.isfinite(out[0]).all()
+    _compare_heads(cfg, x, out, [(0, 0), (4, 9), (7, 15)])
+
+
+def test_split_matches_fused_bitwise(monkeypatch):
+    """Both arrangements run the same arithmetic in the same order."""
+    dev = _dev()
+    cfg = gen.config(3).with_sizes(B=2, H=4, T=200)
+    x = gen.make_inputs(cfg)
+    monkeypatch.setenv("VLA_SPLIT", "0")
+    a = _gpu_forward(cfg, x, dev)
+    monkeypatch.setenv("VLA_SPLIT", "1")
+    b = _gpu_forward(cfg, x, dev)
+    c = _gpu_forward(cfg, x, dev)
+    for ga, gb, gc in zip(a, b, c):
+        assert np.array_equal(ga, gb)
+        assert np.array_equal(gb, gc)
