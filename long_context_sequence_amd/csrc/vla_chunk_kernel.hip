@@ -14,20 +14,23 @@
 //   head (chunks produced, chunks consumed) written with agent-scope
 //   release/acquire.  The launch is cooperative, so all workgroups are resident
 //   and every wait ends; a bounded spin is kept as a guard all the same.
-//     penalty workgroup, chunk p:  [wait until slot p%RING is free]  Z0, Y0,
-//        Grams | barrier | factorise, update A, W' -> ring slot; stage chunk
-//        p+1 | barrier | publish p+1.
-//     memory workgroup, chunk q:   ring slot -> LDS, S K^, S Phi, key-sum prefix
-//        | barrier | publish consumed q+1; 1/|w|, Grams, readout denominators |
-//        barrier | (I+N)^-1, E, readout, update S; wait for chunk q+1; stage
-//        chunk q+1 | barrier.
+//     penalty workgroup, chunk p:  [wait until slot p%RING is free]  Z0,
+//        Grams; wait for this wave's stores of chunk p-1 | barrier | publish
+//        chunks < p; peek the consumed counter; stage chunk p+1, prefetch p+2;
+//        factorise, update A, W' -> ring slot | barrier.
+//     memory workgroup, chunk q:   publish consumed q+1 (its slot is in LDS);
+//        counter peek; S K^, S Phi, key-sum prefix | barrier | 1/|w|, Grams,
+//        readout denominators, wait until chunk q+1 is published | barrier |
+//        loads of slot q+1, stage q+1, prefetch q+2; (I+N)^-1, E, readout,
+//        update S; loads of V of q+1; slot q+1 -> LDS | barrier.
+//   Every wait on device memory finds its operations a segment old or more.
 //
 // fused (any grid size): one workgroup per head with both chains, NA waves
 //   each, so every SIMD holds a wave of each chain.  Period p has two segments
 //   separated by LDS barriers:
-//     segment 1:  penalty waves: Z0, Y0, Grams of chunk p.
-//                 memory waves:  S K^, S Phi, 1/|w|, Grams of chunk p-1; key-sum
-//                                prefix of chunk p.
+//     segment 1:  penalty waves: Z0, Y0, Grams of chunk p; key-sum prefix of
+//                                chunk p.
+//                 memory waves:  S K^, S Phi, 1/|w|, Grams of chunk p-1.
 //     segment 2:  penalty waves: factorise, update A, W of chunk p (into LDS).
 //                 memory waves:  (I+N)^-1, E, readout, update S for chunk p-1;
 //                                readout denominators of chunk p; staging of p+1.
@@ -42,7 +45,7 @@ namespace {
 
 using namespace chunk;
 
-constexpr int RING = 4;   // chunk slots per head between the two chains (power of 2)
+constexpr int RING = 8;   // chunk slots per head between the two chains (power of 2)
 
 // ---------------------------------------------------------------- fused kernel
 template <int D, typename Tin>
@@ -64,31 +67,41 @@ vla_fwd_fused(const Tin *__restrict__ q, const Tin *__restrict__ k,
     const size_t DD = (size_t)D * D;
     const int NC = (T + C - 1) / C;
 
-    Hd hd(L, q, k, v, u, o, T, eps, bh, tid & 63, awave ? w : w - NA, tid - 64 * NA, !awave);
+    // memory waves stage the inputs; penalty-wave threads 0..D-1 own the key sums
+    Hd hd(L, q, k, v, u, o, T, eps, bh, tid & 63, awave ? w : w - NA, tid - 64 * NA, !awave,
+          awave ? tid : -1);
     typename Hd::State st;
+    if (hd.kcol >= 0 && zk0) hd.zk_run = zk0[bh * D + hd.kcol];
     if (awave) {
         hd.load_state(st, A0 ? A0 + bh * DD : nullptr, 1.f / lambda0);
     } else {
         hd.load_state(st, S0 ? S0 + bh * DD : nullptr, 0.f);
-        if (hd.ts < D && zk0) hd.zk_run = zk0[bh * D + hd.ts];
         if (NC > 0) {
             hd.template prefetch<true, true>(0);
             hd.template stage1<true, true>(0);
             hd.template prefetch<true, true>(1);
         }
     }
+    vmem_drain();
     __syncthreads();
 
     if (awave) {
-        f4 y[BPW];
         WToLds<D> wl{L, 0, hd.g, hd.n};
         for (int p = 0; p <= NC; ++p) {
-            if (p < NC) hd.a_products(st, p, y);
+            hd.pp = p;
+            VLA_PROBE(p, 0);
+            if (p < NC) {
+                hd.a_products(st, p);
+                hd.stage2();
+            }
+            VLA_PROBE(p, 1);
             lds_barrier();
+            VLA_PROBE(p, 2);
             if (p < NC) {
                 wl.sp = p & 1;
-                hd.a_update(st, y, wl);
+                hd.a_update(st, p, wl);
             }
+            VLA_PROBE(p, 3);
             lds_barrier();
         }
     } else {
@@ -96,13 +109,17 @@ vla_fwd_fused(const Tin *__restrict__ q, const Tin *__restrict__ k,
         Raw1<Tin> vraw[BPW][4];
         for (int p = 0; p <= NC; ++p) {
             const int cq = p - 1;   // chunk of this period's memory-chain work
+            hd.pp = p;
+            VLA_PROBE(p, 0);
             if (p >= 1) {
                 hd.s_products(st, cq, sk, sq);
                 hd.s_grams(cq, invn4);
             }
-            if (p < NC) hd.stage2();
+            VLA_PROBE(p, 1);
             lds_barrier();
+            VLA_PROBE(p, 2);
             if (p >= 1) hd.s_update(st, cq, sk, sq, invn4, vraw, L.wt[cq & 1]);
+            VLA_PROBE(p, 10);
             if (p < NC) {
                 hd.stage3(p);
                 hd.load_v(p, vraw);   // used in the next period
@@ -111,13 +128,15 @@ vla_fwd_fused(const Tin *__restrict__ q, const Tin *__restrict__ k,
                 hd.template stage1<true, true>(p + 1);
                 hd.template prefetch<true, true>(p + 2);
             }
+            VLA_PROBE(p, 3);
             lds_barrier();
         }
     }
 
     float *const out = awave ? A_out : S_out;
     if (out) hd.store_state(st, out + bh * DD);
-    if (!awave && hd.ts < D && zk_out) zk_out[bh * D + hd.ts] = hd.zk_run;
+    if (hd.kcol >= 0 && zk_out) zk_out[bh * D + hd.kcol] = hd.zk_run;
+    VLA_PROBE_FLUSH();
 }
 
 // ---------------------------------------------------------------- split kernel
@@ -126,11 +145,18 @@ vla_fwd_fused(const Tin *__restrict__ q, const Tin *__restrict__ k,
 // after about a million polls; once one has given up (only possible if the two
 // workgroups were not resident together), the workgroup stops waiting, so the
 // launch still ends.
-__device__ __forceinline__ void wait_at_least(const uint64_t *flag, uint64_t want, bool &alive)
+__device__ __forceinline__ uint64_t peek(const uint64_t *flag)
 {
-    if (alive) {
+    return __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// `seen` is an earlier peek of the counter (issued ahead so that its latency is
+// hidden); polls again only if it was not yet enough.
+__device__ __forceinline__ void wait_from(const uint64_t *flag, uint64_t want, uint64_t seen,
+                                          bool &alive)
+{
+    if (alive && seen < want) {
         int it = 0;
-        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+        while (peek(flag) < want) {
             if (++it == (1 << 20)) {
                 alive = false;
                 break;
@@ -139,6 +165,10 @@ __device__ __forceinline__ void wait_at_least(const uint64_t *flag, uint64_t wan
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+__device__ __forceinline__ void wait_at_least(const uint64_t *flag, uint64_t want, bool &alive)
+{
+    wait_from(flag, want, 0, alive);
 }
 __device__ __forceinline__ void post(uint64_t *flag, uint64_t val)
 {
@@ -182,7 +212,7 @@ vla_fwd_split(const Tin *__restrict__ q, const Tin *__restrict__ k,
     const uint64_t tag = epoch << 32;
     bool alive = true;   // waits of thread 0 still honoured
 
-    Hd hd(L, q, k, v, u, o, T, eps, head, tid & 63, w, tid, true);
+    Hd hd(L, q, k, v, u, o, T, eps, head, tid & 63, w, tid, true, achain ? -1 : tid);
     typename Hd::State st;
 
     if (achain) {
@@ -192,25 +222,60 @@ vla_fwd_split(const Tin *__restrict__ q, const Tin *__restrict__ k,
             hd.template stage1<false, true>(0);
             hd.template prefetch<false, true>(1);
         }
+        vmem_drain();
         __syncthreads();
-        f4 y[BPW];
+        uint64_t seen_c = 0;   // consumed counter peeked one segment ahead (thread 0)
         for (int p = 0; p < NC; ++p) {
-            if (tid == 0 && p >= RING) wait_at_least(consumed, tag | (uint64_t)(p - RING + 1), alive);
-            hd.a_products(st, p, y);
+            hd.pp = p;
+            VLA_PROBE(p, 0);
+            if (tid == 0 && p >= RING) wait_from(consumed, tag | (uint64_t)(p - RING + 1), seen_c, alive);
+            VLA_PROBE(p, 10);
+            hd.a_products(st, p);
+            VLA_PROBE(p, 11);
+            // this wave's slot stores of chunk p-1 (the youngest of its memory
+            // operations, issued a segment ago) are done
+            vmem_drain();
+            VLA_PROBE(p, 1);
             lds_barrier();
-            hd.a_update(st, y, WToGlobal<D>{ringh + (p & (RING - 1)) * WSLOT, hd.g, hd.n});
+            if (tid == 0 && p > 0) post(produced, tag | (uint64_t)p);
+            VLA_PROBE(p, 2);
+            if (tid == 0) seen_c = peek(consumed);
             if (p + 1 < NC) hd.template stage1<false, true>(p + 1);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's slot stores are done
-            lds_barrier();
-            if (tid == 0) post(produced, tag | (uint64_t)(p + 1));
             if (p + 2 < NC) hd.template prefetch<false, true>(p + 2);
+            VLA_PROBE(p, 12);
+            hd.a_update(st, p, WToGlobal<D>{ringh + (p & (RING - 1)) * WSLOT, hd.g, hd.n});
+            VLA_PROBE(p, 3);
+            lds_barrier();
         }
+        vmem_drain();
+        __syncthreads();
+        if (tid == 0 && NC > 0) post(produced, tag | (uint64_t)NC);
         if (A_out) hd.store_state(st, A_out + head * DD);
     } else {
         hd.load_state(st, S0 ? S0 + head * DD : nullptr, 0.f);
-        if (tid < D && zk0) hd.zk_run = zk0[head * D + tid];
+        if (hd.kcol >= 0 && zk0) hd.zk_run = zk0[head * D + hd.kcol];
         f4 sk[BPW], sq[BPW], invn4 = {0.f, 0.f, 0.f, 0.f};
-        Raw1<Tin> vraw[BPW][4];
+        Raw1<Tin> vraw[BPW][4];      // V' of the chunk in flight
+        // thread tid holds entries e = tid + 64 NA j (j < BPW) of a slot's W' (4 D
+        // float4s) and, for tid < 4 NA, one float4 of the |w|^2 partials
+        f4 wreg[BPW], nreg = {0.f, 0.f, 0.f, 0.f};
+        auto slot_load = [&](int cq) {
+            const float *slot = ringh + (cq & (RING - 1)) * WSLOT;
+            sfor<BPW>([&](auto j) {
+                const int e = tid + 64 * NA * j;
+                wreg[j] = ld4(&slot[16 * (e >> 2) + 4 * (e & 3)]);
+            });
+            if (tid < 4 * NA) nreg = ld4(&slot[16 * D + 4 * tid]);
+        };
+        // W' [i][token] and the |w|^2 partials of chunk cq from registers into LDS
+        auto slot_store = [&](int cq) {
+            sfor<BPW>([&](auto j) {
+                const int e = tid + 64 * NA * j, i = e >> 2, c4 = 4 * (e & 3);
+                st4(&L.wt[cq & 1][i * LT + c4], wreg[j]);
+                sfor<4>([&](auto r) { L.w[(c4 + r) * LD + i] = wreg[j][int(r)]; });
+            });
+            if (tid < 4 * NA) st4(&L.nrm[tid >> 2][4 * (tid & 3)], nreg);
+        };
         if (NC > 0) {
             if (tid == 0) wait_at_least(produced, tag | 1u, alive);
             hd.template prefetch<true, false>(0);
@@ -219,38 +284,51 @@ vla_fwd_split(const Tin *__restrict__ q, const Tin *__restrict__ k,
             hd.template prefetch<true, false>(1);
         }
         __syncthreads();
+        if (NC > 0) {
+            slot_load(0);
+            slot_store(0);
+        }
+        vmem_drain();
+        __syncthreads();
         for (int cq = 0; cq < NC; ++cq) {
             const int sl = cq & 1;
-            // W' [i][token] and the |w|^2 partials of chunk cq from its slot
-            {
-                const float *slot = ringh + (cq & (RING - 1)) * WSLOT;
-                for (int e = tid; e < 4 * D; e += 64 * NA) {
-                    const int i = e >> 2, c4 = 4 * (e & 3);
-                    const f4 x = ld4(&slot[16 * i + c4]);
-                    st4(&L.wt[sl][i * LT + c4], x);
-                    sfor<4>([&](auto r) { L.w[(c4 + r) * LD + i] = x[int(r)]; });
-                }
-                if (tid < 4 * NA) st4(&L.nrm[tid >> 2][4 * (tid & 3)], ld4(&slot[16 * D + 4 * tid]));
-            }
+            hd.pp = cq;
+            VLA_PROBE(cq, 0);
+            // the slot of chunk cq is in LDS since the last barrier
+            if (tid == 0) post_relaxed(consumed, tag | (uint64_t)(cq + 1));
+            const uint64_t seen = tid == 0 ? peek(produced) : 0;
+            VLA_PROBE(cq, 10);
             hd.s_products(st, cq, sk, sq);
             hd.stage2();
+            VLA_PROBE(cq, 1);
             lds_barrier();
-            if (tid == 0) post_relaxed(consumed, tag | (uint64_t)(cq + 1));
+            VLA_PROBE(cq, 2);
             hd.s_grams(cq, invn4);
             hd.stage3(cq);
+            VLA_PROBE(cq, 11);
+            if (tid == 0 && cq + 1 < NC) wait_from(produced, tag | (uint64_t)(cq + 2), seen, alive);
+            VLA_PROBE(cq, 12);
             lds_barrier();
-            hd.s_update(st, cq, sk, sq, invn4, vraw, L.wt[sl]);
+            VLA_PROBE(cq, 13);
+            // loads for the next period first, so that they are old when used
             if (cq + 1 < NC) {
-                if (tid == 0) wait_at_least(produced, tag | (uint64_t)(cq + 2), alive);
-                hd.load_v(cq + 1, vraw);
+                slot_load(cq + 1);
                 hd.template stage1<true, false>(cq + 1);
                 hd.template prefetch<true, false>(cq + 2);
             }
+            hd.s_update(st, cq, sk, sq, invn4, vraw, L.wt[sl]);
+            VLA_PROBE(cq, 14);
+            if (cq + 1 < NC) {
+                hd.load_v(cq + 1, vraw);
+                slot_store(cq + 1);
+            }
+            VLA_PROBE(cq, 3);
             lds_barrier();
         }
         if (S_out) hd.store_state(st, S_out + head * DD);
-        if (tid < D && zk_out) zk_out[head * D + tid] = hd.zk_run;
+        if (hd.kcol >= 0 && zk_out) zk_out[head * D + hd.kcol] = hd.zk_run;
     }
+    VLA_PROBE_FLUSH();
 }
 
 // ---------------------------------------------------------------- host side

@@ -45,6 +45,16 @@
 #include "vla_common.h"
 #include "vla_dpp_blocks.h"
 
+// Timing probes: VLA_PROBE(period, point) and VLA_PROBE_FLUSH() (at kernel
+// exit) expand to nothing unless a timing build defines them before including
+// this header.
+#ifndef VLA_PROBE
+#define VLA_PROBE(period, point)
+#endif
+#ifndef VLA_PROBE_FLUSH
+#define VLA_PROBE_FLUSH()
+#endif
+
 namespace vla {
 namespace chunk {
 
@@ -66,20 +76,33 @@ __device__ __forceinline__ f4 mma(float a, float b, f4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Four k-steps of a 16 x 16 product, c + sum_s A_s B_s, split over two
-// accumulators so that consecutive matrix-core operations are independent.
+// Four k-steps of a 16 x 16 product, c + sum_s A_s B_s (dependent accumulation
+// into one register set issues back to back on gfx950).
 __device__ __forceinline__ f4 mma4(const float (&a)[4], const float (&b)[4], f4 c)
 {
-    f4 c1 = mma(a[1], b[1], (f4){0.f, 0.f, 0.f, 0.f});
     c = mma(a[0], b[0], c);
-    c1 = mma(a[3], b[3], c1);
+    c = mma(a[1], b[1], c);
     c = mma(a[2], b[2], c);
-    return c + c1;
+    return mma(a[3], b[3], c);
 }
 __device__ __forceinline__ f4 mma4(f4 a, f4 b, f4 c)
 {
-    const float aa[4] = {a[0], a[1], a[2], a[3]}, ba[4] = {b[0], b[1], b[2], b[3]};
-    return mma4(aa, ba, c);
+    c = mma(a[0], b[0], c);
+    c = mma(a[1], b[1], c);
+    c = mma(a[2], b[2], c);
+    return mma(a[3], b[3], c);
+}
+
+// 1 / x[lane J of this 16-lane row], after the two wait states a VALU write of x
+// needs before a DPP read (x may come straight from an inline-asm FMA).
+template <int J>
+__device__ __forceinline__ float rcp_bcast(float x)
+{
+    float r;
+    asm volatile("s_nop 1\n\tv_rcp_f32_dpp %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
+                 : "=v"(r)
+                 : "v"(x), "n"(J));
+    return r;
 }
 
 // 16-byte loads and stores (LDS or global)
@@ -102,21 +125,16 @@ __device__ __forceinline__ float sum_row16(float x)
     return x;
 }
 
-// x[lane J of this 16-lane row], after the two wait states a VALU write of x
-// needs before a DPP read (x may come straight from an inline-asm FMA).
-template <int J>
-__device__ __forceinline__ float bcast(float x)
-{
-    float r;
-    asm volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
-                 : "=v"(r)
-                 : "v"(x), "n"(J));
-    return r;
-}
-
 // Compiler-only ordering point between LDS writes and reads of other lanes of
 // the same wave (LDS executes one wave's instructions in order).
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory"); }
+
+// Wait until this wave's outstanding device-memory operations are done, as a
+// real s_waitcnt (vmcnt 0, expcnt and lgkmcnt untouched) that the compiler's
+// wait-count tracking sees: after it, registers loaded before a loop no longer
+// look pending inside the loop, where every use would otherwise wait for all
+// operations issued in the previous iteration.
+__device__ __forceinline__ void vmem_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Workgroup barrier for LDS traffic only.  Unlike __syncthreads() it does not
 // wait for outstanding global loads and stores, so prefetches into registers
@@ -170,7 +188,6 @@ struct Cfg {
     static constexpr int NB = D / 16;              // 16-column blocks of a state
     static constexpr int NA = NB % 4 == 0 ? 4 : NB;// waves per chain
     static constexpr int BPW = NB / NA;            // column blocks per wave
-    static constexpr int PA = BPW == 1 ? 2 : 1;    // partial accumulators per d x d product
     static constexpr int LD = D + 4;               // row stride of [token][i] arrays
     static constexpr int LT = C + 4;               // row stride of [i][token] and C x C arrays
     static constexpr int CPT = D / 16;             // staged columns per thread (16 per token)
@@ -187,11 +204,10 @@ struct Lds {
     float zk[C * LD];        // phi(k), then the key sum, of the chunk being staged
     float rden[2][C];        // 1 / max(phi(q)' zkey, eps)
     float z0[C * LD];        // Z0 [token][i]
-    float y0[C * LD];        // Y0 [token][i]
     float z0t[D * LT];       // Z0 [i][token]
     float w[C * LD];         // W [token][i]
     float wt[2][D * LT];     // W [i][token], by chunk parity
-    float gp[NA][2][C * LT]; // per A-wave: I + U^'Z0 (wave 0) or U^'Z0, and U^'Y0
+    float gp[NA][2][C * LT]; // per A-wave: I + U^'Z0 (wave 0) or U^'Z0, and Z0'K^
     float nrm[NA][C];        // per A-wave: partial |w_t|^2
     float nq[NA][2][C * LT]; // per S-wave: Alpha^'K^, Alpha^'Phi
     float lit[NA][C * LT];   // per A-wave: L^-1 transposed
@@ -234,7 +250,7 @@ struct WToGlobal {
 template <int D, typename Tin>
 struct Head {
     using Cf = Cfg<D>;
-    static constexpr int C = Cf::C, NB = Cf::NB, NA = Cf::NA, BPW = Cf::BPW, PA = Cf::PA;
+    static constexpr int C = Cf::C, NB = Cf::NB, NA = Cf::NA, BPW = Cf::BPW;
     static constexpr int LD = Cf::LD, LT = Cf::LT, CPT = Cf::CPT;
     typedef f4 State[BPW][NB];
 
@@ -245,19 +261,20 @@ struct Head {
     float eps;
     size_t tok0;     // first token row of the head
     int g, n, wi;    // lane group, lane in group, wave index within its chain
-    // staging: 16 threads per token (one DPP row), token tl, columns [cc*CPT, +CPT);
-    // thread ts < D also owns key-sum column ts
+    // staging: 16 threads per token (one DPP row), token tl, columns [cc*CPT, +CPT)
     int ts, tl, cc;
     bool pthr;
-    float zk_run = 0.f, zk_cmp = 0.f;   // Kahan-compensated key sum of column ts
+    int kcol;                           // key-sum column of this thread, or -1
+    float zk_run = 0.f, zk_cmp = 0.f;   // its Kahan-compensated key sum
+    int pp = 0;                         // current period (timing probes only)
     RawVec<Tin, CPT> rq, rk, ru;
 
     __device__ __forceinline__ Head(Lds<D> &L_, const Tin *q_, const Tin *k_, const Tin *v_,
                                     const Tin *u_, float *o_, int T_, float eps_, size_t bh,
-                                    int lane, int wi_, int ts_, bool stager)
+                                    int lane, int wi_, int ts_, bool stager, int kcol_)
         : L(L_), q(q_), k(k_), v(v_), u(u_), o(o_), T(T_), eps(eps_), tok0(bh * (size_t)T_),
           g(lane >> 4), n(lane & 15), wi(wi_), ts(ts_), tl((ts_ >> 4) & (C - 1)), cc(ts_ & 15),
-          pthr(stager && ts_ < 16 * C)
+          pthr(stager && ts_ >= 0 && ts_ < 16 * C), kcol(kcol_ >= 0 && kcol_ < D ? kcol_ : -1)
     {
     }
 
@@ -335,15 +352,15 @@ struct Head {
     // compensated sum of the earlier chunks
     __device__ __forceinline__ void stage2()
     {
-        if (ts >= D) return;
+        if (kcol < 0) return;
         float f[C];
 #pragma unroll
-        for (int tt = 0; tt < C; ++tt) f[tt] = L.zk[tt * LD + ts];
+        for (int tt = 0; tt < C; ++tt) f[tt] = L.zk[tt * LD + kcol];
         float loc = 0.f;
 #pragma unroll
         for (int tt = 0; tt < C; ++tt) {
             loc += f[tt];
-            L.zk[tt * LD + ts] = zk_run + loc;
+            L.zk[tt * LD + kcol] = zk_run + loc;
         }
         const float yk = loc - zk_cmp;
         const float tsum = zk_run + yk;
@@ -375,52 +392,37 @@ struct Head {
     }
 
     // ------------------------------------------------------------ penalty chain
-    // Z0' and Y0' of the own blocks (y kept for the second half), Z0 and Y0 into
-    // LDS, and this wave's partials of U^'Z0 and U^'Y0 (rows i of its blocks).
-    __device__ __forceinline__ void a_products(const State &st, int p, f4 (&y)[BPW])
+    // Z0' of the own blocks, Z0 into LDS, and this wave's partials (rows i of its
+    // blocks) of U^'Z0 and of U^'A K^ = Z0'K^ (A symmetric), so that the product
+    // A K^ is off the path to the factorisation.
+    __device__ __forceinline__ void a_products(const State &st, int p)
     {
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
         const int sp = p & 1;
         const float *ub = L.uh[sp], *kb = L.kh[sp];
-        f4 z[BPW], za[BPW][PA], ya[BPW][PA];
-        sfor<BPW>([&](auto bb) { sfor<PA>([&](auto h) { za[bb][h] = zero; ya[bb][h] = zero; }); });
+        f4 z[BPW];
+        sfor<BPW>([&](auto bb) { z[bb] = zero; });
         sfor<NB>([&](auto rho) {
-            constexpr int h = decltype(rho)::value % PA;
             const f4 au = ld4(&ub[n * LD + 16 * rho + 4 * g]);
-            const f4 ak = ld4(&kb[n * LD + 16 * rho + 4 * g]);
             sfor<4>([&](auto r) {
-                sfor<BPW>([&](auto bb) {
-                    za[bb][h] = mma(au[int(r)], st[bb][rho][int(r)], za[bb][h]);
-                    ya[bb][h] = mma(ak[int(r)], st[bb][rho][int(r)], ya[bb][h]);
-                });
+                sfor<BPW>([&](auto bb) { z[bb] = mma(au[int(r)], st[bb][rho][int(r)], z[bb]); });
             });
         });
-        sfor<BPW>([&](auto bb) {
-            z[bb] = za[bb][0];
-            y[bb] = ya[bb][0];
-            if constexpr (PA == 2) {
-                z[bb] += za[bb][1];
-                y[bb] += ya[bb][1];
-            }
-        });
-        // z[bb] register r = Z0[16b + n][4g + r]; same for y
+        // z[bb] register r = Z0[16b + n][4g + r]
         sfor<BPW>([&](auto bb) {
             const int b = wi * BPW + bb;
-            sfor<4>([&](auto r) {
-                L.z0[(4 * g + r) * LD + 16 * b + n] = z[bb][int(r)];
-                L.y0[(4 * g + r) * LD + 16 * b + n] = y[bb][int(r)];
-            });
+            sfor<4>([&](auto r) { L.z0[(4 * g + r) * LD + 16 * b + n] = z[bb][int(r)]; });
             st4(&L.z0t[(16 * b + n) * LT + 4 * g], z[bb]);
         });
         wave_lds_order();
         f4 gu = zero, gk = zero;
         sfor<BPW>([&](auto bb) {
             const int b = wi * BPW + bb;
-            const f4 au = ld4(&ub[n * LD + 16 * b + 4 * g]);
-            const f4 bz = ld4(&L.z0[n * LD + 16 * b + 4 * g]);
-            const f4 by = ld4(&L.y0[n * LD + 16 * b + 4 * g]);
+            const f4 au = ld4(&ub[n * LD + 16 * b + 4 * g]);    // U^_n[16b + 4g + r]
+            const f4 bz = ld4(&L.z0[n * LD + 16 * b + 4 * g]);  // Z0_n[16b + 4g + r]
+            const f4 bk = ld4(&kb[n * LD + 16 * b + 4 * g]);    // K^_n[16b + 4g + r]
             gu = mma4(au, bz, gu);
-            gk = mma4(au, by, gk);
+            gk = mma4(bz, bk, gk);
         });
         if (wi == 0) sfor<4>([&](auto r) { gu[int(r)] += 4 * g + r == n ? 1.f : 0.f; });
         sfor<4>([&](auto r) {
@@ -430,37 +432,69 @@ struct Head {
     }
 
     // Factorise I + G, downdate the own blocks of As, and hand W' and the |w|^2
-    // partials of the chunk to `wout`.
+    // partials of the chunk to `wout`.  The product Y0' = (A K^)' with the state
+    // before the downdate is issued between the factorisation steps.
     template <class WOut>
-    __device__ __forceinline__ void a_update(State &st, const f4 (&y)[BPW], WOut &&wout)
+    __device__ __forceinline__ void a_update(State &st, int p, WOut &&wout)
     {
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
-        // row n of M = I + G in every lane group; B operand of U^'Y0
+        constexpr int KS = 4 * NB;   // k-steps of the Y0 product
+        const float *kb = L.kh[p & 1];
+        f4 ak[NB], y[BPW];
+        sfor<NB>([&](auto rho) { ak[rho] = ld4(&kb[n * LD + 16 * rho + 4 * g]); });
+        sfor<BPW>([&](auto bb) { y[bb] = zero; });
+        // M = I + G summed over the waves' partials in accumulator layout (entry
+        // [4g+r][n]), then row n of M in every lane group through this wave's LDS
+        // scratch; B operand of U^'Y0
         float Mr[16], gub[4];
-        sfor<4>([&](auto q4) {
-            f4 a = ld4(&L.gp[0][0][n * LT + 4 * q4]);
-            sfor<NA - 1>([&](auto w2) { a += ld4(&L.gp[w2 + 1][0][n * LT + 4 * q4]); });
-            sfor<4>([&](auto r) { Mr[4 * q4 + r] = a[int(r)]; });
+        sfor<4>([&](auto r) {
+            float a = L.gp[0][0][(4 * g + r) * LT + n];
+            sfor<NA - 1>([&](auto w2) { a += L.gp[w2 + 1][0][(4 * g + r) * LT + n]; });
+            L.lit[wi][(4 * g + r) * LT + n] = a;
         });
         sfor<4>([&](auto c) {
             float a = L.gp[0][1][(4 * c + g) * LT + n];
             sfor<NA - 1>([&](auto w2) { a += L.gp[w2 + 1][1][(4 * c + g) * LT + n]; });
             gub[c] = a;
         });
-        // LDL' (column by column): lane n holds row n.  LDr[j] = L[n][j] d_j
-        // (d_j in lane j), NLr[j] = -L[n][j] for n > j, 0 otherwise.
+        wave_lds_order();
+        sfor<4>([&](auto q4) {
+            const f4 a = ld4(&L.lit[wi][n * LT + 4 * q4]);
+            sfor<4>([&](auto r) { Mr[4 * q4 + r] = a[int(r)]; });
+        });
+        wave_lds_order();
+        VLA_PROBE(pp, 5);
+        // LDL' (column by column, Crout order): lane n holds row n.  LDr[j] =
+        // L[n][j] d_j (d_j in lane j), NLr[j] = -L[n][j] for n > j, 0 otherwise;
+        // 1/d_j to LDS.  Column j+1's terms k < j are issued around the inversion
+        // of pivot j (software pipelining); only its k = j term waits for it.
         float LDr[16], NLr[16];
-        float invd = 0.f;   // 1 / d_n
+        float ca = Mr[0], cb = 0.f;   // accumulators of the current column
         sfor<16>([&](auto jj) {
             constexpr int j = decltype(jj)::value;
-            float acc = Mr[j];
-            if constexpr (j > 0) ldl_block<j, 0, (j < 8 ? j : 8)>(acc, LDr, NLr);
-            if constexpr (j > 8) ldl_block<j, 8, j - 8>(acc, LDr, NLr);
-            const float inv = __builtin_amdgcn_rcpf(bcast<j>(acc));
+            if constexpr (j > 0) ldl_block<j, j - 1, 1>(ca, LDr, NLr);
+            const float acc = ca + cb;
+            const float inv = rcp_bcast<j>(acc);
+            // column j+1's terms k < j: two while 1/d_j is in flight, the rest
+            // after NLr[j] is formed
+            constexpr int E = j, E1 = E < 2 ? E : 2;
+            float na = 0.f, nb = 0.f;
+            if constexpr (j + 1 < 16) {
+                na = Mr[j + 1];
+                if constexpr (E1 > 0) ldl_early<j + 1, 0, E1>(na, nb, LDr, NLr);
+            }
             LDr[j] = acc;
             NLr[j] = n > j ? -(acc * inv) : 0.f;
-            invd = n == j ? inv : invd;
+            if (g == 0 && n == 0) L.inv[wi][j] = inv;
+            if constexpr (j + 1 < 16 && E > E1) ldl_early<j + 1, E1, E - E1>(na, nb, LDr, NLr);
+            ca = na;
+            cb = nb;
+            sfor<(j + 1) * KS / 16 - j * KS / 16>([&](auto kk) {   // a share of Y0'
+                constexpr int ks = j * KS / 16 + decltype(kk)::value;
+                sfor<BPW>([&](auto bb) { y[bb] = mma(ak[ks / 4][ks % 4], st[bb][ks / 4][ks % 4], y[bb]); });
+            });
         });
+        VLA_PROBE(pp, 6);
         // L^-1 by forward substitution, four columns at a time: lane group g
         // computes column 4c + g in X[c] (lane n = row n).
         float X[4];
@@ -470,16 +504,15 @@ struct Head {
                      : "v"(NLr[0]), "v"(NLr[1]), "v"(NLr[2]), "v"(NLr[3]), "v"(NLr[4]),
                        "v"(NLr[5]), "v"(NLr[6]), "v"(NLr[7]), "v"(NLr[8]), "v"(NLr[9]),
                        "v"(NLr[10]), "v"(NLr[11]), "v"(NLr[12]), "v"(NLr[13]), "v"(NLr[14]));
-        float DX[4];
-        sfor<4>([&](auto c) { DX[c] = X[c] * invd; });
-        if (g == 0) L.inv[wi][n] = invd;
+        VLA_PROBE(pp, 7);
         sfor<4>([&](auto c) { L.lit[wi][(4 * c + g) * LT + n] = X[c]; });
         wave_lds_order();
         const f4 inv4 = ld4(&L.inv[wi][4 * g]);        // 1 / d_{4g+r}
         const f4 lit = ld4(&L.lit[wi][n * LT + 4 * g]);  // L^-1 [4g+r][n]
         // -(D^-1 L^-1 U^'Y0 o Up): A operand of W'
-        f4 hm = mma4(DX, gub, zero);
-        sfor<4>([&](auto r) { hm[int(r)] = 4 * g + r <= n ? -hm[int(r)] : 0.f; });
+        f4 hm = mma4(X, gub, zero);
+        sfor<4>([&](auto r) { hm[int(r)] = 4 * g + r <= n ? -(hm[int(r)] * inv4[int(r)]) : 0.f; });
+        VLA_PROBE(pp, 8);
         f4 nr = zero;
         sfor<BPW>([&](auto bb) {
             const int b = wi * BPW + bb;
@@ -499,6 +532,7 @@ struct Head {
             wout.block(b, wt);
             nr += wt * wt;
         });
+        VLA_PROBE(pp, 9);
         sfor<4>([&](auto r) { nr[int(r)] = sum_row16(nr[int(r)]); });
         wout.norms(wi, nr);
     }
@@ -510,26 +544,16 @@ struct Head {
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
         const int sl = cq & 1;
         const float *kb = L.kh[sl], *pb = L.ph[sl];
-        f4 ska[BPW][PA], sqa[BPW][PA];
-        sfor<BPW>([&](auto bb) { sfor<PA>([&](auto h) { ska[bb][h] = zero; sqa[bb][h] = zero; }); });
+        sfor<BPW>([&](auto bb) { sk[bb] = zero; sq[bb] = zero; });
         sfor<NB>([&](auto rho) {
-            constexpr int h = decltype(rho)::value % PA;
             const f4 ak = ld4(&kb[n * LD + 16 * rho + 4 * g]);
             const f4 ap = ld4(&pb[n * LD + 16 * rho + 4 * g]);
             sfor<4>([&](auto r) {
                 sfor<BPW>([&](auto bb) {
-                    ska[bb][h] = mma(ak[int(r)], st[bb][rho][int(r)], ska[bb][h]);
-                    sqa[bb][h] = mma(ap[int(r)], st[bb][rho][int(r)], sqa[bb][h]);
+                    sk[bb] = mma(ak[int(r)], st[bb][rho][int(r)], sk[bb]);
+                    sq[bb] = mma(ap[int(r)], st[bb][rho][int(r)], sq[bb]);
                 });
             });
-        });
-        sfor<BPW>([&](auto bb) {
-            sk[bb] = ska[bb][0];
-            sq[bb] = sqa[bb][0];
-            if constexpr (PA == 2) {
-                sk[bb] += ska[bb][1];
-                sq[bb] += sqa[bb][1];
-            }
         });
     }
     // 1/|w_t| of chunk cq and this wave's partials of Alpha^'K^, Alpha^'Phi
@@ -573,19 +597,23 @@ struct Head {
         // readout: (Alpha^'Phi o Up)[4g+r][n]
         float NNr[16];
         f4 qa;
-        sfor<4>([&](auto q4) {
-            f4 a = ld4(&L.nq[0][0][n * LT + 4 * q4]);
-            sfor<NA - 1>([&](auto w2) { a += ld4(&L.nq[w2 + 1][0][n * LT + 4 * q4]); });
-            sfor<4>([&](auto r) {
-                constexpr int kx = 4 * decltype(q4)::value + decltype(r)::value;
-                NNr[kx] = n < kx ? -a[int(r)] : 0.f;
-            });
+        sfor<4>([&](auto r) {   // -N[4g+r][n] (strictly upper), then rows through LDS
+            float a = L.nq[0][0][(4 * g + r) * LT + n];
+            sfor<NA - 1>([&](auto w2) { a += L.nq[w2 + 1][0][(4 * g + r) * LT + n]; });
+            L.tit[wi][(4 * g + r) * LT + n] = 4 * g + r < n ? -a : 0.f;
         });
+        wave_lds_order();
+        sfor<4>([&](auto q4) {
+            const f4 a = ld4(&L.tit[wi][n * LT + 4 * q4]);
+            sfor<4>([&](auto r) { NNr[4 * q4 + r] = a[int(r)]; });
+        });
+        wave_lds_order();
         sfor<4>([&](auto r) {
             float a = L.nq[0][1][(4 * g + r) * LT + n];
             sfor<NA - 1>([&](auto w2) { a += L.nq[w2 + 1][1][(4 * g + r) * LT + n]; });
             qa[int(r)] = 4 * g + r <= n ? a : 0.f;
         });
+        VLA_PROBE(pp, 5);
         // (I + N)^-1 by back substitution, four columns at a time: lane group
         // g computes column 4c + g in X[c] (lane n = row n).
         float X[4];
@@ -595,6 +623,7 @@ struct Head {
                      : "v"(NNr[1]), "v"(NNr[2]), "v"(NNr[3]), "v"(NNr[4]), "v"(NNr[5]),
                        "v"(NNr[6]), "v"(NNr[7]), "v"(NNr[8]), "v"(NNr[9]), "v"(NNr[10]),
                        "v"(NNr[11]), "v"(NNr[12]), "v"(NNr[13]), "v"(NNr[14]), "v"(NNr[15]));
+        VLA_PROBE(pp, 6);
         sfor<4>([&](auto c) { L.tit[wi][(4 * c + g) * LT + n] = X[c]; });
         wave_lds_order();
         const f4 ta = ld4(&L.tit[wi][n * LT + 4 * g]);   // (I+N)^-1 [4g+r][n]

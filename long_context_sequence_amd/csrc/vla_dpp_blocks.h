@@ -160,3 +160,151 @@ __device__ __forceinline__ void ldl_block(float &acc, const float (&LD)[16], con
                      : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), [lane] "n"(J));
 }
 
+// Terms k = K0 .. K0+CNT-1 of LDL' column J (all with L[.][k] already known),
+// alternating between two accumulators (k even -> a, odd -> b), so that they can
+// be issued while the pivot of column J-1 is still being inverted; CNT <= 14.
+#define VLA_FBC2(D, S, M) "v_fmac_f32_dpp %" #D ", %" #S ", %" #M " row_newbcast:%[lane] row_mask:0xf bank_mask:0xf\n\t"
+template <int J, int K0, int CNT>
+__device__ __forceinline__ void ldl_early(float &a, float &b, const float (&LD)[16], const float (&NL)[16])
+{
+    if constexpr (CNT == 1) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 3)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(NL[K0 + 0]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 3)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(NL[K0 + 0]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 2) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 4) VLA_FBC2(1, 3, 5)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 4) VLA_FBC2(0, 3, 5)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 3) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 5) VLA_FBC2(1, 3, 6) VLA_FBC2(0, 4, 7)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 5) VLA_FBC2(0, 3, 6) VLA_FBC2(1, 4, 7)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 4) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 6) VLA_FBC2(1, 3, 7) VLA_FBC2(0, 4, 8) VLA_FBC2(1, 5, 9)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 6) VLA_FBC2(0, 3, 7) VLA_FBC2(1, 4, 8) VLA_FBC2(0, 5, 9)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 5) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 7) VLA_FBC2(1, 3, 8) VLA_FBC2(0, 4, 9) VLA_FBC2(1, 5, 10) VLA_FBC2(0, 6, 11)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 7) VLA_FBC2(0, 3, 8) VLA_FBC2(1, 4, 9) VLA_FBC2(0, 5, 10) VLA_FBC2(1, 6, 11)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 6) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 8) VLA_FBC2(1, 3, 9) VLA_FBC2(0, 4, 10) VLA_FBC2(1, 5, 11) VLA_FBC2(0, 6, 12) VLA_FBC2(1, 7, 13)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 8) VLA_FBC2(0, 3, 9) VLA_FBC2(1, 4, 10) VLA_FBC2(0, 5, 11) VLA_FBC2(1, 6, 12) VLA_FBC2(0, 7, 13)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 7) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 9) VLA_FBC2(1, 3, 10) VLA_FBC2(0, 4, 11) VLA_FBC2(1, 5, 12) VLA_FBC2(0, 6, 13) VLA_FBC2(1, 7, 14) VLA_FBC2(0, 8, 15)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 9) VLA_FBC2(0, 3, 10) VLA_FBC2(1, 4, 11) VLA_FBC2(0, 5, 12) VLA_FBC2(1, 6, 13) VLA_FBC2(0, 7, 14) VLA_FBC2(1, 8, 15)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 8) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 10) VLA_FBC2(1, 3, 11) VLA_FBC2(0, 4, 12) VLA_FBC2(1, 5, 13) VLA_FBC2(0, 6, 14) VLA_FBC2(1, 7, 15) VLA_FBC2(0, 8, 16) VLA_FBC2(1, 9, 17)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 10) VLA_FBC2(0, 3, 11) VLA_FBC2(1, 4, 12) VLA_FBC2(0, 5, 13) VLA_FBC2(1, 6, 14) VLA_FBC2(0, 7, 15) VLA_FBC2(1, 8, 16) VLA_FBC2(0, 9, 17)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 9) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 11) VLA_FBC2(1, 3, 12) VLA_FBC2(0, 4, 13) VLA_FBC2(1, 5, 14) VLA_FBC2(0, 6, 15) VLA_FBC2(1, 7, 16) VLA_FBC2(0, 8, 17) VLA_FBC2(1, 9, 18) VLA_FBC2(0, 10, 19)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(LD[K0 + 8]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), "v"(NL[K0 + 8]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 11) VLA_FBC2(0, 3, 12) VLA_FBC2(1, 4, 13) VLA_FBC2(0, 5, 14) VLA_FBC2(1, 6, 15) VLA_FBC2(0, 7, 16) VLA_FBC2(1, 8, 17) VLA_FBC2(0, 9, 18) VLA_FBC2(1, 10, 19)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(LD[K0 + 8]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), "v"(NL[K0 + 8]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 10) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 12) VLA_FBC2(1, 3, 13) VLA_FBC2(0, 4, 14) VLA_FBC2(1, 5, 15) VLA_FBC2(0, 6, 16) VLA_FBC2(1, 7, 17) VLA_FBC2(0, 8, 18) VLA_FBC2(1, 9, 19) VLA_FBC2(0, 10, 20) VLA_FBC2(1, 11, 21)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(LD[K0 + 8]), "v"(LD[K0 + 9]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), "v"(NL[K0 + 8]), "v"(NL[K0 + 9]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 12) VLA_FBC2(0, 3, 13) VLA_FBC2(1, 4, 14) VLA_FBC2(0, 5, 15) VLA_FBC2(1, 6, 16) VLA_FBC2(0, 7, 17) VLA_FBC2(1, 8, 18) VLA_FBC2(0, 9, 19) VLA_FBC2(1, 10, 20) VLA_FBC2(0, 11, 21)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(LD[K0 + 8]), "v"(LD[K0 + 9]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), "v"(NL[K0 + 8]), "v"(NL[K0 + 9]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 11) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 13) VLA_FBC2(1, 3, 14) VLA_FBC2(0, 4, 15) VLA_FBC2(1, 5, 16) VLA_FBC2(0, 6, 17) VLA_FBC2(1, 7, 18) VLA_FBC2(0, 8, 19) VLA_FBC2(1, 9, 20) VLA_FBC2(0, 10, 21) VLA_FBC2(1, 11, 22) VLA_FBC2(0, 12, 23)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(LD[K0 + 8]), "v"(LD[K0 + 9]), "v"(LD[K0 + 10]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), "v"(NL[K0 + 8]), "v"(NL[K0 + 9]), "v"(NL[K0 + 10]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 13) VLA_FBC2(0, 3, 14) VLA_FBC2(1, 4, 15) VLA_FBC2(0, 5, 16) VLA_FBC2(1, 6, 17) VLA_FBC2(0, 7, 18) VLA_FBC2(1, 8, 19) VLA_FBC2(0, 9, 20) VLA_FBC2(1, 10, 21) VLA_FBC2(0, 11, 22) VLA_FBC2(1, 12, 23)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(LD[K0 + 8]), "v"(LD[K0 + 9]), "v"(LD[K0 + 10]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), "v"(NL[K0 + 8]), "v"(NL[K0 + 9]), "v"(NL[K0 + 10]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 12) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 14) VLA_FBC2(1, 3, 15) VLA_FBC2(0, 4, 16) VLA_FBC2(1, 5, 17) VLA_FBC2(0, 6, 18) VLA_FBC2(1, 7, 19) VLA_FBC2(0, 8, 20) VLA_FBC2(1, 9, 21) VLA_FBC2(0, 10, 22) VLA_FBC2(1, 11, 23) VLA_FBC2(0, 12, 24) VLA_FBC2(1, 13, 25)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(LD[K0 + 8]), "v"(LD[K0 + 9]), "v"(LD[K0 + 10]), "v"(LD[K0 + 11]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), "v"(NL[K0 + 8]), "v"(NL[K0 + 9]), "v"(NL[K0 + 10]), "v"(NL[K0 + 11]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 14) VLA_FBC2(0, 3, 15) VLA_FBC2(1, 4, 16) VLA_FBC2(0, 5, 17) VLA_FBC2(1, 6, 18) VLA_FBC2(0, 7, 19) VLA_FBC2(1, 8, 20) VLA_FBC2(0, 9, 21) VLA_FBC2(1, 10, 22) VLA_FBC2(0, 11, 23) VLA_FBC2(1, 12, 24) VLA_FBC2(0, 13, 25)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(LD[K0 + 8]), "v"(LD[K0 + 9]), "v"(LD[K0 + 10]), "v"(LD[K0 + 11]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), "v"(NL[K0 + 8]), "v"(NL[K0 + 9]), "v"(NL[K0 + 10]), "v"(NL[K0 + 11]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 13) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 15) VLA_FBC2(1, 3, 16) VLA_FBC2(0, 4, 17) VLA_FBC2(1, 5, 18) VLA_FBC2(0, 6, 19) VLA_FBC2(1, 7, 20) VLA_FBC2(0, 8, 21) VLA_FBC2(1, 9, 22) VLA_FBC2(0, 10, 23) VLA_FBC2(1, 11, 24) VLA_FBC2(0, 12, 25) VLA_FBC2(1, 13, 26) VLA_FBC2(0, 14, 27)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(LD[K0 + 8]), "v"(LD[K0 + 9]), "v"(LD[K0 + 10]), "v"(LD[K0 + 11]), "v"(LD[K0 + 12]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), "v"(NL[K0 + 8]), "v"(NL[K0 + 9]), "v"(NL[K0 + 10]), "v"(NL[K0 + 11]), "v"(NL[K0 + 12]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 15) VLA_FBC2(0, 3, 16) VLA_FBC2(1, 4, 17) VLA_FBC2(0, 5, 18) VLA_FBC2(1, 6, 19) VLA_FBC2(0, 7, 20) VLA_FBC2(1, 8, 21) VLA_FBC2(0, 9, 22) VLA_FBC2(1, 10, 23) VLA_FBC2(0, 11, 24) VLA_FBC2(1, 12, 25) VLA_FBC2(0, 13, 26) VLA_FBC2(1, 14, 27)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(LD[K0 + 8]), "v"(LD[K0 + 9]), "v"(LD[K0 + 10]), "v"(LD[K0 + 11]), "v"(LD[K0 + 12]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), "v"(NL[K0 + 8]), "v"(NL[K0 + 9]), "v"(NL[K0 + 10]), "v"(NL[K0 + 11]), "v"(NL[K0 + 12]), [lane] "n"(J));
+    }
+    else if constexpr (CNT == 14) {
+        if constexpr (K0 % 2 == 0)
+            asm volatile("s_nop 1\n\t" VLA_FBC2(0, 2, 16) VLA_FBC2(1, 3, 17) VLA_FBC2(0, 4, 18) VLA_FBC2(1, 5, 19) VLA_FBC2(0, 6, 20) VLA_FBC2(1, 7, 21) VLA_FBC2(0, 8, 22) VLA_FBC2(1, 9, 23) VLA_FBC2(0, 10, 24) VLA_FBC2(1, 11, 25) VLA_FBC2(0, 12, 26) VLA_FBC2(1, 13, 27) VLA_FBC2(0, 14, 28) VLA_FBC2(1, 15, 29)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(LD[K0 + 8]), "v"(LD[K0 + 9]), "v"(LD[K0 + 10]), "v"(LD[K0 + 11]), "v"(LD[K0 + 12]), "v"(LD[K0 + 13]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), "v"(NL[K0 + 8]), "v"(NL[K0 + 9]), "v"(NL[K0 + 10]), "v"(NL[K0 + 11]), "v"(NL[K0 + 12]), "v"(NL[K0 + 13]), [lane] "n"(J));
+        else
+            asm volatile("s_nop 1\n\t" VLA_FBC2(1, 2, 16) VLA_FBC2(0, 3, 17) VLA_FBC2(1, 4, 18) VLA_FBC2(0, 5, 19) VLA_FBC2(1, 6, 20) VLA_FBC2(0, 7, 21) VLA_FBC2(1, 8, 22) VLA_FBC2(0, 9, 23) VLA_FBC2(1, 10, 24) VLA_FBC2(0, 11, 25) VLA_FBC2(1, 12, 26) VLA_FBC2(0, 13, 27) VLA_FBC2(1, 14, 28) VLA_FBC2(0, 15, 29)
+                         : "+v"(a), "+v"(b)
+                         : "v"(LD[K0 + 0]), "v"(LD[K0 + 1]), "v"(LD[K0 + 2]), "v"(LD[K0 + 3]), "v"(LD[K0 + 4]), "v"(LD[K0 + 5]), "v"(LD[K0 + 6]), "v"(LD[K0 + 7]), "v"(LD[K0 + 8]), "v"(LD[K0 + 9]), "v"(LD[K0 + 10]), "v"(LD[K0 + 11]), "v"(LD[K0 + 12]), "v"(LD[K0 + 13]), "v"(NL[K0 + 0]), "v"(NL[K0 + 1]), "v"(NL[K0 + 2]), "v"(NL[K0 + 3]), "v"(NL[K0 + 4]), "v"(NL[K0 + 5]), "v"(NL[K0 + 6]), "v"(NL[K0 + 7]), "v"(NL[K0 + 8]), "v"(NL[K0 + 9]), "v"(NL[K0 + 10]), "v"(NL[K0 + 11]), "v"(NL[K0 + 12]), "v"(NL[K0 + 13]), [lane] "n"(J));
+    }
+}
