@@ -28,11 +28,11 @@ METRIC = "VLA fwd tokens·heads/sec (fp32 state) + % of MI355X FP32 vector peak"
 UNIT = "tokens*heads/s"
 FP32_VECTOR_PEAK_TFLOPS = 157.3          # MI355X published FP32 vector (and dense fp32 matrix) peak
 WORKLOAD = 3                              # B=8, H=16, d_h=64, T=4096, bf16 inputs
-KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_chunk_kernel.hip",
+KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_twopass.hip",
                   "long_context_sequence_amd/csrc/vla_chunk_parts.h",
                   "long_context_sequence_amd/csrc/vla_dpp_blocks.h",
                   "long_context_sequence_amd/csrc/vla_common.h"]
-TRAFFIC_SUMMARY = "profiles/vla_fwd_fused_b8h16_d64_t4096_bf16.txt"
+TRAFFIC_SUMMARY = "profiles/vla_forward_b8h16_d64_t4096_bf16.txt"
 COPY_BYTES = 1 << 30                      # plain copy used to scale the HBM counters
 
 
@@ -197,11 +197,12 @@ def main():
     S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
     A = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
     zk = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(vla.workspace_size(B, H, T, d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step():
         vla.vla_forward(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps,
-                        o=o, S_out=S, A_out=A, zkey_out=zk, stream=stream)
+                        o=o, S_out=S, A_out=A, zkey_out=zk, stream=stream, workspace=ws)
 
     for _ in range(args.warmup):
         step()

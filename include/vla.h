@@ -26,20 +26,21 @@
  * lambda0 > 0 and eps > 0.  State arithmetic is fp32 throughout; bf16 inputs
  * are widened exactly.
  *
- * Ownership and execution: the caller owns every buffer.  Calls are
+ * Ownership and execution: the caller owns every buffer, including the
+ * device workspace of vla_forward (size from vla_forward_workspace_size); the
+ * library allocates nothing and keeps no state between calls.  Calls are
  * asynchronous on `stream` (a hipStream_t; NULL = the null stream) and never
- * synchronise.  By default the library allocates nothing.  With the environment
- * variable VLA_SPLIT=1, d_h in {64, 96, 128} runs each head's two chains on two
- * compute units when the whole grid fits; that mode allocates a per-device
- * scratch ring on first use (grown when needed, kept until the process ends),
- * and calls that overlap on one device then race on it.  Arguments are checked before anything is launched; on an
+ * synchronise.  Arguments are checked before anything is launched; on an
  * argument error nothing is launched and no buffer is touched.  A failed launch
  * returns VLA_ERR_HIP.  Faults inside a kernel surface at the caller's next
  * synchronisation.  NaN or Inf inputs propagate without being reported.
- * Concurrent calls on different streams that write the same buffers race.
+ * Concurrent calls that write the same buffers (a shared workspace included)
+ * race.
  */
 #ifndef VLA_H
 #define VLA_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -71,16 +72,37 @@ typedef enum vla_dtype {
  *              initial state in the same layout, or NULL for the defaults
  *              S_0 = 0, A_0 = I / lambda0, zkey_0 = 0.  A0 must be symmetric
  *              positive definite (as every A_t of the recurrence is).
+ * workspace    device scratch of at least workspace_bytes bytes, 256-byte
+ *              aligned, as given by vla_forward_workspace_size for the same
+ *              B, H, T, d_h (may be NULL when that size is 0).  Its contents
+ *              on entry do not matter and are not meaningful on return.
  * stream       hipStream_t to launch on.
  *
- * T == 0 launches a copy of the initial state to the requested outputs.
+ * For d_h in {64, 96, 128} and T >= 1 the sequence runs in two passes
+ * (section 3.2 makes A_t the inverse of A_0^-1 + sum_{s<=t} u^_s u^_s', so
+ * the penalty chain restarts at segment boundaries from that inverse, formed in
+ * fp64; the memory chain then runs from the per-chunk factors the penalty
+ * pass leaves in the workspace).  Results equal the token-by-token recurrence
+ * up to rounding.  T == 0 launches a copy of the initial state to the
+ * requested outputs.  A too small or misaligned workspace is
+ * VLA_ERR_INVALID_ARG.
  */
 vla_status vla_forward(const void *q, const void *k, const void *v, const void *u,
                        int in_dtype, int B, int H, int T, int d_h,
                        float lambda0, float eps,
                        float *o, float *S_out, float *A_out, float *zkey_out,
                        const float *S0, const float *A0, const float *zkey0,
-                       void *stream);
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * vla_forward_workspace_size -- bytes of device workspace vla_forward needs for
+ * these sizes (0 when it needs none: d_h in {16, 32}, or T == 0), in *bytes.
+ * At d_h = 64 it is about 6.2 KB per 16 tokens of each head (the per-chunk
+ * factors) plus a few d_h x d_h matrices per head.  Host-only; launches
+ * nothing.  Errors: VLA_ERR_INVALID_ARG (NULL bytes, bad sizes),
+ * VLA_ERR_UNSUPPORTED (d_h).
+ */
+vla_status vla_forward_workspace_size(int B, int H, int T, int d_h, size_t *bytes);
 
 /*
  * vla_step -- one decode token for every (b, h) head: the same recurrence as

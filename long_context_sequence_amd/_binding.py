@@ -37,7 +37,10 @@ def load() -> ctypes.CDLL:
         lib.vla_forward.restype = ctypes.c_int
         lib.vla_forward.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
-                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.vla_forward_workspace_size.restype = ctypes.c_int
+        lib.vla_forward_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                   ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
         lib.vla_step.restype = ctypes.c_int
         lib.vla_step.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_float, _vp, _vp, _vp, _vp, _vp]
@@ -91,15 +94,27 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def workspace_size(B: int, H: int, T: int, d_h: int) -> int:
+    """Bytes of device workspace vla_forward needs for these sizes."""
+    n = ctypes.c_size_t(0)
+    st = load().vla_forward_workspace_size(int(B), int(H), int(T), int(d_h), ctypes.byref(n))
+    if st != VLA_OK:
+        raise VLAError(st, "vla_forward_workspace_size")
+    return n.value
+
+
 def vla_forward(q, k, v, u, lambda0: float = 0.1, eps: float = 1e-4, *,
                 o=None, S_out=None, A_out=None, zkey_out=None,
-                S0=None, A0=None, zkey0=None, return_state: bool = False, stream=None):
+                S0=None, A0=None, zkey0=None, return_state: bool = False, stream=None,
+                workspace=None):
     """VLA forward over [B, H, T, d_h] device tensors (float32 or bfloat16).
 
     Returns ``o`` ([B, H, T, d_h] float32), or ``(o, S, A, zkey)`` when
     ``return_state`` is set or any state output is passed.  ``S0, A0, zkey0``
-    continue from a given state.  Launches on ``stream`` (default: PyTorch's
-    current stream) without synchronising.
+    continue from a given state.  ``workspace`` is an optional device byte
+    tensor of at least ``workspace_size(B, H, T, d_h)`` bytes (allocated here
+    when not given).  Launches on ``stream`` (default: PyTorch's current
+    stream) without synchronising.
     """
     torch = _torch()
     B, H, T, d = q.shape
@@ -119,9 +134,19 @@ def vla_forward(q, k, v, u, lambda0: float = 0.1, eps: float = 1e-4, *,
                          ("zkey_out", zkey_out, (B, H, d)), ("S0", S0, (B, H, d, d)),
                          ("A0", A0, (B, H, d, d)), ("zkey0", zkey0, (B, H, d))):
         _check(t, name, shp, f32, dev)
+    need = workspace_size(B, H, T, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    elif need:
+        if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace: need {need} bytes")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().vla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _dtype_code(q), B, H, T, d,
                             float(lambda0), float(eps), _ptr(o), _ptr(S_out), _ptr(A_out),
-                            _ptr(zkey_out), _ptr(S0), _ptr(A0), _ptr(zkey0), _stream(stream))
+                            _ptr(zkey_out), _ptr(S0), _ptr(A0), _ptr(zkey0),
+                            _ptr(workspace), ws_bytes, _stream(stream))
     if st != VLA_OK:
         raise VLAError(st, "vla_forward")
     return (o, S_out, A_out, zkey_out) if want_state else o

@@ -24,13 +24,26 @@ vla_status check_common(int in_dtype, int B, int H, int d_h, float eps)
     return VLA_OK;
 }
 
-// d_h in {64, 96, 128} runs on the chunked matrix-core kernel (also for a single
-// decode token: every state element is read and written by the same lane, so the
-// state may be updated in place); d_h in {16, 32} uses the LDS kernel.
-vla_status launch(const vla::FwdArgs &a)
+// d_h in {64, 96, 128}: sequences (T >= 1) run on the two-pass matrix-core
+// kernels; a single decode token and T = 0 on the one-workgroup-per-head kernel
+// (every state element is read and written by the same lane there, so the state
+// may be updated in place).  d_h in {16, 32} uses the LDS kernel.
+vla_status launch(const vla::FwdArgs &a, bool step)
 {
-    hipError_t e = vla::chunk_supported(a.d) ? vla::launch_forward_chunk(a) : vla::launch_forward_ref(a);
+    hipError_t e;
+    if (!vla::chunk_supported(a.d))
+        e = vla::launch_forward_ref(a);
+    else if (step || a.T == 0)
+        e = vla::launch_forward_chunk(a);
+    else
+        e = vla::launch_forward_twopass(a);
     return e == hipSuccess ? VLA_OK : VLA_ERR_HIP;
+}
+
+size_t workspace_bytes(int B, int H, int T, int d_h)
+{
+    if (!vla::chunk_supported(d_h) || T <= 0) return 0;
+    return vla::twopass_workspace_bytes(B * H, T, d_h);
 }
 
 }  // namespace
@@ -40,11 +53,14 @@ extern "C" vla_status vla_forward(const void *q, const void *k, const void *v, c
                                   float lambda0, float eps,
                                   float *o, float *S_out, float *A_out, float *zkey_out,
                                   const float *S0, const float *A0, const float *zkey0,
-                                  void *stream)
+                                  void *workspace, size_t workspace_bytes, void *stream)
 {
     vla_status st = check_common(in_dtype, B, H, d_h, eps);
     if (st != VLA_OK) return st;
     if (T < 0 || !finite_pos(lambda0)) return VLA_ERR_INVALID_ARG;
+    const size_t need = ::workspace_bytes(B, H, T, d_h);
+    if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need))
+        return VLA_ERR_INVALID_ARG;
     const bool need_tok = T > 0;
     if (!ok_ptr(q, need_tok) || !ok_ptr(k, need_tok) || !ok_ptr(v, need_tok) ||
         !ok_ptr(u, need_tok) || !ok_ptr(o, need_tok))
@@ -55,8 +71,17 @@ extern "C" vla_status vla_forward(const void *q, const void *k, const void *v, c
     if (T == 0 && !S_out && !A_out && !zkey_out) return VLA_OK;   // nothing to do
 
     vla::FwdArgs a{q, k, v, u, in_dtype, B, H, T, d_h, lambda0, eps,
-                   o, S_out, A_out, zkey_out, S0, A0, zkey0, (hipStream_t)stream};
-    return launch(a);
+                   o, S_out, A_out, zkey_out, S0, A0, zkey0, (hipStream_t)stream,
+                   workspace, workspace_bytes};
+    return launch(a, false);
+}
+
+extern "C" vla_status vla_forward_workspace_size(int B, int H, int T, int d_h, size_t *bytes)
+{
+    if (!bytes || B < 1 || H < 1 || T < 0 || (long long)B * H > 0x7fffffffLL) return VLA_ERR_INVALID_ARG;
+    if (!supported_d(d_h)) return VLA_ERR_UNSUPPORTED;
+    *bytes = ::workspace_bytes(B, H, T, d_h);
+    return VLA_OK;
 }
 
 extern "C" vla_status vla_step(const void *q, const void *k, const void *v, const void *u,
@@ -70,8 +95,8 @@ extern "C" vla_status vla_step(const void *q, const void *k, const void *v, cons
         return VLA_ERR_INVALID_ARG;
     // lambda0 only shapes the default A_0, which a step never uses (A is given).
     vla::FwdArgs a{q, k, v, u, in_dtype, B, H, 1, d_h, 1.0f, eps,
-                   o, S, A, zkey, S, A, zkey, (hipStream_t)stream};
-    return launch(a);
+                   o, S, A, zkey, S, A, zkey, (hipStream_t)stream, nullptr, 0};
+    return launch(a, true);
 }
 
 extern "C" const char *vla_status_string(int status)

@@ -107,6 +107,53 @@ __device__ __forceinline__ float rcp_bcast(float x)
 
 // 16-byte loads and stores (LDS or global)
 __device__ __forceinline__ f4 ld4(const float *p) { return *reinterpret_cast<const f4 *>(p); }
+
+// Raw buffer view of device memory: a uniform base and extent in a resource
+// descriptor, 32-bit per-lane byte offsets, no 64-bit vector address math.
+// Loads past the extent return 0 and stores past it are dropped (every access
+// here is whole dwords inside or outside a row, never straddling the end).
+struct Buf {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ Buf(const void *base, unsigned bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                              0x00020000))
+    {
+    }
+    __device__ __forceinline__ f4 ld128(unsigned off, unsigned soff = 0) const
+    {
+        return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+    }
+    __device__ __forceinline__ uint2 ld64(unsigned off, unsigned soff = 0) const
+    {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
+        return make_uint2(x[0], x[1]);
+    }
+    __device__ __forceinline__ uint32_t ld32(unsigned off, unsigned soff = 0) const
+    {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+    }
+    __device__ __forceinline__ uint32_t ld16(unsigned off, unsigned soff = 0) const
+    {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
+    }
+    __device__ __forceinline__ void st32(float x, unsigned off, unsigned soff = 0) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, soff, 0);
+    }
+};
+
+// Load of a T at a uniform base plus a 32-bit unsigned byte offset (the form the
+// hardware addresses as scalar base + vector offset, with no 64-bit vector math).
+template <typename T>
+__device__ __forceinline__ T ldo(const void *base, unsigned byte_off)
+{
+    return *reinterpret_cast<const T *>(static_cast<const char *>(base) + byte_off);
+}
+template <typename T>
+__device__ __forceinline__ void sto(void *base, unsigned byte_off, T x)
+{
+    *reinterpret_cast<T *>(static_cast<char *>(base) + byte_off) = x;
+}
 __device__ __forceinline__ void st4(float *p, f4 x) { *reinterpret_cast<f4 *>(p) = x; }
 
 template <int CTRL>
@@ -147,11 +194,15 @@ template <typename Tin> struct Raw1;
 template <> struct Raw1<float> {
     float x;
     __device__ __forceinline__ void load(const float *p, size_t i) { x = p[i]; }
+    __device__ __forceinline__ void load_at(const float *base, unsigned i) { x = ldo<float>(base, 4u * i); }
+    __device__ __forceinline__ void load_buf(const Buf &b, unsigned i) { x = __uint_as_float(b.ld32(4u * i)); }
     __device__ __forceinline__ float get() const { return x; }
 };
 template <> struct Raw1<uint16_t> {
     uint32_t x;
     __device__ __forceinline__ void load(const uint16_t *p, size_t i) { x = p[i]; }
+    __device__ __forceinline__ void load_at(const uint16_t *base, unsigned i) { x = ldo<uint16_t>(base, 2u * i); }
+    __device__ __forceinline__ void load_buf(const Buf &b, unsigned i) { x = b.ld16(2u * i); }
     __device__ __forceinline__ float get() const { return __uint_as_float(x << 16); }
 };
 
@@ -164,6 +215,23 @@ template <int N> struct RawVec<float, N> {   // N in {4, 6, 8}; 8-byte aligned
 #pragma unroll
         for (int i = 0; i < N / 2; ++i) x[i] = reinterpret_cast<const float2 *>(p)[i];
     }
+    __device__ __forceinline__ void load_buf(const Buf &b, unsigned i)   // N == 4
+    {
+        const f4 y = b.ld128(4u * i);
+        x[0] = make_float2(y[0], y[1]);
+        x[1] = make_float2(y[2], y[3]);
+    }
+    __device__ __forceinline__ void load_at(const float *base, unsigned i)
+    {
+        if constexpr (N == 4) {
+            const f4 y = ldo<f4>(base, 4u * i);
+            x[0] = make_float2(y[0], y[1]);
+            x[1] = make_float2(y[2], y[3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < N / 2; ++j) x[j] = ldo<float2>(base, 4u * i + 8u * j);
+        }
+    }
     __device__ __forceinline__ float get(int i) const { return (i & 1) ? x[i >> 1].y : x[i >> 1].x; }
 };
 template <int N> struct RawVec<uint16_t, N> {   // N in {4, 6, 8}; 4-byte aligned
@@ -172,6 +240,23 @@ template <int N> struct RawVec<uint16_t, N> {   // N in {4, 6, 8}; 4-byte aligne
     {
 #pragma unroll
         for (int i = 0; i < N / 2; ++i) x[i] = reinterpret_cast<const uint32_t *>(p)[i];
+    }
+    __device__ __forceinline__ void load_buf(const Buf &b, unsigned i)   // N == 4
+    {
+        const uint2 y = b.ld64(2u * i);
+        x[0] = y.x;
+        x[1] = y.y;
+    }
+    __device__ __forceinline__ void load_at(const uint16_t *base, unsigned i)
+    {
+        if constexpr (N == 4) {
+            const uint2 y = ldo<uint2>(base, 2u * i);
+            x[0] = y.x;
+            x[1] = y.y;
+        } else {
+#pragma unroll
+            for (int j = 0; j < N / 2; ++j) x[j] = ldo<uint32_t>(base, 2u * i + 4u * j);
+        }
     }
     __device__ __forceinline__ float get(int i) const
     {
@@ -198,6 +283,8 @@ struct Cfg {
 template <int D>
 struct Lds {
     static constexpr int C = Cfg<D>::C, NA = Cfg<D>::NA, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
+    static constexpr int UB = 2;   // buffers of u^ (by chunk parity)
+    static constexpr bool KEEP_IK = false;   // no copy of 1/|k| per token
     float uh[2][C * LD];     // u^   [token][i], by chunk parity
     float kh[2][C * LD];     // k^
     float ph[2][C * LD];     // phi(q)
@@ -215,11 +302,11 @@ struct Lds {
     float tit[NA][C * LT];   // per S-wave: (I+N)^-1 transposed
 };
 
-// Where the penalty chain leaves W' and the |w|^2 partials of a chunk: in LDS
-// for a memory chain in the same workgroup ...
-template <int D>
+// Where the penalty chain leaves W' (token- and key-major) and the |w|^2
+// partials of a chunk: in LDS.
+template <int D, typename LdsT = Lds<D>>
 struct WToLds {
-    Lds<D> &L;
+    LdsT &L;
     int sp, g, n;
     __device__ __forceinline__ void block(int b, f4 wt)
     {
@@ -232,29 +319,16 @@ struct WToLds {
         if (n == 0) st4(&L.nrm[wi][4 * g], nr);
     }
 };
-// ... or in a global ring slot ([i][token] rows of 16, then NA x 16 partials) for
-// a memory chain on another compute unit.
-template <int D>
-struct WToGlobal {
-    float *slot;
-    int g, n;
-    __device__ __forceinline__ void block(int b, f4 wt) { st4(&slot[(16 * b + n) * 16 + 4 * g], wt); }
-    __device__ __forceinline__ void norms(int wi, f4 nr)
-    {
-        if (n == 0) st4(&slot[16 * D + 16 * wi + 4 * g], nr);
-    }
-};
-
 // Per-thread view of one head: lane coordinates, input pointers and the two
 // chains' steps.  A wave with chain index wi owns column blocks wi*BPW + bb.
-template <int D, typename Tin>
+template <int D, typename Tin, typename LdsT = Lds<D>>
 struct Head {
     using Cf = Cfg<D>;
     static constexpr int C = Cf::C, NB = Cf::NB, NA = Cf::NA, BPW = Cf::BPW;
     static constexpr int LD = Cf::LD, LT = Cf::LT, CPT = Cf::CPT;
     typedef f4 State[BPW][NB];
 
-    Lds<D> &L;
+    LdsT &L;
     const Tin *q, *k, *v, *u;
     float *o;
     int T;
@@ -269,7 +343,7 @@ struct Head {
     int pp = 0;                         // current period (timing probes only)
     RawVec<Tin, CPT> rq, rk, ru;
 
-    __device__ __forceinline__ Head(Lds<D> &L_, const Tin *q_, const Tin *k_, const Tin *v_,
+    __device__ __forceinline__ Head(LdsT &L_, const Tin *q_, const Tin *k_, const Tin *v_,
                                     const Tin *u_, float *o_, int T_, float eps_, size_t bh,
                                     int lane, int wi_, int ts_, bool stager, int kcol_)
         : L(L_), q(q_), k(k_), v(v_), u(u_), o(o_), T(T_), eps(eps_), tok0(bh * (size_t)T_),
@@ -337,11 +411,14 @@ struct Head {
             const float nu = sum_row16(pu);
             iu = ok && nu > 0.f ? rsqrtf(nu) : 0.f;
         }
+        if constexpr (LdsT::KEEP_IK) {
+            if (cc == 0) L.ikn[slot][tl] = ik;
+        }
         const int e0 = tl * LD + cc * CPT;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             L.kh[slot][e0 + i] = rk.get(i) * ik;
-            if constexpr (WU) L.uh[slot][e0 + i] = ru.get(i) * iu;
+            if constexpr (WU) L.uh[slot % LdsT::UB][e0 + i] = ru.get(i) * iu;
             if constexpr (WQ) {
                 L.ph[slot][e0 + i] = phi_fast(rq.get(i));
                 L.zk[e0 + i] = ok ? phi_fast(rk.get(i)) : 0.f;
@@ -399,7 +476,7 @@ struct Head {
     {
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
         const int sp = p & 1;
-        const float *ub = L.uh[sp], *kb = L.kh[sp];
+        const float *ub = L.uh[sp % LdsT::UB], *kb = L.kh[sp];
         f4 z[BPW];
         sfor<BPW>([&](auto bb) { z[bb] = zero; });
         sfor<NB>([&](auto rho) {
@@ -537,6 +614,106 @@ struct Head {
         wout.norms(wi, nr);
     }
 
+    // a_update with the 16 x 16 factorisation done once per workgroup (for
+    // workgroups whose waves run only the penalty chain, where the four copies
+    // would cost issue slots rather than hide latency): wave 0 factorises I + G
+    // and leaves L^-1 (transposed), 1/d and the A operand of W' in LDS (its own
+    // scratch, L.hms), while every wave forms Y0' of its blocks; then, after a
+    // workgroup barrier, each wave downdates its blocks and forms W'.
+    template <class WOut>
+    __device__ __forceinline__ void a_update_shared(State &st, int p, WOut &&wout)
+    {
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        const float *kb = L.kh[p & 1];
+        f4 y[BPW];
+        sfor<BPW>([&](auto bb) { y[bb] = zero; });
+        sfor<NB>([&](auto rho) {
+            const f4 ak = ld4(&kb[n * LD + 16 * rho + 4 * g]);
+            sfor<4>([&](auto r) {
+                sfor<BPW>([&](auto bb) { y[bb] = mma(ak[int(r)], st[bb][rho][int(r)], y[bb]); });
+            });
+        });
+        if (wi == 0) {
+            float Mr[16], gub[4];
+            sfor<4>([&](auto r) {
+                float a = L.gp[0][0][(4 * g + r) * LT + n];
+                sfor<NA - 1>([&](auto w2) { a += L.gp[w2 + 1][0][(4 * g + r) * LT + n]; });
+                L.lit[0][(4 * g + r) * LT + n] = a;
+            });
+            sfor<4>([&](auto c) {
+                float a = L.gp[0][1][(4 * c + g) * LT + n];
+                sfor<NA - 1>([&](auto w2) { a += L.gp[w2 + 1][1][(4 * c + g) * LT + n]; });
+                gub[c] = a;
+            });
+            wave_lds_order();
+            sfor<4>([&](auto q4) {
+                const f4 a = ld4(&L.lit[0][n * LT + 4 * q4]);
+                sfor<4>([&](auto r) { Mr[4 * q4 + r] = a[int(r)]; });
+            });
+            wave_lds_order();
+            // LDL' as in a_update
+            float LDr[16], NLr[16];
+            float ca = Mr[0], cb = 0.f;
+            sfor<16>([&](auto jj) {
+                constexpr int j = decltype(jj)::value;
+                if constexpr (j > 0) ldl_block<j, j - 1, 1>(ca, LDr, NLr);
+                const float acc = ca + cb;
+                const float inv = rcp_bcast<j>(acc);
+                constexpr int E = j, E1 = E < 2 ? E : 2;
+                float na = 0.f, nb = 0.f;
+                if constexpr (j + 1 < 16) {
+                    na = Mr[j + 1];
+                    if constexpr (E1 > 0) ldl_early<j + 1, 0, E1>(na, nb, LDr, NLr);
+                }
+                LDr[j] = acc;
+                NLr[j] = n > j ? -(acc * inv) : 0.f;
+                if (g == 0 && n == 0) L.inv[0][j] = inv;
+                if constexpr (j + 1 < 16 && E > E1) ldl_early<j + 1, E1, E - E1>(na, nb, LDr, NLr);
+                ca = na;
+                cb = nb;
+            });
+            float X[4];
+            sfor<4>([&](auto c) { X[c] = n == 4 * c + g ? 1.f : 0.f; });
+            asm volatile(VLA_LINV_BLOCK
+                         : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3])
+                         : "v"(NLr[0]), "v"(NLr[1]), "v"(NLr[2]), "v"(NLr[3]), "v"(NLr[4]),
+                           "v"(NLr[5]), "v"(NLr[6]), "v"(NLr[7]), "v"(NLr[8]), "v"(NLr[9]),
+                           "v"(NLr[10]), "v"(NLr[11]), "v"(NLr[12]), "v"(NLr[13]), "v"(NLr[14]));
+            sfor<4>([&](auto c) { L.lit[0][(4 * c + g) * LT + n] = X[c]; });
+            wave_lds_order();
+            const f4 inv4 = ld4(&L.inv[0][4 * g]);
+            f4 hm = mma4(X, gub, zero);
+            sfor<4>([&](auto r) { hm[int(r)] = 4 * g + r <= n ? -(hm[int(r)] * inv4[int(r)]) : 0.f; });
+            st4(&L.hms[4 * (16 * g + n)], hm);
+        }
+        lds_barrier();
+        float X[4];
+        sfor<4>([&](auto c) { X[c] = L.lit[0][(4 * c + g) * LT + n]; });   // L^-1 [n][4c+g]
+        const f4 inv4 = ld4(&L.inv[0][4 * g]);                          // 1 / d_{4g+r}
+        const f4 lit = ld4(&L.lit[0][n * LT + 4 * g]);                  // L^-1 [4g+r][n]
+        const f4 hm = ld4(&L.hms[4 * (16 * g + n)]);
+        f4 nr = zero;
+        sfor<BPW>([&](auto bb) {
+            const int b = wi * BPW + bb;
+            float zb[4];   // Z0'[4c+g][16b+n]
+            sfor<4>([&](auto c) { zb[c] = L.z0[(4 * c + g) * LD + 16 * b + n]; });
+            const f4 q2 = mma4(X, zb, zero);        // L^-1 Z0'
+            const f4 q1 = q2 * inv4;                // D^-1 L^-1 Z0'
+            const f4 xt = mma4(lit, q1, zero);      // (I + G)^-1 Z0'
+            const f4 wt = mma4(hm, q2, y[bb]);      // W'
+            const f4 nx = -xt;
+            f4 az[NB];
+            sfor<NB>([&](auto rho) { az[rho] = ld4(&L.z0t[(16 * rho + n) * LT + 4 * g]); });
+            sfor<4>([&](auto r) {      // As <- As - Z0 (I + G)^-1 Z0'
+                sfor<NB>([&](auto rho) { st[bb][rho] = mma(az[rho][int(r)], nx[int(r)], st[bb][rho]); });
+            });
+            wout.block(b, wt);
+            nr += wt * wt;
+        });
+        sfor<4>([&](auto r) { nr[int(r)] = sum_row16(nr[int(r)]); });
+        wout.norms(wi, nr);
+    }
+
     // ------------------------------------------------------------ memory chain
     // S K^ and S Phi of chunk cq (own blocks), before its write
     __device__ __forceinline__ void s_products(const State &st, int cq, f4 (&sk)[BPW], f4 (&sq)[BPW]) const
@@ -585,6 +762,40 @@ struct Head {
             L.nq[wi][1][(4 * g + r) * LT + n] = gq[int(r)];
         });
     }
+    // The two C x C factors of the memory chain from the waves' partials in
+    // L.nq: (I + N)^-1 and (Alpha^'Phi) o Up, each stored transposed
+    // (tt[m][t] = X[t][m]), so that lane 16 g + n reads X[4 g + r][n] as four
+    // consecutive floats at tt + 16 n + 4 g.  One wave computes them.
+    __device__ __forceinline__ void prep_tp(float *tt, float *pt)
+    {
+        float NNr[16];
+        f4 qa;
+        sfor<4>([&](auto r) {   // -N[4g+r][n] (strictly upper), rows through LDS
+            float a = L.nq[0][0][(4 * g + r) * LT + n];
+            sfor<NA - 1>([&](auto w2) { a += L.nq[w2 + 1][0][(4 * g + r) * LT + n]; });
+            L.tit[wi][(4 * g + r) * LT + n] = 4 * g + r < n ? -a : 0.f;
+        });
+        wave_lds_order();
+        sfor<4>([&](auto q4) {
+            const f4 a = ld4(&L.tit[wi][n * LT + 4 * q4]);
+            sfor<4>([&](auto r) { NNr[4 * q4 + r] = a[int(r)]; });
+        });
+        sfor<4>([&](auto r) {
+            float a = L.nq[0][1][(4 * g + r) * LT + n];
+            sfor<NA - 1>([&](auto w2) { a += L.nq[w2 + 1][1][(4 * g + r) * LT + n]; });
+            qa[int(r)] = 4 * g + r <= n ? a : 0.f;
+        });
+        st4(&pt[16 * n + 4 * g], qa);
+        float X[4];
+        sfor<4>([&](auto c) { X[c] = n == 4 * c + g ? 1.f : 0.f; });
+        asm volatile(VLA_TINV_BLOCK
+                     : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3])
+                     : "v"(NNr[1]), "v"(NNr[2]), "v"(NNr[3]), "v"(NNr[4]), "v"(NNr[5]),
+                       "v"(NNr[6]), "v"(NNr[7]), "v"(NNr[8]), "v"(NNr[9]), "v"(NNr[10]),
+                       "v"(NNr[11]), "v"(NNr[12]), "v"(NNr[13]), "v"(NNr[14]), "v"(NNr[15]));
+        sfor<4>([&](auto c) { tt[16 * (4 * c + g) + n] = X[c]; });   // column 4c+g of (I+N)^-1
+    }
+
     // (I + N)^-1, the errors E, the readout o of chunk cq and the write of S
     // (W [i][token] of the chunk at wtb)
     __device__ __forceinline__ void s_update(State &st, int cq, const f4 (&sk)[BPW], const f4 (&sq)[BPW],

@@ -15,6 +15,8 @@ struct FwdArgs {
     float *o, *S_out, *A_out, *zk_out;
     const float *S0, *A0, *zk0;
     hipStream_t stream;
+    void *ws;             // workspace of the two-pass forward (device memory)
+    size_t ws_bytes;
 };
 
 // Input widening: fp32 as is, bf16 (stored as its 16 bit pattern) exactly.
@@ -31,8 +33,12 @@ __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : expf(
 
 hipError_t launch_forward_ref(const FwdArgs &a);
 
-// Chunked matrix-core kernel (d_h in {64, 96, 128}).
+// Chunked matrix-core kernels (d_h in {64, 96, 128}).
 bool chunk_supported(int d);
+// one workgroup per head with both chains (decode steps and T = 0)
 hipError_t launch_forward_chunk(const FwdArgs &a);
+// two passes over the sequence (forward, T >= 1); needs the workspace below
+size_t twopass_workspace_bytes(int BH, int T, int d);
+hipError_t launch_forward_twopass(const FwdArgs &a);
 
 }  // namespace vla

@@ -1,0 +1,605 @@
+// vla_twopass.hip -- forward pass of the VLA recurrence for d_h in {64, 96, 128}
+// as two passes over the sequence, so that the work of one head spreads over
+// many compute units.
+//
+// Source: "Variational Linear Attention" (arXiv 2605.11196), section 3.2
+// (A_0 = I / lambda0 and unit u, so that A_t is the inverse of
+// A_0^-1 + sum_{s<=t} u^_s u^_s') and section 3.3, Eqs. (9)-(11).
+//
+// The penalty chain (Eq. 9) reads only the inputs, and A_t is the inverse of
+//     M_t = A_0^-1 + sum_{s<=t} u^_s u^_s'.
+// The sequence is cut into segments of whole chunks, and the chain of each
+// segment starts from the inverse of M at its first token, formed directly:
+//
+//   gram     per (head, segment but the last): sum of u^ u^' over the segment
+//            (fp32 matrix-core products of 16 tokens, summed in fp64) and the sum
+//            of phi(k) (fp64).
+//   inverse  per (head, segment > 0): M at the segment start in fp64 and its
+//            inverse by the symmetric sweep operator (fp64), stored as fp32, and
+//            the key sum at the segment start.
+//   penalty  per (head, segment): the blocked penalty chain of vla_chunk_parts.h
+//            from that A; for every chunk of 16 tokens it writes the factors the
+//            memory chain needs to a record: alpha^ (d x C, key-major),
+//            (I + N)^-1 and P = (Alpha^'Phi) o Up (C x C, transposed) and
+//            1 / den (C).  The key sum and den follow Eq. (11).
+//   memory   per (head, group of 16-row value blocks): the memory chain from the
+//            records and q, k, v:
+//                R = V - S K^,  E = R (I + N)^-1,
+//                o = (S Phi + E P) / den,  S <- S + E Alpha^'.
+//            Rows of S do not interact, so the value rows of a head are split
+//            over workgroups, and the key columns of a block over the waves of a
+//            workgroup (partial products summed through LDS in a fixed order).
+//
+// All four run on the caller's stream; the workspace holds the records, the
+// Grams and the segment starts (its size is twopass_workspace_bytes).
+#include "vla_chunk_parts.h"
+
+namespace vla {
+namespace {
+
+using namespace chunk;
+
+constexpr int CH = 16;   // tokens per chunk (Cfg<D>::C)
+
+// One chunk's record (floats).
+template <int D>
+struct Rec {
+    static constexpr int AH = 0;              // alpha^ [key][token]
+    static constexpr int TT = D * CH;         // (I + N)^-1, transposed
+    static constexpr int PT = TT + CH * CH;   // (Alpha^'Phi) o Up, transposed
+    static constexpr int RD = PT + CH * CH;   // 1 / den per token
+    static constexpr int IK = RD + CH;        // 1 / |k| per token (0 past T)
+    static constexpr int SIZE = IK + CH;      // a multiple of 16
+};
+
+// Value blocks per memory workgroup (its 4 waves split each block's key tiles
+// KS = 4 / VBW ways).
+template <int D> struct MemCfg;
+template <> struct MemCfg<64> { static constexpr int VBW = 2; };
+template <> struct MemCfg<96> { static constexpr int VBW = 2; };
+template <> struct MemCfg<128> { static constexpr int VBW = 1; };
+
+// ------------------------------------------------------------------- gram
+// Workgroup (head, segment j < S - 1): G_j = sum of u^ u^' and z_j = sum of
+// phi(k) over the tokens of segment j.  Tokens go in blocks of GB = 64; thread
+// (token tl, part cc) stages columns [cc CPT, +CPT) of u^ of tokens tl + 16 s
+// (s < 4) of a block, transposed ([i][token]), while the loads of the next
+// block are in flight; wave w owns the 16 x 16 tiles w + 4 t of G.  Each
+// block's fp32 matrix-core partial sums are added to fp64 accumulators.
+template <int D, typename Tin>
+__global__ void __launch_bounds__(256)
+vla_gram(const Tin *__restrict__ k, const Tin *__restrict__ u, int T, int S, int SC,
+         double *__restrict__ gram, double *__restrict__ zks)
+{
+    constexpr int NB = D / 16, TPW = NB * NB / 4, CPT = D / 16, GB = 64, LT = GB + 4;
+    __shared__ __align__(16) float ut[2][D * LT];
+    __shared__ double zred[256 * CPT];
+
+    const int S1 = S - 1;
+    const int bh = blockIdx.x / S1, j = blockIdx.x % S1;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tl = tid >> 4, cc = tid & 15;
+    const int t0 = j * SC * CH, t1 = min(T, t0 + SC * CH);   // the segment's tokens
+    const int NBK = (t1 - t0 + GB - 1) / GB;
+    const Tin *uh = u + (size_t)bh * T * D, *kh = k + (size_t)bh * T * D;
+
+    RawVec<Tin, CPT> ru[4], rk[4];
+    double zacc[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) zacc[i] = 0.0;
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    double gacc[TPW][4];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gacc[t][r] = 0.0;
+
+    auto prefetch = [&](int blk) {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const int t = t0 + blk * GB + 16 * s2 + tl;
+            const unsigned off = (unsigned)(t < t1 ? t : t1 - 1) * D + cc * CPT;
+            ru[s2].load(uh + off);
+            rk[s2].load(kh + off);
+        }
+    };
+    auto stage = [&](int blk) {
+        float *dst = ut[blk & 1];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const bool ok = t0 + blk * GB + 16 * s2 + tl < t1;
+            float pu = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) pu = fmaf(ru[s2].get(i), ru[s2].get(i), pu);
+            const float nu = sum_row16(pu);
+            const float iu = ok && nu > 0.f ? rsqrtf(nu) : 0.f;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) dst[(cc * CPT + i) * LT + 16 * s2 + tl] = ru[s2].get(i) * iu;
+            if (ok) {
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) zacc[i] += (double)phi_fast(rk[s2].get(i));
+            }
+        }
+    };
+
+    prefetch(0);
+    stage(0);
+    if (NBK > 1) prefetch(1);
+    vmem_drain();
+    __syncthreads();
+    for (int blk = 0; blk < NBK; ++blk) {
+        const float *src = ut[blk & 1];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int tix = w + 4 * t, a = tix / NB, b = tix % NB;
+            f4 acc = zero;
+#pragma unroll
+            for (int s2 = 0; s2 < GB / 16; ++s2) {
+                const f4 af = ld4(&src[(16 * a + n) * LT + 16 * s2 + 4 * g]);   // u^[16a+n][tok]
+                const f4 bf = ld4(&src[(16 * b + n) * LT + 16 * s2 + 4 * g]);   // u^[16b+n][tok]
+                acc = mma4(af, bf, acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gacc[t][r] += (double)acc[r];
+        }
+        if (blk + 1 < NBK) {
+            stage(blk + 1);
+            if (blk + 2 < NBK) prefetch(blk + 2);
+        }
+        lds_barrier();
+    }
+
+    double *G = gram + ((size_t)bh * S1 + j) * D * D;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int tix = w + 4 * t, a = tix / NB, b = tix % NB;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) G[(size_t)(16 * a + 4 * g + r) * D + 16 * b + n] = gacc[t][r];
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) zred[tid * CPT + i] = zacc[i];
+    __syncthreads();
+    if (tid < D) {
+        const int pc = tid / CPT, pi = tid % CPT;
+        double z = 0.0;
+        for (int t2 = 0; t2 < CH; ++t2) z += zred[(t2 * 16 + pc) * CPT + pi];
+        zks[((size_t)bh * S1 + j) * D + tid] = z;
+    }
+}
+
+// ------------------------------------------------------------------- inverse
+// In-place symmetric sweep of all pivots: M -> -M^-1 (M symmetric positive
+// definite; no pivoting is needed).  Thread (row i, columns [c0, c0 + EPT))
+// holds its entries in m; row k of the current matrix and 1 / m[k][k] are
+// broadcast through rowbuf (double-buffered, so one barrier per pivot; the
+// owner of the diagonal entry forms the reciprocal).  Branch-free: every
+// entry takes one of three candidate values by selects.
+template <int D, int EPT>
+__device__ __forceinline__ void sweep_all(double (&m)[EPT], int i, int c0, double (*rowbuf)[D + 2])
+{
+    static_assert(EPT % 2 == 0, "row slices are read as pairs");
+    // pivot row k with its diagonal entry p replaced by p - 1, and 1/p: then
+    // m <- m - (r 1/p) r' gives every entry of the sweep but (k, k), which is 2
+    // too large.  (Only compile-time indices into m, so that it stays in
+    // registers.)
+    auto publish = [&](int row, int slot) {
+        if (i == row) {
+            const int ed = row - c0;
+            double piv = 0.0;
+            sfor<EPT>([&](auto e) {
+                rowbuf[slot][c0 + e] = e == ed ? m[e] - 1.0 : m[e];
+                piv = e == ed ? m[e] : piv;
+            });
+            if (ed >= 0 && ed < EPT) rowbuf[slot][D] = 1.0 / piv;
+        }
+    };
+    publish(0, 0);
+    __syncthreads();
+    for (int kk = 0; kk < D; ++kk) {
+        const double *rb = rowbuf[kk & 1];
+        const double ui = rb[i] * rb[D];
+        sfor<EPT / 2>([&](auto h) {
+            const double2 x = *reinterpret_cast<const double2 *>(&rb[c0 + 2 * h]);
+            m[2 * h] = fma(-ui, x.x, m[2 * h]);
+            m[2 * h + 1] = fma(-ui, x.y, m[2 * h + 1]);
+        });
+        if (i == kk) {   // the lane holding (k, k)
+            const int ed = kk - c0;
+            sfor<EPT>([&](auto e) { m[e] -= e == ed ? 2.0 : 0.0; });
+        }
+        if (kk + 1 < D) publish(kk + 1, (kk + 1) & 1);
+        __syncthreads();
+    }
+}
+
+// Workgroup (head, segment j >= 1): A at the segment start = M^-1 with
+// M = A_0^-1 + sum_{i<j} G_i, and the key sum at the segment start.  With a
+// caller-given A_0 (or zkey_0) the workgroup of segment 1 also copies it to slot
+// 0, which the penalty pass reads instead, so that the final state may overwrite
+// the initial one.
+template <int D>
+__global__ void __launch_bounds__(8 * D)
+vla_seginv(int S, float lambda0, const float *A0, const float *zk0,
+           const double *__restrict__ gram, const double *__restrict__ zks,
+           float *__restrict__ aseg, float *__restrict__ zseg)
+{
+    constexpr int EPT = D / 8;
+    __shared__ __align__(16) double rowbuf[2][D + 2];
+    const int S1 = S - 1;
+    const int bh = blockIdx.x / S1, j = blockIdx.x % S1 + 1;
+    const int tid = threadIdx.x, i = tid >> 3, c0 = (tid & 7) * EPT;
+    const size_t DD = (size_t)D * D;
+
+    double m[EPT];
+    if (A0) {
+        const float *a0 = A0 + bh * DD + (size_t)i * D + c0;
+        sfor<EPT>([&](auto e) { m[e] = (double)a0[e]; });
+        if (j == 1) sfor<EPT>([&](auto e) { aseg[(size_t)bh * S * DD + (size_t)i * D + c0 + e] = a0[e]; });
+        sweep_all<D, EPT>(m, i, c0, rowbuf);   // -A_0^-1
+        sfor<EPT>([&](auto e) { m[e] = -m[e]; });
+    } else {
+        sfor<EPT>([&](auto e) { m[e] = i == c0 + e ? (double)lambda0 : 0.0; });
+    }
+    for (int s = 0; s < j; ++s) {
+        const double *G = gram + ((size_t)bh * S1 + s) * DD + (size_t)i * D + c0;
+        sfor<EPT>([&](auto e) { m[e] += G[e]; });
+    }
+    sweep_all<D, EPT>(m, i, c0, rowbuf);   // -M^-1
+    float *A = aseg + ((size_t)bh * S + j) * DD + (size_t)i * D + c0;
+    sfor<EPT>([&](auto e) { A[e] = (float)(-m[e]); });
+    if (tid < D) {
+        double z = zk0 ? (double)zk0[bh * D + tid] : 0.0;
+        for (int s = 0; s < j; ++s) z += zks[((size_t)bh * S1 + s) * D + tid];
+        zseg[((size_t)bh * S + j) * D + tid] = (float)z;
+        if (zk0 && j == 1) zseg[(size_t)bh * S * D + tid] = zk0[bh * D + tid];
+    }
+}
+
+// ------------------------------------------------------------------- penalty
+// LDS of a penalty workgroup: the members of Lds<D> its steps use, with a single
+// buffer where the schedule below allows one.
+template <int D>
+struct PLds {
+    static constexpr int C = Cfg<D>::C, NA = Cfg<D>::NA, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
+    static constexpr int UB = 1;
+    static constexpr bool KEEP_IK = true;
+    float uh[1][C * LD];     // u^ [token][i] (read before the next chunk is staged)
+    float kh[2][C * LD];     // k^, by chunk parity
+    float ph[2][C * LD];     // phi(q), by chunk parity
+    float zk[C * LD];        // phi(k), then the inclusive key sum
+    float rden[2][C];
+    float ikn[2][C];         // 1 / |k| per token
+    float z0[C * LD];
+    float z0t[D * LT];
+    float w[C * LD];         // W [token][i]
+    float wt[1][D * LT];     // W [i][token]
+    float gp[NA][2][C * LT];
+    float nrm[NA][C];
+    float nq[NA][2][C * LT];
+    union {                  // L^-1 scratch of the factorisation / (I+N)^-1 scratch
+        float lit[NA][C * LT];
+        float tit[NA][C * LT];
+    };
+    float inv[NA][C];
+    float hms[256];          // A operand of W' (per lane), from wave 0
+};
+
+// Workgroup (head, segment j): the penalty chain over chunks [j SC, (j+1) SC)
+// from A at the segment start, writing each chunk's record.  Per chunk p:
+//   1  Z0, Grams of chunk p; key-sum prefix of chunk p       | barrier
+//   2  wave 0: factorise I + G; all: Y0 of own blocks        | barrier
+//      downdate A, W of chunk p; 1/den of chunk p;
+//      stage chunk p+1, prefetch p+2                         | barrier
+//   3  1/|w|, Alpha^'K^ and Alpha^'Phi partials; alpha^ and
+//      1/den to the record                                   | barrier
+//   4  wave 0: (I+N)^-1 and P to the record.
+template <int D, typename Tin>
+__global__ void __launch_bounds__(64 * Cfg<D>::NA)
+vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ u,
+        int T, int S, int SC, float lambda0, float eps,
+        const float *A0, const float *zk0, const float *aseg, const float *zseg,
+        float *__restrict__ rec, float *A_out, float *zk_out)
+{
+    using Hd = Head<D, Tin, PLds<D>>;
+    constexpr int BPW = Cfg<D>::BPW, LT = Cfg<D>::LT, RS = Rec<D>::SIZE;
+    __shared__ __align__(16) PLds<D> L;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bh = blockIdx.x / S, j = blockIdx.x % S;
+    const size_t DD = (size_t)D * D;
+    const int NC = (T + CH - 1) / CH;
+    const int c0 = j * SC, c1 = min(NC, c0 + SC);
+
+    Hd hd(L, q, k, nullptr, u, nullptr, T, eps, bh, tid & 63, w, tid, true, tid);
+    typename Hd::State st;
+    const float *a_init;
+    if (j > 0)
+        a_init = aseg + ((size_t)bh * S + j) * DD;
+    else
+        a_init = A0 ? (S > 1 ? aseg + (size_t)bh * S * DD : A0 + bh * DD) : nullptr;
+    hd.load_state(st, a_init, 1.f / lambda0);
+    if (hd.kcol >= 0) {
+        if (j > 0)
+            hd.zk_run = zseg[((size_t)bh * S + j) * D + hd.kcol];
+        else if (zk0)
+            hd.zk_run = S > 1 ? zseg[(size_t)bh * S * D + hd.kcol] : zk0[bh * D + hd.kcol];
+    }
+    hd.template prefetch<true, true>(c0);
+    hd.template stage1<true, true>(c0);
+    if (c0 + 1 < c1) hd.template prefetch<true, true>(c0 + 1);
+    vmem_drain();
+    __syncthreads();
+
+    WToLds<D, PLds<D>> wl{L, 0, hd.g, hd.n};
+    float *rb = rec + ((size_t)bh * NC + c0) * RS;
+    for (int p = c0; p < c1; ++p, rb += RS) {
+        hd.a_products(st, p);
+        hd.stage2();
+        lds_barrier();
+        hd.a_update_shared(st, p, wl);
+        hd.stage3(p);
+        if (p + 1 < c1) {
+            hd.template stage1<true, true>(p + 1);
+            if (p + 2 < c1) hd.template prefetch<true, true>(p + 2);
+        }
+        lds_barrier();
+        f4 invn4;
+        hd.s_grams(p, invn4);
+        sfor<BPW>([&](auto bb) {
+            const int b = w * BPW + bb;
+            const f4 a = ld4(&L.wt[0][(16 * b + hd.n) * LT + 4 * hd.g]) * invn4;
+            st4(&rb[Rec<D>::AH + (16 * b + hd.n) * CH + 4 * hd.g], a);
+        });
+        if (tid < CH) rb[Rec<D>::RD + tid] = L.rden[p & 1][tid];
+        else if (tid < 2 * CH) rb[Rec<D>::IK + tid - CH] = L.ikn[p & 1][tid - CH];
+        lds_barrier();
+        if (w == 0) hd.prep_tp(rb + Rec<D>::TT, rb + Rec<D>::PT);
+    }
+    if (j == S - 1) {
+        if (A_out) hd.store_state(st, A_out + bh * DD);
+        if (hd.kcol >= 0 && zk_out) zk_out[bh * D + hd.kcol] = hd.zk_run;
+    }
+}
+
+// ------------------------------------------------------------------- memory
+// Operands of one chunk for one memory wave, as loaded (raw inputs stay raw):
+// k and q of token n, keys 16 rho + 4 g + [0, 4) (rho = the wave's key tiles);
+// alpha^[16 rho + n][4 g + r]; the transposed C x C factors and 1/den, 1/|k|
+// of tokens 4 g + r; v of token 4 g + r, value 16 b + n.
+template <typename Tin, int NT>
+struct MemOps {
+    RawVec<Tin, 4> k[NT], q[NT];
+    f4 aw[NT], ta, pa, rd, ik;
+    Raw1<Tin> v[4];
+};
+
+// Workgroup (head, value group): VBW value blocks of 16 rows; wave w takes block
+// w / KS and key tiles [NT (w % KS), +NT).  The state tiles are S' in MFMA
+// accumulator layout (register r of lane 16 g + n of tile rho holds
+// S[16 b + n][16 rho + 4 g + r]).  Every operand comes straight from device
+// memory into registers, two chunks ahead (three operand sets in rotation).
+// Per chunk c:
+//   (S K)' and (S Phi)' partials of the own key tiles (K raw; the rows are
+//   scaled by 1/|k| after the sum) -> LDS                          | barrier
+//   sum the KS partials (same order in every wave); E' = T'(V - S K^)';
+//   wave 0 of the block: o' = (P'E' + (S Phi)') / den;  S' += Alpha^ E'.
+template <int D, typename Tin>
+__global__ void __launch_bounds__(256)
+vla_mem(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
+        int T, int BH, const float *__restrict__ rec, const float *S0,
+        float *__restrict__ o, float *S_out)
+{
+    constexpr int NB = D / 16, VBW = MemCfg<D>::VBW, KS = 4 / VBW, NT = NB / KS;
+    constexpr int NG = NB / VBW, RS = Rec<D>::SIZE;
+    static_assert(NT * KS == NB && NG * VBW == NB, "block split");
+    __shared__ __align__(16) float red[2][4][2][256];   // per parity and wave: partials
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int vbl = w / KS, ks = w % KS;
+    // the NG workgroups of a head share an XCD (blockIdx mod 8) and its L2
+    int bh, vg;
+    const int x = blockIdx.x;
+    if (BH % 8 == 0) {
+        const int s = x >> 3;
+        bh = (s / NG) * 8 + (x & 7);
+        vg = s % NG;
+    } else {
+        bh = x / NG;
+        vg = x % NG;
+    }
+    const int b = vg * VBW + vbl;
+    const int rho0 = ks * NT;
+    const int NC = (T + CH - 1) / CH;
+    const size_t DD = (size_t)D * D;
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    // per-head bases; 32-bit offsets below
+    const Tin *qh = q + (size_t)bh * T * D, *kh = k + (size_t)bh * T * D, *vh = v + (size_t)bh * T * D;
+    const float *rh = rec + (size_t)bh * NC * RS;
+    float *oh = o + (size_t)bh * T * D;
+
+    f4 st[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        st[t] = S0 ? ld4(&S0[bh * DD + (size_t)(16 * b + n) * D + 16 * (rho0 + t) + 4 * g]) : zero;
+
+    // lane offsets within a chunk (elements); per chunk, buffer views of the
+    // head's inputs from the chunk's first token to T (rows past T read as 0)
+    unsigned offk[NT], offa[NT], offv[4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        offk[t] = n * D + 16 * (rho0 + t) + 4 * g;
+        offa[t] = Rec<D>::AH + (16 * (rho0 + t) + n) * CH + 4 * g;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) offv[r] = (4 * g + r) * D + 16 * b + n;
+    const Buf rbuf(rh, (unsigned)(NC * RS * 4));
+    auto load = [&](int c, MemOps<Tin, NT> &m) {
+        const unsigned rs = (unsigned)c * RS * 4;   // record of chunk c (bytes)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) m.aw[t] = rbuf.ld128(4u * offa[t], rs);
+        m.ta = rbuf.ld128(4u * (Rec<D>::TT + 16 * n + 4 * g), rs);
+        m.pa = rbuf.ld128(4u * (Rec<D>::PT + 16 * n + 4 * g), rs);
+        m.rd = rbuf.ld128(4u * (Rec<D>::RD + 4 * g), rs);
+        m.ik = rbuf.ld128(4u * (Rec<D>::IK + 4 * g), rs);
+        const size_t tb = (size_t)c * CH * D;
+        const unsigned left = (unsigned)(T - c * CH) * D * (unsigned)sizeof(Tin);
+        const Buf kb(kh + tb, left), qb(qh + tb, left), vb(vh + tb, left);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            m.k[t].load_buf(kb, offk[t]);
+            m.q[t].load_buf(qb, offk[t]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m.v[r].load_buf(vb, offv[r]);
+    };
+    // Every load and store of a step is unconditional (chunk indices past the end
+    // clamp, and the waves that do not write o store through an empty view), so
+    // that the compiler's wait counts can leave the next chunks' loads in flight.
+    auto step = [&](int c, const MemOps<Tin, NT> &m, MemOps<Tin, NT> &pre) {
+        load(min(c + 2, NC - 1), pre);
+        const int sl = c & 1;
+        f4 sk = zero, sq = zero;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sk = mma(m.k[t].get(r), st[t][r], sk);
+                sq = mma(phi_fast(m.q[t].get(r)), st[t][r], sq);
+            }
+        }
+        if constexpr (KS > 1) {
+            st4(&red[sl][w][0][lane * 4], sk);
+            st4(&red[sl][w][1][lane * 4], sq);
+            lds_barrier();
+            sk = ld4(&red[sl][vbl * KS][0][lane * 4]);
+#pragma unroll
+            for (int s2 = 1; s2 < KS; ++s2) sk += ld4(&red[sl][vbl * KS + s2][0][lane * 4]);
+            if (ks == 0) {
+                sq = ld4(&red[sl][vbl * KS][1][lane * 4]);
+#pragma unroll
+                for (int s2 = 1; s2 < KS; ++s2) sq += ld4(&red[sl][vbl * KS + s2][1][lane * 4]);
+            }
+        }
+        f4 vm;   // v past T reads as 0 (and 1/|k| is 0 there)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vm[r] = m.v[r].get() - sk[r] * m.ik[r];
+        const f4 e = mma4(m.ta, vm, zero);   // E' = T'(V - S K^)'
+        f4 ob = sq;
+        if (ks == 0) ob = mma4(m.pa, e, sq);  // (S_t phi(q_t))'
+        const Buf ob_(oh + (size_t)c * CH * D, ks == 0 ? (unsigned)(T - c * CH) * D * 4u : 0u);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ob_.st32(ob[r] * m.rd[r], 4u * offv[r]);   // rows past T dropped
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) st[t] = mma(m.aw[t][r], e[r], st[t]);
+        }
+    };
+
+    MemOps<Tin, NT> m0, m1, m2;
+    load(0, m0);
+    load(min(1, NC - 1), m1);
+    int c = 0;
+    for (; c + 3 <= NC; c += 3) {
+        step(c, m0, m2);
+        step(c + 1, m1, m0);
+        step(c + 2, m2, m1);
+    }
+    if (c < NC) step(c, m0, m2);
+    if (c + 1 < NC) step(c + 1, m1, m0);
+    if (S_out) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            st4(&S_out[bh * DD + (size_t)(16 * b + n) * D + 16 * (rho0 + t) + 4 * g], st[t]);
+    }
+}
+
+// ------------------------------------------------------------------- host
+inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+    int NC = 0, S = 1, SC = 0;
+    size_t rec = 0, gram = 0, zks = 0, aseg = 0, zseg = 0, bytes = 0;
+};
+
+// Segments: enough penalty workgroups to fill the device (two per compute unit
+// at d = 64, whose LDS allows two; one otherwise), at least two chunks each.
+Plan make_plan(int BH, int T, int D)
+{
+    Plan p;
+    p.NC = (T + CH - 1) / CH;
+    if (p.NC == 0) return p;
+    const int target = D == 64 ? 512 : 256;
+    int S = (target + BH - 1) / BH;
+    const int smax = p.NC / 2 > 1 ? p.NC / 2 : 1;
+    S = S < smax ? S : smax;
+    p.SC = (p.NC + S - 1) / S;
+    p.S = (p.NC + p.SC - 1) / p.SC;
+    const int rs = 16 * D + 2 * CH * CH + 2 * CH;   // Rec<D>::SIZE
+    size_t off = 0;
+    p.rec = off;
+    off = up256(off + (size_t)BH * p.NC * rs * sizeof(float));
+    if (p.S > 1) {
+        p.gram = off;
+        off = up256(off + (size_t)BH * (p.S - 1) * D * D * sizeof(double));
+        p.zks = off;
+        off = up256(off + (size_t)BH * (p.S - 1) * D * sizeof(double));
+        p.aseg = off;
+        off = up256(off + (size_t)BH * p.S * D * D * sizeof(float));
+        p.zseg = off;
+        off = up256(off + (size_t)BH * p.S * D * sizeof(float));
+    }
+    p.bytes = off;
+    return p;
+}
+
+template <int D, typename Tin>
+hipError_t launch(const FwdArgs &a)
+{
+    const int BH = a.B * a.H;
+    const Plan p = make_plan(BH, a.T, D);
+    char *ws = static_cast<char *>(a.ws);
+    float *rec = reinterpret_cast<float *>(ws + p.rec);
+    double *gram = reinterpret_cast<double *>(ws + p.gram);
+    double *zks = reinterpret_cast<double *>(ws + p.zks);
+    float *aseg = reinterpret_cast<float *>(ws + p.aseg);
+    float *zseg = reinterpret_cast<float *>(ws + p.zseg);
+    const Tin *q = (const Tin *)a.q, *k = (const Tin *)a.k, *v = (const Tin *)a.v,
+              *u = (const Tin *)a.u;
+    if (p.S > 1) {
+        hipLaunchKernelGGL((vla_gram<D, Tin>), dim3(BH * (p.S - 1)), dim3(256), 0, a.stream, k, u,
+                           a.T, p.S, p.SC, gram, zks);
+        hipLaunchKernelGGL((vla_seginv<D>), dim3(BH * (p.S - 1)), dim3(8 * D), 0, a.stream, p.S,
+                           a.lambda0, a.A0, a.zk0, gram, zks, aseg, zseg);
+    }
+    hipLaunchKernelGGL((vla_pen<D, Tin>), dim3(BH * p.S), dim3(64 * Cfg<D>::NA), 0, a.stream, q, k,
+                       u, a.T, p.S, p.SC, a.lambda0, a.eps, a.A0, a.zk0, aseg, zseg, rec, a.A_out,
+                       a.zk_out);
+    constexpr int NG = (D / 16) / MemCfg<D>::VBW;
+    hipLaunchKernelGGL((vla_mem<D, Tin>), dim3(BH * NG), dim3(256), 0, a.stream, q, k, v, a.T, BH,
+                       rec, a.S0, a.o, a.S_out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t twopass_workspace_bytes(int BH, int T, int d)
+{
+    return make_plan(BH, T, d).bytes;
+}
+
+hipError_t launch_forward_twopass(const FwdArgs &a)
+{
+    const bool bf = a.dtype == 1;
+    switch (a.d) {
+    case 64: return bf ? launch<64, uint16_t>(a) : launch<64, float>(a);
+    case 96: return bf ? launch<96, uint16_t>(a) : launch<96, float>(a);
+    case 128: return bf ? launch<128, uint16_t>(a) : launch<128, float>(a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace vla

@@ -22,7 +22,8 @@ def _declared_functions():
 
 def test_header_symbols_exported():
     names = _declared_functions()
-    assert {"vla_forward", "vla_step", "vla_status_string"} <= set(names)
+    assert {"vla_forward", "vla_forward_workspace_size", "vla_step",
+            "vla_status_string"} <= set(names)
     lib = ctypes.CDLL(vla.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in vla.h but not exported"
@@ -35,17 +36,18 @@ def test_status_strings():
     assert "unknown" in vla.vla_status_string(99)
 
 
-FAKE = 0x10000           # 16-byte aligned, never dereferenced: checks fail first
+FAKE = 0x10000           # 256-byte aligned, never dereferenced: checks fail first
 MIS = 0x10004            # misaligned
 
 
 def _fwd(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, dt=0, B=1, H=1, T=4, d=64, lam=0.1, eps=1e-4,
-             o=FAKE, S=None, A=None, z=None, S0=None, A0=None, z0=None, stream=None)
+             o=FAKE, S=None, A=None, z=None, S0=None, A0=None, z0=None, ws=FAKE,
+             ws_bytes=1 << 40, stream=None)
     a.update(kw)
     return B.load().vla_forward(a["q"], a["k"], a["v"], a["u"], a["dt"], a["B"], a["H"], a["T"],
                                 a["d"], a["lam"], a["eps"], a["o"], a["S"], a["A"], a["z"],
-                                a["S0"], a["A0"], a["z0"], a["stream"])
+                                a["S0"], a["A0"], a["z0"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -64,9 +66,30 @@ def _fwd(**kw):
     (dict(d=256), B.VLA_ERR_UNSUPPORTED),
     (dict(dt=2), B.VLA_ERR_UNSUPPORTED),
     (dict(B=1 << 16, H=1 << 16), B.VLA_ERR_INVALID_ARG),
+    (dict(ws=None), B.VLA_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 16), B.VLA_ERR_INVALID_ARG),
+    (dict(ws_bytes=1024), B.VLA_ERR_INVALID_ARG),
 ])
 def test_forward_argument_errors(kw, code):
     assert _fwd(**kw) == code
+
+
+def test_workspace_size():
+    # the per-chunk factors dominate: (16 d + 528) floats per 16 tokens of a head
+    for d in (64, 96, 128):
+        n1 = vla.workspace_size(1, 1, 4096, d)
+        assert n1 >= 256 * (16 * d + 528) * 4
+        assert n1 % 256 == 0
+        assert vla.workspace_size(8, 16, 4096, d) >= 128 * 256 * (16 * d + 528) * 4
+        assert vla.workspace_size(2, 3, 0, d) == 0
+    assert vla.workspace_size(4, 4, 1000, 16) == 0
+    assert vla.workspace_size(4, 4, 1000, 32) == 0
+    n = ctypes.c_size_t(0)
+    lib = B.load()
+    assert lib.vla_forward_workspace_size(1, 1, 8, 48, ctypes.byref(n)) == B.VLA_ERR_UNSUPPORTED
+    assert lib.vla_forward_workspace_size(0, 1, 8, 64, ctypes.byref(n)) == B.VLA_ERR_INVALID_ARG
+    assert lib.vla_forward_workspace_size(1, 1, -1, 64, ctypes.byref(n)) == B.VLA_ERR_INVALID_ARG
+    assert lib.vla_forward_workspace_size(1, 1, 8, 64, None) == B.VLA_ERR_INVALID_ARG
 
 
 def test_forward_empty_no_outputs_is_ok():

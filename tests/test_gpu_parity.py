@@ -277,23 +277,24 @@ def test_run_to_run_bitwise_deterministic():
 
 
 # ---------------------------------------------------------------------------
-# The two-workgroup arrangement (one compute unit per chain, chunks handed over
-# through device memory) is selected with VLA_SPLIT=1 when the whole grid fits.
+# The two-pass forward (d_h in {64, 96, 128}): the penalty chain restarts at
+# segment boundaries from a directly formed inverse, so these cases vary the
+# number and length of segments (set by B*H and T) and the initial state.
 
 
-@pytest.fixture
-def split_mode(monkeypatch):
-    monkeypatch.setenv("VLA_SPLIT", "1")
-
-
-@pytest.mark.parametrize("d,dtype,T", [(64, "bf16", 300), (64, "f32", 16), (96, "f32", 129),
-                                       (128, "bf16", 77), (128, "f32", 1)])
-def test_split_shapes_every_head(split_mode, d, dtype, T):
+@pytest.mark.parametrize("d,dtype,B,H,T", [
+    (64, "bf16", 1, 1, 2000),     # one head: many short segments
+    (96, "f32", 1, 3, 1111),      # ragged last segment and chunk
+    (128, "bf16", 1, 2, 1500),
+    (128, "f32", 3, 1, 33),       # three chunks, one segment
+    (64, "f32", 4, 128, 160),     # 512 heads: a single segment each
+])
+def test_segments_every_head(d, dtype, B, H, T):
     dev = _dev()
-    base = gen.config(3 if dtype == "bf16" else 2)
     import dataclasses
-    cfg = dataclasses.replace(base, d=d).with_sizes(B=2, H=3, T=T)
-    _say(f"split d={d} {dtype} T={T}")
+    base = gen.config(3 if dtype == "bf16" else 2)
+    cfg = dataclasses.replace(base, d=d).with_sizes(B=B, H=H, T=T)
+    _say(f"segments d={d} {dtype} B={B} H={H} T={T}")
     x = gen.make_inputs(cfg)
     out = _gpu_forward(cfg, x, dev)
     ref = oracle.forward(*(_f64(x[n], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
@@ -301,26 +302,48 @@ def test_split_shapes_every_head(split_mode, d, dtype, T):
         _check(name, g, ref[name])
 
 
-def test_split_full_size_sampled_heads(split_mode):
+def test_continuation_given_state_many_segments():
+    """A caller-given initial state with many segments (the inverse of A0 is
+    formed too), written to separate outputs and then in place."""
     dev = _dev()
-    cfg = gen.config(3)
-    _say(f"split {cfg.name} (full size)")
+    vla = _vla()
+    cfg = gen.config(3).with_sizes(B=1, H=2, T=1200)
     x = gen.make_inputs(cfg)
-    out = _gpu_forward(cfg, x, dev)
-    assert np.isfinite(out[0]).all()
-    _compare_heads(cfg, x, out, [(0, 0), (4, 9), (7, 15)])
+    t = {n: _to_dev(x[n], cfg, dev) for n in "qkvu"}
+    T1 = 700
+    o1, S1, A1, z1 = vla.vla_forward(*(t[n][:, :, :T1].contiguous() for n in "qkvu"),
+                                     return_state=True)
+    rest = [t[n][:, :, T1:].contiguous() for n in "qkvu"]
+    o2, S2, A2, z2 = vla.vla_forward(*rest, S0=S1, A0=A1, zkey0=z1, return_state=True)
+    o3 = vla.vla_forward(*rest, S0=S1, A0=A1, zkey0=z1, S_out=S1, A_out=A1, zkey_out=z1)[0]
+    torch.cuda.synchronize()
+    ref = oracle.forward(*(_f64(x[n], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+    _check("o", np.concatenate([o1.cpu().numpy(), o2.cpu().numpy()], axis=2), ref["o"])
+    for name, g in (("S", S2), ("A", A2), ("zkey", z2)):
+        _check(name, g.cpu().numpy(), ref[name])
+    assert torch.equal(o2, o3)
+    assert torch.equal(S1, S2) and torch.equal(A1, A2) and torch.equal(z1, z2)
 
 
-def test_split_matches_fused_bitwise(monkeypatch):
-    """Both arrangements run the same arithmetic in the same order."""
+def test_workspace_reuse_and_stream():
+    """An explicit workspace (dirty from an earlier call of another shape) and a
+    side stream give the same bits as a fresh allocation."""
     dev = _dev()
-    cfg = gen.config(3).with_sizes(B=2, H=4, T=200)
+    vla = _vla()
+    cfg = gen.config(3).with_sizes(B=2, H=3, T=777)
     x = gen.make_inputs(cfg)
-    monkeypatch.setenv("VLA_SPLIT", "0")
-    a = _gpu_forward(cfg, x, dev)
-    monkeypatch.setenv("VLA_SPLIT", "1")
-    b = _gpu_forward(cfg, x, dev)
-    c = _gpu_forward(cfg, x, dev)
-    for ga, gb, gc in zip(a, b, c):
-        assert np.array_equal(ga, gb)
-        assert np.array_equal(gb, gc)
+    t = {n: _to_dev(x[n], cfg, dev) for n in "qkvu"}
+    ref = vla.vla_forward(*(t[n] for n in "qkvu"), return_state=True)
+    ws = torch.full((vla.workspace_size(2, 3, 2000, 64),), 0xAB, dtype=torch.uint8, device=dev)
+    other = gen.config(3).with_sizes(B=2, H=3, T=2000)
+    xo = gen.make_inputs(other)
+    vla.vla_forward(*(_to_dev(xo[n], other, dev) for n in "qkvu"), workspace=ws)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = vla.vla_forward(*(t[n] for n in "qkvu"), return_state=True, workspace=ws,
+                              stream=side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
