@@ -6,11 +6,12 @@ workload (B = 8, H = 16, bf16 q/k/v/u, fp32 state), writing o and the final
 S, A and zkey.  Inputs are resident in HBM before the timed region.
 
 Prints ONE JSON line with the throughput in tokens*heads/s, the percentage of
-the MI355X FP32 peak, a roofline record for the forward kernel (algorithmic
-FLOP / average kernel time from HIP events on the launch stream; the kernel
-does its d x d products on fp32 matrix cores, whose dense peak equals the FP32
-vector peak) and the fp64 CPU oracle timed on the host cores over a bounded
-sample of heads.
+the MI355X FP32 peak, a roofline record for the forward (algorithmic FLOP /
+average time of its launches from HIP events on the launch stream; the kernels
+do their d x d products on fp32 matrix cores, whose dense peak equals the FP32
+vector peak), the same for each of its two passes (penalty: Grams, segment
+inverses and the penalty chain; memory: the memory chain and readout), and the
+fp64 CPU oracle timed on the host cores over a bounded sample of heads.
 """
 import argparse
 import hashlib
@@ -82,6 +83,10 @@ def flops_per_token_head(d: int) -> int:
     A u^, A k^, S k^ and S phi(q) (2 d^2 each) and the rank-1 updates of A and
     S (2 d^2 each); O(d) terms are not counted."""
     return 12 * d * d
+
+
+def tok_heads_total(cfg) -> int:
+    return cfg.B * cfg.H * cfg.T
 
 
 def parse():
@@ -221,6 +226,25 @@ def main():
 
     launch_ms = [s.elapsed_time(e) for s, e in ev]
     kern_ms = float(np.mean(launch_ms))
+
+    # the two passes, timed apart on the same stream
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e0, e1, e2 in pev:
+        e0.record(stream)
+        vla.vla_forward_penalty(t["q"], t["k"], t["u"], cfg.lambda0, cfg.eps, workspace=ws,
+                                A_out=A, zkey_out=zk, stream=stream)
+        e1.record(stream)
+        vla.vla_forward_memory(t["q"], t["k"], t["v"], workspace=ws, o=o, S_out=S, stream=stream)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    pen_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in pev]))
+    mem_ms = float(np.mean([b.elapsed_time(c) for _, b, c in pev]))
+    half = flops_per_token_head(d) // 2 * tok_heads_total(cfg)
+
+    def phase(ms):
+        tf = half / (ms / 1e3) / 1e12
+        return {"ms": ms, "achieved": tf, "frac": tf / FP32_VECTOR_PEAK_TFLOPS,
+                "flop_per_launch": half}
     ms_per_step = wall * 1e3 / args.steps
     tok_heads = B * H * T
     value = tok_heads / (ms_per_step / 1e3)
@@ -249,8 +273,12 @@ def main():
                      "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
                      "traffic": measured_traffic(),
+                     "kernel": "vla_forward: vla_gram, vla_seginv, vla_pen, vla_mem launches",
                      "kernel_ms": kern_ms, "kernel_ms_median": float(np.median(launch_ms)),
-                     "flop_per_launch": flop, "dtype": "fp32"},
+                     "flop_per_launch": flop, "dtype": "fp32",
+                     "phases": {"penalty (vla_gram+vla_seginv+vla_pen; A u^, A k^, A update)":
+                                phase(pen_ms),
+                                "memory (vla_mem; S k^, S phi(q), S update)": phase(mem_ms)}},
         "device_peak": device_peak_tflops(),
     }
     res["decode"] = decode_bench(vla, torch)

@@ -95,6 +95,33 @@ vla_status vla_forward(const void *q, const void *k, const void *v, const void *
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * vla_forward_penalty, vla_forward_memory -- the two passes of vla_forward for
+ * d_h in {64, 96, 128} and T >= 1, for callers that schedule them apart (for
+ * example the penalty pass of one batch on a second stream while the memory
+ * pass of the previous batch runs).  Calling vla_forward_penalty and then
+ * vla_forward_memory on the same workspace and the same inputs, in stream
+ * order, gives exactly the results of vla_forward.
+ *
+ * vla_forward_penalty runs the penalty chain of Eq. (9) and, for every chunk of
+ * 16 tokens, leaves the factors the memory chain needs (alpha^ of Eq. (10), the
+ * key-sum denominators of Eq. (11)) in the workspace; it writes the final A and
+ * zkey (A_out, zkey_out may be NULL).  vla_forward_memory then runs Eqs. (10)
+ * and (11) from those factors and q, k, v, writing o and the final S.  Between
+ * the two calls the workspace must not be used by anything else.  Arguments and
+ * errors as for vla_forward; d_h in {16, 32} is VLA_ERR_UNSUPPORTED and T < 1
+ * VLA_ERR_INVALID_ARG.
+ */
+vla_status vla_forward_penalty(const void *q, const void *k, const void *u, int in_dtype,
+                               int B, int H, int T, int d_h, float lambda0, float eps,
+                               float *A_out, float *zkey_out, const float *A0,
+                               const float *zkey0, void *workspace, size_t workspace_bytes,
+                               void *stream);
+vla_status vla_forward_memory(const void *q, const void *k, const void *v, int in_dtype,
+                              int B, int H, int T, int d_h, float *o, float *S_out,
+                              const float *S0, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
  * vla_forward_workspace_size -- bytes of device workspace vla_forward needs for
  * these sizes (0 when it needs none: d_h in {16, 32}, or T == 0), in *bytes.
  * At d_h = 64 it is about 6.2 KB per 16 tokens of each head (the per-chunk

@@ -38,6 +38,15 @@ def load() -> ctypes.CDLL:
         lib.vla_forward.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.vla_forward_penalty.restype = ctypes.c_int
+        lib.vla_forward_penalty.argtypes = [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                            ctypes.c_float, _vp, _vp, _vp, _vp, _vp,
+                                            ctypes.c_size_t, _vp]
+        lib.vla_forward_memory.restype = ctypes.c_int
+        lib.vla_forward_memory.argtypes = [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                           ctypes.c_size_t, _vp]
         lib.vla_forward_workspace_size.restype = ctypes.c_int
         lib.vla_forward_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                    ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
@@ -134,14 +143,7 @@ def vla_forward(q, k, v, u, lambda0: float = 0.1, eps: float = 1e-4, *,
                          ("zkey_out", zkey_out, (B, H, d)), ("S0", S0, (B, H, d, d)),
                          ("A0", A0, (B, H, d, d)), ("zkey0", zkey0, (B, H, d))):
         _check(t, name, shp, f32, dev)
-    need = workspace_size(B, H, T, d)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
-    elif need:
-        if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
-        if workspace.numel() * workspace.element_size() < need:
-            raise ValueError(f"workspace: need {need} bytes")
+    workspace = _workspace(workspace, B, H, T, d, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().vla_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _dtype_code(q), B, H, T, d,
                             float(lambda0), float(eps), _ptr(o), _ptr(S_out), _ptr(A_out),
@@ -150,6 +152,64 @@ def vla_forward(q, k, v, u, lambda0: float = 0.1, eps: float = 1e-4, *,
     if st != VLA_OK:
         raise VLAError(st, "vla_forward")
     return (o, S_out, A_out, zkey_out) if want_state else o
+
+
+def _workspace(workspace, B, H, T, d, dev):
+    torch = _torch()
+    need = workspace_size(B, H, T, d)
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    if need:
+        if not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace: need {need} bytes")
+    return workspace
+
+
+def vla_forward_penalty(q, k, u, lambda0: float = 0.1, eps: float = 1e-4, *, workspace,
+                        A_out=None, zkey_out=None, A0=None, zkey0=None, stream=None):
+    """First pass of the forward (d_h in {64, 96, 128}): the penalty chain and the
+    per-chunk factors, left in ``workspace`` (a device byte tensor of at least
+    ``workspace_size(B, H, T, d_h)`` bytes).  Writes ``A_out``/``zkey_out`` if given."""
+    B, H, T, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("u", u)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    f32 = _torch().float32
+    for name, t, shp in (("A_out", A_out, (B, H, d, d)), ("zkey_out", zkey_out, (B, H, d)),
+                         ("A0", A0, (B, H, d, d)), ("zkey0", zkey0, (B, H, d))):
+        _check(t, name, shp, f32, dev)
+    workspace = _workspace(workspace, B, H, T, d, dev)
+    st = load().vla_forward_penalty(_ptr(q), _ptr(k), _ptr(u), _dtype_code(q), B, H, T, d,
+                                    float(lambda0), float(eps), _ptr(A_out), _ptr(zkey_out),
+                                    _ptr(A0), _ptr(zkey0), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != VLA_OK:
+        raise VLAError(st, "vla_forward_penalty")
+
+
+def vla_forward_memory(q, k, v, *, workspace, o=None, S_out=None, S0=None, stream=None):
+    """Second pass of the forward: the memory chain and the readout from the
+    factors ``vla_forward_penalty`` left in ``workspace``.  Returns ``o``."""
+    torch = _torch()
+    B, H, T, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    f32 = torch.float32
+    if o is None:
+        o = torch.empty((B, H, T, d), dtype=f32, device=dev)
+    _check(o, "o", (B, H, T, d), f32, dev)
+    _check(S_out, "S_out", (B, H, d, d), f32, dev)
+    _check(S0, "S0", (B, H, d, d), f32, dev)
+    workspace = _workspace(workspace, B, H, T, d, dev)
+    st = load().vla_forward_memory(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, d, _ptr(o),
+                                   _ptr(S_out), _ptr(S0), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != VLA_OK:
+        raise VLAError(st, "vla_forward_memory")
+    return o
 
 
 def vla_step(q, k, v, u, S, A, zkey, eps: float = 1e-4, *, o=None, stream=None):

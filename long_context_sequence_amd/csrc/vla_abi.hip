@@ -36,7 +36,7 @@ vla_status launch(const vla::FwdArgs &a, bool step)
     else if (step || a.T == 0)
         e = vla::launch_forward_chunk(a);
     else
-        e = vla::launch_forward_twopass(a);
+        e = vla::launch_forward_twopass(a, 3);
     return e == hipSuccess ? VLA_OK : VLA_ERR_HIP;
 }
 
@@ -74,6 +74,53 @@ extern "C" vla_status vla_forward(const void *q, const void *k, const void *v, c
                    o, S_out, A_out, zkey_out, S0, A0, zkey0, (hipStream_t)stream,
                    workspace, workspace_bytes};
     return launch(a, false);
+}
+
+// The two phases of the two-pass forward (d_h in {64, 96, 128}, T >= 1).
+static vla_status check_phase(int in_dtype, int B, int H, int T, int d_h, float eps, void *workspace,
+                       size_t workspace_bytes)
+{
+    vla_status st = check_common(in_dtype, B, H, d_h, eps);
+    if (st != VLA_OK) return st;
+    if (!vla::chunk_supported(d_h)) return VLA_ERR_UNSUPPORTED;
+    if (T < 1) return VLA_ERR_INVALID_ARG;
+    const size_t need = ::workspace_bytes(B, H, T, d_h);
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need) return VLA_ERR_INVALID_ARG;
+    return VLA_OK;
+}
+
+extern "C" vla_status vla_forward_penalty(const void *q, const void *k, const void *u, int in_dtype,
+                                          int B, int H, int T, int d_h, float lambda0, float eps,
+                                          float *A_out, float *zkey_out, const float *A0,
+                                          const float *zkey0, void *workspace,
+                                          size_t workspace_bytes, void *stream)
+{
+    vla_status st = check_phase(in_dtype, B, H, T, d_h, eps, workspace, workspace_bytes);
+    if (st != VLA_OK) return st;
+    if (!finite_pos(lambda0)) return VLA_ERR_INVALID_ARG;
+    if (!ok_ptr(q, true) || !ok_ptr(k, true) || !ok_ptr(u, true) || !ok_ptr(A_out, false) ||
+        !ok_ptr(zkey_out, false) || !ok_ptr(A0, false) || !ok_ptr(zkey0, false))
+        return VLA_ERR_INVALID_ARG;
+    vla::FwdArgs a{q, k, nullptr, u, in_dtype, B, H, T, d_h, lambda0, eps,
+                   nullptr, nullptr, A_out, zkey_out, nullptr, A0, zkey0, (hipStream_t)stream,
+                   workspace, workspace_bytes};
+    return vla::launch_forward_twopass(a, 1) == hipSuccess ? VLA_OK : VLA_ERR_HIP;
+}
+
+extern "C" vla_status vla_forward_memory(const void *q, const void *k, const void *v, int in_dtype,
+                                         int B, int H, int T, int d_h, float *o, float *S_out,
+                                         const float *S0, void *workspace, size_t workspace_bytes,
+                                         void *stream)
+{
+    vla_status st = check_phase(in_dtype, B, H, T, d_h, 1.0f, workspace, workspace_bytes);
+    if (st != VLA_OK) return st;
+    if (!ok_ptr(q, true) || !ok_ptr(k, true) || !ok_ptr(v, true) || !ok_ptr(o, true) ||
+        !ok_ptr(S_out, false) || !ok_ptr(S0, false))
+        return VLA_ERR_INVALID_ARG;
+    vla::FwdArgs a{q, k, v, nullptr, in_dtype, B, H, T, d_h, 1.0f, 1.0f,
+                   o, S_out, nullptr, nullptr, S0, nullptr, nullptr, (hipStream_t)stream,
+                   workspace, workspace_bytes};
+    return vla::launch_forward_twopass(a, 2) == hipSuccess ? VLA_OK : VLA_ERR_HIP;
 }
 
 extern "C" vla_status vla_forward_workspace_size(int B, int H, int T, int d_h, size_t *bytes)

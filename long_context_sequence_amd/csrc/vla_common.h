@@ -37,8 +37,10 @@ hipError_t launch_forward_ref(const FwdArgs &a);
 bool chunk_supported(int d);
 // one workgroup per head with both chains (decode steps and T = 0)
 hipError_t launch_forward_chunk(const FwdArgs &a);
-// two passes over the sequence (forward, T >= 1); needs the workspace below
+// two passes over the sequence (forward, T >= 1); needs the workspace below.
+// phases: 1 = penalty pass (Grams, segment inverses, penalty chain and the
+// per-chunk factors in the workspace), 2 = memory pass, 3 = both.
 size_t twopass_workspace_bytes(int BH, int T, int d);
-hipError_t launch_forward_twopass(const FwdArgs &a);
+hipError_t launch_forward_twopass(const FwdArgs &a, int phases);
 
 }  // namespace vla

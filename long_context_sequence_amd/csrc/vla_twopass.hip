@@ -40,6 +40,7 @@ namespace {
 using namespace chunk;
 
 constexpr int CH = 16;   // tokens per chunk (Cfg<D>::C)
+constexpr int MPD = 2;   // memory pass: chunks its operand loads run ahead
 
 // One chunk's record (floats).
 template <int D>
@@ -60,29 +61,45 @@ template <> struct MemCfg<96> { static constexpr int VBW = 2; };
 template <> struct MemCfg<128> { static constexpr int VBW = 1; };
 
 // ------------------------------------------------------------------- gram
-// Workgroup (head, segment j < S - 1): G_j = sum of u^ u^' and z_j = sum of
-// phi(k) over the tokens of segment j.  Tokens go in blocks of GB = 64; thread
-// (token tl, part cc) stages columns [cc CPT, +CPT) of u^ of tokens tl + 16 s
-// (s < 4) of a block, transposed ([i][token]), while the loads of the next
-// block are in flight; wave w owns the 16 x 16 tiles w + 4 t of G.  Each
-// block's fp32 matrix-core partial sums are added to fp64 accumulators.
+// Workgroup (head, segment j < S - 1, part pp < P): the part's share of
+// G_j = sum of u^ u^' and z_j = sum of phi(k) over segment j (the segment's
+// chunks split in P runs, so that the launch has enough workgroups).  Tokens go
+// in blocks of GB = 64; thread (token tl, part cc) stages columns [cc CPT, +CPT)
+// of u^ of tokens tl + 16 s (s < 4) of a block, transposed ([i][token]), while
+// the loads of the next block are in flight.  G is symmetric: only its tiles
+// (a, b) with a <= b are formed, wave w taking tiles w, w + 4, ..., and stored
+// with their mirror images.  Each block's fp32 matrix-core partial sums are
+// added to fp64 accumulators.
 template <int D, typename Tin>
 __global__ void __launch_bounds__(256)
-vla_gram(const Tin *__restrict__ k, const Tin *__restrict__ u, int T, int S, int SC,
+vla_gram(const Tin *__restrict__ k, const Tin *__restrict__ u, int T, int S, int SC, int P,
          double *__restrict__ gram, double *__restrict__ zks)
 {
-    constexpr int NB = D / 16, TPW = NB * NB / 4, CPT = D / 16, GB = 64, LT = GB + 4;
+    constexpr int NB = D / 16, NTILE = NB * (NB + 1) / 2, TPW = (NTILE + 3) / 4;
+    constexpr int CPT = D / 16, GB = 64, LT = GB + 4;
     __shared__ __align__(16) float ut[2][D * LT];
     __shared__ double zred[256 * CPT];
 
     const int S1 = S - 1;
-    const int bh = blockIdx.x / S1, j = blockIdx.x % S1;
+    const int pp = blockIdx.x % P, j = (blockIdx.x / P) % S1, bh = blockIdx.x / (P * S1);
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tl = tid >> 4, cc = tid & 15;
-    const int t0 = j * SC * CH, t1 = min(T, t0 + SC * CH);   // the segment's tokens
-    const int NBK = (t1 - t0 + GB - 1) / GB;
+    const int PC = (SC + P - 1) / P;                 // chunks per part
+    const int cb = j * SC + pp * PC, ce = min(j * SC + SC, cb + PC);
+    const int t0 = cb * CH, t1 = min(T, ce * CH);   // the part's tokens (may be none)
+    const int NBK = t1 > t0 ? (t1 - t0 + GB - 1) / GB : 0;
     const Tin *uh = u + (size_t)bh * T * D, *kh = k + (size_t)bh * T * D;
+
+    // tile index -> (a, b), a <= b
+    int ta[TPW], tb[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        int idx = w + 4 * t, a = 0;
+        while (idx >= NB - a && a < NB - 1) { idx -= NB - a; ++a; }
+        ta[t] = a;
+        tb[t] = a + idx;
+    }
 
     RawVec<Tin, CPT> ru[4], rk[4];
     double zacc[CPT];
@@ -123,25 +140,28 @@ vla_gram(const Tin *__restrict__ k, const Tin *__restrict__ u, int T, int S, int
         }
     };
 
-    prefetch(0);
-    stage(0);
-    if (NBK > 1) prefetch(1);
+    if (NBK > 0) {
+        prefetch(0);
+        stage(0);
+        if (NBK > 1) prefetch(1);
+    }
     vmem_drain();
     __syncthreads();
     for (int blk = 0; blk < NBK; ++blk) {
         const float *src = ut[blk & 1];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            const int tix = w + 4 * t, a = tix / NB, b = tix % NB;
-            f4 acc = zero;
+            if (w + 4 * t < NTILE) {
+                f4 acc = zero;
 #pragma unroll
-            for (int s2 = 0; s2 < GB / 16; ++s2) {
-                const f4 af = ld4(&src[(16 * a + n) * LT + 16 * s2 + 4 * g]);   // u^[16a+n][tok]
-                const f4 bf = ld4(&src[(16 * b + n) * LT + 16 * s2 + 4 * g]);   // u^[16b+n][tok]
-                acc = mma4(af, bf, acc);
+                for (int s2 = 0; s2 < GB / 16; ++s2) {
+                    const f4 af = ld4(&src[(16 * ta[t] + n) * LT + 16 * s2 + 4 * g]);
+                    const f4 bf = ld4(&src[(16 * tb[t] + n) * LT + 16 * s2 + 4 * g]);
+                    acc = mma4(af, bf, acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gacc[t][r] += (double)acc[r];
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) gacc[t][r] += (double)acc[r];
         }
         if (blk + 1 < NBK) {
             stage(blk + 1);
@@ -150,12 +170,20 @@ vla_gram(const Tin *__restrict__ k, const Tin *__restrict__ u, int T, int S, int
         lds_barrier();
     }
 
-    double *G = gram + ((size_t)bh * S1 + j) * D * D;
+    // full symmetric matrix: off-diagonal tiles are written twice
+    double *G = gram + (((size_t)bh * S1 + j) * P + pp) * D * D;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-        const int tix = w + 4 * t, a = tix / NB, b = tix % NB;
+        if (w + 4 * t < NTILE) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) G[(size_t)(16 * a + 4 * g + r) * D + 16 * b + n] = gacc[t][r];
+            for (int r = 0; r < 4; ++r)
+                G[(size_t)(16 * ta[t] + 4 * g + r) * D + 16 * tb[t] + n] = gacc[t][r];
+            if (ta[t] != tb[t]) {
+                double2 *Gt = reinterpret_cast<double2 *>(&G[(size_t)(16 * tb[t] + n) * D + 16 * ta[t] + 4 * g]);
+                Gt[0] = make_double2(gacc[t][0], gacc[t][1]);
+                Gt[1] = make_double2(gacc[t][2], gacc[t][3]);
+            }
+        }
     }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) zred[tid * CPT + i] = zacc[i];
@@ -164,51 +192,92 @@ vla_gram(const Tin *__restrict__ k, const Tin *__restrict__ u, int T, int S, int
         const int pc = tid / CPT, pi = tid % CPT;
         double z = 0.0;
         for (int t2 = 0; t2 < CH; ++t2) z += zred[(t2 * 16 + pc) * CPT + pi];
-        zks[((size_t)bh * S1 + j) * D + tid] = z;
+        zks[(((size_t)bh * S1 + j) * P + pp) * D + tid] = z;
     }
 }
 
 // ------------------------------------------------------------------- inverse
-// In-place symmetric sweep of all pivots: M -> -M^-1 (M symmetric positive
-// definite; no pivoting is needed).  Thread (row i, columns [c0, c0 + EPT))
-// holds its entries in m; row k of the current matrix and 1 / m[k][k] are
-// broadcast through rowbuf (double-buffered, so one barrier per pivot; the
-// owner of the diagonal entry forms the reciprocal).  Branch-free: every
-// entry takes one of three candidate values by selects.
+// In-place symmetric sweep of all pivots, four at a time: M -> -M^-1 (M
+// symmetric positive definite, so no pivoting is needed).  Thread (row i,
+// columns [c0, c0 + EPT)) holds its entries in m.  For the pivot block K of
+// rows/columns 4s .. 4s+3 with diagonal block B, rows K of the current matrix
+// are published with B replaced by B - I (R, 4 x D), together with B^-1; then
+//     m <- m - (R' B^-1) R
+// gives every entry of the block sweep except the diagonal of B's block, which
+// is 2 too large.  One barrier per block (row buffers double-buffered); the
+// first thread of row 4s forms B^-1 (4 x 4 Gauss-Jordan, fp64).  Only
+// compile-time indices into m, so that it stays in registers.
 template <int D, int EPT>
-__device__ __forceinline__ void sweep_all(double (&m)[EPT], int i, int c0, double (*rowbuf)[D + 2])
+__device__ __forceinline__ void sweep_all(double (&m)[EPT], int i, int c0, double (*rowbuf)[4 * D + 16])
 {
-    static_assert(EPT % 2 == 0, "row slices are read as pairs");
-    // pivot row k with its diagonal entry p replaced by p - 1, and 1/p: then
-    // m <- m - (r 1/p) r' gives every entry of the sweep but (k, k), which is 2
-    // too large.  (Only compile-time indices into m, so that it stays in
-    // registers.)
-    auto publish = [&](int row, int slot) {
-        if (i == row) {
-            const int ed = row - c0;
-            double piv = 0.0;
-            sfor<EPT>([&](auto e) {
-                rowbuf[slot][c0 + e] = e == ed ? m[e] - 1.0 : m[e];
-                piv = e == ed ? m[e] : piv;
-            });
-            if (ed >= 0 && ed < EPT) rowbuf[slot][D] = 1.0 / piv;
+    static_assert(EPT % 2 == 0 && D % 4 == 0, "row slices are read as pairs");
+    auto publish = [&](int s, int slot) {
+        const int k = 4 * s;
+        if (i >= k && i < k + 4) {
+            double *rw = rowbuf[slot] + (i - k) * D;
+            sfor<EPT>([&](auto e) { rw[c0 + e] = c0 + e == i ? m[e] - 1.0 : m[e]; });
+            wave_lds_order();   // rows K sit in one wave (threads 8k .. 8k+31)
+            if (i == k && c0 == 0) {
+                double bm[4][8];   // [B | I] -> [I | B^-1]
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        bm[r][c] = rowbuf[slot][r * D + k + c] + (r == c ? 1.0 : 0.0);
+                        bm[r][4 + c] = r == c ? 1.0 : 0.0;
+                    }
+#pragma unroll
+                for (int pv = 0; pv < 4; ++pv) {
+                    const double ip = 1.0 / bm[pv][pv];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) bm[pv][c] *= ip;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (r == pv) continue;
+                        const double f = bm[r][pv];
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) bm[r][c] = fma(-f, bm[pv][c], bm[r][c]);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) rowbuf[slot][4 * D + 4 * r + c] = bm[r][4 + c];
+            }
         }
     };
     publish(0, 0);
     __syncthreads();
-    for (int kk = 0; kk < D; ++kk) {
-        const double *rb = rowbuf[kk & 1];
-        const double ui = rb[i] * rb[D];
-        sfor<EPT / 2>([&](auto h) {
-            const double2 x = *reinterpret_cast<const double2 *>(&rb[c0 + 2 * h]);
-            m[2 * h] = fma(-ui, x.x, m[2 * h]);
-            m[2 * h + 1] = fma(-ui, x.y, m[2 * h + 1]);
-        });
-        if (i == kk) {   // the lane holding (k, k)
-            const int ed = kk - c0;
+    for (int sb = 0; sb < D / 4; ++sb) {
+        const double *rb = rowbuf[sb & 1];
+        double bi[16];
+#pragma unroll
+        for (int q = 0; q < 16; q += 2) {
+            const double2 x = *reinterpret_cast<const double2 *>(&rb[4 * D + q]);
+            bi[q] = x.x;
+            bi[q + 1] = x.y;
+        }
+        double ui[4] = {0.0, 0.0, 0.0, 0.0};   // row i of R' B^-1
+#pragma unroll
+        for (int a2 = 0; a2 < 4; ++a2) {
+            const double ra = rb[a2 * D + i];
+#pragma unroll
+            for (int b2 = 0; b2 < 4; ++b2) ui[b2] = fma(ra, bi[4 * a2 + b2], ui[b2]);
+        }
+#pragma unroll
+        for (int b2 = 0; b2 < 4; ++b2) {
+            sfor<EPT / 2>([&](auto h) {
+                const double2 x = *reinterpret_cast<const double2 *>(&rb[b2 * D + c0 + 2 * h]);
+                m[2 * h] = fma(-ui[b2], x.x, m[2 * h]);
+                m[2 * h + 1] = fma(-ui[b2], x.y, m[2 * h + 1]);
+            });
+        }
+        const int k = 4 * sb;
+        if (i >= k && i < k + 4) {   // the lanes holding the block diagonal
+            const int ed = i - c0;
             sfor<EPT>([&](auto e) { m[e] -= e == ed ? 2.0 : 0.0; });
         }
-        if (kk + 1 < D) publish(kk + 1, (kk + 1) & 1);
+        if (sb + 1 < D / 4) publish(sb + 1, (sb + 1) & 1);
         __syncthreads();
     }
 }
@@ -220,12 +289,12 @@ __device__ __forceinline__ void sweep_all(double (&m)[EPT], int i, int c0, doubl
 // the initial one.
 template <int D>
 __global__ void __launch_bounds__(8 * D)
-vla_seginv(int S, float lambda0, const float *A0, const float *zk0,
+vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
            const double *__restrict__ gram, const double *__restrict__ zks,
            float *__restrict__ aseg, float *__restrict__ zseg)
 {
     constexpr int EPT = D / 8;
-    __shared__ __align__(16) double rowbuf[2][D + 2];
+    __shared__ __align__(16) double rowbuf[2][4 * D + 16];
     const int S1 = S - 1;
     const int bh = blockIdx.x / S1, j = blockIdx.x % S1 + 1;
     const int tid = threadIdx.x, i = tid >> 3, c0 = (tid & 7) * EPT;
@@ -241,16 +310,22 @@ vla_seginv(int S, float lambda0, const float *A0, const float *zk0,
     } else {
         sfor<EPT>([&](auto e) { m[e] = i == c0 + e ? (double)lambda0 : 0.0; });
     }
-    for (int s = 0; s < j; ++s) {
-        const double *G = gram + ((size_t)bh * S1 + s) * DD + (size_t)i * D + c0;
-        sfor<EPT>([&](auto e) { m[e] += G[e]; });
+    // G parts of the segments before j
+    for (int s = 0; s < j * P; ++s) {
+        const double2 *G = reinterpret_cast<const double2 *>(gram + ((size_t)bh * S1 * P + s) * DD +
+                                                             (size_t)i * D + c0);
+        sfor<EPT / 2>([&](auto h) {
+            const double2 x = G[h];
+            m[2 * h] += x.x;
+            m[2 * h + 1] += x.y;
+        });
     }
     sweep_all<D, EPT>(m, i, c0, rowbuf);   // -M^-1
     float *A = aseg + ((size_t)bh * S + j) * DD + (size_t)i * D + c0;
     sfor<EPT>([&](auto e) { A[e] = (float)(-m[e]); });
     if (tid < D) {
         double z = zk0 ? (double)zk0[bh * D + tid] : 0.0;
-        for (int s = 0; s < j; ++s) z += zks[((size_t)bh * S1 + s) * D + tid];
+        for (int s = 0; s < j * P; ++s) z += zks[((size_t)bh * S1 * P + s) * D + tid];
         zseg[((size_t)bh * S + j) * D + tid] = (float)z;
         if (zk0 && j == 1) zseg[(size_t)bh * S * D + tid] = zk0[bh * D + tid];
     }
@@ -379,7 +454,7 @@ struct MemOps {
 // w / KS and key tiles [NT (w % KS), +NT).  The state tiles are S' in MFMA
 // accumulator layout (register r of lane 16 g + n of tile rho holds
 // S[16 b + n][16 rho + 4 g + r]).  Every operand comes straight from device
-// memory into registers, two chunks ahead (three operand sets in rotation).
+// memory into registers, MPD = 2 chunks ahead (three operand sets in rotation).
 // Per chunk c:
 //   (S K)' and (S Phi)' partials of the own key tiles (K raw; the rows are
 //   scaled by 1/|k| after the sum) -> LDS                          | barrier
@@ -459,7 +534,7 @@ vla_mem(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     // clamp, and the waves that do not write o store through an empty view), so
     // that the compiler's wait counts can leave the next chunks' loads in flight.
     auto step = [&](int c, const MemOps<Tin, NT> &m, MemOps<Tin, NT> &pre) {
-        load(min(c + 2, NC - 1), pre);
+        load(min(c + MPD, NC - 1), pre);
         const int sl = c & 1;
         f4 sk = zero, sq = zero;
 #pragma unroll
@@ -502,6 +577,7 @@ vla_mem(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     MemOps<Tin, NT> m0, m1, m2;
     load(0, m0);
     load(min(1, NC - 1), m1);
+    vmem_drain();   // nothing pending at the loop entry: the wait counts inside stay exact
     int c = 0;
     for (; c + 3 <= NC; c += 3) {
         step(c, m0, m2);
@@ -521,7 +597,7 @@ vla_mem(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
 inline size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Plan {
-    int NC = 0, S = 1, SC = 0;
+    int NC = 0, S = 1, SC = 0, P = 1;   // chunks, segments, chunks per segment, gram parts
     size_t rec = 0, gram = 0, zks = 0, aseg = 0, zseg = 0, bytes = 0;
 };
 
@@ -538,15 +614,20 @@ Plan make_plan(int BH, int T, int D)
     S = S < smax ? S : smax;
     p.SC = (p.NC + S - 1) / S;
     p.S = (p.NC + p.SC - 1) / p.SC;
+    if (p.S > 1) {   // gram parts: about 1024 workgroups, each at least 4 chunks
+        const int want = (1024 + BH * (p.S - 1) - 1) / (BH * (p.S - 1));
+        const int most = p.SC / 4 > 1 ? p.SC / 4 : 1;
+        p.P = want < most ? want : most;
+    }
     const int rs = 16 * D + 2 * CH * CH + 2 * CH;   // Rec<D>::SIZE
     size_t off = 0;
     p.rec = off;
     off = up256(off + (size_t)BH * p.NC * rs * sizeof(float));
     if (p.S > 1) {
         p.gram = off;
-        off = up256(off + (size_t)BH * (p.S - 1) * D * D * sizeof(double));
+        off = up256(off + (size_t)BH * (p.S - 1) * p.P * D * D * sizeof(double));
         p.zks = off;
-        off = up256(off + (size_t)BH * (p.S - 1) * D * sizeof(double));
+        off = up256(off + (size_t)BH * (p.S - 1) * p.P * D * sizeof(double));
         p.aseg = off;
         off = up256(off + (size_t)BH * p.S * D * D * sizeof(float));
         p.zseg = off;
@@ -557,7 +638,7 @@ Plan make_plan(int BH, int T, int D)
 }
 
 template <int D, typename Tin>
-hipError_t launch(const FwdArgs &a)
+hipError_t launch(const FwdArgs &a, int phases)
 {
     const int BH = a.B * a.H;
     const Plan p = make_plan(BH, a.T, D);
@@ -569,18 +650,22 @@ hipError_t launch(const FwdArgs &a)
     float *zseg = reinterpret_cast<float *>(ws + p.zseg);
     const Tin *q = (const Tin *)a.q, *k = (const Tin *)a.k, *v = (const Tin *)a.v,
               *u = (const Tin *)a.u;
-    if (p.S > 1) {
-        hipLaunchKernelGGL((vla_gram<D, Tin>), dim3(BH * (p.S - 1)), dim3(256), 0, a.stream, k, u,
-                           a.T, p.S, p.SC, gram, zks);
-        hipLaunchKernelGGL((vla_seginv<D>), dim3(BH * (p.S - 1)), dim3(8 * D), 0, a.stream, p.S,
-                           a.lambda0, a.A0, a.zk0, gram, zks, aseg, zseg);
+    if (phases & 1) {
+        if (p.S > 1) {
+            hipLaunchKernelGGL((vla_gram<D, Tin>), dim3(BH * (p.S - 1) * p.P), dim3(256), 0, a.stream,
+                               k, u, a.T, p.S, p.SC, p.P, gram, zks);
+            hipLaunchKernelGGL((vla_seginv<D>), dim3(BH * (p.S - 1)), dim3(8 * D), 0, a.stream, p.S,
+                               p.P, a.lambda0, a.A0, a.zk0, gram, zks, aseg, zseg);
+        }
+        hipLaunchKernelGGL((vla_pen<D, Tin>), dim3(BH * p.S), dim3(64 * Cfg<D>::NA), 0, a.stream, q,
+                           k, u, a.T, p.S, p.SC, a.lambda0, a.eps, a.A0, a.zk0, aseg, zseg, rec,
+                           a.A_out, a.zk_out);
     }
-    hipLaunchKernelGGL((vla_pen<D, Tin>), dim3(BH * p.S), dim3(64 * Cfg<D>::NA), 0, a.stream, q, k,
-                       u, a.T, p.S, p.SC, a.lambda0, a.eps, a.A0, a.zk0, aseg, zseg, rec, a.A_out,
-                       a.zk_out);
-    constexpr int NG = (D / 16) / MemCfg<D>::VBW;
-    hipLaunchKernelGGL((vla_mem<D, Tin>), dim3(BH * NG), dim3(256), 0, a.stream, q, k, v, a.T, BH,
-                       rec, a.S0, a.o, a.S_out);
+    if (phases & 2) {
+        constexpr int NG = (D / 16) / MemCfg<D>::VBW;
+        hipLaunchKernelGGL((vla_mem<D, Tin>), dim3(BH * NG), dim3(256), 0, a.stream, q, k, v, a.T,
+                           BH, rec, a.S0, a.o, a.S_out);
+    }
     return hipGetLastError();
 }
 
@@ -591,13 +676,13 @@ size_t twopass_workspace_bytes(int BH, int T, int d)
     return make_plan(BH, T, d).bytes;
 }
 
-hipError_t launch_forward_twopass(const FwdArgs &a)
+hipError_t launch_forward_twopass(const FwdArgs &a, int phases)
 {
     const bool bf = a.dtype == 1;
     switch (a.d) {
-    case 64: return bf ? launch<64, uint16_t>(a) : launch<64, float>(a);
-    case 96: return bf ? launch<96, uint16_t>(a) : launch<96, float>(a);
-    case 128: return bf ? launch<128, uint16_t>(a) : launch<128, float>(a);
+    case 64: return bf ? launch<64, uint16_t>(a, phases) : launch<64, float>(a, phases);
+    case 96: return bf ? launch<96, uint16_t>(a, phases) : launch<96, float>(a, phases);
+    case 128: return bf ? launch<128, uint16_t>(a, phases) : launch<128, float>(a, phases);
     default: return hipErrorInvalidValue;
     }
 }

@@ -22,8 +22,8 @@ def _declared_functions():
 
 def test_header_symbols_exported():
     names = _declared_functions()
-    assert {"vla_forward", "vla_forward_workspace_size", "vla_step",
-            "vla_status_string"} <= set(names)
+    assert {"vla_forward", "vla_forward_penalty", "vla_forward_memory",
+            "vla_forward_workspace_size", "vla_step", "vla_status_string"} <= set(names)
     lib = ctypes.CDLL(vla.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in vla.h but not exported"
@@ -90,6 +90,51 @@ def test_workspace_size():
     assert lib.vla_forward_workspace_size(0, 1, 8, 64, ctypes.byref(n)) == B.VLA_ERR_INVALID_ARG
     assert lib.vla_forward_workspace_size(1, 1, -1, 64, ctypes.byref(n)) == B.VLA_ERR_INVALID_ARG
     assert lib.vla_forward_workspace_size(1, 1, 8, 64, None) == B.VLA_ERR_INVALID_ARG
+
+
+def _pen(**kw):
+    a = dict(q=FAKE, k=FAKE, u=FAKE, dt=1, B=2, H=2, T=64, d=64, lam=0.1, eps=1e-4, A=None, z=None,
+             A0=None, z0=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return B.load().vla_forward_penalty(a["q"], a["k"], a["u"], a["dt"], a["B"], a["H"], a["T"],
+                                        a["d"], a["lam"], a["eps"], a["A"], a["z"], a["A0"],
+                                        a["z0"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def _mem(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dt=1, B=2, H=2, T=64, d=64, o=FAKE, S=None, S0=None,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return B.load().vla_forward_memory(a["q"], a["k"], a["v"], a["dt"], a["B"], a["H"], a["T"],
+                                       a["d"], a["o"], a["S"], a["S0"], a["ws"], a["ws_bytes"],
+                                       a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=16), B.VLA_ERR_UNSUPPORTED),
+    (dict(d=32), B.VLA_ERR_UNSUPPORTED),
+    (dict(d=80), B.VLA_ERR_UNSUPPORTED),
+    (dict(T=0), B.VLA_ERR_INVALID_ARG),
+    (dict(ws=None), B.VLA_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 64), B.VLA_ERR_INVALID_ARG),
+    (dict(ws_bytes=4096), B.VLA_ERR_INVALID_ARG),
+    (dict(q=None), B.VLA_ERR_INVALID_ARG),
+    (dict(k=MIS), B.VLA_ERR_INVALID_ARG),
+    (dict(dt=5), B.VLA_ERR_UNSUPPORTED),
+    (dict(B=0), B.VLA_ERR_INVALID_ARG),
+])
+def test_phase_argument_errors(kw, code):
+    assert _pen(**kw) == code
+    assert _mem(**kw) == code
+
+
+def test_phase_specific_argument_errors():
+    assert _pen(lam=-1.0) == B.VLA_ERR_INVALID_ARG
+    assert _pen(u=None) == B.VLA_ERR_INVALID_ARG
+    assert _pen(A=MIS) == B.VLA_ERR_INVALID_ARG
+    assert _mem(v=None) == B.VLA_ERR_INVALID_ARG
+    assert _mem(o=None) == B.VLA_ERR_INVALID_ARG
+    assert _mem(S0=MIS) == B.VLA_ERR_INVALID_ARG
 
 
 def test_forward_empty_no_outputs_is_ok():

@@ -347,3 +347,47 @@ def test_workspace_reuse_and_stream():
     torch.cuda.synchronize()
     for a, b in zip(ref, got):
         assert torch.equal(a, b)
+
+
+def test_phases_equal_forward_and_pipeline_on_two_streams():
+    """vla_forward_penalty then vla_forward_memory give vla_forward's bits; two
+    batches pipelined over two streams (penalty pass of batch 2 while the memory
+    pass of batch 1 runs) give the same bits as well."""
+    dev = _dev()
+    vla = _vla()
+    cfgs = [gen.config(3).with_sizes(B=2, H=2, T=500), gen.config(2).with_sizes(B=1, H=3, T=333)]
+    xs = [gen.make_inputs(c) for c in cfgs]
+    ts = [{n: _to_dev(x[n], c, dev) for n in "qkvu"} for x, c in zip(xs, cfgs)]
+    refs = [vla.vla_forward(*(t[n] for n in "qkvu"), return_state=True) for t in ts]
+    torch.cuda.synchronize()
+    ws = [torch.empty(vla.workspace_size(c.B, c.H, c.T, c.d), dtype=torch.uint8, device=dev)
+          for c in cfgs]
+    outs = []
+    for t, c, w in zip(ts, cfgs, ws):
+        A = torch.empty((c.B, c.H, c.d, c.d), device=dev)
+        z = torch.empty((c.B, c.H, c.d), device=dev)
+        S = torch.empty((c.B, c.H, c.d, c.d), device=dev)
+        outs.append((A, z, S))
+    s1, s2 = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    done_pen = []
+    for i, (t, w, (A, z, S)) in enumerate(zip(ts, ws, outs)):
+        with torch.cuda.stream(s1):
+            vla.vla_forward_penalty(t["q"], t["k"], t["u"], workspace=w, A_out=A, zkey_out=z,
+                                    stream=s1)
+            ev = torch.cuda.Event()
+            ev.record(s1)
+            done_pen.append(ev)
+    os_ = []
+    for i, (t, w, (A, z, S)) in enumerate(zip(ts, ws, outs)):
+        with torch.cuda.stream(s2):
+            s2.wait_event(done_pen[i])
+            os_.append(vla.vla_forward_memory(t["q"], t["k"], t["v"], workspace=w, S_out=S,
+                                              stream=s2))
+    s1.synchronize()
+    s2.synchronize()
+    torch.cuda.synchronize()
+    for (o_ref, S_ref, A_ref, z_ref), o, (A, z, S) in zip(refs, os_, outs):
+        assert torch.equal(o, o_ref)
+        assert torch.equal(S, S_ref) and torch.equal(A, A_ref) and torch.equal(z, z_ref)
