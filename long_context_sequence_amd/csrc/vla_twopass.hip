@@ -18,12 +18,13 @@
 //            inverse by the symmetric sweep operator (fp64), stored as fp32, and
 //            the key sum at the segment start.
 //   penalty  per (head, segment): the blocked penalty chain of vla_chunk_parts.h
-//            from that A; for every chunk of 16 tokens it writes the factors the
-//            memory chain needs to a record: alpha^ (d x C, key-major),
-//            (I + N)^-1 and P = (Alpha^'Phi) o Up (C x C, transposed) and
-//            1 / den (C).  The key sum and den follow Eq. (11).
+//            from that A; for every chunk of 16 tokens it writes the operands
+//            the memory chain needs to a record: alpha^ (d x C, key-major),
+//            (I + N)^-1 and P = (Alpha^'Phi) o Up (C x C, transposed), 1 / den,
+//            and k^ and phi(q) (C x d, token-major).  The key sum and den follow
+//            Eq. (11).
 //   memory   per (head, group of 16-row value blocks): the memory chain from the
-//            records and q, k, v:
+//            records and v:
 //                R = V - S K^,  E = R (I + N)^-1,
 //                o = (S Phi + E P) / den,  S <- S + E Alpha^'.
 //            Rows of S do not interact, so the value rows of a head are split
@@ -50,7 +51,9 @@ struct Rec {
     static constexpr int PT = TT + CH * CH;   // (Alpha^'Phi) o Up, transposed
     static constexpr int RD = PT + CH * CH;   // 1 / den per token
     static constexpr int IK = RD + CH;        // 1 / |k| per token (0 past T)
-    static constexpr int SIZE = IK + CH;      // a multiple of 16
+    static constexpr int KH = IK + CH;        // k^ [token][key] (0 past T)
+    static constexpr int PH = KH + CH * D;    // phi(q) [token][key]
+    static constexpr int SIZE = PH + CH * D;  // a multiple of 16
 };
 
 // Value blocks per memory workgroup (its 4 waves split each block's key tiles
@@ -368,7 +371,7 @@ struct PLds {
 //      stage chunk p+1, prefetch p+2                         | barrier
 //   3  1/|w|, Alpha^'K^ and Alpha^'Phi partials; alpha^ and
 //      1/den to the record                                   | barrier
-//   4  wave 0: (I+N)^-1 and P to the record.
+//   4  wave 1: (I+N)^-1 and P to the record.
 template <int D, typename Tin>
 __global__ void __launch_bounds__(64 * Cfg<D>::NA)
 vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ u,
@@ -387,7 +390,9 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     const int NC = (T + CH - 1) / CH;
     const int c0 = j * SC, c1 = min(NC, c0 + SC);
 
-    Hd hd(L, q, k, nullptr, u, nullptr, T, eps, bh, tid & 63, w, tid, true, tid);
+    // serial work spread over the waves: wave 0 factorises I + G, wave 1 forms
+    // the C x C factors of the record, waves 2 and up own the key sums
+    Hd hd(L, q, k, nullptr, u, nullptr, T, eps, bh, tid & 63, w, tid, true, tid - 128);
     typename Hd::State st;
     const float *a_init;
     if (j > 0)
@@ -429,8 +434,13 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         });
         if (tid < CH) rb[Rec<D>::RD + tid] = L.rden[p & 1][tid];
         else if (tid < 2 * CH) rb[Rec<D>::IK + tid - CH] = L.ikn[p & 1][tid - CH];
+        for (int f = tid; f < CH * D / 4; f += 64 * Cfg<D>::NA) {   // k^ and phi(q), unpadded
+            const int tk = f / (D / 4), c4 = 4 * (f % (D / 4));
+            st4(&rb[Rec<D>::KH + tk * D + c4], ld4(&L.kh[p & 1][tk * Cfg<D>::LD + c4]));
+            st4(&rb[Rec<D>::PH + tk * D + c4], ld4(&L.ph[p & 1][tk * Cfg<D>::LD + c4]));
+        }
         lds_barrier();
-        if (w == 0) hd.prep_tp(rb + Rec<D>::TT, rb + Rec<D>::PT);
+        if (w == 1) hd.prep_tp(rb + Rec<D>::TT, rb + Rec<D>::PT);
     }
     if (j == S - 1) {
         if (A_out) hd.store_state(st, A_out + bh * DD);
@@ -439,14 +449,13 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
 }
 
 // ------------------------------------------------------------------- memory
-// Operands of one chunk for one memory wave, as loaded (raw inputs stay raw):
-// k and q of token n, keys 16 rho + 4 g + [0, 4) (rho = the wave's key tiles);
-// alpha^[16 rho + n][4 g + r]; the transposed C x C factors and 1/den, 1/|k|
-// of tokens 4 g + r; v of token 4 g + r, value 16 b + n.
+// Operands of one chunk for one memory wave, as loaded: k^ and phi(q) of token
+// n, keys 16 rho + 4 g + [0, 4) (rho = the wave's key tiles), and
+// alpha^[16 rho + n][4 g + r], all from the record; the transposed C x C
+// factors and 1/den of tokens 4 g + r; v (raw) of token 4 g + r, value 16 b + n.
 template <typename Tin, int NT>
 struct MemOps {
-    RawVec<Tin, 4> k[NT], q[NT];
-    f4 aw[NT], ta, pa, rd, ik;
+    f4 ak[NT], ap[NT], aw[NT], ta, pa, rd;
     Raw1<Tin> v[4];
 };
 
@@ -462,8 +471,7 @@ struct MemOps {
 //   wave 0 of the block: o' = (P'E' + (S Phi)') / den;  S' += Alpha^ E'.
 template <int D, typename Tin>
 __global__ void __launch_bounds__(256)
-vla_mem(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
-        int T, int BH, const float *__restrict__ rec, const float *S0,
+vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec, const float *S0,
         float *__restrict__ o, float *S_out)
 {
     constexpr int NB = D / 16, VBW = MemCfg<D>::VBW, KS = 4 / VBW, NT = NB / KS;
@@ -491,7 +499,7 @@ vla_mem(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     const size_t DD = (size_t)D * D;
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
     // per-head bases; 32-bit offsets below
-    const Tin *qh = q + (size_t)bh * T * D, *kh = k + (size_t)bh * T * D, *vh = v + (size_t)bh * T * D;
+    const Tin *vh = v + (size_t)bh * T * D;
     const float *rh = rec + (size_t)bh * NC * RS;
     float *oh = o + (size_t)bh * T * D;
 
@@ -500,8 +508,8 @@ vla_mem(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     for (int t = 0; t < NT; ++t)
         st[t] = S0 ? ld4(&S0[bh * DD + (size_t)(16 * b + n) * D + 16 * (rho0 + t) + 4 * g]) : zero;
 
-    // lane offsets within a chunk (elements); per chunk, buffer views of the
-    // head's inputs from the chunk's first token to T (rows past T read as 0)
+    // lane offsets within a chunk (elements); per chunk, a buffer view of v from
+    // the chunk's first token to T (rows past T read as 0)
     unsigned offk[NT], offa[NT], offv[4];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -514,19 +522,15 @@ vla_mem(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     auto load = [&](int c, MemOps<Tin, NT> &m) {
         const unsigned rs = (unsigned)c * RS * 4;   // record of chunk c (bytes)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) m.aw[t] = rbuf.ld128(4u * offa[t], rs);
+        for (int t = 0; t < NT; ++t) {
+            m.ak[t] = rbuf.ld128(4u * (Rec<D>::KH + offk[t]), rs);
+            m.ap[t] = rbuf.ld128(4u * (Rec<D>::PH + offk[t]), rs);
+            m.aw[t] = rbuf.ld128(4u * offa[t], rs);
+        }
         m.ta = rbuf.ld128(4u * (Rec<D>::TT + 16 * n + 4 * g), rs);
         m.pa = rbuf.ld128(4u * (Rec<D>::PT + 16 * n + 4 * g), rs);
         m.rd = rbuf.ld128(4u * (Rec<D>::RD + 4 * g), rs);
-        m.ik = rbuf.ld128(4u * (Rec<D>::IK + 4 * g), rs);
-        const size_t tb = (size_t)c * CH * D;
-        const unsigned left = (unsigned)(T - c * CH) * D * (unsigned)sizeof(Tin);
-        const Buf kb(kh + tb, left), qb(qh + tb, left), vb(vh + tb, left);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            m.k[t].load_buf(kb, offk[t]);
-            m.q[t].load_buf(qb, offk[t]);
-        }
+        const Buf vb(vh + (size_t)c * CH * D, (unsigned)(T - c * CH) * D * (unsigned)sizeof(Tin));
 #pragma unroll
         for (int r = 0; r < 4; ++r) m.v[r].load_buf(vb, offv[r]);
     };
@@ -541,8 +545,8 @@ vla_mem(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                sk = mma(m.k[t].get(r), st[t][r], sk);
-                sq = mma(phi_fast(m.q[t].get(r)), st[t][r], sq);
+                sk = mma(m.ak[t][r], st[t][r], sk);
+                sq = mma(m.ap[t][r], st[t][r], sq);
             }
         }
         if constexpr (KS > 1) {
@@ -558,9 +562,9 @@ vla_mem(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
                 for (int s2 = 1; s2 < KS; ++s2) sq += ld4(&red[sl][vbl * KS + s2][1][lane * 4]);
             }
         }
-        f4 vm;   // v past T reads as 0 (and 1/|k| is 0 there)
+        f4 vm;   // v past T reads as 0 (and k^ is 0 there)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vm[r] = m.v[r].get() - sk[r] * m.ik[r];
+        for (int r = 0; r < 4; ++r) vm[r] = m.v[r].get() - sk[r];
         const f4 e = mma4(m.ta, vm, zero);   // E' = T'(V - S K^)'
         f4 ob = sq;
         if (ks == 0) ob = mma4(m.pa, e, sq);  // (S_t phi(q_t))'
@@ -619,7 +623,7 @@ Plan make_plan(int BH, int T, int D)
         const int most = p.SC / 4 > 1 ? p.SC / 4 : 1;
         p.P = want < most ? want : most;
     }
-    const int rs = 16 * D + 2 * CH * CH + 2 * CH;   // Rec<D>::SIZE
+    const int rs = 16 * D + 2 * CH * CH + 2 * CH + 2 * CH * D;   // Rec<D>::SIZE
     size_t off = 0;
     p.rec = off;
     off = up256(off + (size_t)BH * p.NC * rs * sizeof(float));
@@ -663,8 +667,8 @@ hipError_t launch(const FwdArgs &a, int phases)
     }
     if (phases & 2) {
         constexpr int NG = (D / 16) / MemCfg<D>::VBW;
-        hipLaunchKernelGGL((vla_mem<D, Tin>), dim3(BH * NG), dim3(256), 0, a.stream, q, k, v, a.T,
-                           BH, rec, a.S0, a.o, a.S_out);
+        hipLaunchKernelGGL((vla_mem<D, Tin>), dim3(BH * NG), dim3(256), 0, a.stream, v, a.T, BH, rec,
+                           a.S0, a.o, a.S_out);
     }
     return hipGetLastError();
 }
