@@ -124,8 +124,9 @@ vla_status vla_forward_memory(const void *q, const void *k, const void *v, int i
 /*
  * vla_forward_workspace_size -- bytes of device workspace vla_forward needs for
  * these sizes (0 when it needs none: d_h in {16, 32}, or T == 0), in *bytes.
- * At d_h = 64 it is about 6.2 KB per 16 tokens of each head (the per-chunk
- * factors) plus a few d_h x d_h matrices per head.  Host-only; launches
+ * At d_h = 64 it is about 14.5 KB per 16 tokens of each head (the per-chunk
+ * factors and the chunk's k^ and phi(q)) plus a few d_h x d_h matrices per
+ * head.  Host-only; launches
  * nothing.  Errors: VLA_ERR_INVALID_ARG (NULL bytes, bad sizes),
  * VLA_ERR_UNSUPPORTED (d_h).
  */
