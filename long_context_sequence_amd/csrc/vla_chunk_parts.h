@@ -59,6 +59,7 @@ namespace vla {
 namespace chunk {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 template <typename F, int... Is>
 __device__ __forceinline__ void sfor_impl(F &&f, std::integer_sequence<int, Is...>)
@@ -140,6 +141,17 @@ struct Buf {
     {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, soff, 0);
     }
+    __device__ __forceinline__ void st128(f4 x, unsigned off, unsigned soff = 0) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), r, off, soff, 0);
+    }
+    // 16 bytes per lane from device memory straight into LDS: lane l's bytes
+    // land at lds + 16 l (lds uniform over the wave); bytes past the view read
+    // as 0.  Counted by vmcnt like any load.
+    __device__ __forceinline__ void lds16(float *lds, unsigned off, unsigned soff = 0) const
+    {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, soff, 0, 0);
+    }
 };
 
 // Load of a T at a uniform base plus a 32-bit unsigned byte offset (the form the
@@ -182,6 +194,18 @@ __device__ __forceinline__ void wave_lds_order() { asm volatile("" ::: "memory")
 // look pending inside the loop, where every use would otherwise wait for all
 // operations issued in the previous iteration.
 __device__ __forceinline__ void vmem_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until at most N of this wave's device-memory operations are outstanding
+// (they complete in issue order); expcnt and lgkmcnt untouched.
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | 0x0F70 | ((N >> 4) << 14));
+}
+
+// Compiler-only ordering point for memory operations.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // Workgroup barrier for LDS traffic only.  Unlike __syncthreads() it does not
 // wait for outstanding global loads and stores, so prefetches into registers
@@ -278,6 +302,14 @@ struct Cfg {
     static constexpr int CPT = D / 16;             // staged columns per thread (16 per token)
     static constexpr int WSLOT = 16 * D + 16 * NA; // floats of one chunk's W' and |w|^2 partials
 };
+
+// Layouts of the per-chunk matrices the memory pass reads through LDS: the
+// float offset of granule (16 bytes) c4 of row i of a 16-column matrix, and of
+// row t of a D-column matrix.  The granule index is XOR-swizzled with the row,
+// so that 16-byte reads of 8 consecutive rows at one column hit distinct banks.
+__device__ __forceinline__ constexpr int swz16(int i, int c4) { return 16 * i + 4 * (c4 ^ ((i >> 1) & 3)); }
+template <int D>
+__device__ __forceinline__ constexpr int swzd(int t, int c4) { return D * t + 4 * (c4 ^ (t & 7)); }
 
 // Everything a head keeps in LDS (every member a multiple of 16 bytes).
 template <int D>
@@ -764,8 +796,9 @@ struct Head {
     }
     // The two C x C factors of the memory chain from the waves' partials in
     // L.nq: (I + N)^-1 and (Alpha^'Phi) o Up, each stored transposed
-    // (tt[m][t] = X[t][m]), so that lane 16 g + n reads X[4 g + r][n] as four
-    // consecutive floats at tt + 16 n + 4 g.  One wave computes them.
+    // (X'[m][t] = X[t][m], rows as swz16 places them), so that lane 16 g + n
+    // reads X[4 g + r][n] as four consecutive floats at swz16(n, g).  One wave
+    // computes them.
     __device__ __forceinline__ void prep_tp(float *tt, float *pt)
     {
         float NNr[16];
@@ -785,7 +818,7 @@ struct Head {
             sfor<NA - 1>([&](auto w2) { a += L.nq[w2 + 1][1][(4 * g + r) * LT + n]; });
             qa[int(r)] = 4 * g + r <= n ? a : 0.f;
         });
-        st4(&pt[16 * n + 4 * g], qa);
+        st4(&pt[swz16(n, g)], qa);
         float X[4];
         sfor<4>([&](auto c) { X[c] = n == 4 * c + g ? 1.f : 0.f; });
         asm volatile(VLA_TINV_BLOCK
@@ -793,7 +826,7 @@ struct Head {
                      : "v"(NNr[1]), "v"(NNr[2]), "v"(NNr[3]), "v"(NNr[4]), "v"(NNr[5]),
                        "v"(NNr[6]), "v"(NNr[7]), "v"(NNr[8]), "v"(NNr[9]), "v"(NNr[10]),
                        "v"(NNr[11]), "v"(NNr[12]), "v"(NNr[13]), "v"(NNr[14]), "v"(NNr[15]));
-        sfor<4>([&](auto c) { tt[16 * (4 * c + g) + n] = X[c]; });   // column 4c+g of (I+N)^-1
+        sfor<4>([&](auto c) { tt[swz16(4 * c + g, n >> 2) + (n & 3)] = X[c]; });   // column 4c+g of (I+N)^-1
     }
 
     // (I + N)^-1, the errors E, the readout o of chunk cq and the write of S

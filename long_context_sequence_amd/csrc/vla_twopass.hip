@@ -24,9 +24,11 @@
 //            and k^ and phi(q) (C x d, token-major).  The key sum and den follow
 //            Eq. (11).
 //   memory   per (head, group of 16-row value blocks): the memory chain from the
-//            records and v:
+//            records and v, two chunks per step (the second one's products
+//            with S corrected by cross factors the penalty pass also records):
 //                R = V - S K^,  E = R (I + N)^-1,
 //                o = (S Phi + E P) / den,  S <- S + E Alpha^'.
+//            Records and v reach LDS through direct copies, three steps ahead.
 //            Rows of S do not interact, so the value rows of a head are split
 //            over workgroups, and the key columns of a block over the waves of a
 //            workgroup (partial products summed through LDS in a fixed order).
@@ -41,27 +43,31 @@ namespace {
 using namespace chunk;
 
 constexpr int CH = 16;   // tokens per chunk (Cfg<D>::C)
-constexpr int MPD = 2;   // memory pass: chunks its operand loads run ahead
 
-// One chunk's record (floats).
+// One chunk's record (floats).  The memory pass copies records into LDS as
+// they are, so the matrices it reads are laid out for that: 16-column ones by
+// swz16, d-column ones by swzd.
 template <int D>
 struct Rec {
     static constexpr int AH = 0;              // alpha^ [key][token]
     static constexpr int TT = D * CH;         // (I + N)^-1, transposed
     static constexpr int PT = TT + CH * CH;   // (Alpha^'Phi) o Up, transposed
-    static constexpr int RD = PT + CH * CH;   // 1 / den per token
-    static constexpr int IK = RD + CH;        // 1 / |k| per token (0 past T)
-    static constexpr int KH = IK + CH;        // k^ [token][key] (0 past T)
+    // even chunks c with a chunk c + 1: the cross factors Alpha^_c' K^_{c+1} and
+    // Alpha^_c' Phi_{c+1}, transposed (unset otherwise)
+    static constexpr int QK = PT + CH * CH;
+    static constexpr int QP = QK + CH * CH;
+    static constexpr int RD = QP + CH * CH;   // 1 / den per token
+    static constexpr int KH = RD + CH;        // k^ [token][key] (0 past T)
     static constexpr int PH = KH + CH * D;    // phi(q) [token][key]
-    static constexpr int SIZE = PH + CH * D;  // a multiple of 16
+    static constexpr int SIZE = PH + CH * D;  // a multiple of 4
 };
 
-// Value blocks per memory workgroup (its 4 waves split each block's key tiles
-// KS = 4 / VBW ways).
+// Value blocks per memory workgroup and the ways each block's key tiles are
+// split over its waves (VBW x KS waves per workgroup).
 template <int D> struct MemCfg;
-template <> struct MemCfg<64> { static constexpr int VBW = 2; };
-template <> struct MemCfg<96> { static constexpr int VBW = 2; };
-template <> struct MemCfg<128> { static constexpr int VBW = 1; };
+template <> struct MemCfg<64> { static constexpr int VBW = 2, KS = 2; };
+template <> struct MemCfg<96> { static constexpr int VBW = 2, KS = 2; };
+template <> struct MemCfg<128> { static constexpr int VBW = 1, KS = 4; };
 
 // ------------------------------------------------------------------- gram
 // Workgroup (head, segment j < S - 1, part pp < P): the part's share of
@@ -341,13 +347,12 @@ template <int D>
 struct PLds {
     static constexpr int C = Cfg<D>::C, NA = Cfg<D>::NA, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
     static constexpr int UB = 1;
-    static constexpr bool KEEP_IK = true;
+    static constexpr bool KEEP_IK = false;
     float uh[1][C * LD];     // u^ [token][i] (read before the next chunk is staged)
     float kh[2][C * LD];     // k^, by chunk parity
     float ph[2][C * LD];     // phi(q), by chunk parity
     float zk[C * LD];        // phi(k), then the inclusive key sum
     float rden[2][C];
-    float ikn[2][C];         // 1 / |k| per token
     float z0[C * LD];
     float z0t[D * LT];
     float w[C * LD];         // W [token][i]
@@ -362,6 +367,24 @@ struct PLds {
     float inv[NA][C];
     float hms[256];          // A operand of W' (per lane), from wave 0
 };
+
+// X' for X = Alpha^'Y (C x C) with Alpha^ = W diag(1/|w|) of the current chunk
+// (W and the |w|^2 partials in LDS) and Y (C x d, token-major in LDS, row
+// stride LD) of the next one: dst[swz16(n, g) + r] = X[4 g + r][n].  One wave.
+template <int D>
+__device__ __forceinline__ void cross_factor(const PLds<D> &L, const float *y, int g, int n, float *dst)
+{
+    constexpr int NB = D / 16, LD = Cfg<D>::LD, NA = Cfg<D>::NA;
+    float ns = L.nrm[0][n];
+    sfor<NA - 1>([&](auto w2) { ns += L.nrm[w2 + 1][n]; });
+    const float invm = ns > 0.f ? rsqrtf(ns) : 0.f;   // 1 / |w_n|
+    f4 x = {0.f, 0.f, 0.f, 0.f};
+    sfor<NB>([&](auto b) {
+        const f4 aw = ld4(&L.w[n * LD + 16 * b + 4 * g]) * invm;
+        x = mma4(aw, ld4(&y[n * LD + 16 * b + 4 * g]), x);
+    });
+    st4(&dst[swz16(n, g)], x);
+}
 
 // Workgroup (head, segment j): the penalty chain over chunks [j SC, (j+1) SC)
 // from A at the segment start, writing each chunk's record.  Per chunk p:
@@ -380,7 +403,7 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         float *__restrict__ rec, float *A_out, float *zk_out)
 {
     using Hd = Head<D, Tin, PLds<D>>;
-    constexpr int BPW = Cfg<D>::BPW, LT = Cfg<D>::LT, RS = Rec<D>::SIZE;
+    constexpr int BPW = Cfg<D>::BPW, LT = Cfg<D>::LT, RS = Rec<D>::SIZE, NA = Cfg<D>::NA;
     __shared__ __align__(16) PLds<D> L;
 
     const int tid = threadIdx.x;
@@ -430,14 +453,18 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         sfor<BPW>([&](auto bb) {
             const int b = w * BPW + bb;
             const f4 a = ld4(&L.wt[0][(16 * b + hd.n) * LT + 4 * hd.g]) * invn4;
-            st4(&rb[Rec<D>::AH + (16 * b + hd.n) * CH + 4 * hd.g], a);
+            st4(&rb[Rec<D>::AH + swz16(16 * b + hd.n, hd.g)], a);
         });
         if (tid < CH) rb[Rec<D>::RD + tid] = L.rden[p & 1][tid];
-        else if (tid < 2 * CH) rb[Rec<D>::IK + tid - CH] = L.ikn[p & 1][tid - CH];
         for (int f = tid; f < CH * D / 4; f += 64 * Cfg<D>::NA) {   // k^ and phi(q), unpadded
             const int tk = f / (D / 4), c4 = 4 * (f % (D / 4));
-            st4(&rb[Rec<D>::KH + tk * D + c4], ld4(&L.kh[p & 1][tk * Cfg<D>::LD + c4]));
-            st4(&rb[Rec<D>::PH + tk * D + c4], ld4(&L.ph[p & 1][tk * Cfg<D>::LD + c4]));
+            st4(&rb[Rec<D>::KH + swzd<D>(tk, c4 / 4)], ld4(&L.kh[p & 1][tk * Cfg<D>::LD + c4]));
+            st4(&rb[Rec<D>::PH + swzd<D>(tk, c4 / 4)], ld4(&L.ph[p & 1][tk * Cfg<D>::LD + c4]));
+        }
+        // the cross factors of an even chunk with the next one (staged above)
+        if ((p & 1) == 0 && p + 1 < c1 && w >= NA - 2) {
+            const float *nb = w == NA - 2 ? L.kh[(p + 1) & 1] : L.ph[(p + 1) & 1];
+            cross_factor<D>(L, nb, hd.g, hd.n, rb + (w == NA - 2 ? Rec<D>::QK : Rec<D>::QP));
         }
         lds_barrier();
         if (w == 1) hd.prep_tp(rb + Rec<D>::TT, rb + Rec<D>::PT);
@@ -449,35 +476,71 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
 }
 
 // ------------------------------------------------------------------- memory
-// Operands of one chunk for one memory wave, as loaded: k^ and phi(q) of token
-// n, keys 16 rho + 4 g + [0, 4) (rho = the wave's key tiles), and
-// alpha^[16 rho + n][4 g + r], all from the record; the transposed C x C
-// factors and 1/den of tokens 4 g + r; v (raw) of token 4 g + r, value 16 b + n.
-template <typename Tin, int NT>
+// Staging of the memory pass: per pair of chunks, the two records (as stored)
+// and the workgroup's columns of v for the 32 tokens (token-major), copied
+// from device memory straight into LDS in 1 KB pieces (16 bytes per lane),
+// the same number of pieces per wave.
+template <int D, typename Tin>
+struct MemStage {
+    static constexpr int VBW = MemCfg<D>::VBW, KS = MemCfg<D>::KS, NW = VBW * KS;
+    static constexpr int RS = Rec<D>::SIZE;
+    static constexpr int NR = (2 * RS * 4 + 1023) / 1024;      // pieces of the records
+    static constexpr int ROWB = 16 * VBW * (int)sizeof(Tin);   // bytes of v per token
+    static constexpr int NV = 32 * ROWB / 1024;                // pieces of v
+    static constexpr int NI = (NR + NV + NW - 1) / NW * NW;    // pieces per pair
+    static constexpr int NIW = NI / NW;                        // per wave
+    static constexpr int VOFF = 256 * (NI - NV);               // v, in floats from the stage start
+    static constexpr int SIZE = 256 * NI;                      // floats per stage
+    static constexpr int LPT = ROWB / 16, TPI = 64 / LPT;      // lanes per token, tokens per piece
+    static constexpr int NS = 3 * SIZE * 4 + 2 * NW * 4096 <= 160 * 1024 ? 3 : 2;   // stages
+    static_assert(NV * 1024 == 32 * ROWB && 2 * SIZE * 4 + 2 * NW * 4096 <= 160 * 1024, "LDS");
+};
+
+// Operands of one chunk for one memory wave, read from its stage: k^ and phi(q)
+// of token n, keys 16 rho + 4 g + [0, 4) (rho = the wave's key tiles);
+// alpha^[16 rho + n][4 g + r]; the transposed C x C factors at row n; 1/den of
+// token n; v of token 4 g + r, value 16 b + n.
+template <int NT>
 struct MemOps {
-    f4 ak[NT], ap[NT], aw[NT], ta, pa, rd;
-    Raw1<Tin> v[4];
+    f4 ak[NT], ap[NT], aw[NT], ta, pa;
+    float rd, v[4];
 };
 
 // Workgroup (head, value group): VBW value blocks of 16 rows; wave w takes block
 // w / KS and key tiles [NT (w % KS), +NT).  The state tiles are S' in MFMA
 // accumulator layout (register r of lane 16 g + n of tile rho holds
-// S[16 b + n][16 rho + 4 g + r]).  Every operand comes straight from device
-// memory into registers, MPD = 2 chunks ahead (three operand sets in rotation).
-// Per chunk c:
-//   (S K)' and (S Phi)' partials of the own key tiles (K raw; the rows are
-//   scaled by 1/|k| after the sum) -> LDS                          | barrier
-//   sum the KS partials (same order in every wave); E' = T'(V - S K^)';
-//   wave 0 of the block: o' = (P'E' + (S Phi)') / den;  S' += Alpha^ E'.
+// S[16 b + n][16 rho + 4 g + r]).
+//
+// The chain runs over pairs of chunks (a, b) from S at the start of a:
+//   (S K_a)', (S K_b)' (token x value) and S Phi_a, S Phi_b (value x token)
+//   partials of the own key tiles -> LDS                           | barrier
+//   sum the KS partials (same order in every wave);
+//   E_a' = T_a'(V_a - S K^_a)';
+//   E_b' = T_b'(V_b - S K^_b - E_a Alpha^_a'K^_b)'   (S after a, applied to K^_b);
+//   key split 0: o_a = (S Phi_a + E_a P_a) / den, key split 1:
+//   o_b = (S Phi_b + E_a Alpha^_a'Phi_b + E_b P_b) / den  (value x token, so
+//   that a lane stores four consecutive values of one token);
+//   S' += Alpha^_a E_a' + Alpha^_b E_b'.
+// An odd last chunk takes the single-chunk form of the same step.
+//
+// Pair p is staged in LDS stage p mod NS.  Every wave copies its pieces of pair
+// p + NS right after the barrier of step p (all reads of stage p mod NS are
+// done by then) and waits for its pieces of pair p + 1 before the barrier of
+// step p, so that the barrier publishes them.
 template <int D, typename Tin>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * MemCfg<D>::VBW * MemCfg<D>::KS)
 vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec, const float *S0,
         float *__restrict__ o, float *S_out)
 {
-    constexpr int NB = D / 16, VBW = MemCfg<D>::VBW, KS = 4 / VBW, NT = NB / KS;
-    constexpr int NG = NB / VBW, RS = Rec<D>::SIZE;
-    static_assert(NT * KS == NB && NG * VBW == NB, "block split");
-    __shared__ __align__(16) float red[2][4][2][256];   // per parity and wave: partials
+    using MS = MemStage<D, Tin>;
+    using R = Rec<D>;
+    constexpr int NB = D / 16, VBW = MS::VBW, KS = MS::KS, NW = MS::NW, NT = NB / KS;
+    constexpr int NG = NB / VBW, RS = R::SIZE, NS = MS::NS, NIW = MS::NIW;
+    static_assert(NT * KS == NB && NG * VBW == NB && KS >= 2, "block split");
+    __shared__ __align__(16) float stg0[MS::SIZE];
+    __shared__ __align__(16) float stg1[MS::SIZE];
+    __shared__ __align__(16) float stg2[NS == 3 ? MS::SIZE : 4];
+    __shared__ __align__(16) float red[2][NW][4][256];   // per step parity and wave: partials
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -495,12 +558,11 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
     }
     const int b = vg * VBW + vbl;
     const int rho0 = ks * NT;
-    const int NC = (T + CH - 1) / CH;
+    const int NC = (T + CH - 1) / CH, NP = NC / 2, NPT = (NC + 1) / 2;
     const size_t DD = (size_t)D * D;
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
-    // per-head bases; 32-bit offsets below
-    const Tin *vh = v + (size_t)bh * T * D;
-    const float *rh = rec + (size_t)bh * NC * RS;
+    const Buf rbuf(rec + (size_t)bh * NC * RS, (unsigned)(NC * RS * 4));
+    const Buf vbuf(v + (size_t)bh * T * D, (unsigned)T * D * (unsigned)sizeof(Tin));
     float *oh = o + (size_t)bh * T * D;
 
     f4 st[NT];
@@ -508,88 +570,159 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
     for (int t = 0; t < NT; ++t)
         st[t] = S0 ? ld4(&S0[bh * DD + (size_t)(16 * b + n) * D + 16 * (rho0 + t) + 4 * g]) : zero;
 
-    // lane offsets within a chunk (elements); per chunk, a buffer view of v from
-    // the chunk's first token to T (rows past T read as 0)
-    unsigned offk[NT], offa[NT], offv[4];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        offk[t] = n * D + 16 * (rho0 + t) + 4 * g;
-        offa[t] = Rec<D>::AH + (16 * (rho0 + t) + n) * CH + 4 * g;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) offv[r] = (4 * g + r) * D + 16 * b + n;
-    const Buf rbuf(rh, (unsigned)(NC * RS * 4));
-    auto load = [&](int c, MemOps<Tin, NT> &m) {
-        const unsigned rs = (unsigned)c * RS * 4;   // record of chunk c (bytes)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            m.ak[t] = rbuf.ld128(4u * (Rec<D>::KH + offk[t]), rs);
-            m.ap[t] = rbuf.ld128(4u * (Rec<D>::PH + offk[t]), rs);
-            m.aw[t] = rbuf.ld128(4u * offa[t], rs);
-        }
-        m.ta = rbuf.ld128(4u * (Rec<D>::TT + 16 * n + 4 * g), rs);
-        m.pa = rbuf.ld128(4u * (Rec<D>::PT + 16 * n + 4 * g), rs);
-        m.rd = rbuf.ld128(4u * (Rec<D>::RD + 4 * g), rs);
-        const Buf vb(vh + (size_t)c * CH * D, (unsigned)(T - c * CH) * D * (unsigned)sizeof(Tin));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) m.v[r].load_buf(vb, offv[r]);
+    // this wave's pieces of pair pm into stage s (pieces w, w + NW, ...)
+    auto stage_pair = [&](int pm, float *s) {
+        pm = min(pm, NPT - 1);
+        constexpr int NRP = MS::NI - MS::NV;   // pieces of records
+        auto rpiece = [&](int j) {
+            rbuf.lds16(s + 256 * j, (unsigned)(1024 * j + 16 * lane), (unsigned)pm * 2 * RS * 4);
+        };
+        auto vpiece = [&](int j) {
+            const int tp = (j - NRP) * MS::TPI + lane / MS::LPT;   // token in the pair
+            const unsigned off = ((unsigned)(32 * pm + tp) * D + 16 * VBW * vg) * sizeof(Tin) +
+                                 16 * (lane % MS::LPT);
+            vbuf.lds16(s + 256 * j, off);
+        };
+        sfor<NIW>([&](auto i) {
+            const int j = w + NW * i;
+            if constexpr (NW * (i + 1) <= NRP) rpiece(j);
+            else if constexpr (NW * i >= NRP) vpiece(j);
+            else if (j < NRP) rpiece(j);
+            else vpiece(j);
+        });
     };
-    // Every load and store of a step is unconditional (chunk indices past the end
-    // clamp, and the waves that do not write o store through an empty view), so
-    // that the compiler's wait counts can leave the next chunks' loads in flight.
-    auto step = [&](int c, const MemOps<Tin, NT> &m, MemOps<Tin, NT> &pre) {
-        load(min(c + MPD, NC - 1), pre);
-        const int sl = c & 1;
-        f4 sk = zero, sq = zero;
+    auto ops = [&](const float *s, int xc, MemOps<NT> &m) {   // chunk xc (0 or 1) of a stage
+        const float *c = s + xc * RS;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            m.ak[t] = ld4(c + R::KH + swzd<D>(n, 4 * (rho0 + t) + g));
+            m.ap[t] = ld4(c + R::PH + swzd<D>(n, 4 * (rho0 + t) + g));
+            m.aw[t] = ld4(c + R::AH + swz16(16 * (rho0 + t) + n, g));
+        }
+        m.ta = ld4(c + R::TT + swz16(n, g));
+        m.pa = ld4(c + R::PT + swz16(n, g));
+        m.rd = c[R::RD + n];
+        const Tin *vs = reinterpret_cast<const Tin *>(s + MS::VOFF);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            m.v[r] = load_in(vs, (16 * xc + 4 * g + r) * (16 * VBW) + 16 * vbl + n);
+    };
+    auto sk_part = [&](const f4 (&a)[NT]) {   // (S K)' partial: token x value
+        f4 acc = zero;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sk = mma(m.ak[t][r], st[t][r], sk);
-                sq = mma(m.ap[t][r], st[t][r], sq);
-            }
+            for (int r = 0; r < 4; ++r) acc = mma(a[t][r], st[t][r], acc);
         }
-        if constexpr (KS > 1) {
-            st4(&red[sl][w][0][lane * 4], sk);
-            st4(&red[sl][w][1][lane * 4], sq);
-            lds_barrier();
-            sk = ld4(&red[sl][vbl * KS][0][lane * 4]);
+        return acc;
+    };
+    auto sq_part = [&](const f4 (&a)[NT]) {   // S Phi partial: value x token
+        f4 acc = zero;
 #pragma unroll
-            for (int s2 = 1; s2 < KS; ++s2) sk += ld4(&red[sl][vbl * KS + s2][0][lane * 4]);
-            if (ks == 0) {
-                sq = ld4(&red[sl][vbl * KS][1][lane * 4]);
+        for (int t = 0; t < NT; ++t) {
 #pragma unroll
-                for (int s2 = 1; s2 < KS; ++s2) sq += ld4(&red[sl][vbl * KS + s2][1][lane * 4]);
-            }
+            for (int r = 0; r < 4; ++r) acc = mma(st[t][r], a[t][r], acc);
         }
+        return acc;
+    };
+    auto reduce = [&](int sl, int slot) {
+        f4 s = ld4(&red[sl][vbl * KS][slot][lane * 4]);
+#pragma unroll
+        for (int s2 = 1; s2 < KS; ++s2) s += ld4(&red[sl][vbl * KS + s2][slot][lane * 4]);
+        return s;
+    };
+    auto errors = [&](const MemOps<NT> &m, f4 sk) {   // E' = T'(V - S K^)'
         f4 vm;   // v past T reads as 0 (and k^ is 0 there)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vm[r] = m.v[r].get() - sk[r];
-        const f4 e = mma4(m.ta, vm, zero);   // E' = T'(V - S K^)'
-        f4 ob = sq;
-        if (ks == 0) ob = mma4(m.pa, e, sq);  // (S_t phi(q_t))'
-        const Buf ob_(oh + (size_t)c * CH * D, ks == 0 ? (unsigned)(T - c * CH) * D * 4u : 0u);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ob_.st32(ob[r] * m.rd[r], 4u * offv[r]);   // rows past T dropped
+        for (int r = 0; r < 4; ++r) vm[r] = m.v[r] - sk[r];
+        return mma4(m.ta, vm, zero);
+    };
+    // o of chunk c (value x token) from this wave when it writes it (others
+    // store through an empty view, so that every store is unconditional)
+    auto store_o = [&](int c, bool mine, f4 ob, float rd) {
+        const Buf ob_(oh + (size_t)c * CH * D, mine ? (unsigned)(T - c * CH) * D * 4u : 0u);
+        ob_.st128(ob * rd, 4u * (n * D + 16 * b + 4 * g));   // rows past T dropped
+    };
+    auto update = [&](const MemOps<NT> &m, f4 e) {   // S' += Alpha^ E'
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) st[t] = mma(m.aw[t][r], e[r], st[t]);
         }
     };
+    // the wait before the barrier of a step: this wave's pieces of the next
+    // pair (behind them: a store, and for three stages a store and NIW pieces)
+    auto wait_next = [&]() {
+        if constexpr (NS == 3) vm_wait<NIW + 2>();
+        else vm_wait<1>();
+    };
+    auto step2 = [&](int pm, float *s) {
+        const int sl = pm & 1, ca = 2 * pm;
+        MemOps<NT> ma, mb;
+        ops(s, 0, ma);
+        ops(s, 1, mb);
+        const f4 qk = ld4(s + R::QK + swz16(n, g)), qp = ld4(s + R::QP + swz16(n, g));
+        const f4 ska = sk_part(ma.ak), skb = sk_part(mb.ak);
+        const f4 sqa = sq_part(ma.ap), sqb = sq_part(mb.ap);
+        st4(&red[sl][w][0][lane * 4], ska);
+        st4(&red[sl][w][1][lane * 4], skb);
+        st4(&red[sl][w][2][lane * 4], sqa);
+        st4(&red[sl][w][3][lane * 4], sqb);
+        wait_next();
+        lds_barrier();
+        stage_pair(pm + NS, s);
+        compiler_fence();
+        const f4 ea = errors(ma, reduce(sl, 0));
+        const f4 eb = errors(mb, mma4(qk, ea, reduce(sl, 1)));
+        f4 ob;
+        float rd;
+        if (ks == 0) {
+            ob = mma4(ea, ma.pa, reduce(sl, 2));
+            rd = ma.rd;
+        } else {
+            ob = mma4(eb, mb.pa, mma4(ea, qp, reduce(sl, 3)));
+            rd = mb.rd;
+        }
+        store_o(ks == 0 ? ca : ca + 1, ks < 2, ob, rd);
+        update(ma, ea);
+        update(mb, eb);
+    };
 
-    MemOps<Tin, NT> m0, m1, m2;
-    load(0, m0);
-    load(min(1, NC - 1), m1);
-    vmem_drain();   // nothing pending at the loop entry: the wait counts inside stay exact
-    int c = 0;
-    for (; c + 3 <= NC; c += 3) {
-        step(c, m0, m2);
-        step(c + 1, m1, m0);
-        step(c + 2, m2, m1);
+    stage_pair(0, stg0);
+    stage_pair(1, stg1);
+    if constexpr (NS == 3) stage_pair(2, stg2);
+    vm_wait<0>();
+    lds_barrier();
+    int pm = 0;
+    if constexpr (NS == 3) {
+        for (; pm + 3 <= NP; pm += 3) {
+            step2(pm, stg0);
+            step2(pm + 1, stg1);
+            step2(pm + 2, stg2);
+        }
+        if (pm < NP) step2(pm, stg0);
+        if (pm + 1 < NP) step2(pm + 1, stg1);
+    } else {
+        for (; pm + 2 <= NP; pm += 2) {
+            step2(pm, stg0);
+            step2(pm + 1, stg1);
+        }
+        if (pm < NP) step2(pm, stg0);
     }
-    if (c < NC) step(c, m0, m2);
-    if (c + 1 < NC) step(c + 1, m1, m0);
+    if (NC & 1) {   // the last chunk alone (staged as pair NP)
+        const int c = NC - 1, sl = NP & 1, k = NP % NS;
+        const float *s = k == 0 ? stg0 : (k == 1 ? stg1 : stg2);
+        MemOps<NT> m;
+        ops(s, 0, m);
+        const f4 sk = sk_part(m.ak), sq = sq_part(m.ap);
+        st4(&red[sl][w][0][lane * 4], sk);
+        st4(&red[sl][w][2][lane * 4], sq);
+        lds_barrier();
+        const f4 e = errors(m, reduce(sl, 0));
+        store_o(c, ks == 0, mma4(e, m.pa, reduce(sl, 2)), m.rd);
+        update(m, e);
+    }
+    vm_wait<0>();   // no copy into LDS outlives the workgroup
     if (S_out) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -617,13 +750,14 @@ Plan make_plan(int BH, int T, int D)
     const int smax = p.NC / 2 > 1 ? p.NC / 2 : 1;
     S = S < smax ? S : smax;
     p.SC = (p.NC + S - 1) / S;
+    p.SC += p.SC & 1;   // segments start at even chunks (pairs of the memory pass)
     p.S = (p.NC + p.SC - 1) / p.SC;
     if (p.S > 1) {   // gram parts: about 1024 workgroups, each at least 4 chunks
         const int want = (1024 + BH * (p.S - 1) - 1) / (BH * (p.S - 1));
         const int most = p.SC / 4 > 1 ? p.SC / 4 : 1;
         p.P = want < most ? want : most;
     }
-    const int rs = 16 * D + 2 * CH * CH + 2 * CH + 2 * CH * D;   // Rec<D>::SIZE
+    const int rs = 48 * D + 4 * CH * CH + CH;   // Rec<D>::SIZE
     size_t off = 0;
     p.rec = off;
     off = up256(off + (size_t)BH * p.NC * rs * sizeof(float));
@@ -667,7 +801,8 @@ hipError_t launch(const FwdArgs &a, int phases)
     }
     if (phases & 2) {
         constexpr int NG = (D / 16) / MemCfg<D>::VBW;
-        hipLaunchKernelGGL((vla_mem<D, Tin>), dim3(BH * NG), dim3(256), 0, a.stream, v, a.T, BH, rec,
+        hipLaunchKernelGGL((vla_mem<D, Tin>), dim3(BH * NG), dim3(64 * MemCfg<D>::VBW * MemCfg<D>::KS),
+                           0, a.stream, v, a.T, BH, rec,
                            a.S0, a.o, a.S_out);
     }
     return hipGetLastError();

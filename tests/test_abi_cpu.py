@@ -75,12 +75,12 @@ def test_forward_argument_errors(kw, code):
 
 
 def test_workspace_size():
-    # the per-chunk factors dominate: (16 d + 528) floats per 16 tokens of a head
+    # the per-chunk records dominate: (48 d + 1040) floats per 16 tokens of a head
     for d in (64, 96, 128):
         n1 = vla.workspace_size(1, 1, 4096, d)
-        assert n1 >= 256 * (16 * d + 528) * 4
+        assert n1 >= 256 * (48 * d + 1040) * 4
         assert n1 % 256 == 0
-        assert vla.workspace_size(8, 16, 4096, d) >= 128 * 256 * (16 * d + 528) * 4
+        assert vla.workspace_size(8, 16, 4096, d) >= 128 * 256 * (48 * d + 1040) * 4
         assert vla.workspace_size(2, 3, 0, d) == 0
     assert vla.workspace_size(4, 4, 1000, 16) == 0
     assert vla.workspace_size(4, 4, 1000, 32) == 0
