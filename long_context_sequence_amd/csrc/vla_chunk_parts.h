@@ -71,6 +71,8 @@ __device__ __forceinline__ void sfor(F &&f)
 {
     sfor_impl(f, std::make_integer_sequence<int, N>{});
 }
+template <int N>
+using ic = std::integral_constant<int, N>;
 
 __device__ __forceinline__ f4 mma(float a, float b, f4 c)
 {

@@ -570,10 +570,10 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
     for (int t = 0; t < NT; ++t)
         st[t] = S0 ? ld4(&S0[bh * DD + (size_t)(16 * b + n) * D + 16 * (rho0 + t) + 4 * g]) : zero;
 
-    // this wave's pieces of pair pm into stage s (pieces w, w + NW, ...)
-    auto stage_pair = [&](int pm, float *s) {
+    // this wave's pieces [I0, I1) of pair pm into stage s (pieces w, w + NW, ...)
+    constexpr int NRP = MS::NI - MS::NV;   // pieces of records
+    auto stage_pieces = [&](auto I0, auto I1, int pm, float *s) {
         pm = min(pm, NPT - 1);
-        constexpr int NRP = MS::NI - MS::NV;   // pieces of records
         auto rpiece = [&](int j) {
             rbuf.lds16(s + 256 * j, (unsigned)(1024 * j + 16 * lane), (unsigned)pm * 2 * RS * 4);
         };
@@ -583,13 +583,23 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
                                  16 * (lane % MS::LPT);
             vbuf.lds16(s + 256 * j, off);
         };
-        sfor<NIW>([&](auto i) {
+        sfor<decltype(I1)::value - decltype(I0)::value>([&](auto i0) {
+            constexpr int i = decltype(I0)::value + decltype(i0)::value;
             const int j = w + NW * i;
             if constexpr (NW * (i + 1) <= NRP) rpiece(j);
             else if constexpr (NW * i >= NRP) vpiece(j);
             else if (j < NRP) rpiece(j);
             else vpiece(j);
         });
+    };
+    auto stage_pair = [&](int pm, float *s) { stage_pieces(ic<0>{}, ic<NIW>{}, pm, s); };
+    // the pieces of one step, spread over six points of its second half, so
+    // that the copies of the four waves do not queue up at once
+    auto stage_part = [&](auto K, int pm, float *s) {
+        constexpr int k = decltype(K)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        stage_pieces(ic<k * NIW / 6>{}, ic<(k + 1) * NIW / 6>{}, pm, s);
+        __builtin_amdgcn_sched_barrier(0);
     };
     auto ops = [&](const float *s, int xc, MemOps<NT> &m) {   // chunk xc (0 or 1) of a stage
         const float *c = s + xc * RS;
@@ -651,41 +661,55 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
         }
     };
     // the wait before the barrier of a step: this wave's pieces of the next
-    // pair (behind them: a store, and for three stages a store and NIW pieces)
+    // pair (behind them: the step's store, and for three stages the copies and
+    // the store of one more step)
     auto wait_next = [&]() {
         if constexpr (NS == 3) vm_wait<NIW + 2>();
         else vm_wait<1>();
     };
+    // The readout of a pair needs the S Phi partials of the other waves, which
+    // are formed after the barrier of the pair's step (off the chain from S to
+    // S) and published by the barrier of the next step: the readout of pair p
+    // happens in step p + 1.  What it needs of pair p is carried along.
+    struct Carry {
+        f4 ea, eb, pa, pb, qp;
+        float rd;
+    } cy = {zero, zero, zero, zero, zero, 0.f};
+    auto readout = [&](int sl) {   // the carried pair, partials in red[sl]
+        if (ks == 0) return mma4(cy.ea, cy.pa, reduce(sl, 2));
+        return mma4(cy.eb, cy.pb, mma4(cy.ea, cy.qp, reduce(sl, 3)));
+    };
     auto step2 = [&](int pm, float *s) {
-        const int sl = pm & 1, ca = 2 * pm;
+        const int sl = pm & 1;
         MemOps<NT> ma, mb;
         ops(s, 0, ma);
         ops(s, 1, mb);
         const f4 qk = ld4(s + R::QK + swz16(n, g)), qp = ld4(s + R::QP + swz16(n, g));
-        const f4 ska = sk_part(ma.ak), skb = sk_part(mb.ak);
-        const f4 sqa = sq_part(ma.ap), sqb = sq_part(mb.ap);
-        st4(&red[sl][w][0][lane * 4], ska);
-        st4(&red[sl][w][1][lane * 4], skb);
-        st4(&red[sl][w][2][lane * 4], sqa);
-        st4(&red[sl][w][3][lane * 4], sqb);
+        st4(&red[sl][w][0][lane * 4], sk_part(ma.ak));
+        st4(&red[sl][w][1][lane * 4], sk_part(mb.ak));
         wait_next();
         lds_barrier();
-        stage_pair(pm + NS, s);
-        compiler_fence();
-        const f4 ea = errors(ma, reduce(sl, 0));
+        const f4 r0 = reduce(sl, 0);
+        stage_part(ic<0>{}, pm + NS, s);
+        const f4 ea = errors(ma, r0);
+        stage_part(ic<1>{}, pm + NS, s);
+        const f4 sqa = sq_part(ma.ap);
+        stage_part(ic<2>{}, pm + NS, s);
         const f4 eb = errors(mb, mma4(qk, ea, reduce(sl, 1)));
-        f4 ob;
-        float rd;
-        if (ks == 0) {
-            ob = mma4(ea, ma.pa, reduce(sl, 2));
-            rd = ma.rd;
-        } else {
-            ob = mma4(eb, mb.pa, mma4(ea, qp, reduce(sl, 3)));
-            rd = mb.rd;
-        }
-        store_o(ks == 0 ? ca : ca + 1, ks < 2, ob, rd);
+        stage_part(ic<3>{}, pm + NS, s);
+        const f4 sqb = sq_part(mb.ap);
+        stage_part(ic<4>{}, pm + NS, s);
+        const f4 ob = readout(sl ^ 1);   // pair pm - 1 (nothing at pm = 0)
+        st4(&red[sl][w][2][lane * 4], sqa);
+        st4(&red[sl][w][3][lane * 4], sqb);
         update(ma, ea);
+        stage_part(ic<5>{}, pm + NS, s);
         update(mb, eb);
+        // the step's only store, after its copies (so the waits above count
+        // one store and the copies of a step)
+        const int cp = 2 * (pm - 1) + (ks == 0 ? 0 : 1);
+        store_o(max(cp, 0), pm > 0 && ks < 2, ob, cy.rd);
+        cy = Carry{ea, eb, ma.pa, mb.pa, qp, ks == 0 ? ma.rd : mb.rd};
     };
 
     stage_pair(0, stg0);
@@ -708,6 +732,10 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
             step2(pm + 1, stg1);
         }
         if (pm < NP) step2(pm, stg0);
+    }
+    if (NP > 0) {   // the readout of the last pair
+        lds_barrier();
+        store_o(2 * (NP - 1) + (ks == 0 ? 0 : 1), ks < 2, readout((NP - 1) & 1), cy.rd);
     }
     if (NC & 1) {   // the last chunk alone (staged as pair NP)
         const int c = NC - 1, sl = NP & 1, k = NP % NS;
