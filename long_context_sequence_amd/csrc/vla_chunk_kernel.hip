@@ -67,7 +67,7 @@ vla_fwd_fused(const Tin *__restrict__ q, const Tin *__restrict__ k,
             VLA_PROBE(p, 0);
             if (p < NC) {
                 hd.a_products(st, p);
-                hd.stage2();
+                hd.stage2(p);
             }
             VLA_PROBE(p, 1);
             lds_barrier();

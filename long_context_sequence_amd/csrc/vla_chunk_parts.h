@@ -318,6 +318,7 @@ template <int D>
 struct Lds {
     static constexpr int C = Cfg<D>::C, NA = Cfg<D>::NA, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
     static constexpr int UB = 2;   // buffers of u^ (by chunk parity)
+    static constexpr int ZKB = 1;  // buffers of the key sums
     static constexpr bool KEEP_IK = false;   // no copy of 1/|k| per token
     float uh[2][C * LD];     // u^   [token][i], by chunk parity
     float kh[2][C * LD];     // k^
@@ -377,6 +378,13 @@ struct Head {
     int pp = 0;                         // current period (timing probes only)
     RawVec<Tin, CPT> rq, rk, ru;
 
+    // phi(k), then the key sums, of chunk cq
+    __device__ __forceinline__ float *zkb(int cq) const
+    {
+        if constexpr (LdsT::ZKB == 2) return L.zk[cq & 1];
+        else return L.zk;
+    }
+
     __device__ __forceinline__ Head(LdsT &L_, const Tin *q_, const Tin *k_, const Tin *v_,
                                     const Tin *u_, float *o_, int T_, float eps_, size_t bh,
                                     int lane, int wi_, int ts_, bool stager, int kcol_)
@@ -426,11 +434,13 @@ struct Head {
         if constexpr (WU) ru.load(u + off);
     }
     // k^ (and u^, or phi(q) and phi(k)) of chunk cq into its LDS slot
+    // (rkh, rph: when given, k^ and phi(q) also go there, rows laid out by swzd)
     template <bool WQ, bool WU>
-    __device__ __forceinline__ void stage1(int cq)
+    __device__ __forceinline__ void stage1(int cq, float *rkh = nullptr, float *rph = nullptr)
     {
         if (!pthr) return;
         const int slot = cq & 1;
+        float *zk = zkb(cq);
         const bool ok = cq * C + tl < T;
         float pk = 0.f, pu = 0.f;
 #pragma unroll
@@ -451,44 +461,60 @@ struct Head {
         const int e0 = tl * LD + cc * CPT;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            L.kh[slot][e0 + i] = rk.get(i) * ik;
+            const float kv = rk.get(i) * ik;
+            L.kh[slot][e0 + i] = kv;
+            if (rkh) {
+                const int col = cc * CPT + i;
+                rkh[swzd<D>(tl, col >> 2) + (col & 3)] = kv;
+            }
             if constexpr (WU) L.uh[slot % LdsT::UB][e0 + i] = ru.get(i) * iu;
             if constexpr (WQ) {
-                L.ph[slot][e0 + i] = phi_fast(rq.get(i));
-                L.zk[e0 + i] = ok ? phi_fast(rk.get(i)) : 0.f;
+                const float pq = phi_fast(rq.get(i));
+                L.ph[slot][e0 + i] = pq;
+                if (rph) {
+                    const int col = cc * CPT + i;
+                    rph[swzd<D>(tl, col >> 2) + (col & 3)] = pq;
+                }
+                zk[e0 + i] = ok ? phi_fast(rk.get(i)) : 0.f;
             }
         }
     }
     // inclusive key sum per column: prefix inside the chunk, added to the
     // compensated sum of the earlier chunks
-    __device__ __forceinline__ void stage2()
+    __device__ __forceinline__ void stage2(int cq)
     {
         if (kcol < 0) return;
+        float *zk = zkb(cq);
         float f[C];
 #pragma unroll
-        for (int tt = 0; tt < C; ++tt) f[tt] = L.zk[tt * LD + kcol];
+        for (int tt = 0; tt < C; ++tt) f[tt] = zk[tt * LD + kcol];
         float loc = 0.f;
 #pragma unroll
         for (int tt = 0; tt < C; ++tt) {
             loc += f[tt];
-            L.zk[tt * LD + kcol] = zk_run + loc;
+            zk[tt * LD + kcol] = zk_run + loc;
         }
         const float yk = loc - zk_cmp;
         const float tsum = zk_run + yk;
         zk_cmp = (tsum - zk_run) - yk;
         zk_run = tsum;
     }
-    // readout denominators of chunk cq
-    __device__ __forceinline__ void stage3(int cq)
+    // readout denominators of chunk cq (also to rrd when given)
+    __device__ __forceinline__ void stage3(int cq, float *rrd = nullptr)
     {
         if (!pthr) return;
         const int slot = cq & 1;
+        const float *zk = zkb(cq);
         const int e0 = tl * LD + cc * CPT;
         float pd = 0.f;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) pd = fmaf(L.ph[slot][e0 + i], L.zk[e0 + i], pd);
+        for (int i = 0; i < CPT; ++i) pd = fmaf(L.ph[slot][e0 + i], zk[e0 + i], pd);
         pd = sum_row16(pd);
-        if (cc == 0) L.rden[slot][tl] = __builtin_amdgcn_rcpf(fmaxf(pd, eps));
+        const float rd = __builtin_amdgcn_rcpf(fmaxf(pd, eps));
+        if (cc == 0) {
+            L.rden[slot][tl] = rd;
+            if (rrd) rrd[tl] = rd;
+        }
     }
     // V' rows 4g+r of chunk cq (own blocks), kept as loaded
     __device__ __forceinline__ void load_v(int cq, Raw1<Tin> (&vraw)[BPW][4]) const
@@ -654,8 +680,8 @@ struct Head {
     // and leaves L^-1 (transposed), 1/d and the A operand of W' in LDS (its own
     // scratch, L.hms), while every wave forms Y0' of its blocks; then, after a
     // workgroup barrier, each wave downdates its blocks and forms W'.
-    template <class WOut>
-    __device__ __forceinline__ void a_update_shared(State &st, int p, WOut &&wout)
+    template <class WOut, class Side>
+    __device__ __forceinline__ void a_update_shared(State &st, int p, WOut &&wout, Side &&side)
     {
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
         const float *kb = L.kh[p & 1];
@@ -720,6 +746,7 @@ struct Head {
             sfor<4>([&](auto r) { hm[int(r)] = 4 * g + r <= n ? -(hm[int(r)] * inv4[int(r)]) : 0.f; });
             st4(&L.hms[4 * (16 * g + n)], hm);
         }
+        side();   // every wave, wave 0 after the factorisation
         lds_barrier();
         float X[4];
         sfor<4>([&](auto c) { X[c] = L.lit[0][(4 * c + g) * LT + n]; });   // L^-1 [n][4c+g]

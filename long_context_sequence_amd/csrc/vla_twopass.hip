@@ -347,11 +347,12 @@ template <int D>
 struct PLds {
     static constexpr int C = Cfg<D>::C, NA = Cfg<D>::NA, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
     static constexpr int UB = 1;
+    static constexpr int ZKB = 2;
     static constexpr bool KEEP_IK = false;
     float uh[1][C * LD];     // u^ [token][i] (read before the next chunk is staged)
     float kh[2][C * LD];     // k^, by chunk parity
     float ph[2][C * LD];     // phi(q), by chunk parity
-    float zk[C * LD];        // phi(k), then the inclusive key sum
+    float zk[2][C * LD];     // phi(k), then the inclusive key sum, by chunk parity
     float rden[2][C];
     float z0[C * LD];
     float z0t[D * LT];
@@ -366,6 +367,79 @@ struct PLds {
     };
     float inv[NA][C];
     float hms[256];          // A operand of W' (per lane), from wave 0
+};
+
+// Staging of the penalty pass by its last two waves, 8 lanes per token (lane
+// cc of token tl holds columns [cc CP, +CP)): raw q, k, u of a chunk into
+// registers, then k^, u^, phi(q), phi(k) into LDS, k^ and phi(q) also to the
+// chunk's record; later the readout denominators of the chunk.
+__device__ __forceinline__ float sum_row8(float x)
+{
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    return x;
+}
+
+template <int D, typename Tin>
+struct PenStage {
+    static constexpr int LD = Cfg<D>::LD, CP = D / 8;
+    int tl, cc;
+    bool on;
+    RawVec<Tin, CP> rq, rk, ru;
+    __device__ __forceinline__ explicit PenStage(int ts)
+        : tl((ts >> 3) & (CH - 1)), cc(ts & 7), on(ts >= 0 && ts < 8 * CH)
+    {
+    }
+    // rows past T re-read row T-1 (stage zeroes k^, u^ and phi(k) there)
+    __device__ __forceinline__ void prefetch(const Tin *q, const Tin *k, const Tin *u, size_t tok0,
+                                             int T, int cq)
+    {
+        if (!on) return;
+        const int t = cq * CH + tl;
+        const size_t off = (tok0 + (size_t)(t < T ? t : T - 1)) * D + (size_t)cc * CP;
+        rq.load(q + off);
+        rk.load(k + off);
+        ru.load(u + off);
+    }
+    __device__ __forceinline__ void stage(PLds<D> &L, int cq, int T, float *rkh, float *rph)
+    {
+        if (!on) return;
+        const int slot = cq & 1;
+        const bool ok = cq * CH + tl < T;
+        float pk = 0.f, pu = 0.f;
+#pragma unroll
+        for (int i = 0; i < CP; ++i) {
+            pk = fmaf(rk.get(i), rk.get(i), pk);
+            pu = fmaf(ru.get(i), ru.get(i), pu);
+        }
+        const float nk = sum_row8(pk), nu = sum_row8(pu);
+        const float ik = ok && nk > 0.f ? rsqrtf(nk) : 0.f;
+        const float iu = ok && nu > 0.f ? rsqrtf(nu) : 0.f;
+        const int e0 = tl * LD + cc * CP;
+#pragma unroll
+        for (int i = 0; i < CP; ++i) {
+            const int col = cc * CP + i;
+            const float kv = rk.get(i) * ik, pq = phi_fast(rq.get(i));
+            L.kh[slot][e0 + i] = kv;
+            L.uh[0][e0 + i] = ru.get(i) * iu;
+            L.ph[slot][e0 + i] = pq;
+            L.zk[slot][e0 + i] = ok ? phi_fast(rk.get(i)) : 0.f;
+            rkh[swzd<D>(tl, col >> 2) + (col & 3)] = kv;
+            rph[swzd<D>(tl, col >> 2) + (col & 3)] = pq;
+        }
+    }
+    // 1 / max(phi(q)' zkey, eps) per token of chunk cq (key sums in LDS) to rrd
+    __device__ __forceinline__ void den(const PLds<D> &L, int cq, float eps, float *rrd) const
+    {
+        if (!on) return;
+        const int slot = cq & 1, e0 = tl * LD + cc * CP;
+        float pd = 0.f;
+#pragma unroll
+        for (int i = 0; i < CP; ++i) pd = fmaf(L.ph[slot][e0 + i], L.zk[slot][e0 + i], pd);
+        pd = sum_row8(pd);
+        if (cc == 0) rrd[tl] = __builtin_amdgcn_rcpf(fmaxf(pd, eps));
+    }
 };
 
 // X' for X = Alpha^'Y (C x C) with Alpha^ = W diag(1/|w|) of the current chunk
@@ -388,13 +462,15 @@ __device__ __forceinline__ void cross_factor(const PLds<D> &L, const float *y, i
 
 // Workgroup (head, segment j): the penalty chain over chunks [j SC, (j+1) SC)
 // from A at the segment start, writing each chunk's record.  Per chunk p:
-//   1  Z0, Grams of chunk p; key-sum prefix of chunk p       | barrier
-//   2  wave 0: factorise I + G; all: Y0 of own blocks        | barrier
-//      downdate A, W of chunk p; 1/den of chunk p;
-//      stage chunk p+1, prefetch p+2                         | barrier
-//   3  1/|w|, Alpha^'K^ and Alpha^'Phi partials; alpha^ and
-//      1/den to the record                                   | barrier
-//   4  wave 1: (I+N)^-1 and P to the record.
+//   1  Z0, Grams of chunk p                                  | barrier
+//   2  all: Y0 of own blocks; wave 0: factorise I + G;
+//      wave 1: (I+N)^-1 and P of chunk p-1 to the record;
+//      cross factors of chunk p-1 (if even) with chunk p;
+//      key-sum prefix of chunk p; stage chunk p+1 (k^ and
+//      phi(q) also to its record), prefetch p+2              | barrier
+//   3  downdate A, W of chunk p; 1/den of chunk p            | barrier
+//   4  1/|w|, Alpha^'K^ and Alpha^'Phi partials; alpha^ to
+//      the record.
 template <int D, typename Tin>
 __global__ void __launch_bounds__(64 * Cfg<D>::NA)
 vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ u,
@@ -414,8 +490,10 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     const int c0 = j * SC, c1 = min(NC, c0 + SC);
 
     // serial work spread over the waves: wave 0 factorises I + G, wave 1 forms
-    // the C x C factors of the record, waves 2 and up own the key sums
-    Hd hd(L, q, k, nullptr, u, nullptr, T, eps, bh, tid & 63, w, tid, true, tid - 128);
+    // the C x C factors of the record, the waves from 2 on own the key sums, and
+    // the last two waves stage the inputs
+    Hd hd(L, q, k, nullptr, u, nullptr, T, eps, bh, tid & 63, w, tid, false, tid - 128);
+    PenStage<D, Tin> ps(tid - 64 * (NA - 2));
     typename Hd::State st;
     const float *a_init;
     if (j > 0)
@@ -429,24 +507,37 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         else if (zk0)
             hd.zk_run = S > 1 ? zseg[(size_t)bh * S * D + hd.kcol] : zk0[bh * D + hd.kcol];
     }
-    hd.template prefetch<true, true>(c0);
-    hd.template stage1<true, true>(c0);
-    if (c0 + 1 < c1) hd.template prefetch<true, true>(c0 + 1);
+    const size_t tok0 = (size_t)bh * T;
+    float *rb = rec + ((size_t)bh * NC + c0) * RS;   // record of chunk p below
+    ps.prefetch(q, k, u, tok0, T, c0);
+    ps.stage(L, c0, T, rb + Rec<D>::KH, rb + Rec<D>::PH);
+    if (c0 + 1 < c1) ps.prefetch(q, k, u, tok0, T, c0 + 1);
     vmem_drain();
     __syncthreads();
 
+    // While wave 0 factorises I + G of chunk p, the other waves form the C x C
+    // factors of chunk p - 1 and, for an even p - 1, its cross factors with
+    // chunk p (from W, |w|^2 of chunk p - 1, still in LDS), the key sums of
+    // chunk p, and stage chunk p + 1.
     WToLds<D, PLds<D>> wl{L, 0, hd.g, hd.n};
-    float *rb = rec + ((size_t)bh * NC + c0) * RS;
     for (int p = c0; p < c1; ++p, rb += RS) {
         hd.a_products(st, p);
-        hd.stage2();
         lds_barrier();
-        hd.a_update_shared(st, p, wl);
-        hd.stage3(p);
-        if (p + 1 < c1) {
-            hd.template stage1<true, true>(p + 1);
-            if (p + 2 < c1) hd.template prefetch<true, true>(p + 2);
-        }
+        hd.a_update_shared(st, p, wl, [&]() {
+            if (p > c0) {
+                if (w == 1) hd.prep_tp(rb - RS + Rec<D>::TT, rb - RS + Rec<D>::PT);
+                if (((p - 1) & 1) == 0) {
+                    if (w == 1) cross_factor<D>(L, L.kh[p & 1], hd.g, hd.n, rb - RS + Rec<D>::QK);
+                    if (w == NA - 1) cross_factor<D>(L, L.ph[p & 1], hd.g, hd.n, rb - RS + Rec<D>::QP);
+                }
+            }
+            hd.stage2(p);
+            if (p + 1 < c1) {
+                ps.stage(L, p + 1, T, rb + RS + Rec<D>::KH, rb + RS + Rec<D>::PH);
+                if (p + 2 < c1) ps.prefetch(q, k, u, tok0, T, p + 2);
+            }
+        });
+        ps.den(L, p, eps, rb + Rec<D>::RD);
         lds_barrier();
         f4 invn4;
         hd.s_grams(p, invn4);
@@ -455,20 +546,9 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             const f4 a = ld4(&L.wt[0][(16 * b + hd.n) * LT + 4 * hd.g]) * invn4;
             st4(&rb[Rec<D>::AH + swz16(16 * b + hd.n, hd.g)], a);
         });
-        if (tid < CH) rb[Rec<D>::RD + tid] = L.rden[p & 1][tid];
-        for (int f = tid; f < CH * D / 4; f += 64 * Cfg<D>::NA) {   // k^ and phi(q), unpadded
-            const int tk = f / (D / 4), c4 = 4 * (f % (D / 4));
-            st4(&rb[Rec<D>::KH + swzd<D>(tk, c4 / 4)], ld4(&L.kh[p & 1][tk * Cfg<D>::LD + c4]));
-            st4(&rb[Rec<D>::PH + swzd<D>(tk, c4 / 4)], ld4(&L.ph[p & 1][tk * Cfg<D>::LD + c4]));
-        }
-        // the cross factors of an even chunk with the next one (staged above)
-        if ((p & 1) == 0 && p + 1 < c1 && w >= NA - 2) {
-            const float *nb = w == NA - 2 ? L.kh[(p + 1) & 1] : L.ph[(p + 1) & 1];
-            cross_factor<D>(L, nb, hd.g, hd.n, rb + (w == NA - 2 ? Rec<D>::QK : Rec<D>::QP));
-        }
-        lds_barrier();
-        if (w == 1) hd.prep_tp(rb + Rec<D>::TT, rb + Rec<D>::PT);
     }
+    lds_barrier();
+    if (w == 1 && c1 > c0) hd.prep_tp(rb - RS + Rec<D>::TT, rb - RS + Rec<D>::PT);
     if (j == S - 1) {
         if (A_out) hd.store_state(st, A_out + bh * DD);
         if (hd.kcol >= 0 && zk_out) zk_out[bh * D + hd.kcol] = hd.zk_run;
