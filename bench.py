@@ -5,6 +5,9 @@ One step = one ``vla_forward`` over the whole batch of the d_h = 64, T = 4096
 workload (B = 8, H = 16, bf16 q/k/v/u, fp32 state), writing o and the final
 S, A and zkey.  Inputs are resident in HBM before the timed region.
 
+Warm-up: the --warmup steps, extended until the forward has run for at least
+SETTLE_S seconds (the device clocks take some tens of milliseconds to settle).
+
 Prints ONE JSON line with the throughput in tokens*heads/s, the percentage of
 the MI355X FP32 peak, a roofline record for the forward (algorithmic FLOP /
 average time of its launches from HIP events on the launch stream; the kernels
@@ -27,6 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "VLA fwd tokens·heads/sec (fp32 state) + % of MI355X FP32 vector peak"
 UNIT = "tokens*heads/s"
+SETTLE_S = 0.25                         # minimum warm-up time of the timed kernel
 FP32_VECTOR_PEAK_TFLOPS = 157.3          # MI355X published FP32 vector (and dense fp32 matrix) peak
 WORKLOAD = 3                              # B=8, H=16, d_h=64, T=4096, bf16 inputs
 KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_twopass.hip",
@@ -92,8 +96,8 @@ def tok_heads_total(cfg) -> int:
 def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the oracle timing (e.g. under a profiler)")
     p.add_argument("--cpu-heads", type=int, default=0,
@@ -209,8 +213,16 @@ def main():
         vla.vla_forward(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps,
                         o=o, S_out=S, A_out=A, zkey_out=zk, stream=stream, workspace=ws)
 
-    for _ in range(args.warmup):
+    # warm-up: the W steps asked for, continued until the device has run this
+    # work for SETTLE_S seconds (its clocks take some tens of milliseconds to
+    # settle after an idle period)
+    t_w = time.perf_counter()
+    n_w = 0
+    while n_w < args.warmup or time.perf_counter() - t_w < SETTLE_S:
         step()
+        n_w += 1
+        if n_w % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -259,6 +271,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": n_w,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -319,22 +319,43 @@ vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
     } else {
         sfor<EPT>([&](auto e) { m[e] = i == c0 + e ? (double)lambda0 : 0.0; });
     }
-    // G parts of the segments before j
-    for (int s = 0; s < j * P; ++s) {
-        const double2 *G = reinterpret_cast<const double2 *>(gram + ((size_t)bh * S1 * P + s) * DD +
-                                                             (size_t)i * D + c0);
+    // G parts of the segments before j, in order, loads four parts ahead
+    const int NPART = j * P;
+    const double *gb = gram + (size_t)bh * S1 * P * DD + (size_t)i * D + c0;
+    auto add_part = [&](const double2 (&x)[EPT / 2]) {
         sfor<EPT / 2>([&](auto h) {
-            const double2 x = G[h];
-            m[2 * h] += x.x;
-            m[2 * h + 1] += x.y;
+            m[2 * h] += x[h].x;
+            m[2 * h + 1] += x[h].y;
         });
+    };
+    int s = 0;
+    for (; s + 4 <= NPART; s += 4) {
+        double2 x[4][EPT / 2];
+        sfor<4>([&](auto v) {
+            const double2 *G = reinterpret_cast<const double2 *>(gb + (size_t)(s + v) * DD);
+            sfor<EPT / 2>([&](auto h) { x[v][h] = G[h]; });
+        });
+        sfor<4>([&](auto v) { add_part(x[v]); });
+    }
+    for (; s < NPART; ++s) {
+        double2 x[EPT / 2];
+        const double2 *G = reinterpret_cast<const double2 *>(gb + (size_t)s * DD);
+        sfor<EPT / 2>([&](auto h) { x[h] = G[h]; });
+        add_part(x);
     }
     sweep_all<D, EPT>(m, i, c0, rowbuf);   // -M^-1
     float *A = aseg + ((size_t)bh * S + j) * DD + (size_t)i * D + c0;
     sfor<EPT>([&](auto e) { A[e] = (float)(-m[e]); });
     if (tid < D) {
         double z = zk0 ? (double)zk0[bh * D + tid] : 0.0;
-        for (int s = 0; s < j * P; ++s) z += zks[((size_t)bh * S1 * P + s) * D + tid];
+        const double *zb = zks + (size_t)bh * S1 * P * D + tid;
+        int s2 = 0;
+        for (; s2 + 4 <= NPART; s2 += 4) {
+            double x[4];
+            sfor<4>([&](auto v) { x[v] = zb[(size_t)(s2 + v) * D]; });
+            sfor<4>([&](auto v) { z += x[v]; });
+        }
+        for (; s2 < NPART; ++s2) z += zb[(size_t)s2 * D];
         zseg[((size_t)bh * S + j) * D + tid] = (float)z;
         if (zk0 && j == 1) zseg[(size_t)bh * S * D + tid] = zk0[bh * D + tid];
     }
