@@ -881,10 +881,13 @@ Plan make_plan(int BH, int T, int D)
     p.SC = (p.NC + S - 1) / S;
     p.SC += p.SC & 1;   // segments start at even chunks (pairs of the memory pass)
     p.S = (p.NC + p.SC - 1) / p.SC;
-    if (p.S > 1) {   // gram parts: about 1024 workgroups, each at least 4 chunks
-        const int want = (1024 + BH * (p.S - 1) - 1) / (BH * (p.S - 1));
+    if (p.S > 1) {   // gram parts: at most one round of workgroups (LDS allows
+                     // 3, 2, 1 per compute unit at d = 64, 96, 128), each at
+                     // least 4 chunks
+        const int round = 256 * (D == 64 ? 3 : D == 96 ? 2 : 1);
+        const int want = round / (BH * (p.S - 1));
         const int most = p.SC / 4 > 1 ? p.SC / 4 : 1;
-        p.P = want < most ? want : most;
+        p.P = want < 1 ? 1 : (want < most ? want : most);
     }
     const int rs = 48 * D + 4 * CH * CH + CH;   // Rec<D>::SIZE
     size_t off = 0;
