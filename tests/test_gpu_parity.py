@@ -349,6 +349,38 @@ def test_workspace_reuse_and_stream():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d,dtype,B,H,T", [
+    (64, "bf16", 2, 3, 777),      # odd chunk count: a lone last chunk
+    (96, "f32", 1, 2, 500),
+    (128, "bf16", 1, 1, 48),      # three chunks
+    (64, "f32", 1, 1, 3000),      # one head: many segments
+])
+def test_workspace_of_nans(d, dtype, B, H, T):
+    """A workspace whose every float is NaN gives the bits of a zeroed one: no
+    field the forward leaves unwritten (the cross factors of odd chunks, a
+    record's padding) is ever used."""
+    dev = _dev()
+    vla = _vla()
+    import dataclasses
+    base = gen.config(3 if dtype == "bf16" else 2)
+    cfg = dataclasses.replace(base, d=d).with_sizes(B=B, H=H, T=T)
+    _say(f"NaN workspace d={d} {dtype} B={B} H={H} T={T}")
+    x = gen.make_inputs(cfg)
+    t = {n: _to_dev(x[n], cfg, dev) for n in "qkvu"}
+    n = vla.workspace_size(B, H, T, d)
+    outs = []
+    for fill in (0xFF, 0x00):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device=dev)
+        outs.append(vla.vla_forward(*(t[k] for k in "qkvu"), cfg.lambda0, cfg.eps,
+                                    return_state=True, workspace=ws))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    ref = oracle.forward(*(_f64(x[k], cfg) for k in "qkvu"), cfg.lambda0, cfg.eps)
+    for name, g in zip(("o", "S", "A", "zkey"), outs[0]):
+        _check(name, g.cpu().numpy(), ref[name])
+
+
 def test_phases_equal_forward_and_pipeline_on_two_streams():
     """vla_forward_penalty then vla_forward_memory give vla_forward's bits; two
     batches pipelined over two streams (penalty pass of batch 2 while the memory
