@@ -788,24 +788,25 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
         const f4 qk = ld4(s + R::QK + swz16(n, g)), qp = ld4(s + R::QP + swz16(n, g));
         st4(&red[sl][w][0][lane * 4], sk_part(ma.ak));
         st4(&red[sl][w][1][lane * 4], sk_part(mb.ak));
+        // the S Phi partials are formed before the barrier and go to LDS after
+        // it (read one step later)
+        const f4 sqa = sq_part(ma.ap), sqb = sq_part(mb.ap);
         wait_next();
         lds_barrier();
         const f4 r0 = reduce(sl, 0);
         stage_part(ic<0>{}, pm + NS, s);
         const f4 ea = errors(ma, r0);
         stage_part(ic<1>{}, pm + NS, s);
-        const f4 sqa = sq_part(ma.ap);
+        const f4 ob = readout(sl ^ 1);   // pair pm - 1 (nothing at pm = 0)
         stage_part(ic<2>{}, pm + NS, s);
         const f4 eb = errors(mb, mma4(qk, ea, reduce(sl, 1)));
         stage_part(ic<3>{}, pm + NS, s);
-        const f4 sqb = sq_part(mb.ap);
+        update(ma, ea);
         stage_part(ic<4>{}, pm + NS, s);
-        const f4 ob = readout(sl ^ 1);   // pair pm - 1 (nothing at pm = 0)
+        update(mb, eb);
         st4(&red[sl][w][2][lane * 4], sqa);
         st4(&red[sl][w][3][lane * 4], sqb);
-        update(ma, ea);
         stage_part(ic<5>{}, pm + NS, s);
-        update(mb, eb);
         // the step's only store, after its copies (so the waits above count
         // one store and the copies of a step)
         const int cp = 2 * (pm - 1) + (ks == 0 ? 0 : 1);
