@@ -607,6 +607,7 @@ struct Head {
         // of pivot j (software pipelining); only its k = j term waits for it.
         float LDr[16], NLr[16];
         float ca = Mr[0], cb = 0.f;   // accumulators of the current column
+        float invn = 0.f;
         sfor<16>([&](auto jj) {
             constexpr int j = decltype(jj)::value;
             if constexpr (j > 0) ldl_block<j, j - 1, 1>(ca, LDr, NLr);
@@ -622,7 +623,7 @@ struct Head {
             }
             LDr[j] = acc;
             NLr[j] = n > j ? -(acc * inv) : 0.f;
-            if (g == 0 && n == 0) L.inv[wi][j] = inv;
+            invn = n == j ? inv : invn;   // lane n keeps 1 / d_n
             if constexpr (j + 1 < 16 && E > E1) ldl_early<j + 1, E1, E - E1>(na, nb, LDr, NLr);
             ca = na;
             cb = nb;
@@ -631,6 +632,7 @@ struct Head {
                 sfor<BPW>([&](auto bb) { y[bb] = mma(ak[ks / 4][ks % 4], st[bb][ks / 4][ks % 4], y[bb]); });
             });
         });
+        L.inv[wi][n] = invn;   // every lane group holds the same values
         VLA_PROBE(pp, 6);
         // L^-1 by forward substitution, four columns at a time: lane group g
         // computes column 4c + g in X[c] (lane n = row n).
@@ -714,6 +716,7 @@ struct Head {
             // LDL' as in a_update
             float LDr[16], NLr[16];
             float ca = Mr[0], cb = 0.f;
+            float invn = 0.f;
             sfor<16>([&](auto jj) {
                 constexpr int j = decltype(jj)::value;
                 if constexpr (j > 0) ldl_block<j, j - 1, 1>(ca, LDr, NLr);
@@ -727,11 +730,12 @@ struct Head {
                 }
                 LDr[j] = acc;
                 NLr[j] = n > j ? -(acc * inv) : 0.f;
-                if (g == 0 && n == 0) L.inv[0][j] = inv;
+                invn = n == j ? inv : invn;   // lane n keeps 1 / d_n
                 if constexpr (j + 1 < 16 && E > E1) ldl_early<j + 1, E1, E - E1>(na, nb, LDr, NLr);
                 ca = na;
                 cb = nb;
             });
+            L.inv[0][n] = invn;   // every lane group holds the same values
             float X[4];
             sfor<4>([&](auto c) { X[c] = n == 4 * c + g ? 1.f : 0.f; });
             asm volatile(VLA_LINV_BLOCK
