@@ -25,15 +25,18 @@ vla_status check_common(int in_dtype, int B, int H, int d_h, float eps)
 }
 
 // d_h in {64, 96, 128}: sequences (T >= 1) run on the two-pass matrix-core
-// kernels; a single decode token and T = 0 on the one-workgroup-per-head kernel
-// (every state element is read and written by the same lane there, so the state
-// may be updated in place).  d_h in {16, 32} uses the LDS kernel.
+// kernels; a single decode token on the decode kernel and T = 0 on the
+// one-workgroup-per-head kernel (both read and write every state element from
+// the same lane, so the state may be updated in place).  d_h in {16, 32} uses
+// the LDS kernel.
 vla_status launch(const vla::FwdArgs &a, bool step)
 {
     hipError_t e;
     if (!vla::chunk_supported(a.d))
         e = vla::launch_forward_ref(a);
-    else if (step || a.T == 0)
+    else if (step)
+        e = vla::launch_step(a);
+    else if (a.T == 0)
         e = vla::launch_forward_chunk(a);
     else
         e = vla::launch_forward_twopass(a, 3);

@@ -37,6 +37,8 @@ hipError_t launch_forward_ref(const FwdArgs &a);
 bool chunk_supported(int d);
 // one workgroup per head with both chains (decode steps and T = 0)
 hipError_t launch_forward_chunk(const FwdArgs &a);
+// one decode token, state in place (a.T == 1; S_out, A_out, zk_out are the state)
+hipError_t launch_step(const FwdArgs &a);
 // two passes over the sequence (forward, T >= 1); needs the workspace below.
 // phases: 1 = penalty pass (Grams, segment inverses, penalty chain and the
 // per-chunk factors in the workspace), 2 = memory pass, 3 = both.
