@@ -249,6 +249,39 @@ def test_step_matches_oracle(dtype):
     _check("zkey", zk.cpu().numpy(), ref["zkey"])
 
 
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_step_degenerate_tokens_every_d(d, dtype):
+    """Decode steps for every head dimension of the decode kernel, after a
+    forward, with zero keys, zero penalty directions and very negative queries
+    among the steps."""
+    dev = _dev()
+    vla = _vla()
+    import dataclasses
+    base = gen.config(3 if dtype == "bf16" else 2)
+    cfg = dataclasses.replace(base, d=d).with_sizes(B=1, H=3, T=70)
+    _say(f"steps d={d} {dtype}")
+    x = gen.make_inputs(cfg)
+    neg = gen.bf16_bits(np.float32([-60.0]))[0] if dtype == "bf16" else np.float32(-60.0)
+    x["k"][:, :, 40] = 0     # +0.0 in both storage types
+    x["u"][:, :, 45] = 0
+    x["u"][:, 1, 50:60] = 0
+    x["q"][:, :, 47] = neg
+    t = {n: _to_dev(x[n], cfg, dev) for n in "qkvu"}
+    T1 = 37
+    _, S, A, zk = vla.vla_forward(*(t[n][:, :, :T1].contiguous() for n in "qkvu"), cfg.lambda0,
+                                  cfg.eps, return_state=True)
+    outs = [vla.vla_step(*(t[n][:, :, i].contiguous() for n in "qkvu"), S, A, zk, cfg.eps)
+            for i in range(T1, cfg.T)]
+    torch.cuda.synchronize()
+    o = torch.stack(outs, dim=2).cpu().numpy()
+    ref = oracle.forward(*(_f64(x[n], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+    _check("o", o, ref["o"][:, :, T1:])
+    _check("S", S.cpu().numpy(), ref["S"])
+    _check("A", A.cpu().numpy(), ref["A"])
+    _check("zkey", zk.cpu().numpy(), ref["zkey"])
+
+
 def test_degenerate_tokens():
     """Zero keys, zero penalty directions and very negative queries (the eps
     branch of the readout denominator)."""
