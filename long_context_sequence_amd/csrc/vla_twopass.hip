@@ -28,7 +28,8 @@
 //            with S corrected by cross factors the penalty pass also records):
 //                R = V - S K^,  E = R (I + N)^-1,
 //                o = (S Phi + E P) / den,  S <- S + E Alpha^'.
-//            Records and v reach LDS through direct copies, three steps ahead.
+//            Records and v reach LDS through direct copies, two or three steps
+//            ahead (as many stages as LDS holds).
 //            Rows of S do not interact, so the value rows of a head are split
 //            over workgroups, and the key columns of a block over the waves of a
 //            workgroup (partial products summed through LDS in a fixed order).
@@ -635,14 +636,16 @@ struct MemOps {
 //   E_b' = T_b'(V_b - S K^_b - E_a Alpha^_a'K^_b)'   (S after a, applied to K^_b);
 //   key split 0: o_a = (S Phi_a + E_a P_a) / den, key split 1:
 //   o_b = (S Phi_b + E_a Alpha^_a'Phi_b + E_b P_b) / den  (value x token, so
-//   that a lane stores four consecutive values of one token);
+//   that a lane stores four consecutive values of one token; formed in the
+//   next step, once the S Phi partials of the other waves have crossed its
+//   barrier);
 //   S' += Alpha^_a E_a' + Alpha^_b E_b'.
 // An odd last chunk takes the single-chunk form of the same step.
 //
 // Pair p is staged in LDS stage p mod NS.  Every wave copies its pieces of pair
-// p + NS right after the barrier of step p (all reads of stage p mod NS are
-// done by then) and waits for its pieces of pair p + 1 before the barrier of
-// step p, so that the barrier publishes them.
+// p + NS after the barrier of step p (all reads of stage p mod NS are done by
+// then), spread over the step, and waits for its pieces of pair p + 1 before
+// the barrier of step p, so that the barrier publishes them.
 template <int D, typename Tin>
 __global__ void __launch_bounds__(64 * MemCfg<D>::VBW * MemCfg<D>::KS)
 vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec, const float *S0,
