@@ -124,11 +124,12 @@ vla_status vla_forward_memory(const void *q, const void *k, const void *v, int i
 /*
  * vla_forward_workspace_size -- bytes of device workspace vla_forward needs for
  * these sizes (0 when it needs none: d_h in {16, 32}, or T == 0), in *bytes.
- * At d_h = 64 it is about 14.5 KB per 16 tokens of each head (the per-chunk
- * factors and the chunk's k^ and phi(q)) plus a few d_h x d_h matrices per
- * head.  Host-only; launches
- * nothing.  Errors: VLA_ERR_INVALID_ARG (NULL bytes, bad sizes),
- * VLA_ERR_UNSUPPORTED (d_h).
+ * Per head it holds one record of (48 d_h + 1040) fp32 values for every chunk
+ * of 16 tokens (the chunk's factors, k^ and phi(q): 16.1 KiB at d_h = 64) and,
+ * when the penalty chain is split into segments, per segment the fp64 Gram
+ * partial sums and the fp32 starting A and zkey; at B = 8, H = 16, T = 4096,
+ * d_h = 64 the total is 546.5 MiB.  Host-only; launches nothing.  Errors:
+ * VLA_ERR_INVALID_ARG (NULL bytes, bad sizes), VLA_ERR_UNSUPPORTED (d_h).
  */
 vla_status vla_forward_workspace_size(int B, int H, int T, int d_h, size_t *bytes);
 

@@ -114,34 +114,14 @@ __device__ __forceinline__ f4 ld4(const float *p) { return *reinterpret_cast<con
 // Raw buffer view of device memory: a uniform base and extent in a resource
 // descriptor, 32-bit per-lane byte offsets, no 64-bit vector address math.
 // Loads past the extent return 0 and stores past it are dropped (every access
-// here is whole dwords inside or outside a row, never straddling the end).
+// here is whole 16-byte granules inside or outside a row, never straddling the
+// end).
 struct Buf {
     __amdgpu_buffer_rsrc_t r;
     __device__ __forceinline__ Buf(const void *base, unsigned bytes)
         : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                               0x00020000))
     {
-    }
-    __device__ __forceinline__ f4 ld128(unsigned off, unsigned soff = 0) const
-    {
-        return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
-    }
-    __device__ __forceinline__ uint2 ld64(unsigned off, unsigned soff = 0) const
-    {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0);
-        return make_uint2(x[0], x[1]);
-    }
-    __device__ __forceinline__ uint32_t ld32(unsigned off, unsigned soff = 0) const
-    {
-        return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
-    }
-    __device__ __forceinline__ uint32_t ld16(unsigned off, unsigned soff = 0) const
-    {
-        return __builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0);
-    }
-    __device__ __forceinline__ void st32(float x, unsigned off, unsigned soff = 0) const
-    {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, soff, 0);
     }
     __device__ __forceinline__ void st128(f4 x, unsigned off, unsigned soff = 0) const
     {
@@ -156,18 +136,6 @@ struct Buf {
     }
 };
 
-// Load of a T at a uniform base plus a 32-bit unsigned byte offset (the form the
-// hardware addresses as scalar base + vector offset, with no 64-bit vector math).
-template <typename T>
-__device__ __forceinline__ T ldo(const void *base, unsigned byte_off)
-{
-    return *reinterpret_cast<const T *>(static_cast<const char *>(base) + byte_off);
-}
-template <typename T>
-__device__ __forceinline__ void sto(void *base, unsigned byte_off, T x)
-{
-    *reinterpret_cast<T *>(static_cast<char *>(base) + byte_off) = x;
-}
 __device__ __forceinline__ void st4(float *p, f4 x) { *reinterpret_cast<f4 *>(p) = x; }
 
 template <int CTRL>
@@ -220,69 +188,31 @@ template <typename Tin> struct Raw1;
 template <> struct Raw1<float> {
     float x;
     __device__ __forceinline__ void load(const float *p, size_t i) { x = p[i]; }
-    __device__ __forceinline__ void load_at(const float *base, unsigned i) { x = ldo<float>(base, 4u * i); }
-    __device__ __forceinline__ void load_buf(const Buf &b, unsigned i) { x = __uint_as_float(b.ld32(4u * i)); }
     __device__ __forceinline__ float get() const { return x; }
 };
 template <> struct Raw1<uint16_t> {
     uint32_t x;
     __device__ __forceinline__ void load(const uint16_t *p, size_t i) { x = p[i]; }
-    __device__ __forceinline__ void load_at(const uint16_t *base, unsigned i) { x = ldo<uint16_t>(base, 2u * i); }
-    __device__ __forceinline__ void load_buf(const Buf &b, unsigned i) { x = b.ld16(2u * i); }
     __device__ __forceinline__ float get() const { return __uint_as_float(x << 16); }
 };
 
 // CPT consecutive inputs of one token, held in registers.
 template <typename Tin, int N> struct RawVec;
-template <int N> struct RawVec<float, N> {   // N in {4, 6, 8}; 8-byte aligned
+template <int N> struct RawVec<float, N> {   // N even; 8-byte aligned
     float2 x[N / 2];
     __device__ __forceinline__ void load(const float *p)
     {
 #pragma unroll
         for (int i = 0; i < N / 2; ++i) x[i] = reinterpret_cast<const float2 *>(p)[i];
     }
-    __device__ __forceinline__ void load_buf(const Buf &b, unsigned i)   // N == 4
-    {
-        const f4 y = b.ld128(4u * i);
-        x[0] = make_float2(y[0], y[1]);
-        x[1] = make_float2(y[2], y[3]);
-    }
-    __device__ __forceinline__ void load_at(const float *base, unsigned i)
-    {
-        if constexpr (N == 4) {
-            const f4 y = ldo<f4>(base, 4u * i);
-            x[0] = make_float2(y[0], y[1]);
-            x[1] = make_float2(y[2], y[3]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < N / 2; ++j) x[j] = ldo<float2>(base, 4u * i + 8u * j);
-        }
-    }
     __device__ __forceinline__ float get(int i) const { return (i & 1) ? x[i >> 1].y : x[i >> 1].x; }
 };
-template <int N> struct RawVec<uint16_t, N> {   // N in {4, 6, 8}; 4-byte aligned
+template <int N> struct RawVec<uint16_t, N> {   // N even; 4-byte aligned
     uint32_t x[N / 2];
     __device__ __forceinline__ void load(const uint16_t *p)
     {
 #pragma unroll
         for (int i = 0; i < N / 2; ++i) x[i] = reinterpret_cast<const uint32_t *>(p)[i];
-    }
-    __device__ __forceinline__ void load_buf(const Buf &b, unsigned i)   // N == 4
-    {
-        const uint2 y = b.ld64(2u * i);
-        x[0] = y.x;
-        x[1] = y.y;
-    }
-    __device__ __forceinline__ void load_at(const uint16_t *base, unsigned i)
-    {
-        if constexpr (N == 4) {
-            const uint2 y = ldo<uint2>(base, 2u * i);
-            x[0] = y.x;
-            x[1] = y.y;
-        } else {
-#pragma unroll
-            for (int j = 0; j < N / 2; ++j) x[j] = ldo<uint32_t>(base, 2u * i + 4u * j);
-        }
     }
     __device__ __forceinline__ float get(int i) const
     {
@@ -302,7 +232,6 @@ struct Cfg {
     static constexpr int LD = D + 4;               // row stride of [token][i] arrays
     static constexpr int LT = C + 4;               // row stride of [i][token] and C x C arrays
     static constexpr int CPT = D / 16;             // staged columns per thread (16 per token)
-    static constexpr int WSLOT = 16 * D + 16 * NA; // floats of one chunk's W' and |w|^2 partials
 };
 
 // Layouts of the per-chunk matrices the memory pass reads through LDS: the
@@ -319,7 +248,6 @@ struct Lds {
     static constexpr int C = Cfg<D>::C, NA = Cfg<D>::NA, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
     static constexpr int UB = 2;   // buffers of u^ (by chunk parity)
     static constexpr int ZKB = 1;  // buffers of the key sums
-    static constexpr bool KEEP_IK = false;   // no copy of 1/|k| per token
     float uh[2][C * LD];     // u^   [token][i], by chunk parity
     float kh[2][C * LD];     // k^
     float ph[2][C * LD];     // phi(q)
@@ -434,9 +362,8 @@ struct Head {
         if constexpr (WU) ru.load(u + off);
     }
     // k^ (and u^, or phi(q) and phi(k)) of chunk cq into its LDS slot
-    // (rkh, rph: when given, k^ and phi(q) also go there, rows laid out by swzd)
     template <bool WQ, bool WU>
-    __device__ __forceinline__ void stage1(int cq, float *rkh = nullptr, float *rph = nullptr)
+    __device__ __forceinline__ void stage1(int cq)
     {
         if (!pthr) return;
         const int slot = cq & 1;
@@ -455,26 +382,13 @@ struct Head {
             const float nu = sum_row16(pu);
             iu = ok && nu > 0.f ? rsqrtf(nu) : 0.f;
         }
-        if constexpr (LdsT::KEEP_IK) {
-            if (cc == 0) L.ikn[slot][tl] = ik;
-        }
         const int e0 = tl * LD + cc * CPT;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const float kv = rk.get(i) * ik;
-            L.kh[slot][e0 + i] = kv;
-            if (rkh) {
-                const int col = cc * CPT + i;
-                rkh[swzd<D>(tl, col >> 2) + (col & 3)] = kv;
-            }
+            L.kh[slot][e0 + i] = rk.get(i) * ik;
             if constexpr (WU) L.uh[slot % LdsT::UB][e0 + i] = ru.get(i) * iu;
             if constexpr (WQ) {
-                const float pq = phi_fast(rq.get(i));
-                L.ph[slot][e0 + i] = pq;
-                if (rph) {
-                    const int col = cc * CPT + i;
-                    rph[swzd<D>(tl, col >> 2) + (col & 3)] = pq;
-                }
+                L.ph[slot][e0 + i] = phi_fast(rq.get(i));
                 zk[e0 + i] = ok ? phi_fast(rk.get(i)) : 0.f;
             }
         }
@@ -499,8 +413,8 @@ struct Head {
         zk_cmp = (tsum - zk_run) - yk;
         zk_run = tsum;
     }
-    // readout denominators of chunk cq (also to rrd when given)
-    __device__ __forceinline__ void stage3(int cq, float *rrd = nullptr)
+    // readout denominators of chunk cq
+    __device__ __forceinline__ void stage3(int cq)
     {
         if (!pthr) return;
         const int slot = cq & 1;
@@ -510,11 +424,7 @@ struct Head {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) pd = fmaf(L.ph[slot][e0 + i], zk[e0 + i], pd);
         pd = sum_row16(pd);
-        const float rd = __builtin_amdgcn_rcpf(fmaxf(pd, eps));
-        if (cc == 0) {
-            L.rden[slot][tl] = rd;
-            if (rrd) rrd[tl] = rd;
-        }
+        if (cc == 0) L.rden[slot][tl] = __builtin_amdgcn_rcpf(fmaxf(pd, eps));
     }
     // V' rows 4g+r of chunk cq (own blocks), kept as loaded
     __device__ __forceinline__ void load_v(int cq, Raw1<Tin> (&vraw)[BPW][4]) const

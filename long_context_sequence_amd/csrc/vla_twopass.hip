@@ -385,12 +385,10 @@ struct PLds {
     static constexpr int C = Cfg<D>::C, NA = Cfg<D>::NA, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
     static constexpr int UB = 1;
     static constexpr int ZKB = 2;
-    static constexpr bool KEEP_IK = false;
     float uh[1][C * LD];     // u^ [token][i] (read before the next chunk is staged)
     float kh[2][C * LD];     // k^, by chunk parity
     float ph[2][C * LD];     // phi(q), by chunk parity
     float zk[2][C * LD];     // phi(k), then the inclusive key sum, by chunk parity
-    float rden[2][C];
     float z0[C * LD];
     float z0t[D * LT];
     float w[C * LD];         // W [token][i]
