@@ -1,4 +1,5 @@
-"""fp64 CPU oracle of the VLA per-head forward recurrence -- TEST INFRASTRUCTURE.
+"""fp64 CPU oracle of the VLA per-head recurrence (forward and its gradients) -- TEST
+INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The HIP library never calls it and the
@@ -13,7 +14,11 @@ Pins (tests/test_oracle_pins.py) tie each part to something other than the
 oracle itself: brute-force inverses of the penalty matrix, the first token
 worked by hand, the d = 1 closed form, the epsilon branch, the delta-rule and
 cumulative-sum special cases, the state-update invariants, continuation and
-head independence.  No function here is left unpinned.
+head independence.  The gradients (``backward_head``) are pinned to central
+finite differences of the forward, entry by entry on tiny heads (with the
+denominator floor active and with zero keys and penalty vectors) and along
+random directions on larger ones, and to the first token's gradient worked by
+hand.  No function here is left unpinned.
 """
 from __future__ import annotations
 
@@ -49,6 +54,9 @@ def _load():
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         f = lib.vla_oracle_forward
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double] + [_dp] * 18
+        f = lib.vla_oracle_backward
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double] + [_dp] * 18
         _lib = lib
@@ -137,3 +145,61 @@ def forward(q, k, v, u, lambda0=0.1, eps=1e-4, S0=None, A0=None, zkey0=None,
         with ThreadPoolExecutor(max_workers=n) as ex:
             list(ex.map(one, range(B * H)))
     return dict(o=o, S=S, A=A, zkey=zk)
+
+
+def backward_head(q, k, v, u, dO, lambda0=0.1, eps=1e-4, S0=None, A0=None, zkey0=None,
+                  dS_T=None, dA_T=None, dzkey_T=None):
+    """Gradients of one head (q, k, v, u, dO are [T, d]; dS_T, dA_T [d, d] and
+    dzkey_T [d] are the adjoints of the final state, None for 0).  Returns a
+    dict with ``dq, dk, dv, du`` [T, d], ``dS0`` [d, d], ``dA0`` [d, d] (the
+    gradient with respect to A_0 as a symmetric matrix) and ``dzkey0`` [d].
+    Memory: 2 T d^2 doubles of per-token states."""
+    q = _f64(q)
+    T, d = q.shape
+    k, v, u, dO = _f64(k, (T, d)), _f64(v, (T, d)), _f64(u, (T, d)), _f64(dO, (T, d))
+    S0, A0, zkey0 = _f64(S0, (d, d)), _f64(A0, (d, d)), _f64(zkey0, (d,))
+    dS_T, dA_T, dzkey_T = _f64(dS_T, (d, d)), _f64(dA_T, (d, d)), _f64(dzkey_T, (d,))
+    out = dict(dq=np.zeros((T, d)), dk=np.zeros((T, d)), dv=np.zeros((T, d)),
+               du=np.zeros((T, d)), dS0=np.zeros((d, d)), dA0=np.zeros((d, d)),
+               dzkey0=np.zeros(d))
+    rc = _load().vla_oracle_backward(
+        T, d, float(lambda0), float(eps), _ptr(q), _ptr(k), _ptr(v), _ptr(u),
+        _ptr(S0), _ptr(A0), _ptr(zkey0), _ptr(dO), _ptr(dS_T), _ptr(dA_T), _ptr(dzkey_T),
+        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["du"]),
+        _ptr(out["dS0"]), _ptr(out["dA0"]), _ptr(out["dzkey0"]))
+    if rc != 0:
+        raise ValueError(f"vla_oracle_backward failed with code {rc}")
+    return out
+
+
+def backward(q, k, v, u, dO, lambda0=0.1, eps=1e-4, S0=None, A0=None, zkey0=None,
+             dS_T=None, dA_T=None, dzkey_T=None, workers=None):
+    """All heads of [B, H, T, d] inputs and output adjoints (independent heads on
+    a thread pool).  Returns ``dq, dk, dv, du`` [B, H, T, d], ``dS0``, ``dA0``
+    [B, H, d, d] and ``dzkey0`` [B, H, d]."""
+    q = np.asarray(q)
+    B, H, T, d = q.shape
+    res = dict(dq=np.zeros((B, H, T, d)), dk=np.zeros((B, H, T, d)),
+               dv=np.zeros((B, H, T, d)), du=np.zeros((B, H, T, d)),
+               dS0=np.zeros((B, H, d, d)), dA0=np.zeros((B, H, d, d)),
+               dzkey0=np.zeros((B, H, d)))
+
+    def pick(x, b, h):
+        return None if x is None else x[b, h]
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        r = backward_head(q[b, h], k[b, h], v[b, h], u[b, h], dO[b, h], lambda0, eps,
+                          pick(S0, b, h), pick(A0, b, h), pick(zkey0, b, h),
+                          pick(dS_T, b, h), pick(dA_T, b, h), pick(dzkey_T, b, h))
+        for key, val in r.items():
+            res[key][b, h] = val
+
+    n = min(workers or default_workers(), B * H)
+    if n <= 1:
+        for bh in range(B * H):
+            one(bh)
+    else:
+        with ThreadPoolExecutor(max_workers=n) as ex:
+            list(ex.map(one, range(B * H)))
+    return res

@@ -164,3 +164,236 @@ int vla_oracle_forward(int T, int d, double lambda0, double eps,
     free(work);
     return VLA_ORACLE_OK;
 }
+
+/* phi'(x): 1 for x > 0, exp(x) otherwise (phi is continuous with slope 1 at 0). */
+static double dphi(double x) { return x > 0.0 ? 1.0 : exp(x); }
+
+/*
+ * Reverse mode of the recurrence above, one head, fp64: the gradients of a
+ * scalar loss L with respect to the inputs and the initial state, given the
+ * adjoints of the outputs.  (The pages state the forward only; the chain rule
+ * through Eqs. (9)-(11) is written out here step by step, each forward step
+ * undone in the opposite order.)
+ *
+ * dO      : [T][d] dL/do_t.
+ * dS_T, dA_T : [d][d] dL/dS_T, dL/dA_T (entrywise), or NULL for 0.
+ * dzk_T   : [d] dL/dzkey_T, or NULL for 0.
+ * dq, dk, dv, du : [T][d] outputs (required when T > 0).
+ * dS0     : [d][d] dL/dS_0, or NULL to skip.
+ * dA0     : [d][d] gradient with respect to A_0 as a symmetric matrix,
+ *           (G + G')/2 of the entrywise gradient G, or NULL to skip.
+ * dzk0    : [d] dL/dzkey_0, or NULL to skip.
+ *
+ * The forward runs first (vla_oracle_forward with its per-token traces), so
+ * every A_t and S_t is at hand.  Then, for t = T..1, with gS = dL/dS_t,
+ * gA = dL/dA_t (entrywise, not symmetrised) and gz = dL/dzkey_t:
+ *   Eq. (11)  o = S_t phi(q) / den,  den = max(phi(q)'zkey_t, eps):
+ *             gS += g phi(q)' / den;  gphi(q) = S_t' g / den, and where
+ *             phi(q)'zkey_t >= eps also gden = -(g'S_t phi(q)) / den^2,
+ *             gphi(q) += gden zkey_t, gz += gden phi(q);  the key sum passes
+ *             gz to phi(k_t) and on to zkey_{t-1} unchanged.
+ *   Eq. (10)  ge = gS alpha^;  galpha^ = gS' e;  gv = ge;
+ *             gk^ = -S_{t-1}' ge;  gS <- gS - ge k^'  (= dL/dS_{t-1} so far);
+ *             alpha^ = y/|y|:  gy = (galpha^ - alpha^ (alpha^'galpha^)) / |y|;
+ *             y = A_t k^:  gA += gy k^';  gk^ += A_t' gy.
+ *   Eq. (9)   A_t = A_{t-1} - z z'/delta:  gz_ = -(gA + gA') z / delta,
+ *             gdelta = z'gA z / delta^2;  delta = 1 + u^'z:  gz_ += gdelta u^,
+ *             gu^ = gdelta z;  z = A_{t-1} u^:  gA += gz_ u^' (now
+ *             dL/dA_{t-1}), gu^ += A_{t-1}' gz_.
+ *   normalisation x^ = x/|x|:  gx = (gx^ - x^ (x^'gx^)) / |x|; for k also
+ *             gphi(k) phi'(k).
+ * Conventions where no derivative exists: a zero vector's normalisation passes
+ * no gradient (its x^ is 0 whatever the direction), and the denominator floor
+ * passes gradient to phi(q)'zkey_t only where that is >= eps (the forward's
+ * own branch).
+ *
+ * Memory: the traces hold 2 T d^2 doubles.  Returns 0, or nonzero on bad
+ * arguments / allocation failure.
+ */
+int vla_oracle_backward(int T, int d, double lambda0, double eps,
+                        const double *q, const double *k, const double *v, const double *u,
+                        const double *S0, const double *A0, const double *zkey0,
+                        const double *dO, const double *dS_T, const double *dA_T,
+                        const double *dzk_T,
+                        double *dq, double *dk, double *dv, double *du,
+                        double *dS0, double *dA0, double *dzk0)
+{
+    if (T < 0 || d < 1 || !(lambda0 > 0.0) || !(eps > 0.0))
+        return VLA_ORACLE_EINVAL;
+    if (T > 0 && (!q || !k || !v || !u || !dO || !dq || !dk || !dv || !du))
+        return VLA_ORACLE_EINVAL;
+
+    const size_t dd = (size_t)d * d, Tn = T > 0 ? (size_t)T : 1;
+    double *trA = (double *)malloc(Tn * dd * sizeof(double));
+    double *trS = (double *)malloc(Tn * dd * sizeof(double));
+    double *tz = (double *)malloc(Tn * d * sizeof(double));
+    double *tal = (double *)malloc(Tn * d * sizeof(double));
+    double *te = (double *)malloc(Tn * d * sizeof(double));
+    double *tdel = (double *)malloc(Tn * sizeof(double));
+    double *tden = (double *)malloc(Tn * sizeof(double));
+    double *o = (double *)malloc(Tn * d * sizeof(double));
+    double *tzk = (double *)malloc(Tn * d * sizeof(double));
+    double *mats = (double *)malloc(5 * dd * sizeof(double));
+    double *vec = (double *)malloc(16 * (size_t)d * sizeof(double));
+    int rc = VLA_ORACLE_ENOMEM;
+    if (!trA || !trS || !tz || !tal || !te || !tdel || !tden || !o || !tzk || !mats || !vec)
+        goto out;
+    {
+        double *Sf = mats, *Af = mats + dd, *Ai = mats + 2 * dd, *Si = mats + 3 * dd;
+        double *gA = mats + 4 * dd;
+        double *zkf = vec, *kh = vec + d, *uh = vec + 2 * d, *pq = vec + 3 * d;
+        double *zk = vec + 4 * d, *g = vec + 5 * d, *c1 = vec + 6 * d, *ge = vec + 7 * d;
+        double *gal = vec + 8 * d, *gkh = vec + 9 * d, *y = vec + 10 * d, *gy = vec + 11 * d;
+        double *gz = vec + 12 * d, *guh = vec + 13 * d, *gzk = vec + 14 * d;
+        double *gS = dS0 ? dS0 : NULL;
+        double *gSbuf = NULL;
+
+        rc = vla_oracle_forward(T, d, lambda0, eps, q, k, v, u, S0, A0, zkey0, o, Sf, Af, zkf,
+                                tdel, tal, te, tz, tden, trA, trS);
+        if (rc != VLA_ORACLE_OK) goto out;
+
+        /* the state before token 1 */
+        if (S0) memcpy(Si, S0, dd * sizeof(double));
+        else memset(Si, 0, dd * sizeof(double));
+        if (A0) {
+            memcpy(Ai, A0, dd * sizeof(double));
+        } else {
+            memset(Ai, 0, dd * sizeof(double));
+            for (int i = 0; i < d; ++i) Ai[(size_t)i * d + i] = 1.0 / lambda0;
+        }
+
+        if (!gS) {
+            gSbuf = (double *)malloc(dd * sizeof(double));
+            if (!gSbuf) { rc = VLA_ORACLE_ENOMEM; goto out; }
+            gS = gSbuf;
+        }
+        if (dS_T) memcpy(gS, dS_T, dd * sizeof(double));
+        else memset(gS, 0, dd * sizeof(double));
+        if (dA_T) memcpy(gA, dA_T, dd * sizeof(double));
+        else memset(gA, 0, dd * sizeof(double));
+        if (dzk_T) memcpy(gzk, dzk_T, (size_t)d * sizeof(double));
+        else memset(gzk, 0, (size_t)d * sizeof(double));
+        /* zkey_t = zkey_0 + sum_{s<=t} phi(k_s), for every t */
+        for (int i = 0; i < d; ++i) zk[i] = zkey0 ? zkey0[i] : 0.0;
+        for (int t = 0; t < T; ++t)
+            for (int i = 0; i < d; ++i) {
+                zk[i] += phi(k[(size_t)t * d + i]);
+                tzk[(size_t)t * d + i] = zk[i];
+            }
+        (void)zkf;
+
+        for (int t = T - 1; t >= 0; --t) {
+            const double *qt = q + (size_t)t * d, *kt = k + (size_t)t * d;
+            const double *ut = u + (size_t)t * d;
+            const double *At = trA + (size_t)t * dd, *St = trS + (size_t)t * dd;
+            const double *Ap = t > 0 ? trA + (size_t)(t - 1) * dd : Ai;
+            const double *Sp = t > 0 ? trS + (size_t)(t - 1) * dd : Si;
+            const double *z = tz + (size_t)t * d, *al = tal + (size_t)t * d;
+            const double *e = te + (size_t)t * d;
+            const double delta = tdel[t];
+            double nk2 = 0.0, nu2 = 0.0;
+            for (int i = 0; i < d; ++i) {
+                nk2 += kt[i] * kt[i];
+                nu2 += ut[i] * ut[i];
+            }
+            normalise(kt, kh, d);
+            normalise(ut, uh, d);
+            for (int i = 0; i < d; ++i) {
+                pq[i] = phi(qt[i]);
+                g[i] = dO[(size_t)t * d + i];
+            }
+            memcpy(zk, tzk + (size_t)t * d, (size_t)d * sizeof(double));   /* zkey_t */
+            const double dn = dot(pq, zk, d);
+            const double den = dn < eps ? eps : dn;
+
+            /* Eq. (11) */
+            for (int i = 0; i < d; ++i)
+                for (int j = 0; j < d; ++j) gS[(size_t)i * d + j] += g[i] * pq[j] / den;
+            for (int j = 0; j < d; ++j) {
+                double s = 0.0;
+                for (int i = 0; i < d; ++i) s += St[(size_t)i * d + j] * g[i];
+                c1[j] = s;
+            }
+            double gden = 0.0;
+            if (dn >= eps) gden = -dot(c1, pq, d) / (den * den);
+            for (int j = 0; j < d; ++j) {
+                const double gpq = c1[j] / den + gden * zk[j];
+                dq[(size_t)t * d + j] = gpq * dphi(qt[j]);
+            }
+            for (int j = 0; j < d; ++j) gzk[j] += gden * pq[j];
+
+            /* Eq. (10) */
+            matvec(gS, al, ge, d);
+            for (int j = 0; j < d; ++j) {
+                double s = 0.0, r = 0.0;
+                for (int i = 0; i < d; ++i) {
+                    s += gS[(size_t)i * d + j] * e[i];
+                    r += Sp[(size_t)i * d + j] * ge[i];
+                }
+                gal[j] = s;
+                gkh[j] = -r;
+            }
+            for (int i = 0; i < d; ++i) {
+                dv[(size_t)t * d + i] = ge[i];
+                for (int j = 0; j < d; ++j) gS[(size_t)i * d + j] -= ge[i] * kh[j];
+            }
+            matvec(At, kh, y, d);
+            const double ny = sqrt(dot(y, y, d));
+            if (ny > 0.0) {
+                const double aa = dot(al, gal, d);
+                for (int i = 0; i < d; ++i) gy[i] = (gal[i] - al[i] * aa) / ny;
+            } else {
+                memset(gy, 0, (size_t)d * sizeof(double));
+            }
+            for (int i = 0; i < d; ++i)
+                for (int j = 0; j < d; ++j) gA[(size_t)i * d + j] += gy[i] * kh[j];
+            for (int j = 0; j < d; ++j) {
+                double s = 0.0;
+                for (int i = 0; i < d; ++i) s += At[(size_t)i * d + j] * gy[i];
+                gkh[j] += s;
+            }
+
+            /* Eq. (9) */
+            double gdelta = 0.0;
+            for (int i = 0; i < d; ++i) {
+                double s = 0.0;
+                for (int j = 0; j < d; ++j)
+                    s += (gA[(size_t)i * d + j] + gA[(size_t)j * d + i]) * z[j];
+                gz[i] = -s / delta;
+                for (int j = 0; j < d; ++j) gdelta += z[i] * gA[(size_t)i * d + j] * z[j];
+            }
+            gdelta /= delta * delta;
+            for (int i = 0; i < d; ++i) {
+                gz[i] += gdelta * uh[i];
+                guh[i] = gdelta * z[i];
+            }
+            for (int i = 0; i < d; ++i)
+                for (int j = 0; j < d; ++j) gA[(size_t)i * d + j] += gz[i] * uh[j];
+            for (int j = 0; j < d; ++j) {
+                double s = 0.0;
+                for (int i = 0; i < d; ++i) s += Ap[(size_t)i * d + j] * gz[i];
+                guh[j] += s;
+            }
+
+            /* normalisation of k and u; phi(k_t) in the key sum */
+            const double kk = dot(kh, gkh, d), uu = dot(uh, guh, d);
+            const double nk = sqrt(nk2), nu = sqrt(nu2);
+            for (int i = 0; i < d; ++i) {
+                const double gkn = nk2 > 0.0 ? (gkh[i] - kh[i] * kk) / nk : 0.0;
+                dk[(size_t)t * d + i] = gkn + gzk[i] * dphi(kt[i]);
+                du[(size_t)t * d + i] = nu2 > 0.0 ? (guh[i] - uh[i] * uu) / nu : 0.0;
+            }
+        }
+        if (dA0)
+            for (int i = 0; i < d; ++i)
+                for (int j = 0; j < d; ++j)
+                    dA0[(size_t)i * d + j] = 0.5 * (gA[(size_t)i * d + j] + gA[(size_t)j * d + i]);
+        if (dzk0) memcpy(dzk0, gzk, (size_t)d * sizeof(double));
+        free(gSbuf);
+        rc = VLA_ORACLE_OK;
+    }
+out:
+    free(trA); free(trS); free(tz); free(tal); free(te); free(tdel); free(tden);
+    free(o); free(tzk); free(mats); free(vec);
+    return rc;
+}
