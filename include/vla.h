@@ -148,6 +148,58 @@ vla_status vla_step(const void *q, const void *k, const void *v, const void *u,
                     float *S, float *A, float *zkey, float *o,
                     void *stream);
 
+/*
+ * vla_backward -- gradients of a scalar loss L through vla_forward, for every
+ * (b, h) head: given the adjoints of the forward's outputs, the gradients with
+ * respect to its inputs and initial state.  The pages define the forward only;
+ * this is the chain rule through Eqs. (9), (10) and (11) in reverse token
+ * order (section 3.3), with two conventions where no derivative exists: a zero
+ * k or u (normalised to zero) passes no gradient through its normalisation, and
+ * the floor of Eq. (11) passes gradient to phi(q)'zkey only where
+ * phi(q)'zkey >= eps.
+ *
+ * q, k, v, u, in_dtype, B, H, T, d_h, lambda0, eps, S0, A0, zkey0
+ *              exactly as given to vla_forward (the forward is recomputed).
+ * dO           dL/do, [B][H][T][d_h] fp32 (required when T > 0).
+ * dS_T, dA_T, dzkey_T
+ *              dL/dS_T, dL/dA_T ([B][H][d][d], entrywise) and dL/dzkey_T
+ *              ([B][H][d]) for the final state, or NULL for zero.
+ * dq, dk, dv, du
+ *              outputs [B][H][T][d_h] fp32 (required when T > 0): dL/dq etc.
+ *              with respect to the input values as real numbers (also for
+ *              bf16 inputs).
+ * dS0, dzkey0  outputs dL/dS0 [B][H][d][d] and dL/dzkey0 [B][H][d], or NULL.
+ * dA0          output [B][H][d][d], or NULL: the gradient with respect to A0 as
+ *              a symmetric matrix, (G + G')/2 of the entrywise gradient G
+ *              (A_0 must be symmetric, so only that part is meaningful).
+ * workspace    device scratch of at least vla_backward_workspace_size bytes,
+ *              256-byte aligned (NULL when that size is 0); it receives the
+ *              forward's per-token vectors.
+ * stream       hipStream_t to launch on.
+ *
+ * Outputs must not overlap inputs.  One workgroup per head recomputes the
+ * forward token by token, keeping per token z = A_{t-1} u^, alpha^, e and five
+ * scalars in the workspace, then runs the reverse recurrence from t = T down
+ * to 1 with the states rebuilt from those vectors.  Errors as for vla_forward.
+ */
+vla_status vla_backward(const void *q, const void *k, const void *v, const void *u,
+                        int in_dtype, int B, int H, int T, int d_h,
+                        float lambda0, float eps,
+                        const float *S0, const float *A0, const float *zkey0,
+                        const float *dO, const float *dS_T, const float *dA_T,
+                        const float *dzkey_T,
+                        float *dq, float *dk, float *dv, float *du,
+                        float *dS0, float *dA0, float *dzkey0,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * vla_backward_workspace_size -- bytes of device workspace vla_backward needs:
+ * (3 d_h + 8) fp32 values per token of each head, rounded up to 256 bytes
+ * (0 when T == 0).  Host-only.  Errors: VLA_ERR_INVALID_ARG (NULL bytes, bad
+ * sizes), VLA_ERR_UNSUPPORTED (d_h).
+ */
+vla_status vla_backward_workspace_size(int B, int H, int T, int d_h, size_t *bytes);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *vla_status_string(int status);
 

@@ -1,14 +1,15 @@
-"""MI355X-native Variational Linear Attention (VLA) forward recurrence.
+"""MI355X-native Variational Linear Attention (VLA) recurrence: forward, decode
+step and gradients.
 
 The compute lives in ``libvla.so`` (hand-written gfx950 HIP kernels behind the
 C ABI in ``include/vla.h``); this package is its thin Python binding.
 """
 from ._binding import (VLA_BF16, VLA_ERR_HIP, VLA_ERR_INVALID_ARG, VLA_ERR_UNSUPPORTED,
-                       VLA_F32, VLA_OK, LIB_PATH, VLAError, load, vla_forward,
-                       vla_forward_memory, vla_forward_penalty, vla_status_string, vla_step,
-                       workspace_size)
+                       VLA_F32, VLA_OK, LIB_PATH, VLAError, backward_workspace_size, load,
+                       vla_backward, vla_forward, vla_forward_memory, vla_forward_penalty,
+                       vla_status_string, vla_step, workspace_size)
 
 __all__ = ["vla_forward", "vla_forward_penalty", "vla_forward_memory", "vla_step",
-           "workspace_size", "vla_status_string", "VLAError", "load", "LIB_PATH",
+           "vla_backward", "workspace_size", "backward_workspace_size", "vla_status_string", "VLAError", "load", "LIB_PATH",
            "VLA_OK", "VLA_ERR_INVALID_ARG", "VLA_ERR_UNSUPPORTED", "VLA_ERR_HIP",
            "VLA_F32", "VLA_BF16"]

@@ -53,6 +53,14 @@ def load() -> ctypes.CDLL:
         lib.vla_step.restype = ctypes.c_int
         lib.vla_step.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_float, _vp, _vp, _vp, _vp, _vp]
+        lib.vla_backward.restype = ctypes.c_int
+        lib.vla_backward.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.vla_backward_workspace_size.restype = ctypes.c_int
+        lib.vla_backward_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                    ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
         lib.vla_status_string.restype = ctypes.c_char_p
         lib.vla_status_string.argtypes = [ctypes.c_int]
         _lib = lib
@@ -237,3 +245,58 @@ def vla_step(q, k, v, u, S, A, zkey, eps: float = 1e-4, *, o=None, stream=None):
 
 def vla_status_string(status: int) -> str:
     return status_string(status)
+
+
+def backward_workspace_size(B: int, H: int, T: int, d_h: int) -> int:
+    """Bytes of device workspace vla_backward needs for these sizes."""
+    n = ctypes.c_size_t(0)
+    st = load().vla_backward_workspace_size(int(B), int(H), int(T), int(d_h), ctypes.byref(n))
+    if st != VLA_OK:
+        raise VLAError(st, "vla_backward_workspace_size")
+    return n.value
+
+
+def vla_backward(q, k, v, u, dO, lambda0: float = 0.1, eps: float = 1e-4, *,
+                 S0=None, A0=None, zkey0=None, dS_T=None, dA_T=None, dzkey_T=None,
+                 want_state_grads: bool = True, workspace=None, stream=None):
+    """Gradients through vla_forward for [B, H, T, d_h] device inputs.
+
+    ``dO`` ([B, H, T, d_h] float32) is dL/do; ``dS_T, dA_T, dzkey_T`` are the
+    adjoints of the final state (None for zero).  Returns ``(dq, dk, dv, du,
+    dS0, dA0, dzkey0)`` (float32; the last three None unless
+    ``want_state_grads``); ``dA0`` is the gradient with respect to A0 as a
+    symmetric matrix.  Launches on ``stream`` without synchronising.
+    """
+    torch = _torch()
+    B, H, T, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("u", u)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    f32 = torch.float32
+    _check(dO, "dO", (B, H, T, d), f32, dev)
+    for name, t, shp in (("S0", S0, (B, H, d, d)), ("A0", A0, (B, H, d, d)),
+                         ("zkey0", zkey0, (B, H, d)), ("dS_T", dS_T, (B, H, d, d)),
+                         ("dA_T", dA_T, (B, H, d, d)), ("dzkey_T", dzkey_T, (B, H, d))):
+        _check(t, name, shp, f32, dev)
+    dq, dk, dv, du = (torch.empty((B, H, T, d), dtype=f32, device=dev) for _ in range(4))
+    dS0 = dA0 = dzk0 = None
+    if want_state_grads:
+        dS0 = torch.empty((B, H, d, d), dtype=f32, device=dev)
+        dA0 = torch.empty((B, H, d, d), dtype=f32, device=dev)
+        dzk0 = torch.empty((B, H, d), dtype=f32, device=dev)
+    need = backward_workspace_size(B, H, T, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    elif need and (not workspace.is_cuda or workspace.device != dev
+                   or not workspace.is_contiguous()
+                   or workspace.numel() * workspace.element_size() < need):
+        raise ValueError(f"workspace: need a contiguous device tensor of {need} bytes")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().vla_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _dtype_code(q), B, H, T, d,
+                             float(lambda0), float(eps), _ptr(S0), _ptr(A0), _ptr(zkey0),
+                             _ptr(dO), _ptr(dS_T), _ptr(dA_T), _ptr(dzkey_T), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(du), _ptr(dS0), _ptr(dA0), _ptr(dzk0),
+                             _ptr(workspace), ws_bytes, _stream(stream))
+    if st != VLA_OK:
+        raise VLAError(st, "vla_backward")
+    return dq, dk, dv, du, dS0, dA0, dzk0

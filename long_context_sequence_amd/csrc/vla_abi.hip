@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/vla.h"
+#include "vla_bwd.h"
 #include "vla_common.h"
 
 namespace {
@@ -147,6 +148,47 @@ extern "C" vla_status vla_step(const void *q, const void *k, const void *v, cons
     vla::FwdArgs a{q, k, v, u, in_dtype, B, H, 1, d_h, 1.0f, eps,
                    o, S, A, zkey, S, A, zkey, (hipStream_t)stream, nullptr, 0};
     return launch(a, true);
+}
+
+extern "C" vla_status vla_backward_workspace_size(int B, int H, int T, int d_h, size_t *bytes)
+{
+    if (!bytes || B < 1 || H < 1 || T < 0 || (long long)B * H > 0x7fffffffLL) return VLA_ERR_INVALID_ARG;
+    if (!supported_d(d_h)) return VLA_ERR_UNSUPPORTED;
+    *bytes = vla::backward_workspace_bytes(B * H, T, d_h);
+    return VLA_OK;
+}
+
+extern "C" vla_status vla_backward(const void *q, const void *k, const void *v, const void *u,
+                                   int in_dtype, int B, int H, int T, int d_h,
+                                   float lambda0, float eps,
+                                   const float *S0, const float *A0, const float *zkey0,
+                                   const float *dO, const float *dS_T, const float *dA_T,
+                                   const float *dzkey_T,
+                                   float *dq, float *dk, float *dv, float *du,
+                                   float *dS0, float *dA0, float *dzkey0,
+                                   void *workspace, size_t workspace_bytes, void *stream)
+{
+    vla_status st = check_common(in_dtype, B, H, d_h, eps);
+    if (st != VLA_OK) return st;
+    if (T < 0 || !finite_pos(lambda0)) return VLA_ERR_INVALID_ARG;
+    const size_t need = vla::backward_workspace_bytes(B * H, T, d_h);
+    if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need))
+        return VLA_ERR_INVALID_ARG;
+    const bool need_tok = T > 0;
+    if (!ok_ptr(q, need_tok) || !ok_ptr(k, need_tok) || !ok_ptr(v, need_tok) ||
+        !ok_ptr(u, need_tok) || !ok_ptr(dO, need_tok) || !ok_ptr(dq, need_tok) ||
+        !ok_ptr(dk, need_tok) || !ok_ptr(dv, need_tok) || !ok_ptr(du, need_tok))
+        return VLA_ERR_INVALID_ARG;
+    if (!ok_ptr(S0, false) || !ok_ptr(A0, false) || !ok_ptr(zkey0, false) ||
+        !ok_ptr(dS_T, false) || !ok_ptr(dA_T, false) || !ok_ptr(dzkey_T, false) ||
+        !ok_ptr(dS0, false) || !ok_ptr(dA0, false) || !ok_ptr(dzkey0, false))
+        return VLA_ERR_INVALID_ARG;
+    if (T == 0 && !dS0 && !dA0 && !dzkey0) return VLA_OK;   // nothing to do
+
+    vla::BwdArgs a{q, k, v, u, in_dtype, B, H, T, d_h, lambda0, eps, S0, A0, zkey0,
+                   dO, dS_T, dA_T, dzkey_T, dq, dk, dv, du, dS0, dA0, dzkey0,
+                   workspace, (hipStream_t)stream};
+    return vla::launch_backward(a) == hipSuccess ? VLA_OK : VLA_ERR_HIP;
 }
 
 extern "C" const char *vla_status_string(int status)

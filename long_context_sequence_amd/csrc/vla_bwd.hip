@@ -1,0 +1,525 @@
+// vla_bwd.hip -- reverse mode of the VLA recurrence: gradients of a loss with
+// respect to q, k, v, u and the initial state, given the adjoints of o and of the
+// final state, for d_h in {16, 32, 64, 96, 128}.
+//
+// Source: "Variational Linear Attention" (arXiv 2605.11196), section 3.3,
+// Eqs. (9)-(11) (the forward); the pages train the layer end to end but print
+// no backward, so this is the chain rule through those equations, step by step
+// in reverse order, with the conventions stated at vla_backward in
+// include/vla.h.
+//
+// One workgroup per head, D * TPR threads: thread (row i, columns [c0, c0+EPT))
+// holds that slice of row i of every d x d matrix, so a matrix-vector product is
+// a sum over TPR adjacent lanes (DPP), and rank-1 updates are local.
+//
+// Phase 1 runs the forward one token at a time (states S, A in registers) and
+// keeps, per token, z = A_{t-1} u^, alpha^, e and the scalars delta, 1/|y|,
+// phi(q)'zkey, 1/|k|, 1/|u| in the workspace.  One barrier per token: the token
+// vectors rotate through three LDS slots (staged by the last wave one token
+// ahead, raw loads two tokens ahead) and the row products through two.
+//
+// Phase 2 walks back from t = T-1 with the adjoints dS (held twice, as rows of
+// dS and of dS'), Sigma = dA + dA' (dA only ever acts through its symmetric
+// part) and S' (rows of S', so that the products S'g and S'ge are row sums).
+// Sigma is stored in fp64 (its rank-2 update terms and products stay fp32, each
+// term rounded symmetrically): its entries stay large while the sensitivities
+// they carry down the chain shrink (dL/dA_0 falls roughly as 1/T^2), so fp32
+// storage would round away most of dA0 and du at T in the thousands;
+// S_{t-1} = S_t - e alpha^' and A_{t-1} = A_t + z z' / delta are rebuilt from the
+// stored vectors, the same rank-1 terms the forward added.  Per token:
+//   A  dS += g phi(q)'/den;  ge = dS alpha^, galpha = dS'e, c1 = S_t'g    | barrier
+//   B  gy = (galpha - alpha^ (alpha^'galpha)) / |y|;  dS -= ge k^';
+//      c2 = S_t'ge;  Sigma += gy k^' + k^ gy';  A_t gy;  Sigma z             | barrier
+//   C  gdelta = z'Sigma z / (2 delta^2), gz = -Sigma z / delta + gdelta u^;
+//      A <- A_{t-1}, A_{t-1} gz;  Sigma += gz u^' + u^ gz';  S' <- S_{t-1}'  | barrier
+//   D  (wave 0, overlapping the next token) the token's dq, dk, dv, du from
+//      those vectors, the key-sum adjoint and the normalisation Jacobians.
+// The LDS slots of token vectors and row products alternate by token parity, so
+// wave 0's step D of token t never races the other waves' token t - 1.
+#include "vla_bwd.h"
+#include "vla_chunk_parts.h"
+
+namespace vla {
+namespace {
+
+using namespace chunk;
+
+template <int D> struct BwdCfg;
+template <> struct BwdCfg<16> { static constexpr int TPR = 4, EPT = 4; };
+template <> struct BwdCfg<32> { static constexpr int TPR = 8, EPT = 4; };
+template <> struct BwdCfg<64> { static constexpr int TPR = 16, EPT = 4; };
+template <> struct BwdCfg<96> { static constexpr int TPR = 8, EPT = 12; };
+template <> struct BwdCfg<128> { static constexpr int TPR = 8, EPT = 16; };
+
+// sum over a row's TPR adjacent lanes, the same value in each of them
+template <int TPR>
+__device__ __forceinline__ float row_sum(float x)
+{
+    x += dpp<0xB1>(x);                       // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);                       // quad_perm [2,3,0,1]
+    if constexpr (TPR >= 8) x += dpp<0x141>(x);    // row_half_mirror
+    if constexpr (TPR >= 16) x += dpp<0x140>(x);   // row_mirror
+    return x;
+}
+
+// sum over the wave's 64 lanes, the same value in every lane
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+__device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __expf(x); }
+
+// x y + z w with both products rounded before the sum (no fused multiply-add):
+// the same bits for (x, y, z, w) and (z, w, x, y), so that the two mirror
+// entries of a symmetric rank-2 update receive identical terms.  (Rounded
+// differently, Sigma gains an antisymmetric part that the reverse chain does
+// not shrink, and it swamps the small gradients Sigma carries.)
+__device__ __forceinline__ float sym_sum(float x, float y, float z, float w)
+{
+#pragma clang fp contract(off)
+    return x * y + z * w;
+}
+
+template <int D>
+struct BwdLds {
+    // phase 1: token vectors (three slots) and row products z, w (two slots)
+    float fk[3][D], fu[3][D], fq[3][D], fv[3][D], fpk[3][D];
+    float fsc[3][4];
+    float zw[2][2][D];
+    // phase 2: token vectors and scalars (two slots) ...
+    float g[2][D], pq[2][D], kh[2][D], uh[2][D], z[2][D], al[2][D], e[2][D];
+    float dpq[2][D], pk[2][D], dpk[2][D];
+    float sc[2][8];
+    // ... and the row results of steps A, B, C (two slots)
+    float r1[2][3][D], r2[2][3][D], r3[2][D];
+    // S -> S' between the phases
+    float tr[D * (D + 1)];
+};
+
+template <int D, typename Tin>
+__global__ void __launch_bounds__(D * BwdCfg<D>::TPR)
+vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
+        const Tin *__restrict__ u, int T, float lambda0, float eps,
+        const float *S0, const float *A0, const float *zk0, const float *__restrict__ dO,
+        const float *dS_T, const float *dA_T, const float *dzk_T, float *__restrict__ dq,
+        float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ du, float *dS0,
+        float *dA0, float *dzk0, float *__restrict__ rec)
+{
+    using Cf = BwdCfg<D>;
+    constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NT = D * TPR, NW = NT / 64;
+    constexpr int NV = (D + 63) / 64, RS = 3 * D + 8, P = D + 1;
+    static_assert(EPT % 4 == 0 && NT % 64 == 0 && NT <= 1024, "row slices of whole granules");
+    __shared__ __align__(16) BwdLds<D> L;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row = tid / TPR, c0 = (tid % TPR) * EPT;
+    const bool leader = tid % TPR == 0;
+    const int bh = blockIdx.x;
+    const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
+    float *rh = rec + tok0 * RS;   // this head's per-token records
+
+    // ------------------------------------------------------------ phase 1
+    float S[EPT], A[EPT];
+    {
+        const size_t off = bh * DD + (size_t)row * D + c0;
+        sfor<EPT / 4>([&](auto h) {
+            const f4 x = S0 ? ld4(S0 + off + 4 * h) : f4{0.f, 0.f, 0.f, 0.f};
+            f4 y;
+            if (A0) {
+                y = ld4(A0 + off + 4 * h);
+            } else {
+                sfor<4>([&](auto r) { y[int(r)] = row == c0 + 4 * h + r ? 1.f / lambda0 : 0.f; });
+            }
+            sfor<4>([&](auto r) {
+                S[4 * h + r] = x[int(r)];
+                A[4 * h + r] = y[int(r)];
+            });
+        });
+    }
+    float zk[NV];   // wave 0: zkey, entries lane + 64 c
+    sfor<NV>([&](auto c) {
+        const int j = lane + 64 * c;
+        zk[c] = zk0 && j < D ? zk0[(size_t)bh * D + j] : 0.f;
+    });
+
+    // the last wave stages token vectors: raw values in registers two tokens
+    // ahead, normalised into LDS one token ahead
+    float xq[NV], xk[NV], xu[NV], xv[NV];
+    auto p1_load = [&](int t) {
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                const size_t o = (tok0 + t) * D + j;
+                xq[c] = load_in(q, o);
+                xk[c] = load_in(k, o);
+                xu[c] = load_in(u, o);
+                xv[c] = load_in(v, o);
+            }
+        });
+    };
+    auto p1_stage = [&](int slot) {
+        float nk = 0.f, nu = 0.f;
+        sfor<NV>([&](auto c) {
+            if (lane + 64 * c < D) {
+                nk = fmaf(xk[c], xk[c], nk);
+                nu = fmaf(xu[c], xu[c], nu);
+            }
+        });
+        nk = wave_sum(nk);
+        nu = wave_sum(nu);
+        const float ik = nk > 0.f ? rsqrtf(nk) : 0.f, iu = nu > 0.f ? rsqrtf(nu) : 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                L.fk[slot][j] = xk[c] * ik;
+                L.fu[slot][j] = xu[c] * iu;
+                L.fq[slot][j] = phi_fast(xq[c]);
+                L.fv[slot][j] = xv[c];
+                L.fpk[slot][j] = phi_fast(xk[c]);
+            }
+        });
+        if (lane == 0) {
+            L.fsc[slot][0] = ik;
+            L.fsc[slot][1] = iu;
+        }
+    };
+    if (w == NW - 1 && T > 0) {
+        p1_load(0);
+        p1_stage(0);
+        if (T > 1) p1_load(1);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < T; ++t) {
+        const int s3 = t % 3, s2 = t & 1;
+        float *rt = rh + (size_t)t * RS;
+        // z = A u^, w = A k^ (old A), r = S k^ (old S)
+        float pz = 0.f, pw = 0.f, pr = 0.f;
+        sfor<EPT>([&](auto e) {
+            const int j = c0 + e;
+            const float uj = L.fu[s3][j], kj = L.fk[s3][j];
+            pz = fmaf(A[e], uj, pz);
+            pw = fmaf(A[e], kj, pw);
+            pr = fmaf(S[e], kj, pr);
+        });
+        pz = row_sum<TPR>(pz);
+        pw = row_sum<TPR>(pw);
+        pr = row_sum<TPR>(pr);
+        const float ei = L.fv[s3][row] - pr;
+        if (leader) {
+            L.zw[s2][0][row] = pz;
+            L.zw[s2][1][row] = pw;
+            rt[row] = pz;
+            rt[2 * D + row] = ei;
+        }
+        if (w == NW - 1 && t + 1 < T) {
+            p1_stage((t + 1) % 3);
+            if (t + 2 < T) p1_load(t + 2);
+        }
+        __syncthreads();
+
+        // delta = 1 + u^'z, z'k^, and y = A_t k^ = w - z (z'k^) / delta
+        float a = 0.f, b = 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                const float zj = L.zw[s2][0][j];
+                a = fmaf(L.fu[s3][j], zj, a);
+                b = fmaf(zj, L.fk[s3][j], b);
+            }
+        });
+        const float delta = 1.f + wave_sum(a), ci = wave_sum(b) / delta, id = 1.f / delta;
+        float yy = 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                const float yj = L.zw[s2][1][j] - L.zw[s2][0][j] * ci;
+                yy = fmaf(yj, yj, yy);
+            }
+        });
+        yy = wave_sum(yy);
+        const float iy = yy > 0.f ? rsqrtf(yy) : 0.f;
+        sfor<EPT>([&](auto e) {
+            const int j = c0 + e;
+            const float zj = L.zw[s2][0][j];
+            A[e] = fmaf(-pz * zj, id, A[e]);                               // Eq. (9)
+            S[e] = fmaf(ei, (L.zw[s2][1][j] - zj * ci) * iy, S[e]);        // Eq. (10)
+        });
+        if (w == 0) {
+            float dn = 0.f;
+            sfor<NV>([&](auto c) {
+                const int j = lane + 64 * c;
+                if (j < D) {
+                    rt[D + j] = (L.zw[s2][1][j] - L.zw[s2][0][j] * ci) * iy;
+                    zk[c] += L.fpk[s3][j];
+                    dn = fmaf(L.fq[s3][j], zk[c], dn);
+                }
+            });
+            dn = wave_sum(dn);
+            if (lane == 0) {
+                const f4 s01 = {delta, iy, dn, L.fsc[s3][0]};
+                st4(rt + 3 * D, s01);
+                st4(rt + 3 * D + 4, f4{L.fsc[s3][1], 0.f, 0.f, 0.f});
+            }
+        }
+    }
+
+    // ------------------------------------------------------------ phase 2
+    __syncthreads();
+    sfor<EPT>([&](auto e) { L.tr[row * P + c0 + e] = S[e]; });
+    __syncthreads();
+    float St[EPT], gS[EPT], gSt[EPT];   // S', dS, dS' (row slices)
+    double Sg[EPT];                     // Sigma (row slice)
+    sfor<EPT>([&](auto e) { St[e] = L.tr[(c0 + e) * P + row]; });
+    {
+        const size_t off = bh * DD + (size_t)row * D + c0;
+        sfor<EPT>([&](auto e) {
+            const size_t tr_off = bh * DD + (size_t)(c0 + e) * D + row;
+            gS[e] = dS_T ? dS_T[off + e] : 0.f;
+            gSt[e] = dS_T ? dS_T[tr_off] : 0.f;
+            Sg[e] = dA_T ? (double)dA_T[off + e] + (double)dA_T[tr_off] : 0.0;
+        });
+    }
+    float gzk[NV];
+    sfor<NV>([&](auto c) {
+        const int j = lane + 64 * c;
+        gzk[c] = dzk_T && j < D ? dzk_T[(size_t)bh * D + j] : 0.f;
+    });
+
+    float yg[NV], yq[NV], yk[NV], yu[NV], yz[NV], ya[NV], ye[NV];
+    f4 ys0, ys1;
+    auto p2_load = [&](int t) {
+        const float *rt = rh + (size_t)t * RS;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                const size_t o = (tok0 + t) * D + j;
+                yg[c] = dO[o];
+                yq[c] = load_in(q, o);
+                yk[c] = load_in(k, o);
+                yu[c] = load_in(u, o);
+                yz[c] = rt[j];
+                ya[c] = rt[D + j];
+                ye[c] = rt[2 * D + j];
+            }
+        });
+        ys0 = ld4(rt + 3 * D);
+        ys1 = ld4(rt + 3 * D + 4);
+    };
+    auto p2_stage = [&](int slot) {
+        const float ik = ys0[3], iu = ys1[0];
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                L.g[slot][j] = yg[c];
+                L.pq[slot][j] = phi_fast(yq[c]);
+                L.dpq[slot][j] = dphi(yq[c]);
+                L.kh[slot][j] = yk[c] * ik;
+                L.uh[slot][j] = yu[c] * iu;
+                L.pk[slot][j] = phi_fast(yk[c]);
+                L.dpk[slot][j] = dphi(yk[c]);
+                L.z[slot][j] = yz[c];
+                L.al[slot][j] = ya[c];
+                L.e[slot][j] = ye[c];
+            }
+        });
+        if (lane == 0) {
+            st4(&L.sc[slot][0], ys0);
+            st4(&L.sc[slot][4], ys1);
+        }
+    };
+    if (w == NW - 1 && T > 0) {
+        p2_load(T - 1);
+        p2_stage((T - 1) & 1);
+        if (T > 1) p2_load(T - 2);
+    }
+    __syncthreads();
+
+    for (int t = T - 1; t >= 0; --t) {
+        const int s = t & 1;
+        const float delta = L.sc[s][0], iy = L.sc[s][1], dn = L.sc[s][2];
+        const float iden = 1.f / fmaxf(dn, eps), id = 1.f / delta;
+
+        // A: the readout's share of dS, then dS alpha^, dS'e, S_t'g
+        float pge = 0.f, pga = 0.f, pc1 = 0.f;
+        {
+            const float gi = L.g[s][row] * iden, pqi = L.pq[s][row] * iden;
+            sfor<EPT>([&](auto e) {
+                const int j = c0 + e;
+                const float gj = L.g[s][j];
+                gS[e] = fmaf(gi, L.pq[s][j], gS[e]);
+                gSt[e] = fmaf(pqi, gj, gSt[e]);
+                pge = fmaf(gS[e], L.al[s][j], pge);
+                pga = fmaf(gSt[e], L.e[s][j], pga);
+                pc1 = fmaf(St[e], gj, pc1);
+            });
+        }
+        const float ge_i = row_sum<TPR>(pge);
+        pga = row_sum<TPR>(pga);
+        pc1 = row_sum<TPR>(pc1);
+        if (leader) {
+            L.r1[s][0][row] = ge_i;
+            L.r1[s][1][row] = pga;
+            L.r1[s][2][row] = pc1;
+        }
+        __syncthreads();
+        if (w == NW - 1 && t > 0) {
+            p2_stage(s ^ 1);
+            if (t > 1) p2_load(t - 2);
+        }
+
+        // B: gy; dS -= ge k^'; S_t'ge; Sigma += gy k^' + k^ gy'; A_t gy; Sigma z
+        float aga = 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) aga = fmaf(L.al[s][j], L.r1[s][1][j], aga);
+        });
+        aga = wave_sum(aga);
+        float pc2 = 0.f, paty = 0.f, psz = 0.f;
+        {
+            const float khi = L.kh[s][row];
+            const float gyi = (L.r1[s][1][row] - L.al[s][row] * aga) * iy;
+            sfor<EPT>([&](auto e) {
+                const int j = c0 + e;
+                const float gej = L.r1[s][0][j], khj = L.kh[s][j];
+                const float gyj = (L.r1[s][1][j] - L.al[s][j] * aga) * iy;
+                gS[e] = fmaf(-ge_i, khj, gS[e]);
+                gSt[e] = fmaf(-khi, gej, gSt[e]);
+                pc2 = fmaf(St[e], gej, pc2);
+                Sg[e] += (double)sym_sum(gyi, khj, khi, gyj);
+                paty = fmaf(A[e], gyj, paty);
+                psz = fmaf((float)Sg[e], L.z[s][j], psz);
+            });
+        }
+        pc2 = row_sum<TPR>(pc2);
+        paty = row_sum<TPR>(paty);
+        psz = row_sum<TPR>(psz);
+        if (leader) {
+            L.r2[s][0][row] = pc2;
+            L.r2[s][1][row] = paty;
+            L.r2[s][2][row] = psz;
+        }
+        __syncthreads();
+
+        // C: gdelta, gz; A_{t-1} and A_{t-1} gz; Sigma += gz u^' + u^ gz'; S_{t-1}'
+        float zsz = 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) zsz = fmaf(L.z[s][j], L.r2[s][2][j], zsz);
+        });
+        const float gdel = 0.5f * wave_sum(zsz) * id * id;
+        float pagz = 0.f;
+        {
+            const float zi = L.z[s][row], uhi = L.uh[s][row], ali = L.al[s][row];
+            const float gzi = fmaf(-L.r2[s][2][row], id, gdel * uhi);
+            sfor<EPT>([&](auto e) {
+                const int j = c0 + e;
+                const float zj = L.z[s][j], uhj = L.uh[s][j];
+                const float gzj = fmaf(-L.r2[s][2][j], id, gdel * uhj);
+                A[e] = fmaf(zi * zj, id, A[e]);
+                pagz = fmaf(A[e], gzj, pagz);
+                Sg[e] += (double)sym_sum(gzi, uhj, uhi, gzj);
+                St[e] = fmaf(-ali, L.e[s][j], St[e]);
+            });
+        }
+        pagz = row_sum<TPR>(pagz);
+        if (leader) L.r3[s][row] = pagz;
+        __syncthreads();
+
+        // D (wave 0): the token's gradients
+        if (w == 0) {
+            float a1 = 0.f, a2 = 0.f;
+            sfor<NV>([&](auto c) {
+                const int j = lane + 64 * c;
+                if (j < D) {
+                    a1 = fmaf(L.r1[s][2][j], L.pq[s][j], a1);   // g'S_t phi(q)
+                    a2 = fmaf(L.e[s][j], L.r1[s][0][j], a2);    // e'ge
+                }
+            });
+            a1 = wave_sum(a1);
+            a2 = wave_sum(a2);
+            const float gden = dn >= eps ? -a1 * iden * iden : 0.f;
+            float gkh[NV], guh[NV], a3 = 0.f, a4 = 0.f;
+            const size_t o = (tok0 + t) * D;
+            sfor<NV>([&](auto c) {
+                const int j = lane + 64 * c;
+                gkh[c] = guh[c] = 0.f;
+                if (j < D) {
+                    const float gpq = fmaf(L.r1[s][2][j], iden, gden * zk[c]);
+                    dq[o + j] = gpq * L.dpq[s][j];
+                    dv[o + j] = L.r1[s][0][j];
+                    gzk[c] = fmaf(gden, L.pq[s][j], gzk[c]);
+                    gkh[c] = fmaf(L.al[s][j], a2, L.r2[s][1][j] - L.r2[s][0][j]);
+                    guh[c] = fmaf(gdel, L.z[s][j], L.r3[s][j]);
+                    a3 = fmaf(L.kh[s][j], gkh[c], a3);
+                    a4 = fmaf(L.uh[s][j], guh[c], a4);
+                }
+            });
+            a3 = wave_sum(a3);
+            a4 = wave_sum(a4);
+            const float ik = L.sc[s][3], iu = L.sc[s][4];
+            sfor<NV>([&](auto c) {
+                const int j = lane + 64 * c;
+                if (j < D) {
+                    dk[o + j] = fmaf(ik, gkh[c] - L.kh[s][j] * a3, gzk[c] * L.dpk[s][j]);
+                    du[o + j] = iu * (guh[c] - L.uh[s][j] * a4);
+                    zk[c] -= L.pk[s][j];   // zkey_{t-1}
+                }
+            });
+        }
+    }
+
+    // gradients of the initial state
+    {
+        const size_t off = bh * DD + (size_t)row * D + c0;
+        sfor<EPT / 4>([&](auto h) {
+            if (dS0) st4(dS0 + off + 4 * h, f4{gS[4 * h], gS[4 * h + 1], gS[4 * h + 2], gS[4 * h + 3]});
+            if (dA0)
+                st4(dA0 + off + 4 * h, f4{(float)(0.5 * Sg[4 * h]), (float)(0.5 * Sg[4 * h + 1]),
+                                          (float)(0.5 * Sg[4 * h + 2]), (float)(0.5 * Sg[4 * h + 3])});
+        });
+    }
+    if (w == 0 && dzk0) {
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) dzk0[(size_t)bh * D + j] = gzk[c];
+        });
+    }
+}
+
+template <int D, typename Tin>
+hipError_t launch(const BwdArgs &a)
+{
+    hipLaunchKernelGGL((vla_bwd<D, Tin>), dim3(a.B * a.H), dim3(D * BwdCfg<D>::TPR), 0, a.stream,
+                       (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, (const Tin *)a.u, a.T,
+                       a.lambda0, a.eps, a.S0, a.A0, a.zk0, a.dO, a.dS_T, a.dA_T, a.dzk_T, a.dq,
+                       a.dk, a.dv, a.du, a.dS0, a.dA0, a.dzk0, (float *)a.ws);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int BH, int T, int d)
+{
+    const size_t b = (size_t)BH * (size_t)(T > 0 ? T : 0) * backward_record_floats(d) * sizeof(float);
+    return (b + 255) & ~(size_t)255;
+}
+
+hipError_t launch_backward(const BwdArgs &a)
+{
+    const bool bf = a.dtype == 1;
+    switch (a.d) {
+    case 16: return bf ? launch<16, uint16_t>(a) : launch<16, float>(a);
+    case 32: return bf ? launch<32, uint16_t>(a) : launch<32, float>(a);
+    case 64: return bf ? launch<64, uint16_t>(a) : launch<64, float>(a);
+    case 96: return bf ? launch<96, uint16_t>(a) : launch<96, float>(a);
+    case 128: return bf ? launch<128, uint16_t>(a) : launch<128, float>(a);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace vla

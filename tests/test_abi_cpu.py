@@ -23,7 +23,8 @@ def _declared_functions():
 def test_header_symbols_exported():
     names = _declared_functions()
     assert {"vla_forward", "vla_forward_penalty", "vla_forward_memory",
-            "vla_forward_workspace_size", "vla_step", "vla_status_string"} <= set(names)
+            "vla_forward_workspace_size", "vla_step", "vla_backward",
+            "vla_backward_workspace_size", "vla_status_string"} <= set(names)
     lib = ctypes.CDLL(vla.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in vla.h but not exported"
@@ -168,3 +169,52 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(1, 1, 4, 16)
     with pytest.raises(ValueError):
         vla.vla_forward(x, x, x, x)
+
+
+def _bwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, dt=0, B=1, H=2, T=8, d=64, lam=0.1, eps=1e-4,
+             S0=None, A0=None, z0=None, dO=FAKE, dS=None, dA=None, dz=None, dq=FAKE, dk=FAKE,
+             dv=FAKE, du=FAKE, gS0=None, gA0=None, gz0=None, ws=FAKE, ws_bytes=1 << 40,
+             stream=None)
+    a.update(kw)
+    return B.load().vla_backward(a["q"], a["k"], a["v"], a["u"], a["dt"], a["B"], a["H"],
+                                 a["T"], a["d"], a["lam"], a["eps"], a["S0"], a["A0"], a["z0"],
+                                 a["dO"], a["dS"], a["dA"], a["dz"], a["dq"], a["dk"], a["dv"],
+                                 a["du"], a["gS0"], a["gA0"], a["gz0"], a["ws"], a["ws_bytes"],
+                                 a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dO=None), B.VLA_ERR_INVALID_ARG),
+    (dict(dq=None), B.VLA_ERR_INVALID_ARG),
+    (dict(du=MIS), B.VLA_ERR_INVALID_ARG),
+    (dict(dS=MIS), B.VLA_ERR_INVALID_ARG),
+    (dict(gA0=MIS), B.VLA_ERR_INVALID_ARG),
+    (dict(T=-1), B.VLA_ERR_INVALID_ARG),
+    (dict(lam=0.0), B.VLA_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), B.VLA_ERR_INVALID_ARG),
+    (dict(d=80), B.VLA_ERR_UNSUPPORTED),
+    (dict(dt=3), B.VLA_ERR_UNSUPPORTED),
+    (dict(ws=None), B.VLA_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 64), B.VLA_ERR_INVALID_ARG),
+    (dict(ws_bytes=4096), B.VLA_ERR_INVALID_ARG),
+])
+def test_backward_argument_errors(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_backward_empty_no_outputs_is_ok():
+    # T = 0 and no initial-state gradients requested: nothing launched.
+    assert _bwd(T=0, q=None, k=None, v=None, u=None, dO=None, dq=None, dk=None, dv=None,
+                du=None, ws=None) == B.VLA_OK
+
+
+def test_backward_workspace_size():
+    # (3 d + 8) floats per token of each head, rounded up to 256 bytes
+    for d in (16, 32, 64, 96, 128):
+        n = vla.backward_workspace_size(2, 3, 100, d)
+        raw = 2 * 3 * 100 * (3 * d + 8) * 4
+        assert raw <= n < raw + 256 and n % 256 == 0
+    assert vla.backward_workspace_size(1, 1, 0, 64) == 0
+    with pytest.raises(vla.VLAError):
+        vla.backward_workspace_size(1, 1, 4, 48)
