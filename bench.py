@@ -38,28 +38,33 @@ KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_twopass.hip",
                   "long_context_sequence_amd/csrc/vla_dpp_blocks.h",
                   "long_context_sequence_amd/csrc/vla_common.h"]
 TRAFFIC_SUMMARY = "profiles/vla_forward_b8h16_d64_t4096_bf16.txt"
+BWD_KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_bwd.hip",
+                      "long_context_sequence_amd/csrc/vla_bwd.h",
+                      "long_context_sequence_amd/csrc/vla_chunk_parts.h",
+                      "long_context_sequence_amd/csrc/vla_common.h"]
+BWD_TRAFFIC_SUMMARY = "profiles/vla_backward_b8h16_d64_t4096_bf16.txt"
 COPY_BYTES = 1 << 30                      # plain copy used to scale the HBM counters
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the forward kernel from the committed rocprofv3
-    counter summary (FETCH_SIZE + WRITE_SIZE scaled by a plain copy of known
-    size), or None if there is none or the kernel source changed since."""
-    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+def measured_traffic(summary=TRAFFIC_SUMMARY, sources=None):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE scaled by a plain copy of known size), or
+    None if there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, summary)
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m_hash = re.search(r"^kernel_source_sha256:\s*([0-9a-f]+)", txt, re.M)
     m_traf = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt, re.M)
-    if not m_hash or not m_traf or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_traf or m_hash.group(1) != kernel_source_hash(sources):
         return None
     return float(m_traf.group(1))
 
@@ -89,6 +94,15 @@ def flops_per_token_head(d: int) -> int:
     return 12 * d * d
 
 
+def backward_flops_per_token_head(d: int) -> int:
+    """Algorithmic work of the reverse mode per token of one head: the forward it
+    must recompute (12 d^2) and the reverse products: dS updates from the
+    readout and from e (2 d^2 each), dS alpha^, dS'e, S_t'g, S_{t-1}'ge, the
+    updates of dA by gy k^' and gz u^', A_t gy, (dA + dA')z counted as two
+    products, and A_{t-1} gz (2 d^2 each): 36 d^2 in all."""
+    return 36 * d * d
+
+
 def tok_heads_total(cfg) -> int:
     return cfg.B * cfg.H * cfg.T
 
@@ -102,6 +116,8 @@ def parse():
                    help="skip the oracle timing (e.g. under a profiler)")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads in the CPU-baseline sample (0 = every head of the workload)")
+    p.add_argument("--backward", action="store_true",
+                   help="time vla_backward (gradients) on the same workload instead")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     return p.parse_args()
@@ -144,6 +160,96 @@ def cpu_baseline(cfg, n_heads_req: int):
     return {"value": n_heads * cfg.T / wall, "unit": UNIT, "cores": used, "kind": "oracle",
             "sample": f"{n_heads} of {cfg.B * cfg.H} heads, T={cfg.T}, d_h={cfg.d}, fp64, "
                       f"wall {wall:.2f} s"}
+
+
+def cpu_baseline_backward(cfg, n_heads: int, dO):
+    """fp64 oracle of the gradients over a bounded sample of whole heads."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import gen
+    import oracle
+
+    cores = oracle.default_workers()
+    heads = [divmod(i, cfg.H) for i in range(n_heads)]
+    args = []
+    for b, h in heads:
+        hi = gen.head_inputs(cfg, b, h)
+        args.append([hi[n].astype(np.float64) for n in "qkvu"] + [dO[b, h].astype(np.float64)])
+    used = min(cores, n_heads)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=used) as ex:
+        list(ex.map(lambda a: oracle.backward_head(*a, cfg.lambda0, cfg.eps), args))
+    wall = time.perf_counter() - t0
+    return {"value": n_heads * cfg.T / wall, "unit": UNIT, "cores": used, "kind": "oracle",
+            "sample": f"{n_heads} of {cfg.B * cfg.H} heads, T={cfg.T}, d_h={cfg.d}, fp64 "
+                      f"reverse mode, wall {wall:.2f} s"}
+
+
+def backward_bench(args):
+    """One step = one vla_backward over the whole batch of the same workload:
+    dL/do given (synthetic), gradients of q, k, v, u and of the initial state
+    written; the forward is recomputed inside."""
+    import numpy as np
+    import torch
+
+    import gen
+    import long_context_sequence_amd as vla
+
+    cfg = gen.config(WORKLOAD)
+    B, H, T, d = cfg.B, cfg.H, cfg.T, cfg.d
+    dev = torch.device("cuda:0")
+    x = gen.make_inputs(cfg)
+    t = {n: torch.from_numpy(x[n]).to(dev).view(torch.bfloat16) for n in "qkvu"}
+    dO_host = np.random.default_rng(WORKLOAD).standard_normal((B, H, T, d)).astype(np.float32)
+    dO = torch.from_numpy(dO_host).to(dev)
+    ws = torch.empty(vla.backward_workspace_size(B, H, T, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        vla.vla_backward(t["q"], t["k"], t["v"], t["u"], dO, cfg.lambda0, cfg.eps,
+                         workspace=ws, stream=stream)
+
+    t_w, n_w = time.perf_counter(), 0
+    while n_w < args.warmup or time.perf_counter() - t_w < SETTLE_S:
+        step()
+        n_w += 1
+        torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s0, e0 in ev:
+        s0.record(stream)
+        step()
+        e0.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s0.elapsed_time(e0) for s0, e0 in ev]
+    kern_ms = float(np.mean(launch_ms))
+    ms_per_step = wall * 1e3 / args.steps
+    tok_heads = B * H * T
+    flop = backward_flops_per_token_head(d) * tok_heads
+    achieved = flop / (kern_ms / 1e3) / 1e12
+    res = {
+        "metric": "VLA backward tokens·heads/sec (gradients of q, k, v, u and the initial "
+                  "state; fp32 state)",
+        "value": tok_heads / (ms_per_step / 1e3), "unit": UNIT, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "warmup_run": n_w,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name + " backward", "B": B, "H": H, "d_h": d, "T": T,
+                   "input_dtype": cfg.dtype, "state_dtype": "f32", "parallelism": "single GPU"},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
+                     "traffic": measured_traffic(BWD_TRAFFIC_SUMMARY, BWD_KERNEL_SOURCES),
+                     "kernel": "vla_bwd", "kernel_ms": kern_ms,
+                     "kernel_ms_median": float(np.median(launch_ms)), "flop_per_launch": flop,
+                     "dtype": "fp32"},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_backward(cfg, args.cpu_heads or 32, dO_host)
+    print(json.dumps(res), flush=True)
 
 
 def decode_bench(vla, torch, steps: int = 256):
@@ -189,6 +295,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.backward:
+        backward_bench(args)
         return
 
     import numpy as np

@@ -8,8 +8,9 @@ from ._binding import (VLA_BF16, VLA_ERR_HIP, VLA_ERR_INVALID_ARG, VLA_ERR_UNSUP
                        VLA_F32, VLA_OK, LIB_PATH, VLAError, backward_workspace_size, load,
                        vla_backward, vla_forward, vla_forward_memory, vla_forward_penalty,
                        vla_status_string, vla_step, workspace_size)
+from .autograd import vla_attention
 
 __all__ = ["vla_forward", "vla_forward_penalty", "vla_forward_memory", "vla_step",
-           "vla_backward", "workspace_size", "backward_workspace_size", "vla_status_string", "VLAError", "load", "LIB_PATH",
+           "vla_backward", "vla_attention", "workspace_size", "backward_workspace_size", "vla_status_string", "VLAError", "load", "LIB_PATH",
            "VLA_OK", "VLA_ERR_INVALID_ARG", "VLA_ERR_UNSUPPORTED", "VLA_ERR_HIP",
            "VLA_F32", "VLA_BF16"]

@@ -62,12 +62,15 @@ __device__ __forceinline__ float row_sum(float x)
     return x;
 }
 
-// sum over the wave's 64 lanes, the same value in every lane
+// sum over the wave's 64 lanes, as a wave-uniform value: row sums (DPP), then
+// row 1 += row 0 and row 3 += row 2 (row_bcast:15), row 3 += row 1
+// (row_bcast:31), and lane 63 read out
 __device__ __forceinline__ float wave_sum(float x)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
+    x = row_sum<16>(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
 __device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __expf(x); }

@@ -201,3 +201,21 @@ def test_backward_bench_workload_sampled_heads():
     for n in NAMES:
         assert np.isfinite(got[n]).all(), n
     _compare(cfg, x, adj, got, [(0, 0), (7, 15)])
+
+
+def test_autograd_wrapper_matches_backward():
+    """vla_attention's autograd gradients are vla_backward's (a loss o . w)."""
+    dev = _dev()
+    vla = _vla()
+    cfg = _cfg(64, "f32", 1, 2, 40)
+    x = gen.make_inputs(cfg)
+    t = {n: torch.from_numpy(x[n]).to(dev).requires_grad_(True) for n in "qkvu"}
+    w = torch.from_numpy(np.random.default_rng(9).standard_normal((1, 2, 40, 64))
+                         .astype(np.float32)).to(dev)
+    o = vla.vla_attention(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps)
+    (o * w).sum().backward()
+    torch.cuda.synchronize()
+    ref = vla.vla_backward(*(t[n].detach() for n in "qkvu"), w, cfg.lambda0, cfg.eps)
+    torch.cuda.synchronize()
+    for n, r in zip("qkvu", ref[:4]):
+        assert torch.equal(t[n].grad, r), n
