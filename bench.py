@@ -36,7 +36,8 @@ WORKLOAD = 3                              # B=8, H=16, d_h=64, T=4096, bf16 inpu
 KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_twopass.hip",
                   "long_context_sequence_amd/csrc/vla_chunk_parts.h",
                   "long_context_sequence_amd/csrc/vla_dpp_blocks.h",
-                  "long_context_sequence_amd/csrc/vla_common.h"]
+                  "long_context_sequence_amd/csrc/vla_common.h",
+                  "long_context_sequence_amd/csrc/vla_record.h"]
 TRAFFIC_SUMMARY = "profiles/vla_forward_b8h16_d64_t4096_bf16.txt"
 BWD_KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_bwd.hip",
                       "long_context_sequence_amd/csrc/vla_bwd.h",
@@ -116,6 +117,8 @@ def parse():
                    help="skip the oracle timing (e.g. under a profiler)")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads in the CPU-baseline sample (0 = every head of the workload)")
+    p.add_argument("--scan", action="store_true",
+                   help="time vla_forward_scan (memory chain as a scan over chunks) instead")
     p.add_argument("--backward", action="store_true",
                    help="time vla_backward (gradients) on the same workload instead")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -252,6 +255,74 @@ def backward_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def scan_bench(args):
+    """One step = one vla_forward_scan over the whole batch of the forward's
+    workload (penalty pass, per-chunk maps, up- and down-sweep of the scan,
+    chunk-local readout), for comparison with vla_forward."""
+    import numpy as np
+    import torch
+
+    import gen
+    import long_context_sequence_amd as vla
+
+    cfg = gen.config(WORKLOAD)
+    B, H, T, d = cfg.B, cfg.H, cfg.T, cfg.d
+    dev = torch.device("cuda:0")
+    x = gen.make_inputs(cfg)
+    t = {n: torch.from_numpy(x[n]).to(dev).view(torch.bfloat16) for n in "qkvu"}
+    o = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(vla.scan_workspace_size(B, H, T, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        vla.vla_forward_scan(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps, o=o,
+                             workspace=ws, stream=stream)
+
+    t_w, n_w = time.perf_counter(), 0
+    while n_w < args.warmup or time.perf_counter() - t_w < SETTLE_S:
+        step()
+        n_w += 1
+        if n_w % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s0, e0 in ev:
+        s0.record(stream)
+        step()
+        e0.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = float(np.mean([s0.elapsed_time(e0) for s0, e0 in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    tok_heads = B * H * T
+    flop = flops_per_token_head(d) * tok_heads
+    nc = (T + 15) // 16
+    n = 2
+    while n < nc:
+        n *= 2
+    combine_flop = B * H * 2 * (n - 1) * 4 * d ** 3
+    achieved = flop / (kern_ms / 1e3) / 1e12
+    res = {
+        "metric": "VLA fwd tokens·heads/sec with the memory chain as a scan over chunks "
+                  "(fp32 state), for comparison with vla_forward",
+        "value": tok_heads / (ms_per_step / 1e3), "unit": UNIT, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "warmup_run": n_w,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name + " scan form", "B": B, "H": H, "d_h": d, "T": T,
+                   "input_dtype": cfg.dtype, "state_dtype": "f32", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
+                     "traffic": None, "kernel": "vla_forward_scan (penalty pass + scan kernels)",
+                     "kernel_ms": kern_ms, "flop_per_launch": flop, "dtype": "fp32",
+                     "scan_combine_flop_per_launch": combine_flop,
+                     "scan_combine_tflops": combine_flop / (kern_ms / 1e3) / 1e12},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def decode_bench(vla, torch, steps: int = 256):
     """Single-token decode (vla_step) on the long-context decode shape: B=2,
     H=32, d_h=128, bf16 inputs, state from a 64-token forward.  Each step reads
@@ -298,6 +369,9 @@ def main():
         return
     if args.backward:
         backward_bench(args)
+        return
+    if args.scan:
+        scan_bench(args)
         return
 
     import numpy as np

@@ -149,6 +149,36 @@ vla_status vla_step(const void *q, const void *k, const void *v, const void *u,
                     void *stream);
 
 /*
+ * vla_forward_scan -- the same forward as vla_forward (d_h = 64, T >= 1), with
+ * the memory chain (Eqs. (10), (11)) computed as a parallel scan over chunks of
+ * 16 tokens instead of a chain: section 3.4, Eq. (12), with the combine
+ * corrected to the right multiplication that Eq. (10) implies
+ * (S -> S F + G; (F1, G1) then (F2, G2) is (F1 F2, G1 F2 + G2)).  The penalty
+ * pass is vla_forward's; each chunk's map (F, G) is formed from its factors,
+ * the maps are scanned (work-efficient up- and down-sweep, d x d x d products
+ * per combine) and every chunk's readout runs from its start state.  Provided
+ * to measure the pages' parallel form against the chained memory pass; it
+ * does O(d^3) work per chunk where the chain does O(d^2) per token.
+ *
+ * Arguments, outputs and errors as for vla_forward; results equal vla_forward's
+ * up to rounding.  d_h other than 64 is VLA_ERR_UNSUPPORTED, T < 1
+ * VLA_ERR_INVALID_ARG.  workspace: at least vla_forward_scan_workspace_size
+ * bytes, 256-byte aligned (vla_forward's workspace plus 2 d^2 floats per chunk
+ * of each head, rounded up to a power of two chunks, plus one map per head).
+ */
+vla_status vla_forward_scan(const void *q, const void *k, const void *v, const void *u,
+                            int in_dtype, int B, int H, int T, int d_h,
+                            float lambda0, float eps,
+                            float *o, float *S_out, float *A_out, float *zkey_out,
+                            const float *S0, const float *A0, const float *zkey0,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* vla_forward_scan_workspace_size -- bytes of workspace vla_forward_scan needs
+ * (0 when T == 0).  Host-only.  Errors: VLA_ERR_INVALID_ARG (NULL bytes, bad
+ * sizes), VLA_ERR_UNSUPPORTED (d_h other than 64). */
+vla_status vla_forward_scan_workspace_size(int B, int H, int T, int d_h, size_t *bytes);
+
+/*
  * vla_backward -- gradients of a scalar loss L through vla_forward, for every
  * (b, h) head: given the adjoints of the forward's outputs, the gradients with
  * respect to its inputs and initial state.  The pages define the forward only;

@@ -6,11 +6,13 @@ C ABI in ``include/vla.h``); this package is its thin Python binding.
 """
 from ._binding import (VLA_BF16, VLA_ERR_HIP, VLA_ERR_INVALID_ARG, VLA_ERR_UNSUPPORTED,
                        VLA_F32, VLA_OK, LIB_PATH, VLAError, backward_workspace_size, load,
-                       vla_backward, vla_forward, vla_forward_memory, vla_forward_penalty,
-                       vla_status_string, vla_step, workspace_size)
+                       scan_workspace_size, vla_backward, vla_forward, vla_forward_memory,
+                       vla_forward_penalty, vla_forward_scan, vla_status_string, vla_step,
+                       workspace_size)
 from .autograd import vla_attention
 
 __all__ = ["vla_forward", "vla_forward_penalty", "vla_forward_memory", "vla_step",
-           "vla_backward", "vla_attention", "workspace_size", "backward_workspace_size", "vla_status_string", "VLAError", "load", "LIB_PATH",
+           "vla_backward", "vla_attention", "vla_forward_scan", "workspace_size",
+           "backward_workspace_size", "scan_workspace_size", "vla_status_string", "VLAError", "load", "LIB_PATH",
            "VLA_OK", "VLA_ERR_INVALID_ARG", "VLA_ERR_UNSUPPORTED", "VLA_ERR_HIP",
            "VLA_F32", "VLA_BF16"]

@@ -53,6 +53,12 @@ def load() -> ctypes.CDLL:
         lib.vla_step.restype = ctypes.c_int
         lib.vla_step.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_int, ctypes.c_float, _vp, _vp, _vp, _vp, _vp]
+        lib.vla_forward_scan.restype = ctypes.c_int
+        lib.vla_forward_scan.argtypes = lib.vla_forward.argtypes
+        lib.vla_forward_scan_workspace_size.restype = ctypes.c_int
+        lib.vla_forward_scan_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                        ctypes.c_int,
+                                                        ctypes.POINTER(ctypes.c_size_t)]
         lib.vla_backward.restype = ctypes.c_int
         lib.vla_backward.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float,
@@ -300,3 +306,46 @@ def vla_backward(q, k, v, u, dO, lambda0: float = 0.1, eps: float = 1e-4, *,
     if st != VLA_OK:
         raise VLAError(st, "vla_backward")
     return dq, dk, dv, du, dS0, dA0, dzk0
+
+
+def scan_workspace_size(B: int, H: int, T: int, d_h: int) -> int:
+    """Bytes of device workspace vla_forward_scan needs for these sizes."""
+    n = ctypes.c_size_t(0)
+    st = load().vla_forward_scan_workspace_size(int(B), int(H), int(T), int(d_h), ctypes.byref(n))
+    if st != VLA_OK:
+        raise VLAError(st, "vla_forward_scan_workspace_size")
+    return n.value
+
+
+def vla_forward_scan(q, k, v, u, lambda0: float = 0.1, eps: float = 1e-4, *, o=None,
+                     S0=None, A0=None, zkey0=None, workspace=None, stream=None):
+    """vla_forward with the memory chain as a scan over chunks (d_h = 64).
+    Returns ``(o, S, A, zkey)`` (float32)."""
+    torch = _torch()
+    B, H, T, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("u", u)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    f32 = torch.float32
+    if o is None:
+        o = torch.empty((B, H, T, d), dtype=f32, device=dev)
+    _check(o, "o", (B, H, T, d), f32, dev)
+    S = torch.empty((B, H, d, d), dtype=f32, device=dev)
+    A = torch.empty((B, H, d, d), dtype=f32, device=dev)
+    zk = torch.empty((B, H, d), dtype=f32, device=dev)
+    for name, t, shp in (("S0", S0, (B, H, d, d)), ("A0", A0, (B, H, d, d)),
+                         ("zkey0", zkey0, (B, H, d))):
+        _check(t, name, shp, f32, dev)
+    need = scan_workspace_size(B, H, T, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif (not workspace.is_cuda or workspace.device != dev or not workspace.is_contiguous()
+          or workspace.numel() * workspace.element_size() < need):
+        raise ValueError(f"workspace: need a contiguous device tensor of {need} bytes")
+    st = load().vla_forward_scan(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _dtype_code(q), B, H, T, d,
+                                 float(lambda0), float(eps), _ptr(o), _ptr(S), _ptr(A), _ptr(zk),
+                                 _ptr(S0), _ptr(A0), _ptr(zkey0), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != VLA_OK:
+        raise VLAError(st, "vla_forward_scan")
+    return o, S, A, zk

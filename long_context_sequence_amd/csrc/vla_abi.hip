@@ -150,6 +150,39 @@ extern "C" vla_status vla_step(const void *q, const void *k, const void *v, cons
     return launch(a, true);
 }
 
+extern "C" vla_status vla_forward_scan_workspace_size(int B, int H, int T, int d_h, size_t *bytes)
+{
+    if (!bytes || B < 1 || H < 1 || T < 0 || (long long)B * H > 0x7fffffffLL) return VLA_ERR_INVALID_ARG;
+    if (d_h != 64) return VLA_ERR_UNSUPPORTED;
+    *bytes = vla::scan_workspace_bytes(B * H, T, d_h);
+    return VLA_OK;
+}
+
+extern "C" vla_status vla_forward_scan(const void *q, const void *k, const void *v, const void *u,
+                                       int in_dtype, int B, int H, int T, int d_h,
+                                       float lambda0, float eps,
+                                       float *o, float *S_out, float *A_out, float *zkey_out,
+                                       const float *S0, const float *A0, const float *zkey0,
+                                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    vla_status st = check_common(in_dtype, B, H, d_h, eps);
+    if (st != VLA_OK) return st;
+    if (d_h != 64) return VLA_ERR_UNSUPPORTED;
+    if (T < 1 || !finite_pos(lambda0)) return VLA_ERR_INVALID_ARG;
+    const size_t need = vla::scan_workspace_bytes(B * H, T, d_h);
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need) return VLA_ERR_INVALID_ARG;
+    if (!ok_ptr(q, true) || !ok_ptr(k, true) || !ok_ptr(v, true) || !ok_ptr(u, true) ||
+        !ok_ptr(o, true))
+        return VLA_ERR_INVALID_ARG;
+    if (!ok_ptr(S_out, false) || !ok_ptr(A_out, false) || !ok_ptr(zkey_out, false) ||
+        !ok_ptr(S0, false) || !ok_ptr(A0, false) || !ok_ptr(zkey0, false))
+        return VLA_ERR_INVALID_ARG;
+    vla::FwdArgs a{q, k, v, u, in_dtype, B, H, T, d_h, lambda0, eps,
+                   o, S_out, A_out, zkey_out, S0, A0, zkey0, (hipStream_t)stream,
+                   workspace, workspace_bytes};
+    return vla::launch_forward_scan(a) == hipSuccess ? VLA_OK : VLA_ERR_HIP;
+}
+
 extern "C" vla_status vla_backward_workspace_size(int B, int H, int T, int d_h, size_t *bytes)
 {
     if (!bytes || B < 1 || H < 1 || T < 0 || (long long)B * H > 0x7fffffffLL) return VLA_ERR_INVALID_ARG;

@@ -43,6 +43,14 @@ hipError_t launch_step(const FwdArgs &a);
 // phases: 1 = penalty pass (Grams, segment inverses, penalty chain and the
 // per-chunk factors in the workspace), 2 = memory pass, 3 = both.
 size_t twopass_workspace_bytes(int BH, int T, int d);
+// byte offset of the per-chunk records (vla_record.h) in that workspace; the
+// record of chunk c of head bh is at index bh * ceil(T / 16) + c
+size_t twopass_records_offset(int BH, int T, int d);
 hipError_t launch_forward_twopass(const FwdArgs &a, int phases);
+// the memory chain as a scan over chunks (d_h = 64, T >= 1): the penalty pass,
+// then per-chunk affine maps of S, a work-efficient scan of them and the
+// chunk-local readout; needs the workspace below.
+size_t scan_workspace_bytes(int BH, int T, int d);
+hipError_t launch_forward_scan(const FwdArgs &a);
 
 }  // namespace vla

@@ -37,31 +37,15 @@
 // All four run on the caller's stream; the workspace holds the records, the
 // Grams and the segment starts (its size is twopass_workspace_bytes).
 #include "vla_chunk_parts.h"
+#include "vla_record.h"
 
 namespace vla {
 namespace {
 
 using namespace chunk;
 
-constexpr int CH = 16;   // tokens per chunk (Cfg<D>::C)
-
-// One chunk's record (floats).  The memory pass copies records into LDS as
-// they are, so the matrices it reads are laid out for that: 16-column ones by
-// swz16, d-column ones by swzd.
-template <int D>
-struct Rec {
-    static constexpr int AH = 0;              // alpha^ [key][token]
-    static constexpr int TT = D * CH;         // (I + N)^-1, transposed
-    static constexpr int PT = TT + CH * CH;   // (Alpha^'Phi) o Up, transposed
-    // even chunks c with a chunk c + 1: the cross factors Alpha^_c' K^_{c+1} and
-    // Alpha^_c' Phi_{c+1}, transposed (unset otherwise)
-    static constexpr int QK = PT + CH * CH;
-    static constexpr int QP = QK + CH * CH;
-    static constexpr int RD = QP + CH * CH;   // 1 / den per token
-    static constexpr int KH = RD + CH;        // k^ [token][key] (0 past T)
-    static constexpr int PH = KH + CH * D;    // phi(q) [token][key]
-    static constexpr int SIZE = PH + CH * D;  // a multiple of 4
-};
+using rec::CH;
+using rec::Rec;
 
 // Value blocks per memory workgroup and the ways each block's key tiles are
 // split over its waves (VBW x KS waves per workgroup).
@@ -962,6 +946,11 @@ hipError_t launch(const FwdArgs &a, int phases)
 size_t twopass_workspace_bytes(int BH, int T, int d)
 {
     return make_plan(BH, T, d).bytes;
+}
+
+size_t twopass_records_offset(int BH, int T, int d)
+{
+    return make_plan(BH, T, d).rec;
 }
 
 hipError_t launch_forward_twopass(const FwdArgs &a, int phases)

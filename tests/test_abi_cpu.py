@@ -218,3 +218,34 @@ def test_backward_workspace_size():
     assert vla.backward_workspace_size(1, 1, 0, 64) == 0
     with pytest.raises(vla.VLAError):
         vla.backward_workspace_size(1, 1, 4, 48)
+
+
+def test_scan_argument_errors():
+    lib = B.load()
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, dt=0, B=1, H=1, T=32, d=64, lam=0.1, eps=1e-4,
+                 o=FAKE, ws=FAKE, ws_bytes=1 << 40)
+        a.update(kw)
+        return lib.vla_forward_scan(a["q"], a["k"], a["v"], a["u"], a["dt"], a["B"], a["H"],
+                                    a["T"], a["d"], a["lam"], a["eps"], a["o"], None, None, None,
+                                    None, None, None, a["ws"], a["ws_bytes"], None)
+    assert call(d=96) == B.VLA_ERR_UNSUPPORTED
+    assert call(d=128) == B.VLA_ERR_UNSUPPORTED
+    assert call(T=0) == B.VLA_ERR_INVALID_ARG
+    assert call(o=None) == B.VLA_ERR_INVALID_ARG
+    assert call(ws=None) == B.VLA_ERR_INVALID_ARG
+    assert call(ws_bytes=1024) == B.VLA_ERR_INVALID_ARG
+    assert call(eps=0.0) == B.VLA_ERR_INVALID_ARG
+    # workspace: the forward's plus (n + 1) maps of 2 d^2 floats per head, n a
+    # power of two >= the chunk count (>= 2)
+    for T in (1, 16, 17, 4096):
+        nc = (T + 15) // 16
+        n = 2
+        while n < nc:
+            n *= 2
+        maps = 2 * 3 * (n + 1) * 2 * 64 * 64 * 4
+        got = vla.scan_workspace_size(2, 3, T, 64)
+        assert vla.workspace_size(2, 3, T, 64) + maps <= got < vla.workspace_size(2, 3, T, 64) + maps + 512
+    with pytest.raises(vla.VLAError):
+        vla.scan_workspace_size(1, 1, 64, 96)

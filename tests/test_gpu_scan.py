@@ -1,0 +1,106 @@
+"""GPU parity of the scan form of the forward (vla_forward_scan: the memory
+chain as a scan of per-chunk affine maps, [VLA] section 3.4 Eq. (12) with the
+corrected combine) against the fp64 oracle, and against vla_forward.
+
+Gate as for the forward: max|x_gpu - x_ref| / max|x_ref| <= 2e-3 for o and the
+final S, A, zkey."""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GATE = 2e-3
+
+
+def _vla():
+    import long_context_sequence_amd as vla
+    return vla
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _to_dev(x, cfg, dev):
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    return t.view(torch.bfloat16) if cfg.dtype == "bf16" else t
+
+
+def _f64(x, cfg):
+    return (gen.bf16_bits_to_f32(x) if cfg.dtype == "bf16" else x).astype(np.float64)
+
+
+def rel(g, r):
+    g = np.asarray(g, dtype=np.float64)
+    return float(np.abs(g - r).max() / max(np.abs(r).max(), 1e-30))
+
+
+def _scan(cfg, x, dev, **kw):
+    t = {n: _to_dev(x[n], cfg, dev) for n in "qkvu"}
+    out = _vla().vla_forward_scan(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps, **kw)
+    torch.cuda.synchronize()
+    return [a.cpu().numpy() for a in out]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 33, 100, 300, 1000])
+def test_scan_every_head(dtype, T):
+    dev = _dev()
+    cfg = gen.config(3 if dtype == "bf16" else 2).with_sizes(B=1, H=2, T=T)
+    print(f"scan {dtype} T={T}", flush=True)
+    x = gen.make_inputs(cfg)
+    out = _scan(cfg, x, dev)
+    ref = oracle.forward(*(_f64(x[n], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+    for name, g in zip(("o", "S", "A", "zkey"), out):
+        e = rel(g, ref[name])
+        print(f"  {name}: {e:.2e}", flush=True)
+        assert e <= GATE, (name, e)
+
+
+def test_scan_given_initial_state():
+    dev = _dev()
+    cfg = gen.config(2).with_sizes(B=1, H=2, T=90)
+    x = gen.make_inputs(cfg)
+    rng = np.random.default_rng(17)
+    d = cfg.d
+    m = rng.standard_normal((1, 2, d, d))
+    S0 = (0.3 * rng.standard_normal((1, 2, d, d))).astype(np.float32)
+    A0 = (m @ m.transpose(0, 1, 3, 2) / d + 0.5 * np.eye(d)).astype(np.float32)
+    z0 = rng.uniform(0.5, 2.0, (1, 2, d)).astype(np.float32)
+    out = _scan(cfg, x, dev, S0=torch.from_numpy(S0).to(dev), A0=torch.from_numpy(A0).to(dev),
+                zkey0=torch.from_numpy(z0).to(dev))
+    for h in range(2):
+        r = oracle.forward_head(*(x[n][0, h].astype(np.float64) for n in "qkvu"), cfg.lambda0,
+                                cfg.eps, S0[0, h].astype(np.float64), A0[0, h].astype(np.float64),
+                                z0[0, h].astype(np.float64))
+        for name, g in zip(("o", "S", "A", "zkey"), out):
+            assert rel(g[0, h], r[name]) <= GATE, (name, h)
+
+
+def test_scan_bench_workload_matches_forward_and_oracle():
+    """B=8, H=16, d=64, T=4096 bf16: every head against vla_forward, sampled heads
+    against the oracle."""
+    dev = _dev()
+    vla = _vla()
+    cfg = gen.config(3)
+    x = gen.make_inputs(cfg)
+    out = _scan(cfg, x, dev)
+    t = {n: _to_dev(x[n], cfg, dev) for n in "qkvu"}
+    fwd = vla.vla_forward(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps, return_state=True)
+    torch.cuda.synchronize()
+    for name, g, f in zip(("o", "S", "A", "zkey"), out, fwd):
+        e = rel(g, f.cpu().numpy().astype(np.float64))
+        print(f"  scan vs forward {name}: {e:.2e}", flush=True)
+        assert e <= GATE, name
+    for (b, h) in [(0, 0), (7, 15)]:
+        r = oracle.forward_head(*(_f64(x[n][b, h], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+        for name, g in zip(("o", "S", "A", "zkey"), out):
+            e = rel(g[b, h], r[name])
+            print(f"  scan vs oracle ({b},{h}) {name}: {e:.2e}", flush=True)
+            assert e <= GATE, (name, b, h)
