@@ -16,7 +16,9 @@
 // keeps, per token, z = A_{t-1} u^, alpha^, e and the scalars delta, 1/|y|,
 // phi(q)'zkey, 1/|k|, 1/|u| in the workspace.  One barrier per token: the token
 // vectors rotate through three LDS slots (staged by the last wave one token
-// ahead, raw loads two tokens ahead) and the row products through two.
+// ahead, raw loads two tokens ahead) and the row products through two.  The
+// per-token barriers are LDS-only (global loads stay in flight across them;
+// global data crosses between the phases only, behind a full barrier).
 //
 // Phase 2 walks back from t = T-1 with the adjoints dS (held twice, as rows of
 // dS and of dS'), Sigma = dA + dA' (dA only ever acts through its symmetric
@@ -44,12 +46,20 @@ namespace {
 
 using namespace chunk;
 
-template <int D> struct BwdCfg;
-template <> struct BwdCfg<16> { static constexpr int TPR = 4, EPT = 4; };
-template <> struct BwdCfg<32> { static constexpr int TPR = 8, EPT = 4; };
-template <> struct BwdCfg<64> { static constexpr int TPR = 16, EPT = 4; };
-template <> struct BwdCfg<96> { static constexpr int TPR = 8, EPT = 12; };
-template <> struct BwdCfg<128> { static constexpr int TPR = 8, EPT = 16; };
+// Threads per row (TPR) and where S' lives, by measurement on the backward of
+// 128 (d = 64), 128 (d = 96) and 64 (d = 128) heads: every wave repeats the
+// token's scalar work (dot products, norms, the step scalars), so fewer, wider
+// threads cost less issue; the register file bounds how wide.  d <= 64: four
+// threads per row, all slices in registers (d = 64: 256 threads, 3.05 us per
+// token against 3.10 with 16 per row); d = 96: eight per row in registers
+// (9.5 us against 10.4 and 12.6 with four); d = 128: four per row with S' in
+// LDS (each thread's row slice, contiguous) so that the other four slices fit
+// in registers (21 us against 25 and 29).
+template <int D> struct BwdCfg {
+    static constexpr int TPR = D == 96 ? 8 : 4, EPT = D / TPR;
+    static constexpr bool ST_LDS = D == 128;
+    static constexpr int TRP = ST_LDS ? D + 4 : D + 1;   // row pitch of tr
+};
 
 // sum over a row's TPR adjacent lanes, the same value in each of them
 template <int TPR>
@@ -98,8 +108,8 @@ struct BwdLds {
     float sc[2][8];
     // ... and the row results of steps A, B, C (two slots)
     float r1[2][3][D], r2[2][3][D], r3[2][D];
-    // S -> S' between the phases
-    float tr[D * (D + 1)];
+    // S -> S' between the phases (and S' itself above d = 64)
+    float tr[D * BwdCfg<D>::TRP];
 };
 
 template <int D, typename Tin>
@@ -113,7 +123,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
 {
     using Cf = BwdCfg<D>;
     constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NT = D * TPR, NW = NT / 64;
-    constexpr int NV = (D + 63) / 64, RS = 3 * D + 8, P = D + 1;
+    constexpr int NV = (D + 63) / 64, RS = 3 * D + 8, P = Cf::TRP;
     static_assert(EPT % 4 == 0 && NT % 64 == 0 && NT <= 1024, "row slices of whole granules");
     __shared__ __align__(16) BwdLds<D> L;
 
@@ -151,16 +161,18 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
 
     // the last wave stages token vectors: raw values in registers two tokens
     // ahead, normalised into LDS one token ahead
-    float xq[NV], xk[NV], xu[NV], xv[NV];
+    // (kept as loaded, bf16 as its bit pattern, so that the loads stay in
+    // flight until the staging a token later)
+    Raw1<Tin> xq[NV], xk[NV], xu[NV], xv[NV];
     auto p1_load = [&](int t) {
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
                 const size_t o = (tok0 + t) * D + j;
-                xq[c] = load_in(q, o);
-                xk[c] = load_in(k, o);
-                xu[c] = load_in(u, o);
-                xv[c] = load_in(v, o);
+                xq[c].load(q, o);
+                xk[c].load(k, o);
+                xu[c].load(u, o);
+                xv[c].load(v, o);
             }
         });
     };
@@ -168,8 +180,8 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         float nk = 0.f, nu = 0.f;
         sfor<NV>([&](auto c) {
             if (lane + 64 * c < D) {
-                nk = fmaf(xk[c], xk[c], nk);
-                nu = fmaf(xu[c], xu[c], nu);
+                nk = fmaf(xk[c].get(), xk[c].get(), nk);
+                nu = fmaf(xu[c].get(), xu[c].get(), nu);
             }
         });
         nk = wave_sum(nk);
@@ -178,11 +190,11 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
-                L.fk[slot][j] = xk[c] * ik;
-                L.fu[slot][j] = xu[c] * iu;
-                L.fq[slot][j] = phi_fast(xq[c]);
-                L.fv[slot][j] = xv[c];
-                L.fpk[slot][j] = phi_fast(xk[c]);
+                L.fk[slot][j] = xk[c].get() * ik;
+                L.fu[slot][j] = xu[c].get() * iu;
+                L.fq[slot][j] = phi_fast(xq[c].get());
+                L.fv[slot][j] = xv[c].get();
+                L.fpk[slot][j] = phi_fast(xk[c].get());
             }
         });
         if (lane == 0) {
@@ -195,6 +207,9 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         p1_stage(0);
         if (T > 1) p1_load(1);
     }
+    // drain what the prologue issued, as a wait the compiler sees: otherwise it
+    // waits for every load in flight at the top of each iteration
+    vmem_drain();
     __syncthreads();
 
     for (int t = 0; t < T; ++t) {
@@ -223,7 +238,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             p1_stage((t + 1) % 3);
             if (t + 2 < T) p1_load(t + 2);
         }
-        __syncthreads();
+        lds_barrier();
 
         // delta = 1 + u^'z, z'k^, and y = A_t k^ = w - z (z'k^) / delta
         float a = 0.f, b = 0.f;
@@ -273,11 +288,25 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
 
     // ------------------------------------------------------------ phase 2
     __syncthreads();
-    sfor<EPT>([&](auto e) { L.tr[row * P + c0 + e] = S[e]; });
+    // S' rows: through LDS into registers, or (above d = 64) kept there
+    if constexpr (Cf::ST_LDS) {
+        sfor<EPT>([&](auto e) { L.tr[(c0 + e) * P + row] = S[e]; });
+    } else {
+        sfor<EPT>([&](auto e) { L.tr[row * P + c0 + e] = S[e]; });
+    }
     __syncthreads();
-    float St[EPT], gS[EPT], gSt[EPT];   // S', dS, dS' (row slices)
+    float St[Cf::ST_LDS ? 1 : EPT], gS[EPT], gSt[EPT];   // S', dS, dS' (row slices)
+    float *st_row = &L.tr[row * P + c0];
+    auto st_get = [&](auto e) -> float {
+        if constexpr (Cf::ST_LDS) return st_row[e];
+        else return St[e];
+    };
+    auto st_set = [&](auto e, float x) {
+        if constexpr (Cf::ST_LDS) st_row[e] = x;
+        else St[e] = x;
+    };
     double Sg[EPT];                     // Sigma (row slice)
-    sfor<EPT>([&](auto e) { St[e] = L.tr[(c0 + e) * P + row]; });
+    if constexpr (!Cf::ST_LDS) sfor<EPT>([&](auto e) { St[e] = L.tr[(c0 + e) * P + row]; });
     {
         const size_t off = bh * DD + (size_t)row * D + c0;
         sfor<EPT>([&](auto e) {
@@ -293,7 +322,8 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         gzk[c] = dzk_T && j < D ? dzk_T[(size_t)bh * D + j] : 0.f;
     });
 
-    float yg[NV], yq[NV], yk[NV], yu[NV], yz[NV], ya[NV], ye[NV];
+    float yg[NV], yz[NV], ya[NV], ye[NV];
+    Raw1<Tin> yq[NV], yk[NV], yu[NV];
     f4 ys0, ys1;
     auto p2_load = [&](int t) {
         const float *rt = rh + (size_t)t * RS;
@@ -302,9 +332,9 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             if (j < D) {
                 const size_t o = (tok0 + t) * D + j;
                 yg[c] = dO[o];
-                yq[c] = load_in(q, o);
-                yk[c] = load_in(k, o);
-                yu[c] = load_in(u, o);
+                yq[c].load(q, o);
+                yk[c].load(k, o);
+                yu[c].load(u, o);
                 yz[c] = rt[j];
                 ya[c] = rt[D + j];
                 ye[c] = rt[2 * D + j];
@@ -318,13 +348,14 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
+                const float qj = yq[c].get(), kj = yk[c].get();
                 L.g[slot][j] = yg[c];
-                L.pq[slot][j] = phi_fast(yq[c]);
-                L.dpq[slot][j] = dphi(yq[c]);
-                L.kh[slot][j] = yk[c] * ik;
-                L.uh[slot][j] = yu[c] * iu;
-                L.pk[slot][j] = phi_fast(yk[c]);
-                L.dpk[slot][j] = dphi(yk[c]);
+                L.pq[slot][j] = phi_fast(qj);
+                L.dpq[slot][j] = dphi(qj);
+                L.kh[slot][j] = kj * ik;
+                L.uh[slot][j] = yu[c].get() * iu;
+                L.pk[slot][j] = phi_fast(kj);
+                L.dpk[slot][j] = dphi(kj);
                 L.z[slot][j] = yz[c];
                 L.al[slot][j] = ya[c];
                 L.e[slot][j] = ye[c];
@@ -340,6 +371,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         p2_stage((T - 1) & 1);
         if (T > 1) p2_load(T - 2);
     }
+    vmem_drain();
     __syncthreads();
 
     for (int t = T - 1; t >= 0; --t) {
@@ -358,7 +390,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
                 gSt[e] = fmaf(pqi, gj, gSt[e]);
                 pge = fmaf(gS[e], L.al[s][j], pge);
                 pga = fmaf(gSt[e], L.e[s][j], pga);
-                pc1 = fmaf(St[e], gj, pc1);
+                pc1 = fmaf(st_get(e), gj, pc1);
             });
         }
         const float ge_i = row_sum<TPR>(pge);
@@ -369,7 +401,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             L.r1[s][1][row] = pga;
             L.r1[s][2][row] = pc1;
         }
-        __syncthreads();
+        lds_barrier();
         if (w == NW - 1 && t > 0) {
             p2_stage(s ^ 1);
             if (t > 1) p2_load(t - 2);
@@ -392,7 +424,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
                 const float gyj = (L.r1[s][1][j] - L.al[s][j] * aga) * iy;
                 gS[e] = fmaf(-ge_i, khj, gS[e]);
                 gSt[e] = fmaf(-khi, gej, gSt[e]);
-                pc2 = fmaf(St[e], gej, pc2);
+                pc2 = fmaf(st_get(e), gej, pc2);
                 Sg[e] += (double)sym_sum(gyi, khj, khi, gyj);
                 paty = fmaf(A[e], gyj, paty);
                 psz = fmaf((float)Sg[e], L.z[s][j], psz);
@@ -406,7 +438,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             L.r2[s][1][row] = paty;
             L.r2[s][2][row] = psz;
         }
-        __syncthreads();
+        lds_barrier();
 
         // C: gdelta, gz; A_{t-1} and A_{t-1} gz; Sigma += gz u^' + u^ gz'; S_{t-1}'
         float zsz = 0.f;
@@ -426,12 +458,12 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
                 A[e] = fmaf(zi * zj, id, A[e]);
                 pagz = fmaf(A[e], gzj, pagz);
                 Sg[e] += (double)sym_sum(gzi, uhj, uhi, gzj);
-                St[e] = fmaf(-ali, L.e[s][j], St[e]);
+                st_set(e, fmaf(-ali, L.e[s][j], st_get(e)));
             });
         }
         pagz = row_sum<TPR>(pagz);
         if (leader) L.r3[s][row] = pagz;
-        __syncthreads();
+        lds_barrier();
 
         // D (wave 0): the token's gradients
         if (w == 0) {
