@@ -296,17 +296,21 @@ __device__ __forceinline__ void sweep_all(double (&m)[EPT], int i, int c0, doubl
 // caller-given A_0 (or zkey_0) the workgroup of segment 1 also copies it to slot
 // 0, which the penalty pass reads instead, so that the final state may overwrite
 // the initial one.
+// threads per matrix row of the inverse (the penalty pass measured 404 us with
+// 8, 408 with 4 and 415 with 16 on the bench workload)
+constexpr int SEG_TPR = 8;
+
 template <int D>
-__global__ void __launch_bounds__(8 * D)
+__global__ void __launch_bounds__(SEG_TPR * D)
 vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
            const double *__restrict__ gram, const double *__restrict__ zks,
            float *__restrict__ aseg, float *__restrict__ zseg)
 {
-    constexpr int EPT = D / 8;
+    constexpr int EPT = D / SEG_TPR;
     __shared__ __align__(16) double rowbuf[2][4 * D + 16];
     const int S1 = S - 1;
     const int bh = blockIdx.x / S1, j = blockIdx.x % S1 + 1;
-    const int tid = threadIdx.x, i = tid >> 3, c0 = (tid & 7) * EPT;
+    const int tid = threadIdx.x, i = tid / SEG_TPR, c0 = (tid % SEG_TPR) * EPT;
     const size_t DD = (size_t)D * D;
 
     double m[EPT];
@@ -925,7 +929,7 @@ hipError_t launch(const FwdArgs &a, int phases)
         if (p.S > 1) {
             hipLaunchKernelGGL((vla_gram<D, Tin>), dim3(BH * (p.S - 1) * p.P), dim3(256), 0, a.stream,
                                k, u, a.T, p.S, p.SC, p.P, gram, zks);
-            hipLaunchKernelGGL((vla_seginv<D>), dim3(BH * (p.S - 1)), dim3(8 * D), 0, a.stream, p.S,
+            hipLaunchKernelGGL((vla_seginv<D>), dim3(BH * (p.S - 1)), dim3(SEG_TPR * D), 0, a.stream, p.S,
                                p.P, a.lambda0, a.A0, a.zk0, gram, zks, aseg, zseg);
         }
         hipLaunchKernelGGL((vla_pen<D, Tin>), dim3(BH * p.S), dim3(64 * Cfg<D>::NA), 0, a.stream, q,

@@ -219,3 +219,22 @@ def test_autograd_wrapper_matches_backward():
     torch.cuda.synchronize()
     for n, r in zip("qkvu", ref[:4]):
         assert torch.equal(t[n].grad, r), n
+
+
+@pytest.mark.parametrize("cid,T,heads", [
+    (4, 2048, [(0, 0), (3, 31)]),     # MQAR-shaped recall workload, d = 96, fp32
+    (5, 2048, [(0, 0), (1, 31)]),     # long-context recipe, d = 128, bf16, scaled inputs
+])
+def test_backward_other_workloads_sampled_heads(cid, T, heads):
+    """The recall and long-context workloads' input recipes and head counts at
+    T = 2048 (the oracle keeps 2 T d^2 doubles per head): every head on the
+    GPU, sampled heads against the oracle."""
+    dev = _dev()
+    cfg = gen.config(cid).with_sizes(T=T, decode=0)
+    _say(f"backward workload {cfg.name} at T={T}")
+    x = gen.make_inputs(cfg)
+    adj = _adjoints(cfg.B, cfg.H, cfg.T, cfg.d, seed=10 + cid)
+    got = _gpu_backward(cfg, x, adj, dev)
+    for n in NAMES:
+        assert np.isfinite(got[n]).all(), n
+    _compare(cfg, x, adj, got, heads)
