@@ -40,6 +40,7 @@
 // wave 0's step D of token t never races the other waves' token t - 1.
 #include "vla_bwd.h"
 #include "vla_chunk_parts.h"
+#include "vla_reduce.h"
 
 namespace vla {
 namespace {
@@ -60,28 +61,6 @@ template <int D> struct BwdCfg {
     static constexpr bool ST_LDS = D == 128;
     static constexpr int TRP = ST_LDS ? D + 4 : D + 1;   // row pitch of tr
 };
-
-// sum over a row's TPR adjacent lanes, the same value in each of them
-template <int TPR>
-__device__ __forceinline__ float row_sum(float x)
-{
-    x += dpp<0xB1>(x);                       // quad_perm [1,0,3,2]
-    x += dpp<0x4E>(x);                       // quad_perm [2,3,0,1]
-    if constexpr (TPR >= 8) x += dpp<0x141>(x);    // row_half_mirror
-    if constexpr (TPR >= 16) x += dpp<0x140>(x);   // row_mirror
-    return x;
-}
-
-// sum over the wave's 64 lanes, as a wave-uniform value: row sums (DPP), then
-// row 1 += row 0 and row 3 += row 2 (row_bcast:15), row 3 += row 1
-// (row_bcast:31), and lane 63 read out
-__device__ __forceinline__ float wave_sum(float x)
-{
-    x = row_sum<16>(x);
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xa, 0xf, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xc, 0xf, false));
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-}
 
 __device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __expf(x); }
 

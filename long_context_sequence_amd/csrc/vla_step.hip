@@ -17,6 +17,7 @@
 // (delta, z'k^, |y|, y'phi(q), the denominator) are formed by every wave the
 // same way from them.  Each thread writes back exactly the elements it read.
 #include "vla_chunk_parts.h"
+#include "vla_reduce.h"
 
 namespace vla {
 namespace {
@@ -30,30 +31,6 @@ struct StepCfg {
     static constexpr int ACTIVE = D * TPR;         // threads holding a row slice
     static_assert(EPT % 4 == 0 && ACTIVE <= 1024, "row slices of whole 16-byte granules");
 };
-
-__device__ __forceinline__ float row_sum16(float x)
-{
-    x += dpp<0xB1>(x);
-    x += dpp<0x4E>(x);
-    x += dpp<0x141>(x);
-    x += dpp<0x140>(x);
-    return x;
-}
-__device__ __forceinline__ float row_sum8(float x)
-{
-    x += dpp<0xB1>(x);
-    x += dpp<0x4E>(x);
-    x += dpp<0x141>(x);
-    return x;
-}
-
-// sum over the wave's 64 lanes, the same value in every lane
-__device__ __forceinline__ float wave_sum(float x)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
 
 template <int D, typename Tin>
 __global__ void __launch_bounds__(1024)
@@ -116,11 +93,7 @@ vla_decode(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__re
         pr = fmaf(s[e], kj, pr);
         pp = fmaf(s[e], fq, pp);
     });
-    if constexpr (TPR == 16) {
-        pz = row_sum16(pz), pw = row_sum16(pw), pr = row_sum16(pr), pp = row_sum16(pp);
-    } else {
-        pz = row_sum8(pz), pw = row_sum8(pw), pr = row_sum8(pr), pp = row_sum8(pp);
-    }
+    pz = row_sum<TPR>(pz), pw = row_sum<TPR>(pw), pr = row_sum<TPR>(pr), pp = row_sum<TPR>(pp);
     if (act && tid % TPR == 0) {
         zs[row] = pz;
         ws[row] = pw;
