@@ -41,6 +41,7 @@ KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_twopass.hip",
 TRAFFIC_SUMMARY = "profiles/vla_forward_b8h16_d64_t4096_bf16.txt"
 BWD_KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_bwd.hip",
                       "long_context_sequence_amd/csrc/vla_bwd.h",
+                      "long_context_sequence_amd/csrc/vla_reduce.h",
                       "long_context_sequence_amd/csrc/vla_chunk_parts.h",
                       "long_context_sequence_amd/csrc/vla_common.h"]
 BWD_TRAFFIC_SUMMARY = "profiles/vla_backward_b8h16_d64_t4096_bf16.txt"

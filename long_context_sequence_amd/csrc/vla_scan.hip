@@ -49,7 +49,7 @@ vla_scan_maps(const Tin *__restrict__ v, int T, int NC, int n, const float *__re
 {
     constexpr int D = SD, RS = Rec<D>::SIZE, P = D + 1;
     __shared__ float tinv[CH][CH + 1];            // T[t][s]
-    __shared__ float al[CH][P];                   // alpha^_s[j]
+    __shared__ __align__(16) float al[CH][D + 4];   // alpha^_s[j] (rows 16-byte aligned)
     __shared__ float kh[CH][P], vv[CH][P];        // k^_t[i], v_t[i]
     __shared__ float xk[D][CH + 1], xv[D][CH + 1];   // (K^ T)[i][s], (V T)[i][s]
     __shared__ float f0[D * P];                   // F_0 (first chunk with S_0)
@@ -90,20 +90,26 @@ vla_scan_maps(const Tin *__restrict__ v, int T, int NC, int n, const float *__re
         xv[i][s] = b;
     }
     __syncthreads();
-    // thread: row i, columns [j0, j0 + 16)
+    // thread: row i, columns [j0, j0 + 16); one pass over the chunk's tokens s
     const int i = tid >> 2, j0 = (tid & 3) * 16;
     float fr[16], gr[16];
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
-        const int j = j0 + jj;
-        float a = i == j ? 1.f : 0.f, b = 0.f;
+        fr[jj] = i == j0 + jj ? 1.f : 0.f;
+        gr[jj] = 0.f;
+    }
 #pragma unroll
-        for (int s = 0; s < CH; ++s) {
-            a = fmaf(-xk[i][s], al[s][j], a);
-            b = fmaf(xv[i][s], al[s][j], b);
+    for (int s = 0; s < CH; ++s) {
+        const float xa = -xk[i][s], xb = xv[i][s];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const f4 av = ld4(&al[s][j0 + 4 * h]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                fr[4 * h + r] = fmaf(xa, av[r], fr[4 * h + r]);
+                gr[4 * h + r] = fmaf(xb, av[r], gr[4 * h + r]);
+            }
         }
-        fr[jj] = a;
-        gr[jj] = b;
     }
     if (c == 0 && S0) {   // G_0 <- S_0 F_0 + G_0
 #pragma unroll
@@ -216,7 +222,8 @@ vla_scan_apply(const Tin *__restrict__ v, int T, int NC, int n, const float *__r
 {
     constexpr int D = SD, RS = Rec<D>::SIZE, P = D + 1;
     __shared__ float sm[D * P];                     // S at the chunk start
-    __shared__ float kh[CH][P], ph[CH][P], vv[CH][P];
+    __shared__ __align__(16) float kt[D][CH], pt[D][CH];   // k^_t[m], phi(q_t)[m] as [m][t]
+    __shared__ float vv[CH][P];
     __shared__ float tinv[CH][CH + 1], pm[CH][CH + 1], rd[CH];
     __shared__ float wv[D][CH + 1], ev[D][CH + 1];   // V - S K^, E
 
@@ -232,8 +239,8 @@ vla_scan_apply(const Tin *__restrict__ v, int T, int NC, int n, const float *__r
     const float *r = recs + ((size_t)bh * NC + c) * RS;
     for (int idx = tid; idx < CH * D; idx += 256) {
         const int s = idx / D, j = idx % D;
-        kh[s][j] = r[Rec<D>::KH + swzd<D>(s, j >> 2) + (j & 3)];
-        ph[s][j] = r[Rec<D>::PH + swzd<D>(s, j >> 2) + (j & 3)];
+        kt[j][s] = r[Rec<D>::KH + swzd<D>(s, j >> 2) + (j & 3)];
+        pt[j][s] = r[Rec<D>::PH + swzd<D>(s, j >> 2) + (j & 3)];
         const int tok = c * CH + s;
         vv[s][j] = tok < T ? load_in(v, ((size_t)bh * T + tok) * D + j) : 0.f;
     }
@@ -245,18 +252,19 @@ vla_scan_apply(const Tin *__restrict__ v, int T, int NC, int n, const float *__r
     }
     __syncthreads();
     const int i = tid >> 2, q0 = (tid & 3) * 4;
-    float sp[4];
+    float sk[4] = {0.f, 0.f, 0.f, 0.f}, sp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int m = 0; m < D; ++m) {   // one S entry against the four tokens' k^, phi(q)
+        const float sv = sm[i * P + m];
+        const f4 kv = ld4(&kt[m][q0]), pv = ld4(&pt[m][q0]);
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const int t = q0 + tt;
-        float a = 0.f, b = 0.f;
-        for (int m = 0; m < D; ++m) {
-            a = fmaf(sm[i * P + m], kh[t][m], a);
-            b = fmaf(sm[i * P + m], ph[t][m], b);
+        for (int tt = 0; tt < 4; ++tt) {
+            sk[tt] = fmaf(sv, kv[tt], sk[tt]);
+            sp[tt] = fmaf(sv, pv[tt], sp[tt]);
         }
-        wv[i][t] = vv[t][i] - a;
-        sp[tt] = b;
     }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) wv[i][q0 + tt] = vv[q0 + tt][i] - sk[tt];
     __syncthreads();
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
