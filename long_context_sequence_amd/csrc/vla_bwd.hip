@@ -29,15 +29,19 @@
 // storage would round away most of dA0 and du at T in the thousands;
 // S_{t-1} = S_t - e alpha^' and A_{t-1} = A_t + z z' / delta are rebuilt from the
 // stored vectors, the same rank-1 terms the forward added.  Per token:
-//   A  dS += g phi(q)'/den;  ge = dS alpha^, galpha = dS'e, c1 = S_t'g    | barrier
+//   A  dS += g phi(q)'/den;  ge = dS alpha^, galpha = dS'e, c1 = S_t'g
 //   B  gy = (galpha - alpha^ (alpha^'galpha)) / |y|;  dS -= ge k^';
-//      c2 = S_t'ge;  Sigma += gy k^' + k^ gy';  A_t gy;  Sigma z             | barrier
+//      c2 = S_t'ge;  Sigma += gy k^' + k^ gy';  A_t gy;  Sigma z
 //   C  gdelta = z'Sigma z / (2 delta^2), gz = -Sigma z / delta + gdelta u^;
-//      A <- A_{t-1}, A_{t-1} gz;  Sigma += gz u^' + u^ gz';  S' <- S_{t-1}'  | barrier
-//   D  (wave 0, overlapping the next token) the token's dq, dk, dv, du from
-//      those vectors, the key-sum adjoint and the normalisation Jacobians.
-// The LDS slots of token vectors and row products alternate by token parity, so
-// wave 0's step D of token t never races the other waves' token t - 1.
+//      A <- A_{t-1}, A_{t-1} gz;  Sigma += gz u^' + u^ gz';  S' <- S_{t-1}'
+//   D  (wave 0) the token's dq, dk, dv, du from those vectors, the key-sum
+//      adjoint and the normalisation Jacobians.
+// C of token t and A of token t - 1 share a barrier interval (A needs dS after
+// B of t and S_{t-1}' after C of t, both local), so a token costs two
+// barriers: ... | B(t) | C(t), A(t-1) | B(t-1) | ...; wave 0's D of token t
+// runs at the start of the next interval.  Token vectors rotate through three
+// LDS slots and row results through two, so D of token t never races the
+// staging of token t - 2 or the row results of token t - 1.
 #include "vla_bwd.h"
 #include "vla_chunk_parts.h"
 #include "vla_reduce.h"
@@ -81,10 +85,10 @@ struct BwdLds {
     float fk[3][D], fu[3][D], fq[3][D], fv[3][D], fpk[3][D];
     float fsc[3][4];
     float zw[2][2][D];
-    // phase 2: token vectors and scalars (two slots) ...
-    float g[2][D], pq[2][D], kh[2][D], uh[2][D], z[2][D], al[2][D], e[2][D];
-    float dpq[2][D], pk[2][D], dpk[2][D];
-    float sc[2][8];
+    // phase 2: token vectors and scalars (three slots) ...
+    float g[3][D], pq[3][D], kh[3][D], uh[3][D], z[3][D], al[3][D], e[3][D];
+    float dpq[3][D], pk[3][D], dpk[3][D];
+    float sc[3][8];
     // ... and the row results of steps A, B, C (two slots)
     float r1[2][3][D], r2[2][3][D], r3[2][D];
     // S -> S' between the phases (and S' itself above d = 64)
@@ -347,68 +351,61 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     };
     if (w == NW - 1 && T > 0) {
         p2_load(T - 1);
-        p2_stage((T - 1) & 1);
+        p2_stage((T - 1) % 3);
         if (T > 1) p2_load(T - 2);
     }
     vmem_drain();
     __syncthreads();
 
-    for (int t = T - 1; t >= 0; --t) {
-        const int s = t & 1;
-        const float delta = L.sc[s][0], iy = L.sc[s][1], dn = L.sc[s][2];
-        const float iden = 1.f / fmaxf(dn, eps), id = 1.f / delta;
-
-        // A: the readout's share of dS, then dS alpha^, dS'e, S_t'g
+    // Token t's vectors sit in LDS slot t % 3, its row results in slot t % 2.
+    // Step A: the readout's share of dS, then dS alpha^, dS'e, S_t'g.
+    auto step_a = [&](int t) {
+        const int v3 = t % 3, s = t & 1;
+        const float iden = 1.f / fmaxf(L.sc[v3][2], eps);
         float pge = 0.f, pga = 0.f, pc1 = 0.f;
-        {
-            const float gi = L.g[s][row] * iden, pqi = L.pq[s][row] * iden;
-            sfor<EPT>([&](auto e) {
-                const int j = c0 + e;
-                const float gj = L.g[s][j];
-                gS[e] = fmaf(gi, L.pq[s][j], gS[e]);
-                gSt[e] = fmaf(pqi, gj, gSt[e]);
-                pge = fmaf(gS[e], L.al[s][j], pge);
-                pga = fmaf(gSt[e], L.e[s][j], pga);
-                pc1 = fmaf(st_get(e), gj, pc1);
-            });
-        }
-        const float ge_i = row_sum<TPR>(pge);
+        const float gi = L.g[v3][row] * iden, pqi = L.pq[v3][row] * iden;
+        sfor<EPT>([&](auto e) {
+            const int j = c0 + e;
+            const float gj = L.g[v3][j];
+            gS[e] = fmaf(gi, L.pq[v3][j], gS[e]);
+            gSt[e] = fmaf(pqi, gj, gSt[e]);
+            pge = fmaf(gS[e], L.al[v3][j], pge);
+            pga = fmaf(gSt[e], L.e[v3][j], pga);
+            pc1 = fmaf(st_get(e), gj, pc1);
+        });
+        pge = row_sum<TPR>(pge);
         pga = row_sum<TPR>(pga);
         pc1 = row_sum<TPR>(pc1);
         if (leader) {
-            L.r1[s][0][row] = ge_i;
+            L.r1[s][0][row] = pge;
             L.r1[s][1][row] = pga;
             L.r1[s][2][row] = pc1;
         }
-        lds_barrier();
-        if (w == NW - 1 && t > 0) {
-            p2_stage(s ^ 1);
-            if (t > 1) p2_load(t - 2);
-        }
-
-        // B: gy; dS -= ge k^'; S_t'ge; Sigma += gy k^' + k^ gy'; A_t gy; Sigma z
+    };
+    // Step B: gy; dS -= ge k^'; S_t'ge; Sigma += gy k^' + k^ gy'; A_t gy; Sigma z.
+    auto step_b = [&](int t) {
+        const int v3 = t % 3, s = t & 1;
+        const float iy = L.sc[v3][1];
         float aga = 0.f;
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
-            if (j < D) aga = fmaf(L.al[s][j], L.r1[s][1][j], aga);
+            if (j < D) aga = fmaf(L.al[v3][j], L.r1[s][1][j], aga);
         });
         aga = wave_sum(aga);
         float pc2 = 0.f, paty = 0.f, psz = 0.f;
-        {
-            const float khi = L.kh[s][row];
-            const float gyi = (L.r1[s][1][row] - L.al[s][row] * aga) * iy;
-            sfor<EPT>([&](auto e) {
-                const int j = c0 + e;
-                const float gej = L.r1[s][0][j], khj = L.kh[s][j];
-                const float gyj = (L.r1[s][1][j] - L.al[s][j] * aga) * iy;
-                gS[e] = fmaf(-ge_i, khj, gS[e]);
-                gSt[e] = fmaf(-khi, gej, gSt[e]);
-                pc2 = fmaf(st_get(e), gej, pc2);
-                Sg[e] += (double)sym_sum(gyi, khj, khi, gyj);
-                paty = fmaf(A[e], gyj, paty);
-                psz = fmaf((float)Sg[e], L.z[s][j], psz);
-            });
-        }
+        const float khi = L.kh[v3][row], ge_i = L.r1[s][0][row];
+        const float gyi = (L.r1[s][1][row] - L.al[v3][row] * aga) * iy;
+        sfor<EPT>([&](auto e) {
+            const int j = c0 + e;
+            const float gej = L.r1[s][0][j], khj = L.kh[v3][j];
+            const float gyj = (L.r1[s][1][j] - L.al[v3][j] * aga) * iy;
+            gS[e] = fmaf(-ge_i, khj, gS[e]);
+            gSt[e] = fmaf(-khi, gej, gSt[e]);
+            pc2 = fmaf(st_get(e), gej, pc2);
+            Sg[e] += (double)sym_sum(gyi, khj, khi, gyj);
+            paty = fmaf(A[e], gyj, paty);
+            psz = fmaf((float)Sg[e], L.z[v3][j], psz);
+        });
         pc2 = row_sum<TPR>(pc2);
         paty = row_sum<TPR>(paty);
         psz = row_sum<TPR>(psz);
@@ -417,75 +414,96 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             L.r2[s][1][row] = paty;
             L.r2[s][2][row] = psz;
         }
-        lds_barrier();
-
-        // C: gdelta, gz; A_{t-1} and A_{t-1} gz; Sigma += gz u^' + u^ gz'; S_{t-1}'
+    };
+    // Step C: gdelta, gz; A_{t-1} and A_{t-1} gz; Sigma += gz u^' + u^ gz';
+    // S_{t-1}'.  Returns gdelta.
+    auto step_c = [&](int t) -> float {
+        const int v3 = t % 3, s = t & 1;
+        const float id = 1.f / L.sc[v3][0];
         float zsz = 0.f;
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
-            if (j < D) zsz = fmaf(L.z[s][j], L.r2[s][2][j], zsz);
+            if (j < D) zsz = fmaf(L.z[v3][j], L.r2[s][2][j], zsz);
         });
         const float gdel = 0.5f * wave_sum(zsz) * id * id;
         float pagz = 0.f;
-        {
-            const float zi = L.z[s][row], uhi = L.uh[s][row], ali = L.al[s][row];
-            const float gzi = fmaf(-L.r2[s][2][row], id, gdel * uhi);
-            sfor<EPT>([&](auto e) {
-                const int j = c0 + e;
-                const float zj = L.z[s][j], uhj = L.uh[s][j];
-                const float gzj = fmaf(-L.r2[s][2][j], id, gdel * uhj);
-                A[e] = fmaf(zi * zj, id, A[e]);
-                pagz = fmaf(A[e], gzj, pagz);
-                Sg[e] += (double)sym_sum(gzi, uhj, uhi, gzj);
-                st_set(e, fmaf(-ali, L.e[s][j], st_get(e)));
-            });
-        }
+        const float zi = L.z[v3][row], uhi = L.uh[v3][row], ali = L.al[v3][row];
+        const float gzi = fmaf(-L.r2[s][2][row], id, gdel * uhi);
+        sfor<EPT>([&](auto e) {
+            const int j = c0 + e;
+            const float zj = L.z[v3][j], uhj = L.uh[v3][j];
+            const float gzj = fmaf(-L.r2[s][2][j], id, gdel * uhj);
+            A[e] = fmaf(zi * zj, id, A[e]);
+            pagz = fmaf(A[e], gzj, pagz);
+            Sg[e] += (double)sym_sum(gzi, uhj, uhi, gzj);
+            st_set(e, fmaf(-ali, L.e[v3][j], st_get(e)));
+        });
         pagz = row_sum<TPR>(pagz);
         if (leader) L.r3[s][row] = pagz;
-        lds_barrier();
+        return gdel;
+    };
+    // Step D (wave 0): the token's gradients from the row results.
+    auto step_d = [&](int t, float gdel) {
+        const int v3 = t % 3, s = t & 1;
+        const float dn = L.sc[v3][2], iden = 1.f / fmaxf(dn, eps);
+        float a1 = 0.f, a2 = 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                a1 = fmaf(L.r1[s][2][j], L.pq[v3][j], a1);   // g'S_t phi(q)
+                a2 = fmaf(L.e[v3][j], L.r1[s][0][j], a2);    // e'ge
+            }
+        });
+        a1 = wave_sum(a1);
+        a2 = wave_sum(a2);
+        const float gden = dn >= eps ? -a1 * iden * iden : 0.f;
+        float gkh[NV], guh[NV], a3 = 0.f, a4 = 0.f;
+        const size_t o = (tok0 + t) * D;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            gkh[c] = guh[c] = 0.f;
+            if (j < D) {
+                const float gpq = fmaf(L.r1[s][2][j], iden, gden * zk[c]);
+                dq[o + j] = gpq * L.dpq[v3][j];
+                dv[o + j] = L.r1[s][0][j];
+                gzk[c] = fmaf(gden, L.pq[v3][j], gzk[c]);
+                gkh[c] = fmaf(L.al[v3][j], a2, L.r2[s][1][j] - L.r2[s][0][j]);
+                guh[c] = fmaf(gdel, L.z[v3][j], L.r3[s][j]);
+                a3 = fmaf(L.kh[v3][j], gkh[c], a3);
+                a4 = fmaf(L.uh[v3][j], guh[c], a4);
+            }
+        });
+        a3 = wave_sum(a3);
+        a4 = wave_sum(a4);
+        const float ik = L.sc[v3][3], iu = L.sc[v3][4];
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                dk[o + j] = fmaf(ik, gkh[c] - L.kh[v3][j] * a3, gzk[c] * L.dpk[v3][j]);
+                du[o + j] = iu * (guh[c] - L.uh[v3][j] * a4);
+                zk[c] -= L.pk[v3][j];   // zkey_{t-1}
+            }
+        });
+    };
 
-        // D (wave 0): the token's gradients
-        if (w == 0) {
-            float a1 = 0.f, a2 = 0.f;
-            sfor<NV>([&](auto c) {
-                const int j = lane + 64 * c;
-                if (j < D) {
-                    a1 = fmaf(L.r1[s][2][j], L.pq[s][j], a1);   // g'S_t phi(q)
-                    a2 = fmaf(L.e[s][j], L.r1[s][0][j], a2);    // e'ge
-                }
-            });
-            a1 = wave_sum(a1);
-            a2 = wave_sum(a2);
-            const float gden = dn >= eps ? -a1 * iden * iden : 0.f;
-            float gkh[NV], guh[NV], a3 = 0.f, a4 = 0.f;
-            const size_t o = (tok0 + t) * D;
-            sfor<NV>([&](auto c) {
-                const int j = lane + 64 * c;
-                gkh[c] = guh[c] = 0.f;
-                if (j < D) {
-                    const float gpq = fmaf(L.r1[s][2][j], iden, gden * zk[c]);
-                    dq[o + j] = gpq * L.dpq[s][j];
-                    dv[o + j] = L.r1[s][0][j];
-                    gzk[c] = fmaf(gden, L.pq[s][j], gzk[c]);
-                    gkh[c] = fmaf(L.al[s][j], a2, L.r2[s][1][j] - L.r2[s][0][j]);
-                    guh[c] = fmaf(gdel, L.z[s][j], L.r3[s][j]);
-                    a3 = fmaf(L.kh[s][j], gkh[c], a3);
-                    a4 = fmaf(L.uh[s][j], guh[c], a4);
-                }
-            });
-            a3 = wave_sum(a3);
-            a4 = wave_sum(a4);
-            const float ik = L.sc[s][3], iu = L.sc[s][4];
-            sfor<NV>([&](auto c) {
-                const int j = lane + 64 * c;
-                if (j < D) {
-                    dk[o + j] = fmaf(ik, gkh[c] - L.kh[s][j] * a3, gzk[c] * L.dpk[s][j]);
-                    du[o + j] = iu * (guh[c] - L.uh[s][j] * a4);
-                    zk[c] -= L.pk[s][j];   // zkey_{t-1}
-                }
-            });
+    // Two barriers per token: B(t) | C(t) with A(t - 1) |.  Wave 0 forms token
+    // t + 1's gradients at the start of iteration t, while the others begin B(t).
+    if (T > 0) step_a(T - 1);
+    lds_barrier();
+    float gdel_d = 0.f;
+    for (int t = T - 1; t >= 0; --t) {
+        if (w == NW - 1 && t > 0) {   // token t - 1 into slot (t - 1) % 3
+            p2_stage((t - 1) % 3);
+            if (t > 1) p2_load(t - 2);
         }
+        if (w == 0 && t + 1 < T) step_d(t + 1, gdel_d);
+        step_b(t);
+        lds_barrier();
+        gdel_d = step_c(t);
+        if (t > 0) step_a(t - 1);
+        lds_barrier();
     }
+    if (w == 0 && T > 0) step_d(0, gdel_d);
 
     // gradients of the initial state
     {
