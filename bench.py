@@ -15,6 +15,11 @@ do their d x d products on fp32 matrix cores, whose dense peak equals the FP32
 vector peak), the same for each of its two passes (penalty: Grams, segment
 inverses and the penalty chain; memory: the memory chain and readout), and the
 fp64 CPU oracle timed on the host cores over a bounded sample of heads.
+
+``--backward`` prints the same kind of line for ``vla_backward`` (gradients of
+q, k, v, u and the initial state for a synthetic dL/do) on the same workload,
+``--scan`` for ``vla_forward_scan`` (the memory chain as a scan over chunks, a
+comparison); neither is part of the default run.
 """
 import argparse
 import hashlib

@@ -14,6 +14,12 @@
  *   zkey <- zkey + phi(k_t),  phi = ELU + 1 applied to the raw key,
  *   o_t = S phi(q_t) / max(phi(q_t)' zkey, eps)  (new S)                   Eq. (11)
  *
+ * Entry points: vla_forward (T tokens; vla_forward_penalty and
+ * vla_forward_memory are its two passes), vla_step (one decode token, state in
+ * place), vla_backward (the gradients through vla_forward), vla_forward_scan
+ * (vla_forward with the memory chain as a scan over chunks, for comparison),
+ * the workspace-size queries and vla_status_string.
+ *
  * Data layout (all row-major, contiguous, no strides):
  *   q, k, v, u : [B][H][T][d_h] of the input type (fp32 or bf16), on the device
  *   o          : [B][H][T][d_h] fp32
