@@ -213,10 +213,13 @@ vla_status vla_forward_scan_workspace_size(int B, int H, int T, int d_h, size_t 
  *              forward's per-token vectors.
  * stream       hipStream_t to launch on.
  *
- * Outputs must not overlap inputs.  One workgroup per head recomputes the
- * forward token by token, keeping per token z = A_{t-1} u^, alpha^, e and five
- * scalars in the workspace, then runs the reverse recurrence from t = T down
- * to 1 with the states rebuilt from those vectors.  Errors as for vla_forward.
+ * Outputs must not overlap inputs.  The forward is recomputed first, keeping
+ * per token z = A_{t-1} u^, alpha^, e, zkey_t and five scalars in the workspace: for
+ * d_h in {64, 96, 128} by the chunked two-pass forward of vla_forward (its o
+ * passes through dq, which is then overwritten), for d_h in {16, 32} token by
+ * token in the gradient kernel itself.  One workgroup per head then runs the
+ * reverse recurrence from t = T down to 1 with the states rebuilt from those
+ * vectors.  Errors as for vla_forward.
  */
 vla_status vla_backward(const void *q, const void *k, const void *v, const void *u,
                         int in_dtype, int B, int H, int T, int d_h,
@@ -230,7 +233,10 @@ vla_status vla_backward(const void *q, const void *k, const void *v, const void 
 
 /*
  * vla_backward_workspace_size -- bytes of device workspace vla_backward needs:
- * (3 d_h + 8) fp32 values per token of each head, rounded up to 256 bytes
+ * (4 d_h + 8) fp32 values per token of each head, rounded up to 256 bytes,
+ * and for d_h in {64, 96, 128} also the two-pass forward's workspace
+ * (vla_forward_workspace_size) and the forward's final S, A and zkey
+ * ((2 d_h^2 + d_h) fp32 values per head), each rounded up to 256 bytes
  * (0 when T == 0).  Host-only.  Errors: VLA_ERR_INVALID_ARG (NULL bytes, bad
  * sizes), VLA_ERR_UNSUPPORTED (d_h).
  */

@@ -12,9 +12,18 @@
 // holds that slice of row i of every d x d matrix, so a matrix-vector product is
 // a sum over TPR adjacent lanes (DPP), and rank-1 updates are local.
 //
+// The reverse sweep needs, per token, z = A_{t-1} u^, alpha^, e, the key sum
+// zkey_t and the scalars delta, 1/|y|, phi(q)'zkey, 1/|k|, 1/|u|, and the
+// final states S_T, A_T.  For d in {64, 96, 128} the two-pass forward
+// (vla_twopass.hip) leaves them in the workspace on the matrix cores and the
+// kernel starts at phase 2; for d in {16, 32} phase 1 of the kernel computes
+// them.  The key sum is kept rather than rebuilt by subtraction: zkey_t grows
+// like t, and subtracting phi(k) from a sum formed in another order (the
+// chunked forward's) would leave the early tokens' zkey_t, small against
+// zkey_T, with most of the rounding of zkey_T.
+//
 // Phase 1 runs the forward one token at a time (states S, A in registers) and
-// keeps, per token, z = A_{t-1} u^, alpha^, e and the scalars delta, 1/|y|,
-// phi(q)'zkey, 1/|k|, 1/|u| in the workspace.  One barrier per token: the token
+// keeps those per-token values in the workspace.  One barrier per token: the token
 // vectors rotate through three LDS slots (staged by the last wave one token
 // ahead, raw loads two tokens ahead) and the row products through two.  The
 // per-token barriers are LDS-only (global loads stay in flight across them;
@@ -28,7 +37,9 @@
 // they carry down the chain shrink (dL/dA_0 falls roughly as 1/T^2), so fp32
 // storage would round away most of dA0 and du at T in the thousands;
 // S_{t-1} = S_t - e alpha^' and A_{t-1} = A_t + z z' / delta are rebuilt from the
-// stored vectors, the same rank-1 terms the forward added.  Per token:
+// stored vectors, the same rank-1 terms the forward added (S and A stay of the
+// order of their initial values, so their rebuilds keep relative accuracy).
+// Per token:
 //   A  dS += g phi(q)'/den;  ge = dS alpha^, galpha = dS'e, c1 = S_t'g
 //   B  gy = (galpha - alpha^ (alpha^'galpha)) / |y|;  dS -= ge k^';
 //      c2 = S_t'ge;  Sigma += gy k^' + k^ gy';  A_t gy;  Sigma z
@@ -54,14 +65,16 @@ using namespace chunk;
 // Threads per row (TPR) and where S' lives, by measurement on the backward of
 // 128 (d = 64), 128 (d = 96) and 64 (d = 128) heads: every wave repeats the
 // token's scalar work (dot products, norms, the step scalars), so fewer, wider
-// threads cost less issue; the register file bounds how wide.  d <= 64: four
-// threads per row, all slices in registers (d = 64: 256 threads, 3.05 us per
-// token against 3.10 with 16 per row); d = 96: eight per row in registers
-// (9.5 us against 10.4 and 12.6 with four); d = 128: four per row with S' in
-// LDS (each thread's row slice, contiguous) so that the other four slices fit
-// in registers (21 us against 25 and 29).
+// threads cost less issue; the register file bounds how wide.  d = 64 (reverse
+// sweep only, the records coming from the two-pass forward): eight threads per
+// row, all slices in registers (1.87 us per token against 2.21 with four and
+// 2.01 with sixteen); d = 96: eight per row in registers (9.5 us against 10.4
+// and 12.6 with four, both phases in the kernel); d = 128: four per row with
+// S' in LDS (each thread's row slice, contiguous) so that the other four slices
+// fit in registers (13.6 us for the reverse sweep against 20.7 with eight per
+// row, all in registers); d <= 32 (both phases): four per row.
 template <int D> struct BwdCfg {
-    static constexpr int TPR = D == 96 ? 8 : 4, EPT = D / TPR;
+    static constexpr int TPR = D == 96 || D == 64 ? 8 : 4, EPT = D / TPR;
     static constexpr bool ST_LDS = D == 128;
     static constexpr int TRP = ST_LDS ? D + 4 : D + 1;   // row pitch of tr
 };
@@ -86,8 +99,8 @@ struct BwdLds {
     float fsc[3][4];
     float zw[2][2][D];
     // phase 2: token vectors and scalars (three slots) ...
-    float g[3][D], pq[3][D], kh[3][D], uh[3][D], z[3][D], al[3][D], e[3][D];
-    float dpq[3][D], pk[3][D], dpk[3][D];
+    float g[3][D], pq[3][D], kh[3][D], uh[3][D], z[3][D], al[3][D], e[3][D], zt[3][D];
+    float dpq[3][D], dpk[3][D];
     float sc[3][8];
     // ... and the row results of steps A, B, C (two slots)
     float r1[2][3][D], r2[2][3][D], r3[2][D];
@@ -95,7 +108,9 @@ struct BwdLds {
     float tr[D * BwdCfg<D>::TRP];
 };
 
-template <int D, typename Tin>
+// FWD: the per-token records were left by the two-pass forward (vla_twopass.hip,
+// run with `keep`), and S0, A0, zk0 hold its final state: phase 1 is skipped.
+template <int D, typename Tin, bool FWD = false>
 __global__ void __launch_bounds__(D * BwdCfg<D>::TPR)
 vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
         const Tin *__restrict__ u, int T, float lambda0, float eps,
@@ -106,7 +121,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
 {
     using Cf = BwdCfg<D>;
     constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NT = D * TPR, NW = NT / 64;
-    constexpr int NV = (D + 63) / 64, RS = 3 * D + 8, P = Cf::TRP;
+    constexpr int NV = (D + 63) / 64, RS = 4 * D + 8, P = Cf::TRP;
     static_assert(EPT % 4 == 0 && NT % 64 == 0 && NT <= 1024, "row slices of whole granules");
     __shared__ __align__(16) BwdLds<D> L;
 
@@ -117,6 +132,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     const int bh = blockIdx.x;
     const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
     float *rh = rec + tok0 * RS;   // this head's per-token records
+    const int T1 = FWD ? 0 : T;    // tokens of phase 1
 
     // ------------------------------------------------------------ phase 1
     float S[EPT], A[EPT];
@@ -185,17 +201,17 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             L.fsc[slot][1] = iu;
         }
     };
-    if (w == NW - 1 && T > 0) {
+    if (w == NW - 1 && T1 > 0) {
         p1_load(0);
         p1_stage(0);
-        if (T > 1) p1_load(1);
+        if (T1 > 1) p1_load(1);
     }
     // drain what the prologue issued, as a wait the compiler sees: otherwise it
     // waits for every load in flight at the top of each iteration
     vmem_drain();
     __syncthreads();
 
-    for (int t = 0; t < T; ++t) {
+    for (int t = 0; t < T1; ++t) {
         const int s3 = t % 3, s2 = t & 1;
         float *rt = rh + (size_t)t * RS;
         // z = A u^, w = A k^ (old A), r = S k^ (old S)
@@ -217,9 +233,9 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             rt[row] = pz;
             rt[2 * D + row] = ei;
         }
-        if (w == NW - 1 && t + 1 < T) {
+        if (w == NW - 1 && t + 1 < T1) {
             p1_stage((t + 1) % 3);
-            if (t + 2 < T) p1_load(t + 2);
+            if (t + 2 < T1) p1_load(t + 2);
         }
         lds_barrier();
 
@@ -257,14 +273,15 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
                 if (j < D) {
                     rt[D + j] = (L.zw[s2][1][j] - L.zw[s2][0][j] * ci) * iy;
                     zk[c] += L.fpk[s3][j];
+                    rt[3 * D + j] = zk[c];
                     dn = fmaf(L.fq[s3][j], zk[c], dn);
                 }
             });
             dn = wave_sum(dn);
             if (lane == 0) {
                 const f4 s01 = {delta, iy, dn, L.fsc[s3][0]};
-                st4(rt + 3 * D, s01);
-                st4(rt + 3 * D + 4, f4{L.fsc[s3][1], 0.f, 0.f, 0.f});
+                st4(rt + 4 * D, s01);
+                st4(rt + 4 * D + 4, f4{L.fsc[s3][1], 0.f, 0.f, 0.f});
             }
         }
     }
@@ -305,7 +322,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         gzk[c] = dzk_T && j < D ? dzk_T[(size_t)bh * D + j] : 0.f;
     });
 
-    float yg[NV], yz[NV], ya[NV], ye[NV];
+    float yg[NV], yz[NV], ya[NV], ye[NV], yw[NV];
     Raw1<Tin> yq[NV], yk[NV], yu[NV];
     f4 ys0, ys1;
     auto p2_load = [&](int t) {
@@ -321,10 +338,11 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
                 yz[c] = rt[j];
                 ya[c] = rt[D + j];
                 ye[c] = rt[2 * D + j];
+                yw[c] = rt[3 * D + j];
             }
         });
-        ys0 = ld4(rt + 3 * D);
-        ys1 = ld4(rt + 3 * D + 4);
+        ys0 = ld4(rt + 4 * D);
+        ys1 = ld4(rt + 4 * D + 4);
     };
     auto p2_stage = [&](int slot) {
         const float ik = ys0[3], iu = ys1[0];
@@ -337,11 +355,11 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
                 L.dpq[slot][j] = dphi(qj);
                 L.kh[slot][j] = kj * ik;
                 L.uh[slot][j] = yu[c].get() * iu;
-                L.pk[slot][j] = phi_fast(kj);
                 L.dpk[slot][j] = dphi(kj);
                 L.z[slot][j] = yz[c];
                 L.al[slot][j] = ya[c];
                 L.e[slot][j] = ye[c];
+                L.zt[slot][j] = yw[c];
             }
         });
         if (lane == 0) {
@@ -463,7 +481,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             const int j = lane + 64 * c;
             gkh[c] = guh[c] = 0.f;
             if (j < D) {
-                const float gpq = fmaf(L.r1[s][2][j], iden, gden * zk[c]);
+                const float gpq = fmaf(L.r1[s][2][j], iden, gden * L.zt[v3][j]);
                 dq[o + j] = gpq * L.dpq[v3][j];
                 dv[o + j] = L.r1[s][0][j];
                 gzk[c] = fmaf(gden, L.pq[v3][j], gzk[c]);
@@ -481,7 +499,6 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             if (j < D) {
                 dk[o + j] = fmaf(ik, gkh[c] - L.kh[v3][j] * a3, gzk[c] * L.dpk[v3][j]);
                 du[o + j] = iu * (guh[c] - L.uh[v3][j] * a4);
-                zk[c] -= L.pk[v3][j];   // zkey_{t-1}
             }
         });
     };
@@ -523,22 +540,74 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     }
 }
 
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace: the per-token records; for d in {64, 96, 128} also the two-pass
+// forward's workspace and its final S, A, zkey.
+struct BwdPlan {
+    size_t rec = 0, fwd = 0, st = 0, bytes = 0;
+};
+BwdPlan bwd_plan(int BH, int T, int d)
+{
+    BwdPlan p;
+    if (T <= 0) return p;
+    size_t off = up256((size_t)BH * T * backward_record_floats(d) * sizeof(float));
+    if (chunk_supported(d)) {
+        p.fwd = off;
+        off = up256(off + twopass_workspace_bytes(BH, T, d));
+        p.st = off;
+        off = up256(off + (size_t)BH * (2 * (size_t)d * d + d) * sizeof(float));
+    }
+    p.bytes = off;
+    return p;
+}
+
+// both phases in the one kernel (per-token forward, then the reverse sweep)
+template <int D, typename Tin>
+hipError_t launch_phase1(const BwdArgs &a, dim3 grid, dim3 block, float *rec)
+{
+    hipLaunchKernelGGL((vla_bwd<D, Tin>), grid, block, 0, a.stream, (const Tin *)a.q,
+                       (const Tin *)a.k, (const Tin *)a.v, (const Tin *)a.u, a.T, a.lambda0, a.eps,
+                       a.S0, a.A0, a.zk0, a.dO, a.dS_T, a.dA_T, a.dzk_T, a.dq, a.dk, a.dv, a.du,
+                       a.dS0, a.dA0, a.dzk0, rec);
+    return hipGetLastError();
+}
+
 template <int D, typename Tin>
 hipError_t launch(const BwdArgs &a)
 {
-    hipLaunchKernelGGL((vla_bwd<D, Tin>), dim3(a.B * a.H), dim3(D * BwdCfg<D>::TPR), 0, a.stream,
-                       (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, (const Tin *)a.u, a.T,
-                       a.lambda0, a.eps, a.S0, a.A0, a.zk0, a.dO, a.dS_T, a.dA_T, a.dzk_T, a.dq,
-                       a.dk, a.dv, a.du, a.dS0, a.dA0, a.dzk0, (float *)a.ws);
-    return hipGetLastError();
+    const int BH = a.B * a.H;
+    const BwdPlan p = bwd_plan(BH, a.T, D);
+    char *ws = static_cast<char *>(a.ws);
+    float *rec = reinterpret_cast<float *>(ws + p.rec);
+    const dim3 grid(BH), block(D * BwdCfg<D>::TPR);
+    if constexpr (D >= 64) {   // the head sizes of the matrix-core forward
+        if (a.T <= 0) return launch_phase1<D, Tin>(a, grid, block, rec);
+        // the forward on the matrix-core kernels, keeping the per-token records;
+        // its o goes to dq (overwritten below), its final state to the workspace
+        float *stS = reinterpret_cast<float *>(ws + p.st), *stA = stS + (size_t)BH * D * D;
+        float *stZ = stA + (size_t)BH * D * D;
+        FwdArgs f{a.q, a.k, a.v, a.u, a.dtype, a.B, a.H, a.T, D, a.lambda0, a.eps,
+                  a.dq, stS, stA, stZ, a.S0, a.A0, a.zk0, a.stream,
+                  ws + p.fwd, twopass_workspace_bytes(BH, a.T, D)};
+        f.keep = rec;
+        const hipError_t e = launch_forward_twopass(f, 3);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((vla_bwd<D, Tin, true>), grid, block, 0, a.stream, (const Tin *)a.q,
+                           (const Tin *)a.k, (const Tin *)a.v, (const Tin *)a.u, a.T, a.lambda0,
+                           a.eps, stS, stA, stZ, a.dO, a.dS_T, a.dA_T, a.dzk_T, a.dq, a.dk, a.dv,
+                           a.du, a.dS0, a.dA0, a.dzk0, rec);
+        return hipGetLastError();
+    } else {
+        return launch_phase1<D, Tin>(a, grid, block, rec);
+    }
 }
 
 }  // namespace
 
 size_t backward_workspace_bytes(int BH, int T, int d)
 {
-    const size_t b = (size_t)BH * (size_t)(T > 0 ? T : 0) * backward_record_floats(d) * sizeof(float);
-    return (b + 255) & ~(size_t)255;
+    return bwd_plan(BH, T, d).bytes;
 }
 
 hipError_t launch_backward(const BwdArgs &a)

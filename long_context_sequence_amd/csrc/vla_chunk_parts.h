@@ -123,6 +123,10 @@ struct Buf {
                                               0x00020000))
     {
     }
+    __device__ __forceinline__ void st32(float x, unsigned off, unsigned soff = 0) const
+    {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, soff, 0);
+    }
     __device__ __forceinline__ void st128(f4 x, unsigned off, unsigned soff = 0) const
     {
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, x), r, off, soff, 0);
@@ -281,6 +285,9 @@ struct WToLds {
     {
         if (n == 0) st4(&L.nrm[wi][4 * g], nr);
     }
+    // z_t = A_{t-1} u^_t of the chunk's tokens 4g + r at keys 16b + n, and
+    // 1/delta_t: nothing to do here (a sink that keeps them overrides this)
+    __device__ __forceinline__ void zcols(int, f4, f4) {}
 };
 // Per-thread view of one head: lane coordinates, input pointers and the two
 // chains' steps.  A wave with chain index wi owns column blocks wi*BPW + bb.
@@ -672,11 +679,12 @@ struct Head {
             const int b = wi * BPW + bb;
             float zb[4];   // Z0'[4c+g][16b+n]
             sfor<4>([&](auto c) { zb[c] = L.z0[(4 * c + g) * LD + 16 * b + n]; });
-            const f4 q2 = mma4(X, zb, zero);        // L^-1 Z0'
+            const f4 q2 = mma4(X, zb, zero);        // L^-1 Z0': row t is z_t
             const f4 q1 = q2 * inv4;                // D^-1 L^-1 Z0'
             const f4 xt = mma4(lit, q1, zero);      // (I + G)^-1 Z0'
             const f4 wt = mma4(hm, q2, y[bb]);      // W'
             const f4 nx = -xt;
+            wout.zcols(b, q2, inv4);
             f4 az[NB];
             sfor<NB>([&](auto rho) { az[rho] = ld4(&L.z0t[(16 * rho + n) * LT + 4 * g]); });
             sfor<4>([&](auto r) {      // As <- As - Z0 (I + G)^-1 Z0'

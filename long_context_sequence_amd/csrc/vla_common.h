@@ -17,6 +17,9 @@ struct FwdArgs {
     hipStream_t stream;
     void *ws;             // workspace of the two-pass forward (device memory)
     size_t ws_bytes;
+    // two-pass forward only: when set, the per-token quantities the gradients
+    // need ((4 d + 8) floats per token and head, see vla_bwd.h) go here too
+    float *keep = nullptr;
 };
 
 // Input widening: fp32 as is, bf16 (stored as its 16 bit pattern) exactly.

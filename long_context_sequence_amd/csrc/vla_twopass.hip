@@ -47,6 +47,14 @@ using namespace chunk;
 using rec::CH;
 using rec::Rec;
 
+// Per-token record the forward can leave for the gradients (when asked to): per
+// token z = A_{t-1} u^, alpha^, e, the key sum zkey_t (d each), then delta,
+// 1/|y|, phi(q)'zkey, 1/|k|, 1/|u| and three unused floats.
+template <int D>
+struct Keep {
+    static constexpr int Z = 0, AL = D, E = 2 * D, ZK = 3 * D, SC = 4 * D, RS = 4 * D + 8;
+};
+
 // Value blocks per memory workgroup and the ways each block's key tiles are
 // split over its waves (VBW x KS waves per workgroup).
 template <int D> struct MemCfg;
@@ -404,7 +412,7 @@ __device__ __forceinline__ float sum_row8(float x)
     return x;
 }
 
-template <int D, typename Tin>
+template <int D, typename Tin, bool SAVE = false>
 struct PenStage {
     static constexpr int LD = Cfg<D>::LD, CP = D / 8;
     int tl, cc;
@@ -425,7 +433,8 @@ struct PenStage {
         rk.load(k + off);
         ru.load(u + off);
     }
-    __device__ __forceinline__ void stage(PLds<D> &L, int cq, int T, float *rkh, float *rph)
+    __device__ __forceinline__ void stage(PLds<D> &L, int cq, int T, float *rkh, float *rph,
+                                          float *kept = nullptr)
     {
         if (!on) return;
         const int slot = cq & 1;
@@ -439,6 +448,13 @@ struct PenStage {
         const float nk = sum_row8(pk), nu = sum_row8(pu);
         const float ik = ok && nk > 0.f ? rsqrtf(nk) : 0.f;
         const float iu = ok && nu > 0.f ? rsqrtf(nu) : 0.f;
+        if constexpr (SAVE) {
+            if (cc == 0 && ok) {
+                float *kt = kept + (size_t)(cq * CH + tl) * Keep<D>::RS + Keep<D>::SC;
+                kt[3] = ik;
+                kt[4] = iu;
+            }
+        }
         const int e0 = tl * LD + cc * CP;
 #pragma unroll
         for (int i = 0; i < CP; ++i) {
@@ -453,7 +469,8 @@ struct PenStage {
         }
     }
     // 1 / max(phi(q)' zkey, eps) per token of chunk cq (key sums in LDS) to rrd
-    __device__ __forceinline__ void den(const PLds<D> &L, int cq, float eps, float *rrd) const
+    __device__ __forceinline__ void den(const PLds<D> &L, int cq, float eps, float *rrd,
+                                        int T = 0, float *kept = nullptr) const
     {
         if (!on) return;
         const int slot = cq & 1, e0 = tl * LD + cc * CP;
@@ -462,6 +479,35 @@ struct PenStage {
         for (int i = 0; i < CP; ++i) pd = fmaf(L.ph[slot][e0 + i], L.zk[slot][e0 + i], pd);
         pd = sum_row8(pd);
         if (cc == 0) rrd[tl] = __builtin_amdgcn_rcpf(fmaxf(pd, eps));
+        if constexpr (SAVE) {
+            if (cq * CH + tl < T) {
+                float *kt = kept + (size_t)(cq * CH + tl) * Keep<D>::RS;
+#pragma unroll
+                for (int i = 0; i < CP; i += 4)
+                    st4(kt + Keep<D>::ZK + cc * CP + i, ld4(&L.zk[slot][e0 + i]));
+                if (cc == 0) kt[Keep<D>::SC + 2] = pd;
+            }
+        }
+    }
+};
+
+// The penalty pass's W sink, which also keeps z_t and delta_t of each token
+// (rows of L^-1 Z0' and the pivots of I + G) in the per-token records.
+template <int D>
+struct KeepW : WToLds<D, PLds<D>> {
+    float *kept;   // this head's per-token records
+    int tok, T;    // first token of the chunk, tokens
+    __device__ __forceinline__ void zcols(int b, f4 q2, f4 inv4)
+    {
+        const int g = this->g, n = this->n;
+        sfor<4>([&](auto r) {
+            const int t = tok + 4 * g + r;
+            if (t < T) {
+                float *kt = kept + (size_t)t * Keep<D>::RS;
+                kt[Keep<D>::Z + 16 * b + n] = q2[int(r)];
+                if (b == 0 && n == 0) kt[Keep<D>::SC] = 1.f / inv4[int(r)];
+            }
+        });
     }
 };
 
@@ -494,12 +540,16 @@ __device__ __forceinline__ void cross_factor(const PLds<D> &L, const float *y, i
 //   3  downdate A, W of chunk p; 1/den of chunk p            | barrier
 //   4  1/|w|, Alpha^'K^ and Alpha^'Phi partials; alpha^ to
 //      the record.
-template <int D, typename Tin>
+//
+// With SAVE, the per-token quantities the gradients need (Keep) also go to
+// `kept`: z and delta from the factorisation, alpha^ and 1/|y| with the record,
+// 1/|k|, 1/|u| and phi(q)'zkey from the staging.
+template <int D, typename Tin, bool SAVE = false>
 __global__ void __launch_bounds__(64 * Cfg<D>::NA)
 vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ u,
         int T, int S, int SC, float lambda0, float eps,
         const float *A0, const float *zk0, const float *aseg, const float *zseg,
-        float *__restrict__ rec, float *A_out, float *zk_out)
+        float *__restrict__ rec, float *A_out, float *zk_out, float *kept_all = nullptr)
 {
     using Hd = Head<D, Tin, PLds<D>>;
     constexpr int BPW = Cfg<D>::BPW, LT = Cfg<D>::LT, RS = Rec<D>::SIZE, NA = Cfg<D>::NA;
@@ -516,7 +566,8 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     // the C x C factors of the record, the waves from 2 on own the key sums, and
     // the last two waves stage the inputs
     Hd hd(L, q, k, nullptr, u, nullptr, T, eps, bh, tid & 63, w, tid, false, tid - 128);
-    PenStage<D, Tin> ps(tid - 64 * (NA - 2));
+    PenStage<D, Tin, SAVE> ps(tid - 64 * (NA - 2));
+    float *kept = SAVE ? kept_all + (size_t)bh * T * Keep<D>::RS : nullptr;
     typename Hd::State st;
     const float *a_init;
     if (j > 0)
@@ -533,7 +584,7 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     const size_t tok0 = (size_t)bh * T;
     float *rb = rec + ((size_t)bh * NC + c0) * RS;   // record of chunk p below
     ps.prefetch(q, k, u, tok0, T, c0);
-    ps.stage(L, c0, T, rb + Rec<D>::KH, rb + Rec<D>::PH);
+    ps.stage(L, c0, T, rb + Rec<D>::KH, rb + Rec<D>::PH, kept);
     if (c0 + 1 < c1) ps.prefetch(q, k, u, tok0, T, c0 + 1);
     vmem_drain();
     __syncthreads();
@@ -542,8 +593,13 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     // factors of chunk p - 1 and, for an even p - 1, its cross factors with
     // chunk p (from W, |w|^2 of chunk p - 1, still in LDS), the key sums of
     // chunk p, and stage chunk p + 1.
-    WToLds<D, PLds<D>> wl{L, 0, hd.g, hd.n};
+    auto sink = [&]() {
+        if constexpr (SAVE) return KeepW<D>{{L, 0, hd.g, hd.n}, kept, 0, T};
+        else return WToLds<D, PLds<D>>{L, 0, hd.g, hd.n};
+    };
+    auto wl = sink();
     for (int p = c0; p < c1; ++p, rb += RS) {
+        if constexpr (SAVE) wl.tok = p * CH;
         hd.a_products(st, p);
         lds_barrier();
         hd.a_update_shared(st, p, wl, [&]() {
@@ -556,11 +612,11 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             }
             hd.stage2(p);
             if (p + 1 < c1) {
-                ps.stage(L, p + 1, T, rb + RS + Rec<D>::KH, rb + RS + Rec<D>::PH);
+                ps.stage(L, p + 1, T, rb + RS + Rec<D>::KH, rb + RS + Rec<D>::PH, kept);
                 if (p + 2 < c1) ps.prefetch(q, k, u, tok0, T, p + 2);
             }
         });
-        ps.den(L, p, eps, rb + Rec<D>::RD);
+        ps.den(L, p, eps, rb + Rec<D>::RD, T, kept);
         lds_barrier();
         f4 invn4;
         hd.s_grams(p, invn4);
@@ -568,6 +624,16 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             const int b = w * BPW + bb;
             const f4 a = ld4(&L.wt[0][(16 * b + hd.n) * LT + 4 * hd.g]) * invn4;
             st4(&rb[Rec<D>::AH + swz16(16 * b + hd.n, hd.g)], a);
+            if constexpr (SAVE) {
+                sfor<4>([&](auto r) {
+                    const int t = p * CH + 4 * hd.g + r;
+                    if (t < T) {
+                        float *kt = kept + (size_t)t * Keep<D>::RS;
+                        kt[Keep<D>::AL + 16 * b + hd.n] = a[int(r)];
+                        if (b == 0 && hd.n == 0) kt[Keep<D>::SC + 1] = invn4[int(r)];
+                    }
+                });
+            }
         });
     }
     lds_barrier();
@@ -632,10 +698,14 @@ struct MemOps {
 // p + NS after the barrier of step p (all reads of stage p mod NS are done by
 // then), spread over the step, and waits for its pieces of pair p + 1 before
 // the barrier of step p, so that the barrier publishes them.
-template <int D, typename Tin>
+//
+// With SAVE, the errors e_t also go to the per-token records (Keep): key split
+// 0 writes chunk a's, key split 1 chunk b's, the others store through an empty
+// view, so that every wave issues the same number of stores.
+template <int D, typename Tin, bool SAVE = false>
 __global__ void __launch_bounds__(64 * MemCfg<D>::VBW * MemCfg<D>::KS)
 vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec, const float *S0,
-        float *__restrict__ o, float *S_out)
+        float *__restrict__ o, float *S_out, float *kept_all = nullptr)
 {
     using MS = MemStage<D, Tin>;
     using R = Rec<D>;
@@ -669,6 +739,15 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
     const Buf rbuf(rec + (size_t)bh * NC * RS, (unsigned)(NC * RS * 4));
     const Buf vbuf(v + (size_t)bh * T * D, (unsigned)T * D * (unsigned)sizeof(Tin));
     float *oh = o + (size_t)bh * T * D;
+    float *kept = SAVE ? kept_all + (size_t)bh * T * Keep<D>::RS : nullptr;
+    // the errors of chunk c (this wave's value block) to the records; rows past
+    // T are dropped
+    auto keep_e = [&](int c, bool mine, f4 e) {
+        const Buf kb_(kept, mine ? (unsigned)T * Keep<D>::RS * 4u : 0u);
+        sfor<4>([&](auto r) {
+            kb_.st32(e[int(r)], 4u * ((unsigned)(c * CH + 4 * g + r) * Keep<D>::RS + Keep<D>::E + 16 * b + n));
+        });
+    };
 
     f4 st[NT];
 #pragma unroll
@@ -768,9 +847,10 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
     // the wait before the barrier of a step: this wave's pieces of the next
     // pair (behind them: the step's store, and for three stages the copies and
     // the store of one more step)
+    constexpr int NST = SAVE ? 5 : 1;   // stores per step
     auto wait_next = [&]() {
-        if constexpr (NS == 3) vm_wait<NIW + 2>();
-        else vm_wait<1>();
+        if constexpr (NS == 3) vm_wait<NIW + 2 * NST>();
+        else vm_wait<NST>();
     };
     // The readout of a pair needs the S Phi partials of the other waves, which
     // are formed after the barrier of the pair's step (off the chain from S to
@@ -815,6 +895,7 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
         // one store and the copies of a step)
         const int cp = 2 * (pm - 1) + (ks == 0 ? 0 : 1);
         store_o(max(cp, 0), pm > 0 && ks < 2, ob, cy.rd);
+        if constexpr (SAVE) keep_e(2 * pm + (ks == 0 ? 0 : 1), ks < 2, ks == 0 ? ea : eb);
         cy = Carry{ea, eb, ma.pa, mb.pa, qp, ks == 0 ? ma.rd : mb.rd};
     };
 
@@ -854,6 +935,7 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
         lds_barrier();
         const f4 e = errors(m, reduce(sl, 0));
         store_o(c, ks == 0, mma4(e, m.pa, reduce(sl, 2)), m.rd);
+        if constexpr (SAVE) keep_e(c, ks == 0, e);
         update(m, e);
     }
     vm_wait<0>();   // no copy into LDS outlives the workgroup
@@ -932,15 +1014,25 @@ hipError_t launch(const FwdArgs &a, int phases)
             hipLaunchKernelGGL((vla_seginv<D>), dim3(BH * (p.S - 1)), dim3(SEG_TPR * D), 0, a.stream, p.S,
                                p.P, a.lambda0, a.A0, a.zk0, gram, zks, aseg, zseg);
         }
-        hipLaunchKernelGGL((vla_pen<D, Tin>), dim3(BH * p.S), dim3(64 * Cfg<D>::NA), 0, a.stream, q,
-                           k, u, a.T, p.S, p.SC, a.lambda0, a.eps, a.A0, a.zk0, aseg, zseg, rec,
-                           a.A_out, a.zk_out);
+        if (a.keep)
+            hipLaunchKernelGGL((vla_pen<D, Tin, true>), dim3(BH * p.S), dim3(64 * Cfg<D>::NA), 0,
+                               a.stream, q, k, u, a.T, p.S, p.SC, a.lambda0, a.eps, a.A0, a.zk0,
+                               aseg, zseg, rec, a.A_out, a.zk_out, a.keep);
+        else
+            hipLaunchKernelGGL((vla_pen<D, Tin>), dim3(BH * p.S), dim3(64 * Cfg<D>::NA), 0, a.stream,
+                               q, k, u, a.T, p.S, p.SC, a.lambda0, a.eps, a.A0, a.zk0, aseg, zseg,
+                               rec, a.A_out, a.zk_out, nullptr);
     }
     if (phases & 2) {
         constexpr int NG = (D / 16) / MemCfg<D>::VBW;
-        hipLaunchKernelGGL((vla_mem<D, Tin>), dim3(BH * NG), dim3(64 * MemCfg<D>::VBW * MemCfg<D>::KS),
-                           0, a.stream, v, a.T, BH, rec,
-                           a.S0, a.o, a.S_out);
+        if (a.keep)
+            hipLaunchKernelGGL((vla_mem<D, Tin, true>), dim3(BH * NG),
+                               dim3(64 * MemCfg<D>::VBW * MemCfg<D>::KS), 0, a.stream, v, a.T, BH,
+                               rec, a.S0, a.o, a.S_out, a.keep);
+        else
+            hipLaunchKernelGGL((vla_mem<D, Tin>), dim3(BH * NG),
+                               dim3(64 * MemCfg<D>::VBW * MemCfg<D>::KS), 0, a.stream, v, a.T, BH,
+                               rec, a.S0, a.o, a.S_out, nullptr);
     }
     return hipGetLastError();
 }
