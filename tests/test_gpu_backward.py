@@ -112,6 +112,20 @@ def test_backward_sweep_every_head(d, dtype, T):
     _compare(cfg, x, adj, got, [(0, 0), (0, 1)])
 
 
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("T", [16, 250])
+def test_backward_whole_and_ragged_chunks(d, T):
+    """One whole 16-token chunk, and an even chunk count with a ragged last
+    chunk (the forward that keeps the per-token records steps over chunk pairs)."""
+    dev = _dev()
+    cfg = _cfg(d, "bf16", 1, 3, T)
+    _say(f"backward chunks d={d} T={T}")
+    x = gen.make_inputs(cfg)
+    adj = _adjoints(1, 3, T, d, seed=2000 + d + T)
+    got = _gpu_backward(cfg, x, adj, dev)
+    _compare(cfg, x, adj, got, [(0, 0), (0, 1), (0, 2)])
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_backward_given_initial_state(d):
     """A general initial state (S0, an SPD A0, zkey0) and only dL/do."""
