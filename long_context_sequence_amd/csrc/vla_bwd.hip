@@ -77,6 +77,11 @@ template <int D> struct BwdCfg {
     static constexpr int TPR = D == 96 || D == 64 ? 8 : 4, EPT = D / TPR;
     static constexpr bool ST_LDS = D == 128;
     static constexpr int TRP = ST_LDS ? D + 4 : D + 1;   // row pitch of tr
+    // the reverse sweep's loads and staging spread over the waves (d = 96:
+    // 4.3 us per token against 4.9 with the last wave alone; d = 128: 11.4
+    // against 14.5) or, at d <= 64, left to the last wave (d = 64: 1.85 against
+    // 2.66)
+    static constexpr bool SPREAD = D >= 96;
 };
 
 __device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __expf(x); }
@@ -322,52 +327,67 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         gzk[c] = dzk_T && j < D ? dzk_T[(size_t)bh * D + j] : 0.f;
     });
 
+    // A token's vectors are loaded (raw, a token ahead) and staged into LDS in
+    // nine groups: dO; q; k; u; z; alpha^; e; zkey_t; the scalars (also loaded
+    // by the k and u groups, for 1/|k|, 1/|u|).  The last wave owns them all
+    // (and alone calls p2_load, p2_stage), or with SPREAD group i is wave
+    // NW - 1 - i mod NW's.
+    auto own = [&](int grp) { return !Cf::SPREAD || w == NW - 1 - grp % NW; };
+    const bool stager = Cf::SPREAD || w == NW - 1;
     float yg[NV], yz[NV], ya[NV], ye[NV], yw[NV];
     Raw1<Tin> yq[NV], yk[NV], yu[NV];
     f4 ys0, ys1;
+    if constexpr (Cf::SPREAD) ys0 = ys1 = f4{0.f, 0.f, 0.f, 0.f};   // read by every stager
     auto p2_load = [&](int t) {
         const float *rt = rh + (size_t)t * RS;
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
                 const size_t o = (tok0 + t) * D + j;
-                yg[c] = dO[o];
-                yq[c].load(q, o);
-                yk[c].load(k, o);
-                yu[c].load(u, o);
-                yz[c] = rt[j];
-                ya[c] = rt[D + j];
-                ye[c] = rt[2 * D + j];
-                yw[c] = rt[3 * D + j];
+                if (own(0)) yg[c] = dO[o];
+                if (own(1)) yq[c].load(q, o);
+                if (own(2)) yk[c].load(k, o);
+                if (own(3)) yu[c].load(u, o);
+                if (own(4)) yz[c] = rt[j];
+                if (own(5)) ya[c] = rt[D + j];
+                if (own(6)) ye[c] = rt[2 * D + j];
+                if (own(7)) yw[c] = rt[3 * D + j];
             }
         });
-        ys0 = ld4(rt + 4 * D);
-        ys1 = ld4(rt + 4 * D + 4);
+        if (own(2) || own(3) || own(8)) {
+            ys0 = ld4(rt + 4 * D);
+            ys1 = ld4(rt + 4 * D + 4);
+        }
     };
     auto p2_stage = [&](int slot) {
         const float ik = ys0[3], iu = ys1[0];
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
-                const float qj = yq[c].get(), kj = yk[c].get();
-                L.g[slot][j] = yg[c];
-                L.pq[slot][j] = phi_fast(qj);
-                L.dpq[slot][j] = dphi(qj);
-                L.kh[slot][j] = kj * ik;
-                L.uh[slot][j] = yu[c].get() * iu;
-                L.dpk[slot][j] = dphi(kj);
-                L.z[slot][j] = yz[c];
-                L.al[slot][j] = ya[c];
-                L.e[slot][j] = ye[c];
-                L.zt[slot][j] = yw[c];
+                if (own(0)) L.g[slot][j] = yg[c];
+                if (own(1)) {
+                    const float qj = yq[c].get();
+                    L.pq[slot][j] = phi_fast(qj);
+                    L.dpq[slot][j] = dphi(qj);
+                }
+                if (own(2)) {
+                    const float kj = yk[c].get();
+                    L.kh[slot][j] = kj * ik;
+                    L.dpk[slot][j] = dphi(kj);
+                }
+                if (own(3)) L.uh[slot][j] = yu[c].get() * iu;
+                if (own(4)) L.z[slot][j] = yz[c];
+                if (own(5)) L.al[slot][j] = ya[c];
+                if (own(6)) L.e[slot][j] = ye[c];
+                if (own(7)) L.zt[slot][j] = yw[c];
             }
         });
-        if (lane == 0) {
+        if (own(8) && lane == 0) {
             st4(&L.sc[slot][0], ys0);
             st4(&L.sc[slot][4], ys1);
         }
     };
-    if (w == NW - 1 && T > 0) {
+    if (stager && T > 0) {
         p2_load(T - 1);
         p2_stage((T - 1) % 3);
         if (T > 1) p2_load(T - 2);
@@ -509,7 +529,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     lds_barrier();
     float gdel_d = 0.f;
     for (int t = T - 1; t >= 0; --t) {
-        if (w == NW - 1 && t > 0) {   // token t - 1 into slot (t - 1) % 3
+        if (stager && t > 0) {   // token t - 1 into slot (t - 1) % 3
             p2_stage((t - 1) % 3);
             if (t > 1) p2_load(t - 2);
         }
