@@ -17,9 +17,9 @@ struct BwdArgs {
     hipStream_t stream;
 };
 
-// floats kept per token of a head: z, alpha^, e, the key sum zkey_t (d each)
-// and 8 scalars
-inline size_t backward_record_floats(int d) { return 4 * (size_t)d + 8; }
+// floats kept per token of a head (rec::Keep in vla_record.h): z, alpha^, e,
+// the key sum zkey_t (d each) and 8 scalars
+constexpr size_t backward_record_floats(int d) { return 4 * (size_t)d + 8; }
 size_t backward_workspace_bytes(int BH, int T, int d);
 hipError_t launch_backward(const BwdArgs &a);
 

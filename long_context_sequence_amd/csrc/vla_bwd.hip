@@ -55,6 +55,7 @@
 // staging of token t - 2 or the row results of token t - 1.
 #include "vla_bwd.h"
 #include "vla_chunk_parts.h"
+#include "vla_record.h"
 #include "vla_reduce.h"
 
 namespace vla {
@@ -126,7 +127,9 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
 {
     using Cf = BwdCfg<D>;
     constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NT = D * TPR, NW = NT / 64;
-    constexpr int NV = (D + 63) / 64, RS = 4 * D + 8, P = Cf::TRP;
+    using K = rec::Keep<D>;
+    constexpr int NV = (D + 63) / 64, RS = K::RS, P = Cf::TRP;
+    static_assert(RS == backward_record_floats(D), "record size");
     static_assert(EPT % 4 == 0 && NT % 64 == 0 && NT <= 1024, "row slices of whole granules");
     __shared__ __align__(16) BwdLds<D> L;
 
@@ -235,8 +238,8 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         if (leader) {
             L.zw[s2][0][row] = pz;
             L.zw[s2][1][row] = pw;
-            rt[row] = pz;
-            rt[2 * D + row] = ei;
+            rt[K::Z + row] = pz;
+            rt[K::E + row] = ei;
         }
         if (w == NW - 1 && t + 1 < T1) {
             p1_stage((t + 1) % 3);
@@ -276,17 +279,17 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             sfor<NV>([&](auto c) {
                 const int j = lane + 64 * c;
                 if (j < D) {
-                    rt[D + j] = (L.zw[s2][1][j] - L.zw[s2][0][j] * ci) * iy;
+                    rt[K::AL + j] = (L.zw[s2][1][j] - L.zw[s2][0][j] * ci) * iy;
                     zk[c] += L.fpk[s3][j];
-                    rt[3 * D + j] = zk[c];
+                    rt[K::ZK + j] = zk[c];
                     dn = fmaf(L.fq[s3][j], zk[c], dn);
                 }
             });
             dn = wave_sum(dn);
             if (lane == 0) {
                 const f4 s01 = {delta, iy, dn, L.fsc[s3][0]};
-                st4(rt + 4 * D, s01);
-                st4(rt + 4 * D + 4, f4{L.fsc[s3][1], 0.f, 0.f, 0.f});
+                st4(rt + K::SC, s01);
+                st4(rt + K::SC + 4, f4{L.fsc[s3][1], 0.f, 0.f, 0.f});
             }
         }
     }
@@ -348,15 +351,15 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
                 if (own(1)) yq[c].load(q, o);
                 if (own(2)) yk[c].load(k, o);
                 if (own(3)) yu[c].load(u, o);
-                if (own(4)) yz[c] = rt[j];
-                if (own(5)) ya[c] = rt[D + j];
-                if (own(6)) ye[c] = rt[2 * D + j];
-                if (own(7)) yw[c] = rt[3 * D + j];
+                if (own(4)) yz[c] = rt[K::Z + j];
+                if (own(5)) ya[c] = rt[K::AL + j];
+                if (own(6)) ye[c] = rt[K::E + j];
+                if (own(7)) yw[c] = rt[K::ZK + j];
             }
         });
         if (own(2) || own(3) || own(8)) {
-            ys0 = ld4(rt + 4 * D);
-            ys1 = ld4(rt + 4 * D + 4);
+            ys0 = ld4(rt + K::SC);
+            ys1 = ld4(rt + K::SC + 4);
         }
     };
     auto p2_stage = [&](int slot) {

@@ -1,6 +1,7 @@
 // vla_record.h -- layout of the per-chunk record that the penalty pass of the
 // two-pass forward leaves in the workspace (16 tokens per chunk), read by the
-// memory pass and by the scan form of the memory chain.
+// memory pass and by the scan form of the memory chain; and of the per-token
+// record that the forward can leave for the gradient kernel.
 #pragma once
 
 namespace vla {
@@ -26,6 +27,16 @@ struct Rec {
     static constexpr int KH = RD + CH;        // k^ [token][key] (0 past T)
     static constexpr int PH = KH + CH * D;    // phi(q) [token][key]
     static constexpr int SIZE = PH + CH * D;  // a multiple of 4
+};
+
+// One token's record for the gradients (floats): z = A_{t-1} u^, alpha^, e, the
+// key sum zkey_t (d each), then delta, 1/|y|, phi(q)'zkey_t, 1/|k|, 1/|u| and
+// three unused floats.  Written by the two-pass forward when asked to (or by
+// the gradient kernel's own per-token forward), read by its reverse sweep.
+template <int D>
+struct Keep {
+    static constexpr int Z = 0, AL = D, E = 2 * D, ZK = 3 * D, SC = 4 * D;
+    static constexpr int RS = 4 * D + 8;   // a multiple of 4
 };
 
 }  // namespace rec

@@ -47,13 +47,7 @@ using namespace chunk;
 using rec::CH;
 using rec::Rec;
 
-// Per-token record the forward can leave for the gradients (when asked to): per
-// token z = A_{t-1} u^, alpha^, e, the key sum zkey_t (d each), then delta,
-// 1/|y|, phi(q)'zkey, 1/|k|, 1/|u| and three unused floats.
-template <int D>
-struct Keep {
-    static constexpr int Z = 0, AL = D, E = 2 * D, ZK = 3 * D, SC = 4 * D, RS = 4 * D + 8;
-};
+using rec::Keep;   // the per-token records kept for the gradients
 
 // Value blocks per memory workgroup and the ways each block's key tiles are
 // split over its waves (VBW x KS waves per workgroup).
