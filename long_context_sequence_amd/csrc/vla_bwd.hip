@@ -565,6 +565,10 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// head sizes whose records come from the two-pass forward (vla_twopass.hip
+// instantiates it for d = 64, 96, 128); the others run phase 1
+constexpr bool records_from_forward(int d) { return d == 64 || d == 96 || d == 128; }
+
 // Workspace: the per-token records; for d in {64, 96, 128} also the two-pass
 // forward's workspace and its final S, A, zkey.
 struct BwdPlan {
@@ -575,7 +579,7 @@ BwdPlan bwd_plan(int BH, int T, int d)
     BwdPlan p;
     if (T <= 0) return p;
     size_t off = up256((size_t)BH * T * backward_record_floats(d) * sizeof(float));
-    if (chunk_supported(d)) {
+    if (records_from_forward(d)) {
         p.fwd = off;
         off = up256(off + twopass_workspace_bytes(BH, T, d));
         p.st = off;
@@ -604,7 +608,7 @@ hipError_t launch(const BwdArgs &a)
     char *ws = static_cast<char *>(a.ws);
     float *rec = reinterpret_cast<float *>(ws + p.rec);
     const dim3 grid(BH), block(D * BwdCfg<D>::TPR);
-    if constexpr (D >= 64) {   // the head sizes of the matrix-core forward
+    if constexpr (records_from_forward(D)) {
         if (a.T <= 0) return launch_phase1<D, Tin>(a, grid, block, rec);
         // the forward on the matrix-core kernels, keeping the per-token records;
         // its o goes to dq (overwritten below), its final state to the workspace
