@@ -126,6 +126,19 @@ def test_backward_whole_and_ragged_chunks(d, T):
     _compare(cfg, x, adj, got, [(0, 0), (0, 1), (0, 2)])
 
 
+@pytest.mark.parametrize("d,T", [(64, 4096), (128, 1024)])
+def test_backward_single_head_many_segments(d, T):
+    """One head over a long sequence: the forward that keeps the records splits
+    the penalty chain into many short segments (two chunks each)."""
+    dev = _dev()
+    cfg = _cfg(d, "bf16", 1, 1, T)
+    _say(f"backward single head d={d} T={T}")
+    x = gen.make_inputs(cfg)
+    adj = _adjoints(1, 1, T, d, seed=3000 + d)
+    got = _gpu_backward(cfg, x, adj, dev)
+    _compare(cfg, x, adj, got, [(0, 0)])
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_backward_given_initial_state(d):
     """A general initial state (S0, an SPD A0, zkey0) and only dL/do."""
