@@ -365,7 +365,7 @@ def decode_bench(vla, torch, steps: int = 256):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
               "heads shard across GPUs with no communication, see the design notes.",
               file=sys.stderr)
         sys.exit(2)
