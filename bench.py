@@ -366,7 +366,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
-              "heads shard across GPUs with no communication, see the design notes.",
+              "the heads would shard across GPUs with no communication between them.",
               file=sys.stderr)
         sys.exit(2)
 
