@@ -20,8 +20,7 @@
  *   Eq. (11)       zkey_t = sum_{s<=t} phi(k_s),  phi = ELU + 1,
  *                  o_t = S_t phi(q_t) / max(phi(q_t)' zkey_t, eps)
  *
- * Readings where the pages leave a detail open (each is also listed in the
- * design notes):
+ * Readings where the pages leave a detail open:
  *   - u is unit-normalised here as well as k (section 3.2 states that u is unit
  *     length; normalising an already-unit u changes nothing);
  *   - a zero vector normalises to the zero vector (so u = 0 leaves A unchanged,
