@@ -265,3 +265,45 @@ def test_backward_other_workloads_sampled_heads(cid, T, heads):
     for n in NAMES:
         assert np.isfinite(got[n]).all(), n
     _compare(cfg, x, adj, got, heads)
+
+
+def test_backward_long_context_last_tokens():
+    """The long-context workload at full size (B=2, H=32, d=128, T=65536, bf16
+    inputs): gradients of every head on the GPU, all finite; for sampled heads
+    the last 64 tokens' dq, dk, dv, du against the oracle's reverse mode over
+    those tokens, started from its forward state after the first T - 64 tokens
+    (with no adjoint on the final state, the last tokens' gradients depend on
+    the earlier ones only through that state)."""
+    from concurrent.futures import ThreadPoolExecutor
+    dev = _dev()
+    vla = _vla()
+    cfg = gen.config(5).with_sizes(decode=0)
+    _say(f"backward workload {cfg.name} (full size, last tokens)")
+    x = gen.make_inputs(cfg)
+    B, H, T, d, m = cfg.B, cfg.H, cfg.T, cfg.d, 64
+    heads = [(0, 5), (1, 30)]
+    g = torch.Generator(device=dev).manual_seed(55)
+    dO = torch.randn((B, H, T, d), generator=g, device=dev)
+    dO_tail = {bh: dO[bh[0], bh[1], T - m:].cpu().numpy().astype(np.float64) for bh in heads}
+
+    def ref_head(bh):
+        b, h = bh
+        qkvu = [_f64(x[n][b, h], cfg.dtype) for n in "qkvu"]
+        st = oracle.forward_head(*(a[:T - m] for a in qkvu), cfg.lambda0, cfg.eps)
+        return oracle.backward_head(*(a[T - m:] for a in qkvu), dO_tail[bh], cfg.lambda0,
+                                    cfg.eps, st["S"], st["A"], st["zkey"])
+
+    with ThreadPoolExecutor(max_workers=len(heads)) as ex:
+        fut = ex.submit(lambda: list(map(ref_head, heads)))
+        t = {n: _to_dev(x[n], cfg.dtype, dev) for n in "qkvu"}
+        out = vla.vla_backward(t["q"], t["k"], t["v"], t["u"], dO, cfg.lambda0, cfg.eps)
+        torch.cuda.synchronize()
+        for n, o in zip(NAMES, out):
+            assert bool(torch.isfinite(o).all()), n
+        got = {bh: [o[bh[0], bh[1], T - m:].cpu().numpy() for o in out[:4]] for bh in heads}
+        refs = fut.result()
+    for bh, r in zip(heads, refs):
+        errs = {n: rel(gv, r[n]) for n, gv in zip(NAMES[:4], got[bh])}
+        _say(f"  head {bh}: " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+        for n, e in errs.items():
+            assert e <= GATE, f"{bh} {n}: {e:.3e} > {GATE}"
