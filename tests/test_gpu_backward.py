@@ -267,9 +267,13 @@ def test_backward_other_workloads_sampled_heads(cid, T, heads):
     _compare(cfg, x, adj, got, heads)
 
 
-def test_backward_long_context_last_tokens():
-    """The long-context workload at full size (B=2, H=32, d=128, T=65536, bf16
-    inputs): gradients of every head on the GPU, all finite; for sampled heads
+@pytest.mark.parametrize("cid,heads", [
+    (4, [(0, 0), (3, 31)]),     # MQAR-shaped recall workload: B=4, H=32, d=96, T=16384, fp32
+    (5, [(0, 5), (1, 30)]),     # long-context workload: B=2, H=32, d=128, T=65536, bf16
+])
+def test_backward_full_size_last_tokens(cid, heads):
+    """The recall and long-context workloads at full size: gradients of every
+    head on the GPU, all finite; for sampled heads
     the last 64 tokens' dq, dk, dv, du against the oracle's reverse mode over
     those tokens, started from its forward state after the first T - 64 tokens
     (with no adjoint on the final state, the last tokens' gradients depend on
@@ -277,12 +281,11 @@ def test_backward_long_context_last_tokens():
     from concurrent.futures import ThreadPoolExecutor
     dev = _dev()
     vla = _vla()
-    cfg = gen.config(5).with_sizes(decode=0)
+    cfg = gen.config(cid).with_sizes(decode=0)
     _say(f"backward workload {cfg.name} (full size, last tokens)")
     x = gen.make_inputs(cfg)
     B, H, T, d, m = cfg.B, cfg.H, cfg.T, cfg.d, 64
-    heads = [(0, 5), (1, 30)]
-    g = torch.Generator(device=dev).manual_seed(55)
+    g = torch.Generator(device=dev).manual_seed(50 + cid)
     dO = torch.randn((B, H, T, d), generator=g, device=dev)
     dO_tail = {bh: dO[bh[0], bh[1], T - m:].cpu().numpy().astype(np.float64) for bh in heads}
 
