@@ -18,7 +18,8 @@ head independence.  The gradients (``backward_head``) are pinned to central
 finite differences of the forward, entry by entry on tiny heads (with the
 denominator floor active and with zero keys and penalty vectors) and along
 random directions on larger ones, and to the first token's gradient worked by
-hand.  No function here is left unpinned.
+hand; ``backward_head_checkpointed`` (the same reverse mode split into
+segments) to ``backward_head``.  No function here is left unpinned.
 """
 from __future__ import annotations
 
@@ -169,6 +170,44 @@ def backward_head(q, k, v, u, dO, lambda0=0.1, eps=1e-4, S0=None, A0=None, zkey0
         _ptr(out["dS0"]), _ptr(out["dA0"]), _ptr(out["dzkey0"]))
     if rc != 0:
         raise ValueError(f"vla_oracle_backward failed with code {rc}")
+    return out
+
+
+def backward_head_checkpointed(q, k, v, u, dO, lambda0=0.1, eps=1e-4, S0=None, A0=None,
+                               zkey0=None, dS_T=None, dA_T=None, dzkey_T=None, seg=512):
+    """``backward_head`` for long sequences: the same gradients with memory of
+    order (T / seg + seg) d^2 doubles instead of 2 T d^2.
+
+    The forward runs once segment by segment (``seg`` tokens each), keeping only
+    the state (S, A, zkey) at each segment start; then the segments are taken in
+    reverse order, each by ``backward_head`` from its start state, with the
+    adjoints of its final state set to the initial-state gradients of the
+    segment after it.  The recurrence is the same token by token, so this is
+    the chain rule split at the segment boundaries.  (The gradient with respect
+    to A enters every step only through its symmetric part, so handing on the
+    symmetrised dA0 of a segment changes nothing.)"""
+    q = _f64(q)
+    T, d = q.shape
+    if T <= seg:
+        return backward_head(q, k, v, u, dO, lambda0, eps, S0, A0, zkey0, dS_T, dA_T, dzkey_T)
+    k, v, u, dO = _f64(k, (T, d)), _f64(v, (T, d)), _f64(u, (T, d)), _f64(dO, (T, d))
+    bounds = list(range(0, T, seg)) + [T]
+    starts = []
+    st = (S0, A0, zkey0)
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        starts.append(st)
+        r = forward_head(q[a:b], k[a:b], v[a:b], u[a:b], lambda0, eps, *st)
+        st = (r["S"], r["A"], r["zkey"])
+    out = dict(dq=np.zeros((T, d)), dk=np.zeros((T, d)), dv=np.zeros((T, d)),
+               du=np.zeros((T, d)))
+    adj = (dS_T, dA_T, dzkey_T)
+    for i in reversed(range(len(starts))):
+        a, b = bounds[i], bounds[i + 1]
+        r = backward_head(q[a:b], k[a:b], v[a:b], u[a:b], dO[a:b], lambda0, eps, *starts[i], *adj)
+        for n in ("dq", "dk", "dv", "du"):
+            out[n][a:b] = r[n]
+        adj = (r["dS0"], r["dA0"], r["dzkey0"])
+    out["dS0"], out["dA0"], out["dzkey0"] = adj
     return out
 
 

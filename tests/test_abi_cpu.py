@@ -254,3 +254,30 @@ def test_scan_argument_errors():
         assert vla.workspace_size(2, 3, T, 64) + maps <= got < vla.workspace_size(2, 3, T, 64) + maps + 512
     with pytest.raises(vla.VLAError):
         vla.scan_workspace_size(1, 1, 64, 96)
+
+
+def test_sequence_length_limit():
+    """The passes address a head's buffers (per-chunk records, per-token
+    records, inputs, o) with 32-bit byte offsets, so a sequence whose per-head
+    buffers would reach 2^31 bytes is VLA_ERR_UNSUPPORTED, before anything is
+    launched (a too small workspace shows that a length passed that check)."""
+    lib = B.load()
+    n = ctypes.c_size_t(0)
+    for d in (16, 32, 64, 96, 128):
+        over = (1 << 31) // (4 * d) + 1           # o alone reaches 2^31 bytes
+        assert _fwd(d=d, T=over) == B.VLA_ERR_UNSUPPORTED
+        assert _bwd(d=d, T=over) == B.VLA_ERR_UNSUPPORTED
+        assert lib.vla_forward_workspace_size(1, 1, over, d, ctypes.byref(n)) == \
+            B.VLA_ERR_UNSUPPORTED
+        # the gradients' per-token records: (4 d + 8) floats per token
+        over_keep = (1 << 31) // (4 * (4 * d + 8)) + 1
+        assert _bwd(d=d, T=over_keep) == B.VLA_ERR_UNSUPPORTED
+        assert lib.vla_backward_workspace_size(1, 1, over_keep, d, ctypes.byref(n)) == \
+            B.VLA_ERR_UNSUPPORTED
+    # long sequences well inside the limits pass the check
+    assert _fwd(d=128, T=1_000_000, ws_bytes=1024) == B.VLA_ERR_INVALID_ARG
+    assert _fwd(d=64, T=2_000_000, ws_bytes=1024) == B.VLA_ERR_INVALID_ARG
+    assert _bwd(d=128, T=1_000_000, ws_bytes=1024) == B.VLA_ERR_INVALID_ARG
+    assert _pen(d=128, T=1_000_000, ws_bytes=1024) == B.VLA_ERR_INVALID_ARG
+    assert _pen(d=128, T=5_000_000) == B.VLA_ERR_UNSUPPORTED
+    assert _mem(d=128, T=5_000_000) == B.VLA_ERR_UNSUPPORTED

@@ -3,7 +3,9 @@ fp64 reverse-mode oracle (itself pinned to finite differences of the forward)
 on the same seeded inputs and output adjoints.
 
 Gate, as for the forward: max|g_gpu - g_ref| / max|g_ref| <= 2e-3 for every
-gradient (dq, dk, dv, du and those of the initial state).
+gradient (dq, dk, dv, du and those of the initial state), and for the per-token
+gradients dq, dk, dv, du also max_t |g_gpu,t - g_ref,t| / |g_ref,t| <= 2e-3
+(tests/_parity.py).
 """
 import dataclasses
 from concurrent.futures import ThreadPoolExecutor
@@ -13,11 +15,11 @@ import pytest
 
 import gen
 import oracle
+from _parity import GATE, is_token_rows, rel, rel_rows
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-GATE = 2e-3
 NAMES = ("dq", "dk", "dv", "du", "dS0", "dA0", "dzkey0")
 
 
@@ -43,11 +45,6 @@ def _to_dev(x, dtype, dev):
 
 def _f64(x, dtype):
     return (gen.bf16_bits_to_f32(x) if dtype == "bf16" else x).astype(np.float64)
-
-
-def rel(g, r):
-    g = np.asarray(g, dtype=np.float64)
-    return float(np.abs(g - r).max() / max(np.abs(r).max(), 1e-30))
 
 
 def _adjoints(B, H, T, d, seed, state=True):
@@ -85,13 +82,18 @@ def _compare(cfg, x, adj, got, heads, init=None, gate=GATE):
         return bh, _oracle_head(cfg, x, adj, *bh, init=init)
     with ThreadPoolExecutor(max_workers=min(8, len(heads))) as ex:
         refs = dict(ex.map(one, heads))
-    worst = {}
+    worst, worst_tok = {}, {}
     for (b, h), r in refs.items():
         for n in NAMES:
             worst[n] = max(worst.get(n, 0.0), rel(got[n][b, h], r[n]))
+            if is_token_rows(n):
+                worst_tok[n] = max(worst_tok.get(n, 0.0), rel_rows(got[n][b, h], r[n])[0])
     _say("  " + "  ".join(f"{n} {e:.2e}" for n, e in worst.items()))
+    _say("  per token: " + "  ".join(f"{n} {e:.2e}" for n, e in worst_tok.items()))
     for n, e in worst.items():
         assert e <= gate, f"{n}: {e:.3e} > {gate}"
+    for n, e in worst_tok.items():
+        assert e <= gate, f"{n}: per-token {e:.3e} > {gate}"
 
 
 def _cfg(d, dtype, B, H, T):
@@ -267,46 +269,65 @@ def test_backward_other_workloads_sampled_heads(cid, T, heads):
     _compare(cfg, x, adj, got, heads)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("cid,heads", [
     (4, [(0, 0), (3, 31)]),     # MQAR-shaped recall workload: B=4, H=32, d=96, T=16384, fp32
     (5, [(0, 5), (1, 30)]),     # long-context workload: B=2, H=32, d=128, T=65536, bf16
 ])
-def test_backward_full_size_last_tokens(cid, heads):
+def test_backward_full_size(cid, heads):
     """The recall and long-context workloads at full size: gradients of every
-    head on the GPU, all finite; for sampled heads
-    the last 64 tokens' dq, dk, dv, du against the oracle's reverse mode over
-    those tokens, started from its forward state after the first T - 64 tokens
-    (with no adjoint on the final state, the last tokens' gradients depend on
-    the earlier ones only through that state)."""
+    head on the GPU, all finite.  The first sampled head is checked everywhere:
+    dq, dk, dv, du of every token and the initial state's gradients, against the
+    oracle's reverse mode over the whole sequence (checkpointed, so that it keeps
+    a few segments of per-token states instead of 2 T d^2 doubles).  For the
+    other heads the last 64 tokens' dq, dk, dv, du against the oracle's reverse
+    mode over those tokens, started from its forward state after the first
+    T - 64 tokens (with no adjoint on the final state, the last tokens'
+    gradients depend on the earlier ones only through that state)."""
     from concurrent.futures import ThreadPoolExecutor
     dev = _dev()
     vla = _vla()
     cfg = gen.config(cid).with_sizes(decode=0)
-    _say(f"backward workload {cfg.name} (full size, last tokens)")
+    _say(f"backward workload {cfg.name} (full size)")
     x = gen.make_inputs(cfg)
     B, H, T, d, m = cfg.B, cfg.H, cfg.T, cfg.d, 64
     g = torch.Generator(device=dev).manual_seed(50 + cid)
     dO = torch.randn((B, H, T, d), generator=g, device=dev)
-    dO_tail = {bh: dO[bh[0], bh[1], T - m:].cpu().numpy().astype(np.float64) for bh in heads}
+    dO_h = {bh: dO[bh[0], bh[1]].cpu().numpy().astype(np.float64) for bh in heads}
 
-    def ref_head(bh):
+    def ref_whole(bh):
+        b, h = bh
+        qkvu = [_f64(x[n][b, h], cfg.dtype) for n in "qkvu"]
+        return oracle.backward_head_checkpointed(*qkvu, dO_h[bh], cfg.lambda0, cfg.eps, seg=512)
+
+    def ref_tail(bh):
         b, h = bh
         qkvu = [_f64(x[n][b, h], cfg.dtype) for n in "qkvu"]
         st = oracle.forward_head(*(a[:T - m] for a in qkvu), cfg.lambda0, cfg.eps)
-        return oracle.backward_head(*(a[T - m:] for a in qkvu), dO_tail[bh], cfg.lambda0,
+        return oracle.backward_head(*(a[T - m:] for a in qkvu), dO_h[bh][T - m:], cfg.lambda0,
                                     cfg.eps, st["S"], st["A"], st["zkey"])
 
     with ThreadPoolExecutor(max_workers=len(heads)) as ex:
-        fut = ex.submit(lambda: list(map(ref_head, heads)))
+        futs = [ex.submit(ref_whole if i == 0 else ref_tail, bh) for i, bh in enumerate(heads)]
         t = {n: _to_dev(x[n], cfg.dtype, dev) for n in "qkvu"}
         out = vla.vla_backward(t["q"], t["k"], t["v"], t["u"], dO, cfg.lambda0, cfg.eps)
         torch.cuda.synchronize()
         for n, o in zip(NAMES, out):
             assert bool(torch.isfinite(o).all()), n
-        got = {bh: [o[bh[0], bh[1], T - m:].cpu().numpy() for o in out[:4]] for bh in heads}
-        refs = fut.result()
-    for bh, r in zip(heads, refs):
-        errs = {n: rel(gv, r[n]) for n, gv in zip(NAMES[:4], got[bh])}
-        _say(f"  head {bh}: " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()))
-        for n, e in errs.items():
-            assert e <= GATE, f"{bh} {n}: {e:.3e} > {GATE}"
+        got = {bh: [o[bh[0], bh[1]].cpu().numpy() for o in out] for bh in heads}
+        refs = [f.result() for f in futs]
+    for i, (bh, r) in enumerate(zip(heads, refs)):
+        if i == 0:
+            names, gv = NAMES, got[bh]
+            _say(f"  head {bh}, every token and the initial state:")
+        else:
+            names, gv = NAMES[:4], [a[T - m:] for a in got[bh][:4]]
+            _say(f"  head {bh}, last {m} tokens:")
+        errs = {n: rel(a, r[n]) for n, a in zip(names, gv)}
+        tok = {n: rel_rows(a, r[n]) for n, a in zip(names, gv) if is_token_rows(n)}
+        _say("   " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+        _say("   per token: " + "  ".join(f"{n} {e:.2e} at {at}" for n, (e, at) in tok.items()))
+        for n in errs:
+            assert errs[n] <= GATE, f"{bh} {n}: {errs[n]:.3e} > {GATE}"
+        for n, (e, _) in tok.items():
+            assert e <= GATE, f"{bh} {n}: per-token {e:.3e} > {GATE}"

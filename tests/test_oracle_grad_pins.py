@@ -172,3 +172,26 @@ def test_grad_heads_independent():
         one = oracle.backward_head(q[0, h], k[0, h], v[0, h], u[0, h], dO[0, h], LAMBDA0, EPS)
         for key in one:
             np.testing.assert_array_equal(res[key][0, h], one[key])
+
+
+@pytest.mark.parametrize("seg", [1, 7, 16, 60])
+def test_grad_checkpointed_equals_whole(seg):
+    """backward_head_checkpointed (segments of seg tokens, ragged last one)
+    gives backward_head's gradients, with a general initial state and adjoints
+    on every output; and along a random direction it matches central
+    differences of the forward by itself."""
+    x, adj = _case(50, 6, seed=51)
+    whole = _grads(x, adj)
+    ck = oracle.backward_head_checkpointed(x["q"], x["k"], x["v"], x["u"], adj["dO"], LAMBDA0,
+                                           EPS, x["S0"], x["A0"], x["zkey0"], adj["dS_T"],
+                                           adj["dA_T"], adj["dzkey_T"], seg=seg)
+    for n, g in whole.items():
+        np.testing.assert_allclose(ck[n], g, rtol=1e-11, atol=1e-12 * np.abs(g).max())
+    rng = np.random.default_rng(52)
+    r = {n: rng.standard_normal(a.shape) for n, a in x.items()}
+    r["A0"] = r["A0"] + r["A0"].T
+    h = 1e-6
+    fd = (_loss({n: x[n] + h * r[n] for n in x}, adj)
+          - _loss({n: x[n] - h * r[n] for n in x}, adj)) / (2 * h)
+    want = sum(np.sum(ck[GRAD_OF[n]] * r[n]) for n in x)
+    assert abs(fd - want) <= 1e-6 * max(1.0, abs(want)), (fd, want)
