@@ -15,6 +15,11 @@ do their d x d products on fp32 matrix cores, whose dense peak equals the FP32
 vector peak), the same for each of its two passes (penalty: Grams, segment
 inverses and the penalty chain; memory: the memory chain and readout), and the
 fp64 CPU oracle timed on the host cores over a bounded sample of heads.
+Beside it (key ``workloads``): the forward time and fraction of peak of every
+other workload (single head d_h = 16; 32 heads d_h = 64 T = 1024; the
+MQAR-shaped 128 heads d_h = 96 T = 16384; 64 heads d_h = 128 T = 65536 bf16)
+and the long-context workload's 4096-step ``vla_step`` continuation from its
+forward's final state, in microseconds per step and GB/s of state traffic.
 
 ``--backward`` prints the same kind of line for ``vla_backward`` (gradients of
 q, k, v, u and the initial state for a synthetic dL/do) on the same workload,
@@ -120,6 +125,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the oracle timing (e.g. under a profiler)")
+    p.add_argument("--headline-only", action="store_true",
+                   help="time only the headline workload (skip the other workloads and the "
+                        "decode continuation)")
     p.add_argument("--cpu-heads", type=int, default=0,
                    help="heads in the CPU-baseline sample (0 = every head of the workload)")
     p.add_argument("--scan", action="store_true",
@@ -329,37 +337,103 @@ def scan_bench(args):
     print(json.dumps(res), flush=True)
 
 
-def decode_bench(vla, torch, steps: int = 256):
-    """Single-token decode (vla_step) on the long-context decode shape: B=2,
-    H=32, d_h=128, bf16 inputs, state from a 64-token forward.  Each step reads
-    and writes the fp32 state (S, A: d^2 each, zkey: d) of every head."""
-    import gen
-    cfg = gen.config(5).with_sizes(T=64, decode=steps)
-    B, H, d = cfg.B, cfg.H, cfg.d
+def _time_forward(vla, torch, cfg, x, reps):
+    """Median and mean time of one vla_forward over the workload (events on the
+    launch stream, after a warm-up of at least SETTLE_S seconds); returns them
+    with the final state for a decode continuation."""
+    import numpy as np
+    B, H, T, d = cfg.B, cfg.H, cfg.T, cfg.d
     dev = torch.device("cuda:0")
-    x = gen.make_inputs(cfg)
-    t = {n: torch.from_numpy(x[n]).to(dev).view(torch.bfloat16) for n in x}
-    _, S, A, zk = vla.vla_forward(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps,
-                                  return_state=True)
-    dec = {n: t[n + "_dec"].permute(2, 0, 1, 3).contiguous() for n in "qkvu"}   # [steps,B,H,d]
-    o = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    t = {n: torch.from_numpy(x[n]).to(dev) for n in "qkvu"}
+    if cfg.dtype == "bf16":
+        t = {n: a.view(torch.bfloat16) for n, a in t.items()}
+    o = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    A = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    zk = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(vla.workspace_size(B, H, T, d), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    for i in range(8):
-        vla.vla_step(dec["q"][i], dec["k"][i], dec["v"][i], dec["u"][i], S, A, zk, cfg.eps,
-                     o=o, stream=stream)
+
+    def step():
+        vla.vla_forward(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps, o=o, S_out=S,
+                        A_out=A, zkey_out=zk, stream=stream, workspace=ws)
+    t_w, n_w = time.perf_counter(), 0
+    while n_w < 3 or time.perf_counter() - t_w < SETTLE_S:
+        step()
+        n_w += 1
+        torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    del t, o, ws
+    return float(np.median(ms)), float(np.mean(ms)), (S, A, zk)
+
+
+def _fwd_record(cfg, ms):
+    tok_heads = tok_heads_total(cfg)
+    tf = flops_per_token_head(cfg.d) * tok_heads / (ms / 1e3) / 1e12
+    return {"B": cfg.B, "H": cfg.H, "d_h": cfg.d, "T": cfg.T, "input_dtype": cfg.dtype,
+            "ms": ms, "tokens_heads_per_s": tok_heads / (ms / 1e3), "achieved_tflops": tf,
+            "frac": tf / FP32_VECTOR_PEAK_TFLOPS}
+
+
+def decode_continuation(vla, torch, cfg, x, state):
+    """cfg.decode single-token steps (vla_step) continuing from the forward's
+    final state, on the workload's decode tokens.  Each step reads and writes
+    the fp32 state (S, A: d^2 each, zkey: d) of every head and reads its four
+    input vectors; the state traffic is reported against the HBM peak."""
+    B, H, d, n = cfg.B, cfg.H, cfg.d, cfg.decode
+    dev = torch.device("cuda:0")
+    S, A, zk = (a.clone() for a in state)
+    dec = {}
+    for nm in "qkvu":
+        a = torch.from_numpy(x[nm + "_dec"]).to(dev)
+        a = a.view(torch.bfloat16) if cfg.dtype == "bf16" else a
+        dec[nm] = a.permute(2, 0, 1, 3).contiguous()   # [steps, B, H, d]
+    o = torch.empty((n, B, H, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(8):   # warm-up on scratch copies of the state
+        vla.vla_step(dec["q"][i], dec["k"][i], dec["v"][i], dec["u"][i], S.clone(), A.clone(),
+                     zk.clone(), cfg.eps, o=o[i], stream=stream)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for i in range(steps):
+    for i in range(n):
         vla.vla_step(dec["q"][i], dec["k"][i], dec["v"][i], dec["u"][i], S, A, zk, cfg.eps,
-                     o=o, stream=stream)
+                     o=o[i], stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
-    state_bytes = B * H * (2 * (2 * d * d + d) * 4 + 4 * d * 2 + d * 4)
-    return {"workload": "b2h32_d128_bf16 vla_step (one token for 64 heads)", "steps": steps,
+    us = e0.elapsed_time(e1) * 1e3 / n
+    s_in = 2 if cfg.dtype == "bf16" else 4
+    state_bytes = B * H * (2 * (2 * d * d + d) * 4 + 4 * d * s_in + d * 4)
+    gbps = state_bytes / (us * 1e-6) / 1e9
+    return {"steps": n, "from": f"the forward's final state after T={cfg.T}",
             "us_per_step": us, "tokens_heads_per_s": B * H / (us * 1e-6),
-            "state_bytes_per_step": state_bytes, "state_GBps": state_bytes / (us * 1e-6) / 1e9}
+            "bytes_per_step": state_bytes, "GBps": gbps, "hbm_frac": gbps / 8000.0}
+
+
+def other_workloads(vla, torch):
+    """Forward time of each workload other than the headline one (parity
+    cases, reported beside it), and the long-context workload's decode
+    continuation."""
+    import gen
+    out = {}
+    for cid, reps in ((1, 20), (2, 20), (4, 5), (5, 5)):
+        cfg = gen.config(cid)
+        x = gen.make_inputs(cfg)
+        med, _, state = _time_forward(vla, torch, cfg, x, reps)
+        rec = _fwd_record(cfg, med)
+        if cfg.decode:
+            rec["decode"] = decode_continuation(vla, torch, cfg, x, state)
+        out[cfg.name] = rec
+        del x, state
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -483,7 +557,8 @@ def main():
                                 "memory (vla_mem; S k^, S phi(q), S update)": phase(mem_ms)}},
         "device_peak": device_peak_tflops(),
     }
-    res["decode"] = decode_bench(vla, torch)
+    if not args.headline_only:
+        res["workloads"] = other_workloads(vla, torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)
     print(json.dumps(res), flush=True)

@@ -26,21 +26,21 @@ vla_status check_common(int in_dtype, int B, int H, int d_h, float eps)
 }
 
 // d_h in {64, 96, 128}: sequences (T >= 1) run on the two-pass matrix-core
-// kernels; a single decode token on the decode kernel and T = 0 on the
-// one-workgroup-per-head kernel (both read and write every state element from
-// the same lane, so the state may be updated in place).  d_h in {16, 32} uses
-// the LDS kernel.
+// kernels and a single decode token on the decode kernel (which reads and
+// writes every state element from the same lane, so the state is updated in
+// place); d_h in {16, 32} uses the LDS kernel for both.  T = 0 writes the
+// initial state to the outputs.
 vla_status launch(const vla::FwdArgs &a, bool step)
 {
     hipError_t e;
-    if (!vla::chunk_supported(a.d))
-        e = vla::launch_forward_ref(a);
-    else if (step)
-        e = vla::launch_step(a);
+    if (step)
+        e = vla::chunk_supported(a.d) ? vla::launch_step(a) : vla::launch_forward_ref(a);
     else if (a.T == 0)
-        e = vla::launch_forward_chunk(a);
-    else
+        e = vla::launch_state_init(a);
+    else if (vla::chunk_supported(a.d))
         e = vla::launch_forward_twopass(a, 3);
+    else
+        e = vla::launch_forward_ref(a);
     return e == hipSuccess ? VLA_OK : VLA_ERR_HIP;
 }
 
@@ -62,6 +62,7 @@ extern "C" vla_status vla_forward(const void *q, const void *k, const void *v, c
     vla_status st = check_common(in_dtype, B, H, d_h, eps);
     if (st != VLA_OK) return st;
     if (T < 0 || !finite_pos(lambda0)) return VLA_ERR_INVALID_ARG;
+    if (!vla::twopass_size_ok(T, d_h, false)) return VLA_ERR_UNSUPPORTED;
     const size_t need = ::workspace_bytes(B, H, T, d_h);
     if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need))
         return VLA_ERR_INVALID_ARG;
@@ -88,6 +89,7 @@ static vla_status check_phase(int in_dtype, int B, int H, int T, int d_h, float 
     if (st != VLA_OK) return st;
     if (!vla::chunk_supported(d_h)) return VLA_ERR_UNSUPPORTED;
     if (T < 1) return VLA_ERR_INVALID_ARG;
+    if (!vla::twopass_size_ok(T, d_h, false)) return VLA_ERR_UNSUPPORTED;
     const size_t need = ::workspace_bytes(B, H, T, d_h);
     if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need) return VLA_ERR_INVALID_ARG;
     return VLA_OK;
@@ -130,7 +132,7 @@ extern "C" vla_status vla_forward_memory(const void *q, const void *k, const voi
 extern "C" vla_status vla_forward_workspace_size(int B, int H, int T, int d_h, size_t *bytes)
 {
     if (!bytes || B < 1 || H < 1 || T < 0 || (long long)B * H > 0x7fffffffLL) return VLA_ERR_INVALID_ARG;
-    if (!supported_d(d_h)) return VLA_ERR_UNSUPPORTED;
+    if (!supported_d(d_h) || !vla::twopass_size_ok(T, d_h, false)) return VLA_ERR_UNSUPPORTED;
     *bytes = ::workspace_bytes(B, H, T, d_h);
     return VLA_OK;
 }
@@ -153,7 +155,7 @@ extern "C" vla_status vla_step(const void *q, const void *k, const void *v, cons
 extern "C" vla_status vla_forward_scan_workspace_size(int B, int H, int T, int d_h, size_t *bytes)
 {
     if (!bytes || B < 1 || H < 1 || T < 0 || (long long)B * H > 0x7fffffffLL) return VLA_ERR_INVALID_ARG;
-    if (d_h != 64) return VLA_ERR_UNSUPPORTED;
+    if (d_h != 64 || !vla::twopass_size_ok(T, d_h, false)) return VLA_ERR_UNSUPPORTED;
     *bytes = vla::scan_workspace_bytes(B * H, T, d_h);
     return VLA_OK;
 }
@@ -169,6 +171,7 @@ extern "C" vla_status vla_forward_scan(const void *q, const void *k, const void 
     if (st != VLA_OK) return st;
     if (d_h != 64) return VLA_ERR_UNSUPPORTED;
     if (T < 1 || !finite_pos(lambda0)) return VLA_ERR_INVALID_ARG;
+    if (!vla::twopass_size_ok(T, d_h, false)) return VLA_ERR_UNSUPPORTED;
     const size_t need = vla::scan_workspace_bytes(B * H, T, d_h);
     if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need) return VLA_ERR_INVALID_ARG;
     if (!ok_ptr(q, true) || !ok_ptr(k, true) || !ok_ptr(v, true) || !ok_ptr(u, true) ||
@@ -186,7 +189,7 @@ extern "C" vla_status vla_forward_scan(const void *q, const void *k, const void 
 extern "C" vla_status vla_backward_workspace_size(int B, int H, int T, int d_h, size_t *bytes)
 {
     if (!bytes || B < 1 || H < 1 || T < 0 || (long long)B * H > 0x7fffffffLL) return VLA_ERR_INVALID_ARG;
-    if (!supported_d(d_h)) return VLA_ERR_UNSUPPORTED;
+    if (!supported_d(d_h) || !vla::twopass_size_ok(T, d_h, true)) return VLA_ERR_UNSUPPORTED;
     *bytes = vla::backward_workspace_bytes(B * H, T, d_h);
     return VLA_OK;
 }
@@ -204,6 +207,7 @@ extern "C" vla_status vla_backward(const void *q, const void *k, const void *v, 
     vla_status st = check_common(in_dtype, B, H, d_h, eps);
     if (st != VLA_OK) return st;
     if (T < 0 || !finite_pos(lambda0)) return VLA_ERR_INVALID_ARG;
+    if (!vla::twopass_size_ok(T, d_h, true)) return VLA_ERR_UNSUPPORTED;
     const size_t need = vla::backward_workspace_bytes(B * H, T, d_h);
     if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need))
         return VLA_ERR_INVALID_ARG;

@@ -1,6 +1,6 @@
 // vla_chunk_parts.h -- device parts of the chunked matrix-core kernels of the
-// VLA recurrence (d_h in {64, 96, 128}): data layout, input staging and the two
-// chains.  The kernels in vla_chunk_kernel.hip only arrange them in time.
+// VLA recurrence (d_h in {64, 96, 128}): data layout and the steps of the two
+// chains.  The kernels of vla_twopass.hip arrange them in time.
 //
 // Source: "Variational Linear Attention" (arXiv 2605.11196), section 3.3,
 // Eqs. (9) (Sherman-Morrison downdate of A), (10) (gated delta write of S) and
@@ -44,16 +44,6 @@
 
 #include "vla_common.h"
 #include "vla_dpp_blocks.h"
-
-// Timing probes: VLA_PROBE(period, point) and VLA_PROBE_FLUSH() (at kernel
-// exit) expand to nothing unless a timing build defines them before including
-// this header.
-#ifndef VLA_PROBE
-#define VLA_PROBE(period, point)
-#endif
-#ifndef VLA_PROBE_FLUSH
-#define VLA_PROBE_FLUSH()
-#endif
 
 namespace vla {
 namespace chunk {
@@ -246,32 +236,9 @@ __device__ __forceinline__ constexpr int swz16(int i, int c4) { return 16 * i + 
 template <int D>
 __device__ __forceinline__ constexpr int swzd(int t, int c4) { return D * t + 4 * (c4 ^ (t & 7)); }
 
-// Everything a head keeps in LDS (every member a multiple of 16 bytes).
-template <int D>
-struct Lds {
-    static constexpr int C = Cfg<D>::C, NA = Cfg<D>::NA, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
-    static constexpr int UB = 2;   // buffers of u^ (by chunk parity)
-    static constexpr int ZKB = 1;  // buffers of the key sums
-    float uh[2][C * LD];     // u^   [token][i], by chunk parity
-    float kh[2][C * LD];     // k^
-    float ph[2][C * LD];     // phi(q)
-    float zk[C * LD];        // phi(k), then the key sum, of the chunk being staged
-    float rden[2][C];        // 1 / max(phi(q)' zkey, eps)
-    float z0[C * LD];        // Z0 [token][i]
-    float z0t[D * LT];       // Z0 [i][token]
-    float w[C * LD];         // W [token][i]
-    float wt[2][D * LT];     // W [i][token], by chunk parity
-    float gp[NA][2][C * LT]; // per A-wave: I + U^'Z0 (wave 0) or U^'Z0, and Z0'K^
-    float nrm[NA][C];        // per A-wave: partial |w_t|^2
-    float nq[NA][2][C * LT]; // per S-wave: Alpha^'K^, Alpha^'Phi
-    float lit[NA][C * LT];   // per A-wave: L^-1 transposed
-    float inv[NA][C];        // per A-wave: 1 / d_j
-    float tit[NA][C * LT];   // per S-wave: (I+N)^-1 transposed
-};
-
 // Where the penalty chain leaves W' (token- and key-major) and the |w|^2
 // partials of a chunk: in LDS.
-template <int D, typename LdsT = Lds<D>>
+template <int D, typename LdsT>
 struct WToLds {
     LdsT &L;
     int sp, g, n;
@@ -289,43 +256,27 @@ struct WToLds {
     // 1/delta_t: nothing to do here (a sink that keeps them overrides this)
     __device__ __forceinline__ void zcols(int, f4, f4) {}
 };
-// Per-thread view of one head: lane coordinates, input pointers and the two
-// chains' steps.  A wave with chain index wi owns column blocks wi*BPW + bb.
-template <int D, typename Tin, typename LdsT = Lds<D>>
+// Per-thread view of one head's penalty chain: lane coordinates and the steps.
+// A wave with chain index wi owns column blocks wi*BPW + bb; LdsT is the
+// workgroup's LDS layout (members uh, kh, ph, zk, z0, z0t, w, wt, gp, nrm, nq,
+// lit/tit, inv, hms).
+template <int D, typename LdsT>
 struct Head {
     using Cf = Cfg<D>;
     static constexpr int C = Cf::C, NB = Cf::NB, NA = Cf::NA, BPW = Cf::BPW;
-    static constexpr int LD = Cf::LD, LT = Cf::LT, CPT = Cf::CPT;
+    static constexpr int LD = Cf::LD, LT = Cf::LT;
     typedef f4 State[BPW][NB];
 
     LdsT &L;
-    const Tin *q, *k, *v, *u;
-    float *o;
-    int T;
-    float eps;
-    size_t tok0;     // first token row of the head
-    int g, n, wi;    // lane group, lane in group, wave index within its chain
-    // staging: 16 threads per token (one DPP row), token tl, columns [cc*CPT, +CPT)
-    int ts, tl, cc;
-    bool pthr;
+    int g, n, wi;                       // lane group, lane in group, wave index within the chain
     int kcol;                           // key-sum column of this thread, or -1
     float zk_run = 0.f, zk_cmp = 0.f;   // its Kahan-compensated key sum
-    int pp = 0;                         // current period (timing probes only)
-    RawVec<Tin, CPT> rq, rk, ru;
 
     // phi(k), then the key sums, of chunk cq
-    __device__ __forceinline__ float *zkb(int cq) const
-    {
-        if constexpr (LdsT::ZKB == 2) return L.zk[cq & 1];
-        else return L.zk;
-    }
+    __device__ __forceinline__ float *zkb(int cq) const { return L.zk[cq & 1]; }
 
-    __device__ __forceinline__ Head(LdsT &L_, const Tin *q_, const Tin *k_, const Tin *v_,
-                                    const Tin *u_, float *o_, int T_, float eps_, size_t bh,
-                                    int lane, int wi_, int ts_, bool stager, int kcol_)
-        : L(L_), q(q_), k(k_), v(v_), u(u_), o(o_), T(T_), eps(eps_), tok0(bh * (size_t)T_),
-          g(lane >> 4), n(lane & 15), wi(wi_), ts(ts_), tl((ts_ >> 4) & (C - 1)), cc(ts_ & 15),
-          pthr(stager && ts_ >= 0 && ts_ < 16 * C), kcol(kcol_ >= 0 && kcol_ < D ? kcol_ : -1)
+    __device__ __forceinline__ Head(LdsT &L_, int lane, int wi_, int kcol_)
+        : L(L_), g(lane >> 4), n(lane & 15), wi(wi_), kcol(kcol_ >= 0 && kcol_ < D ? kcol_ : -1)
     {
     }
 
@@ -355,51 +306,6 @@ struct Head {
         });
     }
 
-    // ------------------------------------------------------------ staging
-    // raw inputs of chunk cq into registers (rows past T re-read row T-1; stage1
-    // zeroes them).  WQ: q (memory chain), WU: u (penalty chain); k always.
-    template <bool WQ, bool WU>
-    __device__ __forceinline__ void prefetch(int cq)
-    {
-        if (!pthr) return;
-        const int t = cq * C + tl;
-        const size_t off = (tok0 + (size_t)(t < T ? t : T - 1)) * D + (size_t)cc * CPT;
-        if constexpr (WQ) rq.load(q + off);
-        rk.load(k + off);
-        if constexpr (WU) ru.load(u + off);
-    }
-    // k^ (and u^, or phi(q) and phi(k)) of chunk cq into its LDS slot
-    template <bool WQ, bool WU>
-    __device__ __forceinline__ void stage1(int cq)
-    {
-        if (!pthr) return;
-        const int slot = cq & 1;
-        float *zk = zkb(cq);
-        const bool ok = cq * C + tl < T;
-        float pk = 0.f, pu = 0.f;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            pk = fmaf(rk.get(i), rk.get(i), pk);
-            if constexpr (WU) pu = fmaf(ru.get(i), ru.get(i), pu);
-        }
-        const float nk = sum_row16(pk);
-        const float ik = ok && nk > 0.f ? rsqrtf(nk) : 0.f;
-        float iu = 0.f;
-        if constexpr (WU) {
-            const float nu = sum_row16(pu);
-            iu = ok && nu > 0.f ? rsqrtf(nu) : 0.f;
-        }
-        const int e0 = tl * LD + cc * CPT;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            L.kh[slot][e0 + i] = rk.get(i) * ik;
-            if constexpr (WU) L.uh[slot % LdsT::UB][e0 + i] = ru.get(i) * iu;
-            if constexpr (WQ) {
-                L.ph[slot][e0 + i] = phi_fast(rq.get(i));
-                zk[e0 + i] = ok ? phi_fast(rk.get(i)) : 0.f;
-            }
-        }
-    }
     // inclusive key sum per column: prefix inside the chunk, added to the
     // compensated sum of the earlier chunks
     __device__ __forceinline__ void stage2(int cq)
@@ -420,31 +326,6 @@ struct Head {
         zk_cmp = (tsum - zk_run) - yk;
         zk_run = tsum;
     }
-    // readout denominators of chunk cq
-    __device__ __forceinline__ void stage3(int cq)
-    {
-        if (!pthr) return;
-        const int slot = cq & 1;
-        const float *zk = zkb(cq);
-        const int e0 = tl * LD + cc * CPT;
-        float pd = 0.f;
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) pd = fmaf(L.ph[slot][e0 + i], zk[e0 + i], pd);
-        pd = sum_row16(pd);
-        if (cc == 0) L.rden[slot][tl] = __builtin_amdgcn_rcpf(fmaxf(pd, eps));
-    }
-    // V' rows 4g+r of chunk cq (own blocks), kept as loaded
-    __device__ __forceinline__ void load_v(int cq, Raw1<Tin> (&vraw)[BPW][4]) const
-    {
-        sfor<BPW>([&](auto bb) {
-            const int b = wi * BPW + bb;
-            sfor<4>([&](auto r) {
-                const int t = min(cq * C + 4 * g + r, T - 1);
-                vraw[bb][r].load(v, (tok0 + t) * D + 16 * b + n);
-            });
-        });
-    }
-
     // ------------------------------------------------------------ penalty chain
     // Z0' of the own blocks, Z0 into LDS, and this wave's partials (rows i of its
     // blocks) of U^'Z0 and of U^'A K^ = Z0'K^ (A symmetric), so that the product
@@ -453,7 +334,7 @@ struct Head {
     {
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
         const int sp = p & 1;
-        const float *ub = L.uh[sp % LdsT::UB], *kb = L.kh[sp];
+        const float *ub = L.uh[0], *kb = L.kh[sp];
         f4 z[BPW];
         sfor<BPW>([&](auto bb) { z[bb] = zero; });
         sfor<NB>([&](auto rho) {
@@ -486,119 +367,11 @@ struct Head {
     }
 
     // Factorise I + G, downdate the own blocks of As, and hand W' and the |w|^2
-    // partials of the chunk to `wout`.  The product Y0' = (A K^)' with the state
-    // before the downdate is issued between the factorisation steps.
-    template <class WOut>
-    __device__ __forceinline__ void a_update(State &st, int p, WOut &&wout)
-    {
-        const f4 zero = {0.f, 0.f, 0.f, 0.f};
-        constexpr int KS = 4 * NB;   // k-steps of the Y0 product
-        const float *kb = L.kh[p & 1];
-        f4 ak[NB], y[BPW];
-        sfor<NB>([&](auto rho) { ak[rho] = ld4(&kb[n * LD + 16 * rho + 4 * g]); });
-        sfor<BPW>([&](auto bb) { y[bb] = zero; });
-        // M = I + G summed over the waves' partials in accumulator layout (entry
-        // [4g+r][n]), then row n of M in every lane group through this wave's LDS
-        // scratch; B operand of U^'Y0
-        float Mr[16], gub[4];
-        sfor<4>([&](auto r) {
-            float a = L.gp[0][0][(4 * g + r) * LT + n];
-            sfor<NA - 1>([&](auto w2) { a += L.gp[w2 + 1][0][(4 * g + r) * LT + n]; });
-            L.lit[wi][(4 * g + r) * LT + n] = a;
-        });
-        sfor<4>([&](auto c) {
-            float a = L.gp[0][1][(4 * c + g) * LT + n];
-            sfor<NA - 1>([&](auto w2) { a += L.gp[w2 + 1][1][(4 * c + g) * LT + n]; });
-            gub[c] = a;
-        });
-        wave_lds_order();
-        sfor<4>([&](auto q4) {
-            const f4 a = ld4(&L.lit[wi][n * LT + 4 * q4]);
-            sfor<4>([&](auto r) { Mr[4 * q4 + r] = a[int(r)]; });
-        });
-        wave_lds_order();
-        VLA_PROBE(pp, 5);
-        // LDL' (column by column, Crout order): lane n holds row n.  LDr[j] =
-        // L[n][j] d_j (d_j in lane j), NLr[j] = -L[n][j] for n > j, 0 otherwise;
-        // 1/d_j to LDS.  Column j+1's terms k < j are issued around the inversion
-        // of pivot j (software pipelining); only its k = j term waits for it.
-        float LDr[16], NLr[16];
-        float ca = Mr[0], cb = 0.f;   // accumulators of the current column
-        float invn = 0.f;
-        sfor<16>([&](auto jj) {
-            constexpr int j = decltype(jj)::value;
-            if constexpr (j > 0) ldl_block<j, j - 1, 1>(ca, LDr, NLr);
-            const float acc = ca + cb;
-            const float inv = rcp_bcast<j>(acc);
-            // column j+1's terms k < j: two while 1/d_j is in flight, the rest
-            // after NLr[j] is formed
-            constexpr int E = j, E1 = E < 2 ? E : 2;
-            float na = 0.f, nb = 0.f;
-            if constexpr (j + 1 < 16) {
-                na = Mr[j + 1];
-                if constexpr (E1 > 0) ldl_early<j + 1, 0, E1>(na, nb, LDr, NLr);
-            }
-            LDr[j] = acc;
-            NLr[j] = n > j ? -(acc * inv) : 0.f;
-            invn = n == j ? inv : invn;   // lane n keeps 1 / d_n
-            if constexpr (j + 1 < 16 && E > E1) ldl_early<j + 1, E1, E - E1>(na, nb, LDr, NLr);
-            ca = na;
-            cb = nb;
-            sfor<(j + 1) * KS / 16 - j * KS / 16>([&](auto kk) {   // a share of Y0'
-                constexpr int ks = j * KS / 16 + decltype(kk)::value;
-                sfor<BPW>([&](auto bb) { y[bb] = mma(ak[ks / 4][ks % 4], st[bb][ks / 4][ks % 4], y[bb]); });
-            });
-        });
-        L.inv[wi][n] = invn;   // every lane group holds the same values
-        VLA_PROBE(pp, 6);
-        // L^-1 by forward substitution, four columns at a time: lane group g
-        // computes column 4c + g in X[c] (lane n = row n).
-        float X[4];
-        sfor<4>([&](auto c) { X[c] = n == 4 * c + g ? 1.f : 0.f; });
-        asm volatile(VLA_LINV_BLOCK
-                     : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3])
-                     : "v"(NLr[0]), "v"(NLr[1]), "v"(NLr[2]), "v"(NLr[3]), "v"(NLr[4]),
-                       "v"(NLr[5]), "v"(NLr[6]), "v"(NLr[7]), "v"(NLr[8]), "v"(NLr[9]),
-                       "v"(NLr[10]), "v"(NLr[11]), "v"(NLr[12]), "v"(NLr[13]), "v"(NLr[14]));
-        VLA_PROBE(pp, 7);
-        sfor<4>([&](auto c) { L.lit[wi][(4 * c + g) * LT + n] = X[c]; });
-        wave_lds_order();
-        const f4 inv4 = ld4(&L.inv[wi][4 * g]);        // 1 / d_{4g+r}
-        const f4 lit = ld4(&L.lit[wi][n * LT + 4 * g]);  // L^-1 [4g+r][n]
-        // -(D^-1 L^-1 U^'Y0 o Up): A operand of W'
-        f4 hm = mma4(X, gub, zero);
-        sfor<4>([&](auto r) { hm[int(r)] = 4 * g + r <= n ? -(hm[int(r)] * inv4[int(r)]) : 0.f; });
-        VLA_PROBE(pp, 8);
-        f4 nr = zero;
-        sfor<BPW>([&](auto bb) {
-            const int b = wi * BPW + bb;
-            float zb[4];   // Z0'[4c+g][16b+n]
-            sfor<4>([&](auto c) { zb[c] = L.z0[(4 * c + g) * LD + 16 * b + n]; });
-            const f4 q2 = mma4(X, zb, zero);        // L^-1 Z0'
-            const f4 q1 = q2 * inv4;                // D^-1 L^-1 Z0'
-            const f4 xt = mma4(lit, q1, zero);      // (I + G)^-1 Z0' = L^-T D^-1 L^-1 Z0'
-            // W' = Y0' - ((D^-1 L^-1 U^'Y0) o Up)' L^-1 Z0'
-            const f4 wt = mma4(hm, q2, y[bb]);
-            const f4 nx = -xt;
-            f4 az[NB];
-            sfor<NB>([&](auto rho) { az[rho] = ld4(&L.z0t[(16 * rho + n) * LT + 4 * g]); });
-            sfor<4>([&](auto r) {      // As <- As - Z0 (I + G)^-1 Z0'
-                sfor<NB>([&](auto rho) { st[bb][rho] = mma(az[rho][int(r)], nx[int(r)], st[bb][rho]); });
-            });
-            wout.block(b, wt);
-            nr += wt * wt;
-        });
-        VLA_PROBE(pp, 9);
-        sfor<4>([&](auto r) { nr[int(r)] = sum_row16(nr[int(r)]); });
-        wout.norms(wi, nr);
-    }
-
-    // a_update with the 16 x 16 factorisation done once per workgroup (for
-    // workgroups whose waves run only the penalty chain, where the four copies
-    // would cost issue slots rather than hide latency): wave 0 factorises I + G
-    // and leaves L^-1 (transposed), 1/d and the A operand of W' in LDS (its own
-    // scratch, L.hms), while every wave forms Y0' of its blocks; then, after a
-    // workgroup barrier, each wave downdates its blocks and forms W'.
+    // partials of the chunk to `wout`.  The 16 x 16 factorisation is done once
+    // per workgroup: wave 0 factorises I + G and leaves L^-1 (transposed), 1/d
+    // and the A operand of W' in LDS (L.hms), while every wave forms Y0' of its
+    // blocks and then runs `side` (work off the chain); after a workgroup
+    // barrier, each wave downdates its blocks and forms W'.
     template <class WOut, class Side>
     __device__ __forceinline__ void a_update_shared(State &st, int p, WOut &&wout, Side &&side)
     {
@@ -630,7 +403,11 @@ struct Head {
                 sfor<4>([&](auto r) { Mr[4 * q4 + r] = a[int(r)]; });
             });
             wave_lds_order();
-            // LDL' as in a_update
+            // LDL' (column by column, Crout order): lane n holds row n.  LDr[j] =
+            // L[n][j] d_j (d_j in lane j), NLr[j] = -L[n][j] for n > j, 0
+            // otherwise; 1/d_j to LDS.  Column j+1's terms k < j are issued
+            // around the inversion of pivot j (software pipelining); only its
+            // k = j term waits for it.
             float LDr[16], NLr[16];
             float ca = Mr[0], cb = 0.f;
             float invn = 0.f;
@@ -697,25 +474,6 @@ struct Head {
         wout.norms(wi, nr);
     }
 
-    // ------------------------------------------------------------ memory chain
-    // S K^ and S Phi of chunk cq (own blocks), before its write
-    __device__ __forceinline__ void s_products(const State &st, int cq, f4 (&sk)[BPW], f4 (&sq)[BPW]) const
-    {
-        const f4 zero = {0.f, 0.f, 0.f, 0.f};
-        const int sl = cq & 1;
-        const float *kb = L.kh[sl], *pb = L.ph[sl];
-        sfor<BPW>([&](auto bb) { sk[bb] = zero; sq[bb] = zero; });
-        sfor<NB>([&](auto rho) {
-            const f4 ak = ld4(&kb[n * LD + 16 * rho + 4 * g]);
-            const f4 ap = ld4(&pb[n * LD + 16 * rho + 4 * g]);
-            sfor<4>([&](auto r) {
-                sfor<BPW>([&](auto bb) {
-                    sk[bb] = mma(ak[int(r)], st[bb][rho][int(r)], sk[bb]);
-                    sq[bb] = mma(ap[int(r)], st[bb][rho][int(r)], sq[bb]);
-                });
-            });
-        });
-    }
     // 1/|w_t| of chunk cq and this wave's partials of Alpha^'K^, Alpha^'Phi
     // (from W in L.w and the |w|^2 partials in L.nrm)
     __device__ __forceinline__ void s_grams(int cq, f4 &invn4)
@@ -780,69 +538,6 @@ struct Head {
         sfor<4>([&](auto c) { tt[swz16(4 * c + g, n >> 2) + (n & 3)] = X[c]; });   // column 4c+g of (I+N)^-1
     }
 
-    // (I + N)^-1, the errors E, the readout o of chunk cq and the write of S
-    // (W [i][token] of the chunk at wtb)
-    __device__ __forceinline__ void s_update(State &st, int cq, const f4 (&sk)[BPW], const f4 (&sq)[BPW],
-                                             f4 invn4, const Raw1<Tin> (&vraw)[BPW][4], const float *wtb)
-    {
-        const f4 zero = {0.f, 0.f, 0.f, 0.f};
-        const int sl = cq & 1;
-        const int t0 = cq * C;
-        // row n of -N (strictly upper) in every lane group; A operand of the
-        // readout: (Alpha^'Phi o Up)[4g+r][n]
-        float NNr[16];
-        f4 qa;
-        sfor<4>([&](auto r) {   // -N[4g+r][n] (strictly upper), then rows through LDS
-            float a = L.nq[0][0][(4 * g + r) * LT + n];
-            sfor<NA - 1>([&](auto w2) { a += L.nq[w2 + 1][0][(4 * g + r) * LT + n]; });
-            L.tit[wi][(4 * g + r) * LT + n] = 4 * g + r < n ? -a : 0.f;
-        });
-        wave_lds_order();
-        sfor<4>([&](auto q4) {
-            const f4 a = ld4(&L.tit[wi][n * LT + 4 * q4]);
-            sfor<4>([&](auto r) { NNr[4 * q4 + r] = a[int(r)]; });
-        });
-        wave_lds_order();
-        sfor<4>([&](auto r) {
-            float a = L.nq[0][1][(4 * g + r) * LT + n];
-            sfor<NA - 1>([&](auto w2) { a += L.nq[w2 + 1][1][(4 * g + r) * LT + n]; });
-            qa[int(r)] = 4 * g + r <= n ? a : 0.f;
-        });
-        VLA_PROBE(pp, 5);
-        // (I + N)^-1 by back substitution, four columns at a time: lane group
-        // g computes column 4c + g in X[c] (lane n = row n).
-        float X[4];
-        sfor<4>([&](auto c) { X[c] = n == 4 * c + g ? 1.f : 0.f; });
-        asm volatile(VLA_TINV_BLOCK
-                     : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3])
-                     : "v"(NNr[1]), "v"(NNr[2]), "v"(NNr[3]), "v"(NNr[4]), "v"(NNr[5]),
-                       "v"(NNr[6]), "v"(NNr[7]), "v"(NNr[8]), "v"(NNr[9]), "v"(NNr[10]),
-                       "v"(NNr[11]), "v"(NNr[12]), "v"(NNr[13]), "v"(NNr[14]), "v"(NNr[15]));
-        VLA_PROBE(pp, 6);
-        sfor<4>([&](auto c) { L.tit[wi][(4 * c + g) * LT + n] = X[c]; });
-        wave_lds_order();
-        const f4 ta = ld4(&L.tit[wi][n * LT + 4 * g]);   // (I+N)^-1 [4g+r][n]
-        const f4 rd = ld4(&L.rden[sl][4 * g]);
-        sfor<BPW>([&](auto bb) {
-            const int b = wi * BPW + bb;
-            f4 vm;                           // (V - S K^)' rows 4g+r
-            sfor<4>([&](auto r) {
-                vm[int(r)] = (t0 + 4 * g + r < T ? vraw[bb][r].get() : 0.f) - sk[bb][int(r)];
-            });
-            const f4 e = mma4(ta, vm, zero);      // E' = (I+N)^-T (V - S K^)'
-            const f4 ob = mma4(qa, e, sq[bb]);    // (S_t phi(q_t))'
-            sfor<4>([&](auto r) {
-                const int t = t0 + 4 * g + r;
-                if (t < T) o[(tok0 + t) * D + 16 * b + n] = ob[int(r)] * rd[int(r)];
-            });
-            const f4 es = e * invn4;              // rows of (E diag(1/|w|))'
-            f4 aw[NB];
-            sfor<NB>([&](auto rho) { aw[rho] = ld4(&wtb[(16 * rho + n) * LT + 4 * g]); });
-            sfor<4>([&](auto r) {                 // Ss <- Ss + W diag(1/|w|) E'
-                sfor<NB>([&](auto rho) { st[bb][rho] = mma(aw[rho][int(r)], es[int(r)], st[bb][rho]); });
-            });
-        });
-    }
 };
 
 }  // namespace chunk

@@ -36,16 +36,20 @@ __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : expf(
 
 hipError_t launch_forward_ref(const FwdArgs &a);
 
+// T = 0: the initial state (given, or the defaults) to the requested outputs
+hipError_t launch_state_init(const FwdArgs &a);
+
 // Chunked matrix-core kernels (d_h in {64, 96, 128}).
 bool chunk_supported(int d);
-// one workgroup per head with both chains (decode steps and T = 0)
-hipError_t launch_forward_chunk(const FwdArgs &a);
 // one decode token, state in place (a.T == 1; S_out, A_out, zk_out are the state)
 hipError_t launch_step(const FwdArgs &a);
 // two passes over the sequence (forward, T >= 1); needs the workspace below.
 // phases: 1 = penalty pass (Grams, segment inverses, penalty chain and the
 // per-chunk factors in the workspace), 2 = memory pass, 3 = both.
 size_t twopass_workspace_bytes(int BH, int T, int d);
+// whether every per-head buffer of the forward (and, with keep, of the
+// gradients' per-token records) stays below 2^31 bytes at this T
+bool twopass_size_ok(int T, int d, bool keep);
 // byte offset of the per-chunk records (vla_record.h) in that workspace; the
 // record of chunk c of head bh is at index bh * ceil(T / 16) + c
 size_t twopass_records_offset(int BH, int T, int d);

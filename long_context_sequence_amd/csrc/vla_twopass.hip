@@ -368,13 +368,11 @@ vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
 }
 
 // ------------------------------------------------------------------- penalty
-// LDS of a penalty workgroup: the members of Lds<D> its steps use, with a single
-// buffer where the schedule below allows one.
+// LDS of a penalty workgroup (the members the steps of Head use; u^ has a single
+// buffer, since it is read before the next chunk is staged).
 template <int D>
 struct PLds {
     static constexpr int C = Cfg<D>::C, NA = Cfg<D>::NA, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
-    static constexpr int UB = 1;
-    static constexpr int ZKB = 2;
     float uh[1][C * LD];     // u^ [token][i] (read before the next chunk is staged)
     float kh[2][C * LD];     // k^, by chunk parity
     float ph[2][C * LD];     // phi(q), by chunk parity
@@ -545,7 +543,7 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         const float *A0, const float *zk0, const float *aseg, const float *zseg,
         float *__restrict__ rec, float *A_out, float *zk_out, float *kept_all = nullptr)
 {
-    using Hd = Head<D, Tin, PLds<D>>;
+    using Hd = Head<D, PLds<D>>;
     constexpr int BPW = Cfg<D>::BPW, LT = Cfg<D>::LT, RS = Rec<D>::SIZE, NA = Cfg<D>::NA;
     __shared__ __align__(16) PLds<D> L;
 
@@ -559,7 +557,7 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     // serial work spread over the waves: wave 0 factorises I + G, wave 1 forms
     // the C x C factors of the record, the waves from 2 on own the key sums, and
     // the last two waves stage the inputs
-    Hd hd(L, q, k, nullptr, u, nullptr, T, eps, bh, tid & 63, w, tid, false, tid - 128);
+    Hd hd(L, tid & 63, w, tid - 128);
     PenStage<D, Tin, SAVE> ps(tid - 64 * (NA - 2));
     float *kept = SAVE ? kept_all + (size_t)bh * T * Keep<D>::RS : nullptr;
     typename Hd::State st;
@@ -1032,6 +1030,29 @@ hipError_t launch(const FwdArgs &a, int phases)
 }
 
 }  // namespace
+
+bool chunk_supported(int d) { return d == 64 || d == 96 || d == 128; }
+
+// The passes address a head's records, per-token records, inputs and o with
+// 32-bit byte offsets (buffer resources); each must stay below 2^31 bytes.
+template <int D>
+static bool fits(long long T, bool keep)
+{
+    const long long lim = 1LL << 31, NC = (T + CH - 1) / CH;
+    if (NC * Rec<D>::SIZE * 4 >= lim || T * D * 4 >= lim) return false;
+    return !keep || T * Keep<D>::RS * 4 < lim;
+}
+
+bool twopass_size_ok(int T, int d, bool keep)
+{
+    switch (d) {
+    case 64: return fits<64>(T, keep);
+    case 96: return fits<96>(T, keep);
+    case 128: return fits<128>(T, keep);
+    default: return (long long)T * d * 4 < (1LL << 31) &&
+                    (!keep || (long long)T * (4 * d + 8) * 4 < (1LL << 31));
+    }
+}
 
 size_t twopass_workspace_bytes(int BH, int T, int d)
 {
