@@ -190,27 +190,37 @@ template <> struct Raw1<uint16_t> {
     __device__ __forceinline__ float get() const { return __uint_as_float(x << 16); }
 };
 
-// CPT consecutive inputs of one token, held in registers.
-template <typename Tin, int N> struct RawVec;
-template <int N> struct RawVec<float, N> {   // N even; 8-byte aligned
-    float2 x[N / 2];
-    __device__ __forceinline__ void load(const float *p)
+// N consecutive inputs of one token, held in registers as loaded (bf16 stays a
+// bit pattern), fetched with the widest loads the row offset allows: the
+// offset is a multiple of N elements, so a group of V elements with
+// N % V == 0 and V * sizeof <= 16 is aligned to its own size.
+template <typename Tin, int N>
+struct RawVec {
+    static constexpr int ES = (int)sizeof(Tin);
+    static constexpr int V = (N % 8 == 0 && 8 * ES <= 16) ? 8
+                           : (N % 4 == 0 && 4 * ES <= 16) ? 4 : 2;   // elements per load
+    static constexpr int NW = N * ES / 4;                              // 32-bit words
+    static constexpr int WPL = V * ES / 4;                             // words per load
+    uint32_t x[NW];
+    __device__ __forceinline__ void load(const Tin *p)
     {
-#pragma unroll
-        for (int i = 0; i < N / 2; ++i) x[i] = reinterpret_cast<const float2 *>(p)[i];
-    }
-    __device__ __forceinline__ float get(int i) const { return (i & 1) ? x[i >> 1].y : x[i >> 1].x; }
-};
-template <int N> struct RawVec<uint16_t, N> {   // N even; 4-byte aligned
-    uint32_t x[N / 2];
-    __device__ __forceinline__ void load(const uint16_t *p)
-    {
-#pragma unroll
-        for (int i = 0; i < N / 2; ++i) x[i] = reinterpret_cast<const uint32_t *>(p)[i];
+        static_assert(N % 2 == 0 && NW % WPL == 0, "whole loads");
+        sfor<NW / WPL>([&](auto i) {
+            if constexpr (WPL == 4) {
+                const uint4 v = reinterpret_cast<const uint4 *>(p)[i];
+                x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+            } else if constexpr (WPL == 2) {
+                const uint2 v = reinterpret_cast<const uint2 *>(p)[i];
+                x[2 * i] = v.x; x[2 * i + 1] = v.y;
+            } else {
+                x[i] = reinterpret_cast<const uint32_t *>(p)[i];
+            }
+        });
     }
     __device__ __forceinline__ float get(int i) const
     {
-        return (i & 1) ? bf16_hi(x[i >> 1]) : bf16_lo(x[i >> 1]);
+        if constexpr (ES == 4) return __uint_as_float(x[i]);
+        else return (i & 1) ? bf16_hi(x[i >> 1]) : bf16_lo(x[i >> 1]);
     }
 };
 
@@ -236,17 +246,16 @@ __device__ __forceinline__ constexpr int swz16(int i, int c4) { return 16 * i + 
 template <int D>
 __device__ __forceinline__ constexpr int swzd(int t, int c4) { return D * t + 4 * (c4 ^ (t & 7)); }
 
-// Where the penalty chain leaves W' (token- and key-major) and the |w|^2
+// Where the penalty chain leaves W' (key-major: W[i][token]) and the |w|^2
 // partials of a chunk: in LDS.
 template <int D, typename LdsT>
 struct WToLds {
     LdsT &L;
-    int sp, g, n;
+    int g, n;
     __device__ __forceinline__ void block(int b, f4 wt)
     {
-        constexpr int LD = Cfg<D>::LD, LT = Cfg<D>::LT;
-        sfor<4>([&](auto r) { L.w[(4 * g + r) * LD + 16 * b + n] = wt[int(r)]; });
-        st4(&L.wt[sp][(16 * b + n) * LT + 4 * g], wt);
+        constexpr int LT = Cfg<D>::LT;
+        st4(&L.wt[(16 * b + n) * LT + 4 * g], wt);
     }
     __device__ __forceinline__ void norms(int wi, f4 nr)
     {
@@ -256,10 +265,21 @@ struct WToLds {
     // 1/delta_t: nothing to do here (a sink that keeps them overrides this)
     __device__ __forceinline__ void zcols(int, f4, f4) {}
 };
+
 // Per-thread view of one head's penalty chain: lane coordinates and the steps.
 // A wave with chain index wi owns column blocks wi*BPW + bb; LdsT is the
-// workgroup's LDS layout (members uh, kh, ph, zk, z0, z0t, w, wt, gp, nrm, nq,
+// workgroup's LDS layout (members uh, kh, ph, zk, z0t, wt, gp, nrm, nq,
 // lit/tit, inv, hms).
+//
+// A chunk takes two phases, each ended by a workgroup barrier:
+//   factorisation phase   every wave: Y0 = A K^ (y_products); wave 0:
+//                         factorise I + G (factorize); work off the chain.
+//   update phase          every wave: W, the downdate of A and the |w|^2 and
+//                         W'K^, W'Phi partials of the chunk (downdate), then Z0
+//                         and the G partials of the next chunk with the new A
+//                         (z_products), which need only the wave's own blocks.
+// 1/|w| is applied where the partials are used (prep_tp, the record's alpha^,
+// the cross factors), in the next chunk's factorisation phase.
 template <int D, typename LdsT>
 struct Head {
     using Cf = Cfg<D>;
@@ -326,15 +346,34 @@ struct Head {
         zk_cmp = (tsum - zk_run) - yk;
         zk_run = tsum;
     }
+
+    // 1/|w_t| of the last updated chunk from the waves' |w|^2 partials: for
+    // t = 4g + r (rows of the C x C factors) and for t = n (this lane's token)
+    __device__ __forceinline__ f4 inv_norms4() const
+    {
+        f4 ns4 = ld4(&L.nrm[0][4 * g]);
+        sfor<NA - 1>([&](auto w2) { ns4 += ld4(&L.nrm[w2 + 1][4 * g]); });
+        f4 r4;
+        sfor<4>([&](auto r) { r4[int(r)] = ns4[int(r)] > 0.f ? rsqrtf(ns4[int(r)]) : 0.f; });
+        return r4;
+    }
+    __device__ __forceinline__ float inv_norm_n() const
+    {
+        float ns = L.nrm[0][n];
+        sfor<NA - 1>([&](auto w2) { ns += L.nrm[w2 + 1][n]; });
+        return ns > 0.f ? rsqrtf(ns) : 0.f;
+    }
+
     // ------------------------------------------------------------ penalty chain
-    // Z0' of the own blocks, Z0 into LDS, and this wave's partials (rows i of its
-    // blocks) of U^'Z0 and of U^'A K^ = Z0'K^ (A symmetric), so that the product
-    // A K^ is off the path to the factorisation.
-    __device__ __forceinline__ void a_products(const State &st, int p)
+    // Z0' of the own blocks of chunk cq into L.z0t[cq & 1] (Z0 [i][token]), and
+    // this wave's partials (rows i of its blocks) of U^'Z0 and of U^'A K^ = Z0'K^
+    // (A symmetric), so that the product A K^ is off the path to the
+    // factorisation.  U^ of chunk cq is in L.uh.
+    __device__ __forceinline__ void z_products(const State &st, int cq)
     {
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
-        const int sp = p & 1;
-        const float *ub = L.uh[0], *kb = L.kh[sp];
+        const float *ub = L.uh, *kb = L.kh[cq & 1];
+        float *z0t = L.z0t[cq & 1];
         f4 z[BPW];
         sfor<BPW>([&](auto bb) { z[bb] = zero; });
         sfor<NB>([&](auto rho) {
@@ -344,17 +383,14 @@ struct Head {
             });
         });
         // z[bb] register r = Z0[16b + n][4g + r]
-        sfor<BPW>([&](auto bb) {
-            const int b = wi * BPW + bb;
-            sfor<4>([&](auto r) { L.z0[(4 * g + r) * LD + 16 * b + n] = z[bb][int(r)]; });
-            st4(&L.z0t[(16 * b + n) * LT + 4 * g], z[bb]);
-        });
+        sfor<BPW>([&](auto bb) { st4(&z0t[(16 * (wi * BPW + bb) + n) * LT + 4 * g], z[bb]); });
         wave_lds_order();
         f4 gu = zero, gk = zero;
         sfor<BPW>([&](auto bb) {
             const int b = wi * BPW + bb;
             const f4 au = ld4(&ub[n * LD + 16 * b + 4 * g]);    // U^_n[16b + 4g + r]
-            const f4 bz = ld4(&L.z0[n * LD + 16 * b + 4 * g]);  // Z0_n[16b + 4g + r]
+            f4 bz;                                              // Z0_n[16b + 4g + r]
+            sfor<4>([&](auto r) { bz[int(r)] = z0t[(16 * b + 4 * g + r) * LT + n]; });
             const f4 bk = ld4(&kb[n * LD + 16 * b + 4 * g]);    // K^_n[16b + 4g + r]
             gu = mma4(au, bz, gu);
             gk = mma4(bz, bk, gk);
@@ -366,18 +402,12 @@ struct Head {
         });
     }
 
-    // Factorise I + G, downdate the own blocks of As, and hand W' and the |w|^2
-    // partials of the chunk to `wout`.  The 16 x 16 factorisation is done once
-    // per workgroup: wave 0 factorises I + G and leaves L^-1 (transposed), 1/d
-    // and the A operand of W' in LDS (L.hms), while every wave forms Y0' of its
-    // blocks and then runs `side` (work off the chain); after a workgroup
-    // barrier, each wave downdates its blocks and forms W'.
-    template <class WOut, class Side>
-    __device__ __forceinline__ void a_update_shared(State &st, int p, WOut &&wout, Side &&side)
+    // Y0' = (A K^)' of the own blocks of chunk cq, with the state before the
+    // chunk's downdate.
+    __device__ __forceinline__ void y_products(const State &st, int cq, f4 (&y)[BPW]) const
     {
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
-        const float *kb = L.kh[p & 1];
-        f4 y[BPW];
+        const float *kb = L.kh[cq & 1];
         sfor<BPW>([&](auto bb) { y[bb] = zero; });
         sfor<NB>([&](auto rho) {
             const f4 ak = ld4(&kb[n * LD + 16 * rho + 4 * g]);
@@ -385,67 +415,82 @@ struct Head {
                 sfor<BPW>([&](auto bb) { y[bb] = mma(ak[int(r)], st[bb][rho][int(r)], y[bb]); });
             });
         });
-        if (wi == 0) {
-            float Mr[16], gub[4];
-            sfor<4>([&](auto r) {
-                float a = L.gp[0][0][(4 * g + r) * LT + n];
-                sfor<NA - 1>([&](auto w2) { a += L.gp[w2 + 1][0][(4 * g + r) * LT + n]; });
-                L.lit[0][(4 * g + r) * LT + n] = a;
-            });
-            sfor<4>([&](auto c) {
-                float a = L.gp[0][1][(4 * c + g) * LT + n];
-                sfor<NA - 1>([&](auto w2) { a += L.gp[w2 + 1][1][(4 * c + g) * LT + n]; });
-                gub[c] = a;
-            });
-            wave_lds_order();
-            sfor<4>([&](auto q4) {
-                const f4 a = ld4(&L.lit[0][n * LT + 4 * q4]);
-                sfor<4>([&](auto r) { Mr[4 * q4 + r] = a[int(r)]; });
-            });
-            wave_lds_order();
-            // LDL' (column by column, Crout order): lane n holds row n.  LDr[j] =
-            // L[n][j] d_j (d_j in lane j), NLr[j] = -L[n][j] for n > j, 0
-            // otherwise; 1/d_j to LDS.  Column j+1's terms k < j are issued
-            // around the inversion of pivot j (software pipelining); only its
-            // k = j term waits for it.
-            float LDr[16], NLr[16];
-            float ca = Mr[0], cb = 0.f;
-            float invn = 0.f;
-            sfor<16>([&](auto jj) {
-                constexpr int j = decltype(jj)::value;
-                if constexpr (j > 0) ldl_block<j, j - 1, 1>(ca, LDr, NLr);
-                const float acc = ca + cb;
-                const float inv = rcp_bcast<j>(acc);
-                constexpr int E = j, E1 = E < 2 ? E : 2;
-                float na = 0.f, nb = 0.f;
-                if constexpr (j + 1 < 16) {
-                    na = Mr[j + 1];
-                    if constexpr (E1 > 0) ldl_early<j + 1, 0, E1>(na, nb, LDr, NLr);
-                }
-                LDr[j] = acc;
-                NLr[j] = n > j ? -(acc * inv) : 0.f;
-                invn = n == j ? inv : invn;   // lane n keeps 1 / d_n
-                if constexpr (j + 1 < 16 && E > E1) ldl_early<j + 1, E1, E - E1>(na, nb, LDr, NLr);
-                ca = na;
-                cb = nb;
-            });
-            L.inv[0][n] = invn;   // every lane group holds the same values
-            float X[4];
-            sfor<4>([&](auto c) { X[c] = n == 4 * c + g ? 1.f : 0.f; });
-            asm volatile(VLA_LINV_BLOCK
-                         : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3])
-                         : "v"(NLr[0]), "v"(NLr[1]), "v"(NLr[2]), "v"(NLr[3]), "v"(NLr[4]),
-                           "v"(NLr[5]), "v"(NLr[6]), "v"(NLr[7]), "v"(NLr[8]), "v"(NLr[9]),
-                           "v"(NLr[10]), "v"(NLr[11]), "v"(NLr[12]), "v"(NLr[13]), "v"(NLr[14]));
-            sfor<4>([&](auto c) { L.lit[0][(4 * c + g) * LT + n] = X[c]; });
-            wave_lds_order();
-            const f4 inv4 = ld4(&L.inv[0][4 * g]);
-            f4 hm = mma4(X, gub, zero);
-            sfor<4>([&](auto r) { hm[int(r)] = 4 * g + r <= n ? -(hm[int(r)] * inv4[int(r)]) : 0.f; });
-            st4(&L.hms[4 * (16 * g + n)], hm);
-        }
-        side();   // every wave, wave 0 after the factorisation
-        lds_barrier();
+    }
+
+    // Wave 0: factorise I + G = L D L' from the waves' partials and leave L^-1
+    // (both ways round in L.lit[0]), 1/d (L.inv[0]) and the A operand of W',
+    // -(D^-1 L^-1 U^'Y0) o Up (L.hms), in LDS.
+    __device__ __forceinline__ void factorize()
+    {
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        float Mr[16], gub[4];
+        sfor<4>([&](auto r) {
+            float a = L.gp[0][0][(4 * g + r) * LT + n];
+            sfor<NA - 1>([&](auto w2) { a += L.gp[w2 + 1][0][(4 * g + r) * LT + n]; });
+            L.lit[0][(4 * g + r) * LT + n] = a;
+        });
+        sfor<4>([&](auto c) {
+            float a = L.gp[0][1][(4 * c + g) * LT + n];
+            sfor<NA - 1>([&](auto w2) { a += L.gp[w2 + 1][1][(4 * c + g) * LT + n]; });
+            gub[c] = a;
+        });
+        wave_lds_order();
+        sfor<4>([&](auto q4) {
+            const f4 a = ld4(&L.lit[0][n * LT + 4 * q4]);
+            sfor<4>([&](auto r) { Mr[4 * q4 + r] = a[int(r)]; });
+        });
+        wave_lds_order();
+        // LDL' (column by column, Crout order): lane n holds row n.  LDr[j] =
+        // L[n][j] d_j (d_j in lane j), NLr[j] = -L[n][j] for n > j, 0
+        // otherwise; 1/d_j to LDS.  Column j+1's terms k < j are issued
+        // around the inversion of pivot j (software pipelining); only its
+        // k = j term waits for it.
+        float LDr[16], NLr[16];
+        float ca = Mr[0], cb = 0.f;
+        float invn = 0.f;
+        sfor<16>([&](auto jj) {
+            constexpr int j = decltype(jj)::value;
+            if constexpr (j > 0) ldl_block<j, j - 1, 1>(ca, LDr, NLr);
+            const float acc = ca + cb;
+            const float inv = rcp_bcast<j>(acc);
+            constexpr int E = j, E1 = E < 2 ? E : 2;
+            float na = 0.f, nb = 0.f;
+            if constexpr (j + 1 < 16) {
+                na = Mr[j + 1];
+                if constexpr (E1 > 0) ldl_early<j + 1, 0, E1>(na, nb, LDr, NLr);
+            }
+            LDr[j] = acc;
+            NLr[j] = n > j ? -(acc * inv) : 0.f;
+            invn = n == j ? inv : invn;   // lane n keeps 1 / d_n
+            if constexpr (j + 1 < 16 && E > E1) ldl_early<j + 1, E1, E - E1>(na, nb, LDr, NLr);
+            ca = na;
+            cb = nb;
+        });
+        L.inv[0][n] = invn;   // every lane group holds the same values
+        float X[4];
+        sfor<4>([&](auto c) { X[c] = n == 4 * c + g ? 1.f : 0.f; });
+        asm volatile(VLA_LINV_BLOCK
+                     : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3])
+                     : "v"(NLr[0]), "v"(NLr[1]), "v"(NLr[2]), "v"(NLr[3]), "v"(NLr[4]),
+                       "v"(NLr[5]), "v"(NLr[6]), "v"(NLr[7]), "v"(NLr[8]), "v"(NLr[9]),
+                       "v"(NLr[10]), "v"(NLr[11]), "v"(NLr[12]), "v"(NLr[13]), "v"(NLr[14]));
+        sfor<4>([&](auto c) { L.lit[0][(4 * c + g) * LT + n] = X[c]; });
+        wave_lds_order();
+        const f4 inv4 = ld4(&L.inv[0][4 * g]);
+        f4 hm = mma4(X, gub, zero);
+        sfor<4>([&](auto r) { hm[int(r)] = 4 * g + r <= n ? -(hm[int(r)] * inv4[int(r)]) : 0.f; });
+        st4(&L.hms[4 * (16 * g + n)], hm);
+    }
+
+    // After the factorisation of chunk cq: W' (to `wout`), the downdate
+    // As <- As - Z0 (I + G)^-1 Z0' of the own blocks, the |w|^2 partials, and
+    // this wave's partials of W'K^ and W'Phi (unnormalised alpha^, rows t of
+    // its blocks' keys) into L.nq.
+    template <class WOut>
+    __device__ __forceinline__ void downdate(State &st, int cq, const f4 (&y)[BPW], WOut &&wout)
+    {
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        const float *z0t = L.z0t[cq & 1];
         float X[4];
         sfor<4>([&](auto c) { X[c] = L.lit[0][(4 * c + g) * LT + n]; });   // L^-1 [n][4c+g]
         const f4 inv4 = ld4(&L.inv[0][4 * g]);                          // 1 / d_{4g+r}
@@ -455,7 +500,7 @@ struct Head {
         sfor<BPW>([&](auto bb) {
             const int b = wi * BPW + bb;
             float zb[4];   // Z0'[4c+g][16b+n]
-            sfor<4>([&](auto c) { zb[c] = L.z0[(4 * c + g) * LD + 16 * b + n]; });
+            sfor<4>([&](auto c) { zb[c] = z0t[(16 * b + n) * LT + 4 * c + g]; });
             const f4 q2 = mma4(X, zb, zero);        // L^-1 Z0': row t is z_t
             const f4 q1 = q2 * inv4;                // D^-1 L^-1 Z0'
             const f4 xt = mma4(lit, q1, zero);      // (I + G)^-1 Z0'
@@ -463,7 +508,7 @@ struct Head {
             const f4 nx = -xt;
             wout.zcols(b, q2, inv4);
             f4 az[NB];
-            sfor<NB>([&](auto rho) { az[rho] = ld4(&L.z0t[(16 * rho + n) * LT + 4 * g]); });
+            sfor<NB>([&](auto rho) { az[rho] = ld4(&z0t[(16 * rho + n) * LT + 4 * g]); });
             sfor<4>([&](auto r) {      // As <- As - Z0 (I + G)^-1 Z0'
                 sfor<NB>([&](auto rho) { st[bb][rho] = mma(az[rho][int(r)], nx[int(r)], st[bb][rho]); });
             });
@@ -472,50 +517,35 @@ struct Head {
         });
         sfor<4>([&](auto r) { nr[int(r)] = sum_row16(nr[int(r)]); });
         wout.norms(wi, nr);
-    }
-
-    // 1/|w_t| of chunk cq and this wave's partials of Alpha^'K^, Alpha^'Phi
-    // (from W in L.w and the |w|^2 partials in L.nrm)
-    __device__ __forceinline__ void s_grams(int cq, f4 &invn4)
-    {
-        const f4 zero = {0.f, 0.f, 0.f, 0.f};
-        const int sl = cq & 1;
-        float ns = L.nrm[0][n];
-        f4 ns4 = ld4(&L.nrm[0][4 * g]);
-        sfor<NA - 1>([&](auto w2) {
-            ns += L.nrm[w2 + 1][n];
-            ns4 += ld4(&L.nrm[w2 + 1][4 * g]);
-        });
-        const float invm = ns > 0.f ? rsqrtf(ns) : 0.f;   // 1 / |w_n|
-        sfor<4>([&](auto r) { invn4[int(r)] = ns4[int(r)] > 0.f ? rsqrtf(ns4[int(r)]) : 0.f; });
-        const float *kb = L.kh[sl], *pb = L.ph[sl];
+        wave_lds_order();
+        const float *kb = L.kh[cq & 1], *pb = L.ph[cq & 1];
         f4 gn = zero, gq = zero;
         sfor<BPW>([&](auto bb) {
             const int b = wi * BPW + bb;
-            const f4 aw = ld4(&L.w[n * LD + 16 * b + 4 * g]) * invm;
-            const f4 bk = ld4(&kb[n * LD + 16 * b + 4 * g]);
-            const f4 bp = ld4(&pb[n * LD + 16 * b + 4 * g]);
-            gn = mma4(aw, bk, gn);
-            gq = mma4(aw, bp, gq);
+            f4 aw;   // W_n[16b + 4g + r]
+            sfor<4>([&](auto r) { aw[int(r)] = L.wt[(16 * b + 4 * g + r) * LT + n]; });
+            gn = mma4(aw, ld4(&kb[n * LD + 16 * b + 4 * g]), gn);
+            gq = mma4(aw, ld4(&pb[n * LD + 16 * b + 4 * g]), gq);
         });
         sfor<4>([&](auto r) {
             L.nq[wi][0][(4 * g + r) * LT + n] = gn[int(r)];
             L.nq[wi][1][(4 * g + r) * LT + n] = gq[int(r)];
         });
     }
+
     // The two C x C factors of the memory chain from the waves' partials in
-    // L.nq: (I + N)^-1 and (Alpha^'Phi) o Up, each stored transposed
-    // (X'[m][t] = X[t][m], rows as swz16 places them), so that lane 16 g + n
-    // reads X[4 g + r][n] as four consecutive floats at swz16(n, g).  One wave
-    // computes them.
-    __device__ __forceinline__ void prep_tp(float *tt, float *pt)
+    // L.nq (rows scaled by 1/|w|, invn4 from inv_norms4): (I + N)^-1 and
+    // (Alpha^'Phi) o Up, each stored transposed (X'[m][t] = X[t][m], rows as
+    // swz16 places them), so that lane 16 g + n reads X[4 g + r][n] as four
+    // consecutive floats at swz16(n, g).  One wave computes them.
+    __device__ __forceinline__ void prep_tp(float *tt, float *pt, f4 invn4)
     {
         float NNr[16];
         f4 qa;
         sfor<4>([&](auto r) {   // -N[4g+r][n] (strictly upper), rows through LDS
             float a = L.nq[0][0][(4 * g + r) * LT + n];
             sfor<NA - 1>([&](auto w2) { a += L.nq[w2 + 1][0][(4 * g + r) * LT + n]; });
-            L.tit[wi][(4 * g + r) * LT + n] = 4 * g + r < n ? -a : 0.f;
+            L.tit[wi][(4 * g + r) * LT + n] = 4 * g + r < n ? -(a * invn4[int(r)]) : 0.f;
         });
         wave_lds_order();
         sfor<4>([&](auto q4) {
@@ -525,7 +555,7 @@ struct Head {
         sfor<4>([&](auto r) {
             float a = L.nq[0][1][(4 * g + r) * LT + n];
             sfor<NA - 1>([&](auto w2) { a += L.nq[w2 + 1][1][(4 * g + r) * LT + n]; });
-            qa[int(r)] = 4 * g + r <= n ? a : 0.f;
+            qa[int(r)] = 4 * g + r <= n ? a * invn4[int(r)] : 0.f;
         });
         st4(&pt[swz16(n, g)], qa);
         float X[4];

@@ -368,22 +368,19 @@ vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
 }
 
 // ------------------------------------------------------------------- penalty
-// LDS of a penalty workgroup (the members the steps of Head use; u^ has a single
-// buffer, since it is read before the next chunk is staged).
+// LDS of a penalty workgroup (the members the steps of Head use).
 template <int D>
 struct PLds {
     static constexpr int C = Cfg<D>::C, NA = Cfg<D>::NA, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
-    float uh[1][C * LD];     // u^ [token][i] (read before the next chunk is staged)
+    float uh[C * LD];        // u^ [token][i] of the chunk whose Z0 is formed next
     float kh[2][C * LD];     // k^, by chunk parity
     float ph[2][C * LD];     // phi(q), by chunk parity
     float zk[2][C * LD];     // phi(k), then the inclusive key sum, by chunk parity
-    float z0[C * LD];
-    float z0t[D * LT];
-    float w[C * LD];         // W [token][i]
-    float wt[1][D * LT];     // W [i][token]
-    float gp[NA][2][C * LT];
-    float nrm[NA][C];
-    float nq[NA][2][C * LT];
+    float z0t[2][D * LT];    // Z0 [i][token], by chunk parity
+    float wt[D * LT];        // W [i][token] of the last updated chunk
+    float gp[NA][2][C * LT]; // per wave: partials of I + U^'Z0 and Z0'K^
+    float nrm[NA][C];        // per wave: partial |w_t|^2
+    float nq[NA][2][C * LT]; // per wave: partials of W'K^ and W'Phi
     union {                  // L^-1 scratch of the factorisation / (I+N)^-1 scratch
         float lit[NA][C * LT];
         float tit[NA][C * LT];
@@ -453,7 +450,7 @@ struct PenStage {
             const int col = cc * CP + i;
             const float kv = rk.get(i) * ik, pq = phi_fast(rq.get(i));
             L.kh[slot][e0 + i] = kv;
-            L.uh[0][e0 + i] = ru.get(i) * iu;
+            L.uh[e0 + i] = ru.get(i) * iu;
             L.ph[slot][e0 + i] = pq;
             L.zk[slot][e0 + i] = ok ? phi_fast(rk.get(i)) : 0.f;
             rkh[swzd<D>(tl, col >> 2) + (col & 3)] = kv;
@@ -503,35 +500,37 @@ struct KeepW : WToLds<D, PLds<D>> {
     }
 };
 
-// X' for X = Alpha^'Y (C x C) with Alpha^ = W diag(1/|w|) of the current chunk
-// (W and the |w|^2 partials in LDS) and Y (C x d, token-major in LDS, row
-// stride LD) of the next one: dst[swz16(n, g) + r] = X[4 g + r][n].  One wave.
+// X' for X = Alpha^'Y (C x C) with Alpha^ = W diag(1/|w|) of the last updated
+// chunk (W [i][token] and the |w|^2 partials in LDS) and Y (C x d, token-major in
+// LDS, row stride LD) of the next one: dst[swz16(n, g) + r] = X[4 g + r][n].  One
+// wave.
 template <int D>
-__device__ __forceinline__ void cross_factor(const PLds<D> &L, const float *y, int g, int n, float *dst)
+__device__ __forceinline__ void cross_factor(const PLds<D> &L, const float *y, int g, int n, float invm,
+                                             float *dst)
 {
-    constexpr int NB = D / 16, LD = Cfg<D>::LD, NA = Cfg<D>::NA;
-    float ns = L.nrm[0][n];
-    sfor<NA - 1>([&](auto w2) { ns += L.nrm[w2 + 1][n]; });
-    const float invm = ns > 0.f ? rsqrtf(ns) : 0.f;   // 1 / |w_n|
+    constexpr int NB = D / 16, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
     f4 x = {0.f, 0.f, 0.f, 0.f};
     sfor<NB>([&](auto b) {
-        const f4 aw = ld4(&L.w[n * LD + 16 * b + 4 * g]) * invm;
+        f4 aw;
+        sfor<4>([&](auto r) { aw[int(r)] = L.wt[(16 * b + 4 * g + r) * LT + n] * invm; });
         x = mma4(aw, ld4(&y[n * LD + 16 * b + 4 * g]), x);
     });
     st4(&dst[swz16(n, g)], x);
 }
 
 // Workgroup (head, segment j): the penalty chain over chunks [j SC, (j+1) SC)
-// from A at the segment start, writing each chunk's record.  Per chunk p:
-//   1  Z0, Grams of chunk p                                  | barrier
-//   2  all: Y0 of own blocks; wave 0: factorise I + G;
-//      wave 1: (I+N)^-1 and P of chunk p-1 to the record;
-//      cross factors of chunk p-1 (if even) with chunk p;
-//      key-sum prefix of chunk p; stage chunk p+1 (k^ and
-//      phi(q) also to its record), prefetch p+2              | barrier
-//   3  downdate A, W of chunk p; 1/den of chunk p            | barrier
-//   4  1/|w|, Alpha^'K^ and Alpha^'Phi partials; alpha^ to
-//      the record.
+// from A at the segment start, writing each chunk's record.  Two phases per
+// chunk p, each ended by a barrier:
+//   factorisation   all: Y0 of own blocks; wave 0: factorise I + G of chunk p;
+//                   all: alpha^ of chunk p-1 to the record (1/|w| from the
+//                   partials); wave 1: (I+N)^-1 and P of chunk p-1; cross
+//                   factors of chunk p-1 (if even) with chunk p; key-sum
+//                   prefix of chunk p; stage chunk p+1 (k^ and phi(q) also to
+//                   its record), prefetch p+2
+//   update          all: W, downdate A, |w|^2, W'K^ and W'Phi partials of
+//                   chunk p; Z0 and the G partials of chunk p+1 from the new A
+//                   (own blocks only, so no barrier in between); 1/den of
+//                   chunk p.
 //
 // With SAVE, the per-token quantities the gradients need (Keep) also go to
 // `kept`: z and delta from the factorisation, alpha^ and 1/|y| with the record,
@@ -580,45 +579,24 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     if (c0 + 1 < c1) ps.prefetch(q, k, u, tok0, T, c0 + 1);
     vmem_drain();
     __syncthreads();
+    hd.z_products(st, c0);
+    lds_barrier();
 
-    // While wave 0 factorises I + G of chunk p, the other waves form the C x C
-    // factors of chunk p - 1 and, for an even p - 1, its cross factors with
-    // chunk p (from W, |w|^2 of chunk p - 1, still in LDS), the key sums of
-    // chunk p, and stage chunk p + 1.
     auto sink = [&]() {
-        if constexpr (SAVE) return KeepW<D>{{L, 0, hd.g, hd.n}, kept, 0, T};
-        else return WToLds<D, PLds<D>>{L, 0, hd.g, hd.n};
+        if constexpr (SAVE) return KeepW<D>{{L, hd.g, hd.n}, kept, 0, T};
+        else return WToLds<D, PLds<D>>{L, hd.g, hd.n};
     };
     auto wl = sink();
-    for (int p = c0; p < c1; ++p, rb += RS) {
-        if constexpr (SAVE) wl.tok = p * CH;
-        hd.a_products(st, p);
-        lds_barrier();
-        hd.a_update_shared(st, p, wl, [&]() {
-            if (p > c0) {
-                if (w == 1) hd.prep_tp(rb - RS + Rec<D>::TT, rb - RS + Rec<D>::PT);
-                if (((p - 1) & 1) == 0) {
-                    if (w == 1) cross_factor<D>(L, L.kh[p & 1], hd.g, hd.n, rb - RS + Rec<D>::QK);
-                    if (w == NA - 1) cross_factor<D>(L, L.ph[p & 1], hd.g, hd.n, rb - RS + Rec<D>::QP);
-                }
-            }
-            hd.stage2(p);
-            if (p + 1 < c1) {
-                ps.stage(L, p + 1, T, rb + RS + Rec<D>::KH, rb + RS + Rec<D>::PH, kept);
-                if (p + 2 < c1) ps.prefetch(q, k, u, tok0, T, p + 2);
-            }
-        });
-        ps.den(L, p, eps, rb + Rec<D>::RD, T, kept);
-        lds_barrier();
-        f4 invn4;
-        hd.s_grams(p, invn4);
+    // alpha^ of the last updated chunk (record at rp, first token tp) from W in
+    // L.wt and the |w|^2 partials: the own blocks
+    auto alpha_out = [&](float *rp, int tp, f4 invn4) {
         sfor<BPW>([&](auto bb) {
             const int b = w * BPW + bb;
-            const f4 a = ld4(&L.wt[0][(16 * b + hd.n) * LT + 4 * hd.g]) * invn4;
-            st4(&rb[Rec<D>::AH + swz16(16 * b + hd.n, hd.g)], a);
+            const f4 a = ld4(&L.wt[(16 * b + hd.n) * LT + 4 * hd.g]) * invn4;
+            st4(&rp[Rec<D>::AH + swz16(16 * b + hd.n, hd.g)], a);
             if constexpr (SAVE) {
                 sfor<4>([&](auto r) {
-                    const int t = p * CH + 4 * hd.g + r;
+                    const int t = tp + 4 * hd.g + r;
                     if (t < T) {
                         float *kt = kept + (size_t)t * Keep<D>::RS;
                         kt[Keep<D>::AL + 16 * b + hd.n] = a[int(r)];
@@ -627,9 +605,38 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
                 });
             }
         });
+    };
+    for (int p = c0; p < c1; ++p, rb += RS) {
+        f4 y[BPW];
+        hd.y_products(st, p, y);
+        if (w == 0) hd.factorize();
+        if (p > c0) {
+            const f4 invn4 = hd.inv_norms4();
+            alpha_out(rb - RS, (p - 1) * CH, invn4);
+            if (w == 1) hd.prep_tp(rb - RS + Rec<D>::TT, rb - RS + Rec<D>::PT, invn4);
+            if (((p - 1) & 1) == 0 && (w == 1 || w == NA - 1)) {
+                const float invm = hd.inv_norm_n();
+                if (w == 1) cross_factor<D>(L, L.kh[p & 1], hd.g, hd.n, invm, rb - RS + Rec<D>::QK);
+                else cross_factor<D>(L, L.ph[p & 1], hd.g, hd.n, invm, rb - RS + Rec<D>::QP);
+            }
+        }
+        hd.stage2(p);
+        if (p + 1 < c1) {
+            ps.stage(L, p + 1, T, rb + RS + Rec<D>::KH, rb + RS + Rec<D>::PH, kept);
+            if (p + 2 < c1) ps.prefetch(q, k, u, tok0, T, p + 2);
+        }
+        lds_barrier();
+        if constexpr (SAVE) wl.tok = p * CH;
+        hd.downdate(st, p, y, wl);
+        if (p + 1 < c1) hd.z_products(st, p + 1);
+        ps.den(L, p, eps, rb + Rec<D>::RD, T, kept);
+        lds_barrier();
     }
-    lds_barrier();
-    if (w == 1 && c1 > c0) hd.prep_tp(rb - RS + Rec<D>::TT, rb - RS + Rec<D>::PT);
+    if (c1 > c0) {   // the last chunk's alpha^ and C x C factors
+        const f4 invn4 = hd.inv_norms4();
+        alpha_out(rb - RS, (c1 - 1) * CH, invn4);
+        if (w == 1) hd.prep_tp(rb - RS + Rec<D>::TT, rb - RS + Rec<D>::PT, invn4);
+    }
     if (j == S - 1) {
         if (A_out) hd.store_state(st, A_out + bh * DD);
         if (hd.kcol >= 0 && zk_out) zk_out[bh * D + hd.kcol] = hd.zk_run;
