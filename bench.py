@@ -509,7 +509,7 @@ def main():
         vla.vla_forward_penalty(t["q"], t["k"], t["u"], cfg.lambda0, cfg.eps, workspace=ws,
                                 A_out=A, zkey_out=zk, stream=stream)
         e1.record(stream)
-        vla.vla_forward_memory(t["q"], t["k"], t["v"], workspace=ws, o=o, S_out=S, stream=stream)
+        vla.vla_forward_memory(t["v"], workspace=ws, o=o, S_out=S, stream=stream)
         e2.record(stream)
     torch.cuda.synchronize()
     pen_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in pev]))

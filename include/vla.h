@@ -15,8 +15,8 @@
  *   o_t = S phi(q_t) / max(phi(q_t)' zkey, eps)  (new S)                   Eq. (11)
  *
  * Entry points: vla_forward (T tokens; vla_forward_penalty and
- * vla_forward_memory are its two passes), vla_step (one decode token, state in
- * place), vla_backward (the gradients through vla_forward), vla_forward_scan
+ * vla_forward_memory are its two passes), vla_step (one decode token, state in place),
+ * vla_backward (the gradients through vla_forward), vla_forward_scan
  * (vla_forward with the memory chain as a scan over chunks, for comparison),
  * the workspace-size queries and vla_status_string.
  *
@@ -30,7 +30,13 @@
  *
  * Supported: d_h in {16, 32, 64, 96, 128}; B, H >= 1; T >= 0; finite
  * lambda0 > 0 and eps > 0.  State arithmetic is fp32 throughout; bf16 inputs
- * are widened exactly.
+ * are widened exactly.  The kernels address one head's inputs, o, and the
+ * per-chunk and per-token records in the workspace with 32-bit byte offsets, so
+ * T is limited to sequences whose per-head buffers stay below 2^31 bytes (for
+ * the forward at most 2,088,976 tokens at d_h = 64, 1,520,880 at 96 and
+ * 1,195,696 at 128; for vla_backward, whose per-token records take
+ * (4 d_h + 8) floats, 2,033,601, 1,369,568 and 1,032,444); a longer T is
+ * VLA_ERR_UNSUPPORTED, also from the workspace-size queries.
  *
  * Ownership and execution: the caller owns every buffer, including the
  * device workspace of vla_forward (size from vla_forward_workspace_size); the
@@ -94,7 +100,7 @@ typedef enum vla_dtype {
  * VLA_ERR_INVALID_ARG.
  */
 vla_status vla_forward(const void *q, const void *k, const void *v, const void *u,
-                       int in_dtype, int B, int H, int T, int d_h,
+                       vla_dtype in_dtype, int B, int H, int T, int d_h,
                        float lambda0, float eps,
                        float *o, float *S_out, float *A_out, float *zkey_out,
                        const float *S0, const float *A0, const float *zkey0,
@@ -112,17 +118,19 @@ vla_status vla_forward(const void *q, const void *k, const void *v, const void *
  * 16 tokens, leaves the factors the memory chain needs (alpha^ of Eq. (10), the
  * key-sum denominators of Eq. (11)) in the workspace; it writes the final A and
  * zkey (A_out, zkey_out may be NULL).  vla_forward_memory then runs Eqs. (10)
- * and (11) from those factors and q, k, v, writing o and the final S.  Between
- * the two calls the workspace must not be used by anything else.  Arguments and
- * errors as for vla_forward; d_h in {16, 32} is VLA_ERR_UNSUPPORTED and T < 1
+ * and (11) from those factors and v, writing o and the final S; k^ and phi(q)
+ * come from the records vla_forward_penalty left (it is the pass that reads q
+ * and k), so vla_forward_memory takes neither.  Between the two calls the
+ * workspace must not be used by anything else.  Arguments and errors as for
+ * vla_forward; d_h in {16, 32} is VLA_ERR_UNSUPPORTED and T < 1
  * VLA_ERR_INVALID_ARG.
  */
-vla_status vla_forward_penalty(const void *q, const void *k, const void *u, int in_dtype,
+vla_status vla_forward_penalty(const void *q, const void *k, const void *u, vla_dtype in_dtype,
                                int B, int H, int T, int d_h, float lambda0, float eps,
                                float *A_out, float *zkey_out, const float *A0,
                                const float *zkey0, void *workspace, size_t workspace_bytes,
                                void *stream);
-vla_status vla_forward_memory(const void *q, const void *k, const void *v, int in_dtype,
+vla_status vla_forward_memory(const void *v, vla_dtype in_dtype,
                               int B, int H, int T, int d_h, float *o, float *S_out,
                               const float *S0, void *workspace, size_t workspace_bytes,
                               void *stream);
@@ -142,15 +150,18 @@ vla_status vla_forward_workspace_size(int B, int H, int T, int d_h, size_t *byte
 /*
  * vla_step -- one decode token for every (b, h) head: the same recurrence as
  * vla_forward with T = 1, continuing from the caller's state, which is updated
- * in place.  This is the streaming form of the method: the state is fixed-size
- * (S, A, zkey) and no key/value cache is kept.
+ * in place.  This is the streaming inference the method is built for: the
+ * Portuguese technical summary of the paper ("Resumo Tecnico: Atencao Linear
+ * Variacional", section 5) and the paper's section 3.5 (Table 1: O(d_h^2)
+ * memory, independent of T) describe generation with a fixed-size state
+ * (S, A, zkey) and no key/value cache.
  *
  * q, k, v, u   inputs [B][H][d_h] of type in_dtype.
  * S, A, zkey   in/out state [B][H][d][d], [B][H][d][d], [B][H][d] (required).
  * o            output [B][H][d_h] fp32.
  */
 vla_status vla_step(const void *q, const void *k, const void *v, const void *u,
-                    int in_dtype, int B, int H, int d_h, float eps,
+                    vla_dtype in_dtype, int B, int H, int d_h, float eps,
                     float *S, float *A, float *zkey, float *o,
                     void *stream);
 
@@ -173,7 +184,7 @@ vla_status vla_step(const void *q, const void *k, const void *v, const void *u,
  * of each head, rounded up to a power of two chunks, plus one map per head).
  */
 vla_status vla_forward_scan(const void *q, const void *k, const void *v, const void *u,
-                            int in_dtype, int B, int H, int T, int d_h,
+                            vla_dtype in_dtype, int B, int H, int T, int d_h,
                             float lambda0, float eps,
                             float *o, float *S_out, float *A_out, float *zkey_out,
                             const float *S0, const float *A0, const float *zkey0,
@@ -222,7 +233,7 @@ vla_status vla_forward_scan_workspace_size(int B, int H, int T, int d_h, size_t 
  * vectors.  Errors as for vla_forward.
  */
 vla_status vla_backward(const void *q, const void *k, const void *v, const void *u,
-                        int in_dtype, int B, int H, int T, int d_h,
+                        vla_dtype in_dtype, int B, int H, int T, int d_h,
                         float lambda0, float eps,
                         const float *S0, const float *A0, const float *zkey0,
                         const float *dO, const float *dS_T, const float *dA_T,
@@ -243,7 +254,7 @@ vla_status vla_backward(const void *q, const void *k, const void *v, const void 
 vla_status vla_backward_workspace_size(int B, int H, int T, int d_h, size_t *bytes);
 
 /* Static, human-readable text for a status code (never NULL). */
-const char *vla_status_string(int status);
+const char *vla_status_string(vla_status status);
 
 #ifdef __cplusplus
 }

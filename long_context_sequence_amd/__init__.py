@@ -4,11 +4,11 @@ step and gradients.
 The compute lives in ``libvla.so`` (hand-written gfx950 HIP kernels behind the
 C ABI in ``include/vla.h``); this package is its thin Python binding.
 """
-from ._binding import (VLA_BF16, VLA_ERR_HIP, VLA_ERR_INVALID_ARG, VLA_ERR_UNSUPPORTED,
-                       VLA_F32, VLA_OK, LIB_PATH, VLAError, backward_workspace_size, load,
-                       scan_workspace_size, vla_backward, vla_forward, vla_forward_memory,
-                       vla_forward_penalty, vla_forward_scan, vla_status_string, vla_step,
-                       workspace_size)
+from ._binding import (VLA_BF16, VLA_ERR_HIP, VLA_ERR_INVALID_ARG,
+                       VLA_ERR_UNSUPPORTED, VLA_F32, VLA_OK, LIB_PATH, VLAError,
+                       backward_workspace_size, load, scan_workspace_size, vla_backward,
+                       vla_forward, vla_forward_memory, vla_forward_penalty,
+                       vla_forward_scan, vla_status_string, vla_step, workspace_size)
 from .autograd import vla_attention
 
 __all__ = ["vla_forward", "vla_forward_penalty", "vla_forward_memory", "vla_step",

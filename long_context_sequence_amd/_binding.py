@@ -44,7 +44,7 @@ def load() -> ctypes.CDLL:
                                             ctypes.c_float, _vp, _vp, _vp, _vp, _vp,
                                             ctypes.c_size_t, _vp]
         lib.vla_forward_memory.restype = ctypes.c_int
-        lib.vla_forward_memory.argtypes = [_vp, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        lib.vla_forward_memory.argtypes = [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp]
         lib.vla_forward_workspace_size.restype = ctypes.c_int
@@ -203,14 +203,14 @@ def vla_forward_penalty(q, k, u, lambda0: float = 0.1, eps: float = 1e-4, *, wor
         raise VLAError(st, "vla_forward_penalty")
 
 
-def vla_forward_memory(q, k, v, *, workspace, o=None, S_out=None, S0=None, stream=None):
+def vla_forward_memory(v, *, workspace, o=None, S_out=None, S0=None, stream=None):
     """Second pass of the forward: the memory chain and the readout from the
-    factors ``vla_forward_penalty`` left in ``workspace``.  Returns ``o``."""
+    factors (and k^, phi(q)) ``vla_forward_penalty`` left in ``workspace``, and v.
+    Returns ``o``."""
     torch = _torch()
-    B, H, T, d = q.shape
-    dev = q.device
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check(t, name, (B, H, T, d), q.dtype, dev)
+    B, H, T, d = v.shape
+    dev = v.device
+    _check(v, "v", (B, H, T, d), v.dtype, dev)
     f32 = torch.float32
     if o is None:
         o = torch.empty((B, H, T, d), dtype=f32, device=dev)
@@ -218,8 +218,8 @@ def vla_forward_memory(q, k, v, *, workspace, o=None, S_out=None, S0=None, strea
     _check(S_out, "S_out", (B, H, d, d), f32, dev)
     _check(S0, "S0", (B, H, d, d), f32, dev)
     workspace = _workspace(workspace, B, H, T, d, dev)
-    st = load().vla_forward_memory(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, T, d, _ptr(o),
-                                   _ptr(S_out), _ptr(S0), _ptr(workspace),
+    st = load().vla_forward_memory(_ptr(v), _dtype_code(v), B, H, T, d, _ptr(o), _ptr(S_out),
+                                   _ptr(S0), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream))
     if st != VLA_OK:
         raise VLAError(st, "vla_forward_memory")

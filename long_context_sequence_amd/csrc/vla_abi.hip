@@ -52,26 +52,40 @@ size_t workspace_bytes(int B, int H, int T, int d_h)
 
 }  // namespace
 
-extern "C" vla_status vla_forward(const void *q, const void *k, const void *v, const void *u,
-                                  int in_dtype, int B, int H, int T, int d_h,
-                                  float lambda0, float eps,
-                                  float *o, float *S_out, float *A_out, float *zkey_out,
-                                  const float *S0, const float *A0, const float *zkey0,
-                                  void *workspace, size_t workspace_bytes, void *stream)
+// Every check of vla_forward except the workspace's (shared with
+// vla_forward_noalloc, whose workspace is the library's own).
+vla_status vla::check_forward(const void *q, const void *k, const void *v, const void *u,
+                              int in_dtype, int B, int H, int T, int d_h, float lambda0, float eps,
+                              const float *o, const float *S_out, const float *A_out,
+                              const float *zkey_out, const float *S0, const float *A0,
+                              const float *zkey0)
 {
     vla_status st = check_common(in_dtype, B, H, d_h, eps);
     if (st != VLA_OK) return st;
     if (T < 0 || !finite_pos(lambda0)) return VLA_ERR_INVALID_ARG;
     if (!vla::twopass_size_ok(T, d_h, false)) return VLA_ERR_UNSUPPORTED;
-    const size_t need = ::workspace_bytes(B, H, T, d_h);
-    if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need))
-        return VLA_ERR_INVALID_ARG;
     const bool need_tok = T > 0;
     if (!ok_ptr(q, need_tok) || !ok_ptr(k, need_tok) || !ok_ptr(v, need_tok) ||
         !ok_ptr(u, need_tok) || !ok_ptr(o, need_tok))
         return VLA_ERR_INVALID_ARG;
     if (!ok_ptr(S_out, false) || !ok_ptr(A_out, false) || !ok_ptr(zkey_out, false) ||
         !ok_ptr(S0, false) || !ok_ptr(A0, false) || !ok_ptr(zkey0, false))
+        return VLA_ERR_INVALID_ARG;
+    return VLA_OK;
+}
+
+extern "C" vla_status vla_forward(const void *q, const void *k, const void *v, const void *u,
+                                  vla_dtype in_dtype, int B, int H, int T, int d_h,
+                                  float lambda0, float eps,
+                                  float *o, float *S_out, float *A_out, float *zkey_out,
+                                  const float *S0, const float *A0, const float *zkey0,
+                                  void *workspace, size_t workspace_bytes, void *stream)
+{
+    vla_status st = vla::check_forward(q, k, v, u, in_dtype, B, H, T, d_h, lambda0, eps, o, S_out,
+                                       A_out, zkey_out, S0, A0, zkey0);
+    if (st != VLA_OK) return st;
+    const size_t need = ::workspace_bytes(B, H, T, d_h);
+    if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need))
         return VLA_ERR_INVALID_ARG;
     if (T == 0 && !S_out && !A_out && !zkey_out) return VLA_OK;   // nothing to do
 
@@ -95,7 +109,7 @@ static vla_status check_phase(int in_dtype, int B, int H, int T, int d_h, float 
     return VLA_OK;
 }
 
-extern "C" vla_status vla_forward_penalty(const void *q, const void *k, const void *u, int in_dtype,
+extern "C" vla_status vla_forward_penalty(const void *q, const void *k, const void *u, vla_dtype in_dtype,
                                           int B, int H, int T, int d_h, float lambda0, float eps,
                                           float *A_out, float *zkey_out, const float *A0,
                                           const float *zkey0, void *workspace,
@@ -113,17 +127,15 @@ extern "C" vla_status vla_forward_penalty(const void *q, const void *k, const vo
     return vla::launch_forward_twopass(a, 1) == hipSuccess ? VLA_OK : VLA_ERR_HIP;
 }
 
-extern "C" vla_status vla_forward_memory(const void *q, const void *k, const void *v, int in_dtype,
-                                         int B, int H, int T, int d_h, float *o, float *S_out,
-                                         const float *S0, void *workspace, size_t workspace_bytes,
-                                         void *stream)
+extern "C" vla_status vla_forward_memory(const void *v, vla_dtype in_dtype, int B, int H, int T,
+                                         int d_h, float *o, float *S_out, const float *S0,
+                                         void *workspace, size_t workspace_bytes, void *stream)
 {
     vla_status st = check_phase(in_dtype, B, H, T, d_h, 1.0f, workspace, workspace_bytes);
     if (st != VLA_OK) return st;
-    if (!ok_ptr(q, true) || !ok_ptr(k, true) || !ok_ptr(v, true) || !ok_ptr(o, true) ||
-        !ok_ptr(S_out, false) || !ok_ptr(S0, false))
+    if (!ok_ptr(v, true) || !ok_ptr(o, true) || !ok_ptr(S_out, false) || !ok_ptr(S0, false))
         return VLA_ERR_INVALID_ARG;
-    vla::FwdArgs a{q, k, v, nullptr, in_dtype, B, H, T, d_h, 1.0f, 1.0f,
+    vla::FwdArgs a{nullptr, nullptr, v, nullptr, in_dtype, B, H, T, d_h, 1.0f, 1.0f,
                    o, S_out, nullptr, nullptr, S0, nullptr, nullptr, (hipStream_t)stream,
                    workspace, workspace_bytes};
     return vla::launch_forward_twopass(a, 2) == hipSuccess ? VLA_OK : VLA_ERR_HIP;
@@ -138,7 +150,7 @@ extern "C" vla_status vla_forward_workspace_size(int B, int H, int T, int d_h, s
 }
 
 extern "C" vla_status vla_step(const void *q, const void *k, const void *v, const void *u,
-                               int in_dtype, int B, int H, int d_h, float eps,
+                               vla_dtype in_dtype, int B, int H, int d_h, float eps,
                                float *S, float *A, float *zkey, float *o, void *stream)
 {
     vla_status st = check_common(in_dtype, B, H, d_h, eps);
@@ -161,7 +173,7 @@ extern "C" vla_status vla_forward_scan_workspace_size(int B, int H, int T, int d
 }
 
 extern "C" vla_status vla_forward_scan(const void *q, const void *k, const void *v, const void *u,
-                                       int in_dtype, int B, int H, int T, int d_h,
+                                       vla_dtype in_dtype, int B, int H, int T, int d_h,
                                        float lambda0, float eps,
                                        float *o, float *S_out, float *A_out, float *zkey_out,
                                        const float *S0, const float *A0, const float *zkey0,
@@ -195,7 +207,7 @@ extern "C" vla_status vla_backward_workspace_size(int B, int H, int T, int d_h, 
 }
 
 extern "C" vla_status vla_backward(const void *q, const void *k, const void *v, const void *u,
-                                   int in_dtype, int B, int H, int T, int d_h,
+                                   vla_dtype in_dtype, int B, int H, int T, int d_h,
                                    float lambda0, float eps,
                                    const float *S0, const float *A0, const float *zkey0,
                                    const float *dO, const float *dS_T, const float *dA_T,
@@ -228,7 +240,7 @@ extern "C" vla_status vla_backward(const void *q, const void *k, const void *v, 
     return vla::launch_backward(a) == hipSuccess ? VLA_OK : VLA_ERR_HIP;
 }
 
-extern "C" const char *vla_status_string(int status)
+extern "C" const char *vla_status_string(vla_status status)
 {
     switch (status) {
     case VLA_OK: return "VLA_OK: success";

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/vla.h"
+
 namespace vla {
 
 // Launch arguments after the C-ABI checks (see include/vla.h for meaning).
@@ -35,6 +37,12 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : expf(x); }
 
 hipError_t launch_forward_ref(const FwdArgs &a);
+
+// every argument check of vla_forward except the workspace's (vla_abi.hip)
+vla_status check_forward(const void *q, const void *k, const void *v, const void *u, int in_dtype,
+                         int B, int H, int T, int d_h, float lambda0, float eps, const float *o,
+                         const float *S_out, const float *A_out, const float *zkey_out,
+                         const float *S0, const float *A0, const float *zkey0);
 
 // T = 0: the initial state (given, or the defaults) to the requested outputs
 hipError_t launch_state_init(const FwdArgs &a);

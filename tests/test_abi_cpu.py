@@ -106,9 +106,8 @@ def _mem(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dt=1, B=2, H=2, T=64, d=64, o=FAKE, S=None, S0=None,
              ws=FAKE, ws_bytes=1 << 40, stream=None)
     a.update(kw)
-    return B.load().vla_forward_memory(a["q"], a["k"], a["v"], a["dt"], a["B"], a["H"], a["T"],
-                                       a["d"], a["o"], a["S"], a["S0"], a["ws"], a["ws_bytes"],
-                                       a["stream"])
+    return B.load().vla_forward_memory(a["v"], a["dt"], a["B"], a["H"], a["T"], a["d"], a["o"],
+                                       a["S"], a["S0"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -119,8 +118,6 @@ def _mem(**kw):
     (dict(ws=None), B.VLA_ERR_INVALID_ARG),
     (dict(ws=FAKE + 64), B.VLA_ERR_INVALID_ARG),
     (dict(ws_bytes=4096), B.VLA_ERR_INVALID_ARG),
-    (dict(q=None), B.VLA_ERR_INVALID_ARG),
-    (dict(k=MIS), B.VLA_ERR_INVALID_ARG),
     (dict(dt=5), B.VLA_ERR_UNSUPPORTED),
     (dict(B=0), B.VLA_ERR_INVALID_ARG),
 ])
@@ -130,6 +127,9 @@ def test_phase_argument_errors(kw, code):
 
 
 def test_phase_specific_argument_errors():
+    assert _pen(q=None) == B.VLA_ERR_INVALID_ARG
+    assert _pen(k=MIS) == B.VLA_ERR_INVALID_ARG
+    assert _mem(v=MIS) == B.VLA_ERR_INVALID_ARG
     assert _pen(lam=-1.0) == B.VLA_ERR_INVALID_ARG
     assert _pen(u=None) == B.VLA_ERR_INVALID_ARG
     assert _pen(A=MIS) == B.VLA_ERR_INVALID_ARG
@@ -281,3 +281,4 @@ def test_sequence_length_limit():
     assert _pen(d=128, T=1_000_000, ws_bytes=1024) == B.VLA_ERR_INVALID_ARG
     assert _pen(d=128, T=5_000_000) == B.VLA_ERR_UNSUPPORTED
     assert _mem(d=128, T=5_000_000) == B.VLA_ERR_UNSUPPORTED
+

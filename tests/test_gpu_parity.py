@@ -455,7 +455,7 @@ def test_phases_equal_forward_and_pipeline_on_two_streams():
     for i, (t, w, (A, z, S)) in enumerate(zip(ts, ws, outs)):
         with torch.cuda.stream(s2):
             s2.wait_event(done_pen[i])
-            os_.append(vla.vla_forward_memory(t["q"], t["k"], t["v"], workspace=w, S_out=S,
+            os_.append(vla.vla_forward_memory(t["v"], workspace=w, S_out=S,
                                               stream=s2))
     s1.synchronize()
     s2.synchronize()
