@@ -15,7 +15,8 @@
  *   o_t = S phi(q_t) / max(phi(q_t)' zkey, eps)  (new S)                   Eq. (11)
  *
  * Entry points: vla_forward (T tokens; vla_forward_penalty and
- * vla_forward_memory are its two passes), vla_step (one decode token, state in place),
+ * vla_forward_memory are its two passes; vla_forward_noalloc the same forward
+ * with a library-held workspace), vla_step (one decode token, state in place),
  * vla_backward (the gradients through vla_forward), vla_forward_scan
  * (vla_forward with the memory chain as a scan over chunks, for comparison),
  * the workspace-size queries and vla_status_string.
@@ -40,7 +41,8 @@
  *
  * Ownership and execution: the caller owns every buffer, including the
  * device workspace of vla_forward (size from vla_forward_workspace_size); the
- * library allocates nothing and keeps no state between calls.  Calls are
+ * library allocates nothing and keeps no state between calls (apart from the
+ * fixed device array that vla_forward_noalloc uses as its workspace).  Calls are
  * asynchronous on `stream` (a hipStream_t; NULL = the null stream) and never
  * synchronise.  Arguments are checked before anything is launched; on an
  * argument error nothing is launched and no buffer is touched.  A failed launch
@@ -252,6 +254,27 @@ vla_status vla_backward(const void *q, const void *k, const void *v, const void 
  * sizes), VLA_ERR_UNSUPPORTED (d_h).
  */
 vla_status vla_backward_workspace_size(int B, int H, int T, int d_h, size_t *bytes);
+
+/*
+ * vla_forward_noalloc -- vla_forward for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The workspace is the library's own
+ * device array of VLA_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held until the
+ * process ends; the call allocates nothing.  Arguments, results and errors as
+ * for vla_forward (bit-identical results), plus VLA_ERR_UNSUPPORTED when the
+ * sizes need more workspace than the array holds (vla_forward_workspace_size
+ * gives the need: for example B = 4, H = 8, T = 1024, d_h = 64 fits, B = 8,
+ * H = 16, T = 4096 does not) and VLA_ERR_HIP if the array's device address
+ * cannot be obtained.  Calls that overlap in time on one GPU share the array
+ * and race: serialise them (one stream, or events between streams).
+ */
+#define VLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+vla_status vla_forward_noalloc(const void *q, const void *k, const void *v, const void *u,
+                               vla_dtype in_dtype, int B, int H, int T, int d_h,
+                               float lambda0, float eps,
+                               float *o, float *S_out, float *A_out, float *zkey_out,
+                               const float *S0, const float *A0, const float *zkey0,
+                               void *stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *vla_status_string(vla_status status);

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(PKG, "libvla.so")
 
 VLA_OK, VLA_ERR_INVALID_ARG, VLA_ERR_UNSUPPORTED, VLA_ERR_HIP = 0, 1, 2, 3
 VLA_F32, VLA_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 64 << 20   # VLA_NOALLOC_SCRATCH_BYTES of include/vla.h
 
 _vp = ctypes.c_void_p
 _lib = None
@@ -47,6 +48,11 @@ def load() -> ctypes.CDLL:
         lib.vla_forward_memory.argtypes = [_vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp,
                                            ctypes.c_size_t, _vp]
+        lib.vla_forward_noalloc.restype = ctypes.c_int
+        lib.vla_forward_noalloc.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, _vp,
+                                            _vp, _vp, _vp, _vp]
         lib.vla_forward_workspace_size.restype = ctypes.c_int
         lib.vla_forward_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                    ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
@@ -223,6 +229,32 @@ def vla_forward_memory(v, *, workspace, o=None, S_out=None, S0=None, stream=None
                                    workspace.numel() * workspace.element_size(), _stream(stream))
     if st != VLA_OK:
         raise VLAError(st, "vla_forward_memory")
+    return o
+
+
+def vla_forward_noalloc(q, k, v, u, lambda0: float = 0.1, eps: float = 1e-4, *, o, S_out=None,
+                        A_out=None, zkey_out=None, S0=None, A0=None, zkey0=None, stream=None):
+    """``vla_forward`` with the library's own fixed workspace: nothing is
+    allocated, so every output is passed in (``o`` [B, H, T, d_h] float32 and
+    any of the final-state outputs).  Sizes needing more workspace than
+    ``NOALLOC_SCRATCH_BYTES`` raise VLAError (VLA_ERR_UNSUPPORTED)."""
+    B, H, T, d = q.shape
+    dev = q.device
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("u", u)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    f32 = torch.float32
+    _check(o, "o", (B, H, T, d), f32, dev)
+    for name, t, shp in (("S_out", S_out, (B, H, d, d)), ("A_out", A_out, (B, H, d, d)),
+                         ("zkey_out", zkey_out, (B, H, d)), ("S0", S0, (B, H, d, d)),
+                         ("A0", A0, (B, H, d, d)), ("zkey0", zkey0, (B, H, d))):
+        _check(t, name, shp, f32, dev)
+    st = load().vla_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(u), _dtype_code(q), B, H, T, d,
+                                    float(lambda0), float(eps), _ptr(o), _ptr(S_out),
+                                    _ptr(A_out), _ptr(zkey_out), _ptr(S0), _ptr(A0), _ptr(zkey0),
+                                    _stream(stream))
+    if st != VLA_OK:
+        raise VLAError(st, "vla_forward_noalloc")
     return o
 
 

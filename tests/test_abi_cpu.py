@@ -22,7 +22,7 @@ def _declared_functions():
 
 def test_header_symbols_exported():
     names = _declared_functions()
-    assert {"vla_forward", "vla_forward_penalty", "vla_forward_memory",
+    assert {"vla_forward", "vla_forward_penalty", "vla_forward_memory", "vla_forward_noalloc",
             "vla_forward_workspace_size", "vla_step", "vla_backward",
             "vla_backward_workspace_size", "vla_status_string"} <= set(names)
     lib = ctypes.CDLL(vla.LIB_PATH)
@@ -282,3 +282,29 @@ def test_sequence_length_limit():
     assert _pen(d=128, T=5_000_000) == B.VLA_ERR_UNSUPPORTED
     assert _mem(d=128, T=5_000_000) == B.VLA_ERR_UNSUPPORTED
 
+
+def _noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, u=FAKE, dt=0, B=1, H=1, T=4, d=64, lam=0.1, eps=1e-4,
+             o=FAKE, S=None, A=None, z=None, S0=None, A0=None, z0=None, stream=None)
+    a.update(kw)
+    return B.load().vla_forward_noalloc(a["q"], a["k"], a["v"], a["u"], a["dt"], a["B"], a["H"],
+                                        a["T"], a["d"], a["lam"], a["eps"], a["o"], a["S"],
+                                        a["A"], a["z"], a["S0"], a["A0"], a["z0"], a["stream"])
+
+
+def test_noalloc_argument_errors_and_size_limit():
+    """vla_forward_noalloc checks the arguments as vla_forward does, before any
+    runtime call, and refuses sizes whose workspace exceeds its fixed array."""
+    assert vla.NOALLOC_SCRATCH_BYTES == 64 << 20
+    with open(os.path.join(ROOT, "include", "vla.h")) as f:
+        assert re.search(r"#define VLA_NOALLOC_SCRATCH_BYTES \(64u << 20\)", f.read())
+    assert _noalloc(q=None) == B.VLA_ERR_INVALID_ARG
+    assert _noalloc(o=MIS) == B.VLA_ERR_INVALID_ARG
+    assert _noalloc(d=48) == B.VLA_ERR_UNSUPPORTED
+    assert _noalloc(eps=0.0) == B.VLA_ERR_INVALID_ARG
+    # the bench workload needs 546.5 MiB of workspace: more than the array
+    assert vla.workspace_size(8, 16, 4096, 64) > vla.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(B=8, H=16, T=4096, d=64, dt=1) == B.VLA_ERR_UNSUPPORTED
+    assert vla.workspace_size(4, 8, 1024, 64) <= vla.NOALLOC_SCRATCH_BYTES
+    # T = 0 with no outputs: nothing to do, nothing touched
+    assert _noalloc(T=0, q=None, k=None, v=None, u=None, o=None) == B.VLA_OK
