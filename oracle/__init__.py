@@ -19,7 +19,11 @@ finite differences of the forward, entry by entry on tiny heads (with the
 denominator floor active and with zero keys and penalty vectors) and along
 random directions on larger ones, and to the first token's gradient worked by
 hand; ``backward_head_checkpointed`` (the same reverse mode split into
-segments) to ``backward_head``.  No function here is left unpinned.
+segments) to ``backward_head``.  The baselines: ``linear_attention_head`` to
+the closed-form sum and the causal quadratic readout of the same article;
+``deltanet_head`` to the VLA oracle with u = 0 (beta = 1), to exact recovery
+with orthonormal keys and to the delta-rule residual invariant.  No function
+here is left unpinned.
 """
 from __future__ import annotations
 
@@ -60,6 +64,12 @@ def _load():
         f = lib.vla_oracle_backward
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double] + [_dp] * 18
+        f = lib.vla_oracle_linear_attention
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_int, ctypes.c_int] + [_dp] * 8
+        f = lib.vla_oracle_deltanet
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double] + [_dp] * 8
         _lib = lib
     return _lib
 
@@ -209,6 +219,62 @@ def backward_head_checkpointed(q, k, v, u, dO, lambda0=0.1, eps=1e-4, S0=None, A
         adj = (r["dS0"], r["dA0"], r["dzkey0"])
     out["dS0"], out["dA0"], out["dzkey0"] = adj
     return out
+
+
+def linear_attention_head(q, k, v, S0=None, zkey0=None):
+    """Cumulative-sum linear attention ("Linear Attention" wiki article,
+    recurrent form) on one head: q, k, v are [T, d].  Returns ``o`` [T, d] and
+    the final ``S`` [d, d] (value-major, S += v phi(k)') and ``zkey`` [d]."""
+    q = _f64(q)
+    T, d = q.shape
+    k, v = _f64(k, (T, d)), _f64(v, (T, d))
+    S0, zkey0 = _f64(S0, (d, d)), _f64(zkey0, (d,))
+    o, S, zk = np.zeros((T, d)), np.zeros((d, d)), np.zeros(d)
+    rc = _load().vla_oracle_linear_attention(T, d, _ptr(q), _ptr(k), _ptr(v), _ptr(S0),
+                                             _ptr(zkey0), _ptr(o), _ptr(S), _ptr(zk))
+    if rc != 0:
+        raise ValueError(f"vla_oracle_linear_attention failed with code {rc}")
+    return dict(o=o, S=S, zkey=zk)
+
+
+def deltanet_head(q, k, v, beta=1.0, eps=1e-4, S0=None, zkey0=None):
+    """DeltaNet as the VLA layer with the scalar gate beta in place of alpha^ and
+    no A (delta rule on the unit key; Eq. (11) readout), one head.  Returns ``o``
+    [T, d], the final ``S`` [d, d] and ``zkey`` [d]."""
+    q = _f64(q)
+    T, d = q.shape
+    k, v = _f64(k, (T, d)), _f64(v, (T, d))
+    S0, zkey0 = _f64(S0, (d, d)), _f64(zkey0, (d,))
+    o, S, zk = np.zeros((T, d)), np.zeros((d, d)), np.zeros(d)
+    rc = _load().vla_oracle_deltanet(T, d, float(beta), float(eps), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(S0), _ptr(zkey0), _ptr(o), _ptr(S), _ptr(zk))
+    if rc != 0:
+        raise ValueError(f"vla_oracle_deltanet failed with code {rc}")
+    return dict(o=o, S=S, zkey=zk)
+
+
+def baseline(kind, q, k, v, beta=1.0, eps=1e-4, S0=None, zkey0=None, workers=None):
+    """All heads of [B, H, T, d] inputs for kind "linear" or "delta" (thread
+    pool over heads).  Returns ``o``, ``S``, ``zkey``."""
+    q = np.asarray(q)
+    B, H, T, d = q.shape
+    res = dict(o=np.zeros((B, H, T, d)), S=np.zeros((B, H, d, d)), zkey=np.zeros((B, H, d)))
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        s0 = None if S0 is None else S0[b, h]
+        z0 = None if zkey0 is None else zkey0[b, h]
+        if kind == "linear":
+            r = linear_attention_head(q[b, h], k[b, h], v[b, h], s0, z0)
+        else:
+            r = deltanet_head(q[b, h], k[b, h], v[b, h], beta, eps, s0, z0)
+        for key in res:
+            res[key][b, h] = r[key]
+
+    n = min(workers or default_workers(), B * H)
+    with ThreadPoolExecutor(max_workers=max(1, n)) as ex:
+        list(ex.map(one, range(B * H)))
+    return res
 
 
 def backward(q, k, v, u, dO, lambda0=0.1, eps=1e-4, S0=None, A0=None, zkey0=None,

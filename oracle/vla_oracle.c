@@ -396,3 +396,95 @@ out:
     free(o); free(tzk); free(mats); free(vec);
     return rc;
 }
+
+/*
+ * Baselines on the same inputs (test infrastructure, like everything above).
+ *
+ * Cumulative-sum linear attention, from the "Linear Attention" wiki article,
+ * "recurrent form" section: the state gains phi(k_t) v_t' each token, the key
+ * sum gains phi(k_t), and the output is phi(q_t)'S_t / phi(q_t)'z_t.  Here S is
+ * stored value-major like the VLA state (S[i][j], i value, j key), so
+ *     S_t = S_{t-1} + v_t phi(k_t)',   zkey_t = zkey_{t-1} + phi(k_t),
+ *     o_t = S_t phi(q_t) / (phi(q_t)' zkey_t).
+ * phi = ELU + 1 as in the article's "feature maps" section.  The article's
+ * readout has no floor; phi > 0 keeps the denominator positive.
+ *
+ * q, k, v : [T][d];  S0 [d][d] and zkey0 [d] or NULL (zero);  o [T][d];
+ * S [d][d], zkey [d] out.  Returns 0 or nonzero on bad arguments.
+ */
+int vla_oracle_linear_attention(int T, int d, const double *q, const double *k, const double *v,
+                                const double *S0, const double *zkey0,
+                                double *o, double *S, double *zkey)
+{
+    if (T < 0 || d < 1 || !S || !zkey) return VLA_ORACLE_EINVAL;
+    if (T > 0 && (!q || !k || !v || !o)) return VLA_ORACLE_EINVAL;
+    const size_t dd = (size_t)d * d;
+    if (S0) memcpy(S, S0, dd * sizeof(double));
+    else memset(S, 0, dd * sizeof(double));
+    if (zkey0) memcpy(zkey, zkey0, (size_t)d * sizeof(double));
+    else memset(zkey, 0, (size_t)d * sizeof(double));
+    double *work = (double *)malloc(3 * (size_t)d * sizeof(double));
+    if (!work) return VLA_ORACLE_ENOMEM;
+    double *pk = work, *pq = work + d, *num = work + 2 * d;
+    for (int t = 0; t < T; ++t) {
+        const double *qt = q + (size_t)t * d, *kt = k + (size_t)t * d, *vt = v + (size_t)t * d;
+        for (int j = 0; j < d; ++j) {
+            pk[j] = phi(kt[j]);
+            pq[j] = phi(qt[j]);
+            zkey[j] += pk[j];
+        }
+        for (int i = 0; i < d; ++i)
+            for (int j = 0; j < d; ++j) S[(size_t)i * d + j] += vt[i] * pk[j];
+        matvec(S, pq, num, d);
+        const double den = dot(pq, zkey, d);
+        for (int i = 0; i < d; ++i) o[(size_t)t * d + i] = num[i] / den;
+    }
+    free(work);
+    return VLA_ORACLE_OK;
+}
+
+/*
+ * DeltaNet as the pages' special case of the VLA layer: section 3.5 of
+ * "Variational Linear Attention" obtains DeltaNet by replacing alpha^_t with a
+ * scalar gate and dropping A_t.  With the gate beta on the unit key, the write
+ * of Eq. (10) becomes the delta rule of the kexue.fm article's "linear version"
+ * (W_t = W_{t-1} - eta (W_{t-1} k - v) k', eta = beta, k = k^):
+ *     e_t = v_t - S_{t-1} k^_t,   S_t = S_{t-1} + beta e_t k^_t',
+ * and the readout is Eq. (11) unchanged (raw-key phi sum, max(., eps) floor).
+ *
+ * q, k, v : [T][d];  S0 [d][d], zkey0 [d] or NULL (zero);  o [T][d];
+ * S [d][d], zkey [d] out.  Returns 0 or nonzero on bad arguments.
+ */
+int vla_oracle_deltanet(int T, int d, double beta, double eps, const double *q, const double *k,
+                        const double *v, const double *S0, const double *zkey0,
+                        double *o, double *S, double *zkey)
+{
+    if (T < 0 || d < 1 || !(eps > 0.0) || !S || !zkey) return VLA_ORACLE_EINVAL;
+    if (T > 0 && (!q || !k || !v || !o)) return VLA_ORACLE_EINVAL;
+    const size_t dd = (size_t)d * d;
+    if (S0) memcpy(S, S0, dd * sizeof(double));
+    else memset(S, 0, dd * sizeof(double));
+    if (zkey0) memcpy(zkey, zkey0, (size_t)d * sizeof(double));
+    else memset(zkey, 0, (size_t)d * sizeof(double));
+    double *work = (double *)malloc(4 * (size_t)d * sizeof(double));
+    if (!work) return VLA_ORACLE_ENOMEM;
+    double *kh = work, *e = work + d, *pq = work + 2 * d, *num = work + 3 * d;
+    for (int t = 0; t < T; ++t) {
+        const double *qt = q + (size_t)t * d, *kt = k + (size_t)t * d, *vt = v + (size_t)t * d;
+        normalise(kt, kh, d);
+        matvec(S, kh, e, d);
+        for (int i = 0; i < d; ++i) e[i] = vt[i] - e[i];
+        for (int i = 0; i < d; ++i)
+            for (int j = 0; j < d; ++j) S[(size_t)i * d + j] += beta * e[i] * kh[j];
+        for (int i = 0; i < d; ++i) {
+            pq[i] = phi(qt[i]);
+            zkey[i] += phi(kt[i]);
+        }
+        double den = dot(pq, zkey, d);
+        if (den < eps) den = eps;
+        matvec(S, pq, num, d);
+        for (int i = 0; i < d; ++i) o[(size_t)t * d + i] = num[i] / den;
+    }
+    free(work);
+    return VLA_ORACLE_OK;
+}
