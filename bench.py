@@ -20,6 +20,9 @@ other workload (single head d_h = 16; 32 heads d_h = 64 T = 1024; the
 MQAR-shaped 128 heads d_h = 96 T = 16384; 64 heads d_h = 128 T = 65536 bf16)
 and the long-context workload's 4096-step ``vla_step`` continuation from its
 forward's final state, in microseconds per step and GB/s of state traffic.
+Also (key ``baselines``) the pages' comparison models on the headline inputs:
+cumulative-sum linear attention and DeltaNet, their time against the forward's,
+and the state-norm contrast |S_T|_F of the three on the recall-shaped recipe.
 
 ``--backward`` prints the same kind of line for ``vla_backward`` (gradients of
 q, k, v, u and the initial state for a synthetic dL/do) on the same workload,
@@ -417,6 +420,65 @@ def decode_continuation(vla, torch, cfg, x, state):
             "bytes_per_step": state_bytes, "GBps": gbps, "hbm_frac": gbps / 8000.0}
 
 
+def baselines(vla, torch, vla_ms):
+    """The pages' comparison models on the headline workload's inputs: the
+    cumulative-sum linear attention and DeltaNet (gate 1 on the unit key), each
+    one vla_baseline_forward call (per-chunk records, then the forward's memory
+    pass), timed like the forward; VLA's time over theirs; and the state-norm
+    contrast of section 4.1 on the recall-shaped recipe: |S_T|_F (mean over
+    heads) after T tokens for the three layers."""
+    import numpy as np
+    import gen
+    cfg = gen.config(WORKLOAD)
+    B, H, T, d = cfg.B, cfg.H, cfg.T, cfg.d
+    dev = torch.device("cuda:0")
+    x = gen.make_inputs(cfg)
+    t = {n: torch.from_numpy(x[n]).to(dev).view(torch.bfloat16) for n in "qkv"}
+    o = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    zk = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(vla.baseline_workspace_size(B, H, T, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {"workload": cfg.name, "vla_ms": vla_ms}
+    for kind, per_tok in (("linear", 4), ("delta", 6)):
+        def step():
+            vla.vla_baseline(kind, t["q"], t["k"], t["v"], 1.0, cfg.eps, o=o, S_out=S,
+                             zkey_out=zk, workspace=ws, stream=stream)
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < SETTLE_S:
+            step()
+            torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(20)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+        out[kind] = {"ms": ms, "tokens_heads_per_s": B * H * T / (ms / 1e3),
+                     "vla_time_ratio": vla_ms / ms,
+                     "flop_per_token_head": per_tok * d * d,
+                     "vla_flop_ratio": 12 / per_tok}
+    del t, o, ws
+    rc = gen.config(4).with_sizes(B=1, H=8, T=4096)
+    xr = gen.make_inputs(rc)
+    tr = {n: torch.from_numpy(xr[n]).to(dev) for n in "qkvu"}
+    norms = {"workload": f"recall-shaped, B=1, H=8, d_h={rc.d}", "T": [], "linear": [],
+             "delta": [], "vla": []}
+    for Tn in (256, 1024, 4096):
+        sl = {n: tr[n][:, :, :Tn].contiguous() for n in "qkvu"}
+        _, s_la, _ = vla.vla_baseline("linear", sl["q"], sl["k"], sl["v"], return_state=True)
+        _, s_dn, _ = vla.vla_baseline("delta", sl["q"], sl["k"], sl["v"], return_state=True)
+        _, s_v, _, _ = vla.vla_forward(sl["q"], sl["k"], sl["v"], sl["u"], return_state=True)
+        torch.cuda.synchronize()
+        norms["T"].append(Tn)
+        for key, sv in (("linear", s_la), ("delta", s_dn), ("vla", s_v)):
+            norms[key].append(float(sv.norm(dim=(-2, -1)).mean()))
+    out["state_norm"] = norms
+    return out
+
+
 def other_workloads(vla, torch):
     """Forward time of each workload other than the headline one (parity
     cases, reported beside it), and the long-context workload's decode
@@ -558,6 +620,7 @@ def main():
         "device_peak": device_peak_tflops(),
     }
     if not args.headline_only:
+        res["baselines"] = baselines(vla, torch, kern_ms)
         res["workloads"] = other_workloads(vla, torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_heads)

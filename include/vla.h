@@ -276,6 +276,40 @@ vla_status vla_forward_noalloc(const void *q, const void *k, const void *v, cons
                                const float *S0, const float *A0, const float *zkey0,
                                void *stream);
 
+/*
+ * vla_baseline_forward -- the two baselines the pages compare VLA with, on the
+ * same inputs and layouts (d_h in {64, 96, 128}):
+ *   VLA_BASELINE_LINEAR  cumulative-sum linear attention, the recurrent form
+ *                        of the "Linear Attention" wiki article: per token
+ *                        S <- S + v phi(k)', zkey <- zkey + phi(k),
+ *                        o = S phi(q) / (phi(q)' zkey)  (no floor; phi > 0);
+ *   VLA_BASELINE_DELTA   DeltaNet as "Variational Linear Attention" section 3.5
+ *                        obtains it from VLA (alpha^ replaced by the scalar gate
+ *                        beta on the unit key, no A), i.e. the delta rule of the
+ *                        kexue.fm article's "linear version" with eta = beta:
+ *                        e = v - S k^, S <- S + beta e k^', o by Eq. (11)
+ *                        (max(., eps) floor).
+ * phi = ELU + 1 of the raw q and k; S [B][H][d][d] value-major as for
+ * vla_forward.  beta is used by VLA_BASELINE_DELTA only (finite; 1 for the plain
+ * delta rule).  S_out, zkey_out, S0, zkey0 as for vla_forward (NULL = skip /
+ * zero).  workspace: at least vla_baseline_workspace_size bytes, 256-byte
+ * aligned.  Errors as for vla_forward; an unknown kind or d_h in {16, 32} is
+ * VLA_ERR_UNSUPPORTED.  These exist to measure VLA's constant factor and state
+ * growth against them (section 3.5 Table 1, section 4.1); they share the
+ * forward's memory-chain kernel.
+ */
+typedef enum vla_baseline {
+    VLA_BASELINE_LINEAR = 0,
+    VLA_BASELINE_DELTA = 1
+} vla_baseline;
+vla_status vla_baseline_forward(vla_baseline kind, const void *q, const void *k, const void *v,
+                                vla_dtype in_dtype, int B, int H, int T, int d_h, float beta,
+                                float eps, float *o, float *S_out, float *zkey_out,
+                                const float *S0, const float *zkey0, void *workspace,
+                                size_t workspace_bytes, void *stream);
+/* bytes of workspace vla_baseline_forward needs (0 when T == 0).  Host-only. */
+vla_status vla_baseline_workspace_size(int B, int H, int T, int d_h, size_t *bytes);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *vla_status_string(vla_status status);
 

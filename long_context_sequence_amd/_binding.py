@@ -73,6 +73,14 @@ def load() -> ctypes.CDLL:
         lib.vla_backward_workspace_size.restype = ctypes.c_int
         lib.vla_backward_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                     ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        lib.vla_baseline_forward.restype = ctypes.c_int
+        lib.vla_baseline_forward.argtypes = [ctypes.c_int, _vp, _vp, _vp, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_float, ctypes.c_float, _vp,
+                                             _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.vla_baseline_workspace_size.restype = ctypes.c_int
+        lib.vla_baseline_workspace_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                    ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
         lib.vla_status_string.restype = ctypes.c_char_p
         lib.vla_status_string.argtypes = [ctypes.c_int]
         _lib = lib
@@ -256,6 +264,55 @@ def vla_forward_noalloc(q, k, v, u, lambda0: float = 0.1, eps: float = 1e-4, *, 
     if st != VLA_OK:
         raise VLAError(st, "vla_forward_noalloc")
     return o
+
+
+BASELINES = {"linear": 0, "delta": 1}   # vla_baseline of include/vla.h
+
+
+def baseline_workspace_size(B: int, H: int, T: int, d_h: int) -> int:
+    """Bytes of device workspace vla_baseline needs for these sizes."""
+    n = ctypes.c_size_t(0)
+    st = load().vla_baseline_workspace_size(int(B), int(H), int(T), int(d_h), ctypes.byref(n))
+    if st != VLA_OK:
+        raise VLAError(st, "vla_baseline_workspace_size")
+    return n.value
+
+
+def vla_baseline(kind: str, q, k, v, beta: float = 1.0, eps: float = 1e-4, *, o=None,
+                 S_out=None, zkey_out=None, S0=None, zkey0=None, return_state: bool = False,
+                 stream=None, workspace=None):
+    """A baseline on the same [B, H, T, d_h] inputs: kind "linear" (cumulative-sum
+    linear attention) or "delta" (DeltaNet, gate beta on the unit key).  Returns
+    ``o``, or ``(o, S, zkey)`` with ``return_state`` or a state output."""
+    torch = _torch()
+    B, H, T, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, (B, H, T, d), q.dtype, dev)
+    f32 = torch.float32
+    if o is None:
+        o = torch.empty((B, H, T, d), dtype=f32, device=dev)
+    want_state = return_state or S_out is not None or zkey_out is not None
+    if return_state:
+        S_out = torch.empty((B, H, d, d), dtype=f32, device=dev) if S_out is None else S_out
+        zkey_out = torch.empty((B, H, d), dtype=f32, device=dev) if zkey_out is None else zkey_out
+    _check(o, "o", (B, H, T, d), f32, dev)
+    for name, t, shp in (("S_out", S_out, (B, H, d, d)), ("zkey_out", zkey_out, (B, H, d)),
+                         ("S0", S0, (B, H, d, d)), ("zkey0", zkey0, (B, H, d))):
+        _check(t, name, shp, f32, dev)
+    need = baseline_workspace_size(B, H, T, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace: need {need} bytes")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().vla_baseline_forward(BASELINES[kind], _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
+                                     B, H, T, d, float(beta), float(eps), _ptr(o), _ptr(S_out),
+                                     _ptr(zkey_out), _ptr(S0), _ptr(zkey0), _ptr(workspace),
+                                     ws_bytes, _stream(stream))
+    if st != VLA_OK:
+        raise VLAError(st, "vla_baseline_forward")
+    return (o, S_out, zkey_out) if want_state else o
 
 
 def vla_step(q, k, v, u, S, A, zkey, eps: float = 1e-4, *, o=None, stream=None):

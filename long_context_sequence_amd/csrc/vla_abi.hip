@@ -240,6 +240,44 @@ extern "C" vla_status vla_backward(const void *q, const void *k, const void *v, 
     return vla::launch_backward(a) == hipSuccess ? VLA_OK : VLA_ERR_HIP;
 }
 
+extern "C" vla_status vla_baseline_workspace_size(int B, int H, int T, int d_h, size_t *bytes)
+{
+    if (!bytes || B < 1 || H < 1 || T < 0 || (long long)B * H > 0x7fffffffLL) return VLA_ERR_INVALID_ARG;
+    if (!vla::chunk_supported(d_h) || !vla::twopass_size_ok(T, d_h, false)) return VLA_ERR_UNSUPPORTED;
+    *bytes = vla::baseline_workspace_bytes(B * H, T, d_h);
+    return VLA_OK;
+}
+
+extern "C" vla_status vla_baseline_forward(vla_baseline kind, const void *q, const void *k,
+                                           const void *v, vla_dtype in_dtype, int B, int H, int T,
+                                           int d_h, float beta, float eps, float *o, float *S_out,
+                                           float *zkey_out, const float *S0, const float *zkey0,
+                                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (kind != VLA_BASELINE_LINEAR && kind != VLA_BASELINE_DELTA) return VLA_ERR_UNSUPPORTED;
+    vla_status st = check_common(in_dtype, B, H, d_h, eps);
+    if (st != VLA_OK) return st;
+    if (!vla::chunk_supported(d_h)) return VLA_ERR_UNSUPPORTED;
+    if (T < 0 || !isfinite(beta)) return VLA_ERR_INVALID_ARG;
+    if (!vla::twopass_size_ok(T, d_h, false)) return VLA_ERR_UNSUPPORTED;
+    const size_t need = vla::baseline_workspace_bytes(B * H, T, d_h);
+    if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < need))
+        return VLA_ERR_INVALID_ARG;
+    const bool need_tok = T > 0;
+    if (!ok_ptr(q, need_tok) || !ok_ptr(k, need_tok) || !ok_ptr(v, need_tok) || !ok_ptr(o, need_tok))
+        return VLA_ERR_INVALID_ARG;
+    if (!ok_ptr(S_out, false) || !ok_ptr(zkey_out, false) || !ok_ptr(S0, false) ||
+        !ok_ptr(zkey0, false))
+        return VLA_ERR_INVALID_ARG;
+    if (T == 0 && !S_out && !zkey_out) return VLA_OK;
+    vla::FwdArgs a{q, k, v, nullptr, in_dtype, B, H, T, d_h, 1.0f, eps,
+                   o, S_out, nullptr, zkey_out, S0, nullptr, zkey0, (hipStream_t)stream,
+                   workspace, workspace_bytes};
+    hipError_t e = T == 0 ? vla::launch_state_init(a)
+                          : vla::launch_baseline(a, kind == VLA_BASELINE_DELTA, beta);
+    return e == hipSuccess ? VLA_OK : VLA_ERR_HIP;
+}
+
 extern "C" const char *vla_status_string(vla_status status)
 {
     switch (status) {

@@ -62,6 +62,13 @@ bool twopass_size_ok(int T, int d, bool keep);
 // record of chunk c of head bh is at index bh * ceil(T / 16) + c
 size_t twopass_records_offset(int BH, int T, int d);
 hipError_t launch_forward_twopass(const FwdArgs &a, int phases);
+// the memory pass alone, on per-chunk records at rec laid out as the penalty
+// pass leaves them (vla_record.h); lin: records with k^ = 0 and (I + N)^-1 = I
+// (linear attention), whose errors are the values themselves
+hipError_t launch_memory_pass(const FwdArgs &a, const float *rec, bool lin);
+// the baselines (vla_baseline.hip): records from the inputs, then the memory pass
+size_t baseline_workspace_bytes(int BH, int T, int d);
+hipError_t launch_baseline(const FwdArgs &a, bool delta, float beta);
 // the memory chain as a scan over chunks (d_h = 64, T >= 1): the penalty pass,
 // then per-chunk affine maps of S, a work-efficient scan of them and the
 // chunk-local readout; needs the workspace below.

@@ -701,7 +701,11 @@ struct MemOps {
 // With SAVE, the errors e_t also go to the per-token records (Keep): key split
 // 0 writes chunk a's, key split 1 chunk b's, the others store through an empty
 // view, so that every wave issues the same number of stores.
-template <int D, typename Tin, bool SAVE = false>
+//
+// With LIN (records of cumulative-sum linear attention: k^ = 0 and
+// (I + N)^-1 = I), the errors are the values themselves, so the products with
+// K^ and the triangular solves are skipped.
+template <int D, typename Tin, bool SAVE = false, bool LIN = false>
 __global__ void __launch_bounds__(64 * MemCfg<D>::VBW * MemCfg<D>::KS)
 vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec, const float *S0,
         float *__restrict__ o, float *S_out, float *kept_all = nullptr)
@@ -788,11 +792,11 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
         const float *c = s + xc * RS;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            m.ak[t] = ld4(c + R::KH + swzd<D>(n, 4 * (rho0 + t) + g));
+            if constexpr (!LIN) m.ak[t] = ld4(c + R::KH + swzd<D>(n, 4 * (rho0 + t) + g));
             m.ap[t] = ld4(c + R::PH + swzd<D>(n, 4 * (rho0 + t) + g));
             m.aw[t] = ld4(c + R::AH + swz16(16 * (rho0 + t) + n, g));
         }
-        m.ta = ld4(c + R::TT + swz16(n, g));
+        if constexpr (!LIN) m.ta = ld4(c + R::TT + swz16(n, g));
         m.pa = ld4(c + R::PT + swz16(n, g));
         m.rd = c[R::RD + n];
         const Tin *vs = reinterpret_cast<const Tin *>(s + MS::VOFF);
@@ -829,6 +833,12 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
 #pragma unroll
         for (int r = 0; r < 4; ++r) vm[r] = m.v[r] - sk[r];
         return mma4(m.ta, vm, zero);
+    };
+    auto values = [&](const MemOps<NT> &m) {   // E' = V' (linear attention)
+        f4 vm;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vm[r] = m.v[r];
+        return vm;
     };
     // o of chunk c (value x token) from this wave when it writes it (others
     // store through an empty view, so that every store is unconditional)
@@ -868,21 +878,24 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
         MemOps<NT> ma, mb;
         ops(s, 0, ma);
         ops(s, 1, mb);
-        const f4 qk = ld4(s + R::QK + swz16(n, g)), qp = ld4(s + R::QP + swz16(n, g));
-        st4(&red[sl][w][0][lane * 4], sk_part(ma.ak));
-        st4(&red[sl][w][1][lane * 4], sk_part(mb.ak));
+        const f4 qp = ld4(s + R::QP + swz16(n, g));
+        f4 qk = zero;
+        if constexpr (!LIN) {
+            qk = ld4(s + R::QK + swz16(n, g));
+            st4(&red[sl][w][0][lane * 4], sk_part(ma.ak));
+            st4(&red[sl][w][1][lane * 4], sk_part(mb.ak));
+        }
         // the S Phi partials are formed before the barrier and go to LDS after
         // it (read one step later)
         const f4 sqa = sq_part(ma.ap), sqb = sq_part(mb.ap);
         wait_next();
         lds_barrier();
-        const f4 r0 = reduce(sl, 0);
         stage_part(ic<0>{}, pm + NS, s);
-        const f4 ea = errors(ma, r0);
+        const f4 ea = LIN ? values(ma) : errors(ma, reduce(sl, 0));
         stage_part(ic<1>{}, pm + NS, s);
         const f4 ob = readout(sl ^ 1);   // pair pm - 1 (nothing at pm = 0)
         stage_part(ic<2>{}, pm + NS, s);
-        const f4 eb = errors(mb, mma4(qk, ea, reduce(sl, 1)));
+        const f4 eb = LIN ? values(mb) : errors(mb, mma4(qk, ea, reduce(sl, 1)));
         stage_part(ic<3>{}, pm + NS, s);
         update(ma, ea);
         stage_part(ic<4>{}, pm + NS, s);
@@ -928,11 +941,10 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
         const float *s = k == 0 ? stg0 : (k == 1 ? stg1 : stg2);
         MemOps<NT> m;
         ops(s, 0, m);
-        const f4 sk = sk_part(m.ak), sq = sq_part(m.ap);
-        st4(&red[sl][w][0][lane * 4], sk);
-        st4(&red[sl][w][2][lane * 4], sq);
+        if constexpr (!LIN) st4(&red[sl][w][0][lane * 4], sk_part(m.ak));
+        st4(&red[sl][w][2][lane * 4], sq_part(m.ap));
         lds_barrier();
-        const f4 e = errors(m, reduce(sl, 0));
+        const f4 e = LIN ? values(m) : errors(m, reduce(sl, 0));
         store_o(c, ks == 0, mma4(e, m.pa, reduce(sl, 2)), m.rd);
         if constexpr (SAVE) keep_e(c, ks == 0, e);
         update(m, e);
@@ -1036,7 +1048,33 @@ hipError_t launch(const FwdArgs &a, int phases)
     return hipGetLastError();
 }
 
+template <int D, typename Tin>
+hipError_t launch_mem_only(const FwdArgs &a, const float *rec, bool lin)
+{
+    constexpr int NG = (D / 16) / MemCfg<D>::VBW;
+    const int BH = a.B * a.H;
+    const dim3 grid(BH * NG), block(64 * MemCfg<D>::VBW * MemCfg<D>::KS);
+    if (lin)
+        hipLaunchKernelGGL((vla_mem<D, Tin, false, true>), grid, block, 0, a.stream,
+                           (const Tin *)a.v, a.T, BH, rec, a.S0, a.o, a.S_out, nullptr);
+    else
+        hipLaunchKernelGGL((vla_mem<D, Tin>), grid, block, 0, a.stream, (const Tin *)a.v, a.T, BH,
+                           rec, a.S0, a.o, a.S_out, nullptr);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_memory_pass(const FwdArgs &a, const float *rec, bool lin)
+{
+    const bool bf = a.dtype == 1;
+    switch (a.d) {
+    case 64: return bf ? launch_mem_only<64, uint16_t>(a, rec, lin) : launch_mem_only<64, float>(a, rec, lin);
+    case 96: return bf ? launch_mem_only<96, uint16_t>(a, rec, lin) : launch_mem_only<96, float>(a, rec, lin);
+    case 128: return bf ? launch_mem_only<128, uint16_t>(a, rec, lin) : launch_mem_only<128, float>(a, rec, lin);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 bool chunk_supported(int d) { return d == 64 || d == 96 || d == 128; }
 

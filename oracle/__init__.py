@@ -66,10 +66,10 @@ def _load():
         f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double] + [_dp] * 18
         f = lib.vla_oracle_linear_attention
         f.restype = ctypes.c_int
-        f.argtypes = [ctypes.c_int, ctypes.c_int] + [_dp] * 8
+        f.argtypes = [ctypes.c_int, ctypes.c_int] + [_dp] * 9
         f = lib.vla_oracle_deltanet
         f.restype = ctypes.c_int
-        f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double] + [_dp] * 8
+        f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double] + [_dp] * 9
         _lib = lib
     return _lib
 
@@ -223,34 +223,37 @@ def backward_head_checkpointed(q, k, v, u, dO, lambda0=0.1, eps=1e-4, S0=None, A
 
 def linear_attention_head(q, k, v, S0=None, zkey0=None):
     """Cumulative-sum linear attention ("Linear Attention" wiki article,
-    recurrent form) on one head: q, k, v are [T, d].  Returns ``o`` [T, d] and
-    the final ``S`` [d, d] (value-major, S += v phi(k)') and ``zkey`` [d]."""
+    recurrent form) on one head: q, k, v are [T, d].  Returns ``o`` [T, d], the
+    final ``S`` [d, d] (value-major, S += v phi(k)') and ``zkey`` [d], and
+    ``scale`` [T] = |S_t|_F |phi(q_t)| / den_t (the size of o_t without
+    cancellation)."""
     q = _f64(q)
     T, d = q.shape
     k, v = _f64(k, (T, d)), _f64(v, (T, d))
     S0, zkey0 = _f64(S0, (d, d)), _f64(zkey0, (d,))
-    o, S, zk = np.zeros((T, d)), np.zeros((d, d)), np.zeros(d)
+    o, S, zk, sc = np.zeros((T, d)), np.zeros((d, d)), np.zeros(d), np.zeros(T)
     rc = _load().vla_oracle_linear_attention(T, d, _ptr(q), _ptr(k), _ptr(v), _ptr(S0),
-                                             _ptr(zkey0), _ptr(o), _ptr(S), _ptr(zk))
+                                             _ptr(zkey0), _ptr(o), _ptr(S), _ptr(zk), _ptr(sc))
     if rc != 0:
         raise ValueError(f"vla_oracle_linear_attention failed with code {rc}")
-    return dict(o=o, S=S, zkey=zk)
+    return dict(o=o, S=S, zkey=zk, scale=sc)
 
 
 def deltanet_head(q, k, v, beta=1.0, eps=1e-4, S0=None, zkey0=None):
     """DeltaNet as the VLA layer with the scalar gate beta in place of alpha^ and
     no A (delta rule on the unit key; Eq. (11) readout), one head.  Returns ``o``
-    [T, d], the final ``S`` [d, d] and ``zkey`` [d]."""
+    [T, d], the final ``S`` [d, d] and ``zkey`` [d], and ``scale`` [T] as for
+    ``linear_attention_head``."""
     q = _f64(q)
     T, d = q.shape
     k, v = _f64(k, (T, d)), _f64(v, (T, d))
     S0, zkey0 = _f64(S0, (d, d)), _f64(zkey0, (d,))
-    o, S, zk = np.zeros((T, d)), np.zeros((d, d)), np.zeros(d)
+    o, S, zk, sc = np.zeros((T, d)), np.zeros((d, d)), np.zeros(d), np.zeros(T)
     rc = _load().vla_oracle_deltanet(T, d, float(beta), float(eps), _ptr(q), _ptr(k), _ptr(v),
-                                     _ptr(S0), _ptr(zkey0), _ptr(o), _ptr(S), _ptr(zk))
+                                     _ptr(S0), _ptr(zkey0), _ptr(o), _ptr(S), _ptr(zk), _ptr(sc))
     if rc != 0:
         raise ValueError(f"vla_oracle_deltanet failed with code {rc}")
-    return dict(o=o, S=S, zkey=zk)
+    return dict(o=o, S=S, zkey=zk, scale=sc)
 
 
 def baseline(kind, q, k, v, beta=1.0, eps=1e-4, S0=None, zkey0=None, workers=None):
@@ -258,7 +261,8 @@ def baseline(kind, q, k, v, beta=1.0, eps=1e-4, S0=None, zkey0=None, workers=Non
     pool over heads).  Returns ``o``, ``S``, ``zkey``."""
     q = np.asarray(q)
     B, H, T, d = q.shape
-    res = dict(o=np.zeros((B, H, T, d)), S=np.zeros((B, H, d, d)), zkey=np.zeros((B, H, d)))
+    res = dict(o=np.zeros((B, H, T, d)), S=np.zeros((B, H, d, d)), zkey=np.zeros((B, H, d)),
+               scale=np.zeros((B, H, T)))
 
     def one(bh):
         b, h = divmod(bh, H)

@@ -410,11 +410,13 @@ out:
  * readout has no floor; phi > 0 keeps the denominator positive.
  *
  * q, k, v : [T][d];  S0 [d][d] and zkey0 [d] or NULL (zero);  o [T][d];
- * S [d][d], zkey [d] out.  Returns 0 or nonzero on bad arguments.
+ * S [d][d], zkey [d] out;  tr_scale [T] or NULL: per token
+ * |S_t|_F |phi(q_t)| / den_t, the size o_t has when nothing cancels.
+ * Returns 0 or nonzero on bad arguments.
  */
 int vla_oracle_linear_attention(int T, int d, const double *q, const double *k, const double *v,
                                 const double *S0, const double *zkey0,
-                                double *o, double *S, double *zkey)
+                                double *o, double *S, double *zkey, double *tr_scale)
 {
     if (T < 0 || d < 1 || !S || !zkey) return VLA_ORACLE_EINVAL;
     if (T > 0 && (!q || !k || !v || !o)) return VLA_ORACLE_EINVAL;
@@ -438,6 +440,7 @@ int vla_oracle_linear_attention(int T, int d, const double *q, const double *k, 
         matvec(S, pq, num, d);
         const double den = dot(pq, zkey, d);
         for (int i = 0; i < d; ++i) o[(size_t)t * d + i] = num[i] / den;
+        if (tr_scale) tr_scale[t] = sqrt(dot(S, S, d * d) * dot(pq, pq, d)) / den;
     }
     free(work);
     return VLA_ORACLE_OK;
@@ -453,11 +456,12 @@ int vla_oracle_linear_attention(int T, int d, const double *q, const double *k, 
  * and the readout is Eq. (11) unchanged (raw-key phi sum, max(., eps) floor).
  *
  * q, k, v : [T][d];  S0 [d][d], zkey0 [d] or NULL (zero);  o [T][d];
- * S [d][d], zkey [d] out.  Returns 0 or nonzero on bad arguments.
+ * S [d][d], zkey [d] out;  tr_scale [T] or NULL: per token
+ * |S_t|_F |phi(q_t)| / den_t.  Returns 0 or nonzero on bad arguments.
  */
 int vla_oracle_deltanet(int T, int d, double beta, double eps, const double *q, const double *k,
                         const double *v, const double *S0, const double *zkey0,
-                        double *o, double *S, double *zkey)
+                        double *o, double *S, double *zkey, double *tr_scale)
 {
     if (T < 0 || d < 1 || !(eps > 0.0) || !S || !zkey) return VLA_ORACLE_EINVAL;
     if (T > 0 && (!q || !k || !v || !o)) return VLA_ORACLE_EINVAL;
@@ -484,6 +488,7 @@ int vla_oracle_deltanet(int T, int d, double beta, double eps, const double *q, 
         if (den < eps) den = eps;
         matvec(S, pq, num, d);
         for (int i = 0; i < d; ++i) o[(size_t)t * d + i] = num[i] / den;
+        if (tr_scale) tr_scale[t] = sqrt(dot(S, S, d * d) * dot(pq, pq, d)) / den;
     }
     free(work);
     return VLA_ORACLE_OK;

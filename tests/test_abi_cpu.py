@@ -308,3 +308,35 @@ def test_noalloc_argument_errors_and_size_limit():
     assert vla.workspace_size(4, 8, 1024, 64) <= vla.NOALLOC_SCRATCH_BYTES
     # T = 0 with no outputs: nothing to do, nothing touched
     assert _noalloc(T=0, q=None, k=None, v=None, u=None, o=None) == B.VLA_OK
+
+
+def test_baseline_argument_errors():
+    lib = B.load()
+
+    def call(**kw):
+        a = dict(kind=0, q=FAKE, k=FAKE, v=FAKE, dt=1, B=1, H=2, T=32, d=64, beta=1.0,
+                 eps=1e-4, o=FAKE, S=None, z=None, S0=None, z0=None, ws=FAKE, ws_bytes=1 << 40)
+        a.update(kw)
+        return lib.vla_baseline_forward(a["kind"], a["q"], a["k"], a["v"], a["dt"], a["B"],
+                                        a["H"], a["T"], a["d"], a["beta"], a["eps"], a["o"],
+                                        a["S"], a["z"], a["S0"], a["z0"], a["ws"], a["ws_bytes"],
+                                        None)
+    assert call(kind=2) == B.VLA_ERR_UNSUPPORTED
+    assert call(d=32) == B.VLA_ERR_UNSUPPORTED
+    assert call(d=48) == B.VLA_ERR_UNSUPPORTED
+    assert call(dt=7) == B.VLA_ERR_UNSUPPORTED
+    assert call(q=None) == B.VLA_ERR_INVALID_ARG
+    assert call(v=MIS) == B.VLA_ERR_INVALID_ARG
+    assert call(o=None) == B.VLA_ERR_INVALID_ARG
+    assert call(beta=float("nan")) == B.VLA_ERR_INVALID_ARG
+    assert call(eps=0.0) == B.VLA_ERR_INVALID_ARG
+    assert call(T=-1) == B.VLA_ERR_INVALID_ARG
+    assert call(ws=None) == B.VLA_ERR_INVALID_ARG
+    assert call(ws_bytes=1024) == B.VLA_ERR_INVALID_ARG
+    assert call(T=0, q=None, k=None, v=None, o=None, ws=None) == B.VLA_OK
+    # records as the forward's (48 d + 1040 floats per chunk) plus fp64 group sums
+    n = vla.baseline_workspace_size(2, 3, 1000, 64)
+    assert n >= 2 * 3 * 63 * (48 * 64 + 1040) * 4 and n % 256 == 0
+    assert vla.baseline_workspace_size(1, 1, 0, 96) == 0
+    with pytest.raises(vla.VLAError):
+        vla.baseline_workspace_size(1, 1, 16, 32)

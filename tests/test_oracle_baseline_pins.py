@@ -155,3 +155,19 @@ def test_baseline_all_heads_wrapper():
                    else oracle.deltanet_head(q[0, h], k[0, h], v[0, h], 0.6, 1e-4))
             for key in one:
                 np.testing.assert_array_equal(res[key][0, h], one[key])
+
+
+def test_baseline_scale_trace():
+    """The per-token scale is |S_t|_F |phi(q_t)| / den_t with S_t the state after
+    token t (checked against runs over each prefix)."""
+    T, d = 7, 5
+    q, k, v = _draw(T, d, 11)
+    for fn, args in ((oracle.linear_attention_head, ()), (oracle.deltanet_head, (0.8, 1e-4))):
+        r = fn(q, k, v, *args)
+        for t in range(T):
+            p = fn(q[:t + 1], k[:t + 1], v[:t + 1], *args)
+            den = _phi(q[t]) @ p["zkey"]
+            if fn is oracle.deltanet_head:
+                den = max(den, 1e-4)
+            want = np.linalg.norm(p["S"]) * np.linalg.norm(_phi(q[t])) / den
+            assert abs(r["scale"][t] - want) <= 1e-12 * want
