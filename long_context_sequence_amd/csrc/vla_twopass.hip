@@ -212,7 +212,7 @@ __device__ __forceinline__ void sweep_all(double (&m)[EPT], int i, int c0, doubl
         if (i >= k && i < k + 4) {
             double *rw = rowbuf[slot] + (i - k) * D;
             sfor<EPT>([&](auto e) { rw[c0 + e] = c0 + e == i ? m[e] - 1.0 : m[e]; });
-            wave_lds_order();   // rows K sit in one wave (threads 8k .. 8k+31)
+            wave_lds_order();   // rows K sit in one wave (threads 4 TPR s .. 4 TPR s + 4 TPR - 1)
             // B^-1 = adj(B) / det(B), one entry per lane in the first 16
             // publishing lanes (the same instructions in each: det(B) from the
             // 2 x 2 minors of rows 0-1 and 2-3, entry (r, c) from the 3 x 3
@@ -300,15 +300,15 @@ __device__ __forceinline__ void sweep_all(double (&m)[EPT], int i, int c0, doubl
 // the initial one.
 // threads per matrix row of the inverse (the penalty pass measured 404 us with
 // 8, 408 with 4 and 415 with 16 on the bench workload)
-constexpr int SEG_TPR = 8;
+template <int D> constexpr int seg_tpr() { return 8; }
 
 template <int D>
-__global__ void __launch_bounds__(SEG_TPR * D)
+__global__ void __launch_bounds__(seg_tpr<D>() * D)
 vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
            const double *__restrict__ gram, const double *__restrict__ zks,
            float *__restrict__ aseg, float *__restrict__ zseg)
 {
-    constexpr int EPT = D / SEG_TPR;
+    constexpr int SEG_TPR = seg_tpr<D>(), EPT = D / SEG_TPR;
     __shared__ __align__(16) double rowbuf[2][4 * D + 16];
     const int S1 = S - 1;
     const int bh = blockIdx.x / S1, j = blockIdx.x % S1 + 1;
@@ -325,7 +325,9 @@ vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
     } else {
         sfor<EPT>([&](auto e) { m[e] = i == c0 + e ? (double)lambda0 : 0.0; });
     }
-    // G parts of the segments before j, in order, loads four parts ahead
+    // G parts of the segments before j, in order, loads NPF parts ahead (two at
+    // d = 128, where 1024 threads have at most 128 registers each)
+    constexpr int NPF = D == 128 ? 2 : 4;
     const int NPART = j * P;
     const double *gb = gram + (size_t)bh * S1 * P * DD + (size_t)i * D + c0;
     auto add_part = [&](const double2 (&x)[EPT / 2]) {
@@ -335,13 +337,13 @@ vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
         });
     };
     int s = 0;
-    for (; s + 4 <= NPART; s += 4) {
-        double2 x[4][EPT / 2];
-        sfor<4>([&](auto v) {
+    for (; s + NPF <= NPART; s += NPF) {
+        double2 x[NPF][EPT / 2];
+        sfor<NPF>([&](auto v) {
             const double2 *G = reinterpret_cast<const double2 *>(gb + (size_t)(s + v) * DD);
             sfor<EPT / 2>([&](auto h) { x[v][h] = G[h]; });
         });
-        sfor<4>([&](auto v) { add_part(x[v]); });
+        sfor<NPF>([&](auto v) { add_part(x[v]); });
     }
     for (; s < NPART; ++s) {
         double2 x[EPT / 2];
@@ -371,28 +373,32 @@ vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
 // LDS of a penalty workgroup (the members the steps of Head use).
 template <int D>
 struct PLds {
+    // the small, often-read arrays first, so that their offsets fit the 16-bit
+    // immediate offsets of LDS instructions
     static constexpr int C = Cfg<D>::C, NA = Cfg<D>::NA, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
-    float uh[C * LD];        // u^ [token][i] of the chunk whose Z0 is formed next
-    float kh[2][C * LD];     // k^, by chunk parity
-    float ph[2][C * LD];     // phi(q), by chunk parity
-    float zk[2][C * LD];     // phi(k), then the inclusive key sum, by chunk parity
-    float z0t[2][D * LT];    // Z0 [i][token], by chunk parity
-    float wt[D * LT];        // W [i][token] of the last updated chunk
     float gp[NA][2][C * LT]; // per wave: partials of I + U^'Z0 and Z0'K^
-    float nrm[NA][C];        // per wave: partial |w_t|^2
     float nq[NA][2][C * LT]; // per wave: partials of W'K^ and W'Phi
+    float nrm[NA][C];        // per wave: partial |w_t|^2
     union {                  // L^-1 scratch of the factorisation / (I+N)^-1 scratch
         float lit[NA][C * LT];
         float tit[NA][C * LT];
     };
     float inv[NA][C];
     float hms[256];          // A operand of W' (per lane), from wave 0
+    float wt[D * LT];        // W [i][token] of the last updated chunk
+    float z0t[2][D * LT];    // Z0 [i][token], by chunk parity
+    float uh[C * LD];        // u^ [token][i] of the chunk whose Z0 is formed next
+    float kh[2][C * LD];     // k^, by chunk parity
+    float ph[2][C * LD];     // phi(q), by chunk parity
+    float zk[2][C * LD];     // phi(k), then the inclusive key sum, by chunk parity
 };
 
-// Staging of the penalty pass by its last two waves, 8 lanes per token (lane
+// Staging of the penalty pass by its last NWS waves, LPT lanes per token (lane
 // cc of token tl holds columns [cc CP, +CP)): raw q, k, u of a chunk into
 // registers, then k^, u^, phi(q), phi(k) into LDS, k^ and phi(q) also to the
-// chunk's record; later the readout denominators of the chunk.
+// chunk's record; later the readout denominators of the chunk.  With six waves
+// (d = 96) four of them stage, 16 lanes per token, so that the raw inputs held
+// across the update phase take half the registers.
 __device__ __forceinline__ float sum_row8(float x)
 {
     x += dpp<0xB1>(x);
@@ -403,13 +409,20 @@ __device__ __forceinline__ float sum_row8(float x)
 
 template <int D, typename Tin, bool SAVE = false>
 struct PenStage {
-    static constexpr int LD = Cfg<D>::LD, CP = D / 8;
+    static constexpr int LPT = Cfg<D>::NA >= 6 ? 16 : 8;   // lanes per token
+    static constexpr int NWS = LPT * CH / 64;              // staging waves
+    static constexpr int LD = Cfg<D>::LD, CP = D / LPT;
     int tl, cc;
     bool on;
     RawVec<Tin, CP> rq, rk, ru;
     __device__ __forceinline__ explicit PenStage(int ts)
-        : tl((ts >> 3) & (CH - 1)), cc(ts & 7), on(ts >= 0 && ts < 8 * CH)
+        : tl((ts / LPT) & (CH - 1)), cc(ts % LPT), on(ts >= 0 && ts < LPT * CH)
     {
+    }
+    __device__ __forceinline__ static float row_sum(float x)
+    {
+        if constexpr (LPT == 16) return sum_row16(x);
+        else return sum_row8(x);
     }
     // rows past T re-read row T-1 (stage zeroes k^, u^ and phi(k) there)
     __device__ __forceinline__ void prefetch(const Tin *q, const Tin *k, const Tin *u, size_t tok0,
@@ -434,7 +447,7 @@ struct PenStage {
             pk = fmaf(rk.get(i), rk.get(i), pk);
             pu = fmaf(ru.get(i), ru.get(i), pu);
         }
-        const float nk = sum_row8(pk), nu = sum_row8(pu);
+        const float nk = row_sum(pk), nu = row_sum(pu);
         const float ik = ok && nk > 0.f ? rsqrtf(nk) : 0.f;
         const float iu = ok && nu > 0.f ? rsqrtf(nu) : 0.f;
         if constexpr (SAVE) {
@@ -466,14 +479,19 @@ struct PenStage {
         float pd = 0.f;
 #pragma unroll
         for (int i = 0; i < CP; ++i) pd = fmaf(L.ph[slot][e0 + i], L.zk[slot][e0 + i], pd);
-        pd = sum_row8(pd);
+        pd = row_sum(pd);
         if (cc == 0) rrd[tl] = __builtin_amdgcn_rcpf(fmaxf(pd, eps));
         if constexpr (SAVE) {
             if (cq * CH + tl < T) {
                 float *kt = kept + (size_t)(cq * CH + tl) * Keep<D>::RS;
+                if constexpr (CP % 4 == 0) {
 #pragma unroll
-                for (int i = 0; i < CP; i += 4)
-                    st4(kt + Keep<D>::ZK + cc * CP + i, ld4(&L.zk[slot][e0 + i]));
+                    for (int i = 0; i < CP; i += 4)
+                        st4(kt + Keep<D>::ZK + cc * CP + i, ld4(&L.zk[slot][e0 + i]));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < CP; ++i) kt[Keep<D>::ZK + cc * CP + i] = L.zk[slot][e0 + i];
+                }
                 if (cc == 0) kt[Keep<D>::SC + 2] = pd;
             }
         }
@@ -557,7 +575,7 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     // the C x C factors of the record, the waves from 2 on own the key sums, and
     // the last two waves stage the inputs
     Hd hd(L, tid & 63, w, tid - 128);
-    PenStage<D, Tin, SAVE> ps(tid - 64 * (NA - 2));
+    PenStage<D, Tin, SAVE> ps(tid - 64 * (NA - PenStage<D, Tin, SAVE>::NWS));
     float *kept = SAVE ? kept_all + (size_t)bh * T * Keep<D>::RS : nullptr;
     typename Hd::State st;
     const float *a_init;
@@ -1022,7 +1040,7 @@ hipError_t launch(const FwdArgs &a, int phases)
         if (p.S > 1) {
             hipLaunchKernelGGL((vla_gram<D, Tin>), dim3(BH * (p.S - 1) * p.P), dim3(256), 0, a.stream,
                                k, u, a.T, p.S, p.SC, p.P, gram, zks);
-            hipLaunchKernelGGL((vla_seginv<D>), dim3(BH * (p.S - 1)), dim3(SEG_TPR * D), 0, a.stream, p.S,
+            hipLaunchKernelGGL((vla_seginv<D>), dim3(BH * (p.S - 1)), dim3(seg_tpr<D>() * D), 0, a.stream, p.S,
                                p.P, a.lambda0, a.A0, a.zk0, gram, zks, aseg, zseg);
         }
         if (a.keep)
