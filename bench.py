@@ -389,7 +389,12 @@ def decode_continuation(vla, torch, cfg, x, state):
     """cfg.decode single-token steps (vla_step) continuing from the forward's
     final state, on the workload's decode tokens.  Each step reads and writes
     the fp32 state (S, A: d^2 each, zkey: d) of every head and reads its four
-    input vectors; the state traffic is reported against the HBM peak."""
+    input vectors; the state traffic is reported against the HBM peak.
+
+    Timed two ways over the same steps: captured once in a HIP graph (one kernel
+    node per token, as a serving loop launches them; us_per_step) and launched
+    one Python call per token (us_per_step_eager, bound by the host's launch
+    rate).  The state is reset to the forward's final state before each."""
     B, H, d, n = cfg.B, cfg.H, cfg.d, cfg.decode
     dev = torch.device("cuda:0")
     S, A, zk = (a.clone() for a in state)
@@ -399,24 +404,48 @@ def decode_continuation(vla, torch, cfg, x, state):
         a = a.view(torch.bfloat16) if cfg.dtype == "bf16" else a
         dec[nm] = a.permute(2, 0, 1, 3).contiguous()   # [steps, B, H, d]
     o = torch.empty((n, B, H, d), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-    for i in range(8):   # warm-up on scratch copies of the state
-        vla.vla_step(dec["q"][i], dec["k"][i], dec["v"][i], dec["u"][i], S.clone(), A.clone(),
-                     zk.clone(), cfg.eps, o=o[i], stream=stream)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(n):
+
+    def reset():
+        for dst, src in zip((S, A, zk), state):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    def run(i):
         vla.vla_step(dec["q"][i], dec["k"][i], dec["v"][i], dec["u"][i], S, A, zk, cfg.eps,
-                     o=o[i], stream=stream)
-    e1.record(stream)
+                     o=o[i], stream=torch.cuda.current_stream())
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(8):   # warm-up
+        run(i)
+    reset()
+    e0.record()
+    for i in range(n):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us_eager = e0.elapsed_time(e1) * 1e3 / n
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(n):
+                run(i)
+    reset()
+    graph.replay()   # warm-up replay
+    reset()
+    e0.record()
+    graph.replay()
+    e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / n
+    del graph
     s_in = 2 if cfg.dtype == "bf16" else 4
     state_bytes = B * H * (2 * (2 * d * d + d) * 4 + 4 * d * s_in + d * 4)
     gbps = state_bytes / (us * 1e-6) / 1e9
     return {"steps": n, "from": f"the forward's final state after T={cfg.T}",
-            "us_per_step": us, "tokens_heads_per_s": B * H / (us * 1e-6),
+            "us_per_step": us, "launch": "HIP graph, one node per token",
+            "us_per_step_eager": us_eager, "tokens_heads_per_s": B * H / (us * 1e-6),
             "bytes_per_step": state_bytes, "GBps": gbps, "hbm_frac": gbps / 8000.0}
 
 

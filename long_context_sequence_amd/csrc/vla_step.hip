@@ -11,8 +11,12 @@
 // both products with S use the old S (S_new phi(q) = S phi(q) + e (alpha^'phi(q))),
 // so each state is read once and written once.
 //
-// One workgroup per head, 1024 threads: thread i holds EPT consecutive columns
-// of one row of A and of S (TPR threads per row), so that the row products are
+// One workgroup per head, 1024 threads: the TPR adjacent threads of a row hold
+// its 16-byte granules round-robin (thread g of the row holds granules g, g+TPR,
+// g+2 TPR, ...), so that one load or store instruction of a wave covers whole
+// 128-byte lines of TPR/2 ... rows (a thread holding consecutive columns makes
+// each instruction touch every line at a quarter of its width, which halves
+// the rate at which one CU writes the state back); the row products are
 // reductions over adjacent lanes; the d-vectors live in LDS, and the scalars
 // (delta, z'k^, |y|, y'phi(q), the denominator) are formed by every wave the
 // same way from them.  Each thread writes back exactly the elements it read.
@@ -28,6 +32,7 @@ template <int D>
 struct StepCfg {
     static constexpr int TPR = D == 64 ? 16 : 8;   // threads per row
     static constexpr int EPT = D / TPR;            // columns per thread (4, 12, 16)
+    static constexpr int NG = EPT / 4;             // granules per thread
     static constexpr int ACTIVE = D * TPR;         // threads holding a row slice
     static_assert(EPT % 4 == 0 && ACTIVE <= 1024, "row slices of whole 16-byte granules");
 };
@@ -46,27 +51,37 @@ vla_decode(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__re
     const int bh = blockIdx.x;
     const size_t DD = (size_t)D * D;
     const bool act = tid < Cf::ACTIVE;
-    const int row = act ? tid / TPR : 0, c0 = (tid % TPR) * EPT;
+    const int row = act ? tid / TPR : 0, g = tid % TPR;
+    // column of element e = 4 h + r of this thread (granule g + TPR h)
+    auto col = [&](int e) { return 4 * (g + TPR * (e >> 2)) + (e & 3); };
 
-    // state slices first, so that their loads overlap the vector set-up
+    // the token's vectors first (their wait then leaves the state loads in flight)
+    float xq = 0.f, xk = 0.f, xv = 0.f, xu = 0.f, xz = 0.f;
+    if (tid < D) {
+        const size_t off = (size_t)bh * D + tid;
+        xq = load_in(q, off);
+        xk = load_in(k, off);
+        xv = load_in(v, off);
+        xu = load_in(u, off);
+        xz = zkey[off];
+    }
     float a[EPT], s[EPT];
-    float *Ah = A + bh * DD + (size_t)row * D + c0, *Sh = S + bh * DD + (size_t)row * D + c0;
+    float *Ah = A + bh * DD + (size_t)row * D + 4 * g, *Sh = S + bh * DD + (size_t)row * D + 4 * g;
     if (act) {
-        sfor<EPT / 4>([&](auto h) {
-            const f4 x = ld4(Ah + 4 * h), y = ld4(Sh + 4 * h);
+        sfor<Cf::NG>([&](auto h) {
+            const f4 x = ld4(Ah + 4 * TPR * h), y = ld4(Sh + 4 * TPR * h);
             sfor<4>([&](auto r) {
                 a[4 * h + r] = x[int(r)];
                 s[4 * h + r] = y[int(r)];
             });
         });
     }
-    if (tid < D) {
-        const size_t off = (size_t)bh * D + tid;
-        qf[tid] = load_in(q, off);
-        kf[tid] = load_in(k, off);
-        vf[tid] = load_in(v, off);
-        uf[tid] = load_in(u, off);
-        zkf[tid] = zkey[off];
+    if (tid < D) {           // phi(q) and the new key sum zkey + phi(k) are kept
+        qf[tid] = phi_fast(xq);
+        kf[tid] = xk;
+        vf[tid] = xv;
+        uf[tid] = xu;
+        zkf[tid] = xz + phi_fast(xk);
     }
     __syncthreads();
 
@@ -83,17 +98,19 @@ vla_decode(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__re
     pu = wave_sum(pu);
     const float ik = pk > 0.f ? rsqrtf(pk) : 0.f, iu = pu > 0.f ? rsqrtf(pu) : 0.f;
 
-    // row products: z = A u^, w = A k^ (old A), r = S k^, p = S phi(q) (old S)
+    // row products: z = A u^, w = A k^ (old A), r = S k^, p = S phi(q) (old S),
+    // with the raw u and k and the inverse norms applied to the sums
     float pz = 0.f, pw = 0.f, pr = 0.f, pp = 0.f;
     sfor<EPT>([&](auto e) {
-        const int j = c0 + e;
-        const float uj = uf[j] * iu, kj = kf[j] * ik, fq = phi_fast(qf[j]);
+        const int j = col(e);
+        const float uj = uf[j], kj = kf[j];
         pz = fmaf(a[e], uj, pz);
         pw = fmaf(a[e], kj, pw);
         pr = fmaf(s[e], kj, pr);
-        pp = fmaf(s[e], fq, pp);
+        pp = fmaf(s[e], qf[j], pp);
     });
-    pz = row_sum<TPR>(pz), pw = row_sum<TPR>(pw), pr = row_sum<TPR>(pr), pp = row_sum<TPR>(pp);
+    pz = row_sum<TPR>(pz) * iu, pw = row_sum<TPR>(pw) * ik;
+    pr = row_sum<TPR>(pr) * ik, pp = row_sum<TPR>(pp);
     if (act && tid % TPR == 0) {
         zs[row] = pz;
         ws[row] = pw;
@@ -105,20 +122,20 @@ vla_decode(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__re
     sfor<NV>([&](auto c) {
         const int j = lane + 64 * c;
         if (j < D) {
-            du = fmaf(uf[j] * iu, zs[j], du);
-            dk = fmaf(zs[j], kf[j] * ik, dk);
+            du = fmaf(uf[j], zs[j], du);
+            dk = fmaf(zs[j], kf[j], dk);
         }
     });
-    const float delta = 1.f + wave_sum(du), zk = wave_sum(dk);
+    const float delta = fmaf(wave_sum(du), iu, 1.f), zk = wave_sum(dk) * ik;
     const float ci = zk / delta, id = 1.f / delta;
     float yy = 0.f, yq = 0.f, dn = 0.f;
     sfor<NV>([&](auto c) {
         const int j = lane + 64 * c;
         if (j < D) {
-            const float yj = ws[j] - zs[j] * ci, fq = phi_fast(qf[j]);
+            const float yj = ws[j] - zs[j] * ci, fq = qf[j];
             yy = fmaf(yj, yj, yy);
             yq = fmaf(yj, fq, yq);
-            dn = fmaf(fq, zkf[j] + phi_fast(kf[j]), dn);
+            dn = fmaf(fq, zkf[j], dn);
         }
     });
     yy = wave_sum(yy);
@@ -129,17 +146,17 @@ vla_decode(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__re
     if (act) {
         const float zi = pz, ei = vf[row] - pr;
         sfor<EPT>([&](auto e) {
-            const int j = c0 + e;
+            const int j = col(e);
             a[e] = fmaf(-zi * zs[j], id, a[e]);                  // A - z z' / delta
             s[e] = fmaf(ei, (ws[j] - zs[j] * ci) * iy, s[e]);    // S + e alpha^'
         });
-        sfor<EPT / 4>([&](auto h) {
-            st4(Ah + 4 * h, f4{a[4 * h], a[4 * h + 1], a[4 * h + 2], a[4 * h + 3]});
-            st4(Sh + 4 * h, f4{s[4 * h], s[4 * h + 1], s[4 * h + 2], s[4 * h + 3]});
+        sfor<Cf::NG>([&](auto h) {
+            st4(Ah + 4 * TPR * h, f4{a[4 * h], a[4 * h + 1], a[4 * h + 2], a[4 * h + 3]});
+            st4(Sh + 4 * TPR * h, f4{s[4 * h], s[4 * h + 1], s[4 * h + 2], s[4 * h + 3]});
         });
         if (tid % TPR == 0) o[(size_t)bh * D + row] = (pp + ei * aq) * rden;
     }
-    if (tid < D) zkey[(size_t)bh * D + tid] = zkf[tid] + phi_fast(kf[tid]);
+    if (tid < D) zkey[(size_t)bh * D + tid] = zkf[tid];
 }
 
 template <int D, typename Tin>

@@ -256,6 +256,51 @@ def test_step_matches_oracle(dtype):
     _check("zkey", zk.cpu().numpy(), ref["zkey"])
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_step_graph_replay(d):
+    """Decode steps captured in a HIP graph (one node per token, the way a serving
+    loop launches them) give, on every replay, exactly the eager steps' outputs
+    and state; the state is reset by eager copies between the replays."""
+    dev = _dev()
+    vla = _vla()
+    import dataclasses
+    cfg = dataclasses.replace(gen.config(5), d=d).with_sizes(B=2, H=3, T=24, decode=0)
+    x = gen.make_inputs(cfg)
+    B, H, n = cfg.B, cfg.H, cfg.T
+    t = {m: _to_dev(x[m], cfg, dev).permute(2, 0, 1, 3).contiguous() for m in "qkvu"}
+    S0 = 0.1 * torch.randn(B, H, d, d, device=dev)
+    A0 = (torch.eye(d, device=dev) / cfg.lambda0).expand(B, H, d, d).contiguous()
+    z0 = torch.rand(B, H, d, device=dev) + 0.5
+    S, A, zk = S0.clone(), A0.clone(), z0.clone()
+    o_eager = torch.empty(n, B, H, d, device=dev)
+    for i in range(n):
+        vla.vla_step(*(t[m][i] for m in "qkvu"), S, A, zk, cfg.eps, o=o_eager[i])
+    torch.cuda.synchronize()
+    want = [a.clone() for a in (o_eager, S, A, zk)]
+    S.copy_(S0), A.copy_(A0), zk.copy_(z0)
+    o = torch.empty_like(o_eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(n):
+                vla.vla_step(*(t[m][i] for m in "qkvu"), S, A, zk, cfg.eps, o=o[i])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        S.copy_(S0), A.copy_(A0), zk.copy_(z0), o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, ref in zip(("o", "S", "A", "zkey"), (o, S, A, zk), want):
+            assert torch.equal(got, ref), f"replay {rep}: {name} differs from the eager steps"
+    ref = oracle.forward(*(_f64(x[m], cfg) for m in "qkvu"), cfg.lambda0, cfg.eps,
+                         S0=S0.double().cpu().numpy(), A0=A0.double().cpu().numpy(),
+                         zkey0=z0.double().cpu().numpy())
+    check("o", o.permute(1, 2, 0, 3).cpu().numpy(), ref["o"])
+    check("S", S.cpu().numpy(), ref["S"])
+
+
 @pytest.mark.parametrize("d", [16, 32, 64, 96, 128])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_step_degenerate_tokens_every_d(d, dtype):
