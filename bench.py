@@ -101,6 +101,24 @@ def device_peak_tflops():
             "tflops": cus.value * khz.value * 1e3 * 256 / 1e12}
 
 
+def attainable_peak_tflops():
+    """Attainable fp32 throughput measured on this device by the probe library
+    (libvla_peak.so): the fp32 MFMA the kernels use and the plain (unpacked)
+    fp32 vector FMA, each one launch filling every compute unit, or None."""
+    import ctypes
+    path = os.path.join(ROOT, "long_context_sequence_amd", "libvla_peak.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.vla_peak_probe.restype = ctypes.c_int
+    lib.vla_peak_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    out = {}
+    for kind, name, iters in ((0, "mfma_f32_16x16x4", 4000), (1, "valu_fma_f32_unpacked", 8000)):
+        v = ctypes.c_double(0.0)
+        out[name] = v.value if lib.vla_peak_probe(kind, iters, ctypes.byref(v)) == 0 else None
+    return out
+
+
 def flops_per_token_head(d: int) -> int:
     """Algorithmic work of one token of one head: the matrix-vector products
     A u^, A k^, S k^ and S phi(q) (2 d^2 each) and the rank-1 updates of A and
@@ -647,6 +665,7 @@ def main():
                                 phase(pen_ms),
                                 "memory (vla_mem; S k^, S phi(q), S update)": phase(mem_ms)}},
         "device_peak": device_peak_tflops(),
+        "attainable_peak_tflops": attainable_peak_tflops(),
     }
     if not args.headline_only:
         res["baselines"] = baselines(vla, torch, kern_ms)

@@ -18,6 +18,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvla.so")
+# the benchmark's attainable-throughput probe, a library of its own
+PEAK_SRC = os.path.join(PKG, "peak", "vla_peak.hip")
+PEAK_LIB = os.path.join(PKG, "libvla_peak.so")
 ARCH = os.environ.get("VLA_OFFLOAD_ARCH", "gfx950")
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -47,16 +50,19 @@ def _compile(src: str) -> str:
 
 
 def build(jobs: int | None = None) -> str:
-    """Compile every csrc/*.hip and link libvla.so (always rebuilds)."""
+    """Compile every csrc/*.hip and link libvla.so, and build the probe library
+    libvla_peak.so (always rebuilds)."""
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [PEAK_SRC]
     n = jobs or min(16, max(1, os.cpu_count() or 1), len(srcs))
     with ThreadPoolExecutor(max_workers=n) as ex:
         objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    subprocess.run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
-                   check=True)
-    os.replace(tmp, LIB)
+    peak_obj = objs.pop()
+    for lib, parts in ((LIB, objs), (PEAK_LIB, [peak_obj])):
+        tmp = lib + ".tmp"
+        subprocess.run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *parts, "-o", tmp],
+                       check=True)
+        os.replace(tmp, lib)
     return LIB
 
 
