@@ -10,7 +10,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libvla.so")
+# VLA_LIB names another build of the same sources (the sanitizer test's)
+LIB_PATH = os.environ.get("VLA_LIB") or os.path.join(PKG, "libvla.so")
 
 VLA_OK, VLA_ERR_INVALID_ARG, VLA_ERR_UNSUPPORTED, VLA_ERR_HIP = 0, 1, 2, 3
 VLA_F32, VLA_BF16 = 0, 1

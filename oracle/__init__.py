@@ -36,7 +36,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "vla_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# VLA_ORACLE_LIB names another build of vla_oracle.c (the sanitizer test's)
+_LIB = os.environ.get("VLA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
@@ -55,7 +56,8 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if "VLA_ORACLE_LIB" not in os.environ and (
+                not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         f = lib.vla_oracle_forward
