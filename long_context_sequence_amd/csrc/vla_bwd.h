@@ -23,4 +23,29 @@ constexpr size_t backward_record_floats(int d) { return 4 * (size_t)d + 8; }
 size_t backward_workspace_bytes(int BH, int T, int d);
 hipError_t launch_backward(const BwdArgs &a);
 
+// The reverse sweep as two chains running side by side (vla_bwd_split.hip), for
+// d in {64, 96, 128}: per head a workgroup for the memory chain's adjoint (dS),
+// which writes dq, dv, its share of dk and the gate adjoint dL/dalpha^ per token
+// (galpha, [B][H][T][d]), and one for the penalty chain's adjoint (Sigma),
+// which follows it token by token, adds its share of dk and writes du.  rec
+// holds the forward's per-token records, S_T and A_T its final state; sync is
+// B H + 1 ints of workspace (role tickets and per-head progress), reset by the
+// launch itself.
+hipError_t launch_backward_split(const BwdArgs &a, const float *rec, const float *S_T,
+                                 const float *A_T, float *galpha, int *sync);
+
+// x y + z w with both products rounded before the sum (no fused multiply-add):
+// the same bits for (x, y, z, w) and (z, w, x, y), so that the two mirror
+// entries of a symmetric rank-2 update receive identical terms.  (Rounded
+// differently, Sigma gains an antisymmetric part that the reverse chain does
+// not shrink, and it swamps the small gradients Sigma carries.)
+__device__ __forceinline__ float sym_sum(float x, float y, float z, float w)
+{
+#pragma clang fp contract(off)
+    return x * y + z * w;
+}
+
+// derivative of phi = ELU + 1
+__device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __expf(x); }
+
 }  // namespace vla

@@ -85,18 +85,6 @@ template <int D> struct BwdCfg {
     static constexpr bool SPREAD = D >= 96;
 };
 
-__device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __expf(x); }
-
-// x y + z w with both products rounded before the sum (no fused multiply-add):
-// the same bits for (x, y, z, w) and (z, w, x, y), so that the two mirror
-// entries of a symmetric rank-2 update receive identical terms.  (Rounded
-// differently, Sigma gains an antisymmetric part that the reverse chain does
-// not shrink, and it swamps the small gradients Sigma carries.)
-__device__ __forceinline__ float sym_sum(float x, float y, float z, float w)
-{
-#pragma clang fp contract(off)
-    return x * y + z * w;
-}
 
 template <int D>
 struct BwdLds {
@@ -570,9 +558,11 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr bool records_from_forward(int d) { return d == 64 || d == 96 || d == 128; }
 
 // Workspace: the per-token records; for d in {64, 96, 128} also the two-pass
-// forward's workspace and its final S, A, zkey.
+// forward's workspace, its final S, A, zkey, the gate adjoints dL/dalpha^ that
+// the memory chain's sweep hands to the penalty chain's, and their
+// synchronisation words.
 struct BwdPlan {
-    size_t rec = 0, fwd = 0, st = 0, bytes = 0;
+    size_t rec = 0, fwd = 0, st = 0, ga = 0, sync = 0, bytes = 0;
 };
 BwdPlan bwd_plan(int BH, int T, int d)
 {
@@ -584,6 +574,10 @@ BwdPlan bwd_plan(int BH, int T, int d)
         off = up256(off + twopass_workspace_bytes(BH, T, d));
         p.st = off;
         off = up256(off + (size_t)BH * (2 * (size_t)d * d + d) * sizeof(float));
+        p.ga = off;
+        off = up256(off + (size_t)BH * T * d * sizeof(float));
+        p.sync = off;
+        off = up256(off + ((size_t)BH + 1) * sizeof(int));
     }
     p.bytes = off;
     return p;
@@ -620,11 +614,8 @@ hipError_t launch(const BwdArgs &a)
         f.keep = rec;
         const hipError_t e = launch_forward_twopass(f, 3);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((vla_bwd<D, Tin, true>), grid, block, 0, a.stream, (const Tin *)a.q,
-                           (const Tin *)a.k, (const Tin *)a.v, (const Tin *)a.u, a.T, a.lambda0,
-                           a.eps, stS, stA, stZ, a.dO, a.dS_T, a.dA_T, a.dzk_T, a.dq, a.dk, a.dv,
-                           a.du, a.dS0, a.dA0, a.dzk0, rec);
-        return hipGetLastError();
+        return launch_backward_split(a, rec, stS, stA, reinterpret_cast<float *>(ws + p.ga),
+                                     reinterpret_cast<int *>(ws + p.sync));
     } else {
         return launch_phase1<D, Tin>(a, grid, block, rec);
     }

@@ -1,0 +1,585 @@
+// vla_bwd_split.hip -- the reverse sweep of the gradients for d_h in {64, 96, 128}
+// as two chains, each in a kernel of its own with one barrier per token.
+//
+// Source: "Variational Linear Attention" (arXiv 2605.11196), section 3.3,
+// Eqs. (9)-(11); the pages print no backward, so this is the chain rule through
+// those equations in reverse order (the conventions are stated at vla_backward
+// in include/vla.h).  The forward's two chains meet only at alpha^ (Eq. (10)):
+// the memory chain (S) reads it, the penalty chain (A) makes it.  In reverse
+// the adjoint of S (dS) never needs the adjoint of A, and the adjoint of A
+// (Sigma = dA + dA', symmetric) needs from the memory side only dL/dalpha^_t.
+// So the sweep runs as:
+//
+//   vla_bwd_s  the memory chain's adjoint, per token t from T - 1 down:
+//              dS += g phi(q)'/den (g = dL/do_t);  ge = dS alpha^ (= dL/dv_t),
+//              galpha = dS'e (= dL/dalpha^_t), c1 = S_t'g;  dS -= ge k^';
+//              c2 = S_t'ge;  S_{t-1}' = S_t' - alpha^ e'.  It writes dq, dv, the
+//              memory chain's share of dk (with the key-sum adjoint) and galpha.
+//   vla_bwd_a  the penalty chain's adjoint: gy = (galpha - alpha^(alpha^'galpha))
+//              / |y|;  Sigma += gy k^' + k^ gy';  A_t gy;  Sigma z;
+//              gdelta = z'Sigma z / (2 delta^2), gz = -Sigma z / delta + gdelta u^;
+//              A_{t-1} = A_t + z z'/delta;  A_{t-1} gz;  Sigma += gz u^' + u^ gz'.
+//              It adds the penalty chain's share of dk and writes du.
+//
+// The per-token arithmetic is the combined sweep's (vla_bwd.hip, which serves
+// d <= 32): the same operations in the same order, with dk's normalisation
+// Jacobian applied to each chain's share separately (it is linear).
+//
+// Layout as in vla_bwd.hip: one workgroup per head, D * TPR threads, thread
+// (row i, columns [c0, c0 + EPT)) holds that slice of row i of each d x d
+// matrix; row products are DPP sums over TPR adjacent lanes.  Per token one
+// barrier: the row products of step 1 of token t go through LDS, then step 2
+// of token t and step 1 of token t - 1 (thread-local dependencies only) share
+// the next interval, and wave 0 forms token t + 1's gradients in it from the
+// row results (three LDS slots) and the token vectors (four slots: the
+// gradient's token, the two steps' tokens and the one being staged).  Token
+// vectors are loaded by their own waves two tokens ahead and staged one token
+// ahead (wave 0 stages nothing).
+#include "vla_bwd.h"
+#include "vla_chunk_parts.h"
+#include "vla_record.h"
+#include "vla_reduce.h"
+
+namespace vla {
+namespace {
+
+using namespace chunk;
+
+template <int D>
+struct SplitCfg {
+    static constexpr int TPR = 8, EPT = D / TPR, NT = D * TPR, NW = NT / 64, NV = (D + 63) / 64;
+    static constexpr int W = 64 * NV;   // ring row: what NV wave-wide 4-byte copies fill
+    static_assert(EPT % 4 == 0 && NT % 64 == 0 && NT <= 1024, "row slices of whole granules");
+};
+
+// Token vectors reach LDS by direct copies (4 bytes per lane, NV copies per
+// token and group), LA tokens ahead of the interval whose step 2 they feed,
+// into rings of RING slots.  Groups that need a transform (q, k, u, the gate
+// adjoint) are transformed two tokens ahead into four working slots by the
+// wave that copied them.  At the end of each interval a copying wave waits for
+// its copies of the token three ahead (the next interval transforms it and the
+// one after uses it), so LA - 3 tokens of copies stay in flight.
+constexpr int RING = 8, LA = 6;
+static_assert(LA + 2 <= RING, "tokens in use at once: t + 1 down to t - LA");
+
+// The memory chain's workgroup publishes its progress every PUB tokens; a
+// waiting wave polls at most SPIN_LIMIT times (each poll sleeps 256 cycles:
+// about a second in all).
+constexpr int PUB = 16, SPIN_LIMIT = 1 << 20;
+
+// element j of a raw ring row: fp32 as stored, or bf16 (two per word)
+template <typename Tin>
+__device__ __forceinline__ float raw_get(const float *row, int j)
+{
+    if constexpr (sizeof(Tin) == 4) {
+        return row[j];
+    } else {
+        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(row)[j] << 16);
+    }
+}
+
+// One copying wave's stream: token x's bytes at base + x * stride (+ 256 per
+// copy) into ring row x mod RING; ncopy copies per token, padded to NV with
+// repeats of the first so that every copying wave issues NV per token.
+struct Stream {
+    Buf buf;
+    unsigned stride, ncopy;
+    float *ring;
+    int row;   // ring row width (floats)
+    template <int NV>
+    __device__ __forceinline__ void issue(int x, int lane) const
+    {
+        float *dst = ring + (x & (RING - 1)) * row;
+        const unsigned vo = (unsigned)x * stride + 4u * (unsigned)lane;
+        sfor<NV>([&](auto i) {
+            const unsigned ii = (unsigned)i < ncopy ? (unsigned)i : 0u;
+            buf.lds4(dst + 64 * ii, vo + 256u * ii);
+        });
+    }
+};
+
+// ------------------------------------------------------------- memory chain
+template <int D>
+struct SLds {
+    static constexpr int W = SplitCfg<D>::W;
+    float g[RING][W], al[RING][W], e[RING][W], zt[RING][W], rq[RING][W], rk[RING][W];
+    float sc[RING][64];
+    float pq[4][D], dpq[4][D], kh[4][D], dpk[4][D];
+    float r1[3][3][D];   // ge, galpha, c1
+    float r2[3][D];      // c2
+};
+
+template <int D, typename Tin>
+__device__ __forceinline__ void
+bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, int T, float eps,
+      const float *__restrict__ S_T, const float *__restrict__ dO, const float *dS_T,
+      const float *dzk_T, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
+      float *dS0, float *dzk0, const float *__restrict__ rec, float *__restrict__ galpha,
+      int *progress)
+{
+    using Cf = SplitCfg<D>;
+    using K = rec::Keep<D>;
+    constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NW = Cf::NW, NV = Cf::NV, RS = K::RS, W = Cf::W;
+    static_assert(NW >= 8, "seven copying waves besides wave 0");
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row = tid / TPR, c0 = (tid % TPR) * EPT;
+    const bool leader = tid % TPR == 0;
+    const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
+    const float *rh = rec + tok0 * RS;
+
+    // dS and dS' (row slices) from dL/dS_T, S_T' from the forward's final S
+    float gS[EPT], gSt[EPT], St[EPT];
+    sfor<EPT>([&](auto e) {
+        const size_t off = bh * DD + (size_t)row * D + c0 + e, toff = bh * DD + (size_t)(c0 + e) * D + row;
+        gS[e] = dS_T ? dS_T[off] : 0.f;
+        gSt[e] = dS_T ? dS_T[toff] : 0.f;
+        St[e] = S_T[toff];
+    });
+    float gzk[NV];   // wave 0: the key-sum adjoint, entries lane + 64 c
+    sfor<NV>([&](auto c) {
+        const int j = lane + 64 * c;
+        gzk[c] = dzk_T && j < D ? dzk_T[(size_t)bh * D + j] : 0.f;
+    });
+
+    // copying groups: 0 dL/do, 1 alpha^, 2 e, 3 zkey_t, 4 q, 5 k, 6 the scalars;
+    // group i is wave NW - 1 - i's
+    const int grp = NW - 1 - w;
+    const bool copier = grp <= 6;
+    Stream st{Buf(nullptr, 0u), 0u, 1u, nullptr, W};
+    {
+        const unsigned recb = (unsigned)(T * RS * 4), inb = (unsigned)(T * D * sizeof(Tin));
+        const unsigned ncf = (D + 63) / 64, nci = (D * (unsigned)sizeof(Tin) + 255) / 256;
+        if (grp == 0) st = Stream{Buf(dO + tok0 * D, (unsigned)(T * D * 4)), D * 4u, ncf, &L.g[0][0], W};
+        if (grp == 1) st = Stream{Buf(rh + K::AL, recb - K::AL * 4u), RS * 4u, ncf, &L.al[0][0], W};
+        if (grp == 2) st = Stream{Buf(rh + K::E, recb - K::E * 4u), RS * 4u, ncf, &L.e[0][0], W};
+        if (grp == 3) st = Stream{Buf(rh + K::ZK, recb - K::ZK * 4u), RS * 4u, ncf, &L.zt[0][0], W};
+        if (grp == 4) st = Stream{Buf(q + tok0 * D, inb), D * (unsigned)sizeof(Tin), nci, &L.rq[0][0], W};
+        if (grp == 5) st = Stream{Buf(k + tok0 * D, inb), D * (unsigned)sizeof(Tin), nci, &L.rk[0][0], W};
+        if (grp == 6) st = Stream{Buf(rh + K::SC, recb - K::SC * 4u), RS * 4u, 1u, &L.sc[0][0], 64};
+    }
+    auto issue = [&](int x) {
+        if (copier) st.template issue<NV>(x, lane);
+    };
+    // q: phi(q), phi'(q); k: k^ = k / |k|, phi'(k) (two tokens ahead)
+    auto transform = [&](int x) {
+        const int rs = x & (RING - 1), ws = x & 3;
+        if (grp == 4 || grp == 5) {
+            const float sc = grp == 5 ? L.sc[rs][3] : 1.f;
+            const float *raw = grp == 4 ? L.rq[rs] : L.rk[rs];
+            float *d1 = grp == 4 ? L.pq[ws] : L.kh[ws], *d2 = grp == 4 ? L.dpq[ws] : L.dpk[ws];
+            sfor<NV>([&](auto c) {
+                const int j = lane + 64 * c;
+                if (j < D) {
+                    const float xv = raw_get<Tin>(raw, j);
+                    d1[j] = grp == 4 ? phi_fast(xv) : xv * sc;
+                    d2[j] = dphi(xv);
+                }
+            });
+        }
+    };
+
+    // step 1: the readout's share of dS, then dS alpha^, dS'e, S_t'g
+    auto step1 = [&](int t) {
+        const int v = t & 3, r = t & (RING - 1), s = t % 3;
+        const float iden = 1.f / fmaxf(L.sc[r][2], eps);
+        const float gi = L.g[r][row] * iden, pqi = L.pq[v][row] * iden;
+        float pge = 0.f, pga = 0.f, pc1 = 0.f;
+        sfor<EPT>([&](auto e) {
+            const int j = c0 + e;
+            const float gj = L.g[r][j];
+            gS[e] = fmaf(gi, L.pq[v][j], gS[e]);
+            gSt[e] = fmaf(pqi, gj, gSt[e]);
+            pge = fmaf(gS[e], L.al[r][j], pge);
+            pga = fmaf(gSt[e], L.e[r][j], pga);
+            pc1 = fmaf(St[e], gj, pc1);
+        });
+        pge = row_sum<TPR>(pge);
+        pga = row_sum<TPR>(pga);
+        pc1 = row_sum<TPR>(pc1);
+        if (leader) {
+            L.r1[s][0][row] = pge;
+            L.r1[s][1][row] = pga;
+            L.r1[s][2][row] = pc1;
+        }
+    };
+    // step 2: dS -= ge k^', S_t'ge, then S_{t-1}' = S_t' - alpha^ e'
+    auto step2 = [&](int t) {
+        const int v = t & 3, r = t & (RING - 1), s = t % 3;
+        const float khi = L.kh[v][row], gei = L.r1[s][0][row], ali = L.al[r][row];
+        float pc2 = 0.f;
+        sfor<EPT>([&](auto e) {
+            const int j = c0 + e;
+            const float gej = L.r1[s][0][j];
+            gS[e] = fmaf(-gei, L.kh[v][j], gS[e]);
+            gSt[e] = fmaf(-khi, gej, gSt[e]);
+            pc2 = fmaf(St[e], gej, pc2);
+            St[e] = fmaf(-ali, L.e[r][j], St[e]);
+        });
+        pc2 = row_sum<TPR>(pc2);
+        if (leader) L.r2[s][row] = pc2;
+    };
+    // wave 0: token t's dq, dv, galpha and the memory chain's share of dk
+    auto grads = [&](int t) {
+        const int v = t & 3, r = t & (RING - 1), s = t % 3;
+        const float dn = L.sc[r][2], iden = 1.f / fmaxf(dn, eps), ik = L.sc[r][3];
+        float a1 = 0.f, a2 = 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                a1 = fmaf(L.r1[s][2][j], L.pq[v][j], a1);   // g'S_t phi(q)
+                a2 = fmaf(L.e[r][j], L.r1[s][0][j], a2);    // e'ge
+            }
+        });
+        a1 = wave_sum(a1);
+        a2 = wave_sum(a2);
+        const float gden = dn >= eps ? -a1 * iden * iden : 0.f;
+        const size_t o = (tok0 + t) * D;
+        float gkh[NV], a3 = 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            gkh[c] = 0.f;
+            if (j < D) {
+                const float gpq = fmaf(L.r1[s][2][j], iden, gden * L.zt[r][j]);
+                dq[o + j] = gpq * L.dpq[v][j];
+                dv[o + j] = L.r1[s][0][j];
+                galpha[o + j] = L.r1[s][1][j];
+                gzk[c] = fmaf(gden, L.pq[v][j], gzk[c]);
+                gkh[c] = fmaf(L.al[r][j], a2, -L.r2[s][j]);
+                a3 = fmaf(L.kh[v][j], gkh[c], a3);
+            }
+        });
+        a3 = wave_sum(a3);
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) dk[o + j] = fmaf(ik, gkh[c] - L.kh[v][j] * a3, gzk[c] * L.dpk[v][j]);
+        });
+    };
+
+    for (int i = 0; i < LA && i < T; ++i) issue(T - 1 - i);
+    // drain every load so far as a wait the compiler sees (otherwise it waits
+    // for every load in flight at the top of each iteration)
+    vmem_drain();
+    __syncthreads();
+    if (T > 0) transform(T - 1);
+    if (T > 1) transform(T - 2);
+    __syncthreads();
+    if (T > 0) step1(T - 1);
+    lds_barrier();
+    // wave 0: tokens >= t are out (dq, dv, the memory chain's dk share and
+    // galpha written): publish t to the penalty chain's workgroup
+    auto publish = [&](int t) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        if (lane == 0) __hip_atomic_store(progress + bh, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    for (int t = T - 1; t >= 0; --t) {
+        if (t >= LA) issue(t - LA);
+        if (t >= 2) transform(t - 2);
+        if (w == 0 && t + 1 < T) {
+            grads(t + 1);
+            if ((t + 1) % PUB == 0) publish(t + 1);
+        }
+        step2(t);
+        if (t >= 1) step1(t - 1);
+        if (copier) {   // this wave's copies of token t - 3 done
+            if (t >= LA) vm_wait<(LA - 3) * NV>();
+            else vmem_drain();
+        }
+        lds_barrier();
+    }
+    if (w == 0 && T > 0) {
+        grads(0);
+        publish(0);
+    }
+
+    {
+        const size_t off = bh * DD + (size_t)row * D + c0;
+        if (dS0)
+            sfor<EPT / 4>([&](auto h) {
+                st4(dS0 + off + 4 * h, f4{gS[4 * h], gS[4 * h + 1], gS[4 * h + 2], gS[4 * h + 3]});
+            });
+    }
+    if (w == 0 && dzk0) {
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) dzk0[(size_t)bh * D + j] = gzk[c];
+        });
+    }
+}
+
+// ------------------------------------------------------------ penalty chain
+template <int D>
+struct ALds {
+    static constexpr int W = SplitCfg<D>::W;
+    float ga[RING][W], al[RING][W], z[RING][W], rk[RING][W], ru[RING][W];
+    float sc[RING][64];
+    float gy[4][D], kh[4][D], uh[4][D];
+    float r2[3][2][D];   // A_t gy, Sigma z
+    float r3[3][D];      // A_{t-1} gz
+};
+
+template <int D, typename Tin>
+__device__ __forceinline__ void
+bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, int T,
+      const float *__restrict__ A_T, const float *dA_T, float *__restrict__ dk, float *__restrict__ du,
+      float *dA0, const float *__restrict__ rec, const float *__restrict__ galpha, const int *progress)
+{
+    using Cf = SplitCfg<D>;
+    using K = rec::Keep<D>;
+    constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NW = Cf::NW, NV = Cf::NV, RS = K::RS, W = Cf::W;
+    static_assert(NW >= 7, "six copying waves besides wave 0");
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row = tid / TPR, c0 = (tid % TPR) * EPT;
+    const bool leader = tid % TPR == 0;
+    const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
+    const float *rh = rec + tok0 * RS;
+
+    // A_T (row slice) and Sigma = dA_T + dA_T' (fp64 storage: its entries stay
+    // of order one while the sensitivities it carries down the chain shrink)
+    float A[EPT];
+    double Sg[EPT];
+    sfor<EPT>([&](auto e) {
+        const size_t off = bh * DD + (size_t)row * D + c0 + e, toff = bh * DD + (size_t)(c0 + e) * D + row;
+        A[e] = A_T[off];
+        Sg[e] = dA_T ? (double)dA_T[off] + (double)dA_T[toff] : 0.0;
+    });
+
+    // copying groups: 0 galpha, 1 alpha^, 2 z, 3 k, 4 u, 5 the scalars; group i
+    // is wave NW - 1 - i's
+    const int grp = NW - 1 - w;
+    const bool copier = grp <= 5;
+    Stream st{Buf(nullptr, 0u), 0u, 1u, nullptr, W};
+    {
+        const unsigned recb = (unsigned)(T * RS * 4), inb = (unsigned)(T * D * sizeof(Tin));
+        const unsigned ncf = (D + 63) / 64, nci = (D * (unsigned)sizeof(Tin) + 255) / 256;
+        if (grp == 0) st = Stream{Buf(galpha + tok0 * D, (unsigned)(T * D * 4)), D * 4u, ncf, &L.ga[0][0], W};
+        if (grp == 1) st = Stream{Buf(rh + K::AL, recb - K::AL * 4u), RS * 4u, ncf, &L.al[0][0], W};
+        if (grp == 2) st = Stream{Buf(rh + K::Z, recb - K::Z * 4u), RS * 4u, ncf, &L.z[0][0], W};
+        if (grp == 3) st = Stream{Buf(k + tok0 * D, inb), D * (unsigned)sizeof(Tin), nci, &L.rk[0][0], W};
+        if (grp == 4) st = Stream{Buf(u + tok0 * D, inb), D * (unsigned)sizeof(Tin), nci, &L.ru[0][0], W};
+        if (grp == 5) st = Stream{Buf(rh + K::SC, recb - K::SC * 4u), RS * 4u, 1u, &L.sc[0][0], 64};
+    }
+    // Tokens >= seen are out of the memory chain's workgroup (its last
+    // published value, read with acquire ordering).  A wait gives up after
+    // SPIN_LIMIT polls (its workgroup, already running, should publish within
+    // microseconds); from then on the wave waits no more and the outputs of
+    // the head are NaN, so a failure shows instead of hanging.
+    int seen = T;
+    bool lost = false;
+    auto await = [&](int x) {
+        for (int n = 0; seen > x && !lost; ++n) {
+            seen = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(progress + bh, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT));
+            if (seen > x) {
+                if (n >= SPIN_LIMIT) lost = true;
+                __builtin_amdgcn_s_sleep(4);
+            }
+        }
+    };
+    auto issue = [&](int x) {
+        if (grp == 0) await(x);   // galpha of token x must be out
+        if (copier) st.template issue<NV>(x, lane);
+    };
+    // gy = (galpha - alpha^ (alpha^'galpha)) / |y|; k^ = k / |k|; u^ = u / |u|
+    auto transform = [&](int x) {
+        const int rs = x & (RING - 1), ws = x & 3;
+        if (grp == 0) {
+            float aga = 0.f;
+            sfor<NV>([&](auto c) {
+                const int j = lane + 64 * c;
+                if (j < D) aga = fmaf(L.al[rs][j], L.ga[rs][j], aga);
+            });
+            aga = wave_sum(aga);
+            const float iy = L.sc[rs][1];
+            sfor<NV>([&](auto c) {
+                const int j = lane + 64 * c;
+                if (j < D) L.gy[ws][j] = (L.ga[rs][j] - L.al[rs][j] * aga) * iy;
+            });
+        } else if (grp == 3 || grp == 4) {
+            const float sc = grp == 3 ? L.sc[rs][3] : L.sc[rs][4];
+            const float *raw = grp == 3 ? L.rk[rs] : L.ru[rs];
+            float *dst = grp == 3 ? L.kh[ws] : L.uh[ws];
+            sfor<NV>([&](auto c) {
+                const int j = lane + 64 * c;
+                if (j < D) dst[j] = raw_get<Tin>(raw, j) * sc;
+            });
+        }
+    };
+
+    // step 1: Sigma += gy k^' + k^ gy', then A_t gy and Sigma z
+    auto step1 = [&](int t) {
+        const int v = t & 3, r = t & (RING - 1), s = t % 3;
+        const float gyi = L.gy[v][row], khi = L.kh[v][row];
+        float paty = 0.f, psz = 0.f;
+        sfor<EPT>([&](auto e) {
+            const int j = c0 + e;
+            const float gyj = L.gy[v][j];
+            Sg[e] += (double)sym_sum(gyi, L.kh[v][j], khi, gyj);
+            paty = fmaf(A[e], gyj, paty);
+            psz = fmaf((float)Sg[e], L.z[r][j], psz);
+        });
+        paty = row_sum<TPR>(paty);
+        psz = row_sum<TPR>(psz);
+        if (leader) {
+            L.r2[s][0][row] = paty;
+            L.r2[s][1][row] = psz;
+        }
+    };
+    // step 2: gdelta, gz; A_{t-1} and A_{t-1} gz; Sigma += gz u^' + u^ gz'.
+    // Returns gdelta.
+    auto step2 = [&](int t) -> float {
+        const int v = t & 3, r = t & (RING - 1), s = t % 3;
+        const float id = 1.f / L.sc[r][0];
+        float zsz = 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) zsz = fmaf(L.z[r][j], L.r2[s][1][j], zsz);
+        });
+        const float gdel = 0.5f * wave_sum(zsz) * id * id;
+        const float zi = L.z[r][row], uhi = L.uh[v][row];
+        const float gzi = fmaf(-L.r2[s][1][row], id, gdel * uhi);
+        float pagz = 0.f;
+        sfor<EPT>([&](auto e) {
+            const int j = c0 + e;
+            const float zj = L.z[r][j], uhj = L.uh[v][j];
+            const float gzj = fmaf(-L.r2[s][1][j], id, gdel * uhj);
+            A[e] = fmaf(zi * zj, id, A[e]);
+            pagz = fmaf(A[e], gzj, pagz);
+            Sg[e] += (double)sym_sum(gzi, uhj, uhi, gzj);
+        });
+        pagz = row_sum<TPR>(pagz);
+        if (leader) L.r3[s][row] = pagz;
+        return gdel;
+    };
+    // wave 0: token t's du and the penalty chain's share of dk (added to the
+    // memory chain's, written by vla_bwd_s)
+    auto grads = [&](int t, float gdel) {
+        const int v = t & 3, r = t & (RING - 1), s = t % 3;
+        const float ik = L.sc[r][3], iu = L.sc[r][4];
+        await(t);   // the memory chain's dk share of token t is written (returns at once)
+        const float bad = lost ? __builtin_nanf("") : 0.f;
+        float guh[NV], a4 = 0.f, a5 = 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            guh[c] = 0.f;
+            if (j < D) {
+                guh[c] = fmaf(gdel, L.z[r][j], L.r3[s][j]);
+                a4 = fmaf(L.uh[v][j], guh[c], a4);
+                a5 = fmaf(L.kh[v][j], L.r2[s][0][j], a5);
+            }
+        });
+        a4 = wave_sum(a4);
+        a5 = wave_sum(a5);
+        const size_t o = (tok0 + t) * D;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                du[o + j] = iu * (guh[c] - L.uh[v][j] * a4) + bad;
+                dk[o + j] += ik * (L.r2[s][0][j] - L.kh[v][j] * a5) + bad;
+            }
+        });
+    };
+
+    for (int i = 0; i < LA && i < T; ++i) issue(T - 1 - i);
+    vmem_drain();
+    __syncthreads();
+    if (T > 0) transform(T - 1);
+    if (T > 1) transform(T - 2);
+    __syncthreads();
+    if (T > 0) step1(T - 1);
+    lds_barrier();
+    float gdel_g = 0.f;   // wave 0: gdelta of the token whose gradients come next
+    for (int t = T - 1; t >= 0; --t) {
+        if (t >= LA) issue(t - LA);
+        if (t >= 2) transform(t - 2);
+        if (w == 0 && t + 1 < T) grads(t + 1, gdel_g);
+        gdel_g = step2(t);
+        if (t >= 1) step1(t - 1);
+        if (copier) {
+            if (t >= LA) vm_wait<(LA - 3) * NV>();
+            else vmem_drain();
+        }
+        lds_barrier();
+    }
+    if (w == 0 && T > 0) grads(0, gdel_g);
+
+    if (dA0) {
+        const size_t off = bh * DD + (size_t)row * D + c0;
+        sfor<EPT / 4>([&](auto h) {
+            st4(dA0 + off + 4 * h, f4{(float)(0.5 * Sg[4 * h]), (float)(0.5 * Sg[4 * h + 1]),
+                                      (float)(0.5 * Sg[4 * h + 2]), (float)(0.5 * Sg[4 * h + 3])});
+        });
+    }
+}
+
+// Resets the role tickets and every head's progress (T: no token out yet).
+__global__ void __launch_bounds__(256) vla_bwd_sync_init(int *sync, int BH, int T)
+{
+    for (int i = blockIdx.x * 256 + threadIdx.x; i <= BH; i += gridDim.x * 256) sync[i] = i == 0 ? 0 : T;
+}
+
+// 2 BH workgroups.  Each takes a ticket when it starts: tickets 0 .. BH - 1
+// run the memory chains of heads 0 .. BH - 1, the rest the penalty chains.  A
+// penalty workgroup waits only on the memory workgroup of its head, which took
+// its ticket earlier and so is already running and never waits itself: the
+// launch finishes whatever the number of resident workgroups.
+template <int D, typename Tin>
+__global__ void __launch_bounds__(SplitCfg<D>::NT)
+vla_bwd_sweep(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ u, int T,
+              float eps, const float *__restrict__ S_T, const float *__restrict__ A_T,
+              const float *__restrict__ dO, const float *dS_T, const float *dA_T, const float *dzk_T,
+              float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
+              float *__restrict__ du, float *dS0, float *dA0, float *dzk0,
+              const float *__restrict__ rec, float *__restrict__ galpha, int *sync, int BH)
+{
+    __shared__ __align__(16) union {
+        SLds<D> s;
+        ALds<D> a;
+    } L;
+    __shared__ int ticket;
+    if (threadIdx.x == 0) ticket = __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int tk = ticket;
+    if (tk < BH)
+        bwd_s<D, Tin>(L.s, tk, q, k, T, eps, S_T, dO, dS_T, dzk_T, dq, dk, dv, dS0, dzk0, rec, galpha,
+                      sync + 1);
+    else
+        bwd_a<D, Tin>(L.a, tk - BH, k, u, T, A_T, dA_T, dk, du, dA0, rec, galpha, sync + 1);
+}
+
+template <int D, typename Tin>
+hipError_t launch(const BwdArgs &a, const float *rec, const float *S_T, const float *A_T, float *galpha,
+                  int *sync)
+{
+    const int BH = a.B * a.H;
+    hipLaunchKernelGGL(vla_bwd_sync_init, dim3((BH + 256) / 256), dim3(256), 0, a.stream, sync, BH, a.T);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((vla_bwd_sweep<D, Tin>), dim3(2 * BH), dim3(SplitCfg<D>::NT), 0, a.stream,
+                       (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.u, a.T, a.eps, S_T, A_T, a.dO,
+                       a.dS_T, a.dA_T, a.dzk_T, a.dq, a.dk, a.dv, a.du, a.dS0, a.dA0, a.dzk0, rec, galpha,
+                       sync, BH);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_split(const BwdArgs &a, const float *rec, const float *S_T,
+                                 const float *A_T, float *galpha, int *sync)
+{
+    const bool bf = a.dtype == 1;
+    switch (a.d) {
+    case 64: return bf ? launch<64, uint16_t>(a, rec, S_T, A_T, galpha, sync)
+                       : launch<64, float>(a, rec, S_T, A_T, galpha, sync);
+    case 96: return bf ? launch<96, uint16_t>(a, rec, S_T, A_T, galpha, sync)
+                       : launch<96, float>(a, rec, S_T, A_T, galpha, sync);
+    case 128: return bf ? launch<128, uint16_t>(a, rec, S_T, A_T, galpha, sync)
+                        : launch<128, float>(a, rec, S_T, A_T, galpha, sync);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace vla

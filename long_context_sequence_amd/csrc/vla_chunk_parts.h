@@ -128,6 +128,11 @@ struct Buf {
     {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, soff, 0, 0);
     }
+    // 4 bytes per lane straight into LDS: lane l's bytes land at lds + 4 l
+    __device__ __forceinline__ void lds4(float *lds, unsigned off, unsigned soff = 0) const
+    {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, off, soff, 0, 0);
+    }
 };
 
 __device__ __forceinline__ void st4(float *p, f4 x) { *reinterpret_cast<f4 *>(p) = x; }
