@@ -8,19 +8,22 @@
 // in reverse order, with the conventions stated at vla_backward in
 // include/vla.h.
 //
+// This kernel serves d in {16, 32} (both phases below) and T = 0 at every d
+// (the initial state's gradients are the final state's adjoints).  For d in
+// {64, 96, 128} the two-pass forward (vla_twopass.hip) keeps the per-token
+// records and the reverse sweep runs as two chains side by side
+// (vla_bwd_split.hip).
+//
 // One workgroup per head, D * TPR threads: thread (row i, columns [c0, c0+EPT))
 // holds that slice of row i of every d x d matrix, so a matrix-vector product is
 // a sum over TPR adjacent lanes (DPP), and rank-1 updates are local.
 //
 // The reverse sweep needs, per token, z = A_{t-1} u^, alpha^, e, the key sum
 // zkey_t and the scalars delta, 1/|y|, phi(q)'zkey, 1/|k|, 1/|u|, and the
-// final states S_T, A_T.  For d in {64, 96, 128} the two-pass forward
-// (vla_twopass.hip) leaves them in the workspace on the matrix cores and the
-// kernel starts at phase 2; for d in {16, 32} phase 1 of the kernel computes
-// them.  The key sum is kept rather than rebuilt by subtraction: zkey_t grows
-// like t, and subtracting phi(k) from a sum formed in another order (the
-// chunked forward's) would leave the early tokens' zkey_t, small against
-// zkey_T, with most of the rounding of zkey_T.
+// final states S_T, A_T; phase 1 computes them.  The key sum is kept rather
+// than rebuilt by subtraction: zkey_t grows like t, and subtracting phi(k) from
+// a sum formed in another order would leave the early tokens' zkey_t, small
+// against zkey_T, with most of the rounding of zkey_T.
 //
 // Phase 1 runs the forward one token at a time (states S, A in registers) and
 // keeps those per-token values in the workspace.  One barrier per token: the token
@@ -63,17 +66,10 @@ namespace {
 
 using namespace chunk;
 
-// Threads per row (TPR) and where S' lives, by measurement on the backward of
-// 128 (d = 64), 128 (d = 96) and 64 (d = 128) heads: every wave repeats the
-// token's scalar work (dot products, norms, the step scalars), so fewer, wider
-// threads cost less issue; the register file bounds how wide.  d = 64 (reverse
-// sweep only, the records coming from the two-pass forward): eight threads per
-// row, all slices in registers (1.87 us per token against 2.21 with four and
-// 2.01 with sixteen); d = 96: eight per row in registers (9.5 us against 10.4
-// and 12.6 with four, both phases in the kernel); d = 128: four per row with
-// S' in LDS (each thread's row slice, contiguous) so that the other four slices
-// fit in registers (13.6 us for the reverse sweep against 20.7 with eight per
-// row, all in registers); d <= 32 (both phases): four per row.
+// Threads per row (TPR) and where S' lives: every wave repeats the token's
+// scalar work (dot products, norms, the step scalars), so fewer, wider threads
+// cost less issue; the register file bounds how wide.  d <= 32 (both phases):
+// four per row.  For d >= 64 only T = 0 reaches this kernel (no token loop).
 template <int D> struct BwdCfg {
     static constexpr int TPR = D == 96 || D == 64 ? 8 : 4, EPT = D / TPR;
     static constexpr bool ST_LDS = D == 128;
@@ -102,9 +98,7 @@ struct BwdLds {
     float tr[D * BwdCfg<D>::TRP];
 };
 
-// FWD: the per-token records were left by the two-pass forward (vla_twopass.hip,
-// run with `keep`), and S0, A0, zk0 hold its final state: phase 1 is skipped.
-template <int D, typename Tin, bool FWD = false>
+template <int D, typename Tin>
 __global__ void __launch_bounds__(D * BwdCfg<D>::TPR)
 vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
         const Tin *__restrict__ u, int T, float lambda0, float eps,
@@ -128,7 +122,7 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     const int bh = blockIdx.x;
     const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
     float *rh = rec + tok0 * RS;   // this head's per-token records
-    const int T1 = FWD ? 0 : T;    // tokens of phase 1
+    const int T1 = T;              // tokens of phase 1
 
     // ------------------------------------------------------------ phase 1
     float S[EPT], A[EPT];

@@ -1,5 +1,5 @@
 // vla_bwd_split.hip -- the reverse sweep of the gradients for d_h in {64, 96, 128}
-// as two chains, each in a kernel of its own with one barrier per token.
+// as two chains running side by side, each with one barrier per token.
 //
 // Source: "Variational Linear Attention" (arXiv 2605.11196), section 3.3,
 // Eqs. (9)-(11); the pages print no backward, so this is the chain rule through
@@ -8,33 +8,37 @@
 // the memory chain (S) reads it, the penalty chain (A) makes it.  In reverse
 // the adjoint of S (dS) never needs the adjoint of A, and the adjoint of A
 // (Sigma = dA + dA', symmetric) needs from the memory side only dL/dalpha^_t.
-// So the sweep runs as:
+// So each head gets two workgroups:
 //
-//   vla_bwd_s  the memory chain's adjoint, per token t from T - 1 down:
+//   memory     the memory chain's adjoint, per token t from T - 1 down:
 //              dS += g phi(q)'/den (g = dL/do_t);  ge = dS alpha^ (= dL/dv_t),
 //              galpha = dS'e (= dL/dalpha^_t), c1 = S_t'g;  dS -= ge k^';
 //              c2 = S_t'ge;  S_{t-1}' = S_t' - alpha^ e'.  It writes dq, dv, the
-//              memory chain's share of dk (with the key-sum adjoint) and galpha.
-//   vla_bwd_a  the penalty chain's adjoint: gy = (galpha - alpha^(alpha^'galpha))
-//              / |y|;  Sigma += gy k^' + k^ gy';  A_t gy;  Sigma z;
-//              gdelta = z'Sigma z / (2 delta^2), gz = -Sigma z / delta + gdelta u^;
-//              A_{t-1} = A_t + z z'/delta;  A_{t-1} gz;  Sigma += gz u^' + u^ gz'.
-//              It adds the penalty chain's share of dk and writes du.
+//              memory chain's share of dk (with the key-sum adjoint) and galpha,
+//              and publishes how far it is.
+//   penalty    the penalty chain's adjoint, a few tokens behind: gy = (galpha -
+//              alpha^(alpha^'galpha)) / |y|;  Sigma += gy k^' + k^ gy';  A_t gy;
+//              Sigma z;  gdelta = z'Sigma z / (2 delta^2), gz = -Sigma z / delta +
+//              gdelta u^;  A_{t-1} = A_t + z z'/delta;  A_{t-1} gz;  Sigma += gz u^'
+//              + u^ gz'.  It adds the penalty chain's share of dk and writes du.
 //
-// The per-token arithmetic is the combined sweep's (vla_bwd.hip, which serves
-// d <= 32): the same operations in the same order, with dk's normalisation
-// Jacobian applied to each chain's share separately (it is linear).
+// The per-token arithmetic is the one-workgroup sweep's (vla_bwd.hip, which
+// serves d <= 32): the same operations in the same order, with dk's
+// normalisation Jacobian applied to each chain's share separately (it is
+// linear).
 //
-// Layout as in vla_bwd.hip: one workgroup per head, D * TPR threads, thread
-// (row i, columns [c0, c0 + EPT)) holds that slice of row i of each d x d
-// matrix; row products are DPP sums over TPR adjacent lanes.  Per token one
-// barrier: the row products of step 1 of token t go through LDS, then step 2
-// of token t and step 1 of token t - 1 (thread-local dependencies only) share
-// the next interval, and wave 0 forms token t + 1's gradients in it from the
-// row results (three LDS slots) and the token vectors (four slots: the
-// gradient's token, the two steps' tokens and the one being staged).  Token
-// vectors are loaded by their own waves two tokens ahead and staged one token
-// ahead (wave 0 stages nothing).
+// Layout: D * TPR row threads, thread (row i, columns [c0, c0 + EPT)) holding
+// that slice of row i of each d x d matrix (row products are DPP sums over TPR
+// adjacent lanes), and two service waves (SplitCfg): the copy wave brings the token
+// vectors into LDS (direct copies LA tokens ahead into rings of RING slots,
+// transforms two tokens ahead into working slots), the gradient wave forms
+// each token's gradients from the row results.  Per token one barrier: the row
+// products of step 1 of token t go through LDS, then step 2 of token t and
+// step 1 of token t - 1 (thread-local dependencies only) share the next
+// interval, while the gradient wave forms token t + 1's gradients (row results
+// in three LDS slots, transformed vectors in four: the gradient's token, the two
+// steps' tokens and the one being transformed).  So the row threads run only
+// the chain's own steps (where the service waves come on top of them).
 #include "vla_bwd.h"
 #include "vla_chunk_parts.h"
 #include "vla_record.h"
@@ -47,24 +51,30 @@ using namespace chunk;
 
 template <int D>
 struct SplitCfg {
-    static constexpr int TPR = 8, EPT = D / TPR, NT = D * TPR, NW = NT / 64, NV = (D + 63) / 64;
+    // eight threads per row; the two service waves come on top where the
+    // workgroup has room (d = 64, 96), otherwise (d = 128: 1024 row threads,
+    // and four per row would need more registers than four waves per SIMD
+    // leave) the last two row waves serve as well
+    static constexpr int TPR = 8, EPT = D / TPR, NR = D * TPR, NWR = NR / 64;
+    static constexpr bool EXTRA = NR + 128 <= 1024;
+    static constexpr int NT = EXTRA ? NR + 128 : NR;
+    static constexpr int WCOPY = EXTRA ? NWR : NWR - 1, WGRAD = EXTRA ? NWR + 1 : NWR - 2;
+    static constexpr int NV = (D + 63) / 64;
     static constexpr int W = 64 * NV;   // ring row: what NV wave-wide 4-byte copies fill
-    static_assert(EPT % 4 == 0 && NT % 64 == 0 && NT <= 1024, "row slices of whole granules");
+    static_assert(EPT % 4 == 0 && NR % 64 == 0 && NT <= 1024, "row slices of whole granules");
 };
 
 // Token vectors reach LDS by direct copies (4 bytes per lane, NV copies per
-// token and group), LA tokens ahead of the interval whose step 2 they feed,
-// into rings of RING slots.  Groups that need a transform (q, k, u, the gate
-// adjoint) are transformed two tokens ahead into four working slots by the
-// wave that copied them.  At the end of each interval a copying wave waits for
-// its copies of the token three ahead (the next interval transforms it and the
-// one after uses it), so LA - 3 tokens of copies stay in flight.
+// token and stream), LA tokens ahead of the interval whose step 2 they feed,
+// into rings of RING slots.  At the end of each interval the copy wave waits
+// for its copies of the token three ahead (the next interval transforms it and
+// the one after uses it), so LA - 3 tokens of copies stay in flight.
 constexpr int RING = 8, LA = 6;
 static_assert(LA + 2 <= RING, "tokens in use at once: t + 1 down to t - LA");
 
-// The memory chain's workgroup publishes its progress every PUB tokens; a
-// waiting wave polls at most SPIN_LIMIT times (each poll sleeps 256 cycles:
-// about a second in all).
+// The memory workgroup publishes its progress every PUB tokens; a waiting wave
+// polls at most SPIN_LIMIT times (each poll sleeps 256 cycles; about a second
+// in all).
 constexpr int PUB = 16, SPIN_LIMIT = 1 << 20;
 
 // element j of a raw ring row: fp32 as stored, or bf16 (two per word)
@@ -78,9 +88,9 @@ __device__ __forceinline__ float raw_get(const float *row, int j)
     }
 }
 
-// One copying wave's stream: token x's bytes at base + x * stride (+ 256 per
-// copy) into ring row x mod RING; ncopy copies per token, padded to NV with
-// repeats of the first so that every copying wave issues NV per token.
+// One stream of per-token vectors: token x's bytes at base + x * stride (+ 256
+// per copy) into ring row x mod RING; ncopy copies per token, padded to NV with
+// repeats of the first so that every stream issues NV per token.
 struct Stream {
     Buf buf;
     unsigned stride, ncopy;
@@ -97,6 +107,19 @@ struct Stream {
         });
     }
 };
+
+template <int D>
+__device__ __forceinline__ Stream fstream(const float *base, unsigned bytes, unsigned stride, float *ring)
+{
+    return Stream{Buf(base, bytes), stride, (unsigned)(D + 63) / 64, ring, SplitCfg<D>::W};
+}
+
+template <int D, typename Tin>
+__device__ __forceinline__ Stream istream(const Tin *base, int T, float *ring)
+{
+    return Stream{Buf(base, (unsigned)(T * D * sizeof(Tin))), D * (unsigned)sizeof(Tin),
+                  (D * (unsigned)sizeof(Tin) + 255) / 256, ring, SplitCfg<D>::W};
+}
 
 // ------------------------------------------------------------- memory chain
 template <int D>
@@ -119,13 +142,14 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
 {
     using Cf = SplitCfg<D>;
     using K = rec::Keep<D>;
-    constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NW = Cf::NW, NV = Cf::NV, RS = K::RS, W = Cf::W;
-    static_assert(NW >= 8, "seven copying waves besides wave 0");
+    constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NV = Cf::NV, RS = K::RS;
+    constexpr int NG = 7;   // streams: dL/do, alpha^, e, zkey_t, q, k, the scalars
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int row = tid / TPR, c0 = (tid % TPR) * EPT;
-    const bool leader = tid % TPR == 0;
+    const bool rows = w < Cf::NWR;
+    const int row = rows ? tid / TPR : 0, c0 = (tid % TPR) * EPT;
+    const bool leader = rows && tid % TPR == 0;
     const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
     const float *rh = rec + tok0 * RS;
 
@@ -133,51 +157,43 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
     float gS[EPT], gSt[EPT], St[EPT];
     sfor<EPT>([&](auto e) {
         const size_t off = bh * DD + (size_t)row * D + c0 + e, toff = bh * DD + (size_t)(c0 + e) * D + row;
-        gS[e] = dS_T ? dS_T[off] : 0.f;
-        gSt[e] = dS_T ? dS_T[toff] : 0.f;
-        St[e] = S_T[toff];
+        gS[e] = rows && dS_T ? dS_T[off] : 0.f;
+        gSt[e] = rows && dS_T ? dS_T[toff] : 0.f;
+        St[e] = rows ? S_T[toff] : 0.f;
     });
-    float gzk[NV];   // wave 0: the key-sum adjoint, entries lane + 64 c
+    float gzk[NV];   // gradient wave: the key-sum adjoint, entries lane + 64 c
     sfor<NV>([&](auto c) {
         const int j = lane + 64 * c;
         gzk[c] = dzk_T && j < D ? dzk_T[(size_t)bh * D + j] : 0.f;
     });
 
-    // copying groups: 0 dL/do, 1 alpha^, 2 e, 3 zkey_t, 4 q, 5 k, 6 the scalars;
-    // group i is wave NW - 1 - i's
-    const int grp = NW - 1 - w;
-    const bool copier = grp <= 6;
-    Stream st{Buf(nullptr, 0u), 0u, 1u, nullptr, W};
-    {
-        const unsigned recb = (unsigned)(T * RS * 4), inb = (unsigned)(T * D * sizeof(Tin));
-        const unsigned ncf = (D + 63) / 64, nci = (D * (unsigned)sizeof(Tin) + 255) / 256;
-        if (grp == 0) st = Stream{Buf(dO + tok0 * D, (unsigned)(T * D * 4)), D * 4u, ncf, &L.g[0][0], W};
-        if (grp == 1) st = Stream{Buf(rh + K::AL, recb - K::AL * 4u), RS * 4u, ncf, &L.al[0][0], W};
-        if (grp == 2) st = Stream{Buf(rh + K::E, recb - K::E * 4u), RS * 4u, ncf, &L.e[0][0], W};
-        if (grp == 3) st = Stream{Buf(rh + K::ZK, recb - K::ZK * 4u), RS * 4u, ncf, &L.zt[0][0], W};
-        if (grp == 4) st = Stream{Buf(q + tok0 * D, inb), D * (unsigned)sizeof(Tin), nci, &L.rq[0][0], W};
-        if (grp == 5) st = Stream{Buf(k + tok0 * D, inb), D * (unsigned)sizeof(Tin), nci, &L.rk[0][0], W};
-        if (grp == 6) st = Stream{Buf(rh + K::SC, recb - K::SC * 4u), RS * 4u, 1u, &L.sc[0][0], 64};
-    }
+    const unsigned recb = (unsigned)(T * RS * 4);
+    const Stream sg[NG] = {
+        fstream<D>(dO + tok0 * D, (unsigned)(T * D * 4), D * 4u, &L.g[0][0]),
+        fstream<D>(rh + K::AL, recb - K::AL * 4u, RS * 4u, &L.al[0][0]),
+        fstream<D>(rh + K::E, recb - K::E * 4u, RS * 4u, &L.e[0][0]),
+        fstream<D>(rh + K::ZK, recb - K::ZK * 4u, RS * 4u, &L.zt[0][0]),
+        istream<D, Tin>(q + tok0 * D, T, &L.rq[0][0]),
+        istream<D, Tin>(k + tok0 * D, T, &L.rk[0][0]),
+        Stream{Buf(rh + K::SC, recb - K::SC * 4u), RS * 4u, 1u, &L.sc[0][0], 64}};
     auto issue = [&](int x) {
-        if (copier) st.template issue<NV>(x, lane);
+        if (w == Cf::WCOPY) sfor<NG>([&](auto i) { sg[i].template issue<NV>(x, lane); });
     };
     // q: phi(q), phi'(q); k: k^ = k / |k|, phi'(k) (two tokens ahead)
     auto transform = [&](int x) {
+        if (w != Cf::WCOPY) return;
         const int rs = x & (RING - 1), ws = x & 3;
-        if (grp == 4 || grp == 5) {
-            const float sc = grp == 5 ? L.sc[rs][3] : 1.f;
-            const float *raw = grp == 4 ? L.rq[rs] : L.rk[rs];
-            float *d1 = grp == 4 ? L.pq[ws] : L.kh[ws], *d2 = grp == 4 ? L.dpq[ws] : L.dpk[ws];
-            sfor<NV>([&](auto c) {
-                const int j = lane + 64 * c;
-                if (j < D) {
-                    const float xv = raw_get<Tin>(raw, j);
-                    d1[j] = grp == 4 ? phi_fast(xv) : xv * sc;
-                    d2[j] = dphi(xv);
-                }
-            });
-        }
+        const float ik = L.sc[rs][3];
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                const float xq = raw_get<Tin>(L.rq[rs], j), xk = raw_get<Tin>(L.rk[rs], j);
+                L.pq[ws][j] = phi_fast(xq);
+                L.dpq[ws][j] = dphi(xq);
+                L.kh[ws][j] = xk * ik;
+                L.dpk[ws][j] = dphi(xk);
+            }
+        });
     };
 
     // step 1: the readout's share of dS, then dS alpha^, dS'e, S_t'g
@@ -220,7 +236,7 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
         pc2 = row_sum<TPR>(pc2);
         if (leader) L.r2[s][row] = pc2;
     };
-    // wave 0: token t's dq, dv, galpha and the memory chain's share of dk
+    // gradient wave: token t's dq, dv, galpha and the memory chain's share of dk
     auto grads = [&](int t) {
         const int v = t & 3, r = t & (RING - 1), s = t % 3;
         const float dn = L.sc[r][2], iden = 1.f / fmaxf(dn, eps), ik = L.sc[r][3];
@@ -256,6 +272,12 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
             if (j < D) dk[o + j] = fmaf(ik, gkh[c] - L.kh[v][j] * a3, gzk[c] * L.dpk[v][j]);
         });
     };
+    // gradient wave: tokens >= t are out (dq, dv, the memory chain's dk share
+    // and galpha written): publish t to the penalty workgroup
+    auto publish = [&](int t) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        if (lane == 0) __hip_atomic_store(progress + bh, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
 
     for (int i = 0; i < LA && i < T; ++i) issue(T - 1 - i);
     // drain every load so far as a wait the compiler sees (otherwise it waits
@@ -265,42 +287,37 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
     if (T > 0) transform(T - 1);
     if (T > 1) transform(T - 2);
     __syncthreads();
-    if (T > 0) step1(T - 1);
+    if (rows && T > 0) step1(T - 1);
     lds_barrier();
-    // wave 0: tokens >= t are out (dq, dv, the memory chain's dk share and
-    // galpha written): publish t to the penalty chain's workgroup
-    auto publish = [&](int t) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        if (lane == 0) __hip_atomic_store(progress + bh, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
     for (int t = T - 1; t >= 0; --t) {
         if (t >= LA) issue(t - LA);
         if (t >= 2) transform(t - 2);
-        if (w == 0 && t + 1 < T) {
+        if (w == Cf::WGRAD && t + 1 < T) {
             grads(t + 1);
             if ((t + 1) % PUB == 0) publish(t + 1);
         }
-        step2(t);
-        if (t >= 1) step1(t - 1);
-        if (copier) {   // this wave's copies of token t - 3 done
-            if (t >= LA) vm_wait<(LA - 3) * NV>();
+        if (rows) {
+            step2(t);
+            if (t >= 1) step1(t - 1);
+        }
+        if (w == Cf::WCOPY) {   // this wave's copies of token t - 3 done
+            if (t >= LA) vm_wait<(LA - 3) * NG * NV>();
             else vmem_drain();
         }
         lds_barrier();
     }
-    if (w == 0 && T > 0) {
+    if (w == Cf::WGRAD && T > 0) {
         grads(0);
         publish(0);
     }
 
-    {
+    if (rows && dS0) {
         const size_t off = bh * DD + (size_t)row * D + c0;
-        if (dS0)
-            sfor<EPT / 4>([&](auto h) {
-                st4(dS0 + off + 4 * h, f4{gS[4 * h], gS[4 * h + 1], gS[4 * h + 2], gS[4 * h + 3]});
-            });
+        sfor<EPT / 4>([&](auto h) {
+            st4(dS0 + off + 4 * h, f4{gS[4 * h], gS[4 * h + 1], gS[4 * h + 2], gS[4 * h + 3]});
+        });
     }
-    if (w == 0 && dzk0) {
+    if (w == Cf::WGRAD && dzk0) {
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) dzk0[(size_t)bh * D + j] = gzk[c];
@@ -317,6 +334,7 @@ struct ALds {
     float gy[4][D], kh[4][D], uh[4][D];
     float r2[3][2][D];   // A_t gy, Sigma z
     float r3[3][D];      // A_{t-1} gz
+    float gd[3];         // gdelta
 };
 
 template <int D, typename Tin>
@@ -327,13 +345,14 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
 {
     using Cf = SplitCfg<D>;
     using K = rec::Keep<D>;
-    constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NW = Cf::NW, NV = Cf::NV, RS = K::RS, W = Cf::W;
-    static_assert(NW >= 7, "six copying waves besides wave 0");
+    constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NV = Cf::NV, RS = K::RS;
+    constexpr int NG = 6;   // streams: galpha, alpha^, z, k, u, the scalars
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int row = tid / TPR, c0 = (tid % TPR) * EPT;
-    const bool leader = tid % TPR == 0;
+    const bool rows = w < Cf::NWR;
+    const int row = rows ? tid / TPR : 0, c0 = (tid % TPR) * EPT;
+    const bool leader = rows && tid % TPR == 0;
     const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
     const float *rh = rec + tok0 * RS;
 
@@ -343,30 +362,24 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
     double Sg[EPT];
     sfor<EPT>([&](auto e) {
         const size_t off = bh * DD + (size_t)row * D + c0 + e, toff = bh * DD + (size_t)(c0 + e) * D + row;
-        A[e] = A_T[off];
-        Sg[e] = dA_T ? (double)dA_T[off] + (double)dA_T[toff] : 0.0;
+        A[e] = rows ? A_T[off] : 0.f;
+        Sg[e] = rows && dA_T ? (double)dA_T[off] + (double)dA_T[toff] : 0.0;
     });
 
-    // copying groups: 0 galpha, 1 alpha^, 2 z, 3 k, 4 u, 5 the scalars; group i
-    // is wave NW - 1 - i's
-    const int grp = NW - 1 - w;
-    const bool copier = grp <= 5;
-    Stream st{Buf(nullptr, 0u), 0u, 1u, nullptr, W};
-    {
-        const unsigned recb = (unsigned)(T * RS * 4), inb = (unsigned)(T * D * sizeof(Tin));
-        const unsigned ncf = (D + 63) / 64, nci = (D * (unsigned)sizeof(Tin) + 255) / 256;
-        if (grp == 0) st = Stream{Buf(galpha + tok0 * D, (unsigned)(T * D * 4)), D * 4u, ncf, &L.ga[0][0], W};
-        if (grp == 1) st = Stream{Buf(rh + K::AL, recb - K::AL * 4u), RS * 4u, ncf, &L.al[0][0], W};
-        if (grp == 2) st = Stream{Buf(rh + K::Z, recb - K::Z * 4u), RS * 4u, ncf, &L.z[0][0], W};
-        if (grp == 3) st = Stream{Buf(k + tok0 * D, inb), D * (unsigned)sizeof(Tin), nci, &L.rk[0][0], W};
-        if (grp == 4) st = Stream{Buf(u + tok0 * D, inb), D * (unsigned)sizeof(Tin), nci, &L.ru[0][0], W};
-        if (grp == 5) st = Stream{Buf(rh + K::SC, recb - K::SC * 4u), RS * 4u, 1u, &L.sc[0][0], 64};
-    }
-    // Tokens >= seen are out of the memory chain's workgroup (its last
-    // published value, read with acquire ordering).  A wait gives up after
-    // SPIN_LIMIT polls (its workgroup, already running, should publish within
-    // microseconds); from then on the wave waits no more and the outputs of
-    // the head are NaN, so a failure shows instead of hanging.
+    const unsigned recb = (unsigned)(T * RS * 4);
+    const Stream sg[NG] = {
+        fstream<D>(galpha + tok0 * D, (unsigned)(T * D * 4), D * 4u, &L.ga[0][0]),
+        fstream<D>(rh + K::AL, recb - K::AL * 4u, RS * 4u, &L.al[0][0]),
+        fstream<D>(rh + K::Z, recb - K::Z * 4u, RS * 4u, &L.z[0][0]),
+        istream<D, Tin>(k + tok0 * D, T, &L.rk[0][0]),
+        istream<D, Tin>(u + tok0 * D, T, &L.ru[0][0]),
+        Stream{Buf(rh + K::SC, recb - K::SC * 4u), RS * 4u, 1u, &L.sc[0][0], 64}};
+
+    // Tokens >= seen are out of the memory workgroup (its last published
+    // value, read with acquire ordering).  A wait gives up after SPIN_LIMIT
+    // polls (the memory workgroup, already running, publishes within
+    // microseconds); from then on the wave waits no more and the head's
+    // outputs are NaN, so a failure shows instead of hanging.
     int seen = T;
     bool lost = false;
     auto await = [&](int x) {
@@ -380,33 +393,30 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
         }
     };
     auto issue = [&](int x) {
-        if (grp == 0) await(x);   // galpha of token x must be out
-        if (copier) st.template issue<NV>(x, lane);
+        if (w == Cf::WCOPY) {
+            await(x);   // galpha of token x must be out
+            sfor<NG>([&](auto i) { sg[i].template issue<NV>(x, lane); });
+        }
     };
     // gy = (galpha - alpha^ (alpha^'galpha)) / |y|; k^ = k / |k|; u^ = u / |u|
     auto transform = [&](int x) {
+        if (w != Cf::WCOPY) return;
         const int rs = x & (RING - 1), ws = x & 3;
-        if (grp == 0) {
-            float aga = 0.f;
-            sfor<NV>([&](auto c) {
-                const int j = lane + 64 * c;
-                if (j < D) aga = fmaf(L.al[rs][j], L.ga[rs][j], aga);
-            });
-            aga = wave_sum(aga);
-            const float iy = L.sc[rs][1];
-            sfor<NV>([&](auto c) {
-                const int j = lane + 64 * c;
-                if (j < D) L.gy[ws][j] = (L.ga[rs][j] - L.al[rs][j] * aga) * iy;
-            });
-        } else if (grp == 3 || grp == 4) {
-            const float sc = grp == 3 ? L.sc[rs][3] : L.sc[rs][4];
-            const float *raw = grp == 3 ? L.rk[rs] : L.ru[rs];
-            float *dst = grp == 3 ? L.kh[ws] : L.uh[ws];
-            sfor<NV>([&](auto c) {
-                const int j = lane + 64 * c;
-                if (j < D) dst[j] = raw_get<Tin>(raw, j) * sc;
-            });
-        }
+        float aga = 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) aga = fmaf(L.al[rs][j], L.ga[rs][j], aga);
+        });
+        aga = wave_sum(aga);
+        const float iy = L.sc[rs][1], ik = L.sc[rs][3], iu = L.sc[rs][4];
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                L.gy[ws][j] = (L.ga[rs][j] - L.al[rs][j] * aga) * iy;
+                L.kh[ws][j] = raw_get<Tin>(L.rk[rs], j) * ik;
+                L.uh[ws][j] = raw_get<Tin>(L.ru[rs], j) * iu;
+            }
+        });
     };
 
     // step 1: Sigma += gy k^' + k^ gy', then A_t gy and Sigma z
@@ -428,9 +438,8 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
             L.r2[s][1][row] = psz;
         }
     };
-    // step 2: gdelta, gz; A_{t-1} and A_{t-1} gz; Sigma += gz u^' + u^ gz'.
-    // Returns gdelta.
-    auto step2 = [&](int t) -> float {
+    // step 2: gdelta, gz; A_{t-1} and A_{t-1} gz; Sigma += gz u^' + u^ gz'
+    auto step2 = [&](int t) {
         const int v = t & 3, r = t & (RING - 1), s = t % 3;
         const float id = 1.f / L.sc[r][0];
         float zsz = 0.f;
@@ -452,14 +461,14 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
         });
         pagz = row_sum<TPR>(pagz);
         if (leader) L.r3[s][row] = pagz;
-        return gdel;
+        if (tid == 0) L.gd[s] = gdel;
     };
-    // wave 0: token t's du and the penalty chain's share of dk (added to the
-    // memory chain's, written by vla_bwd_s)
-    auto grads = [&](int t, float gdel) {
+    // gradient wave: token t's du and the penalty chain's share of dk (added
+    // to the memory chain's, written by the memory workgroup)
+    auto grads = [&](int t) {
         const int v = t & 3, r = t & (RING - 1), s = t % 3;
-        const float ik = L.sc[r][3], iu = L.sc[r][4];
-        await(t);   // the memory chain's dk share of token t is written (returns at once)
+        const float ik = L.sc[r][3], iu = L.sc[r][4], gdel = L.gd[s];
+        await(t);   // the memory chain's dk share of token t is out (returns at once)
         const float bad = lost ? __builtin_nanf("") : 0.f;
         float guh[NV], a4 = 0.f, a5 = 0.f;
         sfor<NV>([&](auto c) {
@@ -489,24 +498,25 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
     if (T > 0) transform(T - 1);
     if (T > 1) transform(T - 2);
     __syncthreads();
-    if (T > 0) step1(T - 1);
+    if (rows && T > 0) step1(T - 1);
     lds_barrier();
-    float gdel_g = 0.f;   // wave 0: gdelta of the token whose gradients come next
     for (int t = T - 1; t >= 0; --t) {
         if (t >= LA) issue(t - LA);
         if (t >= 2) transform(t - 2);
-        if (w == 0 && t + 1 < T) grads(t + 1, gdel_g);
-        gdel_g = step2(t);
-        if (t >= 1) step1(t - 1);
-        if (copier) {
-            if (t >= LA) vm_wait<(LA - 3) * NV>();
+        if (w == Cf::WGRAD && t + 1 < T) grads(t + 1);
+        if (rows) {
+            step2(t);
+            if (t >= 1) step1(t - 1);
+        }
+        if (w == Cf::WCOPY) {
+            if (t >= LA) vm_wait<(LA - 3) * NG * NV>();
             else vmem_drain();
         }
         lds_barrier();
     }
-    if (w == 0 && T > 0) grads(0, gdel_g);
+    if (w == Cf::WGRAD && T > 0) grads(0);
 
-    if (dA0) {
+    if (rows && dA0) {
         const size_t off = bh * DD + (size_t)row * D + c0;
         sfor<EPT / 4>([&](auto h) {
             st4(dA0 + off + 4 * h, f4{(float)(0.5 * Sg[4 * h]), (float)(0.5 * Sg[4 * h + 1]),
