@@ -52,8 +52,10 @@ KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_twopass.hip",
                   "long_context_sequence_amd/csrc/vla_common.h",
                   "long_context_sequence_amd/csrc/vla_record.h"]
 TRAFFIC_SUMMARY = "profiles/vla_forward_b8h16_d64_t4096_bf16.txt"
-# the backward call: the two-pass forward keeping the per-token records, then vla_bwd
+# the backward call: the two-pass forward keeping the per-token records, then the
+# reverse sweep (vla_bwd_sync_init, vla_bwd_sweep)
 BWD_KERNEL_SOURCES = KERNEL_SOURCES + ["long_context_sequence_amd/csrc/vla_bwd.hip",
+                                       "long_context_sequence_amd/csrc/vla_bwd_split.hip",
                                        "long_context_sequence_amd/csrc/vla_bwd.h",
                                        "long_context_sequence_amd/csrc/vla_reduce.h"]
 BWD_TRAFFIC_SUMMARY = "profiles/vla_backward_b8h16_d64_t4096_bf16.txt"
@@ -281,7 +283,9 @@ def backward_bench(args):
                      "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
                      "traffic": measured_traffic(BWD_TRAFFIC_SUMMARY, BWD_KERNEL_SOURCES),
                      "kernel": "vla_backward call: vla_gram, vla_seginv, vla_pen, vla_mem "
-                               "(keeping the per-token records), vla_bwd", "kernel_ms": kern_ms,
+                               "(keeping the per-token records), vla_bwd_sync_init, "
+                               "vla_bwd_sweep (the two adjoint chains side by side)",
+                     "kernel_ms": kern_ms,
                      "kernel_ms_median": float(np.median(launch_ms)), "flop_per_launch": flop,
                      "dtype": "fp32"},
     }
