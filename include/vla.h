@@ -230,9 +230,12 @@ vla_status vla_forward_scan_workspace_size(int B, int H, int T, int d_h, size_t 
  * per token z = A_{t-1} u^, alpha^, e, zkey_t and five scalars in the workspace: for
  * d_h in {64, 96, 128} by the chunked two-pass forward of vla_forward (its o
  * passes through dq, which is then overwritten), for d_h in {16, 32} token by
- * token in the gradient kernel itself.  One workgroup per head then runs the
- * reverse recurrence from t = T down to 1 with the states rebuilt from those
- * vectors.  Errors as for vla_forward.
+ * token in the gradient kernel itself.  The reverse recurrence then runs from
+ * t = T down to 1 with the states rebuilt from those vectors: for d_h in
+ * {64, 96, 128} as two workgroups per head in one launch (the memory chain's
+ * adjoint, and the penalty chain's following it through dL/dalpha^ kept in the
+ * workspace), for d_h in {16, 32} as one workgroup per head.  Errors as for
+ * vla_forward.
  */
 vla_status vla_backward(const void *q, const void *k, const void *v, const void *u,
                         vla_dtype in_dtype, int B, int H, int T, int d_h,
