@@ -64,8 +64,8 @@ struct SplitCfg {
     static_assert(EPT % 4 == 0 && NR % 64 == 0 && NT <= 1024, "row slices of whole granules");
 };
 
-// Token vectors reach LDS by direct copies (4 bytes per lane, NV copies per
-// token and stream), LA tokens ahead of the interval whose step 2 they feed,
+// Token vectors reach LDS by direct copies (4 bytes per lane, 256 bytes per
+// copy), LA tokens ahead of the interval whose step 2 they feed,
 // into rings of RING slots.  At the end of each interval the copy wave waits
 // for its copies of the token three ahead (the next interval transforms it and
 // the one after uses it), so LA - 3 tokens of copies stay in flight.
@@ -89,36 +89,46 @@ __device__ __forceinline__ float raw_get(const float *row, int j)
 }
 
 // One stream of per-token vectors: token x's bytes at base + x * stride (+ 256
-// per copy) into ring row x mod RING; ncopy copies per token, padded to NV with
-// repeats of the first so that every stream issues NV per token.
+// per copy) into ring row x mod RING, NC copies per token.  The copy wave's
+// wait counts are the exact number of copies per token (copies_per_token):
+// padding a stream with repeated copies would not do, since the compiler
+// merges identical copies.
+template <int NC>
 struct Stream {
     Buf buf;
-    unsigned stride, ncopy;
+    unsigned stride;
     float *ring;
     int row;   // ring row width (floats)
-    template <int NV>
     __device__ __forceinline__ void issue(int x, int lane) const
     {
         float *dst = ring + (x & (RING - 1)) * row;
         const unsigned vo = (unsigned)x * stride + 4u * (unsigned)lane;
-        sfor<NV>([&](auto i) {
-            const unsigned ii = (unsigned)i < ncopy ? (unsigned)i : 0u;
-            buf.lds4(dst + 64 * ii, vo + 256u * ii);
-        });
+        sfor<NC>([&](auto i) { buf.lds4(dst + 64 * i, vo + 256u * i); });
     }
 };
 
+// copies per token: a d-vector of floats, of inputs, the 8 scalars
+template <int D> constexpr int NCF = (D + 63) / 64;
+template <int D, typename Tin> constexpr int NCI = (D * (int)sizeof(Tin) + 255) / 256;
+
 template <int D>
-__device__ __forceinline__ Stream fstream(const float *base, unsigned bytes, unsigned stride, float *ring)
+__device__ __forceinline__ Stream<NCF<D>> fstream(const float *base, unsigned bytes, unsigned stride,
+                                                  float *ring)
 {
-    return Stream{Buf(base, bytes), stride, (unsigned)(D + 63) / 64, ring, SplitCfg<D>::W};
+    return Stream<NCF<D>>{Buf(base, bytes), stride, ring, SplitCfg<D>::W};
 }
 
 template <int D, typename Tin>
-__device__ __forceinline__ Stream istream(const Tin *base, int T, float *ring)
+__device__ __forceinline__ Stream<NCI<D, Tin>> istream(const Tin *base, int T, float *ring)
 {
-    return Stream{Buf(base, (unsigned)(T * D * sizeof(Tin))), D * (unsigned)sizeof(Tin),
-                  (D * (unsigned)sizeof(Tin) + 255) / 256, ring, SplitCfg<D>::W};
+    return Stream<NCI<D, Tin>>{Buf(base, (unsigned)(T * D * sizeof(Tin))), D * (unsigned)sizeof(Tin),
+                               ring, SplitCfg<D>::W};
+}
+
+__device__ __forceinline__ Stream<1> scstream(const float *base, unsigned bytes, unsigned stride,
+                                              float *ring)
+{
+    return Stream<1>{Buf(base, bytes), stride, ring, 64};
 }
 
 // ------------------------------------------------------------- memory chain
@@ -143,7 +153,8 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
     using Cf = SplitCfg<D>;
     using K = rec::Keep<D>;
     constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NV = Cf::NV, RS = K::RS;
-    constexpr int NG = 7;   // streams: dL/do, alpha^, e, zkey_t, q, k, the scalars
+    // streams: dL/do, alpha^, e, zkey_t (floats), q, k (inputs), the scalars
+    constexpr int CPT = 4 * NCF<D> + 2 * NCI<D, Tin> + 1;   // copies per token
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -168,16 +179,23 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
     });
 
     const unsigned recb = (unsigned)(T * RS * 4);
-    const Stream sg[NG] = {
-        fstream<D>(dO + tok0 * D, (unsigned)(T * D * 4), D * 4u, &L.g[0][0]),
-        fstream<D>(rh + K::AL, recb - K::AL * 4u, RS * 4u, &L.al[0][0]),
-        fstream<D>(rh + K::E, recb - K::E * 4u, RS * 4u, &L.e[0][0]),
-        fstream<D>(rh + K::ZK, recb - K::ZK * 4u, RS * 4u, &L.zt[0][0]),
-        istream<D, Tin>(q + tok0 * D, T, &L.rq[0][0]),
-        istream<D, Tin>(k + tok0 * D, T, &L.rk[0][0]),
-        Stream{Buf(rh + K::SC, recb - K::SC * 4u), RS * 4u, 1u, &L.sc[0][0], 64}};
+    const auto s_g = fstream<D>(dO + tok0 * D, (unsigned)(T * D * 4), D * 4u, &L.g[0][0]);
+    const auto s_al = fstream<D>(rh + K::AL, recb - K::AL * 4u, RS * 4u, &L.al[0][0]);
+    const auto s_e = fstream<D>(rh + K::E, recb - K::E * 4u, RS * 4u, &L.e[0][0]);
+    const auto s_zt = fstream<D>(rh + K::ZK, recb - K::ZK * 4u, RS * 4u, &L.zt[0][0]);
+    const auto s_q = istream<D, Tin>(q + tok0 * D, T, &L.rq[0][0]);
+    const auto s_k = istream<D, Tin>(k + tok0 * D, T, &L.rk[0][0]);
+    const auto s_sc = scstream(rh + K::SC, recb - K::SC * 4u, RS * 4u, &L.sc[0][0]);
     auto issue = [&](int x) {
-        if (w == Cf::WCOPY) sfor<NG>([&](auto i) { sg[i].template issue<NV>(x, lane); });
+        if (w == Cf::WCOPY) {
+            s_g.issue(x, lane);
+            s_al.issue(x, lane);
+            s_e.issue(x, lane);
+            s_zt.issue(x, lane);
+            s_q.issue(x, lane);
+            s_k.issue(x, lane);
+            s_sc.issue(x, lane);
+        }
     };
     // q: phi(q), phi'(q); k: k^ = k / |k|, phi'(k) (two tokens ahead)
     auto transform = [&](int x) {
@@ -301,7 +319,7 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
             if (t >= 1) step1(t - 1);
         }
         if (w == Cf::WCOPY) {   // this wave's copies of token t - 3 done
-            if (t >= LA) vm_wait<(LA - 3) * NG * NV>();
+            if (t >= LA) vm_wait<(LA - 3) * CPT>();
             else vmem_drain();
         }
         lds_barrier();
@@ -346,7 +364,8 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
     using Cf = SplitCfg<D>;
     using K = rec::Keep<D>;
     constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NV = Cf::NV, RS = K::RS;
-    constexpr int NG = 6;   // streams: galpha, alpha^, z, k, u, the scalars
+    // streams: galpha, alpha^, z (floats), k, u (inputs), the scalars
+    constexpr int CPT = 3 * NCF<D> + 2 * NCI<D, Tin> + 1;   // copies per token
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -367,13 +386,12 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
     });
 
     const unsigned recb = (unsigned)(T * RS * 4);
-    const Stream sg[NG] = {
-        fstream<D>(galpha + tok0 * D, (unsigned)(T * D * 4), D * 4u, &L.ga[0][0]),
-        fstream<D>(rh + K::AL, recb - K::AL * 4u, RS * 4u, &L.al[0][0]),
-        fstream<D>(rh + K::Z, recb - K::Z * 4u, RS * 4u, &L.z[0][0]),
-        istream<D, Tin>(k + tok0 * D, T, &L.rk[0][0]),
-        istream<D, Tin>(u + tok0 * D, T, &L.ru[0][0]),
-        Stream{Buf(rh + K::SC, recb - K::SC * 4u), RS * 4u, 1u, &L.sc[0][0], 64}};
+    const auto s_ga = fstream<D>(galpha + tok0 * D, (unsigned)(T * D * 4), D * 4u, &L.ga[0][0]);
+    const auto s_al = fstream<D>(rh + K::AL, recb - K::AL * 4u, RS * 4u, &L.al[0][0]);
+    const auto s_z = fstream<D>(rh + K::Z, recb - K::Z * 4u, RS * 4u, &L.z[0][0]);
+    const auto s_k = istream<D, Tin>(k + tok0 * D, T, &L.rk[0][0]);
+    const auto s_u = istream<D, Tin>(u + tok0 * D, T, &L.ru[0][0]);
+    const auto s_sc = scstream(rh + K::SC, recb - K::SC * 4u, RS * 4u, &L.sc[0][0]);
 
     // Tokens >= seen are out of the memory workgroup (its last published
     // value, read with acquire ordering).  A wait gives up after SPIN_LIMIT
@@ -395,7 +413,12 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
     auto issue = [&](int x) {
         if (w == Cf::WCOPY) {
             await(x);   // galpha of token x must be out
-            sfor<NG>([&](auto i) { sg[i].template issue<NV>(x, lane); });
+            s_ga.issue(x, lane);
+            s_al.issue(x, lane);
+            s_z.issue(x, lane);
+            s_k.issue(x, lane);
+            s_u.issue(x, lane);
+            s_sc.issue(x, lane);
         }
     };
     // gy = (galpha - alpha^ (alpha^'galpha)) / |y|; k^ = k / |k|; u^ = u / |u|
@@ -509,7 +532,7 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
             if (t >= 1) step1(t - 1);
         }
         if (w == Cf::WCOPY) {
-            if (t >= LA) vm_wait<(LA - 3) * NG * NV>();
+            if (t >= LA) vm_wait<(LA - 3) * CPT>();
             else vmem_drain();
         }
         lds_barrier();

@@ -206,6 +206,41 @@ def test_backward_deterministic():
         assert np.array_equal(a[n], b[n]), n
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_more_workgroups_than_fit(d):
+    """Far more heads than the device holds workgroups at once (2 per head in the
+    reverse sweep): the penalty-chain workgroups that start early wait only on
+    memory-chain workgroups already running, so every head completes; sampled
+    heads, the first and last included, against the oracle."""
+    dev = _dev()
+    B, H, T = 4, 160 if d == 64 else 96, 40
+    cfg = _cfg(d, "bf16", B, H, T)
+    _say(f"backward d={d} B={B} H={H} T={T} ({2 * B * H} sweep workgroups)")
+    x = gen.make_inputs(cfg)
+    adj = _adjoints(B, H, T, d, seed=11)
+    got = _gpu_backward(cfg, x, adj, dev)
+    for n in NAMES:
+        assert np.isfinite(got[n]).all(), n
+    _compare(cfg, x, adj, got, [(0, 0), (1, H // 2), (2, 7), (B - 1, H - 1)])
+
+
+@pytest.mark.parametrize("d,dtype", [(96, "f32"), (96, "bf16"), (128, "f32"), (128, "bf16")])
+def test_backward_repeat_bitwise(d, dtype):
+    """Repeated calls give the same bits at the head sizes whose token streams
+    take several copies per token (every copy of a token must have landed
+    before the token is used); 128 heads, so both chains of every head run side
+    by side."""
+    dev = _dev()
+    cfg = _cfg(d, dtype, 4, 32, 160)
+    x = gen.make_inputs(cfg)
+    adj = _adjoints(4, 32, 160, d, seed=17)
+    first = _gpu_backward(cfg, x, adj, dev)
+    for rep in range(3):
+        again = _gpu_backward(cfg, x, adj, dev)
+        for n in NAMES:
+            assert np.array_equal(again[n], first[n]), f"call {rep + 1}: {n}"
+
+
 def test_backward_workload_every_head():
     """B=4, H=8, d=64, T=1024 fp32 (the forward parity workload), every head."""
     dev = _dev()
