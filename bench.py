@@ -157,6 +157,9 @@ def parse():
                    help="time vla_forward_scan (memory chain as a scan over chunks) instead")
     p.add_argument("--backward", action="store_true",
                    help="time vla_backward (gradients) on the same workload instead")
+    p.add_argument("--decode", action="store_true",
+                   help="only the long-context workload's decode continuation (its forward "
+                        "once for the state, then the vla_step tokens), its own JSON line")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     return p.parse_args()
@@ -530,6 +533,26 @@ def baselines(vla, torch, vla_ms):
     return out
 
 
+def decode_bench():
+    """The long-context workload's forward once (for the state), then its
+    decode tokens as in decode_continuation; one JSON line."""
+    import torch
+
+    import gen
+    import long_context_sequence_amd as vla
+    cfg = gen.config(5)
+    x = gen.make_inputs(cfg)
+    _, _, state = _time_forward(vla, torch, cfg, x, 1)
+    dec = decode_continuation(vla, torch, cfg, x, state)
+    print(json.dumps({
+        "metric": "VLA decode step, µs per token for all heads (fp32 state)",
+        "value": dec["us_per_step"], "unit": "us", "n_gpus": 1, "higher_is_better": False,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name + " decode", "B": cfg.B, "H": cfg.H, "d_h": cfg.d,
+                   "input_dtype": cfg.dtype, "state_dtype": "f32"},
+        "decode": dec}), flush=True)
+
+
 def other_workloads(vla, torch):
     """Forward time of each workload other than the headline one (parity
     cases, reported beside it), and the long-context workload's decode
@@ -565,6 +588,9 @@ def main():
         return
     if args.scan:
         scan_bench(args)
+        return
+    if args.decode:
+        decode_bench()
         return
 
     import numpy as np
