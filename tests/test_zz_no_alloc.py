@@ -58,3 +58,35 @@ def test_noalloc_rejects_oversized():
     o = torch.empty((B, H, T, d), device=dev)
     with pytest.raises(vla.VLAError):
         vla.vla_forward_noalloc(e, e, e, e, o=o)
+
+
+def test_noalloc_graph_replay():
+    """The use it exists for: captured in a HIP graph (nothing allocated inside
+    the capture), replayed three times with eager work between, every replay
+    equal to vla_forward's result."""
+    import dataclasses
+    import long_context_sequence_amd as vla
+    dev = _dev()
+    cfg = dataclasses.replace(gen.config(3), d=64).with_sizes(B=2, H=4, T=500)
+    B, H, T, d = cfg.B, cfg.H, cfg.T, cfg.d
+    t = _inputs(cfg, dev)
+    ref = vla.vla_forward(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps, return_state=True)
+    outs = [torch.empty((B, H, T, d), device=dev), torch.empty((B, H, d, d), device=dev),
+            torch.empty((B, H, d, d), device=dev), torch.empty((B, H, d), device=dev)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            vla.vla_forward_noalloc(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps,
+                                    o=outs[0], S_out=outs[1], A_out=outs[2], zkey_out=outs[3])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for a in outs:
+            a.fill_(float("nan"))
+        torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("o", "S", "A", "zkey"), outs, ref):
+            assert torch.equal(a, b), f"replay {rep}: {name}"
