@@ -25,14 +25,15 @@ hipError_t launch_backward(const BwdArgs &a);
 
 // The reverse sweep as two chains running side by side (vla_bwd_split.hip), for
 // d in {64, 96, 128}: per head a workgroup for the memory chain's adjoint (dS),
-// which writes dq, dv, its share of dk and the gate adjoint dL/dalpha^ per token
-// (galpha, [B][H][T][d]), and one for the penalty chain's adjoint (Sigma),
-// which follows it token by token, adds its share of dk and writes du.  rec
-// holds the forward's per-token records, S_T and A_T its final state; sync is
-// B H + 1 ints of workspace (role tickets and per-head progress), reset by the
-// launch itself.
+// which writes dv and the gate adjoint dL/dalpha^ per token (galpha,
+// [B][H][T][d]), and one for the penalty chain's adjoint in the conjugated
+// frame Q = A Sigma A, with S' and A, which follows it token by token and
+// writes dq, dk and du.  rec holds the forward's per-token records, S_T and A_T
+// its final state; sync is B H + 1 ints of workspace (role tickets and per-head
+// progress), reset by the launch itself; qb is B H d^2 floats of workspace
+// (Q_T when dL/dA_T is given, Q_0 when A_0 is).
 hipError_t launch_backward_split(const BwdArgs &a, const float *rec, const float *S_T,
-                                 const float *A_T, float *galpha, int *sync);
+                                 const float *A_T, float *galpha, int *sync, float *qb);
 
 // x y + z w with both products rounded before the sum (no fused multiply-add):
 // the same bits for (x, y, z, w) and (z, w, x, y), so that the two mirror

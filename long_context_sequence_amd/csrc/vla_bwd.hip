@@ -553,10 +553,11 @@ constexpr bool records_from_forward(int d) { return d == 64 || d == 96 || d == 1
 
 // Workspace: the per-token records; for d in {64, 96, 128} also the two-pass
 // forward's workspace, its final S, A, zkey, the gate adjoints dL/dalpha^ that
-// the memory chain's sweep hands to the penalty chain's, and their
-// synchronisation words.
+// the memory chain's sweep hands to the penalty chain's, their
+// synchronisation words and one d x d matrix per head for the penalty
+// adjoint's conjugated form at the ends of the sweep.
 struct BwdPlan {
-    size_t rec = 0, fwd = 0, st = 0, ga = 0, sync = 0, bytes = 0;
+    size_t rec = 0, fwd = 0, st = 0, ga = 0, sync = 0, qb = 0, bytes = 0;
 };
 BwdPlan bwd_plan(int BH, int T, int d)
 {
@@ -572,6 +573,8 @@ BwdPlan bwd_plan(int BH, int T, int d)
         off = up256(off + (size_t)BH * T * d * sizeof(float));
         p.sync = off;
         off = up256(off + ((size_t)BH + 1) * sizeof(int));
+        p.qb = off;
+        off = up256(off + (size_t)BH * d * d * sizeof(float));
     }
     p.bytes = off;
     return p;
@@ -609,7 +612,8 @@ hipError_t launch(const BwdArgs &a)
         const hipError_t e = launch_forward_twopass(f, 3);
         if (e != hipSuccess) return e;
         return launch_backward_split(a, rec, stS, stA, reinterpret_cast<float *>(ws + p.ga),
-                                     reinterpret_cast<int *>(ws + p.sync));
+                                     reinterpret_cast<int *>(ws + p.sync),
+                                     reinterpret_cast<float *>(ws + p.qb));
     } else {
         return launch_phase1<D, Tin>(a, grid, block, rec);
     }

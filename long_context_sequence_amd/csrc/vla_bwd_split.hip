@@ -4,45 +4,52 @@
 // Source: "Variational Linear Attention" (arXiv 2605.11196), section 3.3,
 // Eqs. (9)-(11); the pages print no backward, so this is the chain rule through
 // those equations in reverse order (the conventions are stated at vla_backward
-// in include/vla.h).  The forward's two chains meet only at alpha^ (Eq. (10)):
-// the memory chain (S) reads it, the penalty chain (A) makes it.  In reverse
-// the adjoint of S (dS) never needs the adjoint of A, and the adjoint of A
-// (Sigma = dA + dA', symmetric) needs from the memory side only dL/dalpha^_t.
-// So each head gets two workgroups:
+// in include/vla.h).  The forward's two chains meet only at alpha^ (Eq. (10)).
+// In reverse the adjoint of S (dS) never needs the adjoint of A, and the
+// adjoint of A needs from the memory side only g_alpha = dL/dalpha^_t.
 //
-//   memory     the memory chain's adjoint, per token t from T - 1 down:
-//              dS += g phi(q)'/den (g = dL/do_t);  ge = dS alpha^ (= dL/dv_t),
-//              galpha = dS'e (= dL/dalpha^_t), c1 = S_t'g;  dS -= ge k^';
-//              c2 = S_t'ge;  S_{t-1}' = S_t' - alpha^ e'.  It writes dq, dv, the
-//              memory chain's share of dk (with the key-sum adjoint) and galpha,
-//              and publishes how far it is.
-//   penalty    the penalty chain's adjoint, a few tokens behind: gy = (galpha -
-//              alpha^(alpha^'galpha)) / |y|;  Sigma += gy k^' + k^ gy';  A_t gy;
-//              Sigma z;  gdelta = z'Sigma z / (2 delta^2), gz = -Sigma z / delta +
-//              gdelta u^;  A_{t-1} = A_t + z z'/delta;  A_{t-1} gz;  Sigma += gz u^'
-//              + u^ gz'.  It adds the penalty chain's share of dk and writes du.
+// The adjoint of A in conjugated form.  With z = A_{t-1} u^ and delta = 1 +
+// u^'z, Eq. (9) reads A_t = (I - z u^'/delta) A_{t-1}, so the map that carries
+// the adjoint Sigma (= dA + dA') from A_t back to A_{t-1} is
+// M_t = I - u^ z'/delta = A_{t-1}^-1 A_t: Sigma_{t-1} = M_t Sigma'_t M_t', where
+// Sigma'_t = Sigma_t + gy k^' + k^ gy' adds the gate's share (gy = dL/dy_t for
+// y_t = A_t k^_t).  In the frame Q_t = A_t Sigma_t A_t the transport cancels:
+//     Q_{t-1} = Q_t + p y' + y p',   p = A_t gy,
+// and the gradient with respect to u^_t, which the chain rule assembles from
+// Sigma'_t z, z'Sigma'_t z and A_{t-1}, collapses to -Q_{t-1} u^_t (checked
+// in fp64 against the per-token recurrence, to rounding).  At the end
+// Sigma_0 = A_0^-1 Q_0 A_0^-1.  So the penalty side is an accumulation with
+// plain fp32 multiply-adds (the conjugated quantities carry no cancellation;
+// an fp32 model of this gives 2e-6 relative error in dL/du at T = 4096, where
+// an fp32 Sigma gave 7e-3) next to A_t itself (A_{t-1} = A_t + z z'/delta).
 //
-// The per-token arithmetic is the one-workgroup sweep's (vla_bwd.hip, which
-// serves d <= 32): the same operations in the same order, with dk's
-// normalisation Jacobian applied to each chain's share separately (it is
-// linear).
+// Two workgroups per head:
+//
+//   memory     dS and dS' (row slices), per token t from T - 1 down:
+//              dS += g phi(q)'/den (g = dL/do_t); ge = dS alpha^ (= dL/dv_t),
+//              g_alpha = dS'e; dS -= ge k^'.  It writes dv and g_alpha and
+//              publishes how far it is.
+//   penalty    A, Q and S' (row slices), a few tokens behind: p = A_t gy,
+//              Q u^, S_t'g, S_t'ge; Q += p y' + y p'; A_{t-1} = A_t + z z'/delta;
+//              S_{t-1}' = S_t' - alpha^ e'.  From these it writes du, dq and dk
+//              (both chains' shares) and the key-sum adjoint.
 //
 // Layout: D * TPR row threads, thread (row i, columns [c0, c0 + EPT)) holding
 // that slice of row i of each d x d matrix (row products are DPP sums over TPR
-// adjacent lanes), and two service waves (SplitCfg): the copy wave brings the token
-// vectors into LDS (direct copies LA tokens ahead into rings of RING slots,
-// transforms two tokens ahead into working slots), the gradient wave forms
-// each token's gradients from the row results.  Per token one barrier: the row
-// products of step 1 of token t go through LDS, then step 2 of token t and
-// step 1 of token t - 1 (thread-local dependencies only) share the next
+// adjacent lanes), and two service waves (SplitCfg): the copy wave brings the
+// token vectors into LDS (direct copies LA tokens ahead into rings of RING
+// slots, transforms two tokens ahead into working slots), the gradient wave
+// forms each token's gradients from the row results.  Per token one barrier:
+// the row products of step 1 of token t go through LDS, then step 2 of token t
+// and step 1 of token t - 1 (thread-local dependencies only) share the next
 // interval, while the gradient wave forms token t + 1's gradients (row results
 // in three LDS slots, transformed vectors in four: the gradient's token, the two
-// steps' tokens and the one being transformed).  So the row threads run only
-// the chain's own steps (where the service waves come on top of them).
+// steps' tokens and the one being transformed).
 #include "vla_bwd.h"
 #include "vla_chunk_parts.h"
 #include "vla_record.h"
 #include "vla_reduce.h"
+#include "vla_sweep.h"
 
 namespace vla {
 namespace {
@@ -90,9 +97,8 @@ __device__ __forceinline__ float raw_get(const float *row, int j)
 
 // One stream of per-token vectors: token x's bytes at base + x * stride (+ 256
 // per copy) into ring row x mod RING, NC copies per token.  The copy wave's
-// wait counts are the exact number of copies per token (copies_per_token):
-// padding a stream with repeated copies would not do, since the compiler
-// merges identical copies.
+// wait counts are the exact number of copies per token: padding a stream with
+// repeated copies would not do, since the compiler merges identical copies.
 template <int NC>
 struct Stream {
     Buf buf;
@@ -135,26 +141,23 @@ __device__ __forceinline__ Stream<1> scstream(const float *base, unsigned bytes,
 template <int D>
 struct SLds {
     static constexpr int W = SplitCfg<D>::W;
-    float g[RING][W], al[RING][W], e[RING][W], zt[RING][W], rq[RING][W], rk[RING][W];
+    float g[RING][W], al[RING][W], e[RING][W], rq[RING][W], rk[RING][W];
     float sc[RING][64];
-    float pq[4][D], dpq[4][D], kh[4][D], dpk[4][D];
-    float r1[3][3][D];   // ge, galpha, c1
-    float r2[3][D];      // c2
+    float pq[4][D], kh[4][D];
+    float r1[3][2][D];   // ge, g_alpha
 };
 
 template <int D, typename Tin>
 __device__ __forceinline__ void
 bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, int T, float eps,
-      const float *__restrict__ S_T, const float *__restrict__ dO, const float *dS_T,
-      const float *dzk_T, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
-      float *dS0, float *dzk0, const float *__restrict__ rec, float *__restrict__ galpha,
-      int *progress)
+      const float *__restrict__ dO, const float *dS_T, float *__restrict__ dv, float *dS0,
+      const float *__restrict__ rec, float *__restrict__ galpha, int *progress)
 {
     using Cf = SplitCfg<D>;
     using K = rec::Keep<D>;
     constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NV = Cf::NV, RS = K::RS;
-    // streams: dL/do, alpha^, e, zkey_t (floats), q, k (inputs), the scalars
-    constexpr int CPT = 4 * NCF<D> + 2 * NCI<D, Tin> + 1;   // copies per token
+    // streams: dL/do, alpha^, e (floats), q, k (inputs), the scalars
+    constexpr int CPT = 3 * NCF<D> + 2 * NCI<D, Tin> + 1;   // copies per token
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -164,25 +167,18 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
     const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
     const float *rh = rec + tok0 * RS;
 
-    // dS and dS' (row slices) from dL/dS_T, S_T' from the forward's final S
-    float gS[EPT], gSt[EPT], St[EPT];
+    // dS and dS' (row slices) from dL/dS_T
+    float gS[EPT], gSt[EPT];
     sfor<EPT>([&](auto e) {
         const size_t off = bh * DD + (size_t)row * D + c0 + e, toff = bh * DD + (size_t)(c0 + e) * D + row;
         gS[e] = rows && dS_T ? dS_T[off] : 0.f;
         gSt[e] = rows && dS_T ? dS_T[toff] : 0.f;
-        St[e] = rows ? S_T[toff] : 0.f;
-    });
-    float gzk[NV];   // gradient wave: the key-sum adjoint, entries lane + 64 c
-    sfor<NV>([&](auto c) {
-        const int j = lane + 64 * c;
-        gzk[c] = dzk_T && j < D ? dzk_T[(size_t)bh * D + j] : 0.f;
     });
 
     const unsigned recb = (unsigned)(T * RS * 4);
     const auto s_g = fstream<D>(dO + tok0 * D, (unsigned)(T * D * 4), D * 4u, &L.g[0][0]);
     const auto s_al = fstream<D>(rh + K::AL, recb - K::AL * 4u, RS * 4u, &L.al[0][0]);
     const auto s_e = fstream<D>(rh + K::E, recb - K::E * 4u, RS * 4u, &L.e[0][0]);
-    const auto s_zt = fstream<D>(rh + K::ZK, recb - K::ZK * 4u, RS * 4u, &L.zt[0][0]);
     const auto s_q = istream<D, Tin>(q + tok0 * D, T, &L.rq[0][0]);
     const auto s_k = istream<D, Tin>(k + tok0 * D, T, &L.rk[0][0]);
     const auto s_sc = scstream(rh + K::SC, recb - K::SC * 4u, RS * 4u, &L.sc[0][0]);
@@ -191,13 +187,12 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
             s_g.issue(x, lane);
             s_al.issue(x, lane);
             s_e.issue(x, lane);
-            s_zt.issue(x, lane);
             s_q.issue(x, lane);
             s_k.issue(x, lane);
             s_sc.issue(x, lane);
         }
     };
-    // q: phi(q), phi'(q); k: k^ = k / |k|, phi'(k) (two tokens ahead)
+    // q: phi(q); k: k^ = k / |k| (two tokens ahead)
     auto transform = [&](int x) {
         if (w != Cf::WCOPY) return;
         const int rs = x & (RING - 1), ws = x & 3;
@@ -205,93 +200,56 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
-                const float xq = raw_get<Tin>(L.rq[rs], j), xk = raw_get<Tin>(L.rk[rs], j);
-                L.pq[ws][j] = phi_fast(xq);
-                L.dpq[ws][j] = dphi(xq);
-                L.kh[ws][j] = xk * ik;
-                L.dpk[ws][j] = dphi(xk);
+                L.pq[ws][j] = phi_fast(raw_get<Tin>(L.rq[rs], j));
+                L.kh[ws][j] = raw_get<Tin>(L.rk[rs], j) * ik;
             }
         });
     };
 
-    // step 1: the readout's share of dS, then dS alpha^, dS'e, S_t'g
+    // step 1: the readout's share of dS, then dS alpha^ and dS'e
     auto step1 = [&](int t) {
         const int v = t & 3, r = t & (RING - 1), s = t % 3;
         const float iden = 1.f / fmaxf(L.sc[r][2], eps);
         const float gi = L.g[r][row] * iden, pqi = L.pq[v][row] * iden;
-        float pge = 0.f, pga = 0.f, pc1 = 0.f;
+        float pge = 0.f, pga = 0.f;
         sfor<EPT>([&](auto e) {
             const int j = c0 + e;
-            const float gj = L.g[r][j];
             gS[e] = fmaf(gi, L.pq[v][j], gS[e]);
-            gSt[e] = fmaf(pqi, gj, gSt[e]);
+            gSt[e] = fmaf(pqi, L.g[r][j], gSt[e]);
             pge = fmaf(gS[e], L.al[r][j], pge);
             pga = fmaf(gSt[e], L.e[r][j], pga);
-            pc1 = fmaf(St[e], gj, pc1);
         });
         pge = row_sum<TPR>(pge);
         pga = row_sum<TPR>(pga);
-        pc1 = row_sum<TPR>(pc1);
         if (leader) {
             L.r1[s][0][row] = pge;
             L.r1[s][1][row] = pga;
-            L.r1[s][2][row] = pc1;
         }
     };
-    // step 2: dS -= ge k^', S_t'ge, then S_{t-1}' = S_t' - alpha^ e'
+    // step 2: dS -= ge k^'
     auto step2 = [&](int t) {
-        const int v = t & 3, r = t & (RING - 1), s = t % 3;
-        const float khi = L.kh[v][row], gei = L.r1[s][0][row], ali = L.al[r][row];
-        float pc2 = 0.f;
+        const int v = t & 3, s = t % 3;
+        const float khi = L.kh[v][row], gei = L.r1[s][0][row];
         sfor<EPT>([&](auto e) {
             const int j = c0 + e;
-            const float gej = L.r1[s][0][j];
             gS[e] = fmaf(-gei, L.kh[v][j], gS[e]);
-            gSt[e] = fmaf(-khi, gej, gSt[e]);
-            pc2 = fmaf(St[e], gej, pc2);
-            St[e] = fmaf(-ali, L.e[r][j], St[e]);
+            gSt[e] = fmaf(-khi, L.r1[s][0][j], gSt[e]);
         });
-        pc2 = row_sum<TPR>(pc2);
-        if (leader) L.r2[s][row] = pc2;
     };
-    // gradient wave: token t's dq, dv, galpha and the memory chain's share of dk
+    // gradient wave: token t's dv and g_alpha
     auto grads = [&](int t) {
-        const int v = t & 3, r = t & (RING - 1), s = t % 3;
-        const float dn = L.sc[r][2], iden = 1.f / fmaxf(dn, eps), ik = L.sc[r][3];
-        float a1 = 0.f, a2 = 0.f;
-        sfor<NV>([&](auto c) {
-            const int j = lane + 64 * c;
-            if (j < D) {
-                a1 = fmaf(L.r1[s][2][j], L.pq[v][j], a1);   // g'S_t phi(q)
-                a2 = fmaf(L.e[r][j], L.r1[s][0][j], a2);    // e'ge
-            }
-        });
-        a1 = wave_sum(a1);
-        a2 = wave_sum(a2);
-        const float gden = dn >= eps ? -a1 * iden * iden : 0.f;
+        const int s = t % 3;
         const size_t o = (tok0 + t) * D;
-        float gkh[NV], a3 = 0.f;
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
-            gkh[c] = 0.f;
             if (j < D) {
-                const float gpq = fmaf(L.r1[s][2][j], iden, gden * L.zt[r][j]);
-                dq[o + j] = gpq * L.dpq[v][j];
                 dv[o + j] = L.r1[s][0][j];
                 galpha[o + j] = L.r1[s][1][j];
-                gzk[c] = fmaf(gden, L.pq[v][j], gzk[c]);
-                gkh[c] = fmaf(L.al[r][j], a2, -L.r2[s][j]);
-                a3 = fmaf(L.kh[v][j], gkh[c], a3);
             }
         });
-        a3 = wave_sum(a3);
-        sfor<NV>([&](auto c) {
-            const int j = lane + 64 * c;
-            if (j < D) dk[o + j] = fmaf(ik, gkh[c] - L.kh[v][j] * a3, gzk[c] * L.dpk[v][j]);
-        });
     };
-    // gradient wave: tokens >= t are out (dq, dv, the memory chain's dk share
-    // and galpha written): publish t to the penalty workgroup
+    // gradient wave: tokens >= t are out (dv and g_alpha written): publish t to
+    // the penalty workgroup
     auto publish = [&](int t) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         if (lane == 0) __hip_atomic_store(progress + bh, t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -335,37 +293,36 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
             st4(dS0 + off + 4 * h, f4{gS[4 * h], gS[4 * h + 1], gS[4 * h + 2], gS[4 * h + 3]});
         });
     }
-    if (w == Cf::WGRAD && dzk0) {
-        sfor<NV>([&](auto c) {
-            const int j = lane + 64 * c;
-            if (j < D) dzk0[(size_t)bh * D + j] = gzk[c];
-        });
-    }
 }
 
 // ------------------------------------------------------------ penalty chain
 template <int D>
 struct ALds {
     static constexpr int W = SplitCfg<D>::W;
-    float ga[RING][W], al[RING][W], z[RING][W], rk[RING][W], ru[RING][W];
+    float ga[RING][W], gv[RING][W], g[RING][W], al[RING][W], z[RING][W], e[RING][W], zt[RING][W];
+    float rq[RING][W], rk[RING][W], ru[RING][W];
     float sc[RING][64];
-    float gy[4][D], kh[4][D], uh[4][D];
-    float r2[3][2][D];   // A_t gy, Sigma z
-    float r3[3][D];      // A_{t-1} gz
-    float gd[3];         // gdelta
+    float gy[4][D], y[4][D], kh[4][D], uh[4][D], pq[4][D], dpq[4][D], dpk[4][D];
+    float yu[4];          // y'u^ per working slot
+    float r1[3][4][D];    // A_t gy, Q_t u^, S_t'g, S_t'ge
 };
 
 template <int D, typename Tin>
 __device__ __forceinline__ void
-bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, int T,
-      const float *__restrict__ A_T, const float *dA_T, float *__restrict__ dk, float *__restrict__ du,
-      float *dA0, const float *__restrict__ rec, const float *__restrict__ galpha, const int *progress)
+bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k,
+      const Tin *__restrict__ u, int T, float lambda0, float eps, const float *__restrict__ S_T,
+      const float *__restrict__ A_T, const float *__restrict__ dO, const float *dzk_T,
+      float *__restrict__ dq, float *__restrict__ dk, const float *__restrict__ dv,
+      float *__restrict__ du, bool qin, float *qb, float *dA0, bool a0given, float *dzk0,
+      const float *__restrict__ rec, const float *__restrict__ galpha, const int *progress)
 {
     using Cf = SplitCfg<D>;
     using K = rec::Keep<D>;
     constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NV = Cf::NV, RS = K::RS;
-    // streams: galpha, alpha^, z (floats), k, u (inputs), the scalars
-    constexpr int CPT = 3 * NCF<D> + 2 * NCI<D, Tin> + 1;   // copies per token
+    // streams: g_alpha, dL/dv, dL/do, alpha^, z, e, zkey_t (floats), q, k, u
+    // (inputs), the scalars
+    constexpr int CPT = 7 * NCF<D> + 3 * NCI<D, Tin> + 1;   // copies per token
+    static_assert((LA - 3) * CPT < 64, "wait count fits vmcnt");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -375,20 +332,30 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
     const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
     const float *rh = rec + tok0 * RS;
 
-    // A_T (row slice) and Sigma = dA_T + dA_T' (fp64 storage: its entries stay
-    // of order one while the sensitivities it carries down the chain shrink)
-    float A[EPT];
-    double Sg[EPT];
+    // A_T, Q_T = A_T Sigma_T A_T (formed beforehand when dL/dA_T is given) and
+    // S_T' (row slices)
+    float A[EPT], Q[EPT], St[EPT];
     sfor<EPT>([&](auto e) {
         const size_t off = bh * DD + (size_t)row * D + c0 + e, toff = bh * DD + (size_t)(c0 + e) * D + row;
         A[e] = rows ? A_T[off] : 0.f;
-        Sg[e] = rows && dA_T ? (double)dA_T[off] + (double)dA_T[toff] : 0.0;
+        Q[e] = rows && qin ? qb[off] : 0.f;
+        St[e] = rows ? S_T[toff] : 0.f;
+    });
+    float gzk[NV];   // gradient wave: the key-sum adjoint, entries lane + 64 c
+    sfor<NV>([&](auto c) {
+        const int j = lane + 64 * c;
+        gzk[c] = dzk_T && j < D ? dzk_T[(size_t)bh * D + j] : 0.f;
     });
 
-    const unsigned recb = (unsigned)(T * RS * 4);
-    const auto s_ga = fstream<D>(galpha + tok0 * D, (unsigned)(T * D * 4), D * 4u, &L.ga[0][0]);
+    const unsigned recb = (unsigned)(T * RS * 4), vb = (unsigned)(T * D * 4);
+    const auto s_ga = fstream<D>(galpha + tok0 * D, vb, D * 4u, &L.ga[0][0]);
+    const auto s_gv = fstream<D>(dv + tok0 * D, vb, D * 4u, &L.gv[0][0]);
+    const auto s_g = fstream<D>(dO + tok0 * D, vb, D * 4u, &L.g[0][0]);
     const auto s_al = fstream<D>(rh + K::AL, recb - K::AL * 4u, RS * 4u, &L.al[0][0]);
     const auto s_z = fstream<D>(rh + K::Z, recb - K::Z * 4u, RS * 4u, &L.z[0][0]);
+    const auto s_e = fstream<D>(rh + K::E, recb - K::E * 4u, RS * 4u, &L.e[0][0]);
+    const auto s_zt = fstream<D>(rh + K::ZK, recb - K::ZK * 4u, RS * 4u, &L.zt[0][0]);
+    const auto s_q = istream<D, Tin>(q + tok0 * D, T, &L.rq[0][0]);
     const auto s_k = istream<D, Tin>(k + tok0 * D, T, &L.rk[0][0]);
     const auto s_u = istream<D, Tin>(u + tok0 * D, T, &L.ru[0][0]);
     const auto s_sc = scstream(rh + K::SC, recb - K::SC * 4u, RS * 4u, &L.sc[0][0]);
@@ -412,16 +379,22 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
     };
     auto issue = [&](int x) {
         if (w == Cf::WCOPY) {
-            await(x);   // galpha of token x must be out
+            await(x);   // g_alpha and dL/dv of token x must be out
             s_ga.issue(x, lane);
+            s_gv.issue(x, lane);
+            s_g.issue(x, lane);
             s_al.issue(x, lane);
             s_z.issue(x, lane);
+            s_e.issue(x, lane);
+            s_zt.issue(x, lane);
+            s_q.issue(x, lane);
             s_k.issue(x, lane);
             s_u.issue(x, lane);
             s_sc.issue(x, lane);
         }
     };
-    // gy = (galpha - alpha^ (alpha^'galpha)) / |y|; k^ = k / |k|; u^ = u / |u|
+    // gy = (g_alpha - alpha^ (alpha^'g_alpha)) / |y|; y = A_t k^ = alpha^ |y|;
+    // k^, u^; phi(q), phi'(q), phi'(k); y'u^
     auto transform = [&](int x) {
         if (w != Cf::WCOPY) return;
         const int rs = x & (RING - 1), ws = x & 3;
@@ -432,85 +405,106 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
         });
         aga = wave_sum(aga);
         const float iy = L.sc[rs][1], ik = L.sc[rs][3], iu = L.sc[rs][4];
+        const float ny = iy > 0.f ? 1.f / iy : 0.f;   // |y| (0 with a zero key)
+        float yu = 0.f;
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
-                L.gy[ws][j] = (L.ga[rs][j] - L.al[rs][j] * aga) * iy;
-                L.kh[ws][j] = raw_get<Tin>(L.rk[rs], j) * ik;
-                L.uh[ws][j] = raw_get<Tin>(L.ru[rs], j) * iu;
+                const float al = L.al[rs][j], xq = raw_get<Tin>(L.rq[rs], j), xk = raw_get<Tin>(L.rk[rs], j);
+                const float yj = al * ny, uhj = raw_get<Tin>(L.ru[rs], j) * iu;
+                L.gy[ws][j] = (L.ga[rs][j] - al * aga) * iy;
+                L.y[ws][j] = yj;
+                L.kh[ws][j] = xk * ik;
+                L.uh[ws][j] = uhj;
+                L.pq[ws][j] = phi_fast(xq);
+                L.dpq[ws][j] = dphi(xq);
+                L.dpk[ws][j] = dphi(xk);
+                yu = fmaf(yj, uhj, yu);
             }
         });
+        yu = wave_sum(yu);
+        if (lane == 0) L.yu[ws] = yu;
     };
 
-    // step 1: Sigma += gy k^' + k^ gy', then A_t gy and Sigma z
+    // step 1: A_t gy, Q_t u^, S_t'g, S_t'ge
     auto step1 = [&](int t) {
         const int v = t & 3, r = t & (RING - 1), s = t % 3;
-        const float gyi = L.gy[v][row], khi = L.kh[v][row];
-        float paty = 0.f, psz = 0.f;
+        float pp = 0.f, pq = 0.f, p1 = 0.f, p2 = 0.f;
         sfor<EPT>([&](auto e) {
             const int j = c0 + e;
-            const float gyj = L.gy[v][j];
-            Sg[e] += (double)sym_sum(gyi, L.kh[v][j], khi, gyj);
-            paty = fmaf(A[e], gyj, paty);
-            psz = fmaf((float)Sg[e], L.z[r][j], psz);
+            pp = fmaf(A[e], L.gy[v][j], pp);
+            pq = fmaf(Q[e], L.uh[v][j], pq);
+            p1 = fmaf(St[e], L.g[r][j], p1);
+            p2 = fmaf(St[e], L.gv[r][j], p2);
         });
-        paty = row_sum<TPR>(paty);
-        psz = row_sum<TPR>(psz);
+        pp = row_sum<TPR>(pp);
+        pq = row_sum<TPR>(pq);
+        p1 = row_sum<TPR>(p1);
+        p2 = row_sum<TPR>(p2);
         if (leader) {
-            L.r2[s][0][row] = paty;
-            L.r2[s][1][row] = psz;
+            L.r1[s][0][row] = pp;
+            L.r1[s][1][row] = pq;
+            L.r1[s][2][row] = p1;
+            L.r1[s][3][row] = p2;
         }
     };
-    // step 2: gdelta, gz; A_{t-1} and A_{t-1} gz; Sigma += gz u^' + u^ gz'
+    // step 2: Q += p y' + y p'; A_{t-1} = A_t + z z'/delta; S_{t-1}' = S_t' - alpha^ e'
     auto step2 = [&](int t) {
         const int v = t & 3, r = t & (RING - 1), s = t % 3;
         const float id = 1.f / L.sc[r][0];
-        float zsz = 0.f;
-        sfor<NV>([&](auto c) {
-            const int j = lane + 64 * c;
-            if (j < D) zsz = fmaf(L.z[r][j], L.r2[s][1][j], zsz);
-        });
-        const float gdel = 0.5f * wave_sum(zsz) * id * id;
-        const float zi = L.z[r][row], uhi = L.uh[v][row];
-        const float gzi = fmaf(-L.r2[s][1][row], id, gdel * uhi);
-        float pagz = 0.f;
+        const float pi = L.r1[s][0][row], yi = L.y[v][row], zi = L.z[r][row], ali = L.al[r][row];
         sfor<EPT>([&](auto e) {
             const int j = c0 + e;
-            const float zj = L.z[r][j], uhj = L.uh[v][j];
-            const float gzj = fmaf(-L.r2[s][1][j], id, gdel * uhj);
-            A[e] = fmaf(zi * zj, id, A[e]);
-            pagz = fmaf(A[e], gzj, pagz);
-            Sg[e] += (double)sym_sum(gzi, uhj, uhi, gzj);
+            Q[e] = fmaf(pi, L.y[v][j], Q[e]);
+            Q[e] = fmaf(yi, L.r1[s][0][j], Q[e]);
+            A[e] = fmaf(zi * L.z[r][j], id, A[e]);
+            St[e] = fmaf(-ali, L.e[r][j], St[e]);
         });
-        pagz = row_sum<TPR>(pagz);
-        if (leader) L.r3[s][row] = pagz;
-        if (tid == 0) L.gd[s] = gdel;
     };
-    // gradient wave: token t's du and the penalty chain's share of dk (added
-    // to the memory chain's, written by the memory workgroup)
+    // gradient wave: token t's du, dq and dk (both chains' shares)
     auto grads = [&](int t) {
         const int v = t & 3, r = t & (RING - 1), s = t % 3;
-        const float ik = L.sc[r][3], iu = L.sc[r][4], gdel = L.gd[s];
-        await(t);   // the memory chain's dk share of token t is out (returns at once)
-        const float bad = lost ? __builtin_nanf("") : 0.f;
-        float guh[NV], a4 = 0.f, a5 = 0.f;
+        const float dn = L.sc[r][2], iden = 1.f / fmaxf(dn, eps), ik = L.sc[r][3], iu = L.sc[r][4];
+        const float yu = L.yu[v];
+        float s1 = 0.f, a1 = 0.f, a2 = 0.f;
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
-            guh[c] = 0.f;
             if (j < D) {
-                guh[c] = fmaf(gdel, L.z[r][j], L.r3[s][j]);
-                a4 = fmaf(L.uh[v][j], guh[c], a4);
-                a5 = fmaf(L.kh[v][j], L.r2[s][0][j], a5);
+                s1 = fmaf(L.r1[s][0][j], L.uh[v][j], s1);   // p'u^
+                a1 = fmaf(L.r1[s][2][j], L.pq[v][j], a1);   // g'S_t phi(q)
+                a2 = fmaf(L.e[r][j], L.gv[r][j], a2);       // e'ge
             }
         });
+        s1 = wave_sum(s1);
+        a1 = wave_sum(a1);
+        a2 = wave_sum(a2);
+        const float gden = dn >= eps ? -a1 * iden * iden : 0.f;
+        float wq[NV], gkh[NV], a3 = 0.f, a4 = 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            wq[c] = gkh[c] = 0.f;
+            if (j < D) {
+                const float p = L.r1[s][0][j];
+                // Q_{t-1} u^ = Q_t u^ + p (y'u^) + y (p'u^)
+                wq[c] = fmaf(L.y[v][j], s1, fmaf(p, yu, L.r1[s][1][j]));
+                gkh[c] = fmaf(L.al[r][j], a2, p - L.r1[s][3][j]);
+                a3 = fmaf(L.kh[v][j], gkh[c], a3);
+                a4 = fmaf(L.uh[v][j], wq[c], a4);
+            }
+        });
+        await(t);   // the memory chain's token t is out (returns at once)
+        const float bad = lost ? __builtin_nanf("") : 0.f;
+        a3 = wave_sum(a3);
         a4 = wave_sum(a4);
-        a5 = wave_sum(a5);
         const size_t o = (tok0 + t) * D;
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
-                du[o + j] = iu * (guh[c] - L.uh[v][j] * a4) + bad;
-                dk[o + j] += ik * (L.r2[s][0][j] - L.kh[v][j] * a5) + bad;
+                const float gpq = fmaf(L.r1[s][2][j], iden, gden * L.zt[r][j]);
+                gzk[c] = fmaf(gden, L.pq[v][j], gzk[c]);
+                dq[o + j] = gpq * L.dpq[v][j] + bad;
+                dk[o + j] = fmaf(ik, gkh[c] - L.kh[v][j] * a3, gzk[c] * L.dpk[v][j]) + bad;
+                du[o + j] = -iu * (wq[c] - L.uh[v][j] * a4) + bad;
             }
         });
     };
@@ -539,11 +533,24 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ k, const Tin *__restrict__ u, 
     }
     if (w == Cf::WGRAD && T > 0) grads(0);
 
+    if (w == Cf::WGRAD && dzk0) {
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) dzk0[(size_t)bh * D + j] = gzk[c];
+        });
+    }
+    // dL/dA_0 = Sigma_0 / 2 = A_0^-1 Q_0 A_0^-1 / 2: here for the default
+    // A_0 = I / lambda0; with a given A_0, Q_0 goes to qb for vla_bwd_sandwich
     if (rows && dA0) {
         const size_t off = bh * DD + (size_t)row * D + c0;
+        const float sc = 0.5f * lambda0 * lambda0;
         sfor<EPT / 4>([&](auto h) {
-            st4(dA0 + off + 4 * h, f4{(float)(0.5 * Sg[4 * h]), (float)(0.5 * Sg[4 * h + 1]),
-                                      (float)(0.5 * Sg[4 * h + 2]), (float)(0.5 * Sg[4 * h + 3])});
+            if (a0given) {
+                st4(qb + off + 4 * h, f4{Q[4 * h], Q[4 * h + 1], Q[4 * h + 2], Q[4 * h + 3]});
+            } else {
+                st4(dA0 + off + 4 * h,
+                    f4{sc * Q[4 * h], sc * Q[4 * h + 1], sc * Q[4 * h + 2], sc * Q[4 * h + 3]});
+            }
         });
     }
 }
@@ -562,11 +569,11 @@ __global__ void __launch_bounds__(256) vla_bwd_sync_init(int *sync, int BH, int 
 template <int D, typename Tin>
 __global__ void __launch_bounds__(SplitCfg<D>::NT)
 vla_bwd_sweep(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ u, int T,
-              float eps, const float *__restrict__ S_T, const float *__restrict__ A_T,
-              const float *__restrict__ dO, const float *dS_T, const float *dA_T, const float *dzk_T,
+              float lambda0, float eps, const float *__restrict__ S_T, const float *__restrict__ A_T,
+              const float *__restrict__ dO, const float *dS_T, const float *dzk_T,
               float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
-              float *__restrict__ du, float *dS0, float *dA0, float *dzk0,
-              const float *__restrict__ rec, float *__restrict__ galpha, int *sync, int BH)
+              float *__restrict__ du, float *dS0, float *dA0, float *dzk0, bool qin, bool a0given,
+              float *qb, const float *__restrict__ rec, float *__restrict__ galpha, int *sync, int BH)
 {
     __shared__ __align__(16) union {
         SLds<D> s;
@@ -577,40 +584,110 @@ vla_bwd_sweep(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *_
     __syncthreads();
     const int tk = ticket;
     if (tk < BH)
-        bwd_s<D, Tin>(L.s, tk, q, k, T, eps, S_T, dO, dS_T, dzk_T, dq, dk, dv, dS0, dzk0, rec, galpha,
-                      sync + 1);
+        bwd_s<D, Tin>(L.s, tk, q, k, T, eps, dO, dS_T, dv, dS0, rec, galpha, sync + 1);
     else
-        bwd_a<D, Tin>(L.a, tk - BH, k, u, T, A_T, dA_T, dk, du, dA0, rec, galpha, sync + 1);
+        bwd_a<D, Tin>(L.a, tk - BH, q, k, u, T, lambda0, eps, S_T, A_T, dO, dzk_T, dq, dk, dv, du, qin,
+                      qb, dA0, a0given, dzk0, rec, galpha, sync + 1);
+}
+
+// ----------------------------------------------- conjugation of the final adjoints
+// One workgroup per head, thread (row i, columns [c0, c0 + EPT)): out = L M L
+// with L, M symmetric d x d, through LDS (L and L M).
+//   mode 0 (before the sweep): Q_T = A_T Sigma_T A_T, Sigma_T = dA_T + dA_T'
+//   mode 1 (after it): dL/dA_0 = A_0^-1 Q_0 A_0^-1 / 2, with A_0^-1 by the
+//          symmetric sweep (fp64)
+template <int D>
+struct ConjLds {
+    float l[D][D + 1];
+    float lm[D][D + 1];
+    double rowbuf[2][4 * D + 16];
+};
+
+template <int D>
+__global__ void __launch_bounds__(D * 8)
+vla_bwd_sandwich(int mode, const float *__restrict__ lmat, const float *__restrict__ dA_T,
+                 float *qb, float *__restrict__ dA0)
+{
+    constexpr int TPR = 8, EPT = D / TPR;
+    __shared__ __align__(16) ConjLds<D> L;
+    const int bh = blockIdx.x, tid = threadIdx.x, i = tid / TPR, c0 = (tid % TPR) * EPT;
+    const size_t base = (size_t)bh * D * D;
+    const float *lh = lmat + base;
+    if (mode == 0) {
+        sfor<EPT>([&](auto e) { L.l[i][c0 + e] = lh[(size_t)i * D + c0 + e]; });
+    } else {
+        double m[EPT];
+        sfor<EPT>([&](auto e) { m[e] = (double)lh[(size_t)i * D + c0 + e]; });
+        sweep_all<D, EPT>(m, i, c0, L.rowbuf);   // -A_0^-1
+        sfor<EPT>([&](auto e) { L.l[i][c0 + e] = (float)-m[e]; });
+    }
+    __syncthreads();
+    // L M, row i, columns [c0, c0 + EPT): M from global (Sigma_T or Q_0)
+    float acc[EPT];
+    sfor<EPT>([&](auto e) { acc[e] = 0.f; });
+    for (int a = 0; a < D; ++a) {
+        const float la = L.l[i][a];
+        sfor<EPT>([&](auto e) {
+            const int c = c0 + e;
+            const float mv = mode == 0 ? dA_T[base + (size_t)a * D + c] + dA_T[base + (size_t)c * D + a]
+                                       : qb[base + (size_t)a * D + c];
+            acc[e] = fmaf(la, mv, acc[e]);
+        });
+    }
+    sfor<EPT>([&](auto e) { L.lm[i][c0 + e] = acc[e]; });
+    __syncthreads();
+    // (L M) L
+    sfor<EPT>([&](auto e) { acc[e] = 0.f; });
+    for (int a = 0; a < D; ++a) {
+        const float x = L.lm[i][a];
+        sfor<EPT>([&](auto e) { acc[e] = fmaf(x, L.l[a][c0 + e], acc[e]); });
+    }
+    sfor<EPT>([&](auto e) {
+        if (mode == 0) qb[base + (size_t)i * D + c0 + e] = acc[e];
+        else dA0[base + (size_t)i * D + c0 + e] = 0.5f * acc[e];
+    });
+}
+
+template <int D>
+hipError_t sandwich(int mode, int BH, const float *lmat, const float *dA_T, float *qb, float *dA0,
+                    hipStream_t stream)
+{
+    hipLaunchKernelGGL(vla_bwd_sandwich<D>, dim3(BH), dim3(D * 8), 0, stream, mode, lmat, dA_T, qb, dA0);
+    return hipGetLastError();
 }
 
 template <int D, typename Tin>
 hipError_t launch(const BwdArgs &a, const float *rec, const float *S_T, const float *A_T, float *galpha,
-                  int *sync)
+                  int *sync, float *qb)
 {
     const int BH = a.B * a.H;
+    const bool qin = a.dA_T != nullptr, a0given = a.A0 != nullptr && a.dA0 != nullptr;
+    hipError_t e;
+    if (qin && (e = sandwich<D>(0, BH, A_T, a.dA_T, qb, nullptr, a.stream)) != hipSuccess) return e;
     hipLaunchKernelGGL(vla_bwd_sync_init, dim3((BH + 256) / 256), dim3(256), 0, a.stream, sync, BH, a.T);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((vla_bwd_sweep<D, Tin>), dim3(2 * BH), dim3(SplitCfg<D>::NT), 0, a.stream,
-                       (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.u, a.T, a.eps, S_T, A_T, a.dO,
-                       a.dS_T, a.dA_T, a.dzk_T, a.dq, a.dk, a.dv, a.du, a.dS0, a.dA0, a.dzk0, rec, galpha,
-                       sync, BH);
-    return hipGetLastError();
+                       (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.u, a.T, a.lambda0, a.eps, S_T,
+                       A_T, a.dO, a.dS_T, a.dzk_T, a.dq, a.dk, a.dv, a.du, a.dS0, a.dA0, a.dzk0, qin,
+                       a0given, qb, rec, galpha, sync, BH);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a0given) return sandwich<D>(1, BH, a.A0, nullptr, qb, a.dA0, a.stream);
+    return hipSuccess;
 }
 
 }  // namespace
 
 hipError_t launch_backward_split(const BwdArgs &a, const float *rec, const float *S_T,
-                                 const float *A_T, float *galpha, int *sync)
+                                 const float *A_T, float *galpha, int *sync, float *qb)
 {
     const bool bf = a.dtype == 1;
     switch (a.d) {
-    case 64: return bf ? launch<64, uint16_t>(a, rec, S_T, A_T, galpha, sync)
-                       : launch<64, float>(a, rec, S_T, A_T, galpha, sync);
-    case 96: return bf ? launch<96, uint16_t>(a, rec, S_T, A_T, galpha, sync)
-                       : launch<96, float>(a, rec, S_T, A_T, galpha, sync);
-    case 128: return bf ? launch<128, uint16_t>(a, rec, S_T, A_T, galpha, sync)
-                        : launch<128, float>(a, rec, S_T, A_T, galpha, sync);
+    case 64: return bf ? launch<64, uint16_t>(a, rec, S_T, A_T, galpha, sync, qb)
+                       : launch<64, float>(a, rec, S_T, A_T, galpha, sync, qb);
+    case 96: return bf ? launch<96, uint16_t>(a, rec, S_T, A_T, galpha, sync, qb)
+                       : launch<96, float>(a, rec, S_T, A_T, galpha, sync, qb);
+    case 128: return bf ? launch<128, uint16_t>(a, rec, S_T, A_T, galpha, sync, qb)
+                        : launch<128, float>(a, rec, S_T, A_T, galpha, sync, qb);
     default: return hipErrorInvalidValue;
     }
 }

@@ -212,7 +212,8 @@ def test_backward_empty_no_outputs_is_ok():
 def test_backward_workspace_size():
     # (4 d + 8) floats per token of each head, rounded up to 256 bytes; for the
     # head sizes of the two-pass forward also its workspace, the final state,
-    # d floats per token of each head (the gate adjoints) and B H + 1 ints
+    # d floats per token of each head (the gate adjoints), B H + 1 ints and a
+    # d x d matrix per head
     def up(x):
         return (x + 255) // 256 * 256
     for d in (16, 32, 64, 96, 128):
@@ -220,7 +221,7 @@ def test_backward_workspace_size():
         want = up(2 * 3 * 100 * (4 * d + 8) * 4)
         if d >= 64:
             want += (up(vla.workspace_size(2, 3, 100, d)) + up(2 * 3 * (2 * d * d + d) * 4)
-                     + up(2 * 3 * 100 * d * 4) + up((2 * 3 + 1) * 4))
+                     + up(2 * 3 * 100 * d * 4) + up((2 * 3 + 1) * 4) + up(2 * 3 * d * d * 4))
         assert n == want, d
     assert vla.backward_workspace_size(1, 1, 0, 64) == 0
     with pytest.raises(vla.VLAError):
