@@ -34,12 +34,14 @@
 //              S_{t-1}' = S_t' - alpha^ e'.  From these it writes du, dq and dk
 //              (both chains' shares) and the key-sum adjoint.
 //
-// Layout: D * TPR row threads, thread (row i, columns [c0, c0 + EPT)) holding
-// that slice of row i of each d x d matrix (row products are DPP sums over TPR
-// adjacent lanes), and two service waves (SplitCfg): the copy wave brings the
-// token vectors into LDS (direct copies LA tokens ahead into rings of RING
-// slots, transforms two tokens ahead into working slots), the gradient wave
-// forms each token's gradients from the row results.  Per token one barrier:
+// Layout: (D / RB) * TPR row threads, thread (rows i0, i0 + 1, columns [c0,
+// c0 + EPT)) holding that block of each d x d matrix (row products are DPP
+// sums over TPR adjacent lanes; a token vector's entries are read from LDS
+// once for the block's two rows, which halves the LDS traffic of one row per
+// thread, the bound of this sweep), and two service waves (SplitCfg): the copy
+// wave brings the token vectors into LDS (direct copies LA tokens ahead into
+// rings of RING slots, transforms two tokens ahead into working slots), the
+// gradient wave forms each token's gradients from the row results.  Per token one barrier:
 // the row products of step 1 of token t go through LDS, then step 2 of token t
 // and step 1 of token t - 1 (thread-local dependencies only) share the next
 // interval, while the gradient wave forms token t + 1's gradients (row results
@@ -58,26 +60,35 @@ using namespace chunk;
 
 template <int D>
 struct SplitCfg {
-    // eight threads per row; the two service waves come on top where the
-    // workgroup has room (d = 64, 96), otherwise (d = 128: 1024 row threads,
-    // and four per row would need more registers than four waves per SIMD
-    // leave) the last two row waves serve as well
-    static constexpr int TPR = 8, EPT = D / TPR, NR = D * TPR, NWR = NR / 64;
-    static constexpr bool EXTRA = NR + 128 <= 1024;
-    static constexpr int NT = EXTRA ? NR + 128 : NR;
-    static constexpr int WCOPY = EXTRA ? NWR : NWR - 1, WGRAD = EXTRA ? NWR + 1 : NWR - 2;
+    // eight threads per pair of rows, then the two service waves
+    static constexpr int TPR = 8, EPT = D / TPR, RB = 2, NR = D / RB * TPR, NWR = NR / 64;
+    static constexpr int NT = NR + 128, WCOPY = NWR, WGRAD = NWR + 1;
     static constexpr int NV = (D + 63) / 64;
     static constexpr int W = 64 * NV;   // ring row: what NV wave-wide 4-byte copies fill
-    static_assert(EPT % 4 == 0 && NR % 64 == 0 && NT <= 1024, "row slices of whole granules");
+    static_assert(EPT % 4 == 0 && NR % 64 == 0 && NT <= 1024, "row blocks of whole granules");
 };
 
 // Token vectors reach LDS by direct copies (4 bytes per lane, 256 bytes per
 // copy), LA tokens ahead of the interval whose step 2 they feed,
 // into rings of RING slots.  At the end of each interval the copy wave waits
 // for its copies of the token three ahead (the next interval transforms it and
-// the one after uses it), so LA - 3 tokens of copies stay in flight.
-constexpr int RING = 8, LA = 6;
-static_assert(LA + 2 <= RING, "tokens in use at once: t + 1 down to t - LA");
+// the one after uses it), so LA - 3 tokens of copies stay in flight: as many as
+// the wait count can express (63 copies) for a chain that issues cpt copies
+// per token, at most LA_MAX.  (A copy takes a couple of microseconds to land,
+// several intervals.)
+#ifndef VLA_BWD_LA_MAX
+#define VLA_BWD_LA_MAX 12
+#endif
+constexpr int LA_MAX = VLA_BWD_LA_MAX;
+// d = 128 keeps six tokens in eight slots (with the larger rings, LDS offsets
+// past 64 KB, its loop runs out of registers)
+template <int D> constexpr int RING = D == 128 ? 8 : 16;
+constexpr int lookahead(int cpt, int d)
+{
+    const int la = 3 + 63 / cpt < LA_MAX ? 3 + 63 / cpt : LA_MAX;
+    return d == 128 && la > 6 ? 6 : la;
+}
+static_assert(LA_MAX + 2 <= RING<64>, "tokens in use at once: t + 1 down to t - LA");
 
 // The memory workgroup publishes its progress every PUB tokens; a waiting wave
 // polls at most SPIN_LIMIT times (each poll sleeps 256 cycles; about a second
@@ -99,7 +110,7 @@ __device__ __forceinline__ float raw_get(const float *row, int j)
 // per copy) into ring row x mod RING, NC copies per token.  The copy wave's
 // wait counts are the exact number of copies per token: padding a stream with
 // repeated copies would not do, since the compiler merges identical copies.
-template <int NC>
+template <int NC, int R>
 struct Stream {
     Buf buf;
     unsigned stride;
@@ -107,7 +118,7 @@ struct Stream {
     int row;   // ring row width (floats)
     __device__ __forceinline__ void issue(int x, int lane) const
     {
-        float *dst = ring + (x & (RING - 1)) * row;
+        float *dst = ring + (x & (R - 1)) * row;
         const unsigned vo = (unsigned)x * stride + 4u * (unsigned)lane;
         sfor<NC>([&](auto i) { buf.lds4(dst + 64 * i, vo + 256u * i); });
     }
@@ -118,31 +129,32 @@ template <int D> constexpr int NCF = (D + 63) / 64;
 template <int D, typename Tin> constexpr int NCI = (D * (int)sizeof(Tin) + 255) / 256;
 
 template <int D>
-__device__ __forceinline__ Stream<NCF<D>> fstream(const float *base, unsigned bytes, unsigned stride,
-                                                  float *ring)
+__device__ __forceinline__ Stream<NCF<D>, RING<D>> fstream(const float *base, unsigned bytes,
+                                                           unsigned stride, float *ring)
 {
-    return Stream<NCF<D>>{Buf(base, bytes), stride, ring, SplitCfg<D>::W};
+    return Stream<NCF<D>, RING<D>>{Buf(base, bytes), stride, ring, SplitCfg<D>::W};
 }
 
 template <int D, typename Tin>
-__device__ __forceinline__ Stream<NCI<D, Tin>> istream(const Tin *base, int T, float *ring)
+__device__ __forceinline__ Stream<NCI<D, Tin>, RING<D>> istream(const Tin *base, int T, float *ring)
 {
-    return Stream<NCI<D, Tin>>{Buf(base, (unsigned)(T * D * sizeof(Tin))), D * (unsigned)sizeof(Tin),
-                               ring, SplitCfg<D>::W};
+    return Stream<NCI<D, Tin>, RING<D>>{Buf(base, (unsigned)(T * D * sizeof(Tin))),
+                                        D * (unsigned)sizeof(Tin), ring, SplitCfg<D>::W};
 }
 
-__device__ __forceinline__ Stream<1> scstream(const float *base, unsigned bytes, unsigned stride,
-                                              float *ring)
+template <int D>
+__device__ __forceinline__ Stream<1, RING<D>> scstream(const float *base, unsigned bytes, unsigned stride,
+                                                       float *ring)
 {
-    return Stream<1>{Buf(base, bytes), stride, ring, 64};
+    return Stream<1, RING<D>>{Buf(base, bytes), stride, ring, 64};
 }
 
 // ------------------------------------------------------------- memory chain
 template <int D>
 struct SLds {
-    static constexpr int W = SplitCfg<D>::W;
-    float g[RING][W], al[RING][W], e[RING][W], rq[RING][W], rk[RING][W];
-    float sc[RING][64];
+    static constexpr int W = SplitCfg<D>::W, R = RING<D>;
+    float g[R][W], al[R][W], e[R][W], rq[R][W], rk[R][W];
+    float sc[R][64];
     float pq[4][D], kh[4][D];
     float r1[3][2][D];   // ge, g_alpha
 };
@@ -155,24 +167,28 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
 {
     using Cf = SplitCfg<D>;
     using K = rec::Keep<D>;
-    constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NV = Cf::NV, RS = K::RS;
+    constexpr int TPR = Cf::TPR, EPT = Cf::EPT, RB = Cf::RB, NV = Cf::NV, RS = K::RS;
     // streams: dL/do, alpha^, e (floats), q, k (inputs), the scalars
     constexpr int CPT = 3 * NCF<D> + 2 * NCI<D, Tin> + 1;   // copies per token
+    constexpr int LA = lookahead(CPT, D);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool rows = w < Cf::NWR;
-    const int row = rows ? tid / TPR : 0, c0 = (tid % TPR) * EPT;
+    const int i0 = rows ? tid / TPR * RB : 0, c0 = (tid % TPR) * EPT;
     const bool leader = rows && tid % TPR == 0;
     const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
     const float *rh = rec + tok0 * RS;
 
-    // dS and dS' (row slices) from dL/dS_T
-    float gS[EPT], gSt[EPT];
-    sfor<EPT>([&](auto e) {
-        const size_t off = bh * DD + (size_t)row * D + c0 + e, toff = bh * DD + (size_t)(c0 + e) * D + row;
-        gS[e] = rows && dS_T ? dS_T[off] : 0.f;
-        gSt[e] = rows && dS_T ? dS_T[toff] : 0.f;
+    // dS and dS' (row blocks) from dL/dS_T
+    float gS[RB][EPT], gSt[RB][EPT];
+    sfor<RB>([&](auto h) {
+        sfor<EPT>([&](auto e) {
+            const size_t off = bh * DD + (size_t)(i0 + h) * D + c0 + e;
+            const size_t toff = bh * DD + (size_t)(c0 + e) * D + i0 + h;
+            gS[h][e] = rows && dS_T ? dS_T[off] : 0.f;
+            gSt[h][e] = rows && dS_T ? dS_T[toff] : 0.f;
+        });
     });
 
     const unsigned recb = (unsigned)(T * RS * 4);
@@ -181,7 +197,7 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
     const auto s_e = fstream<D>(rh + K::E, recb - K::E * 4u, RS * 4u, &L.e[0][0]);
     const auto s_q = istream<D, Tin>(q + tok0 * D, T, &L.rq[0][0]);
     const auto s_k = istream<D, Tin>(k + tok0 * D, T, &L.rk[0][0]);
-    const auto s_sc = scstream(rh + K::SC, recb - K::SC * 4u, RS * 4u, &L.sc[0][0]);
+    const auto s_sc = scstream<D>(rh + K::SC, recb - K::SC * 4u, RS * 4u, &L.sc[0][0]);
     auto issue = [&](int x) {
         if (w == Cf::WCOPY) {
             s_g.issue(x, lane);
@@ -195,7 +211,7 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
     // q: phi(q); k: k^ = k / |k| (two tokens ahead)
     auto transform = [&](int x) {
         if (w != Cf::WCOPY) return;
-        const int rs = x & (RING - 1), ws = x & 3;
+        const int rs = x & (RING<D> - 1), ws = x & 3;
         const float ik = L.sc[rs][3];
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
@@ -208,32 +224,50 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
 
     // step 1: the readout's share of dS, then dS alpha^ and dS'e
     auto step1 = [&](int t) {
-        const int v = t & 3, r = t & (RING - 1), s = t % 3;
+        const int v = t & 3, r = t & (RING<D> - 1), s = t % 3;
         const float iden = 1.f / fmaxf(L.sc[r][2], eps);
-        const float gi = L.g[r][row] * iden, pqi = L.pq[v][row] * iden;
-        float pge = 0.f, pga = 0.f;
+        float gi[RB], pqi[RB], pge[RB], pga[RB];
+        sfor<RB>([&](auto h) {
+            gi[h] = L.g[r][i0 + h] * iden;
+            pqi[h] = L.pq[v][i0 + h] * iden;
+            pge[h] = pga[h] = 0.f;
+        });
         sfor<EPT>([&](auto e) {
             const int j = c0 + e;
-            gS[e] = fmaf(gi, L.pq[v][j], gS[e]);
-            gSt[e] = fmaf(pqi, L.g[r][j], gSt[e]);
-            pge = fmaf(gS[e], L.al[r][j], pge);
-            pga = fmaf(gSt[e], L.e[r][j], pga);
+            const float pqj = L.pq[v][j], gj = L.g[r][j], alj = L.al[r][j], ej = L.e[r][j];
+            sfor<RB>([&](auto h) {
+                gS[h][e] = fmaf(gi[h], pqj, gS[h][e]);
+                gSt[h][e] = fmaf(pqi[h], gj, gSt[h][e]);
+                pge[h] = fmaf(gS[h][e], alj, pge[h]);
+                pga[h] = fmaf(gSt[h][e], ej, pga[h]);
+            });
         });
-        pge = row_sum<TPR>(pge);
-        pga = row_sum<TPR>(pga);
+        sfor<RB>([&](auto h) {
+            pge[h] = row_sum<TPR>(pge[h]);
+            pga[h] = row_sum<TPR>(pga[h]);
+        });
         if (leader) {
-            L.r1[s][0][row] = pge;
-            L.r1[s][1][row] = pga;
+            sfor<RB>([&](auto h) {
+                L.r1[s][0][i0 + h] = pge[h];
+                L.r1[s][1][i0 + h] = pga[h];
+            });
         }
     };
     // step 2: dS -= ge k^'
     auto step2 = [&](int t) {
         const int v = t & 3, s = t % 3;
-        const float khi = L.kh[v][row], gei = L.r1[s][0][row];
+        float khi[RB], gei[RB];
+        sfor<RB>([&](auto h) {
+            khi[h] = L.kh[v][i0 + h];
+            gei[h] = L.r1[s][0][i0 + h];
+        });
         sfor<EPT>([&](auto e) {
             const int j = c0 + e;
-            gS[e] = fmaf(-gei, L.kh[v][j], gS[e]);
-            gSt[e] = fmaf(-khi, L.r1[s][0][j], gSt[e]);
+            const float khj = L.kh[v][j], gej = L.r1[s][0][j];
+            sfor<RB>([&](auto h) {
+                gS[h][e] = fmaf(-gei[h], khj, gS[h][e]);
+                gSt[h][e] = fmaf(-khi[h], gej, gSt[h][e]);
+            });
         });
     };
     // gradient wave: token t's dv and g_alpha
@@ -288,9 +322,11 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
     }
 
     if (rows && dS0) {
-        const size_t off = bh * DD + (size_t)row * D + c0;
-        sfor<EPT / 4>([&](auto h) {
-            st4(dS0 + off + 4 * h, f4{gS[4 * h], gS[4 * h + 1], gS[4 * h + 2], gS[4 * h + 3]});
+        sfor<RB>([&](auto h) {
+            float *dst = dS0 + bh * DD + (size_t)(i0 + h) * D + c0;
+            sfor<EPT / 4>([&](auto q) {
+                st4(dst + 4 * q, f4{gS[h][4 * q], gS[h][4 * q + 1], gS[h][4 * q + 2], gS[h][4 * q + 3]});
+            });
         });
     }
 }
@@ -298,13 +334,14 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
 // ------------------------------------------------------------ penalty chain
 template <int D>
 struct ALds {
-    static constexpr int W = SplitCfg<D>::W;
-    float ga[RING][W], gv[RING][W], g[RING][W], al[RING][W], z[RING][W], e[RING][W], zt[RING][W];
-    float rq[RING][W], rk[RING][W], ru[RING][W];
-    float sc[RING][64];
+    static constexpr int W = SplitCfg<D>::W, R = RING<D>;
+    float ga[R][W], gv[R][W], g[R][W], al[R][W], z[R][W], e[R][W], zt[R][W];
+    float rq[R][W], rk[R][W], ru[R][W];
+    float sc[R][64];
     float gy[4][D], y[4][D], kh[4][D], uh[4][D], pq[4][D], dpq[4][D], dpk[4][D];
-    float yu[4];          // y'u^ per working slot
+    float ts[4][4];       // per working slot: y'u^, e'ge, k^'alpha^
     float r1[3][4][D];    // A_t gy, Q_t u^, S_t'g, S_t'ge
+    int lost;             // the copy wave gave up waiting
 };
 
 template <int D, typename Tin>
@@ -318,28 +355,32 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k,
 {
     using Cf = SplitCfg<D>;
     using K = rec::Keep<D>;
-    constexpr int TPR = Cf::TPR, EPT = Cf::EPT, NV = Cf::NV, RS = K::RS;
+    constexpr int TPR = Cf::TPR, EPT = Cf::EPT, RB = Cf::RB, NV = Cf::NV, RS = K::RS;
     // streams: g_alpha, dL/dv, dL/do, alpha^, z, e, zkey_t (floats), q, k, u
     // (inputs), the scalars
     constexpr int CPT = 7 * NCF<D> + 3 * NCI<D, Tin> + 1;   // copies per token
+    constexpr int LA = lookahead(CPT, D);
     static_assert((LA - 3) * CPT < 64, "wait count fits vmcnt");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool rows = w < Cf::NWR;
-    const int row = rows ? tid / TPR : 0, c0 = (tid % TPR) * EPT;
+    const int i0 = rows ? tid / TPR * RB : 0, c0 = (tid % TPR) * EPT;
     const bool leader = rows && tid % TPR == 0;
     const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
     const float *rh = rec + tok0 * RS;
 
     // A_T, Q_T = A_T Sigma_T A_T (formed beforehand when dL/dA_T is given) and
-    // S_T' (row slices)
-    float A[EPT], Q[EPT], St[EPT];
-    sfor<EPT>([&](auto e) {
-        const size_t off = bh * DD + (size_t)row * D + c0 + e, toff = bh * DD + (size_t)(c0 + e) * D + row;
-        A[e] = rows ? A_T[off] : 0.f;
-        Q[e] = rows && qin ? qb[off] : 0.f;
-        St[e] = rows ? S_T[toff] : 0.f;
+    // S_T' (row blocks)
+    float A[RB][EPT], Q[RB][EPT], St[RB][EPT];
+    sfor<RB>([&](auto h) {
+        sfor<EPT>([&](auto e) {
+            const size_t off = bh * DD + (size_t)(i0 + h) * D + c0 + e;
+            const size_t toff = bh * DD + (size_t)(c0 + e) * D + i0 + h;
+            A[h][e] = rows ? A_T[off] : 0.f;
+            Q[h][e] = rows && qin ? qb[off] : 0.f;
+            St[h][e] = rows ? S_T[toff] : 0.f;
+        });
     });
     float gzk[NV];   // gradient wave: the key-sum adjoint, entries lane + 64 c
     sfor<NV>([&](auto c) {
@@ -358,7 +399,7 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k,
     const auto s_q = istream<D, Tin>(q + tok0 * D, T, &L.rq[0][0]);
     const auto s_k = istream<D, Tin>(k + tok0 * D, T, &L.rk[0][0]);
     const auto s_u = istream<D, Tin>(u + tok0 * D, T, &L.ru[0][0]);
-    const auto s_sc = scstream(rh + K::SC, recb - K::SC * 4u, RS * 4u, &L.sc[0][0]);
+    const auto s_sc = scstream<D>(rh + K::SC, recb - K::SC * 4u, RS * 4u, &L.sc[0][0]);
 
     // Tokens >= seen are out of the memory workgroup (its last published
     // value, read with acquire ordering).  A wait gives up after SPIN_LIMIT
@@ -380,6 +421,7 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k,
     auto issue = [&](int x) {
         if (w == Cf::WCOPY) {
             await(x);   // g_alpha and dL/dv of token x must be out
+            if (lost && lane == 0) L.lost = 1;
             s_ga.issue(x, lane);
             s_gv.issue(x, lane);
             s_g.issue(x, lane);
@@ -394,121 +436,136 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k,
         }
     };
     // gy = (g_alpha - alpha^ (alpha^'g_alpha)) / |y|; y = A_t k^ = alpha^ |y|;
-    // k^, u^; phi(q), phi'(q), phi'(k); y'u^
+    // k^, u^; phi(q), phi'(q), phi'(k); the token's y'u^, e'ge, k^'alpha^
     auto transform = [&](int x) {
         if (w != Cf::WCOPY) return;
-        const int rs = x & (RING - 1), ws = x & 3;
-        float aga = 0.f;
-        sfor<NV>([&](auto c) {
-            const int j = lane + 64 * c;
-            if (j < D) aga = fmaf(L.al[rs][j], L.ga[rs][j], aga);
-        });
-        aga = wave_sum(aga);
+        const int rs = x & (RING<D> - 1), ws = x & 3;
         const float iy = L.sc[rs][1], ik = L.sc[rs][3], iu = L.sc[rs][4];
         const float ny = iy > 0.f ? 1.f / iy : 0.f;   // |y| (0 with a zero key)
-        float yu = 0.f;
+        float aga = 0.f, yu = 0.f, ege = 0.f, kal = 0.f;
+        sfor<NV>([&](auto c) {
+            const int j = lane + 64 * c;
+            if (j < D) {
+                const float al = L.al[rs][j];
+                aga = fmaf(al, L.ga[rs][j], aga);
+                yu = fmaf(al * ny, raw_get<Tin>(L.ru[rs], j) * iu, yu);
+                ege = fmaf(L.e[rs][j], L.gv[rs][j], ege);
+                kal = fmaf(raw_get<Tin>(L.rk[rs], j) * ik, al, kal);
+            }
+        });
+        aga = wave_sum(aga);
+        yu = wave_sum(yu);
+        ege = wave_sum(ege);
+        kal = wave_sum(kal);
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
                 const float al = L.al[rs][j], xq = raw_get<Tin>(L.rq[rs], j), xk = raw_get<Tin>(L.rk[rs], j);
-                const float yj = al * ny, uhj = raw_get<Tin>(L.ru[rs], j) * iu;
                 L.gy[ws][j] = (L.ga[rs][j] - al * aga) * iy;
-                L.y[ws][j] = yj;
+                L.y[ws][j] = al * ny;
                 L.kh[ws][j] = xk * ik;
-                L.uh[ws][j] = uhj;
+                L.uh[ws][j] = raw_get<Tin>(L.ru[rs], j) * iu;
                 L.pq[ws][j] = phi_fast(xq);
                 L.dpq[ws][j] = dphi(xq);
                 L.dpk[ws][j] = dphi(xk);
-                yu = fmaf(yj, uhj, yu);
             }
         });
-        yu = wave_sum(yu);
-        if (lane == 0) L.yu[ws] = yu;
+        if (lane == 0) {
+            L.ts[ws][0] = yu;
+            L.ts[ws][1] = ege;
+            L.ts[ws][2] = kal;
+        }
     };
 
     // step 1: A_t gy, Q_t u^, S_t'g, S_t'ge
     auto step1 = [&](int t) {
-        const int v = t & 3, r = t & (RING - 1), s = t % 3;
-        float pp = 0.f, pq = 0.f, p1 = 0.f, p2 = 0.f;
+        const int v = t & 3, r = t & (RING<D> - 1), s = t % 3;
+        float pr[4][RB];
+        sfor<4>([&](auto c) { sfor<RB>([&](auto h) { pr[c][h] = 0.f; }); });
         sfor<EPT>([&](auto e) {
             const int j = c0 + e;
-            pp = fmaf(A[e], L.gy[v][j], pp);
-            pq = fmaf(Q[e], L.uh[v][j], pq);
-            p1 = fmaf(St[e], L.g[r][j], p1);
-            p2 = fmaf(St[e], L.gv[r][j], p2);
+            const float gyj = L.gy[v][j], uhj = L.uh[v][j], gj = L.g[r][j], gvj = L.gv[r][j];
+            sfor<RB>([&](auto h) {
+                pr[0][h] = fmaf(A[h][e], gyj, pr[0][h]);
+                pr[1][h] = fmaf(Q[h][e], uhj, pr[1][h]);
+                pr[2][h] = fmaf(St[h][e], gj, pr[2][h]);
+                pr[3][h] = fmaf(St[h][e], gvj, pr[3][h]);
+            });
         });
-        pp = row_sum<TPR>(pp);
-        pq = row_sum<TPR>(pq);
-        p1 = row_sum<TPR>(p1);
-        p2 = row_sum<TPR>(p2);
+        sfor<4>([&](auto c) { sfor<RB>([&](auto h) { pr[c][h] = row_sum<TPR>(pr[c][h]); }); });
         if (leader) {
-            L.r1[s][0][row] = pp;
-            L.r1[s][1][row] = pq;
-            L.r1[s][2][row] = p1;
-            L.r1[s][3][row] = p2;
+            sfor<4>([&](auto c) { sfor<RB>([&](auto h) { L.r1[s][c][i0 + h] = pr[c][h]; }); });
         }
     };
     // step 2: Q += p y' + y p'; A_{t-1} = A_t + z z'/delta; S_{t-1}' = S_t' - alpha^ e'
     auto step2 = [&](int t) {
-        const int v = t & 3, r = t & (RING - 1), s = t % 3;
+        const int v = t & 3, r = t & (RING<D> - 1), s = t % 3;
         const float id = 1.f / L.sc[r][0];
-        const float pi = L.r1[s][0][row], yi = L.y[v][row], zi = L.z[r][row], ali = L.al[r][row];
+        float pi[RB], yi[RB], zi[RB], ali[RB];
+        sfor<RB>([&](auto h) {
+            pi[h] = L.r1[s][0][i0 + h];
+            yi[h] = L.y[v][i0 + h];
+            zi[h] = L.z[r][i0 + h];
+            ali[h] = L.al[r][i0 + h];
+        });
         sfor<EPT>([&](auto e) {
             const int j = c0 + e;
-            Q[e] = fmaf(pi, L.y[v][j], Q[e]);
-            Q[e] = fmaf(yi, L.r1[s][0][j], Q[e]);
-            A[e] = fmaf(zi * L.z[r][j], id, A[e]);
-            St[e] = fmaf(-ali, L.e[r][j], St[e]);
+            const float yj = L.y[v][j], pj = L.r1[s][0][j], zj = L.z[r][j], ej = L.e[r][j];
+            sfor<RB>([&](auto h) {
+                Q[h][e] = fmaf(pi[h], yj, Q[h][e]);
+                Q[h][e] = fmaf(yi[h], pj, Q[h][e]);
+                A[h][e] = fmaf(zi[h] * zj, id, A[h][e]);
+                St[h][e] = fmaf(-ali[h], ej, St[h][e]);
+            });
         });
     };
-    // gradient wave: token t's du, dq and dk (both chains' shares)
+    // gradient wave: token t's du, dq and dk (both chains' shares).  With
+    // p = A_t gy, w = Q_{t-1} u^ = Q_t u^ + p (y'u^) + y (p'u^) and
+    // gkh = alpha^ (e'ge) - S_t'ge + p, every reduction it needs is one of
+    // p'u^, c1'phi(q), k^'c2, k^'p, u^'Q_t u^ (one round) or a token scalar:
+    //     k^'gkh = (e'ge)(k^'alpha^) - k^'c2 + k^'p,  u^'w = u^'Q_t u^ + 2 (y'u^)(p'u^)
     auto grads = [&](int t) {
-        const int v = t & 3, r = t & (RING - 1), s = t % 3;
+        const int v = t & 3, r = t & (RING<D> - 1), s = t % 3;
         const float dn = L.sc[r][2], iden = 1.f / fmaxf(dn, eps), ik = L.sc[r][3], iu = L.sc[r][4];
-        const float yu = L.yu[v];
-        float s1 = 0.f, a1 = 0.f, a2 = 0.f;
+        const float yu = L.ts[v][0], ege = L.ts[v][1], kal = L.ts[v][2];
+        float s1 = 0.f, a1 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
-                s1 = fmaf(L.r1[s][0][j], L.uh[v][j], s1);   // p'u^
+                const float p = L.r1[s][0][j], uhj = L.uh[v][j], khj = L.kh[v][j];
+                s1 = fmaf(p, uhj, s1);                      // p'u^
                 a1 = fmaf(L.r1[s][2][j], L.pq[v][j], a1);   // g'S_t phi(q)
-                a2 = fmaf(L.e[r][j], L.gv[r][j], a2);       // e'ge
+                b1 = fmaf(khj, L.r1[s][3][j], b1);          // k^'S_t'ge
+                b2 = fmaf(khj, p, b2);                      // k^'p
+                b3 = fmaf(uhj, L.r1[s][1][j], b3);          // u^'Q_t u^
             }
         });
         s1 = wave_sum(s1);
         a1 = wave_sum(a1);
-        a2 = wave_sum(a2);
+        b1 = wave_sum(b1);
+        b2 = wave_sum(b2);
+        b3 = wave_sum(b3);
         const float gden = dn >= eps ? -a1 * iden * iden : 0.f;
-        float wq[NV], gkh[NV], a3 = 0.f, a4 = 0.f;
-        sfor<NV>([&](auto c) {
-            const int j = lane + 64 * c;
-            wq[c] = gkh[c] = 0.f;
-            if (j < D) {
-                const float p = L.r1[s][0][j];
-                // Q_{t-1} u^ = Q_t u^ + p (y'u^) + y (p'u^)
-                wq[c] = fmaf(L.y[v][j], s1, fmaf(p, yu, L.r1[s][1][j]));
-                gkh[c] = fmaf(L.al[r][j], a2, p - L.r1[s][3][j]);
-                a3 = fmaf(L.kh[v][j], gkh[c], a3);
-                a4 = fmaf(L.uh[v][j], wq[c], a4);
-            }
-        });
-        await(t);   // the memory chain's token t is out (returns at once)
-        const float bad = lost ? __builtin_nanf("") : 0.f;
-        a3 = wave_sum(a3);
-        a4 = wave_sum(a4);
+        const float a3 = fmaf(ege, kal, b2 - b1), a4 = fmaf(2.f * yu, s1, b3);
+        const float bad = L.lost ? __builtin_nanf("") : 0.f;
         const size_t o = (tok0 + t) * D;
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
+                const float p = L.r1[s][0][j], khj = L.kh[v][j], uhj = L.uh[v][j];
+                const float wq = fmaf(L.y[v][j], s1, fmaf(p, yu, L.r1[s][1][j]));
+                const float gkh = fmaf(L.al[r][j], ege, p - L.r1[s][3][j]);
                 const float gpq = fmaf(L.r1[s][2][j], iden, gden * L.zt[r][j]);
                 gzk[c] = fmaf(gden, L.pq[v][j], gzk[c]);
                 dq[o + j] = gpq * L.dpq[v][j] + bad;
-                dk[o + j] = fmaf(ik, gkh[c] - L.kh[v][j] * a3, gzk[c] * L.dpk[v][j]) + bad;
-                du[o + j] = -iu * (wq[c] - L.uh[v][j] * a4) + bad;
+                dk[o + j] = fmaf(ik, gkh - khj * a3, gzk[c] * L.dpk[v][j]) + bad;
+                du[o + j] = -iu * (wq - uhj * a4) + bad;
             }
         });
     };
 
+    if (tid == 0) L.lost = 0;
+    __syncthreads();
     for (int i = 0; i < LA && i < T; ++i) issue(T - 1 - i);
     vmem_drain();
     __syncthreads();
@@ -542,15 +599,13 @@ bwd_a(ALds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k,
     // dL/dA_0 = Sigma_0 / 2 = A_0^-1 Q_0 A_0^-1 / 2: here for the default
     // A_0 = I / lambda0; with a given A_0, Q_0 goes to qb for vla_bwd_sandwich
     if (rows && dA0) {
-        const size_t off = bh * DD + (size_t)row * D + c0;
-        const float sc = 0.5f * lambda0 * lambda0;
-        sfor<EPT / 4>([&](auto h) {
-            if (a0given) {
-                st4(qb + off + 4 * h, f4{Q[4 * h], Q[4 * h + 1], Q[4 * h + 2], Q[4 * h + 3]});
-            } else {
-                st4(dA0 + off + 4 * h,
-                    f4{sc * Q[4 * h], sc * Q[4 * h + 1], sc * Q[4 * h + 2], sc * Q[4 * h + 3]});
-            }
+        const float sc = a0given ? 1.f : 0.5f * lambda0 * lambda0;
+        sfor<RB>([&](auto h) {
+            float *dst = (a0given ? qb : dA0) + bh * DD + (size_t)(i0 + h) * D + c0;
+            sfor<EPT / 4>([&](auto q) {
+                st4(dst + 4 * q, f4{sc * Q[h][4 * q], sc * Q[h][4 * q + 1], sc * Q[h][4 * q + 2],
+                                    sc * Q[h][4 * q + 3]});
+            });
         });
     }
 }
