@@ -50,7 +50,8 @@ KERNEL_SOURCES = ["long_context_sequence_amd/csrc/vla_twopass.hip",
                   "long_context_sequence_amd/csrc/vla_chunk_parts.h",
                   "long_context_sequence_amd/csrc/vla_dpp_blocks.h",
                   "long_context_sequence_amd/csrc/vla_common.h",
-                  "long_context_sequence_amd/csrc/vla_record.h"]
+                  "long_context_sequence_amd/csrc/vla_record.h",
+                  "long_context_sequence_amd/csrc/vla_sweep.h"]
 TRAFFIC_SUMMARY = "profiles/vla_forward_b8h16_d64_t4096_bf16.txt"
 # the backward call: the two-pass forward keeping the per-token records, then the
 # reverse sweep (vla_bwd_sync_init, vla_bwd_sweep)

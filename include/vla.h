@@ -233,9 +233,9 @@ vla_status vla_forward_scan_workspace_size(int B, int H, int T, int d_h, size_t 
  * token in the gradient kernel itself.  The reverse recurrence then runs from
  * t = T down to 1 with the states rebuilt from those vectors: for d_h in
  * {64, 96, 128} as two workgroups per head in one launch (the memory chain's
- * adjoint, and the penalty chain's following it through dL/dalpha^ kept in the
- * workspace), for d_h in {16, 32} as one workgroup per head.  Errors as for
- * vla_forward.
+ * adjoint, and the penalty chain's, in the frame A Sigma A of the adjoint Sigma
+ * of A, following it through dL/dalpha^ kept in the workspace and dL/dv), for
+ * d_h in {16, 32} as one workgroup per head.  Errors as for vla_forward.
  */
 vla_status vla_backward(const void *q, const void *k, const void *v, const void *u,
                         vla_dtype in_dtype, int B, int H, int T, int d_h,
@@ -251,9 +251,10 @@ vla_status vla_backward(const void *q, const void *k, const void *v, const void 
  * vla_backward_workspace_size -- bytes of device workspace vla_backward needs:
  * (4 d_h + 8) fp32 values per token of each head, rounded up to 256 bytes,
  * and for d_h in {64, 96, 128} also the two-pass forward's workspace
- * (vla_forward_workspace_size) and the forward's final S, A and zkey
- * ((2 d_h^2 + d_h) fp32 values per head), each rounded up to 256 bytes
- * (0 when T == 0).  Host-only.  Errors: VLA_ERR_INVALID_ARG (NULL bytes, bad
+ * (vla_forward_workspace_size), the forward's final S, A and zkey
+ * ((2 d_h^2 + d_h) fp32 values per head), d_h fp32 values per token of each
+ * head (dL/dalpha^), B H + 1 ints (synchronisation words) and d_h^2 fp32
+ * values per head, each rounded up to 256 bytes (0 when T == 0).  Host-only.  Errors: VLA_ERR_INVALID_ARG (NULL bytes, bad
  * sizes), VLA_ERR_UNSUPPORTED (d_h).
  */
 vla_status vla_backward_workspace_size(int B, int H, int T, int d_h, size_t *bytes);
