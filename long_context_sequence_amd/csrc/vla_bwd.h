@@ -32,7 +32,10 @@ hipError_t launch_backward(const BwdArgs &a);
 // its final state; sync is B H + 1 ints of workspace (role tickets and per-head
 // progress), reset by the launch itself; qb is B H d^2 floats of workspace
 // (Q_T when dL/dA_T is given, Q_0 when A_0 is).
-hipError_t launch_backward_split(const BwdArgs &a, const float *rec, const float *S_T,
+// frec: the forward's per-chunk records (vla_record.h); at d = 64 both chains
+// then go sixteen tokens at a time on the matrix cores; null, or another d,
+// takes the token-by-token chains.
+hipError_t launch_backward_split(const BwdArgs &a, const float *rec, const float *frec, const float *S_T,
                                  const float *A_T, float *galpha, int *sync, float *qb);
 
 // x y + z w with both products rounded before the sum (no fused multiply-add):

@@ -56,6 +56,7 @@
 // runs at the start of the next interval.  Token vectors rotate through three
 // LDS slots and row results through two, so D of token t never races the
 // staging of token t - 2 or the row results of token t - 1.
+
 #include "vla_bwd.h"
 #include "vla_chunk_parts.h"
 #include "vla_record.h"
@@ -611,7 +612,9 @@ hipError_t launch(const BwdArgs &a)
         f.keep = rec;
         const hipError_t e = launch_forward_twopass(f, 3);
         if (e != hipSuccess) return e;
-        return launch_backward_split(a, rec, stS, stA, reinterpret_cast<float *>(ws + p.ga),
+        const float *frec = reinterpret_cast<const float *>(ws + p.fwd + twopass_records_offset(BH, a.T, D));
+        return launch_backward_split(a, rec, frec, stS, stA,
+                                     reinterpret_cast<float *>(ws + p.ga),
                                      reinterpret_cast<int *>(ws + p.sync),
                                      reinterpret_cast<float *>(ws + p.qb));
     } else {

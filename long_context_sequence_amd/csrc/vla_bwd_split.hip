@@ -1,5 +1,8 @@
 // vla_bwd_split.hip -- the reverse sweep of the gradients for d_h in {64, 96, 128}
-// as two chains running side by side, each with one barrier per token.
+// as two chains running side by side: token by token (one barrier per token),
+// or, at d = 64 with the forward's per-chunk records, sixteen tokens per step
+// on the matrix cores (bwd_mc and bwd_pc: each chain's recurrence unrolled over
+// a chunk, so that every product with a d x d state takes sixteen columns).
 //
 // Source: "Variational Linear Attention" (arXiv 2605.11196), section 3.3,
 // Eqs. (9)-(11); the pages print no backward, so this is the chain rule through
@@ -47,6 +50,8 @@
 // interval, while the gradient wave forms token t + 1's gradients (row results
 // in three LDS slots, transformed vectors in four: the gradient's token, the two
 // steps' tokens and the one being transformed).
+#include <type_traits>
+
 #include "vla_bwd.h"
 #include "vla_chunk_parts.h"
 #include "vla_record.h"
@@ -326,6 +331,530 @@ bwd_s(SLds<D> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k, 
             float *dst = dS0 + bh * DD + (size_t)(i0 + h) * D + c0;
             sfor<EPT / 4>([&](auto q) {
                 st4(dst + 4 * q, f4{gS[h][4 * q], gS[h][4 * q + 1], gS[h][4 * q + 2], gS[h][4 * q + 3]});
+            });
+        });
+    }
+}
+
+// ------------------------------------------------ memory chain, chunk by chunk
+// The same adjoint sixteen tokens at a time on the matrix cores.  For the
+// chunk's tokens (columns t, in token order) with dS = G at the chunk's end,
+// the per-token recurrence above unrolls to
+//     GE (I + L) = G Alpha^ + GM U,   L[s][t] = k^_s'alpha^_t (s > t),
+//                                     U[s][t] = phi_s'alpha^_t (s >= t),
+//     GA = G'E + Phi ((GM'E) o [s >= t]) - K^ ((GE'E) o [s > t]),
+//     G <- G + GM Phi' - GE K^'
+// (GM = dL/do / den, columns of Alpha^, K^, Phi, E the chunk's vectors; GE =
+// dL/dv, GA = g_alpha).  L is N' of the forward's (I + N) (N[s][t] =
+// alpha^_s'k^_t, s < t) and U is its P = (Alpha^'Phi) o Up transposed: the
+// forward's chunk record holds both factors already transposed, (I + N)^-1'
+// = (I + L)^-1 and P' = U.
+//
+// Layout: wave w < NB (= D / 16) owns column block w of G and of H = G': tiles
+// X[rho] (rows 16 rho .. 16 rho + 15), register r of lane (n, g) (n = lane &
+// 15, g = lane >> 4) holding X[16 rho + 4 g + r][16 w + n], the accumulator
+// layout of the 16 x 16 x 4 fp32 MFMA.  A tile used as the first operand is
+// its transpose (k = 4 g + r), so G'E and G Alpha^ = H'Alpha^ come from the
+// stored G and H with the chunk's vectors from LDS; the rank-16 updates take
+// both operands from LDS.  The chunk's vectors sit key-major in LDS ([i][t],
+// row stride LS = 20: both operand patterns hit 64 distinct banks).
+constexpr int LS = 20, PUBC = 4;
+
+// one chunk's raw data as copied: the record's Alpha^ .. U' range and its k^,
+// phi(q) range, e and dL/do [token][key], den per token
+template <int D>
+struct MCStage {
+    static constexpr int N1 = 16 * D + 512, N2 = 32 * D;
+    static constexpr int A1 = 0, A2 = A1 + N1, AE = A2 + N2, AO = AE + 16 * D, AN = AO + 16 * D;
+    static constexpr int SIZE = AN + 64;
+    static_assert(N1 % 256 == 0 && N2 % 256 == 0 && 16 * D % 256 == 0, "whole copies");
+};
+
+// (d = 128 keeps the per-token memory chain: its chunk buffers would not fit
+// in LDS next to the rest)
+template <int D> constexpr bool MC_OK = D == 64;
+
+template <int D>
+struct MCLds {
+    float raw[2][MCStage<D>::SIZE];
+    float ah[D][LS], kh[D][LS], ph[D][LS], gm[D][LS], e[D][LS], ge[D][LS];
+    float tt[16][LS], uu[16][LS], u2[16][LS], u3[16][LS];
+    float rhs[D / 16][16][LS];
+};
+
+template <int D, typename Tin>
+__device__ __forceinline__ void
+bwd_mc(MCLds<D> &L, int bh, int T, float eps, const float *__restrict__ dO, const float *dS_T,
+       float *__restrict__ dv, float *dS0, const float *__restrict__ rec, const float *__restrict__ frec,
+       float *__restrict__ galpha, int *progress)
+{
+    using K = rec::Keep<D>;
+    using R = rec::Rec<D>;
+    constexpr int NB = D / 16, RS = K::RS, NT = SplitCfg<D>::NT, G4 = D / 4;
+    const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool mw = w < NB;   // a matrix wave
+    const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
+    const int NC = (T + 15) / 16;
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    f4 G[NB], H[NB];
+    sfor<NB>([&](auto rho) {
+        sfor<4>([&](auto r) {
+            const int i = 16 * rho + 4 * g + r, j = 16 * w + n;
+            G[rho][int(r)] = mw && dS_T ? dS_T[bh * DD + (size_t)i * D + j] : 0.f;
+            H[rho][int(r)] = mw && dS_T ? dS_T[bh * DD + (size_t)j * D + i] : 0.f;
+        });
+    });
+
+    // X[base + n][4 q + g] and X[4 q + g][n] of a [*][LS] array
+    auto at_ng = [&](const float (*X)[LS], int base, int q) { return X[base + n][4 * q + g]; };
+    auto at_gn = [&](const float (*X)[LS], int base, int q) { return X[base + 4 * q + g][n]; };
+
+    // Staging: the two spare waves copy chunk c - 1's raw data straight into
+    // LDS (16 bytes per lane) while chunk c is computed: wave NB the chunk
+    // record's Alpha^ .. U' and k^, phi(q) ranges, wave NB + 1 the 16 tokens' e
+    // (from the per-token records), dL/do and den; at the top of the next
+    // chunk every thread stores them key-major (bytes past a view read as 0).
+    using SL = MCStage<D>;
+    const Buf bk(rec + tok0 * RS, (unsigned)(T * RS * 4));
+    const Buf bo(dO + tok0 * D, (unsigned)(T * D * 4));
+    const Buf bf(frec + (size_t)bh * NC * R::SIZE, (unsigned)(NC * R::SIZE * 4));
+    auto copy = [&](int c) {   // spare waves
+        float *raw = L.raw[c & 1];
+        const int t0 = 16 * c;
+        const unsigned cb = (unsigned)(c * R::SIZE) * 4u + 16u * lane;
+        if (w == NB) {
+            sfor<SL::N1 / 256>([&](auto j) { bf.lds16(raw + SL::A1 + 256 * j, cb + 1024u * j); });
+            sfor<SL::N2 / 256>([&](auto j) {
+                bf.lds16(raw + SL::A2 + 256 * j, cb + 4u * R::KH + 1024u * j);
+            });
+        } else if (w == NB + 1) {
+            sfor<16 * D / 256>([&](auto j) {
+                const int f = 256 * j + 4 * lane, t = f / D, col = f % D;
+                bk.lds16(raw + SL::AE + 256 * j, 4u * (unsigned)((t0 + t) * RS + K::E + col));
+                bo.lds16(raw + SL::AO + 256 * j, 4u * (unsigned)((t0 + t) * D + col));
+            });
+            bk.lds4(raw + SL::AN, 4u * (unsigned)((t0 + (lane & 15)) * RS + K::SC + 2) +
+                                      (lane < 16 ? 0u : 0x40000000u));
+        }
+    };
+    auto copies_done = [&]() {   // spare waves: this chunk's copies have landed
+        if (w == NB) vm_wait<0>();
+        if (w == NB + 1) vm_wait<0>();
+    };
+    auto stage = [&](int c) {
+        const float *raw = L.raw[c & 1];
+        const int t0 = 16 * c;
+        for (int x = tid; x < 16 * G4; x += NT) {   // token-major vectors, key-major in LDS
+            const int t = x / G4, c4 = x % G4;
+            const bool ok = t0 + t < T;
+            const float id = ok ? 1.f / fmaxf(raw[SL::AN + t], eps) : 0.f;
+            const f4 kh = ld4(raw + SL::A2 + swzd<D>(t, c4));
+            const f4 ph = ld4(raw + SL::A2 + 16 * D + swzd<D>(t, c4));
+            const f4 ee = ld4(raw + SL::AE + t * D + 4 * c4);
+            const f4 go = ld4(raw + SL::AO + t * D + 4 * c4);
+            sfor<4>([&](auto r) {
+                const int i = 4 * c4 + r;
+                L.kh[i][t] = ok ? kh[int(r)] : 0.f;
+                L.ph[i][t] = ok ? ph[int(r)] : 0.f;
+                L.e[i][t] = ee[int(r)];
+                L.gm[i][t] = go[int(r)] * id;
+            });
+        }
+        for (int x = tid; x < 4 * D; x += NT) {   // alpha^ [key][token]
+            const int i = x >> 2, c4 = x & 3;
+            const f4 a = ld4(raw + SL::A1 + swz16(i, c4));
+            sfor<4>([&](auto r) { L.ah[i][4 * c4 + r] = t0 + 4 * c4 + r < T ? a[int(r)] : 0.f; });
+        }
+        if (tid < 128) {   // (I + L)^-1, U (identity, 0 past T)
+            const int m = tid >> 6, i = (tid >> 2) & 15, c4 = tid & 3;
+            const f4 a = ld4(raw + SL::A1 + (m ? R::PT : R::TT) + swz16(i, c4));
+            float(*dst)[LS] = m ? L.uu : L.tt;
+            sfor<4>([&](auto r) {
+                const int j = 4 * c4 + r;
+                dst[i][j] = t0 + i < T && t0 + j < T ? a[int(r)] : (m == 0 && i == j ? 1.f : 0.f);
+            });
+        }
+    };
+
+    if (NC > 0) copy(NC - 1);
+    for (int c = NC - 1; c >= 0; --c) {
+        const int t0 = 16 * c;
+        copies_done();
+        lds_barrier();
+        stage(c);
+        lds_barrier();
+        if (c > 0) copy(c - 1);
+        // ---- GE = (G Alpha^ + GM U)(I + L)^-1 on the matrix waves; U2 on the next
+        f4 x2 = zero;
+        if (mw) {
+            f4 x1 = zero;
+            sfor<NB>([&](auto rho) {
+                sfor<4>([&](auto r) {
+                    x1 = mma(H[rho][int(r)], L.ah[16 * rho + 4 * g + r][n], x1);
+                    x2 = mma(G[rho][int(r)], L.e[16 * rho + 4 * g + r][n], x2);
+                });
+            });
+            sfor<4>([&](auto q) { x1 = mma(at_ng(L.gm, 16 * w, q), at_gn(L.uu, 0, q), x1); });
+            sfor<4>([&](auto r) { L.rhs[w][4 * g + r][n] = x1[int(r)]; });
+            wave_lds_order();
+            f4 ge = zero;
+            sfor<4>([&](auto q) { ge = mma(at_ng(L.rhs[w], 0, q), at_gn(L.tt, 0, q), ge); });
+            sfor<4>([&](auto r) { L.ge[16 * w + 4 * g + r][n] = ge[int(r)]; });
+            if (t0 + n < T) st4(dv + (tok0 + t0 + n) * D + 16 * w + 4 * g, ge);
+        } else if (w == NB) {   // U2 = (GM'E) o [s >= t]
+            f4 u2 = zero;
+            sfor<G4>([&](auto q) { u2 = mma(at_gn(L.gm, 0, q), at_gn(L.e, 0, q), u2); });
+            sfor<4>([&](auto r) { L.u2[4 * g + r][n] = 4 * g + r >= n ? u2[int(r)] : 0.f; });
+        }
+        lds_barrier();
+        if (mw) {   // the updates' GM and Phi terms
+            sfor<NB>([&](auto rho) {
+                sfor<4>([&](auto q) {
+                    G[rho] = mma(at_ng(L.gm, 16 * rho, q), at_ng(L.ph, 16 * w, q), G[rho]);
+                    H[rho] = mma(at_ng(L.ph, 16 * rho, q), at_ng(L.gm, 16 * w, q), H[rho]);
+                });
+            });
+        } else if (w == NB) {   // U3 = (GE'E) o [s > t]
+            f4 u3 = zero;
+            sfor<G4>([&](auto q) { u3 = mma(at_gn(L.ge, 0, q), at_gn(L.e, 0, q), u3); });
+            sfor<4>([&](auto r) { L.u3[4 * g + r][n] = 4 * g + r > n ? u3[int(r)] : 0.f; });
+        }
+        lds_barrier();
+        if (mw) {   // GA, then the updates' GE and K^ terms
+            sfor<4>([&](auto q) {
+                x2 = mma(at_ng(L.ph, 16 * w, q), at_gn(L.u2, 0, q), x2);
+                x2 = mma(-at_ng(L.kh, 16 * w, q), at_gn(L.u3, 0, q), x2);
+            });
+            if (t0 + n < T) st4(galpha + (tok0 + t0 + n) * D + 16 * w + 4 * g, x2);
+            sfor<NB>([&](auto rho) {
+                sfor<4>([&](auto q) {
+                    G[rho] = mma(at_ng(L.ge, 16 * rho, q), -at_ng(L.kh, 16 * w, q), G[rho]);
+                    H[rho] = mma(at_ng(L.kh, 16 * rho, q), -at_ng(L.ge, 16 * w, q), H[rho]);
+                });
+            });
+        }
+        // every PUBC chunks (and at the end): tokens >= t0 are out (dv and
+        // g_alpha written); each matrix wave waits for its stores, then one
+        // release (it writes the L2 back, thousands of cycles) and publish t0
+        if (c % PUBC == 0) {
+            if (mw) vmem_drain();
+            lds_barrier();
+            if (tid == 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __hip_atomic_store(progress + bh, t0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+
+    if (mw && dS0) {
+        sfor<NB>([&](auto rho) {
+            sfor<4>([&](auto r) {
+                dS0[bh * DD + (size_t)(16 * rho + 4 * g + r) * D + 16 * w + n] = G[rho][int(r)];
+            });
+        });
+    }
+}
+
+// ----------------------------------------------- penalty chain, chunk by chunk
+// The conjugated penalty adjoint and the S' products sixteen tokens at a time.
+// With A, Q = A Sigma A and S at the chunk's end (after its last token) and
+// the chunk's columns GY, Y, U^, Z, E, G (= dL/do), GE (= dL/dv), Alpha^:
+//     P  = A GY + Z ((Z'GY) o [s > t] / delta_s)          (p_t = A_t gy_t)
+//     W  = Q U^ + P ((Y'U^) o [s >= t]) + Y ((P'U^) o [s >= t])   (Q_{t-1} u^_t)
+//     C1 = S'G - Alpha^ ((E'G) o [s > t]),  C2 = S'GE - Alpha^ ((E'GE) o [s > t])
+//     Q += P Y' + Y P',  A += Z diag(1/delta) Z',  S -= E Alpha^'
+// (the per-token recurrence unrolled over the chunk; row s, column t of the
+// 16 x 16 factors).  Layout as in the memory chain: wave w < NB owns column
+// block w of A, Q and S; the spare waves copy the next chunk and form the five
+// 16 x 16 factors; then every thread forms the chunk's gradients, sixteen
+// lanes per token (DPP sums over them), four keys each.
+template <int D, typename Tin>
+struct PCStage {
+    static constexpr int NIN = 16 * D * (int)sizeof(Tin) / 4;          // one input, 16 tokens
+    static constexpr int NK = (16 * (4 * D + 8) + 255) / 256 * 256;    // 16 per-token records
+    static constexpr int AK = 0, AGA = AK + NK, AGE = AGA + 16 * D, AO = AGE + 16 * D;
+    static constexpr int AQ = AO + 16 * D, AKK = AQ + NIN, AU = AKK + NIN, SIZE = AU + NIN;
+    static_assert(NIN % 256 == 0 && 16 * D % 256 == 0, "whole copies");
+};
+
+// The arrays the products read come first, inside the 64 KB that one address
+// register and the instructions' offset field reach; C1, C2 and W take the
+// places of G, GY and Z, which are dead by the time they are written.
+template <int D, typename Tin>
+struct PCLds {
+    float ge[D][LS], ah[D][LS], y[D][LS], uh[D][LS], e[D][LS], p[D][LS];
+    union { float gm[D][LS]; float c1[D][LS]; };
+    union { float gy[D][LS]; float c2[D][LS]; };
+    union { float z[D][LS]; float w[D][LS]; };
+    float v1[16][LS], v2[16][LS], v3[16][LS], v4[16][LS], v5[16][LS];
+    float phi[16][D];
+    float idl[16], gden[16];
+    float gzk[2][D];   // the key-sum adjoint carried from the later chunks
+    int lost;
+    float raw[2][PCStage<D, Tin>::SIZE];
+};
+
+template <int D, typename Tin>
+__device__ __forceinline__ void
+bwd_pc(PCLds<D, Tin> &L, int bh, const Tin *__restrict__ q, const Tin *__restrict__ k,
+       const Tin *__restrict__ u, int T, float lambda0, float eps, const float *__restrict__ S_T,
+       const float *__restrict__ A_T, const float *__restrict__ dO, const float *dzk_T,
+       float *__restrict__ dq, float *__restrict__ dk, const float *__restrict__ dv,
+       float *__restrict__ du, bool qin, float *qb, float *dA0, bool a0given, float *dzk0,
+       const float *__restrict__ rec, const float *__restrict__ galpha, const int *progress)
+{
+    static_assert(D == 64, "sixteen lanes of four keys per token");
+    using K = rec::Keep<D>;
+    using SL = PCStage<D, Tin>;
+    constexpr int NB = D / 16, RS = K::RS;
+    static_assert(SplitCfg<D>::NT == 64 * (NB + 2), "four matrix waves and two copy waves");
+    const int tid = threadIdx.x, lane = tid & 63, n = lane & 15, g = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool mw = w < NB;
+    const size_t DD = (size_t)D * D, tok0 = (size_t)bh * T;
+    const int NC = (T + 15) / 16;
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    f4 A[NB], Q[NB], S[NB];
+    sfor<NB>([&](auto rho) {
+        sfor<4>([&](auto r) {
+            const size_t off = bh * DD + (size_t)(16 * rho + 4 * g + r) * D + 16 * w + n;
+            A[rho][int(r)] = mw ? A_T[off] : 0.f;
+            Q[rho][int(r)] = mw && qin ? qb[off] : 0.f;
+            S[rho][int(r)] = mw ? S_T[off] : 0.f;
+        });
+    });
+    // chunk c reads the carry from gzk[c & 1] and leaves it in gzk[(c + 1) & 1],
+    // so the first read is gzk[(NC - 1) & 1] and the last write is gzk[1]
+    if (tid < D) L.gzk[(NC - 1) & 1][tid] = dzk_T ? dzk_T[(size_t)bh * D + tid] : 0.f;
+    if (tid == 0) L.lost = 0;
+    lds_barrier();
+
+    auto at_ng = [&](const float (*X)[LS], int base, int qq) { return X[base + n][4 * qq + g]; };
+    auto at_gn = [&](const float (*X)[LS], int base, int qq) { return X[base + 4 * qq + g][n]; };
+
+    // As in the memory chain's adjoint: a copy gives up after SPIN_LIMIT polls
+    // and the head's gradients become NaN.
+    int seen = T;
+    bool lost = false;
+    auto await = [&](int x) {
+        for (int it = 0; seen > x && !lost; ++it) {
+            seen = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(progress + bh, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT));
+            if (seen > x) {
+                if (it >= SPIN_LIMIT) lost = true;
+                __builtin_amdgcn_s_sleep(4);
+            }
+        }
+    };
+    const Buf bk(rec + tok0 * RS, (unsigned)(T * RS * 4));
+    const Buf ba(galpha + tok0 * D, (unsigned)(T * D * 4));
+    const Buf bv(dv + tok0 * D, (unsigned)(T * D * 4));
+    const Buf bo(dO + tok0 * D, (unsigned)(T * D * 4));
+    const unsigned ib = (unsigned)(T * D * sizeof(Tin));
+    const Buf bq(q + tok0 * D, ib), bkk(k + tok0 * D, ib), bu(u + tok0 * D, ib);
+    auto copy = [&](int c) {   // spare waves
+        float *raw = L.raw[c & 1];
+        const int t0 = 16 * c;
+        const unsigned lo = 16u * lane;
+        if (w == NB) {
+            sfor<SL::NK / 256>([&](auto j) { bk.lds16(raw + SL::AK + 256 * j, 4u * t0 * RS + lo + 1024u * j); });
+            await(t0);   // g_alpha and dL/dv of the chunk are out
+            if (lost && lane == 0) L.lost = 1;
+            sfor<16 * D / 256>([&](auto j) {
+                ba.lds16(raw + SL::AGA + 256 * j, 4u * t0 * D + lo + 1024u * j);
+                bv.lds16(raw + SL::AGE + 256 * j, 4u * t0 * D + lo + 1024u * j);
+            });
+        } else if (w == NB + 1) {
+            const unsigned ti = (unsigned)(t0 * D * sizeof(Tin));
+            sfor<16 * D / 256>([&](auto j) { bo.lds16(raw + SL::AO + 256 * j, 4u * t0 * D + lo + 1024u * j); });
+            sfor<SL::NIN / 256>([&](auto j) {
+                bq.lds16(raw + SL::AQ + 256 * j, ti + lo + 1024u * j);
+                bkk.lds16(raw + SL::AKK + 256 * j, ti + lo + 1024u * j);
+                bu.lds16(raw + SL::AU + 256 * j, ti + lo + 1024u * j);
+            });
+        }
+    };
+    auto inp = [&](const float *raw, int off, int idx) { return raw_get<Tin>(raw + off, idx); };
+    // token t, keys [4j, 4j + 4) of this thread (tid < 256)
+    const int tt = tid >> 4, jj = tid & 15;
+    auto stage = [&](int c) {
+        if (tid >= 256) return;
+        const float *raw = L.raw[c & 1];
+        const int t0 = 16 * c;
+        const bool ok = t0 + tt < T;
+        const float *kr = raw + SL::AK + tt * RS;
+        const float iy = kr[K::SC + 1], iu = kr[K::SC + 4], dl = kr[K::SC + 0];
+        const f4 al = ld4(kr + K::AL + 4 * jj), zz = ld4(kr + K::Z + 4 * jj), ee = ld4(kr + K::E + 4 * jj);
+        const f4 ga = ld4(raw + SL::AGA + tt * D + 4 * jj), ge = ld4(raw + SL::AGE + tt * D + 4 * jj);
+        const f4 go = ld4(raw + SL::AO + tt * D + 4 * jj);
+        float aga = 0.f;
+        sfor<4>([&](auto r) { aga = fmaf(al[int(r)], ga[int(r)], aga); });
+        aga = row_sum<16>(aga);
+        const float ny = iy > 0.f ? 1.f / iy : 0.f;
+        sfor<4>([&](auto r) {
+            const int i = 4 * jj + r;
+            const float xq = inp(raw, SL::AQ, tt * D + i), xu = inp(raw, SL::AU, tt * D + i);
+            L.ge[i][tt] = ok ? ge[int(r)] : 0.f;
+            L.ah[i][tt] = ok ? al[int(r)] : 0.f;
+            L.gy[i][tt] = ok ? (ga[int(r)] - al[int(r)] * aga) * iy : 0.f;
+            L.y[i][tt] = ok ? al[int(r)] * ny : 0.f;
+            L.uh[i][tt] = ok ? xu * iu : 0.f;
+            L.z[i][tt] = ok ? zz[int(r)] : 0.f;
+            L.e[i][tt] = ok ? ee[int(r)] : 0.f;
+            L.gm[i][tt] = ok ? go[int(r)] : 0.f;
+            L.phi[tt][i] = ok ? phi_fast(xq) : 0.f;
+        });
+        if (jj == 0) L.idl[tt] = ok ? 1.f / dl : 0.f;
+    };
+
+    if (NC > 0 && w >= NB) copy(NC - 1);
+    for (int c = NC - 1; c >= 0; --c) {
+        const int t0 = 16 * c;
+        if (w >= NB) vm_wait<0>();   // this chunk's copies have landed
+        lds_barrier();
+        stage(c);
+        lds_barrier();
+        if (c > 0 && w >= NB) copy(c - 1);
+        // ---- products with the state at the chunk's end; the factors
+        f4 x3 = zero, x4 = zero, x5 = zero, x6 = zero;
+        if (mw) {
+            sfor<NB>([&](auto rho) {
+                sfor<4>([&](auto r) {
+                    const int i = 16 * rho + 4 * g + r;
+                    x3 = mma(A[rho][int(r)], L.gy[i][n], x3);
+                    x4 = mma(Q[rho][int(r)], L.uh[i][n], x4);
+                    x5 = mma(S[rho][int(r)], L.gm[i][n], x5);
+                    x6 = mma(S[rho][int(r)], L.ge[i][n], x6);
+                });
+            });
+        } else if (w == NB) {   // V1 = (Z'GY) o [s > t] / delta_s, V2 = (Y'U^) o [s >= t]
+            f4 v1 = zero, v2 = zero;
+            sfor<D / 4>([&](auto qq) {
+                v1 = mma(at_gn(L.z, 0, qq), at_gn(L.gy, 0, qq), v1);
+                v2 = mma(at_gn(L.y, 0, qq), at_gn(L.uh, 0, qq), v2);
+            });
+            sfor<4>([&](auto r) {
+                const int s = 4 * g + r;
+                L.v1[s][n] = s > n ? v1[int(r)] * L.idl[s] : 0.f;
+                L.v2[s][n] = s >= n ? v2[int(r)] : 0.f;
+            });
+        } else if (w == NB + 1) {   // V4 = (E'G) o [s > t], V5 = (E'GE) o [s > t]
+            f4 v4 = zero, v5 = zero;
+            sfor<D / 4>([&](auto qq) {
+                v4 = mma(at_gn(L.e, 0, qq), at_gn(L.gm, 0, qq), v4);
+                v5 = mma(at_gn(L.e, 0, qq), at_gn(L.ge, 0, qq), v5);
+            });
+            sfor<4>([&](auto r) {
+                const int s = 4 * g + r;
+                L.v4[s][n] = s > n ? v4[int(r)] : 0.f;
+                L.v5[s][n] = s > n ? v5[int(r)] : 0.f;
+            });
+        }
+        lds_barrier();
+        if (mw) {   // P, C1, C2
+            sfor<4>([&](auto qq) {
+                x3 = mma(at_ng(L.z, 16 * w, qq), at_gn(L.v1, 0, qq), x3);
+                x5 = mma(-at_ng(L.ah, 16 * w, qq), at_gn(L.v4, 0, qq), x5);
+                x6 = mma(-at_ng(L.ah, 16 * w, qq), at_gn(L.v5, 0, qq), x6);
+            });
+            sfor<4>([&](auto r) {
+                const int i = 16 * w + 4 * g + r;
+                L.p[i][n] = x3[int(r)];
+                L.c1[i][n] = x5[int(r)];
+                L.c2[i][n] = x6[int(r)];
+            });
+        }
+        lds_barrier();
+        if (mw) {   // Q += P Y' + Y P', A += Z diag(1/delta) Z', S -= E Alpha^'
+            sfor<NB>([&](auto rho) {
+                sfor<4>([&](auto qq) {
+                    Q[rho] = mma(at_ng(L.p, 16 * rho, qq), at_ng(L.y, 16 * w, qq), Q[rho]);
+                    Q[rho] = mma(at_ng(L.y, 16 * rho, qq), at_ng(L.p, 16 * w, qq), Q[rho]);
+                    A[rho] = mma(at_ng(L.z, 16 * rho, qq) * L.idl[4 * qq + g], at_ng(L.z, 16 * w, qq), A[rho]);
+                    S[rho] = mma(-at_ng(L.e, 16 * rho, qq), at_ng(L.ah, 16 * w, qq), S[rho]);
+                });
+            });
+        } else if (w == NB) {   // V3 = (P'U^) o [s >= t]
+            f4 v3 = zero;
+            sfor<D / 4>([&](auto qq) { v3 = mma(at_gn(L.p, 0, qq), at_gn(L.uh, 0, qq), v3); });
+            sfor<4>([&](auto r) { L.v3[4 * g + r][n] = 4 * g + r >= n ? v3[int(r)] : 0.f; });
+        }
+        lds_barrier();
+        if (mw) {   // W = Q U^ + P V2 + Y V3
+            sfor<4>([&](auto qq) {
+                x4 = mma(at_ng(L.p, 16 * w, qq), at_gn(L.v2, 0, qq), x4);
+                x4 = mma(at_ng(L.y, 16 * w, qq), at_gn(L.v3, 0, qq), x4);
+            });
+            sfor<4>([&](auto r) { L.w[16 * w + 4 * g + r][n] = x4[int(r)]; });
+        }
+        // ---- the chunk's gradients: sixteen lanes per token, four keys each
+        const float *raw = L.raw[c & 1];
+        const float *kr = raw + SL::AK + tt * RS;
+        const bool ok = tid < 256 && t0 + tt < T;
+        const float dn = kr[K::SC + 2], iden = 1.f / fmaxf(dn, eps), ik = kr[K::SC + 3], iu = kr[K::SC + 4];
+        if (tid < 256) {
+            float a1 = 0.f;
+            sfor<4>([&](auto r) { a1 = fmaf(L.c1[4 * jj + r][tt], L.phi[tt][4 * jj + r], a1); });
+            a1 = row_sum<16>(a1);
+            if (jj == 0) L.gden[tt] = ok && dn >= eps ? -a1 * iden * iden : 0.f;
+        }
+        lds_barrier();
+        if (tid < 256) {
+            const float gden = L.gden[tt], bad = L.lost ? __builtin_nanf("") : 0.f;
+            const float *carry = L.gzk[c & 1];
+            const f4 al = ld4(kr + K::AL + 4 * jj), ee = ld4(kr + K::E + 4 * jj), zk = ld4(kr + K::ZK + 4 * jj);
+            float gz[4], c1v[4], gkh[4], kh[4], uhv[4], wv[4], a2 = 0.f, a3 = 0.f, a4 = 0.f;
+            sfor<4>([&](auto r) {
+                const int i = 4 * jj + r;
+                float acc = carry[i];
+                for (int s2 = tt; s2 < 16; ++s2) acc = fmaf(L.gden[s2], L.phi[s2][i], acc);
+                gz[r] = acc;
+                c1v[r] = L.c1[i][tt];
+                kh[r] = inp(raw, SL::AKK, tt * D + i) * ik;
+                uhv[r] = L.uh[i][tt];
+                wv[r] = L.w[i][tt];
+                a2 = fmaf(ee[int(r)], L.ge[i][tt], a2);
+                a4 = fmaf(uhv[r], wv[r], a4);
+            });
+            a2 = row_sum<16>(a2);
+            sfor<4>([&](auto r) {
+                const int i = 4 * jj + r;
+                gkh[r] = fmaf(al[int(r)], a2, L.p[i][tt] - L.c2[i][tt]);
+                a3 = fmaf(kh[r], gkh[r], a3);
+            });
+            a3 = row_sum<16>(a3);
+            a4 = row_sum<16>(a4);
+            if (tt == 0) sfor<4>([&](auto r) { L.gzk[(c + 1) & 1][4 * jj + r] = gz[r]; });
+            if (ok) {
+                f4 oq, ok4, ou;
+                sfor<4>([&](auto r) {
+                    const int i = 4 * jj + r;
+                    const float xq = inp(raw, SL::AQ, tt * D + i), xk = inp(raw, SL::AKK, tt * D + i);
+                    oq[int(r)] = fmaf(c1v[r], iden, gden * zk[int(r)]) * dphi(xq) + bad;
+                    ok4[int(r)] = fmaf(ik, gkh[r] - kh[r] * a3, gz[r] * dphi(xk)) + bad;
+                    ou[int(r)] = -iu * (wv[r] - uhv[r] * a4) + bad;
+                });
+                const size_t o = (tok0 + t0 + tt) * D + 4 * jj;
+                st4(dq + o, oq);
+                st4(dk + o, ok4);
+                st4(du + o, ou);
+            }
+        }
+    }
+
+    lds_barrier();
+    if (dzk0 && tid < D) dzk0[(size_t)bh * D + tid] = L.gzk[1][tid];
+    // dL/dA_0 = A_0^-1 Q_0 A_0^-1 / 2: here for the default A_0 = I / lambda0;
+    // with a given A_0, Q_0 goes to qb for vla_bwd_sandwich
+    if (mw && dA0) {
+        const float sc = a0given ? 1.f : 0.5f * lambda0 * lambda0;
+        float *dst = a0given ? qb : dA0;
+        sfor<NB>([&](auto rho) {
+            sfor<4>([&](auto r) {
+                dst[bh * DD + (size_t)(16 * rho + 4 * g + r) * D + 16 * w + n] = sc * Q[rho][int(r)];
             });
         });
     }
@@ -628,16 +1157,30 @@ vla_bwd_sweep(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *_
               const float *__restrict__ dO, const float *dS_T, const float *dzk_T,
               float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
               float *__restrict__ du, float *dS0, float *dA0, float *dzk0, bool qin, bool a0given,
-              float *qb, const float *__restrict__ rec, float *__restrict__ galpha, int *sync, int BH)
+              float *qb, const float *__restrict__ rec, const float *__restrict__ frec,
+              float *__restrict__ galpha, int *sync, int BH)
 {
     __shared__ __align__(16) union {
         SLds<D> s;
+        std::conditional_t<MC_OK<D>, MCLds<D>, char[16]> m;
+        std::conditional_t<MC_OK<D>, PCLds<D, Tin>, char[16]> pc;
         ALds<D> a;
     } L;
     __shared__ int ticket;
     if (threadIdx.x == 0) ticket = __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const int tk = ticket;
+    if constexpr (MC_OK<D>) {
+        if (tk < BH && frec) {
+            bwd_mc<D, Tin>(L.m, tk, T, eps, dO, dS_T, dv, dS0, rec, frec, galpha, sync + 1);
+            return;
+        }
+        if (frec) {
+            bwd_pc<D, Tin>(L.pc, tk - BH, q, k, u, T, lambda0, eps, S_T, A_T, dO, dzk_T, dq, dk, dv, du, qin,
+                           qb, dA0, a0given, dzk0, rec, galpha, sync + 1);
+            return;
+        }
+    }
     if (tk < BH)
         bwd_s<D, Tin>(L.s, tk, q, k, T, eps, dO, dS_T, dv, dS0, rec, galpha, sync + 1);
     else
@@ -712,8 +1255,8 @@ hipError_t sandwich(int mode, int BH, const float *lmat, const float *dA_T, floa
 }
 
 template <int D, typename Tin>
-hipError_t launch(const BwdArgs &a, const float *rec, const float *S_T, const float *A_T, float *galpha,
-                  int *sync, float *qb)
+hipError_t launch(const BwdArgs &a, const float *rec, const float *frec, const float *S_T, const float *A_T,
+                  float *galpha, int *sync, float *qb)
 {
     const int BH = a.B * a.H;
     const bool qin = a.dA_T != nullptr, a0given = a.A0 != nullptr && a.dA0 != nullptr;
@@ -724,7 +1267,7 @@ hipError_t launch(const BwdArgs &a, const float *rec, const float *S_T, const fl
     hipLaunchKernelGGL((vla_bwd_sweep<D, Tin>), dim3(2 * BH), dim3(SplitCfg<D>::NT), 0, a.stream,
                        (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.u, a.T, a.lambda0, a.eps, S_T,
                        A_T, a.dO, a.dS_T, a.dzk_T, a.dq, a.dk, a.dv, a.du, a.dS0, a.dA0, a.dzk0, qin,
-                       a0given, qb, rec, galpha, sync, BH);
+                       a0given, qb, rec, frec, galpha, sync, BH);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a0given) return sandwich<D>(1, BH, a.A0, nullptr, qb, a.dA0, a.stream);
     return hipSuccess;
@@ -732,17 +1275,17 @@ hipError_t launch(const BwdArgs &a, const float *rec, const float *S_T, const fl
 
 }  // namespace
 
-hipError_t launch_backward_split(const BwdArgs &a, const float *rec, const float *S_T,
+hipError_t launch_backward_split(const BwdArgs &a, const float *rec, const float *frec, const float *S_T,
                                  const float *A_T, float *galpha, int *sync, float *qb)
 {
     const bool bf = a.dtype == 1;
     switch (a.d) {
-    case 64: return bf ? launch<64, uint16_t>(a, rec, S_T, A_T, galpha, sync, qb)
-                       : launch<64, float>(a, rec, S_T, A_T, galpha, sync, qb);
-    case 96: return bf ? launch<96, uint16_t>(a, rec, S_T, A_T, galpha, sync, qb)
-                       : launch<96, float>(a, rec, S_T, A_T, galpha, sync, qb);
-    case 128: return bf ? launch<128, uint16_t>(a, rec, S_T, A_T, galpha, sync, qb)
-                        : launch<128, float>(a, rec, S_T, A_T, galpha, sync, qb);
+    case 64: return bf ? launch<64, uint16_t>(a, rec, frec, S_T, A_T, galpha, sync, qb)
+                       : launch<64, float>(a, rec, frec, S_T, A_T, galpha, sync, qb);
+    case 96: return bf ? launch<96, uint16_t>(a, rec, frec, S_T, A_T, galpha, sync, qb)
+                       : launch<96, float>(a, rec, frec, S_T, A_T, galpha, sync, qb);
+    case 128: return bf ? launch<128, uint16_t>(a, rec, frec, S_T, A_T, galpha, sync, qb)
+                        : launch<128, float>(a, rec, frec, S_T, A_T, galpha, sync, qb);
     default: return hipErrorInvalidValue;
     }
 }
