@@ -581,15 +581,16 @@ struct PCStage {
 
 // The arrays the products read come first, inside the 64 KB that one address
 // register and the instructions' offset field reach; C1, C2 and W take the
-// places of G, GY and Z, which are dead by the time they are written.
+// places of G, GY and Z, and GZ (dL/dphi(k) per key and token) that of E,
+// which are dead by the time they are written.
 template <int D, typename Tin>
 struct PCLds {
-    float ge[D][LS], ah[D][LS], y[D][LS], uh[D][LS], e[D][LS], p[D][LS];
+    float ge[D][LS], ah[D][LS], y[D][LS], uh[D][LS], p[D][LS], phi[D][LS];
     union { float gm[D][LS]; float c1[D][LS]; };
     union { float gy[D][LS]; float c2[D][LS]; };
     union { float z[D][LS]; float w[D][LS]; };
+    union { float e[D][LS]; float gz[D][LS]; };
     float v1[16][LS], v2[16][LS], v3[16][LS], v4[16][LS], v5[16][LS];
-    float phi[16][D];
     float idl[16], gden[16];
     float gzk[2][D];   // the key-sum adjoint carried from the later chunks
     int lost;
@@ -705,7 +706,7 @@ bwd_pc(PCLds<D, Tin> &L, int bh, const Tin *__restrict__ q, const Tin *__restric
             L.z[i][tt] = ok ? zz[int(r)] : 0.f;
             L.e[i][tt] = ok ? ee[int(r)] : 0.f;
             L.gm[i][tt] = ok ? go[int(r)] : 0.f;
-            L.phi[tt][i] = ok ? phi_fast(xq) : 0.f;
+            L.phi[i][tt] = ok ? phi_fast(xq) : 0.f;
         });
         if (jj == 0) L.idl[tt] = ok ? 1.f / dl : 0.f;
     };
@@ -781,37 +782,48 @@ bwd_pc(PCLds<D, Tin> &L, int bh, const Tin *__restrict__ q, const Tin *__restric
             f4 v3 = zero;
             sfor<D / 4>([&](auto qq) { v3 = mma(at_gn(L.p, 0, qq), at_gn(L.uh, 0, qq), v3); });
             sfor<4>([&](auto r) { L.v3[4 * g + r][n] = 4 * g + r >= n ? v3[int(r)] : 0.f; });
+        } else {   // dL/dden_t = -(c1_t'phi(q_t)) / den_t^2 (lane: token n, keys 16 g + [0, 16))
+            const float *kn = L.raw[c & 1] + SL::AK + n * RS;
+            float a1 = 0.f;
+            sfor<16>([&](auto x) {
+                const int i = 16 * g + ((x + 4 * g) & 15);
+                a1 = fmaf(L.c1[i][n], L.phi[i][n], a1);
+            });
+            a1 += __shfl_xor(a1, 16);
+            a1 += __shfl_xor(a1, 32);
+            const float dn = kn[K::SC + 2], id = 1.f / fmaxf(dn, eps);
+            if (g == 0) L.gden[n] = t0 + n < T && dn >= eps ? -a1 * id * id : 0.f;
         }
         lds_barrier();
-        if (mw) {   // W = Q U^ + P V2 + Y V3
+        if (mw) {   // W = Q U^ + P V2 + Y V3; GZ = carry + Phi' ((gden_s) o [s >= t])
+            f4 gzt;
+            sfor<4>([&](auto r) { gzt[int(r)] = L.gzk[c & 1][16 * w + 4 * g + r]; });
             sfor<4>([&](auto qq) {
                 x4 = mma(at_ng(L.p, 16 * w, qq), at_gn(L.v2, 0, qq), x4);
                 x4 = mma(at_ng(L.y, 16 * w, qq), at_gn(L.v3, 0, qq), x4);
+                const int s = 4 * qq + g;
+                gzt = mma(at_ng(L.phi, 16 * w, qq), s >= n ? L.gden[s] : 0.f, gzt);
             });
-            sfor<4>([&](auto r) { L.w[16 * w + 4 * g + r][n] = x4[int(r)]; });
+            sfor<4>([&](auto r) {
+                const int i = 16 * w + 4 * g + r;
+                L.w[i][n] = x4[int(r)];
+                L.gz[i][n] = gzt[int(r)];
+                if (n == 0) L.gzk[(c + 1) & 1][i] = gzt[int(r)];
+            });
         }
+        lds_barrier();
         // ---- the chunk's gradients: sixteen lanes per token, four keys each
         const float *raw = L.raw[c & 1];
         const float *kr = raw + SL::AK + tt * RS;
         const bool ok = tid < 256 && t0 + tt < T;
-        const float dn = kr[K::SC + 2], iden = 1.f / fmaxf(dn, eps), ik = kr[K::SC + 3], iu = kr[K::SC + 4];
-        if (tid < 256) {
-            float a1 = 0.f;
-            sfor<4>([&](auto r) { a1 = fmaf(L.c1[4 * jj + r][tt], L.phi[tt][4 * jj + r], a1); });
-            a1 = row_sum<16>(a1);
-            if (jj == 0) L.gden[tt] = ok && dn >= eps ? -a1 * iden * iden : 0.f;
-        }
-        lds_barrier();
+        const float iden = 1.f / fmaxf(kr[K::SC + 2], eps), ik = kr[K::SC + 3], iu = kr[K::SC + 4];
         if (tid < 256) {
             const float gden = L.gden[tt], bad = L.lost ? __builtin_nanf("") : 0.f;
-            const float *carry = L.gzk[c & 1];
             const f4 al = ld4(kr + K::AL + 4 * jj), ee = ld4(kr + K::E + 4 * jj), zk = ld4(kr + K::ZK + 4 * jj);
             float gz[4], c1v[4], gkh[4], kh[4], uhv[4], wv[4], a2 = 0.f, a3 = 0.f, a4 = 0.f;
             sfor<4>([&](auto r) {
                 const int i = 4 * jj + r;
-                float acc = carry[i];
-                for (int s2 = tt; s2 < 16; ++s2) acc = fmaf(L.gden[s2], L.phi[s2][i], acc);
-                gz[r] = acc;
+                gz[r] = L.gz[i][tt];
                 c1v[r] = L.c1[i][tt];
                 kh[r] = inp(raw, SL::AKK, tt * D + i) * ik;
                 uhv[r] = L.uh[i][tt];
@@ -827,7 +839,6 @@ bwd_pc(PCLds<D, Tin> &L, int bh, const Tin *__restrict__ q, const Tin *__restric
             });
             a3 = row_sum<16>(a3);
             a4 = row_sum<16>(a4);
-            if (tt == 0) sfor<4>([&](auto r) { L.gzk[(c + 1) & 1][4 * jj + r] = gz[r]; });
             if (ok) {
                 f4 oq, ok4, ou;
                 sfor<4>([&](auto r) {
