@@ -679,8 +679,14 @@ bwd_pc(PCLds<D, Tin> &L, int bh, const Tin *__restrict__ q, const Tin *__restric
         }
     };
     auto inp = [&](const float *raw, int off, int idx) { return raw_get<Tin>(raw + off, idx); };
-    // token t, keys [4j, 4j + 4) of this thread (tid < 256)
+    // token tt, keys jj + 16 r (r < 4) of this thread (tid < 256): the sixteen
+    // lanes of a token meet distinct LDS banks in the key-major arrays
     const int tt = tid >> 4, jj = tid & 15;
+    auto col4 = [&](const float *row) {
+        f4 x;
+        sfor<4>([&](auto r) { x[int(r)] = row[jj + 16 * r]; });
+        return x;
+    };
     auto stage = [&](int c) {
         if (tid >= 256) return;
         const float *raw = L.raw[c & 1];
@@ -688,15 +694,15 @@ bwd_pc(PCLds<D, Tin> &L, int bh, const Tin *__restrict__ q, const Tin *__restric
         const bool ok = t0 + tt < T;
         const float *kr = raw + SL::AK + tt * RS;
         const float iy = kr[K::SC + 1], iu = kr[K::SC + 4], dl = kr[K::SC + 0];
-        const f4 al = ld4(kr + K::AL + 4 * jj), zz = ld4(kr + K::Z + 4 * jj), ee = ld4(kr + K::E + 4 * jj);
-        const f4 ga = ld4(raw + SL::AGA + tt * D + 4 * jj), ge = ld4(raw + SL::AGE + tt * D + 4 * jj);
-        const f4 go = ld4(raw + SL::AO + tt * D + 4 * jj);
+        const f4 al = col4(kr + K::AL), zz = col4(kr + K::Z), ee = col4(kr + K::E);
+        const f4 ga = col4(raw + SL::AGA + tt * D), ge = col4(raw + SL::AGE + tt * D);
+        const f4 go = col4(raw + SL::AO + tt * D);
         float aga = 0.f;
         sfor<4>([&](auto r) { aga = fmaf(al[int(r)], ga[int(r)], aga); });
         aga = row_sum<16>(aga);
         const float ny = iy > 0.f ? 1.f / iy : 0.f;
         sfor<4>([&](auto r) {
-            const int i = 4 * jj + r;
+            const int i = jj + 16 * r;
             const float xq = inp(raw, SL::AQ, tt * D + i), xu = inp(raw, SL::AU, tt * D + i);
             L.ge[i][tt] = ok ? ge[int(r)] : 0.f;
             L.ah[i][tt] = ok ? al[int(r)] : 0.f;
@@ -711,6 +717,21 @@ bwd_pc(PCLds<D, Tin> &L, int bh, const Tin *__restrict__ q, const Tin *__restric
         if (jj == 0) L.idl[tt] = ok ? 1.f / dl : 0.f;
     };
 
+    // A chunk's dq, dk and du go out after the next chunk's stage: the stage's
+    // reads of the copied rows wait for all of the wave's memory operations,
+    // and by then the stores have had a whole chunk to complete.
+    f4 oq = zero, ok4 = zero, ou = zero;
+    size_t oo = 0;
+    bool opend = false;
+    auto flush = [&]() {
+        if (opend) {
+            sfor<4>([&](auto r) {
+                dq[oo + 16 * r] = oq[int(r)];
+                dk[oo + 16 * r] = ok4[int(r)];
+                du[oo + 16 * r] = ou[int(r)];
+            });
+        }
+    };
     if (NC > 0 && w >= NB) copy(NC - 1);
     for (int c = NC - 1; c >= 0; --c) {
         const int t0 = 16 * c;
@@ -718,6 +739,7 @@ bwd_pc(PCLds<D, Tin> &L, int bh, const Tin *__restrict__ q, const Tin *__restric
         lds_barrier();
         stage(c);
         lds_barrier();
+        flush();
         if (c > 0 && w >= NB) copy(c - 1);
         // ---- products with the state at the chunk's end; the factors
         f4 x3 = zero, x4 = zero, x5 = zero, x6 = zero;
@@ -819,10 +841,10 @@ bwd_pc(PCLds<D, Tin> &L, int bh, const Tin *__restrict__ q, const Tin *__restric
         const float iden = 1.f / fmaxf(kr[K::SC + 2], eps), ik = kr[K::SC + 3], iu = kr[K::SC + 4];
         if (tid < 256) {
             const float gden = L.gden[tt], bad = L.lost ? __builtin_nanf("") : 0.f;
-            const f4 al = ld4(kr + K::AL + 4 * jj), ee = ld4(kr + K::E + 4 * jj), zk = ld4(kr + K::ZK + 4 * jj);
+            const f4 al = col4(kr + K::AL), ee = col4(kr + K::E), zk = col4(kr + K::ZK);
             float gz[4], c1v[4], gkh[4], kh[4], uhv[4], wv[4], a2 = 0.f, a3 = 0.f, a4 = 0.f;
             sfor<4>([&](auto r) {
-                const int i = 4 * jj + r;
+                const int i = jj + 16 * r;
                 gz[r] = L.gz[i][tt];
                 c1v[r] = L.c1[i][tt];
                 kh[r] = inp(raw, SL::AKK, tt * D + i) * ik;
@@ -833,29 +855,27 @@ bwd_pc(PCLds<D, Tin> &L, int bh, const Tin *__restrict__ q, const Tin *__restric
             });
             a2 = row_sum<16>(a2);
             sfor<4>([&](auto r) {
-                const int i = 4 * jj + r;
+                const int i = jj + 16 * r;
                 gkh[r] = fmaf(al[int(r)], a2, L.p[i][tt] - L.c2[i][tt]);
                 a3 = fmaf(kh[r], gkh[r], a3);
             });
             a3 = row_sum<16>(a3);
             a4 = row_sum<16>(a4);
+            opend = ok;
             if (ok) {
-                f4 oq, ok4, ou;
                 sfor<4>([&](auto r) {
-                    const int i = 4 * jj + r;
+                    const int i = jj + 16 * r;
                     const float xq = inp(raw, SL::AQ, tt * D + i), xk = inp(raw, SL::AKK, tt * D + i);
                     oq[int(r)] = fmaf(c1v[r], iden, gden * zk[int(r)]) * dphi(xq) + bad;
                     ok4[int(r)] = fmaf(ik, gkh[r] - kh[r] * a3, gz[r] * dphi(xk)) + bad;
                     ou[int(r)] = -iu * (wv[r] - uhv[r] * a4) + bad;
                 });
-                const size_t o = (tok0 + t0 + tt) * D + 4 * jj;
-                st4(dq + o, oq);
-                st4(dk + o, ok4);
-                st4(du + o, ou);
+                oo = (tok0 + t0 + tt) * D + jj;
             }
         }
     }
 
+    flush();
     lds_barrier();
     if (dzk0 && tid < D) dzk0[(size_t)bh * D + tid] = L.gzk[1][tid];
     // dL/dA_0 = A_0^-1 Q_0 A_0^-1 / 2: here for the default A_0 = I / lambda0;
