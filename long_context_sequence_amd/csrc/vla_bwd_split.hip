@@ -740,40 +740,47 @@ bwd_pc(PCLds<D, Tin> &L, int bh, const Tin *__restrict__ q, const Tin *__restric
         stage(c);
         lds_barrier();
         flush();
+        // ---- products with the state at the chunk's end and one 16 x 16 factor
+        // per matrix wave: V1 = (Z'GY) o [s > t] / delta_s, V2 = (Y'U^) o [s >= t],
+        // V4 = (E'G) o [s > t], V5 = (E'GE) o [s > t]; the copy waves fetch the
+        // next chunk
         if (c > 0 && w >= NB) copy(c - 1);
-        // ---- products with the state at the chunk's end; the factors
         f4 x3 = zero, x4 = zero, x5 = zero, x6 = zero;
         if (mw) {
-            sfor<NB>([&](auto rho) {
+            const float(*fa)[LS] = w == 0 ? L.z : w == 1 ? L.y : L.e;
+            const float(*fb)[LS] = w == 0 ? L.gy : w == 1 ? L.uh : w == 2 ? L.gm : L.ge;
+            float(*fo)[LS] = w == 0 ? L.v1 : w == 1 ? L.v2 : w == 2 ? L.v4 : L.v5;
+            f4 v = zero;
+            // operands of row block rho + 1 are read while block rho's go in
+            float bo[2][6][4];
+            auto fetch = [&](int rho, float(&b)[6][4]) {
                 sfor<4>([&](auto r) {
                     const int i = 16 * rho + 4 * g + r;
-                    x3 = mma(A[rho][int(r)], L.gy[i][n], x3);
-                    x4 = mma(Q[rho][int(r)], L.uh[i][n], x4);
-                    x5 = mma(S[rho][int(r)], L.gm[i][n], x5);
-                    x6 = mma(S[rho][int(r)], L.ge[i][n], x6);
+                    b[0][r] = L.gy[i][n];
+                    b[1][r] = L.uh[i][n];
+                    b[2][r] = L.gm[i][n];
+                    b[3][r] = L.ge[i][n];
+                    b[4][r] = fa[i][n];
+                    b[5][r] = fb[i][n];
+                });
+            };
+            fetch(0, bo[0]);
+            sfor<NB>([&](auto rho) {
+                if constexpr (rho + 1 < NB) fetch(rho + 1, bo[(rho + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead
+                const float(&b)[6][4] = bo[rho & 1];
+                sfor<4>([&](auto r) {
+                    x3 = mma(A[rho][int(r)], b[0][r], x3);
+                    x4 = mma(Q[rho][int(r)], b[1][r], x4);
+                    x5 = mma(S[rho][int(r)], b[2][r], x5);
+                    x6 = mma(S[rho][int(r)], b[3][r], x6);
+                    v = mma(b[4][r], b[5][r], v);
                 });
             });
-        } else if (w == NB) {   // V1 = (Z'GY) o [s > t] / delta_s, V2 = (Y'U^) o [s >= t]
-            f4 v1 = zero, v2 = zero;
-            sfor<D / 4>([&](auto qq) {
-                v1 = mma(at_gn(L.z, 0, qq), at_gn(L.gy, 0, qq), v1);
-                v2 = mma(at_gn(L.y, 0, qq), at_gn(L.uh, 0, qq), v2);
-            });
             sfor<4>([&](auto r) {
                 const int s = 4 * g + r;
-                L.v1[s][n] = s > n ? v1[int(r)] * L.idl[s] : 0.f;
-                L.v2[s][n] = s >= n ? v2[int(r)] : 0.f;
-            });
-        } else if (w == NB + 1) {   // V4 = (E'G) o [s > t], V5 = (E'GE) o [s > t]
-            f4 v4 = zero, v5 = zero;
-            sfor<D / 4>([&](auto qq) {
-                v4 = mma(at_gn(L.e, 0, qq), at_gn(L.gm, 0, qq), v4);
-                v5 = mma(at_gn(L.e, 0, qq), at_gn(L.ge, 0, qq), v5);
-            });
-            sfor<4>([&](auto r) {
-                const int s = 4 * g + r;
-                L.v4[s][n] = s > n ? v4[int(r)] : 0.f;
-                L.v5[s][n] = s > n ? v5[int(r)] : 0.f;
+                const bool keep = w == 1 ? s >= n : s > n;
+                fo[s][n] = keep ? v[int(r)] * (w == 0 ? L.idl[s] : 1.f) : 0.f;
             });
         }
         lds_barrier();
