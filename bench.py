@@ -283,7 +283,8 @@ def backward_bench(args):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": cfg.name + " backward", "B": B, "H": H, "d_h": d, "T": T,
                    "input_dtype": cfg.dtype, "state_dtype": "f32", "parallelism": "single GPU"},
-        "roofline": {"bound": "alu", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
+        "roofline": {"bound": "mfma" if d == 64 else "alu", "achieved": achieved,
+                     "peak": FP32_VECTOR_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
                      "traffic": measured_traffic(BWD_TRAFFIC_SUMMARY, BWD_KERNEL_SOURCES),
                      "kernel": "vla_backward call: vla_gram, vla_seginv, vla_pen, vla_mem "
