@@ -156,6 +156,11 @@ def parse():
                    help="heads in the CPU-baseline sample (0 = every head of the workload)")
     p.add_argument("--scan", action="store_true",
                    help="time vla_forward_scan (memory chain as a scan over chunks) instead")
+    p.add_argument("--scan-crossover", action="store_true",
+                   help="time vla_forward against vla_forward_scan on the d_h = 128, T = 65536 "
+                        "head shape for the head counts in --scan-heads")
+    p.add_argument("--scan-heads", default="1,2,4,8,16,64")
+    p.add_argument("--scan-reps", type=int, default=5)
     p.add_argument("--backward", action="store_true",
                    help="time vla_backward (gradients) on the same workload instead")
     p.add_argument("--decode", action="store_true",
@@ -365,6 +370,78 @@ def scan_bench(args):
                      "scan_combine_tflops": combine_flop / (kern_ms / 1e3) / 1e12},
     }
     print(json.dumps(res), flush=True)
+
+
+def scan_crossover(args):
+    """The scan form where the pages expect it to pay: the long-context head
+    shape (d_h = 128, T = 65536, bf16; the recipe of that workload) with few
+    heads.  For each head count, vla_forward and vla_forward_scan are timed on
+    the same inputs (HIP events on the launch stream, median of the repeats
+    after a warm-up); one JSON line holds the table."""
+    import numpy as np
+    import torch
+
+    import gen
+    import long_context_sequence_amd as vla
+
+    base = gen.config(5)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    rows = []
+    for h in [int(v) for v in args.scan_heads.split(",")]:
+        cfg = base.with_sizes(B=1, H=h, decode=0)
+        B, H, T, d = cfg.B, cfg.H, cfg.T, cfg.d
+        x = gen.make_inputs(cfg)
+        t = {n: torch.from_numpy(x[n]).to(dev).view(torch.bfloat16) for n in "qkvu"}
+        del x
+        o = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+        ws_f = torch.empty(vla.workspace_size(B, H, T, d), dtype=torch.uint8, device=dev)
+        ws_s = torch.empty(vla.scan_workspace_size(B, H, T, d), dtype=torch.uint8, device=dev)
+
+        def fwd():
+            vla.vla_forward(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps, o=o,
+                            workspace=ws_f, stream=stream)
+
+        def scan():
+            vla.vla_forward_scan(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps, o=o,
+                                 workspace=ws_s, stream=stream)
+
+        def timed(step):
+            t_w, n_w = time.perf_counter(), 0
+            while n_w < 2 or time.perf_counter() - t_w < 1.0:
+                step()
+                n_w += 1
+                torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.scan_reps)]
+            for e0, e1 in ev:
+                e0.record(stream)
+                step()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+        f_ms, s_ms = timed(fwd), timed(scan)
+        nc = (T + 15) // 16
+        n = 2
+        while n < nc:
+            n *= 2
+        comb = B * H * 2 * (n - 1) * 4 * d ** 3
+        rows.append({"heads": B * H, "forward_ms": f_ms, "scan_ms": s_ms,
+                     "scan_over_forward": s_ms / f_ms,
+                     "forward_tokens_heads_per_s": B * H * T / (f_ms / 1e3),
+                     "scan_tokens_heads_per_s": B * H * T / (s_ms / 1e3),
+                     "scan_combine_flop": comb,
+                     "scan_combine_tflops_if_all_time": comb / (s_ms / 1e3) / 1e12})
+        print(json.dumps({"progress": rows[-1]}), flush=True)
+        del t, o, ws_f, ws_s
+        torch.cuda.empty_cache()
+    print(json.dumps({
+        "metric": "VLA forward ms, chained memory pass against the scan over chunks (Eq. (12), "
+                  "right-multiplication combine), few heads of the long-context shape",
+        "config": {"workload": base.name + " head shape, B = 1, H = heads, no decode",
+                   "d_h": base.d, "T": base.T, "input_dtype": base.dtype},
+        "data": "synthetic", "rows": rows}), flush=True)
 
 
 def _time_forward(vla, torch, cfg, x, reps):
@@ -587,6 +664,9 @@ def main():
         return
     if args.backward:
         backward_bench(args)
+        return
+    if args.scan_crossover:
+        scan_crossover(args)
         return
     if args.scan:
         scan_bench(args)

@@ -168,7 +168,8 @@ vla_status vla_step(const void *q, const void *k, const void *v, const void *u,
                     void *stream);
 
 /*
- * vla_forward_scan -- the same forward as vla_forward (d_h = 64, T >= 1), with
+ * vla_forward_scan -- the same forward as vla_forward (d_h in {64, 96, 128},
+ * T >= 1), with
  * the memory chain (Eqs. (10), (11)) computed as a parallel scan over chunks of
  * 16 tokens instead of a chain: section 3.4, Eq. (12), with the combine
  * corrected to the right multiplication that Eq. (10) implies
@@ -180,7 +181,7 @@ vla_status vla_step(const void *q, const void *k, const void *v, const void *u,
  * does O(d^3) work per chunk where the chain does O(d^2) per token.
  *
  * Arguments, outputs and errors as for vla_forward; results equal vla_forward's
- * up to rounding.  d_h other than 64 is VLA_ERR_UNSUPPORTED, T < 1
+ * up to rounding.  d_h other than 64, 96 or 128 is VLA_ERR_UNSUPPORTED, T < 1
  * VLA_ERR_INVALID_ARG.  workspace: at least vla_forward_scan_workspace_size
  * bytes, 256-byte aligned (vla_forward's workspace plus 2 d^2 floats per chunk
  * of each head, rounded up to a power of two chunks, plus one map per head).
@@ -194,7 +195,7 @@ vla_status vla_forward_scan(const void *q, const void *k, const void *v, const v
 
 /* vla_forward_scan_workspace_size -- bytes of workspace vla_forward_scan needs
  * (0 when T == 0).  Host-only.  Errors: VLA_ERR_INVALID_ARG (NULL bytes, bad
- * sizes), VLA_ERR_UNSUPPORTED (d_h other than 64). */
+ * sizes), VLA_ERR_UNSUPPORTED (d_h other than 64, 96, 128). */
 vla_status vla_forward_scan_workspace_size(int B, int H, int T, int d_h, size_t *bytes);
 
 /*

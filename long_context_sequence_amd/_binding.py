@@ -409,7 +409,7 @@ def scan_workspace_size(B: int, H: int, T: int, d_h: int) -> int:
 
 def vla_forward_scan(q, k, v, u, lambda0: float = 0.1, eps: float = 1e-4, *, o=None,
                      S0=None, A0=None, zkey0=None, workspace=None, stream=None):
-    """vla_forward with the memory chain as a scan over chunks (d_h = 64).
+    """vla_forward with the memory chain as a scan over chunks (d_h in {64, 96, 128}).
     Returns ``(o, S, A, zkey)`` (float32)."""
     torch = _torch()
     B, H, T, d = q.shape

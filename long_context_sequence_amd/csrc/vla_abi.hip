@@ -167,7 +167,7 @@ extern "C" vla_status vla_step(const void *q, const void *k, const void *v, cons
 extern "C" vla_status vla_forward_scan_workspace_size(int B, int H, int T, int d_h, size_t *bytes)
 {
     if (!bytes || B < 1 || H < 1 || T < 0 || (long long)B * H > 0x7fffffffLL) return VLA_ERR_INVALID_ARG;
-    if (d_h != 64 || !vla::twopass_size_ok(T, d_h, false)) return VLA_ERR_UNSUPPORTED;
+    if (!vla::scan_supported(d_h) || !vla::twopass_size_ok(T, d_h, false)) return VLA_ERR_UNSUPPORTED;
     *bytes = vla::scan_workspace_bytes(B * H, T, d_h);
     return VLA_OK;
 }
@@ -181,7 +181,7 @@ extern "C" vla_status vla_forward_scan(const void *q, const void *k, const void 
 {
     vla_status st = check_common(in_dtype, B, H, d_h, eps);
     if (st != VLA_OK) return st;
-    if (d_h != 64) return VLA_ERR_UNSUPPORTED;
+    if (!vla::scan_supported(d_h)) return VLA_ERR_UNSUPPORTED;
     if (T < 1 || !finite_pos(lambda0)) return VLA_ERR_INVALID_ARG;
     if (!vla::twopass_size_ok(T, d_h, false)) return VLA_ERR_UNSUPPORTED;
     const size_t need = vla::scan_workspace_bytes(B * H, T, d_h);

@@ -72,6 +72,7 @@ hipError_t launch_baseline(const FwdArgs &a, bool delta, float beta);
 // the memory chain as a scan over chunks (d_h = 64, T >= 1): the penalty pass,
 // then per-chunk affine maps of S, a work-efficient scan of them and the
 // chunk-local readout; needs the workspace below.
+bool scan_supported(int d);   // d_h in {64, 96, 128}
 size_t scan_workspace_bytes(int BH, int T, int d);
 hipError_t launch_forward_scan(const FwdArgs &a);
 

@@ -1,6 +1,6 @@
 // vla_scan.hip -- the memory chain of the forward (Eqs. (10), (11)) as a
-// parallel scan over chunks, d_h = 64: the pages' own parallel form, built to be
-// measured against the chained memory pass.
+// parallel scan over chunks, d_h in {64, 96, 128}: the pages' own parallel form,
+// built to be measured against the chained memory pass.
 //
 // Source: "Variational Linear Attention" (arXiv 2605.11196), section 3.4,
 // Eq. (12): the write of Eq. (10) is an affine map of S, so the states are a
@@ -17,7 +17,7 @@
 //                 to a power of two n; S_0 folded into G_0 (G_0 <- S_0 F_0 + G_0)
 //   vla_scan_level  log2 n up-sweep and log2 n down-sweep levels of the
 //                 work-efficient (Blelloch) scan; one workgroup per combine, two
-//                 64 x 64 x 64 products on fp32 matrix cores
+//                 d x d x d products on fp32 matrix cores
 //   vla_scan_apply  S at each chunk start (the G of the exclusive prefix; S_0 for
 //                 the first chunk), then the chunk's readout
 //                 E = (V - S K^) T, o = (S Phi + E P) / den; final S = the total's G
@@ -35,19 +35,17 @@ using namespace chunk;
 using rec::CH;
 using rec::Rec;
 
-constexpr int SD = 64;          // head dimension of the scan form
-constexpr int SDD = SD * SD;
-
 // map slots of a head: n chunk maps, then the total
-__host__ __device__ inline size_t slot_floats(int n) { return (size_t)(n + 1) * 2 * SDD; }
+__host__ __device__ inline size_t slot_floats(int n, int d) { return (size_t)(n + 1) * 2 * d * d; }
 
 // ------------------------------------------------------------------- maps
-template <typename Tin>
-__global__ void __launch_bounds__(256)
+// Thread (row i, columns [j0, j0 + 16)) of both maps: d^2 / 16 threads.
+template <int D, typename Tin>
+__global__ void __launch_bounds__(D * D / 16)
 vla_scan_maps(const Tin *__restrict__ v, int T, int NC, int n, const float *__restrict__ recs,
               const float *S0, float *__restrict__ maps)
 {
-    constexpr int D = SD, RS = Rec<D>::SIZE, P = D + 1;
+    constexpr int RS = Rec<D>::SIZE, P = D + 1, DD = D * D, NT = DD / 16;
     __shared__ float tinv[CH][CH + 1];            // T[t][s]
     __shared__ __align__(16) float al[CH][D + 4];   // alpha^_s[j] (rows 16-byte aligned)
     __shared__ float kh[CH][P], vv[CH][P];        // k^_t[i], v_t[i]
@@ -55,9 +53,9 @@ vla_scan_maps(const Tin *__restrict__ v, int T, int NC, int n, const float *__re
     __shared__ float f0[D * P];                   // F_0 (first chunk with S_0)
 
     const int bh = blockIdx.x / n, c = blockIdx.x % n, tid = threadIdx.x;
-    float *F = maps + (size_t)bh * slot_floats(n) + (size_t)c * 2 * SDD, *G = F + SDD;
+    float *F = maps + (size_t)bh * slot_floats(n, D) + (size_t)c * 2 * DD, *G = F + DD;
     if (c >= NC) {   // identity map
-        for (int idx = tid * 4; idx < SDD; idx += 1024) {
+        for (int idx = tid * 4; idx < DD; idx += 4 * NT) {
             f4 x;
             sfor<4>([&](auto r) { x[int(r)] = (idx + r) / D == (idx + r) % D ? 1.f : 0.f; });
             st4(F + idx, x);
@@ -66,11 +64,11 @@ vla_scan_maps(const Tin *__restrict__ v, int T, int NC, int n, const float *__re
         return;
     }
     const float *r = recs + ((size_t)bh * NC + c) * RS;
-    {
+    if (tid < CH * CH) {
         const int t = tid >> 4, s = tid & 15;
         tinv[t][s] = r[Rec<D>::TT + swz16(s, t >> 2) + (t & 3)];   // stored transposed
     }
-    for (int idx = tid; idx < CH * D; idx += 256) {
+    for (int idx = tid; idx < CH * D; idx += NT) {
         const int s = idx / D, j = idx % D;
         al[s][j] = r[Rec<D>::AH + swz16(j, s >> 2) + (s & 3)];
         kh[s][j] = r[Rec<D>::KH + swzd<D>(s, j >> 2) + (j & 3)];
@@ -78,7 +76,7 @@ vla_scan_maps(const Tin *__restrict__ v, int T, int NC, int n, const float *__re
         vv[s][j] = tok < T ? load_in(v, ((size_t)bh * T + tok) * D + j) : 0.f;
     }
     __syncthreads();
-    for (int idx = tid; idx < D * CH; idx += 256) {
+    for (int idx = tid; idx < D * CH; idx += NT) {
         const int i = idx / CH, s = idx % CH;
         float a = 0.f, b = 0.f;
 #pragma unroll
@@ -90,8 +88,8 @@ vla_scan_maps(const Tin *__restrict__ v, int T, int NC, int n, const float *__re
         xv[i][s] = b;
     }
     __syncthreads();
-    // thread: row i, columns [j0, j0 + 16); one pass over the chunk's tokens s
-    const int i = tid >> 2, j0 = (tid & 3) * 16;
+    // one pass over the chunk's tokens s
+    const int i = tid / (D / 16), j0 = (tid % (D / 16)) * 16;
     float fr[16], gr[16];
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
@@ -115,7 +113,7 @@ vla_scan_maps(const Tin *__restrict__ v, int T, int NC, int n, const float *__re
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) f0[i * P + j0 + jj] = fr[jj];
         __syncthreads();
-        const float *s0 = S0 + (size_t)bh * SDD + (size_t)i * D;
+        const float *s0 = S0 + (size_t)bh * DD + (size_t)i * D;
         for (int m = 0; m < D; ++m) {
             const float sm = s0[m];
 #pragma unroll
@@ -136,34 +134,35 @@ vla_scan_maps(const Tin *__restrict__ v, int T, int NC, int n, const float *__re
 //     total slot and slot n - 1 becomes the identity;
 //   down-sweep: L = slot i (the prefix before the pair), R = slot j (the left
 //     half's total): out to slot i, and slot j <- L.
-// Wave w forms row block w of both products: lane (n, g) holds rows 16 w + n of
-// F_L and G_L, columns 16 g .. 16 g + 15, and k-step s contracts over key
-// 16 g + s (A operand from registers, B = F_R from LDS, rows padded to 65).
-template <bool DOWN, bool LAST>
-__global__ void __launch_bounds__(256)
+// Wave w (d / 16 waves) forms row block w of both products: lane (n, g) holds
+// rows 16 w + n of F_L and G_L, columns KG g .. KG g + KG - 1 (KG = d / 4), and
+// k-step s contracts over key KG g + s (A operand from registers, B = F_R from
+// LDS, rows padded to d + 1).
+template <int D, bool DOWN, bool LAST>
+__global__ void __launch_bounds__(4 * D)
 vla_scan_level(float *maps, int n, int span)
 {
-    constexpr int D = SD, P = D + 1;
+    constexpr int P = D + 1, DD = D * D, NT = 4 * D, KG = D / 4, TN = D / 16;
     __shared__ float fr[D * P];
 
     const int per = n / (2 * span);
     const int bh = blockIdx.x / per, k = blockIdx.x % per;
     const int i = (k + 1) * 2 * span - 1, j = i - span;
-    float *base = maps + (size_t)bh * slot_floats(n);
-    float *Si = base + (size_t)i * 2 * SDD, *Sj = base + (size_t)j * 2 * SDD;
+    float *base = maps + (size_t)bh * slot_floats(n, D);
+    float *Si = base + (size_t)i * 2 * DD, *Sj = base + (size_t)j * 2 * DD;
     const float *FL = DOWN ? Si : Sj, *FR = DOWN ? Sj : Si;
-    const float *GL = FL + SDD, *GR = FR + SDD;
+    const float *GL = FL + DD, *GR = FR + DD;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nn = lane & 15, g = lane >> 4;
-    for (int idx = tid * 4; idx < SDD; idx += 1024) {
+    for (int idx = tid * 4; idx < DD; idx += 4 * NT) {
         const f4 x = ld4(FR + idx);
         const int row = idx / D, col = idx % D;
         sfor<4>([&](auto r) { fr[row * P + col + r] = x[int(r)]; });
     }
-    float af[16], ag[16];
+    float af[KG], ag[KG];
     {
-        const float *fl = FL + (16 * w + nn) * D + 16 * g, *gl = GL + (16 * w + nn) * D + 16 * g;
-        sfor<4>([&](auto h) {
+        const float *fl = FL + (16 * w + nn) * D + KG * g, *gl = GL + (16 * w + nn) * D + KG * g;
+        sfor<KG / 4>([&](auto h) {
             const f4 x = ld4(fl + 4 * h), y = ld4(gl + 4 * h);
             sfor<4>([&](auto r) {
                 af[4 * h + r] = x[int(r)];
@@ -171,40 +170,40 @@ vla_scan_level(float *maps, int n, int span)
             });
         });
     }
-    f4 accF[4], accG[4];
-    sfor<4>([&](auto tn) {
+    f4 accF[TN], accG[TN];
+    sfor<TN>([&](auto tn) {
         accF[tn] = f4{0.f, 0.f, 0.f, 0.f};
         sfor<4>([&](auto r) { accG[tn][int(r)] = GR[(16 * w + 4 * g + r) * D + 16 * tn + nn]; });
     });
     __syncthreads();   // every read of slot j and of slot i is done before either is written
 
-    sfor<16>([&](auto s) {
-        sfor<4>([&](auto tn) {
-            const float b = fr[(16 * g + s) * P + 16 * tn + nn];
+    sfor<KG>([&](auto s) {
+        sfor<TN>([&](auto tn) {
+            const float b = fr[(KG * g + s) * P + 16 * tn + nn];
             accF[tn] = mma(af[s], b, accF[tn]);
             accG[tn] = mma(ag[s], b, accG[tn]);
         });
     });
 
-    float *out = LAST ? base + (size_t)n * 2 * SDD : Si;
-    sfor<4>([&](auto tn) {
+    float *out = LAST ? base + (size_t)n * 2 * DD : Si;
+    sfor<TN>([&](auto tn) {
         sfor<4>([&](auto r) {
             const int row = 16 * w + 4 * g + r, col = 16 * tn + nn;
             out[row * D + col] = accF[tn][int(r)];
-            out[SDD + row * D + col] = accG[tn][int(r)];
+            out[DD + row * D + col] = accG[tn][int(r)];
         });
     });
     if (LAST) {   // slot n - 1 <- identity (this is slot i)
-        for (int idx = tid * 4; idx < SDD; idx += 1024) {
+        for (int idx = tid * 4; idx < DD; idx += 4 * NT) {
             f4 x;
             sfor<4>([&](auto r) { x[int(r)] = (idx + r) / D == (idx + r) % D ? 1.f : 0.f; });
             st4(Si + idx, x);
-            st4(Si + SDD + idx, f4{0.f, 0.f, 0.f, 0.f});
+            st4(Si + DD + idx, f4{0.f, 0.f, 0.f, 0.f});
         }
     }
     if (DOWN) {   // slot j <- L (the rows this lane holds)
-        float *fj = Sj + (16 * w + nn) * D + 16 * g, *gj = Sj + SDD + (16 * w + nn) * D + 16 * g;
-        sfor<4>([&](auto h) {
+        float *fj = Sj + (16 * w + nn) * D + KG * g, *gj = Sj + DD + (16 * w + nn) * D + KG * g;
+        sfor<KG / 4>([&](auto h) {
             st4(fj + 4 * h, f4{af[4 * h], af[4 * h + 1], af[4 * h + 2], af[4 * h + 3]});
             st4(gj + 4 * h, f4{ag[4 * h], ag[4 * h + 1], ag[4 * h + 2], ag[4 * h + 3]});
         });
@@ -213,14 +212,14 @@ vla_scan_level(float *maps, int n, int span)
 
 // ------------------------------------------------------------------- apply
 // Workgroup (head, chunk): S at the chunk start, then the chunk's outputs.
-// Thread (row i, tokens 4 q .. 4 q + 3).
-template <typename Tin>
-__global__ void __launch_bounds__(256)
+// Thread (row i, tokens 4 q .. 4 q + 3): 4 d threads.
+template <int D, typename Tin>
+__global__ void __launch_bounds__(4 * D)
 vla_scan_apply(const Tin *__restrict__ v, int T, int NC, int n, const float *__restrict__ recs,
                const float *S0, const float *__restrict__ maps, float *__restrict__ o,
                float *S_out)
 {
-    constexpr int D = SD, RS = Rec<D>::SIZE, P = D + 1;
+    constexpr int RS = Rec<D>::SIZE, P = D + 1, DD = D * D, NT = 4 * D;
     __shared__ float sm[D * P];                     // S at the chunk start
     __shared__ __align__(16) float kt[D][CH], pt[D][CH];   // k^_t[m], phi(q_t)[m] as [m][t]
     __shared__ float vv[CH][P];
@@ -228,23 +227,23 @@ vla_scan_apply(const Tin *__restrict__ v, int T, int NC, int n, const float *__r
     __shared__ float wv[D][CH + 1], ev[D][CH + 1];   // V - S K^, E
 
     const int bh = blockIdx.x / NC, c = blockIdx.x % NC, tid = threadIdx.x;
-    const float *slots = maps + (size_t)bh * slot_floats(n);
-    const float *Sst = c == 0 ? (S0 ? S0 + (size_t)bh * SDD : nullptr)
-                              : slots + (size_t)c * 2 * SDD + SDD;   // G of the exclusive prefix
-    for (int idx = tid * 4; idx < SDD; idx += 1024) {
+    const float *slots = maps + (size_t)bh * slot_floats(n, D);
+    const float *Sst = c == 0 ? (S0 ? S0 + (size_t)bh * DD : nullptr)
+                              : slots + (size_t)c * 2 * DD + DD;   // G of the exclusive prefix
+    for (int idx = tid * 4; idx < DD; idx += 4 * NT) {
         const f4 x = Sst ? ld4(Sst + idx) : f4{0.f, 0.f, 0.f, 0.f};
         const int row = idx / D, col = idx % D;
         sfor<4>([&](auto r) { sm[row * P + col + r] = x[int(r)]; });
     }
     const float *r = recs + ((size_t)bh * NC + c) * RS;
-    for (int idx = tid; idx < CH * D; idx += 256) {
+    for (int idx = tid; idx < CH * D; idx += NT) {
         const int s = idx / D, j = idx % D;
         kt[j][s] = r[Rec<D>::KH + swzd<D>(s, j >> 2) + (j & 3)];
         pt[j][s] = r[Rec<D>::PH + swzd<D>(s, j >> 2) + (j & 3)];
         const int tok = c * CH + s;
         vv[s][j] = tok < T ? load_in(v, ((size_t)bh * T + tok) * D + j) : 0.f;
     }
-    {
+    if (tid < CH * CH) {
         const int t = tid >> 4, s = tid & 15;
         tinv[t][s] = r[Rec<D>::TT + swz16(s, t >> 2) + (t & 3)];
         pm[t][s] = r[Rec<D>::PT + swz16(s, t >> 2) + (t & 3)];
@@ -284,9 +283,9 @@ vla_scan_apply(const Tin *__restrict__ v, int T, int NC, int n, const float *__r
         if (tok < T) o[((size_t)bh * T + tok) * D + i] = a * rd[t];
     }
     if (c == 0 && S_out) {   // S_T = the G of the total map (S_0 folded into G_0)
-        const float *tg = slots + (size_t)n * 2 * SDD + SDD;
-        for (int idx = tid * 4; idx < SDD; idx += 1024)
-            st4(S_out + (size_t)bh * SDD + idx, ld4(tg + idx));
+        const float *tg = slots + (size_t)n * 2 * DD + DD;
+        for (int idx = tid * 4; idx < DD; idx += 4 * NT)
+            st4(S_out + (size_t)bh * DD + idx, ld4(tg + idx));
     }
 }
 
@@ -299,49 +298,63 @@ int scan_slots(int NC)
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-template <typename Tin>
+template <int D, typename Tin>
 hipError_t launch(const FwdArgs &a)
 {
     const int BH = a.B * a.H, NC = (a.T + CH - 1) / CH, n = scan_slots(NC);
     hipError_t e = launch_forward_twopass(a, 1);   // records, A_out, zkey_out
     if (e != hipSuccess) return e;
     const float *recs = reinterpret_cast<const float *>(static_cast<const char *>(a.ws) +
-                                                        twopass_records_offset(BH, a.T, SD));
+                                                        twopass_records_offset(BH, a.T, D));
     float *maps = reinterpret_cast<float *>(static_cast<char *>(a.ws) +
-                                            up256(twopass_workspace_bytes(BH, a.T, SD)));
+                                            up256(twopass_workspace_bytes(BH, a.T, D)));
     const Tin *v = static_cast<const Tin *>(a.v);
-    hipLaunchKernelGGL((vla_scan_maps<Tin>), dim3(BH * n), dim3(256), 0, a.stream, v, a.T, NC, n,
-                       recs, a.S0, maps);
+    hipLaunchKernelGGL((vla_scan_maps<D, Tin>), dim3(BH * n), dim3(D * D / 16), 0, a.stream, v, a.T,
+                       NC, n, recs, a.S0, maps);
     for (int span = 1; span < n; span *= 2) {
         const int grid = BH * (n / (2 * span));
         if (2 * span == n)
-            hipLaunchKernelGGL((vla_scan_level<false, true>), dim3(grid), dim3(256), 0, a.stream,
+            hipLaunchKernelGGL((vla_scan_level<D, false, true>), dim3(grid), dim3(4 * D), 0, a.stream,
                                maps, n, span);
         else
-            hipLaunchKernelGGL((vla_scan_level<false, false>), dim3(grid), dim3(256), 0, a.stream,
-                               maps, n, span);
+            hipLaunchKernelGGL((vla_scan_level<D, false, false>), dim3(grid), dim3(4 * D), 0,
+                               a.stream, maps, n, span);
     }
     for (int span = n / 2; span >= 1; span /= 2)
-        hipLaunchKernelGGL((vla_scan_level<true, false>), dim3(BH * (n / (2 * span))), dim3(256), 0,
-                           a.stream, maps, n, span);
-    hipLaunchKernelGGL((vla_scan_apply<Tin>), dim3(BH * NC), dim3(256), 0, a.stream, v, a.T, NC, n,
-                       recs, a.S0, maps, a.o, a.S_out);
+        hipLaunchKernelGGL((vla_scan_level<D, true, false>), dim3(BH * (n / (2 * span))), dim3(4 * D),
+                           0, a.stream, maps, n, span);
+    hipLaunchKernelGGL((vla_scan_apply<D, Tin>), dim3(BH * NC), dim3(4 * D), 0, a.stream, v, a.T, NC,
+                       n, recs, a.S0, maps, a.o, a.S_out);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs &a)
+{
+    return a.dtype == 1 ? launch<D, uint16_t>(a) : launch<D, float>(a);
 }
 
 }  // namespace
 
+bool scan_supported(int d) { return d == 64 || d == 96 || d == 128; }
+
 size_t scan_workspace_bytes(int BH, int T, int d)
 {
-    if (d != SD || T <= 0) return 0;
+    if (!scan_supported(d) || T <= 0) return 0;
     const int n = scan_slots((T + CH - 1) / CH);
-    return up256(twopass_workspace_bytes(BH, T, d)) + up256((size_t)BH * slot_floats(n) * sizeof(float));
+    return up256(twopass_workspace_bytes(BH, T, d)) +
+           up256((size_t)BH * slot_floats(n, d) * sizeof(float));
 }
 
 hipError_t launch_forward_scan(const FwdArgs &a)
 {
-    if (a.d != SD || a.T < 1) return hipErrorInvalidValue;
-    return a.dtype == 1 ? launch<uint16_t>(a) : launch<float>(a);
+    if (a.T < 1) return hipErrorInvalidValue;
+    switch (a.d) {
+    case 64: return launch_d<64>(a);
+    case 96: return launch_d<96>(a);
+    case 128: return launch_d<128>(a);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace vla

@@ -238,8 +238,8 @@ def test_scan_argument_errors():
         return lib.vla_forward_scan(a["q"], a["k"], a["v"], a["u"], a["dt"], a["B"], a["H"],
                                     a["T"], a["d"], a["lam"], a["eps"], a["o"], None, None, None,
                                     None, None, None, a["ws"], a["ws_bytes"], None)
-    assert call(d=96) == B.VLA_ERR_UNSUPPORTED
-    assert call(d=128) == B.VLA_ERR_UNSUPPORTED
+    assert call(d=32) == B.VLA_ERR_UNSUPPORTED
+    assert call(d=48) == B.VLA_ERR_UNSUPPORTED
     assert call(T=0) == B.VLA_ERR_INVALID_ARG
     assert call(o=None) == B.VLA_ERR_INVALID_ARG
     assert call(ws=None) == B.VLA_ERR_INVALID_ARG
@@ -247,16 +247,17 @@ def test_scan_argument_errors():
     assert call(eps=0.0) == B.VLA_ERR_INVALID_ARG
     # workspace: the forward's plus (n + 1) maps of 2 d^2 floats per head, n a
     # power of two >= the chunk count (>= 2)
-    for T in (1, 16, 17, 4096):
-        nc = (T + 15) // 16
-        n = 2
-        while n < nc:
-            n *= 2
-        maps = 2 * 3 * (n + 1) * 2 * 64 * 64 * 4
-        got = vla.scan_workspace_size(2, 3, T, 64)
-        assert vla.workspace_size(2, 3, T, 64) + maps <= got < vla.workspace_size(2, 3, T, 64) + maps + 512
+    for d in (64, 96, 128):
+        for T in (1, 16, 17, 4096):
+            nc = (T + 15) // 16
+            n = 2
+            while n < nc:
+                n *= 2
+            maps = 2 * 3 * (n + 1) * 2 * d * d * 4
+            got = vla.scan_workspace_size(2, 3, T, d)
+            assert vla.workspace_size(2, 3, T, d) + maps <= got < vla.workspace_size(2, 3, T, d) + maps + 512
     with pytest.raises(vla.VLAError):
-        vla.scan_workspace_size(1, 1, 64, 96)
+        vla.scan_workspace_size(1, 1, 64, 32)
 
 
 def test_sequence_length_limit():

@@ -93,3 +93,63 @@ def test_scan_bench_workload_matches_forward_and_oracle():
         for name, g in zip(("o", "S", "A", "zkey"), out):
             print(f"  scan vs oracle ({b},{h}):", flush=True)
             check(name, g[b, h], r[name])
+
+
+def _wide(cid, **sizes):
+    """Config 4 (d = 96, fp32 inputs) or 5 (d = 128, bf16 inputs) at other sizes."""
+    return gen.config(cid).with_sizes(decode=0, **sizes)
+
+
+@pytest.mark.parametrize("cid", [4, 5])
+@pytest.mark.parametrize("T", [1, 17, 100, 300])
+def test_scan_wider_heads(cid, T):
+    dev = _dev()
+    cfg = _wide(cid, B=1, H=2, T=T)
+    print(f"scan d={cfg.d} {cfg.dtype} T={T}", flush=True)
+    x = gen.make_inputs(cfg)
+    out = _scan(cfg, x, dev)
+    ref = oracle.forward(*(_f64(x[n], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+    for name, g in zip(("o", "S", "A", "zkey"), out):
+        check(name, g, ref[name])
+
+
+@pytest.mark.parametrize("cid", [4, 5])
+def test_scan_wider_heads_given_initial_state(cid):
+    dev = _dev()
+    cfg = _wide(cid, B=1, H=2, T=70)
+    print(f"scan d={cfg.d} given state", flush=True)
+    x = gen.make_inputs(cfg)
+    rng = np.random.default_rng(23)
+    d = cfg.d
+    m = rng.standard_normal((1, 2, d, d))
+    S0 = (0.3 * rng.standard_normal((1, 2, d, d))).astype(np.float32)
+    A0 = (m @ m.transpose(0, 1, 3, 2) / d + 0.5 * np.eye(d)).astype(np.float32)
+    z0 = rng.uniform(0.5, 2.0, (1, 2, d)).astype(np.float32)
+    out = _scan(cfg, x, dev, S0=torch.from_numpy(S0).to(dev), A0=torch.from_numpy(A0).to(dev),
+                zkey0=torch.from_numpy(z0).to(dev))
+    for h in range(2):
+        r = oracle.forward_head(*(_f64(x[n][0, h], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps,
+                                S0[0, h].astype(np.float64), A0[0, h].astype(np.float64),
+                                z0[0, h].astype(np.float64))
+        for name, g in zip(("o", "S", "A", "zkey"), out):
+            check(f"{name}[0,{h}]", g[0, h], r[name])
+
+
+def test_scan_d128_long_head_matches_forward_and_oracle():
+    """d = 128, bf16, one head of 8192 tokens (512 chunks: nine up- and nine
+    down-sweep levels) against vla_forward and the oracle."""
+    dev = _dev()
+    vla = _vla()
+    cfg = _wide(5, B=1, H=1, T=8192)
+    x = gen.make_inputs(cfg)
+    out = _scan(cfg, x, dev)
+    t = {n: _to_dev(x[n], cfg, dev) for n in "qkvu"}
+    fwd = vla.vla_forward(t["q"], t["k"], t["v"], t["u"], cfg.lambda0, cfg.eps, return_state=True)
+    torch.cuda.synchronize()
+    for name, g, f in zip(("o", "S", "A", "zkey"), out, fwd):
+        print("  scan vs forward:", flush=True)
+        check(name, g, f.cpu().numpy().astype(np.float64))
+    r = oracle.forward_head(*(_f64(x[n][0, 0], cfg) for n in "qkvu"), cfg.lambda0, cfg.eps)
+    for name, g in zip(("o", "S", "A", "zkey"), out):
+        print("  scan vs oracle:", flush=True)
+        check(name, g[0, 0], r[name])
