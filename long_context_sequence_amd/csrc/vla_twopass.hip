@@ -193,11 +193,47 @@ vla_gram(const Tin *__restrict__ k, const Tin *__restrict__ u, int T, int S, int
     }
 }
 
+// ------------------------------------------------------------------- prefix
+// With many segments per head (few heads), the inverse of segment j would sum
+// the Gram parts of all j earlier segments, O(S^2) reads per head.  Thread e
+// (an entry of G, or of the key sum past the d^2 entries) runs once through a
+// head's parts in order and leaves in part 0 of segment j the sum over segments
+// 0 .. j; the parts of eight segments are read before their sums are written.
+template <int D>
+__global__ void __launch_bounds__(256)
+vla_gram_prefix(int S, int P, double *__restrict__ gram, double *__restrict__ zks)
+{
+    constexpr int DD = D * D, NE = DD + D, NBLK = (NE + 255) / 256, SB = 8;
+    const int bh = blockIdx.x / NBLK, e = (blockIdx.x % NBLK) * 256 + threadIdx.x;
+    if (e >= NE) return;
+    const int S1 = S - 1;
+    double *b = e < DD ? gram + (size_t)bh * S1 * P * DD + e : zks + (size_t)bh * S1 * P * D + (e - DD);
+    const size_t stride = e < DD ? (size_t)DD : (size_t)D;   // between consecutive parts
+    double acc = 0.0;
+    for (int j0 = 0; j0 < S1; j0 += SB) {
+        double x[SB];
+        sfor<SB>([&](auto v) {
+            double t = 0.0;
+            if (j0 + v < S1)
+                for (int pp = 0; pp < P; ++pp) t += b[((size_t)(j0 + v) * P + pp) * stride];
+            x[v] = t;
+        });
+        sfor<SB>([&](auto v) {
+            if (j0 + v < S1) {
+                acc += x[v];
+                b[(size_t)(j0 + v) * P * stride] = acc;
+            }
+        });
+    }
+}
+
 // ------------------------------------------------------------------- inverse
 // (sweep_all, vla_sweep.h)
 
 // Workgroup (head, segment j >= 1): A at the segment start = M^-1 with
-// M = A_0^-1 + sum_{i<j} G_i, and the key sum at the segment start.  With a
+// M = A_0^-1 + sum_{i<j} G_i, and the key sum at the segment start.  With
+// `prefixed` the sums over the earlier segments are ready in part 0 of segment
+// j - 1 (vla_gram_prefix); otherwise the parts are summed here.  With a
 // caller-given A_0 (or zkey_0) the workgroup of segment 1 also copies it to slot
 // 0, which the penalty pass reads instead, so that the final state may overwrite
 // the initial one.
@@ -209,7 +245,7 @@ template <int D>
 __global__ void __launch_bounds__(seg_tpr<D>() * D)
 vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
            const double *__restrict__ gram, const double *__restrict__ zks,
-           float *__restrict__ aseg, float *__restrict__ zseg)
+           float *__restrict__ aseg, float *__restrict__ zseg, bool prefixed)
 {
     constexpr int SEG_TPR = seg_tpr<D>(), EPT = D / SEG_TPR;
     __shared__ __align__(16) double rowbuf[2][4 * D + 16];
@@ -231,8 +267,9 @@ vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
     // G parts of the segments before j, in order, loads NPF parts ahead (two at
     // d = 128, where 1024 threads have at most 128 registers each)
     constexpr int NPF = D == 128 ? 2 : 4;
-    const int NPART = j * P;
-    const double *gb = gram + (size_t)bh * S1 * P * DD + (size_t)i * D + c0;
+    const int NPART = prefixed ? 1 : j * P;
+    const double *gb = gram + (size_t)bh * S1 * P * DD + (prefixed ? (size_t)(j - 1) * P * DD : 0) +
+                       (size_t)i * D + c0;
     auto add_part = [&](const double2 (&x)[EPT / 2]) {
         sfor<EPT / 2>([&](auto h) {
             m[2 * h] += x[h].x;
@@ -259,7 +296,7 @@ vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
     sfor<EPT>([&](auto e) { A[e] = (float)(-m[e]); });
     if (tid < D) {
         double z = zk0 ? (double)zk0[bh * D + tid] : 0.0;
-        const double *zb = zks + (size_t)bh * S1 * P * D + tid;
+        const double *zb = zks + (size_t)bh * S1 * P * D + (prefixed ? (size_t)(j - 1) * P * D : 0) + tid;
         int s2 = 0;
         for (; s2 + 4 <= NPART; s2 += 4) {
             double x[4];
@@ -943,8 +980,14 @@ hipError_t launch(const FwdArgs &a, int phases)
         if (p.S > 1) {
             hipLaunchKernelGGL((vla_gram<D, Tin>), dim3(BH * (p.S - 1) * p.P), dim3(256), 0, a.stream,
                                k, u, a.T, p.S, p.SC, p.P, gram, zks);
+            // prefix sums over the segments once a head has many (a launch
+            // more than the direct sums cost with a few)
+            const bool prefixed = (p.S - 1) * p.P > 16;
+            if (prefixed)
+                hipLaunchKernelGGL((vla_gram_prefix<D>), dim3(BH * ((D * D + D + 255) / 256)), dim3(256), 0,
+                                   a.stream, p.S, p.P, gram, zks);
             hipLaunchKernelGGL((vla_seginv<D>), dim3(BH * (p.S - 1)), dim3(seg_tpr<D>() * D), 0, a.stream, p.S,
-                               p.P, a.lambda0, a.A0, a.zk0, gram, zks, aseg, zseg);
+                               p.P, a.lambda0, a.A0, a.zk0, gram, zks, aseg, zseg, prefixed);
         }
         if (a.keep)
             hipLaunchKernelGGL((vla_pen<D, Tin, true>), dim3(BH * p.S), dim3(64 * Cfg<D>::NA), 0,

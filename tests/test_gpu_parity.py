@@ -373,6 +373,7 @@ def test_run_to_run_bitwise_deterministic():
     (128, "bf16", 1, 2, 1500),
     (128, "f32", 3, 1, 33),       # three chunks, one segment
     (64, "f32", 4, 128, 160),     # 512 heads: a single segment each
+    (96, "bf16", 2, 2, 8192),     # 64 segments of two Gram parts, summed by the prefix pass
 ])
 def test_segments_every_head(d, dtype, B, H, T):
     dev = _dev()
