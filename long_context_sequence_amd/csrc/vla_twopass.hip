@@ -228,7 +228,7 @@ vla_gram_prefix(int S, int P, double *__restrict__ gram, double *__restrict__ zk
 }
 
 // ------------------------------------------------------------------- inverse
-// (sweep_all, vla_sweep.h)
+// (sweep_tiles, vla_sweep.h)
 
 // Workgroup (head, segment j >= 1): A at the segment start = M^-1 with
 // M = A_0^-1 + sum_{i<j} G_i, and the key sum at the segment start.  With
@@ -237,63 +237,60 @@ vla_gram_prefix(int S, int P, double *__restrict__ gram, double *__restrict__ zk
 // caller-given A_0 (or zkey_0) the workgroup of segment 1 also copies it to slot
 // 0, which the penalty pass reads instead, so that the final state may overwrite
 // the initial one.
-// threads per matrix row of the inverse (the penalty pass measured 404 us with
-// 8, 408 with 4 and 415 with 16 on the bench workload)
-template <int D> constexpr int seg_tpr() { return 8; }
-
+// The matrix lives in fp64 matrix-core tiles (sweep_tiles, vla_sweep.h): D / 16
+// waves, wave I holding tile row I.
 template <int D>
-__global__ void __launch_bounds__(seg_tpr<D>() * D)
+__global__ void __launch_bounds__(4 * D)
 vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
            const double *__restrict__ gram, const double *__restrict__ zks,
            float *__restrict__ aseg, float *__restrict__ zseg, bool prefixed)
 {
-    constexpr int SEG_TPR = seg_tpr<D>(), EPT = D / SEG_TPR;
+    constexpr int NB = D / 16;
     __shared__ __align__(16) double rowbuf[2][4 * D + 16];
     const int S1 = S - 1;
     const int bh = blockIdx.x / S1, j = blockIdx.x % S1 + 1;
-    const int tid = threadIdx.x, i = tid / SEG_TPR, c0 = (tid % SEG_TPR) * EPT;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+    const int I = __builtin_amdgcn_readfirstlane(tid >> 6);
     const size_t DD = (size_t)D * D;
+    // element (row, column) of tile (I, J), register r
+    auto rc = [&](int J, int r) { return (size_t)(16 * I + g + 4 * r) * D + 16 * J + n; };
 
-    double m[EPT];
+    Tiles64<D> t;
     if (A0) {
-        const float *a0 = A0 + bh * DD + (size_t)i * D + c0;
-        sfor<EPT>([&](auto e) { m[e] = (double)a0[e]; });
-        if (j == 1) sfor<EPT>([&](auto e) { aseg[(size_t)bh * S * DD + (size_t)i * D + c0 + e] = a0[e]; });
-        sweep_all<D, EPT>(m, i, c0, rowbuf);   // -A_0^-1
-        sfor<EPT>([&](auto e) { m[e] = -m[e]; });
+        const float *a0 = A0 + bh * DD;
+        sfor<NB>([&](auto J) { sfor<4>([&](auto r) { t[J][int(r)] = (double)a0[rc(J, r)]; }); });
+        if (j == 1)
+            sfor<NB>([&](auto J) { sfor<4>([&](auto r) { aseg[(size_t)bh * S * DD + rc(J, r)] = a0[rc(J, r)]; }); });
+        sweep_tiles<D>(t, I, lane, rowbuf);   // -A_0^-1
+        sfor<NB>([&](auto J) { t[J] = -t[J]; });
     } else {
-        sfor<EPT>([&](auto e) { m[e] = i == c0 + e ? (double)lambda0 : 0.0; });
-    }
-    // G parts of the segments before j, in order, loads NPF parts ahead (two at
-    // d = 128, where 1024 threads have at most 128 registers each)
-    constexpr int NPF = D == 128 ? 2 : 4;
-    const int NPART = prefixed ? 1 : j * P;
-    const double *gb = gram + (size_t)bh * S1 * P * DD + (prefixed ? (size_t)(j - 1) * P * DD : 0) +
-                       (size_t)i * D + c0;
-    auto add_part = [&](const double2 (&x)[EPT / 2]) {
-        sfor<EPT / 2>([&](auto h) {
-            m[2 * h] += x[h].x;
-            m[2 * h + 1] += x[h].y;
+        sfor<NB>([&](auto J) {
+            sfor<4>([&](auto r) { t[J][int(r)] = 16 * I + g + 4 * r == 16 * J + n ? (double)lambda0 : 0.0; });
         });
+    }
+    // G parts of the segments before j, in order, two parts in flight
+    const int NPART = prefixed ? 1 : j * P;
+    const double *gb = gram + (size_t)bh * S1 * P * DD + (prefixed ? (size_t)(j - 1) * P * DD : 0);
+    auto load_part = [&](int s2, Tiles64<D> &x) {
+        const double *G = gb + (size_t)s2 * DD;
+        sfor<NB>([&](auto J) { sfor<4>([&](auto r) { x[J][int(r)] = G[rc(J, r)]; }); });
     };
     int s = 0;
-    for (; s + NPF <= NPART; s += NPF) {
-        double2 x[NPF][EPT / 2];
-        sfor<NPF>([&](auto v) {
-            const double2 *G = reinterpret_cast<const double2 *>(gb + (size_t)(s + v) * DD);
-            sfor<EPT / 2>([&](auto h) { x[v][h] = G[h]; });
-        });
-        sfor<NPF>([&](auto v) { add_part(x[v]); });
+    for (; s + 2 <= NPART; s += 2) {
+        Tiles64<D> x0, x1;
+        load_part(s, x0);
+        load_part(s + 1, x1);
+        sfor<NB>([&](auto J) { t[J] += x0[J]; });
+        sfor<NB>([&](auto J) { t[J] += x1[J]; });
     }
-    for (; s < NPART; ++s) {
-        double2 x[EPT / 2];
-        const double2 *G = reinterpret_cast<const double2 *>(gb + (size_t)s * DD);
-        sfor<EPT / 2>([&](auto h) { x[h] = G[h]; });
-        add_part(x);
+    if (s < NPART) {
+        Tiles64<D> x0;
+        load_part(s, x0);
+        sfor<NB>([&](auto J) { t[J] += x0[J]; });
     }
-    sweep_all<D, EPT>(m, i, c0, rowbuf);   // -M^-1
-    float *A = aseg + ((size_t)bh * S + j) * DD + (size_t)i * D + c0;
-    sfor<EPT>([&](auto e) { A[e] = (float)(-m[e]); });
+    sweep_tiles<D>(t, I, lane, rowbuf);   // -M^-1
+    float *A = aseg + ((size_t)bh * S + j) * DD;
+    sfor<NB>([&](auto J) { sfor<4>([&](auto r) { A[rc(J, r)] = (float)(-t[J][int(r)]); }); });
     if (tid < D) {
         double z = zk0 ? (double)zk0[bh * D + tid] : 0.0;
         const double *zb = zks + (size_t)bh * S1 * P * D + (prefixed ? (size_t)(j - 1) * P * D : 0) + tid;
@@ -986,7 +983,7 @@ hipError_t launch(const FwdArgs &a, int phases)
             if (prefixed)
                 hipLaunchKernelGGL((vla_gram_prefix<D>), dim3(BH * ((D * D + D + 255) / 256)), dim3(256), 0,
                                    a.stream, p.S, p.P, gram, zks);
-            hipLaunchKernelGGL((vla_seginv<D>), dim3(BH * (p.S - 1)), dim3(seg_tpr<D>() * D), 0, a.stream, p.S,
+            hipLaunchKernelGGL((vla_seginv<D>), dim3(BH * (p.S - 1)), dim3(4 * D), 0, a.stream, p.S,
                                p.P, a.lambda0, a.A0, a.zk0, gram, zks, aseg, zseg, prefixed);
         }
         if (a.keep)
