@@ -232,6 +232,14 @@ struct RawVec {
 // phi = ELU + 1 with the hardware exp2 path (relative error ~1e-6 here).
 __device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
+// 1 / sqrt(x) as the single hardware instruction (v_rsq_f32, about 1 ulp), for
+// x > 0 that is a normal float; rsqrtf also rescales denormal x, which costs five
+// more instructions.  Used for |w_t|^2 = |A_t k^_t|^2 with unit k^: A_t is the
+// inverse of A_0^-1 + sum_{s<=t} u^_s u^_s' (section 3.2), whose eigenvalues are
+// at most |A_0^-1| + t, so a nonzero |w_t|^2 is at least (|A_0^-1| + t)^-2, far
+// above the denormal range for any sequence length the library accepts.
+__device__ __forceinline__ float rsq_normal(float x) { return __builtin_amdgcn_rsqf(x); }
+
 template <int D>
 struct Cfg {
     static constexpr int C = 16;                   // tokens per chunk
@@ -359,14 +367,14 @@ struct Head {
         f4 ns4 = ld4(&L.nrm[0][4 * g]);
         sfor<NA - 1>([&](auto w2) { ns4 += ld4(&L.nrm[w2 + 1][4 * g]); });
         f4 r4;
-        sfor<4>([&](auto r) { r4[int(r)] = ns4[int(r)] > 0.f ? rsqrtf(ns4[int(r)]) : 0.f; });
+        sfor<4>([&](auto r) { r4[int(r)] = ns4[int(r)] > 0.f ? rsq_normal(ns4[int(r)]) : 0.f; });
         return r4;
     }
     __device__ __forceinline__ float inv_norm_n() const
     {
         float ns = L.nrm[0][n];
         sfor<NA - 1>([&](auto w2) { ns += L.nrm[w2 + 1][n]; });
-        return ns > 0.f ? rsqrtf(ns) : 0.f;
+        return ns > 0.f ? rsq_normal(ns) : 0.f;
     }
 
     // ------------------------------------------------------------ penalty chain
@@ -507,10 +515,9 @@ struct Head {
             float zb[4];   // Z0'[4c+g][16b+n]
             sfor<4>([&](auto c) { zb[c] = z0t[(16 * b + n) * LT + 4 * c + g]; });
             const f4 q2 = mma4(X, zb, zero);        // L^-1 Z0': row t is z_t
-            const f4 q1 = q2 * inv4;                // D^-1 L^-1 Z0'
-            const f4 xt = mma4(lit, q1, zero);      // (I + G)^-1 Z0'
+            const f4 q1 = q2 * -inv4;               // -D^-1 L^-1 Z0' (the sign rides on the multiply)
+            const f4 nx = mma4(lit, q1, zero);      // -(I + G)^-1 Z0'
             const f4 wt = mma4(hm, q2, y[bb]);      // W'
-            const f4 nx = -xt;
             wout.zcols(b, q2, inv4);
             f4 az[NB];
             sfor<NB>([&](auto rho) { az[rho] = ld4(&z0t[(16 * rho + n) * LT + 4 * g]); });
@@ -550,7 +557,8 @@ struct Head {
         sfor<4>([&](auto r) {   // -N[4g+r][n] (strictly upper), rows through LDS
             float a = L.nq[0][0][(4 * g + r) * LT + n];
             sfor<NA - 1>([&](auto w2) { a += L.nq[w2 + 1][0][(4 * g + r) * LT + n]; });
-            L.tit[wi][(4 * g + r) * LT + n] = 4 * g + r < n ? -(a * invn4[int(r)]) : 0.f;
+            const float sc = 4 * g + r < n ? -invn4[int(r)] : 0.f;   // a select, not a branch
+            L.tit[wi][(4 * g + r) * LT + n] = a * sc;
         });
         wave_lds_order();
         sfor<4>([&](auto q4) {
@@ -560,7 +568,7 @@ struct Head {
         sfor<4>([&](auto r) {
             float a = L.nq[0][1][(4 * g + r) * LT + n];
             sfor<NA - 1>([&](auto w2) { a += L.nq[w2 + 1][1][(4 * g + r) * LT + n]; });
-            qa[int(r)] = 4 * g + r <= n ? a * invn4[int(r)] : 0.f;
+            qa[int(r)] = a * (4 * g + r <= n ? invn4[int(r)] : 0.f);
         });
         st4(&pt[swz16(n, g)], qa);
         float X[4];

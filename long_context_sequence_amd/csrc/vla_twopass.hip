@@ -508,11 +508,20 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     const int NC = (T + CH - 1) / CH;
     const int c0 = j * SC, c1 = min(NC, c0 + SC);
 
-    // serial work spread over the waves: wave 0 factorises I + G, wave 1 forms
-    // the C x C factors of the record, the waves from 2 on own the key sums, and
-    // the last two waves stage the inputs
-    Hd hd(L, tid & 63, w, tid - 128);
-    PenStage<D, Tin, SAVE> ps(tid - 64 * (NA - PenStage<D, Tin, SAVE>::NWS));
+    // serial work spread over the waves.  Wave 0 factorises I + G and the waves
+    // from 2 on own the key sums.  Six waves (d = 96): wave 1 forms the C x C
+    // factors of the record and the key cross factors, the last wave the phi(q)
+    // cross factors, and the last four stage the inputs.  Four waves: two
+    // workgroups share a compute unit, and the dispatcher puts wave i of one on
+    // the SIMD of wave i - 1 (mod 4) of the other (measured), so the roles are
+    // spread to even out those pairs: waves 1 and 3 stage the inputs, and wave 2
+    // forms the C x C factors and both cross factors besides its key sums.
+    constexpr int NWS = PenStage<D, Tin, SAVE>::NWS;
+    constexpr bool FOUR = NA == 4;
+    const int lane = tid & 63;
+    Hd hd(L, lane, w, tid - 128);
+    PenStage<D, Tin, SAVE> ps(FOUR ? (w == 1 ? lane : (w == 3 ? 64 + lane : -1)) : tid - 64 * (NA - NWS));
+    const int wfac = FOUR ? 2 : 1;   // the wave of the record's C x C factors
     float *kept = SAVE ? kept_all + (size_t)bh * T * Keep<D>::RS : nullptr;
     typename Hd::State st;
     const float *a_init;
@@ -568,11 +577,15 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         if (p > c0) {
             const f4 invn4 = hd.inv_norms4();
             alpha_out(rb - RS, (p - 1) * CH, invn4);
-            if (w == 1) hd.prep_tp(rb - RS + Rec<D>::TT, rb - RS + Rec<D>::PT, invn4);
-            if (((p - 1) & 1) == 0 && (w == 1 || w == NA - 1)) {
-                const float invm = hd.inv_norm_n();
-                if (w == 1) cross_factor<D>(L, L.kh[p & 1], hd.g, hd.n, invm, rb - RS + Rec<D>::QK);
-                else cross_factor<D>(L, L.ph[p & 1], hd.g, hd.n, invm, rb - RS + Rec<D>::QP);
+            if (w == wfac) hd.prep_tp(rb - RS + Rec<D>::TT, rb - RS + Rec<D>::PT, invn4);
+            if (((p - 1) & 1) == 0) {   // cross factors of an even chunk with the next
+                if (FOUR ? w == 2 : w == 1) {
+                    const float invm = hd.inv_norm_n();
+                    cross_factor<D>(L, L.kh[p & 1], hd.g, hd.n, invm, rb - RS + Rec<D>::QK);
+                    if constexpr (FOUR) cross_factor<D>(L, L.ph[p & 1], hd.g, hd.n, invm, rb - RS + Rec<D>::QP);
+                } else if (!FOUR && w == NA - 1) {
+                    cross_factor<D>(L, L.ph[p & 1], hd.g, hd.n, hd.inv_norm_n(), rb - RS + Rec<D>::QP);
+                }
             }
         }
         hd.stage2(p);
@@ -590,7 +603,7 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     if (c1 > c0) {   // the last chunk's alpha^ and C x C factors
         const f4 invn4 = hd.inv_norms4();
         alpha_out(rb - RS, (c1 - 1) * CH, invn4);
-        if (w == 1) hd.prep_tp(rb - RS + Rec<D>::TT, rb - RS + Rec<D>::PT, invn4);
+        if (w == wfac) hd.prep_tp(rb - RS + Rec<D>::TT, rb - RS + Rec<D>::PT, invn4);
     }
     if (j == S - 1) {
         if (A_out) hd.store_state(st, A_out + bh * DD);
