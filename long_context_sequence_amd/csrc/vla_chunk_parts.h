@@ -222,6 +222,25 @@ struct RawVec {
             }
         });
     }
+    // the same from a buffer view at byte offset `off` (32-bit offsets: no 64-bit
+    // address arithmetic per load; bytes past the view read as 0)
+    __device__ __forceinline__ void load(const Buf &b, unsigned off)
+    {
+        static_assert(N % 2 == 0 && NW % WPL == 0, "whole loads");
+        sfor<NW / WPL>([&](auto i) {
+            const unsigned o = off + 4u * WPL * (unsigned)i;
+            if constexpr (WPL == 4) {
+                const v4u v = __builtin_amdgcn_raw_buffer_load_b128(b.r, o, 0, 0);
+                x[4 * i] = v[0]; x[4 * i + 1] = v[1]; x[4 * i + 2] = v[2]; x[4 * i + 3] = v[3];
+            } else if constexpr (WPL == 2) {
+                typedef unsigned v2u __attribute__((ext_vector_type(2)));
+                const v2u v = __builtin_amdgcn_raw_buffer_load_b64(b.r, o, 0, 0);
+                x[2 * i] = v[0]; x[2 * i + 1] = v[1];
+            } else {
+                x[i] = __builtin_amdgcn_raw_buffer_load_b32(b.r, o, 0, 0);
+            }
+        });
+    }
     __device__ __forceinline__ float get(int i) const
     {
         if constexpr (ES == 4) return __uint_as_float(x[i]);

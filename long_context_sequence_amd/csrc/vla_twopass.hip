@@ -109,17 +109,21 @@ vla_gram(const Tin *__restrict__ k, const Tin *__restrict__ u, int T, int S, int
 #pragma unroll
         for (int r = 0; r < 4; ++r) gacc[t][r] = 0.0;
 
+    const Buf ub(uh, (unsigned)T * D * sizeof(Tin)), kb(kh, (unsigned)T * D * sizeof(Tin));
     auto prefetch = [&](int blk) {
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
             const int t = t0 + blk * GB + 16 * s2 + tl;
-            const unsigned off = (unsigned)(t < t1 ? t : t1 - 1) * D + cc * CPT;
-            ru[s2].load(uh + off);
-            rk[s2].load(kh + off);
+            const unsigned off = ((unsigned)(t < t1 ? t : t1 - 1) * D + cc * CPT) * sizeof(Tin);
+            ru[s2].load(ub, off);
+            rk[s2].load(kb, off);
         }
     };
     auto stage = [&](int blk) {
         float *dst = ut[blk & 1];
+        float zblk[CPT];   // this block's phi(k), four tokens per column in fp32
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) zblk[i] = 0.f;
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
             const bool ok = t0 + blk * GB + 16 * s2 + tl < t1;
@@ -132,9 +136,11 @@ vla_gram(const Tin *__restrict__ k, const Tin *__restrict__ u, int T, int S, int
             for (int i = 0; i < CPT; ++i) dst[(cc * CPT + i) * LT + 16 * s2 + tl] = ru[s2].get(i) * iu;
             if (ok) {
 #pragma unroll
-                for (int i = 0; i < CPT; ++i) zacc[i] += (double)phi_fast(rk[s2].get(i));
+                for (int i = 0; i < CPT; ++i) zblk[i] += phi_fast(rk[s2].get(i));
             }
         }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) zacc[i] += (double)zblk[i];
     };
 
     if (NBK > 0) {
@@ -361,16 +367,16 @@ struct PenStage {
         if constexpr (LPT == 16) return sum_row16(x);
         else return sum_row8(x);
     }
-    // rows past T re-read row T-1 (stage zeroes k^, u^ and phi(k) there)
-    __device__ __forceinline__ void prefetch(const Tin *q, const Tin *k, const Tin *u, size_t tok0,
-                                             int T, int cq)
+    // rows past T re-read row T-1 (stage zeroes k^, u^ and phi(k) there); the
+    // views cover one head's T x d inputs
+    __device__ __forceinline__ void prefetch(const Buf &qb, const Buf &kb, const Buf &ub, int T, int cq)
     {
         if (!on) return;
         const int t = cq * CH + tl;
-        const size_t off = (tok0 + (size_t)(t < T ? t : T - 1)) * D + (size_t)cc * CP;
-        rq.load(q + off);
-        rk.load(k + off);
-        ru.load(u + off);
+        const unsigned off = ((unsigned)(t < T ? t : T - 1) * D + (unsigned)(cc * CP)) * sizeof(Tin);
+        rq.load(qb, off);
+        rk.load(kb, off);
+        ru.load(ub, off);
     }
     __device__ __forceinline__ void stage(PLds<D> &L, int cq, int T, float *rkh, float *rph,
                                           float *kept = nullptr)
@@ -536,11 +542,13 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         else if (zk0)
             hd.zk_run = S > 1 ? zseg[(size_t)bh * S * D + hd.kcol] : zk0[bh * D + hd.kcol];
     }
-    const size_t tok0 = (size_t)bh * T;
+    const size_t hoff = (size_t)bh * T * D;
+    const unsigned hbytes = (unsigned)T * D * sizeof(Tin);
+    const Buf qb(q + hoff, hbytes), kb(k + hoff, hbytes), ub(u + hoff, hbytes);
     float *rb = rec + ((size_t)bh * NC + c0) * RS;   // record of chunk p below
-    ps.prefetch(q, k, u, tok0, T, c0);
+    ps.prefetch(qb, kb, ub, T, c0);
     ps.stage(L, c0, T, rb + Rec<D>::KH, rb + Rec<D>::PH, kept);
-    if (c0 + 1 < c1) ps.prefetch(q, k, u, tok0, T, c0 + 1);
+    if (c0 + 1 < c1) ps.prefetch(qb, kb, ub, T, c0 + 1);
     vmem_drain();
     __syncthreads();
     hd.z_products(st, c0);
@@ -591,7 +599,7 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         hd.stage2(p);
         if (p + 1 < c1) {
             ps.stage(L, p + 1, T, rb + RS + Rec<D>::KH, rb + RS + Rec<D>::PH, kept);
-            if (p + 2 < c1) ps.prefetch(q, k, u, tok0, T, p + 2);
+            if (p + 2 < c1) ps.prefetch(qb, kb, ub, T, p + 2);
         }
         lds_barrier();
         if constexpr (SAVE) wl.tok = p * CH;
