@@ -8,11 +8,11 @@
 // in reverse order, with the conventions stated at vla_backward in
 // include/vla.h.
 //
-// This kernel serves d in {16, 32} (both phases below) and T = 0 at every d
-// (the initial state's gradients are the final state's adjoints).  For d in
-// {64, 96, 128} the two-pass forward (vla_twopass.hip) keeps the per-token
-// records and the reverse sweep runs as two chains side by side
-// (vla_bwd_split.hip).
+// This kernel serves d in {16, 32} (both phases below).  For d in {64, 96, 128}
+// the two-pass forward (vla_twopass.hip) keeps the per-token records and the
+// reverse sweep runs as two chains side by side (vla_bwd_split.hip); T = 0 at
+// every d takes a copy kernel (vla_bwd_empty: the initial state's gradients are
+// the final state's adjoints).
 //
 // One workgroup per head, D * TPR threads: thread (row i, columns [c0, c0+EPT))
 // holds that slice of row i of every d x d matrix, so a matrix-vector product is
@@ -67,19 +67,14 @@ namespace {
 
 using namespace chunk;
 
-// Threads per row (TPR) and where S' lives: every wave repeats the token's
-// scalar work (dot products, norms, the step scalars), so fewer, wider threads
-// cost less issue; the register file bounds how wide.  d <= 32 (both phases):
-// four per row.  For d >= 64 only T = 0 reaches this kernel (no token loop).
+// Threads per row (TPR): every wave repeats the token's scalar work (dot
+// products, norms, the step scalars), so fewer, wider threads cost less issue;
+// four per row at d <= 32, the sizes this kernel serves.  The last wave loads
+// and stages the token vectors.
 template <int D> struct BwdCfg {
-    static constexpr int TPR = D == 96 || D == 64 ? 8 : 4, EPT = D / TPR;
-    static constexpr bool ST_LDS = D == 128;
-    static constexpr int TRP = ST_LDS ? D + 4 : D + 1;   // row pitch of tr
-    // the reverse sweep's loads and staging spread over the waves (d = 96:
-    // 4.3 us per token against 4.9 with the last wave alone; d = 128: 11.4
-    // against 14.5) or, at d <= 64, left to the last wave (d = 64: 1.85 against
-    // 2.66)
-    static constexpr bool SPREAD = D >= 96;
+    static_assert(D <= 32, "d >= 64 runs the split sweep (vla_bwd_split.hip)");
+    static constexpr int TPR = 4, EPT = D / TPR;
+    static constexpr int TRP = D + 1;   // row pitch of tr
 };
 
 
@@ -279,25 +274,14 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
 
     // ------------------------------------------------------------ phase 2
     __syncthreads();
-    // S' rows: through LDS into registers, or (above d = 64) kept there
-    if constexpr (Cf::ST_LDS) {
-        sfor<EPT>([&](auto e) { L.tr[(c0 + e) * P + row] = S[e]; });
-    } else {
-        sfor<EPT>([&](auto e) { L.tr[row * P + c0 + e] = S[e]; });
-    }
+    // S' rows: through LDS into registers
+    sfor<EPT>([&](auto e) { L.tr[row * P + c0 + e] = S[e]; });
     __syncthreads();
-    float St[Cf::ST_LDS ? 1 : EPT], gS[EPT], gSt[EPT];   // S', dS, dS' (row slices)
-    float *st_row = &L.tr[row * P + c0];
-    auto st_get = [&](auto e) -> float {
-        if constexpr (Cf::ST_LDS) return st_row[e];
-        else return St[e];
-    };
-    auto st_set = [&](auto e, float x) {
-        if constexpr (Cf::ST_LDS) st_row[e] = x;
-        else St[e] = x;
-    };
+    float St[EPT], gS[EPT], gSt[EPT];   // S', dS, dS' (row slices)
+    auto st_get = [&](auto e) -> float { return St[e]; };
+    auto st_set = [&](auto e, float x) { St[e] = x; };
     double Sg[EPT];                     // Sigma (row slice)
-    if constexpr (!Cf::ST_LDS) sfor<EPT>([&](auto e) { St[e] = L.tr[(c0 + e) * P + row]; });
+    sfor<EPT>([&](auto e) { St[e] = L.tr[(c0 + e) * P + row]; });
     {
         const size_t off = bh * DD + (size_t)row * D + c0;
         sfor<EPT>([&](auto e) {
@@ -316,31 +300,28 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     // A token's vectors are loaded (raw, a token ahead) and staged into LDS in
     // nine groups: dO; q; k; u; z; alpha^; e; zkey_t; the scalars (also loaded
     // by the k and u groups, for 1/|k|, 1/|u|).  The last wave owns them all
-    // (and alone calls p2_load, p2_stage), or with SPREAD group i is wave
-    // NW - 1 - i mod NW's.
-    auto own = [&](int grp) { return !Cf::SPREAD || w == NW - 1 - grp % NW; };
-    const bool stager = Cf::SPREAD || w == NW - 1;
+    // and alone calls p2_load, p2_stage.
+    const bool stager = w == NW - 1;
     float yg[NV], yz[NV], ya[NV], ye[NV], yw[NV];
     Raw1<Tin> yq[NV], yk[NV], yu[NV];
     f4 ys0, ys1;
-    if constexpr (Cf::SPREAD) ys0 = ys1 = f4{0.f, 0.f, 0.f, 0.f};   // read by every stager
     auto p2_load = [&](int t) {
         const float *rt = rh + (size_t)t * RS;
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
                 const size_t o = (tok0 + t) * D + j;
-                if (own(0)) yg[c] = dO[o];
-                if (own(1)) yq[c].load(q, o);
-                if (own(2)) yk[c].load(k, o);
-                if (own(3)) yu[c].load(u, o);
-                if (own(4)) yz[c] = rt[K::Z + j];
-                if (own(5)) ya[c] = rt[K::AL + j];
-                if (own(6)) ye[c] = rt[K::E + j];
-                if (own(7)) yw[c] = rt[K::ZK + j];
+                yg[c] = dO[o];
+                yq[c].load(q, o);
+                yk[c].load(k, o);
+                yu[c].load(u, o);
+                yz[c] = rt[K::Z + j];
+                ya[c] = rt[K::AL + j];
+                ye[c] = rt[K::E + j];
+                yw[c] = rt[K::ZK + j];
             }
         });
-        if (own(2) || own(3) || own(8)) {
+        {
             ys0 = ld4(rt + K::SC);
             ys1 = ld4(rt + K::SC + 4);
         }
@@ -350,25 +331,25 @@ vla_bwd(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         sfor<NV>([&](auto c) {
             const int j = lane + 64 * c;
             if (j < D) {
-                if (own(0)) L.g[slot][j] = yg[c];
-                if (own(1)) {
+                L.g[slot][j] = yg[c];
+                {
                     const float qj = yq[c].get();
                     L.pq[slot][j] = phi_fast(qj);
                     L.dpq[slot][j] = dphi(qj);
                 }
-                if (own(2)) {
+                {
                     const float kj = yk[c].get();
                     L.kh[slot][j] = kj * ik;
                     L.dpk[slot][j] = dphi(kj);
                 }
-                if (own(3)) L.uh[slot][j] = yu[c].get() * iu;
-                if (own(4)) L.z[slot][j] = yz[c];
-                if (own(5)) L.al[slot][j] = ya[c];
-                if (own(6)) L.e[slot][j] = ye[c];
-                if (own(7)) L.zt[slot][j] = yw[c];
+                L.uh[slot][j] = yu[c].get() * iu;
+                L.z[slot][j] = yz[c];
+                L.al[slot][j] = ya[c];
+                L.e[slot][j] = ye[c];
+                L.zt[slot][j] = yw[c];
             }
         });
-        if (own(8) && lane == 0) {
+        if (lane == 0) {
             st4(&L.sc[slot][0], ys0);
             st4(&L.sc[slot][4], ys1);
         }
@@ -581,10 +562,38 @@ BwdPlan bwd_plan(int BH, int T, int d)
     return p;
 }
 
+// T = 0: no token to go through, so the initial state's gradients are the final
+// state's adjoints, dA0 symmetrised as (G + G')/2 (A_0 is a symmetric matrix);
+// missing adjoints are zero.  A grid-stride pass over the B H d^2 entries.
+__global__ void __launch_bounds__(256)
+vla_bwd_empty(int BH, int D, const float *dS_T, const float *dA_T, const float *dzk_T, float *dS0,
+              float *dA0, float *dzk0)
+{
+    const size_t DD = (size_t)D * D, n = (size_t)BH * DD;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (size_t)gridDim.x * blockDim.x) {
+        if (dS0) dS0[e] = dS_T ? dS_T[e] : 0.f;
+        if (dA0) {
+            const size_t h = e / DD, r = e % DD, i = r / D, j = r % D;
+            dA0[e] = dA_T ? (float)(0.5 * ((double)dA_T[e] + (double)dA_T[h * DD + j * D + i])) : 0.f;
+        }
+        if (dzk0 && e < (size_t)BH * D) dzk0[e] = dzk_T ? dzk_T[e] : 0.f;
+    }
+}
+
+hipError_t launch_empty(const BwdArgs &a)
+{
+    const size_t n = (size_t)a.B * a.H * a.d * a.d;
+    const unsigned blocks = (unsigned)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+    hipLaunchKernelGGL(vla_bwd_empty, dim3(blocks), dim3(256), 0, a.stream, a.B * a.H, a.d, a.dS_T, a.dA_T,
+                       a.dzk_T, a.dS0, a.dA0, a.dzk0);
+    return hipGetLastError();
+}
+
 // both phases in the one kernel (per-token forward, then the reverse sweep)
 template <int D, typename Tin>
 hipError_t launch_phase1(const BwdArgs &a, dim3 grid, dim3 block, float *rec)
 {
+    static_assert(!records_from_forward(D), "phase 1 serves d in {16, 32}");
     hipLaunchKernelGGL((vla_bwd<D, Tin>), grid, block, 0, a.stream, (const Tin *)a.q,
                        (const Tin *)a.k, (const Tin *)a.v, (const Tin *)a.u, a.T, a.lambda0, a.eps,
                        a.S0, a.A0, a.zk0, a.dO, a.dS_T, a.dA_T, a.dzk_T, a.dq, a.dk, a.dv, a.du,
@@ -599,9 +608,8 @@ hipError_t launch(const BwdArgs &a)
     const BwdPlan p = bwd_plan(BH, a.T, D);
     char *ws = static_cast<char *>(a.ws);
     float *rec = reinterpret_cast<float *>(ws + p.rec);
-    const dim3 grid(BH), block(D * BwdCfg<D>::TPR);
+    if (a.T <= 0) return launch_empty(a);
     if constexpr (records_from_forward(D)) {
-        if (a.T <= 0) return launch_phase1<D, Tin>(a, grid, block, rec);
         // the forward on the matrix-core kernels, keeping the per-token records;
         // its o goes to dq (overwritten below), its final state to the workspace
         float *stS = reinterpret_cast<float *>(ws + p.st), *stA = stS + (size_t)BH * D * D;
@@ -618,7 +626,7 @@ hipError_t launch(const BwdArgs &a)
                                      reinterpret_cast<int *>(ws + p.sync),
                                      reinterpret_cast<float *>(ws + p.qb));
     } else {
-        return launch_phase1<D, Tin>(a, grid, block, rec);
+        return launch_phase1<D, Tin>(a, dim3(BH), dim3(D * BwdCfg<D>::TPR), rec);
     }
 }
 

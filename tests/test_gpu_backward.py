@@ -178,12 +178,13 @@ def test_backward_degenerate_tokens(d):
     assert np.all(got["du"][:, :, 7] == 0.0)
 
 
-def test_backward_empty_sequence():
+@pytest.mark.parametrize("d", [16, 32, 64, 96, 128])
+def test_backward_empty_sequence(d):
     """T = 0: the initial state's gradients are the final state's adjoints
-    (dA0 symmetrised)."""
+    (dA0 symmetrised), at every head size; a missing adjoint gives zeros."""
     dev = _dev()
     vla = _vla()
-    B, H, d = 1, 2, 64
+    B, H = 1, 3
     e = torch.empty((B, H, 0, d), device=dev)
     dS = torch.randn(B, H, d, d, device=dev)
     dA = torch.randn(B, H, d, d, device=dev)
@@ -191,8 +192,14 @@ def test_backward_empty_sequence():
     out = vla.vla_backward(e, e, e, e, e, 0.1, 1e-4, dS_T=dS, dA_T=dA, dzkey_T=dz)
     torch.cuda.synchronize()
     assert torch.equal(out[4], dS)
-    assert torch.allclose(out[5], 0.5 * (dA + dA.transpose(-1, -2)), rtol=0, atol=0)
+    ref = (0.5 * (dA.double() + dA.double().transpose(-1, -2))).float()
+    assert torch.equal(out[5], ref)
     assert torch.equal(out[6], dz)
+    out = vla.vla_backward(e, e, e, e, e, 0.1, 1e-4, dA_T=dA)
+    torch.cuda.synchronize()
+    assert torch.equal(out[4], torch.zeros_like(dS))
+    assert torch.equal(out[5], ref)
+    assert torch.equal(out[6], torch.zeros_like(dz))
 
 
 def test_backward_deterministic():
