@@ -51,11 +51,17 @@ using rec::Rec;
 using rec::Keep;   // the per-token records kept for the gradients
 
 // Value blocks per memory workgroup and the ways each block's key tiles are
-// split over its waves (VBW x KS waves per workgroup).
+// split over its waves (VBW x KS waves per workgroup).  The stages of a
+// workgroup fill most of the LDS, so one workgroup runs per compute unit; the
+// splits are chosen so that the B H (d / 16) / VBW workgroups fit one round
+// on 256 compute units at the workloads' head counts (d = 96: 128 heads x 2;
+// d = 128: 64 heads x 4), since a second round would run the whole chain
+// again: at d = 128 four value blocks of one key split each in two rounds
+// took 8.7 ms, two blocks of two key splits in one round 4.8 ms.
 template <int D> struct MemCfg;
 template <> struct MemCfg<64> { static constexpr int VBW = 2, KS = 2; };
-template <> struct MemCfg<96> { static constexpr int VBW = 2, KS = 2; };
-template <> struct MemCfg<128> { static constexpr int VBW = 1, KS = 4; };
+template <> struct MemCfg<96> { static constexpr int VBW = 3, KS = 2; };
+template <> struct MemCfg<128> { static constexpr int VBW = 2, KS = 2; };
 
 // ------------------------------------------------------------------- gram
 // Workgroup (head, segment j < S - 1, part pp < P): the part's share of
@@ -635,7 +641,6 @@ struct MemStage {
     static constexpr int NIW = NI / NW;                        // per wave
     static constexpr int VOFF = 256 * (NI - NV);               // v, in floats from the stage start
     static constexpr int SIZE = 256 * NI;                      // floats per stage
-    static constexpr int LPT = ROWB / 16, TPI = 64 / LPT;      // lanes per token, tokens per piece
     static constexpr int NS = 3 * SIZE * 4 + 2 * NW * 4096 <= 160 * 1024 ? 3 : 2;   // stages
     static_assert(NV * 1024 == 32 * ROWB && 2 * SIZE * 4 + 2 * NW * 4096 <= 160 * 1024, "LDS");
 };
@@ -691,9 +696,23 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
     constexpr int NB = D / 16, VBW = MS::VBW, KS = MS::KS, NW = MS::NW, NT = NB / KS;
     constexpr int NG = NB / VBW, RS = R::SIZE, NS = MS::NS, NIW = MS::NIW;
     static_assert(NT * KS == NB && NG * VBW == NB && KS >= 2, "block split");
-    __shared__ __align__(16) float stg0[MS::SIZE];
-    __shared__ __align__(16) float stg1[MS::SIZE];
-    __shared__ __align__(16) float stg2[NS == 3 ? MS::SIZE : 4];
+    // the stages: three separate arrays, or two with no third allocated (at
+    // d = 128 with fp32 inputs the two fill the LDS to the byte)
+    float *stg[3];
+    if constexpr (NS == 3) {
+        __shared__ __align__(16) float stg0[MS::SIZE];
+        __shared__ __align__(16) float stg1[MS::SIZE];
+        __shared__ __align__(16) float stg2[MS::SIZE];
+        stg[0] = stg0;
+        stg[1] = stg1;
+        stg[2] = stg2;
+    } else {
+        __shared__ __align__(16) float stg0[MS::SIZE];
+        __shared__ __align__(16) float stg1[MS::SIZE];
+        stg[0] = stg0;
+        stg[1] = stg1;
+        stg[2] = stg0;
+    }
     __shared__ __align__(16) float red[2][NW][4][256];   // per step parity and wave: partials
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
@@ -741,9 +760,11 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
             rbuf.lds16(s + 256 * j, (unsigned)(1024 * j + 16 * lane), (unsigned)pm * 2 * RS * 4);
         };
         auto vpiece = [&](int j) {
-            const int tp = (j - NRP) * MS::TPI + lane / MS::LPT;   // token in the pair
-            const unsigned off = ((unsigned)(32 * pm + tp) * D + 16 * VBW * vg) * sizeof(Tin) +
-                                 16 * (lane % MS::LPT);
+            // byte b of the pair's v slice (tokens of ROWB bytes back to back; a
+            // 16-byte granule never straddles two tokens, ROWB being a multiple of 16)
+            const unsigned b = 1024u * (unsigned)(j - NRP) + 16u * (unsigned)lane;
+            const unsigned tp = b / MS::ROWB, cb = b % MS::ROWB;   // token in the pair, byte in its row
+            const unsigned off = ((32u * (unsigned)pm + tp) * D + 16u * VBW * (unsigned)vg) * sizeof(Tin) + cb;
             vbuf.lds16(s + 256 * j, off);
         };
         sfor<decltype(I1)::value - decltype(I0)::value>([&](auto i0) {
@@ -887,26 +908,26 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
         cy = Carry{ea, eb, ma.pa, mb.pa, qp, ks == 0 ? ma.rd : mb.rd};
     };
 
-    stage_pair(0, stg0);
-    stage_pair(1, stg1);
-    if constexpr (NS == 3) stage_pair(2, stg2);
+    stage_pair(0, stg[0]);
+    stage_pair(1, stg[1]);
+    if constexpr (NS == 3) stage_pair(2, stg[NS - 1]);
     vm_wait<0>();
     lds_barrier();
     int pm = 0;
     if constexpr (NS == 3) {
         for (; pm + 3 <= NP; pm += 3) {
-            step2(pm, stg0);
-            step2(pm + 1, stg1);
-            step2(pm + 2, stg2);
+            step2(pm, stg[0]);
+            step2(pm + 1, stg[1]);
+            step2(pm + 2, stg[NS - 1]);
         }
-        if (pm < NP) step2(pm, stg0);
-        if (pm + 1 < NP) step2(pm + 1, stg1);
+        if (pm < NP) step2(pm, stg[0]);
+        if (pm + 1 < NP) step2(pm + 1, stg[1]);
     } else {
         for (; pm + 2 <= NP; pm += 2) {
-            step2(pm, stg0);
-            step2(pm + 1, stg1);
+            step2(pm, stg[0]);
+            step2(pm + 1, stg[1]);
         }
-        if (pm < NP) step2(pm, stg0);
+        if (pm < NP) step2(pm, stg[0]);
     }
     if (NP > 0) {   // the readout of the last pair
         lds_barrier();
@@ -914,7 +935,7 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
     }
     if (NC & 1) {   // the last chunk alone (staged as pair NP)
         const int c = NC - 1, sl = NP & 1, k = NP % NS;
-        const float *s = k == 0 ? stg0 : (k == 1 ? stg1 : stg2);
+        const float *s = stg[k];
         MemOps<NT> m;
         ops(s, 0, m);
         if constexpr (!LIN) st4(&red[sl][w][0][lane * 4], sk_part(m.ak));
