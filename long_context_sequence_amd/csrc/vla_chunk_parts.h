@@ -40,6 +40,7 @@
 // of the unit triangular factors are computed four columns at a time, one per
 // lane group.
 #pragma once
+#include <type_traits>
 #include <utility>
 
 #include "vla_common.h"
@@ -294,7 +295,9 @@ struct WToLds {
         if (n == 0) st4(&L.nrm[wi][4 * g], nr);
     }
     // z_t = A_{t-1} u^_t of the chunk's tokens 4g + r at keys 16b + n, and
-    // 1/delta_t: nothing to do here (a sink that keeps them overrides this)
+    // 1/delta_t: nothing to do here (a sink that keeps them overrides this and
+    // sets KEEPS_Z, so that the downdate forms them)
+    static constexpr bool KEEPS_Z = false;
     __device__ __forceinline__ void zcols(int, f4, f4) {}
 };
 
@@ -451,7 +454,12 @@ struct Head {
 
     // Wave 0: factorise I + G = L D L' from the waves' partials and leave L^-1
     // (both ways round in L.lit[0]), 1/d (L.inv[0]) and the A operand of W',
-    // -(D^-1 L^-1 U^'Y0) o Up (L.hms), in LDS.
+    // H = -(D^-1 L^-1 U^'Y0) o Up (L.hms), in LDS.  With EXPL, the two C x C
+    // matrices the downdate applies to Z0' are formed here once instead:
+    // M = -(I + G)^-1 = -L^-T D^-1 L^-1 (L.mx) and H' L^-1 (L.hms), each as the
+    // A operand a lane needs with the contraction index 4 g + c, so that every
+    // wave takes two products per block in place of three.
+    template <bool EXPL>
     __device__ __forceinline__ void factorize()
     {
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -511,33 +519,58 @@ struct Head {
         const f4 inv4 = ld4(&L.inv[0][4 * g]);
         f4 hm = mma4(X, gub, zero);
         sfor<4>([&](auto r) { hm[int(r)] = 4 * g + r <= n ? -(hm[int(r)] * inv4[int(r)]) : 0.f; });
-        st4(&L.hms[4 * (16 * g + n)], hm);
+        if constexpr (EXPL) {
+            // register c of lane 16 g + n: L^-1 [4g+c][n]
+            const f4 lit = ld4(&L.lit[0][n * LT + 4 * g]);
+            // (H' L^-1)' = L^-T H: register c of lane 16 g + n is (H' L^-1)[n][4g+c]
+            st4(&L.hms[4 * (16 * g + n)], mma4(lit, hm, zero));
+            // M[4g+c][n], read as M[n][4g+c] (M is symmetric)
+            st4(&L.mx[4 * (16 * g + n)], mma4(lit * -inv4, lit, zero));
+        } else {
+            st4(&L.hms[4 * (16 * g + n)], hm);
+        }
     }
 
     // After the factorisation of chunk cq: W' (to `wout`), the downdate
     // As <- As - Z0 (I + G)^-1 Z0' of the own blocks, the |w|^2 partials, and
     // this wave's partials of W'K^ and W'Phi (unnormalised alpha^, rows t of
     // its blocks' keys) into L.nq.
+    // With a sink that keeps z_t, the products go through L^-1 Z0' (whose rows
+    // are the z_t); otherwise through M and H' L^-1 from factorize<true>.
     template <class WOut>
     __device__ __forceinline__ void downdate(State &st, int cq, const f4 (&y)[BPW], WOut &&wout)
     {
+        constexpr bool EXPL = !std::decay_t<WOut>::KEEPS_Z;
         const f4 zero = {0.f, 0.f, 0.f, 0.f};
         const float *z0t = L.z0t[cq & 1];
         float X[4];
-        sfor<4>([&](auto c) { X[c] = L.lit[0][(4 * c + g) * LT + n]; });   // L^-1 [n][4c+g]
-        const f4 inv4 = ld4(&L.inv[0][4 * g]);                          // 1 / d_{4g+r}
-        const f4 lit = ld4(&L.lit[0][n * LT + 4 * g]);                  // L^-1 [4g+r][n]
-        const f4 hm = ld4(&L.hms[4 * (16 * g + n)]);
+        f4 inv4, lit, hm;
+        if constexpr (EXPL) {
+            lit = ld4(&L.mx[4 * (16 * g + n)]);    // M [n][4g+c]
+            hm = ld4(&L.hms[4 * (16 * g + n)]);    // (H' L^-1) [n][4g+c]
+        } else {
+            sfor<4>([&](auto c) { X[c] = L.lit[0][(4 * c + g) * LT + n]; });   // L^-1 [n][4c+g]
+            inv4 = ld4(&L.inv[0][4 * g]);                          // 1 / d_{4g+r}
+            lit = ld4(&L.lit[0][n * LT + 4 * g]);                  // L^-1 [4g+r][n]
+            hm = ld4(&L.hms[4 * (16 * g + n)]);
+        }
         f4 nr = zero;
         sfor<BPW>([&](auto bb) {
             const int b = wi * BPW + bb;
-            float zb[4];   // Z0'[4c+g][16b+n]
-            sfor<4>([&](auto c) { zb[c] = z0t[(16 * b + n) * LT + 4 * c + g]; });
-            const f4 q2 = mma4(X, zb, zero);        // L^-1 Z0': row t is z_t
-            const f4 q1 = q2 * -inv4;               // -D^-1 L^-1 Z0' (the sign rides on the multiply)
-            const f4 nx = mma4(lit, q1, zero);      // -(I + G)^-1 Z0'
-            const f4 wt = mma4(hm, q2, y[bb]);      // W'
-            wout.zcols(b, q2, inv4);
+            f4 nx, wt;
+            if constexpr (EXPL) {
+                const f4 zb = ld4(&z0t[(16 * b + n) * LT + 4 * g]);   // Z0'[4g+c][16b+n]
+                nx = mma4(lit, zb, zero);           // -(I + G)^-1 Z0'
+                wt = mma4(hm, zb, y[bb]);           // W'
+            } else {
+                float zb[4];   // Z0'[4c+g][16b+n]
+                sfor<4>([&](auto c) { zb[c] = z0t[(16 * b + n) * LT + 4 * c + g]; });
+                const f4 q2 = mma4(X, zb, zero);    // L^-1 Z0': row t is z_t
+                const f4 q1 = q2 * -inv4;           // -D^-1 L^-1 Z0' (the sign rides on the multiply)
+                nx = mma4(lit, q1, zero);           // -(I + G)^-1 Z0'
+                wt = mma4(hm, q2, y[bb]);           // W'
+                wout.zcols(b, q2, inv4);
+            }
             f4 az[NB];
             sfor<NB>([&](auto rho) { az[rho] = ld4(&z0t[(16 * rho + n) * LT + 4 * g]); });
             sfor<4>([&](auto r) {      // As <- As - Z0 (I + G)^-1 Z0'

@@ -334,6 +334,7 @@ struct PLds {
     };
     float inv[NA][C];
     float hms[256];          // A operand of W' (per lane), from wave 0
+    float mx[256];           // A operand of -(I + G)^-1 (per lane), from wave 0
     float wt[D * LT];        // W [i][token] of the last updated chunk
     float z0t[2][D * LT];    // Z0 [i][token], by chunk parity
     float uh[C * LD];        // u^ [token][i] of the chunk whose Z0 is formed next
@@ -451,6 +452,7 @@ struct PenStage {
 // (rows of L^-1 Z0' and the pivots of I + G) in the per-token records.
 template <int D>
 struct KeepW : WToLds<D, PLds<D>> {
+    static constexpr bool KEEPS_Z = true;
     float *kept;   // this head's per-token records
     int tok, T;    // first token of the chunk, tokens
     __device__ __forceinline__ void zcols(int b, f4 q2, f4 inv4)
@@ -587,7 +589,7 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     for (int p = c0; p < c1; ++p, rb += RS) {
         f4 y[BPW];
         hd.y_products(st, p, y);
-        if (w == 0) hd.factorize();
+        if (w == 0) hd.template factorize<!SAVE>();
         if (p > c0) {
             const f4 invn4 = hd.inv_norms4();
             alpha_out(rb - RS, (p - 1) * CH, invn4);
