@@ -304,7 +304,7 @@ struct WToLds {
 // Per-thread view of one head's penalty chain: lane coordinates and the steps.
 // A wave with chain index wi owns column blocks wi*BPW + bb; LdsT is the
 // workgroup's LDS layout (members uh, kh, ph, zk, z0t, wt, gp, nrm, nq,
-// lit/tit, inv, hms).
+// lit/tit, inv, hms, mx).
 //
 // A chunk takes two phases, each ended by a workgroup barrier:
 //   factorisation phase   every wave: Y0 = A K^ (y_products); wave 0:
