@@ -91,7 +91,7 @@ __device__ __forceinline__ f4 ctc(const float *al, const float *y, int g, int n)
 // (I + N)^-1 from N (accumulator layout; only c < t is used) to the record's
 // transposed layout at tt, by back substitution four columns at a time (one
 // wave, its scratch nt).
-__device__ __forceinline__ void tinv_out(f4 nx, int g, int n, float *nt, float *tt)
+__device__ __forceinline__ void tinv_out(f4 nx, int g, int n, float *nt, float *tt, float (&X)[4])
 {
     constexpr int LT = CH + 4;
     sfor<4>([&](auto r) { nt[(4 * g + r) * LT + n] = 4 * g + r < n ? -nx[int(r)] : 0.f; });
@@ -101,7 +101,6 @@ __device__ __forceinline__ void tinv_out(f4 nx, int g, int n, float *nt, float *
         const f4 a = ld4(&nt[n * LT + 4 * q4]);
         sfor<4>([&](auto r) { NNr[4 * q4 + r] = a[int(r)]; });
     });
-    float X[4];
     sfor<4>([&](auto c) { X[c] = n == 4 * c + g ? 1.f : 0.f; });
     asm volatile(VLA_TINV_BLOCK
                  : "+v"(X[0]), "+v"(X[1]), "+v"(X[2]), "+v"(X[3])
@@ -203,12 +202,19 @@ vla_bl_prep(const Tin *__restrict__ q, const Tin *__restrict__ k, int T, int NG,
     };
     const f4 eye4 = {n == 4 * g ? 1.f : 0.f, n == 4 * g + 1 ? 1.f : 0.f, n == 4 * g + 2 ? 1.f : 0.f,
                      n == 4 * g + 3 ? 1.f : 0.f};
-    // the C x C factors of chunk c in slot s: (I + N)^-1 (wave wt) and P (wave wp)
-    auto factors = [&](int c, int s, int wt, int wp) {
+    // the C x C factors of chunk c in slot s: (I + N)^-1 (wave wt) and P (wave wp);
+    // with ydst (DeltaNet, chunk b of a pair), wave wt also leaves the pair's key
+    // cross factor solved by chunk b's triangle (its scratch and wave wt + 1's)
+    auto factors = [&](int c, int s, int wt, int wp, float *ydst = nullptr) {
         float *rc = rh + (size_t)c * RS;
         if (w == wt) {
-            if constexpr (DELTA) tinv_out(ctc<D>(L.al[s], L.kh[s], g, n), g, n, L.nt[w], rc + R::TT);
-            else st4(&rc[R::TT + swz16(n, g)], eye4);
+            if constexpr (DELTA) {
+                float X[4];
+                tinv_out(ctc<D>(L.al[s], L.kh[s], g, n), g, n, L.nt[w], rc + R::TT, X);
+                if (ydst) solved_cross(ctc<D>(L.al[0], L.kh[1], g, n), X, g, n, L.nt[w], L.nt[w + 1], ydst);
+            } else {
+                st4(&rc[R::TT + swz16(n, g)], eye4);
+            }
         }
         if (w == wp) {
             f4 p = ctc<D>(L.al[s], L.ph[s], g, n);
@@ -228,12 +234,9 @@ vla_bl_prep(const Tin *__restrict__ q, const Tin *__restrict__ k, int T, int NG,
         if (pair) alpha_out(c + 1, 1);
         factors(c, 0, 0, 1);
         if (pair) {
-            factors(c + 1, 1, 2, 3);
             float *rc = rh + (size_t)c * RS;
-            if (w == 0) {   // Alpha^_a'K^_b (0 for linear attention)
-                const f4 x = DELTA ? ctc<D>(L.al[0], L.kh[1], g, n) : f4{0.f, 0.f, 0.f, 0.f};
-                st4(&rc[R::QK + swz16(n, g)], x);
-            }
+            factors(c + 1, 1, 2, 3, rc + R::QK);
+            if (!DELTA && w == 0) st4(&rc[R::QK + swz16(n, g)], f4{0.f, 0.f, 0.f, 0.f});   // unused
             if (w == 1) st4(&rc[R::QP + swz16(n, g)], ctc<D>(L.al[0], L.ph[1], g, n));
         }
         __syncthreads();

@@ -279,6 +279,28 @@ __device__ __forceinline__ constexpr int swz16(int i, int c4) { return 16 * i + 
 template <int D>
 __device__ __forceinline__ constexpr int swzd(int t, int c4) { return D * t + 4 * (c4 ^ (t & 7)); }
 
+// The key cross factor of a pair of chunks (a, b) as the memory pass applies it:
+// there E_b' = T_b'(V_b - S K^_b)' - T_b'(Alpha^_a'K^_b)' E_a', with T_b =
+// (I + N_b)^-1, so the record holds Y = -T_b'(Alpha^_a'K^_b)' and the product
+// with E_a' is the only one that waits for E_a.  q: register r of lane 16 g + n
+// holds (Alpha^_a'K^_b)[4g+r][n] (a 16 x 16 product's result); xi[c]: row n of
+// column 4c+g of T_b (as the triangular inverse leaves it).  Y goes to dst as
+// the record's 16-column layout stores it; s1, s2: C x (C + 4) LDS scratch.
+__device__ __forceinline__ void solved_cross(f4 q, const float (&xi)[4], int g, int n, float *s1,
+                                             float *s2, float *dst)
+{
+    constexpr int LT = 16 + 4;
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    sfor<4>([&](auto r) { s1[(4 * g + r) * LT + n] = -q[int(r)]; });   // -(Alpha^_a'K^_b), row-major
+    sfor<4>([&](auto c) { s2[n * LT + 4 * c + g] = xi[c]; });          // T_b, row-major
+    wave_lds_order();
+    const f4 a = ld4(&s1[n * LT + 4 * g]);
+    f4 b;
+    sfor<4>([&](auto r) { b[int(r)] = s2[(4 * g + r) * LT + n]; });
+    // register r of lane 16 g + n: (-(Alpha^_a'K^_b) T_b)[4g+r][n] = Y[n][4g+r]
+    st4(&dst[swz16(n, g)], mma4(a, b, zero));
+}
+
 // Where the penalty chain leaves W' (key-major: W[i][token]) and the |w|^2
 // partials of a chunk: in LDS.
 template <int D, typename LdsT>
@@ -602,7 +624,10 @@ struct Head {
     // (Alpha^'Phi) o Up, each stored transposed (X'[m][t] = X[t][m], rows as
     // swz16 places them), so that lane 16 g + n reads X[4 g + r][n] as four
     // consecutive floats at swz16(n, g).  One wave computes them.
-    __device__ __forceinline__ void prep_tp(float *tt, float *pt, f4 invn4)
+    // With ydst, also the solved key cross factor of the pair (previous chunk,
+    // this one) from qk, the previous chunk's Alpha^'K^ (solved_cross; wave wi + 1's
+    // scratch, unused otherwise).
+    __device__ __forceinline__ void prep_tp(float *tt, float *pt, f4 invn4, f4 qk = {}, float *ydst = nullptr)
     {
         float NNr[16];
         f4 qa;
@@ -631,6 +656,7 @@ struct Head {
                        "v"(NNr[6]), "v"(NNr[7]), "v"(NNr[8]), "v"(NNr[9]), "v"(NNr[10]),
                        "v"(NNr[11]), "v"(NNr[12]), "v"(NNr[13]), "v"(NNr[14]), "v"(NNr[15]));
         sfor<4>([&](auto c) { tt[swz16(4 * c + g, n >> 2) + (n & 3)] = X[c]; });   // column 4c+g of (I+N)^-1
+        if (ydst) solved_cross(qk, X, g, n, L.tit[wi], L.tit[wi + 1], ydst);
     }
 
 };

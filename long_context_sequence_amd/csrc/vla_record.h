@@ -19,8 +19,9 @@ struct Rec {
     static constexpr int AH = 0;              // alpha^ [key][token]
     static constexpr int TT = D * CH;         // (I + N)^-1, transposed
     static constexpr int PT = TT + CH * CH;   // (Alpha^'Phi) o Up, transposed
-    // even chunks c with a chunk c + 1: the cross factors Alpha^_c' K^_{c+1} and
-    // Alpha^_c' Phi_{c+1}, transposed (unset otherwise)
+    // even chunks c with a chunk c + 1: the key cross factor solved by the next
+    // chunk's triangle, -(Alpha^_c' K^_{c+1}) (I + N_{c+1})^-1, and the readout
+    // cross factor Alpha^_c' Phi_{c+1}, transposed (unset otherwise)
     static constexpr int QK = PT + CH * CH;
     static constexpr int QP = QK + CH * CH;
     static constexpr int RD = QP + CH * CH;   // 1 / den per token

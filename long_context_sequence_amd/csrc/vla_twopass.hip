@@ -469,13 +469,12 @@ struct KeepW : WToLds<D, PLds<D>> {
     }
 };
 
-// X' for X = Alpha^'Y (C x C) with Alpha^ = W diag(1/|w|) of the last updated
-// chunk (W [i][token] and the |w|^2 partials in LDS) and Y (C x d, token-major in
-// LDS, row stride LD) of the next one: dst[swz16(n, g) + r] = X[4 g + r][n].  One
-// wave.
+// X = Alpha^'Y (C x C) with Alpha^ = W diag(1/|w|) of the last updated chunk
+// (W [i][token] and the |w|^2 partials in LDS) and Y (C x d, token-major in LDS,
+// row stride LD) of the next one: register r of lane 16 g + n holds X[4 g + r][n]
+// (stored as is, st4 at swz16(n, g), the record holds X').  One wave.
 template <int D>
-__device__ __forceinline__ void cross_factor(const PLds<D> &L, const float *y, int g, int n, float invm,
-                                             float *dst)
+__device__ __forceinline__ f4 cross_factor(const PLds<D> &L, const float *y, int g, int n, float invm)
 {
     constexpr int NB = D / 16, LD = Cfg<D>::LD, LT = Cfg<D>::LT;
     f4 x = {0.f, 0.f, 0.f, 0.f};
@@ -484,7 +483,7 @@ __device__ __forceinline__ void cross_factor(const PLds<D> &L, const float *y, i
         sfor<4>([&](auto r) { aw[int(r)] = L.wt[(16 * b + 4 * g + r) * LT + n] * invm; });
         x = mma4(aw, ld4(&y[n * LD + 16 * b + 4 * g]), x);
     });
-    st4(&dst[swz16(n, g)], x);
+    return x;
 }
 
 // Workgroup (head, segment j): the penalty chain over chunks [j SC, (j+1) SC)
@@ -586,6 +585,17 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
             }
         });
     };
+    // Alpha^'K^ of an even chunk with the next, kept by wave wfac until the
+    // next chunk's (I + N)^-1 exists; the record gets it solved (solved_cross)
+    f4 qk = {0.f, 0.f, 0.f, 0.f};
+    // the C x C factors of chunk c (record at rc), with the solved key cross
+    // factor of the pair (c - 1, c) when chunk c - 1 is an even chunk of the segment
+    auto factors = [&](float *rc, int c, f4 invn4) {
+        if (w == wfac) {
+            const bool pair = c - 1 >= c0 && ((c - 1) & 1) == 0;
+            hd.prep_tp(rc + Rec<D>::TT, rc + Rec<D>::PT, invn4, qk, pair ? rc - RS + Rec<D>::QK : nullptr);
+        }
+    };
     for (int p = c0; p < c1; ++p, rb += RS) {
         f4 y[BPW];
         hd.y_products(st, p, y);
@@ -593,14 +603,17 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
         if (p > c0) {
             const f4 invn4 = hd.inv_norms4();
             alpha_out(rb - RS, (p - 1) * CH, invn4);
-            if (w == wfac) hd.prep_tp(rb - RS + Rec<D>::TT, rb - RS + Rec<D>::PT, invn4);
+            factors(rb - RS, p - 1, invn4);
             if (((p - 1) & 1) == 0) {   // cross factors of an even chunk with the next
-                if (FOUR ? w == 2 : w == 1) {
+                if (FOUR ? w == 2 : w == 1) {   // wave wfac
                     const float invm = hd.inv_norm_n();
-                    cross_factor<D>(L, L.kh[p & 1], hd.g, hd.n, invm, rb - RS + Rec<D>::QK);
-                    if constexpr (FOUR) cross_factor<D>(L, L.ph[p & 1], hd.g, hd.n, invm, rb - RS + Rec<D>::QP);
+                    qk = cross_factor<D>(L, L.kh[p & 1], hd.g, hd.n, invm);
+                    if constexpr (FOUR)
+                        st4(&(rb - RS + Rec<D>::QP)[swz16(hd.n, hd.g)],
+                            cross_factor<D>(L, L.ph[p & 1], hd.g, hd.n, invm));
                 } else if (!FOUR && w == NA - 1) {
-                    cross_factor<D>(L, L.ph[p & 1], hd.g, hd.n, hd.inv_norm_n(), rb - RS + Rec<D>::QP);
+                    st4(&(rb - RS + Rec<D>::QP)[swz16(hd.n, hd.g)],
+                        cross_factor<D>(L, L.ph[p & 1], hd.g, hd.n, hd.inv_norm_n()));
                 }
             }
         }
@@ -619,7 +632,7 @@ vla_pen(const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restr
     if (c1 > c0) {   // the last chunk's alpha^ and C x C factors
         const f4 invn4 = hd.inv_norms4();
         alpha_out(rb - RS, (c1 - 1) * CH, invn4);
-        if (w == wfac) hd.prep_tp(rb - RS + Rec<D>::TT, rb - RS + Rec<D>::PT, invn4);
+        factors(rb - RS, c1 - 1, invn4);
     }
     if (j == S - 1) {
         if (A_out) hd.store_state(st, A_out + bh * DD);
@@ -667,7 +680,9 @@ struct MemOps {
 //   partials of the own key tiles -> LDS                           | barrier
 //   sum the KS partials (same order in every wave);
 //   E_a' = T_a'(V_a - S K^_a)';
-//   E_b' = T_b'(V_b - S K^_b - E_a Alpha^_a'K^_b)'   (S after a, applied to K^_b);
+//   E_b' = T_b'(V_b - S K^_b - E_a Alpha^_a'K^_b)'   (S after a, applied to K^_b),
+//   formed as T_b'(V_b - S K^_b)' + X_ab' E_a' with the record's solved cross
+//   factor X_ab = -(Alpha^_a'K^_b) T_b, so only the last product waits for E_a;
 //   key split 0: o_a = (S Phi_a + E_a P_a) / den, key split 1:
 //   o_b = (S Phi_b + E_a Alpha^_a'Phi_b + E_b P_b) / den  (value x token, so
 //   that a lane stores four consecutive values of one token; formed in the
@@ -890,11 +905,14 @@ vla_mem(const Tin *__restrict__ v, int T, int BH, const float *__restrict__ rec,
         wait_next();
         lds_barrier();
         stage_part(ic<0>{}, pm + NS, s);
+        // T_b'(V_b - S K^_b)' does not wait for E_a; the record's key cross
+        // factor is already solved (Y = -T_b'(Alpha^_a'K^_b)')
+        const f4 xb = LIN ? zero : errors(mb, reduce(sl, 1));
         const f4 ea = LIN ? values(ma) : errors(ma, reduce(sl, 0));
         stage_part(ic<1>{}, pm + NS, s);
         const f4 ob = readout(sl ^ 1);   // pair pm - 1 (nothing at pm = 0)
         stage_part(ic<2>{}, pm + NS, s);
-        const f4 eb = LIN ? values(mb) : errors(mb, mma4(qk, ea, reduce(sl, 1)));
+        const f4 eb = LIN ? values(mb) : mma4(qk, ea, xb);
         stage_part(ic<3>{}, pm + NS, s);
         update(ma, ea);
         stage_part(ic<4>{}, pm + NS, s);
