@@ -21,8 +21,9 @@
 //   prep     per (head, group): the key sum at the group start (zkey_0 plus the
 //            earlier groups' sums, fp64), then chunk pairs in order: staging,
 //            key-sum prefix and 1/den per token, and the C x C factors on the
-//            matrix cores (N, P, and for a pair the cross factors Alpha^_a'K^_b
-//            and Alpha^_a'Phi_b), (I + N)^-1 by back substitution.
+//            matrix cores (N, P, and for a pair the cross factors Alpha^_a'K^_b,
+//            stored solved by chunk b's triangle as the forward's records hold
+//            it, and Alpha^_a'Phi_b), (I + N)^-1 by back substitution.
 //   memory   the forward's memory pass on those records.
 #include "vla_chunk_parts.h"
 #include "vla_record.h"
