@@ -280,7 +280,9 @@ vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
             sfor<4>([&](auto r) { t[J][int(r)] = 16 * I + g + 4 * r == 16 * J + n ? (double)lambda0 : 0.0; });
         });
     }
-    // G parts of the segments before j, in order, two parts in flight
+    // G parts of the segments before j, in order, PF parts in flight (as many
+    // as the registers allow: four at d = 64, two otherwise)
+    constexpr int PF = D == 64 ? 4 : 2;
     const int NPART = prefixed ? 1 : j * P;
     const double *gb = gram + (size_t)bh * S1 * P * DD + (prefixed ? (size_t)(j - 1) * P * DD : 0);
     auto load_part = [&](int s2, Tiles64<D> &x) {
@@ -288,14 +290,12 @@ vla_seginv(int S, int P, float lambda0, const float *A0, const float *zk0,
         sfor<NB>([&](auto J) { sfor<4>([&](auto r) { x[J][int(r)] = G[rc(J, r)]; }); });
     };
     int s = 0;
-    for (; s + 2 <= NPART; s += 2) {
-        Tiles64<D> x0, x1;
-        load_part(s, x0);
-        load_part(s + 1, x1);
-        sfor<NB>([&](auto J) { t[J] += x0[J]; });
-        sfor<NB>([&](auto J) { t[J] += x1[J]; });
+    for (; s + PF <= NPART; s += PF) {
+        Tiles64<D> x[PF];
+        sfor<PF>([&](auto i) { load_part(s + i, x[i]); });
+        sfor<PF>([&](auto i) { sfor<NB>([&](auto J) { t[J] += x[i][J]; }); });
     }
-    if (s < NPART) {
+    for (; s < NPART; ++s) {
         Tiles64<D> x0;
         load_part(s, x0);
         sfor<NB>([&](auto J) { t[J] += x0[J]; });
